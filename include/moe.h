@@ -1,0 +1,187 @@
+/*
+ * moe.h -- C ABI of libmoe: one GPU's share of a Mixture-of-Experts layer
+ * forward on MI355X (gfx950), as hand-written HIP kernels.
+ *
+ * Sources for the operations declared here:
+ *   [kucoin]   "Cursor's MoK logra un aumento del 2.37x en el rendimiento en
+ *              NVIDIA GB300 NVL72" (kucoin.com/es news; same text in Vietnamese,
+ *              Hindi and Chinese), sections 01, 02 and 03.
+ *   [qubstore] "Смесь котят: как Cursor создал открытое ядро, ускоряющее обучение
+ *              ИИ до 2,4 раз" (qubstore.ru): MoE primer, pull, ring buffer and
+ *              megakernel paragraphs.
+ *
+ * Shapes: R source ranks (each with its own token and output buffers; on one GPU
+ * the "remote" ranks are separate HBM allocations), T tokens per rank, hidden size
+ * d, E global experts of which E_local live on this GPU, top-k = k, expert SwiGLU
+ * width F.  A "pair" is one (rank, token, j) choice, j in [0, k); N is the number
+ * of pairs whose expert is local (known on the device only, = offsets[E_local]).
+ *
+ * Conventions for every call below:
+ *   - All buffer pointers are DEVICE pointers owned by the caller, except the
+ *     per-rank pointer tables (`const T* const* p`), which are HOST arrays of R
+ *     device pointers, read during the call only.  R <= MOE_MAX_RANKS.
+ *   - The library allocates no memory and keeps no pointer after a call returns.
+ *     Scratch lives in the caller's workspace `ws` of at least
+ *     moe_workspace_bytes() bytes, 256-byte aligned.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL =
+ *     the default stream)
+ *     and make no host<->device copy or synchronisation; the only host-side work
+ *     is argument checking and kernel launches.
+ *   - Return 0 on success, a negative MOE_E* code otherwise; a failing call
+ *     launches nothing (argument errors) or reports the HIP launch error.
+ *     Errors detected on the device (invalid expert placement, watchdog) are
+ *     written to a status word in the workspace, read by moe_read_status().
+ *   - NaN or infinite logits are outside the contract.
+ *   - Row storage: element type per moe_dtype_t, rows of d (or F) elements,
+ *     densely packed; every row must be 16-byte aligned (d * elem_size % 16 == 0).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MAX_RANKS 64
+
+/* error codes */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)   /* bad shape, k, dtype, placement or NULL pointer */
+#define MOE_EALIGN (-2)   /* row not 16-byte aligned, or d/F not a multiple the kernels need */
+#define MOE_ENOSPC (-3)   /* workspace too small, or ring smaller than one slot */
+#define MOE_EHIP (-4)     /* a HIP launch failed */
+#define MOE_ETIMEOUT (-5) /* a device-side wait exceeded its watchdog budget */
+#define MOE_EUNSUP (-6)   /* combination not built (e.g. dtype for this entry point) */
+
+typedef enum {
+  MOE_F32 = 0,   /* fp32 rows and weights, fp32 arithmetic */
+  MOE_BF16 = 1,  /* bf16 rows and weights, fp32 accumulation, bf16 h and outputs */
+  MOE_MXFP8 = 2  /* reserved: E4M3 elements with E8M0 scales per 32 along K */
+} moe_dtype_t;
+
+typedef struct {
+  int32_t R, T, d, E, k, F;
+  int32_t dtype; /* moe_dtype_t */
+} moe_shape_t;
+
+/* Expert placement: which global experts live on this GPU.
+ * expert_to_local: DEVICE array [E] of int32, value in [0, E_local) or -1; the
+ * local ids must be a bijection onto [0, E_local) (checked on the device: a bad
+ * map sets MOE_EINVAL in the status word and the layout yields N = 0). */
+typedef struct {
+  const int32_t* expert_to_local;
+  int32_t E_local;
+} moe_placement_t;
+
+/* Execution knobs.  Zero selects the default of each field. */
+typedef struct {
+  int32_t minibatch_rows;   /* rows of one expert released to compute at once (default 128) */
+  int32_t comm_cus;         /* persistent path: workgroups doing data movement (default 32) */
+  int32_t ring_slots;       /* persistent path: ring slots (default: as many as ring_bytes holds) */
+  int32_t trace;            /* reserved */
+  uint64_t watchdog_cycles; /* persistent path: spin budget of every device wait (default ~2 s) */
+} moe_exec_t;
+
+/* Limits checked by every call: 1 <= k <= 16, k <= E <= 1024, 1 <= E_local <= E. */
+
+/* Worst-case local pairs: R * T * min(k, E_local).  Sizes of xe/ye/pull_src below. */
+int64_t moe_max_pairs(const moe_shape_t* s, const moe_placement_t* p);
+
+/* Workspace bytes needed by every call below for this shape (a pure host function). */
+size_t moe_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex);
+
+/*
+ * moe_layout -- routing and sort-free layout generation.
+ *   [kucoin §01] the router picks several experts per token every step; the
+ *   system counts each expert's tokens, decides where they land on the target and
+ *   keeps one expert's tokens contiguous for the grouped GEMM.
+ *   [kucoin §02] / [qubstore, pull] the puller needs only (source GPU, position in
+ *   the source) -- a two-column schedule -- and decides local placement itself,
+ *   without sorting.
+ * Computes, for every rank r and token t (logits[r] is [T][E] fp32):
+ *   topk_idx[r][t][j]: the k largest logits, ties to the lower expert id, listed
+ *                      in descending logit order                    [R][T][k] int32
+ *   topk_w[r][t][j]:   exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k kept  [R][T][k] fp32
+ *   counts[e]:         pairs routed to global expert e, over all ranks       [E] int32
+ *   offsets[l]:        exclusive prefix of counts over local ids; offsets[E_local] = N
+ *                                                                   [E_local+1] int32
+ *   pull_src[s]:       (source rank, source token) of local row s, rows of one
+ *                      expert in ascending (r, t, j) order   [moe_max_pairs][2] int32
+ *   slot_of[r][t][j]:  row s of the pair, or -1 if its expert is not local [R][T][k] int32
+ * Also writes the chunk table (<= minibatch_rows rows of one expert per chunk)
+ * into `ws`, used by the calls below.  All outputs are bit-exact (integer work;
+ * the gate uses fp32 expf).
+ */
+int moe_layout(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+               const float* const* logits, int32_t* topk_idx, float* topk_w, int32_t* counts,
+               int32_t* offsets, int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes,
+               void* stream);
+
+/*
+ * moe_dispatch_pull -- pull dispatch [kucoin §02: the expert side reads the
+ * token rows it needs from their source; qubstore, pull paragraph].
+ *   xe[s][:] = x[pull_src[s].rank][pull_src[s].token][:]  for s in [0, N)
+ * x: R device pointers, each [T][d] rows.  xe: [moe_max_pairs][d] rows.
+ * offsets/ws: from moe_layout (N is read on the device).  Bit-exact copy.
+ */
+int moe_dispatch_pull(const moe_shape_t* s, const moe_placement_t* p, const void* const* x,
+                      const int32_t* pull_src, const int32_t* offsets, void* xe, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn -- grouped SwiGLU expert FFN [kucoin §01: grouped GEMM over
+ * expert-contiguous rows; kucoin §02: SwiGLU in the expert data path].
+ * For every local expert l and row s in [offsets[l], offsets[l+1]):
+ *   h = silu(xe[s] W1[l]^T) * (xe[s] W3[l]^T)   (length F; stored as the row dtype)
+ *   ye[s] = h W2[l]^T                             (length d; fp32 accumulate)
+ * w1, w3: [E_local][F][d]; w2: [E_local][d][F]; xe, ye: [moe_max_pairs][d].
+ * bf16: d and F must be multiples of 64.  Accuracy: see moe_forward tolerances
+ * in the tests (bf16 max row-relative error <= 2e-2 against an fp64 oracle).
+ */
+int moe_expert_ffn(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+                   const void* xe, const int32_t* offsets, const void* w1, const void* w3,
+                   const void* w2, void* ye, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine_push -- push combine then the final weighted merge
+ *   [kucoin §01: combine returns each result to the token's original position;
+ *   kucoin §02: combine is a push since the destination is known; kucoin §03: the
+ *   final weighted merge is a step of its own].
+ * Push: for s in [0, N): recv[r][t][j][:] = ye[s][:] where (r, t) = pull_src[s]
+ *   and j is the pair with slot_of[r][t][j] == s (bit-exact copy, no atomics).
+ * Merge: y[r][t][:] = sum over ascending j with slot_of[r][t][j] >= 0 of
+ *   topk_w[r][t][j] * recv[r][t][j][:], fp32 accumulation, rounded once to the row
+ *   dtype; exactly 0 for a token with no local pair.  Deterministic.
+ * recv: R device pointers, each [T][k][d]; y: R device pointers, each [T][d].
+ */
+int moe_combine_push(const moe_shape_t* s, const moe_placement_t* p, const void* ye,
+                     const int32_t* pull_src, const int32_t* slot_of, const float* topk_w,
+                     const int32_t* offsets, void* const* recv, void* const* y, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/*
+ * moe_forward -- the four calls above in order on one stream (the unfused,
+ * multi-kernel path).  xe and ye are [moe_max_pairs][d] staging rows.
+ */
+int moe_forward(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+                const float* const* logits, const void* const* x, const void* w1, const void* w3,
+                const void* w2, void* xe, void* ye, void* const* recv, void* const* y,
+                int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes, void* stream);
+
+/* Syncs `stream` and returns the device status word (0, MOE_EINVAL or MOE_ETIMEOUT). */
+int moe_read_status(const void* ws, void* stream);
+
+/* Static description of an error code. */
+const char* moe_strerror(int code);
+
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,92 @@
+// Shared device/host definitions of libmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// fixed tile geometry
+// ---------------------------------------------------------------------------
+constexpr int kTokPerLayoutBlock = 64;   // tokens per histogram block of the layout
+constexpr int kGemmBM = 256;             // rows of one grouped-GEMM tile (bf16 path)
+constexpr int kGemmBN = 256;             // output columns of one tile
+constexpr int kGemmBK = 64;              // K step staged in LDS
+constexpr int kSimtBM = 64;              // fp32 SIMT path tile
+constexpr int kSimtBN = 64;
+
+// ---------------------------------------------------------------------------
+// workspace layout (computed on the host from the shape; every region 256-byte aligned)
+// ---------------------------------------------------------------------------
+enum CtrlSlot {
+  kCtrlStatus = 0,   // device status word (MOE_OK / MOE_EINVAL / MOE_ETIMEOUT)
+  kCtrlN = 1,        // local pairs N
+  kCtrlMTiles = 2,   // grouped-GEMM row tiles over all local experts
+  kCtrlChunks = 3,   // minibatch chunks over all local experts
+  kCtrlWords = 64
+};
+
+struct WsLayout {
+  size_t ctrl, l2g, mtile_base, chunk_base, blockhist, blockbase, hbuf, total;
+  int32_t nb;        // layout blocks
+  int64_t max_pairs;
+  int32_t max_mtiles;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline WsLayout ws_layout(const moe_shape_t& s, int32_t E_local) {
+  WsLayout w{};
+  const int64_t tokens = int64_t(s.R) * s.T;
+  w.nb = int32_t((tokens + kTokPerLayoutBlock - 1) / kTokPerLayoutBlock);
+  w.max_pairs = tokens * (s.k < E_local ? s.k : E_local);
+  const int bm = (s.dtype == MOE_F32) ? kSimtBM : kGemmBM;
+  w.max_mtiles = int32_t((w.max_pairs + bm - 1) / bm + E_local);
+  const size_t esz = (s.dtype == MOE_F32) ? 4 : 2;
+  size_t o = 0;
+  w.ctrl = o;        o = align256(o + kCtrlWords * 4);
+  w.l2g = o;         o = align256(o + size_t(E_local) * 4);
+  w.mtile_base = o;  o = align256(o + size_t(E_local + 1) * 4);
+  w.chunk_base = o;  o = align256(o + size_t(E_local + 1) * 4);
+  w.blockhist = o;   o = align256(o + size_t(w.nb) * s.E * 4);
+  w.blockbase = o;   o = align256(o + size_t(w.nb) * E_local * 4);
+  w.hbuf = o;        o = align256(o + size_t(w.max_pairs) * s.F * esz);
+  w.total = o;
+  return w;
+}
+
+// per-rank pointer table passed by value to kernels
+template <typename T>
+struct RankPtrs {
+  T p[MOE_MAX_RANKS];
+};
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(uint32_t(b) << 16);
+}
+
+// round-to-nearest-even fp32 -> bf16 (finite inputs)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + __expf(-a)); }
+
+}  // namespace moe

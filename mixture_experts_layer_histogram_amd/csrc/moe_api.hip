@@ -1,0 +1,200 @@
+// extern "C" entry points of libmoe: argument checks, workspace sizing, launches.
+// Every check runs before the first HIP call, so argument errors need no GPU.
+#include <string.h>
+
+#include "common.hpp"
+
+namespace moe {
+hipError_t launch_layout(const moe_shape_t& s, const int32_t* e2l, int El, int mb, const float* const* logits,
+                         int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                         int32_t* pull_src, int32_t* slot_of, char* ws, const WsLayout& L, hipStream_t st);
+hipError_t launch_dispatch(const moe_shape_t& s, const void* const* x, const int32_t* pull_src, char* xe,
+                           const int32_t* ctrl, int cus, hipStream_t st);
+hipError_t launch_ffn(const moe_shape_t& s, int El, const void* xe, const int32_t* offsets, const void* w1,
+                      const void* w3, const void* w2, void* ye, char* ws, const WsLayout& L, int cus,
+                      hipStream_t st);
+hipError_t launch_combine(const moe_shape_t& s, const char* ye, const int32_t* pull_src,
+                          const int32_t* slot_of, const float* topk_w, void* const* recv, void* const* y,
+                          const int32_t* ctrl, int cus, hipStream_t st);
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+int check_shape(const moe_shape_t* s, const moe_placement_t* p) {
+  if (!s || !p) return MOE_EINVAL;
+  if (s->R < 1 || s->R > MOE_MAX_RANKS || s->T < 1 || s->d < 1 || s->F < 1) return MOE_EINVAL;
+  if (s->E < 1 || s->E > 1024 || s->k < 1 || s->k > 16 || s->k > s->E) return MOE_EINVAL;
+  if (p->E_local < 1 || p->E_local > s->E) return MOE_EINVAL;
+  if (int64_t(s->R) * s->T * s->k >= (int64_t(1) << 31)) return MOE_EINVAL;
+  if (s->dtype == MOE_MXFP8) return MOE_EUNSUP;
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_EINVAL;
+  const int esz = s->dtype == MOE_F32 ? 4 : 2;
+  if ((int64_t(s->d) * esz) % 16 || (int64_t(s->F) * esz) % 16) return MOE_EALIGN;
+  if (s->dtype == MOE_BF16 && (s->d % kGemmBK || s->F % kGemmBK)) return MOE_EALIGN;
+  return MOE_OK;
+}
+
+int check_ws(const moe_shape_t* s, const moe_placement_t* p, const void* ws, size_t ws_bytes) {
+  if (!ws) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return MOE_EALIGN;
+  if (ws_bytes < ws_layout(*s, p->E_local).total) return MOE_ENOSPC;
+  return MOE_OK;
+}
+
+template <typename T>
+int check_ptr_table(const T* const* tab, int R) {
+  if (!tab) return MOE_EINVAL;
+  for (int r = 0; r < R; ++r)
+    if (!tab[r] || (reinterpret_cast<uintptr_t>(tab[r]) & 15)) return tab[r] ? MOE_EALIGN : MOE_EINVAL;
+  return MOE_OK;
+}
+
+int aligned16(const void* q) { return q && !(reinterpret_cast<uintptr_t>(q) & 15); }
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static int cached[64] = {0};
+  if (dev < 64 && cached[dev]) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (n < 8) n = 8;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
+int minibatch_of(const moe_exec_t* ex) { return (ex && ex->minibatch_rows > 0) ? ex->minibatch_rows : 128; }
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_max_pairs(const moe_shape_t* s, const moe_placement_t* p) {
+  if (!s || !p || s->R < 1 || s->T < 1 || s->k < 1 || p->E_local < 1) return -1;
+  return int64_t(s->R) * s->T * (s->k < p->E_local ? s->k : p->E_local);
+}
+
+size_t moe_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex) {
+  (void)ex;
+  if (check_shape(s, p) != MOE_OK) return 0;
+  return ws_layout(*s, p->E_local).total;
+}
+
+int moe_layout(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+               const float* const* logits, int32_t* topk_idx, float* topk_w, int32_t* counts,
+               int32_t* offsets, int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes,
+               void* stream) {
+  int rc = check_shape(s, p);
+  if (rc) return rc;
+  if (!p->expert_to_local || !topk_idx || !topk_w || !counts || !offsets || !pull_src || !slot_of)
+    return MOE_EINVAL;
+  if (ex && ex->minibatch_rows < 0) return MOE_EINVAL;
+  if ((rc = check_ptr_table(logits, s->R))) return rc;
+  if ((rc = check_ws(s, p, ws, ws_bytes))) return rc;
+  const WsLayout L = ws_layout(*s, p->E_local);
+  return hip_rc(launch_layout(*s, p->expert_to_local, p->E_local, minibatch_of(ex), logits, topk_idx, topk_w,
+                              counts, offsets, pull_src, slot_of, static_cast<char*>(ws), L,
+                              static_cast<hipStream_t>(stream)));
+}
+
+int moe_dispatch_pull(const moe_shape_t* s, const moe_placement_t* p, const void* const* x,
+                      const int32_t* pull_src, const int32_t* offsets, void* xe, void* ws, size_t ws_bytes,
+                      void* stream) {
+  int rc = check_shape(s, p);
+  if (rc) return rc;
+  if (!pull_src || !offsets) return MOE_EINVAL;
+  if (!aligned16(xe)) return xe ? MOE_EALIGN : MOE_EINVAL;
+  if ((rc = check_ptr_table(x, s->R))) return rc;
+  if ((rc = check_ws(s, p, ws, ws_bytes))) return rc;
+  const WsLayout L = ws_layout(*s, p->E_local);
+  return hip_rc(launch_dispatch(*s, x, pull_src, static_cast<char*>(xe),
+                                reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + L.ctrl), cu_count(),
+                                static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_ffn(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex, const void* xe,
+                   const int32_t* offsets, const void* w1, const void* w3, const void* w2, void* ye, void* ws,
+                   size_t ws_bytes, void* stream) {
+  (void)ex;
+  int rc = check_shape(s, p);
+  if (rc) return rc;
+  if (!offsets) return MOE_EINVAL;
+  const void* bufs[] = {xe, w1, w3, w2, ye};
+  for (const void* b : bufs)
+    if (!aligned16(b)) return b ? MOE_EALIGN : MOE_EINVAL;
+  if ((rc = check_ws(s, p, ws, ws_bytes))) return rc;
+  const WsLayout L = ws_layout(*s, p->E_local);
+  return hip_rc(launch_ffn(*s, p->E_local, xe, offsets, w1, w3, w2, ye, static_cast<char*>(ws), L, cu_count(),
+                           static_cast<hipStream_t>(stream)));
+}
+
+int moe_combine_push(const moe_shape_t* s, const moe_placement_t* p, const void* ye, const int32_t* pull_src,
+                     const int32_t* slot_of, const float* topk_w, const int32_t* offsets, void* const* recv,
+                     void* const* y, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(s, p);
+  if (rc) return rc;
+  if (!pull_src || !slot_of || !topk_w || !offsets) return MOE_EINVAL;
+  if (!aligned16(ye)) return ye ? MOE_EALIGN : MOE_EINVAL;
+  if ((rc = check_ptr_table(recv, s->R))) return rc;
+  if ((rc = check_ptr_table(y, s->R))) return rc;
+  if ((rc = check_ws(s, p, ws, ws_bytes))) return rc;
+  const WsLayout L = ws_layout(*s, p->E_local);
+  return hip_rc(launch_combine(*s, static_cast<const char*>(ye), pull_src, slot_of, topk_w, recv, y,
+                               reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + L.ctrl), cu_count(),
+                               static_cast<hipStream_t>(stream)));
+}
+
+int moe_forward(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex, const float* const* logits,
+                const void* const* x, const void* w1, const void* w3, const void* w2, void* xe, void* ye,
+                void* const* recv, void* const* y, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                int32_t* offsets, int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes,
+                void* stream) {
+  int rc = check_shape(s, p);
+  if (rc) return rc;
+  // validate every stage's arguments before launching any of them
+  if (!p->expert_to_local || !topk_idx || !topk_w || !counts || !offsets || !pull_src || !slot_of)
+    return MOE_EINVAL;
+  const void* bufs[] = {xe, ye, w1, w3, w2};
+  for (const void* b : bufs)
+    if (!aligned16(b)) return b ? MOE_EALIGN : MOE_EINVAL;
+  if ((rc = check_ptr_table(logits, s->R)) || (rc = check_ptr_table(x, s->R)) ||
+      (rc = check_ptr_table(recv, s->R)) || (rc = check_ptr_table(y, s->R)))
+    return rc;
+  if ((rc = check_ws(s, p, ws, ws_bytes))) return rc;
+  if ((rc = moe_layout(s, p, ex, logits, topk_idx, topk_w, counts, offsets, pull_src, slot_of, ws, ws_bytes,
+                       stream)))
+    return rc;
+  if ((rc = moe_dispatch_pull(s, p, x, pull_src, offsets, xe, ws, ws_bytes, stream))) return rc;
+  if ((rc = moe_expert_ffn(s, p, ex, xe, offsets, w1, w3, w2, ye, ws, ws_bytes, stream))) return rc;
+  return moe_combine_push(s, p, ye, pull_src, slot_of, topk_w, offsets, recv, y, ws, ws_bytes, stream);
+}
+
+int moe_read_status(const void* ws, void* stream) {
+  if (!ws) return MOE_EINVAL;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_EHIP;
+  int32_t st = 0;
+  if (hipMemcpy(&st, static_cast<const char*>(ws) + kCtrlStatus * 4, 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return MOE_EHIP;
+  return st;
+}
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (shape, k, dtype, placement or null pointer)";
+    case MOE_EALIGN: return "misaligned buffer or unsupported d/F multiple";
+    case MOE_ENOSPC: return "workspace or ring too small";
+    case MOE_EHIP: return "HIP launch failed";
+    case MOE_ETIMEOUT: return "device wait exceeded its watchdog budget";
+    case MOE_EUNSUP: return "combination not supported by this build";
+    default: return "unknown error";
+  }
+}
+
+const char* moe_version(void) { return "libmoe 0.1 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,179 @@
+// Row movers for gfx950: pull dispatch, push combine and the ordered weighted merge.
+//
+// Operations (MoK article, kucoin.com/es "Cursor's MoK logra un aumento del 2.37x ...",
+// sections 01-03): the expert side pulls each token row it needs from its source
+// buffer (dispatch); results are pushed back to the token's own position (combine);
+// the final weighted merge sums a token's expert outputs with its gate weights.
+//
+// These are HBM-bound copies, so every lane moves 16-byte vectors and keeps several
+// of them in flight; there is no reuse for LDS staging to exploit.  A wave owns one
+// row at a time; the grid strides over rows, and the row count N is read from the
+// layout's control block on the device (no host round trip).
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kMoveUnroll = 8;   // 16-byte vectors in flight per lane
+
+__device__ __forceinline__ void copy_row(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int n16,
+                                         int lane) {
+  for (int base = 0; base < n16; base += 64 * kMoveUnroll) {
+    u32x4 v[kMoveUnroll];
+#pragma unroll
+    for (int u = 0; u < kMoveUnroll; ++u) {
+      const int i = base + u * 64 + lane;
+      if (i < n16) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kMoveUnroll; ++u) {
+      const int i = base + u * 64 + lane;
+      if (i < n16) dst[i] = v[u];
+    }
+  }
+}
+
+// xe[s] = x[pull_src[s].rank][pull_src[s].token]
+__global__ __launch_bounds__(256) void dispatch_pull_kernel(RankPtrs<const char*> x,
+                                                            const int32_t* __restrict__ pull_src,
+                                                            const int32_t* __restrict__ ctrl,
+                                                            char* __restrict__ xe, int row_bytes) {
+  const int N = ctrl[kCtrlN];
+  const int lane = threadIdx.x & 63;
+  const int n16 = row_bytes >> 4;
+  const int nw = gridDim.x * 4;
+  for (int s = blockIdx.x * 4 + (threadIdx.x >> 6); s < N; s += nw) {
+    const int r = pull_src[2 * int64_t(s)];
+    const int t = pull_src[2 * int64_t(s) + 1];
+    copy_row(reinterpret_cast<const u32x4*>(x.p[r] + int64_t(t) * row_bytes),
+             reinterpret_cast<u32x4*>(xe + int64_t(s) * row_bytes), n16, lane);
+  }
+}
+
+// recv[r][t][j] = ye[s] for the pair (r, t, j) whose row is s
+__global__ __launch_bounds__(256) void combine_push_kernel(const char* __restrict__ ye,
+                                                           const int32_t* __restrict__ pull_src,
+                                                           const int32_t* __restrict__ slot_of,
+                                                           const int32_t* __restrict__ ctrl,
+                                                           RankPtrs<char*> recv, int T, int k,
+                                                           int row_bytes) {
+  const int N = ctrl[kCtrlN];
+  const int lane = threadIdx.x & 63;
+  const int n16 = row_bytes >> 4;
+  const int nw = gridDim.x * 4;
+  for (int s = blockIdx.x * 4 + (threadIdx.x >> 6); s < N; s += nw) {
+    const int r = pull_src[2 * int64_t(s)];
+    const int t = pull_src[2 * int64_t(s) + 1];
+    const int32_t* so = slot_of + (int64_t(r) * T + t) * k;
+    int j = 0;
+    for (int jj = 0; jj < k; ++jj)
+      if (so[jj] == s) j = jj;
+    copy_row(reinterpret_cast<const u32x4*>(ye + int64_t(s) * row_bytes),
+             reinterpret_cast<u32x4*>(recv.p[r] + (int64_t(t) * k + j) * row_bytes), n16, lane);
+  }
+}
+
+// y[r][t] = sum over ascending j with a local expert of g[r][t][j] * recv[r][t][j]
+template <bool BF16>
+__global__ __launch_bounds__(256) void weighted_merge_kernel(RankPtrs<const char*> recv,
+                                                             RankPtrs<char*> y,
+                                                             const int32_t* __restrict__ slot_of,
+                                                             const float* __restrict__ topk_w, int R,
+                                                             int T, int k, int d) {
+  constexpr int EPV = BF16 ? 8 : 4;      // elements per 16-byte vector
+  constexpr int VPL = 4;                 // vectors per lane per column batch
+  const int lane = threadIdx.x & 63;
+  const int row_bytes = d * (BF16 ? 2 : 4);
+  const int n16 = row_bytes >> 4;
+  const int64_t RT = int64_t(R) * T;
+  const int64_t nw = int64_t(gridDim.x) * 4;
+  for (int64_t g = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); g < RT; g += nw) {
+    const int r = int(g / T);
+    const int t = int(g - int64_t(r) * T);
+    const int32_t* so = slot_of + g * k;
+    const float* gw = topk_w + g * k;
+    const char* rrow = recv.p[r] + int64_t(t) * k * row_bytes;
+    u32x4* yrow = reinterpret_cast<u32x4*>(y.p[r] + int64_t(t) * row_bytes);
+    for (int cb = 0; cb < n16; cb += 64 * VPL) {
+      float acc[VPL][EPV];
+#pragma unroll
+      for (int u = 0; u < VPL; ++u)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[u][e] = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        if (so[j] < 0) continue;
+        const float gj = gw[j];
+        const u32x4* src = reinterpret_cast<const u32x4*>(rrow + int64_t(j) * row_bytes);
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) {
+          const int i = cb + u * 64 + lane;
+          if (i < n16) {
+            const u32x4 v = __builtin_nontemporal_load(src + i);
+            if (BF16) {
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                acc[u][2 * w] = fmaf(gj, __uint_as_float(v[w] << 16), acc[u][2 * w]);
+                acc[u][2 * w + 1] = fmaf(gj, __uint_as_float(v[w] & 0xFFFF0000u), acc[u][2 * w + 1]);
+              }
+            } else {
+#pragma unroll
+              for (int w = 0; w < 4; ++w) acc[u][w] = fmaf(gj, __uint_as_float(v[w]), acc[u][w]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < VPL; ++u) {
+        const int i = cb + u * 64 + lane;
+        if (i < n16) {
+          u32x4 o;
+          if (BF16) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(acc[u][2 * w], acc[u][2 * w + 1]);
+          } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) o[w] = __float_as_uint(acc[u][w]);
+          }
+          yrow[i] = o;
+        }
+      }
+    }
+  }
+}
+
+static int mover_grid(int cus) { return cus * 8; }
+
+hipError_t launch_dispatch(const moe_shape_t& s, const void* const* x, const int32_t* pull_src, char* xe,
+                           const int32_t* ctrl, int cus, hipStream_t st) {
+  RankPtrs<const char*> xp{};
+  for (int r = 0; r < s.R; ++r) xp.p[r] = static_cast<const char*>(x[r]);
+  const int row_bytes = s.d * (s.dtype == MOE_F32 ? 4 : 2);
+  hipLaunchKernelGGL(dispatch_pull_kernel, dim3(mover_grid(cus)), dim3(256), 0, st, xp, pull_src, ctrl, xe,
+                     row_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const moe_shape_t& s, const char* ye, const int32_t* pull_src,
+                          const int32_t* slot_of, const float* topk_w, void* const* recv, void* const* y,
+                          const int32_t* ctrl, int cus, hipStream_t st) {
+  RankPtrs<char*> rp{};
+  RankPtrs<const char*> rcp{};
+  RankPtrs<char*> yp{};
+  for (int r = 0; r < s.R; ++r) {
+    rp.p[r] = static_cast<char*>(recv[r]);
+    rcp.p[r] = static_cast<const char*>(recv[r]);
+    yp.p[r] = static_cast<char*>(y[r]);
+  }
+  const bool bf = s.dtype != MOE_F32;
+  const int row_bytes = s.d * (bf ? 2 : 4);
+  hipLaunchKernelGGL(combine_push_kernel, dim3(mover_grid(cus)), dim3(256), 0, st, ye, pull_src, slot_of,
+                     ctrl, rp, s.T, s.k, row_bytes);
+  if (bf)
+    hipLaunchKernelGGL(weighted_merge_kernel<true>, dim3(mover_grid(cus)), dim3(256), 0, st, rcp, yp,
+                       slot_of, topk_w, s.R, s.T, s.k, s.d);
+  else
+    hipLaunchKernelGGL(weighted_merge_kernel<false>, dim3(mover_grid(cus)), dim3(256), 0, st, rcp, yp,
+                       slot_of, topk_w, s.R, s.T, s.k, s.d);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,94 @@
+"""Device buffers for one layer invocation (torch allocation and upload only).
+
+``DeviceProblem`` owns every input and output tensor the C ABI needs for one
+config, uploads the seeded host inputs once, and calls the binding.  No
+arithmetic of the layer happens here.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import moe
+
+
+def _to_device_store(a: np.ndarray, dtype: str, device):
+    import torch
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+    return t.view(torch.bfloat16)
+
+
+class DeviceProblem:
+    def __init__(self, cfg, inp, device="cuda:0", minibatch=None, alloc_outputs=True):
+        import torch
+        self.torch = torch
+        self.cfg = cfg
+        self.device = torch.device(device)
+        dt = cfg.dtype
+        self.shape = moe.Shape(cfg.R, cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, moe.DTYPE_CODE[dt])
+        self.e2l = torch.from_numpy(np.ascontiguousarray(inp.expert_to_local, dtype=np.int32)).to(self.device)
+        self.placement = moe.Placement(self.e2l.data_ptr(), cfg.E_local)
+        self.ex = moe.Exec(minibatch or cfg.minibatch, 0, 0, 0, 0)
+        self.logits = [torch.from_numpy(np.ascontiguousarray(inp.logits[r])).to(self.device)
+                       for r in range(cfg.R)]
+        self.x = [_to_device_store(inp.x_store[r], dt, self.device) for r in range(cfg.R)]
+        self.w1 = _to_device_store(inp.w1_store, dt, self.device)
+        self.w3 = _to_device_store(inp.w3_store, dt, self.device)
+        self.w2 = _to_device_store(inp.w2_store, dt, self.device)
+        self.nmax = moe.moe_max_pairs(self.shape, self.placement)
+        self.ws_bytes = moe.moe_workspace_bytes(self.shape, self.placement, self.ex)
+        if self.ws_bytes == 0:
+            raise ValueError("shape rejected by moe_workspace_bytes")
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        if alloc_outputs:
+            self.alloc_outputs()
+
+    def alloc_outputs(self):
+        torch, cfg, dev = self.torch, self.cfg, self.device
+        ed = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+        R, T, k, d = cfg.R, cfg.T, cfg.k, cfg.d
+        self.topk_idx = torch.empty((R, T, k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((R, T, k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(cfg.E_local + 1, dtype=torch.int32, device=dev)
+        self.pull_src = torch.empty((self.nmax, 2), dtype=torch.int32, device=dev)
+        self.slot_of = torch.empty((R, T, k), dtype=torch.int32, device=dev)
+        self.xe = torch.empty((self.nmax, d), dtype=ed, device=dev)
+        self.ye = torch.empty((self.nmax, d), dtype=ed, device=dev)
+        self.recv = [torch.zeros((T, k, d), dtype=ed, device=dev) for _ in range(R)]
+        self.y = [torch.empty((T, d), dtype=ed, device=dev) for _ in range(R)]
+
+    # ---- the C entry points on this problem's buffers ----
+    def layout(self, stream=None):
+        moe.moe_layout(self.shape, self.placement, self.ex, self.logits, self.topk_idx, self.topk_w,
+                       self.counts, self.offsets, self.pull_src, self.slot_of, self.ws, stream=stream)
+
+    def dispatch(self, stream=None):
+        moe.moe_dispatch_pull(self.shape, self.placement, self.x, self.pull_src, self.offsets, self.xe,
+                              self.ws, stream=stream)
+
+    def ffn(self, stream=None):
+        moe.moe_expert_ffn(self.shape, self.placement, self.ex, self.xe, self.offsets, self.w1, self.w3,
+                           self.w2, self.ye, self.ws, stream=stream)
+
+    def combine(self, stream=None):
+        moe.moe_combine_push(self.shape, self.placement, self.ye, self.pull_src, self.slot_of, self.topk_w,
+                             self.offsets, self.recv, self.y, self.ws, stream=stream)
+
+    def forward(self, stream=None):
+        moe.moe_forward(self.shape, self.placement, self.ex, self.logits, self.x, self.w1, self.w3, self.w2,
+                        self.xe, self.ye, self.recv, self.y, self.topk_idx, self.topk_w, self.counts,
+                        self.offsets, self.pull_src, self.slot_of, self.ws, stream=stream)
+
+    def status(self, stream=None) -> int:
+        return moe.moe_read_status(self.ws, stream)
+
+    # ---- host copies ----
+    def N(self) -> int:
+        return int(self.offsets[-1].item())
+
+    @staticmethod
+    def rows_f64(t) -> np.ndarray:
+        """Exact float64 values of a device tensor (fp32 or bf16)."""
+        return t.float().cpu().numpy().astype(np.float64)

@@ -1,0 +1,179 @@
+"""Thin ctypes binding of libmoe (include/moe.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libmoe.so.  Tensors are torch device tensors (PyTorch is used for device memory
+and streams); each function takes the same arguments as its C namesake and
+raises MoEError on a non-zero return code.  There is no fallback: importing the
+binding without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+
+MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
+DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
+MOE_MAX_RANKS = 64
+ERRORS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_ENOSPC", -4: "MOE_EHIP",
+          -5: "MOE_ETIMEOUT", -6: "MOE_EUNSUP"}
+
+# every symbol include/moe.h declares
+EXPORTS = ["moe_max_pairs", "moe_workspace_bytes", "moe_layout", "moe_dispatch_pull",
+           "moe_expert_ffn", "moe_combine_push", "moe_forward", "moe_read_status",
+           "moe_strerror", "moe_version"]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {ERRORS.get(code, code)} ({strerror(code)})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("R", ctypes.c_int32), ("T", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("F", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class Placement(ctypes.Structure):
+    _fields_ = [("expert_to_local", ctypes.c_void_p), ("E_local", ctypes.c_int32)]
+
+
+class Exec(ctypes.Structure):
+    _fields_ = [("minibatch_rows", ctypes.c_int32), ("comm_cus", ctypes.c_int32),
+                ("ring_slots", ctypes.c_int32), ("trace", ctypes.c_int32),
+                ("watchdog_cycles", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (built in-tree by build.py); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libmoe.so not built: {LIB_PATH} (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        P, VP, I32, SZ = ctypes.POINTER, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        S, PL, EX = P(Shape), P(Placement), P(Exec)
+        L.moe_max_pairs.argtypes = [S, PL]
+        L.moe_max_pairs.restype = ctypes.c_int64
+        L.moe_workspace_bytes.argtypes = [S, PL, EX]
+        L.moe_workspace_bytes.restype = SZ
+        L.moe_layout.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_dispatch_pull.argtypes = [S, PL, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_expert_ffn.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_combine_push.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_forward.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, VP, VP, VP,
+                                  VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_read_status.argtypes = [VP, VP]
+        L.moe_strerror.argtypes = [I32]
+        L.moe_strerror.restype = ctypes.c_char_p
+        L.moe_version.restype = ctypes.c_char_p
+        for f in ("moe_layout", "moe_dispatch_pull", "moe_expert_ffn", "moe_combine_push",
+                  "moe_forward", "moe_read_status"):
+            getattr(L, f).restype = I32
+        _lib = L
+    return _lib
+
+
+# --------------------------------------------------------------------------- marshalling
+def _p(t):
+    """Device pointer of a tensor (or an int address / None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _table(ts):
+    """Host array of R device pointers."""
+    if ts is None:
+        return None
+    ptrs = [_p(t) for t in ts]
+    return ctypes.cast((ctypes.c_void_p * len(ptrs))(*ptrs), ctypes.c_void_p)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str) -> int:
+    if rc != 0:
+        raise MoEError(rc, where)
+    return rc
+
+
+def strerror(code: int) -> str:
+    return lib().moe_strerror(int(code)).decode()
+
+
+def moe_version() -> str:
+    return lib().moe_version().decode()
+
+
+def moe_max_pairs(shape: Shape, placement: Placement) -> int:
+    return int(lib().moe_max_pairs(ctypes.byref(shape), ctypes.byref(placement)))
+
+
+def moe_workspace_bytes(shape: Shape, placement: Placement, ex: Exec | None = None) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(shape), ctypes.byref(placement),
+                                         ctypes.byref(ex) if ex is not None else None))
+
+
+def moe_layout(shape, placement, ex, logits, topk_idx, topk_w, counts, offsets, pull_src, slot_of,
+               ws, ws_bytes=None, stream=None, check=True):
+    rc = lib().moe_layout(ctypes.byref(shape), ctypes.byref(placement),
+                          ctypes.byref(ex) if ex is not None else None, _table(logits), _p(topk_idx),
+                          _p(topk_w), _p(counts), _p(offsets), _p(pull_src), _p(slot_of), _p(ws),
+                          ws.numel() if ws_bytes is None else ws_bytes, _stream(stream))
+    return _check(rc, "moe_layout") if check else rc
+
+
+def moe_dispatch_pull(shape, placement, x, pull_src, offsets, xe, ws, ws_bytes=None, stream=None,
+                      check=True):
+    rc = lib().moe_dispatch_pull(ctypes.byref(shape), ctypes.byref(placement), _table(x), _p(pull_src),
+                                 _p(offsets), _p(xe), _p(ws), ws.numel() if ws_bytes is None else ws_bytes,
+                                 _stream(stream))
+    return _check(rc, "moe_dispatch_pull") if check else rc
+
+
+def moe_expert_ffn(shape, placement, ex, xe, offsets, w1, w3, w2, ye, ws, ws_bytes=None, stream=None,
+                   check=True):
+    rc = lib().moe_expert_ffn(ctypes.byref(shape), ctypes.byref(placement),
+                              ctypes.byref(ex) if ex is not None else None, _p(xe), _p(offsets), _p(w1),
+                              _p(w3), _p(w2), _p(ye), _p(ws), ws.numel() if ws_bytes is None else ws_bytes,
+                              _stream(stream))
+    return _check(rc, "moe_expert_ffn") if check else rc
+
+
+def moe_combine_push(shape, placement, ye, pull_src, slot_of, topk_w, offsets, recv, y, ws, ws_bytes=None,
+                     stream=None, check=True):
+    rc = lib().moe_combine_push(ctypes.byref(shape), ctypes.byref(placement), _p(ye), _p(pull_src),
+                                _p(slot_of), _p(topk_w), _p(offsets), _table(recv), _table(y), _p(ws),
+                                ws.numel() if ws_bytes is None else ws_bytes, _stream(stream))
+    return _check(rc, "moe_combine_push") if check else rc
+
+
+def moe_forward(shape, placement, ex, logits, x, w1, w3, w2, xe, ye, recv, y, topk_idx, topk_w, counts,
+                offsets, pull_src, slot_of, ws, ws_bytes=None, stream=None, check=True):
+    rc = lib().moe_forward(ctypes.byref(shape), ctypes.byref(placement),
+                           ctypes.byref(ex) if ex is not None else None, _table(logits), _table(x), _p(w1),
+                           _p(w3), _p(w2), _p(xe), _p(ye), _table(recv), _table(y), _p(topk_idx),
+                           _p(topk_w), _p(counts), _p(offsets), _p(pull_src), _p(slot_of), _p(ws),
+                           ws.numel() if ws_bytes is None else ws_bytes, _stream(stream))
+    return _check(rc, "moe_forward") if check else rc
+
+
+def moe_read_status(ws, stream=None) -> int:
+    return int(lib().moe_read_status(_p(ws), _stream(stream)))

@@ -1,0 +1,130 @@
+"""C-ABI host-side tests (no GPU): the library loads, exports what include/moe.h
+declares, sizes its workspace, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_histogram_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# aligned fake device addresses: every call below must fail its checks before using them
+FAKE = 0x7F0000000000
+
+
+def _declared_symbols():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    declared = _declared_symbols()
+    assert declared, "no declarations parsed"
+    assert set(declared) == set(moe.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_version_and_strerror():
+    assert "gfx950" in moe.moe_version()
+    for code in moe.ERRORS:
+        assert moe.strerror(code)
+    assert moe.strerror(-99) == "unknown error"
+
+
+def _shape(**kw):
+    d = dict(R=8, T=4096, d=7168, E=256, k=8, F=2048, dtype=moe.MOE_BF16)
+    d.update(kw)
+    return moe.Shape(d["R"], d["T"], d["d"], d["E"], d["k"], d["F"], d["dtype"])
+
+
+def _pl(El=32):
+    return moe.Placement(FAKE, El)
+
+
+def test_max_pairs_and_workspace():
+    s, p = _shape(), _pl()
+    assert moe.moe_max_pairs(s, p) == 8 * 4096 * 8
+    assert moe.moe_max_pairs(_shape(k=8), _pl(4)) == 8 * 4096 * 4
+    ws = moe.moe_workspace_bytes(s, p)
+    # the GEMM1 output staging (max pairs x F bf16) dominates
+    assert ws >= 8 * 4096 * 8 * 2048 * 2
+    assert ws % 256 == 0
+    assert moe.moe_workspace_bytes(_shape(T=8192), p) > ws
+    assert moe.moe_workspace_bytes(_shape(k=0), p) == 0
+
+
+@pytest.mark.parametrize("kw,El,code", [
+    (dict(k=0), 32, -1),
+    (dict(k=17, E=256), 32, -1),
+    (dict(k=9, E=8), 8, -1),
+    (dict(E=2048), 32, -1),
+    (dict(R=65), 32, -1),
+    (dict(T=0), 32, -1),
+    (dict(), 0, -1),
+    (dict(), 300, -1),
+    (dict(dtype=7), 32, -1),
+    (dict(dtype=moe.MOE_MXFP8), 32, -6),
+    (dict(d=7160), 32, -2),                         # bf16 K step needs d % 64 == 0
+    (dict(F=2000), 32, -2),
+    (dict(d=130, dtype=moe.MOE_F32), 32, -2),       # fp32 row of 520 B is not 16-byte aligned
+])
+def test_bad_shapes_rejected_before_launch(kw, El, code):
+    s, p = _shape(**kw), _pl(El)
+    tab = (ctypes.c_void_p * 64)(*([FAKE] * 64))
+    rc = moe.lib().moe_layout(ctypes.byref(s), ctypes.byref(p), None, ctypes.cast(tab, ctypes.c_void_p),
+                              FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert rc == code
+
+
+def test_null_and_misaligned_pointers_rejected():
+    s, p = _shape(), _pl()
+    L = moe.lib()
+    tab = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    tabp = ctypes.cast(tab, ctypes.c_void_p)
+    big = 1 << 40
+    # null output
+    assert L.moe_layout(ctypes.byref(s), ctypes.byref(p), None, tabp, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, big, None) == -1
+    # null placement map
+    assert L.moe_layout(ctypes.byref(s), ctypes.byref(moe.Placement(None, 32)), None, tabp, FAKE, FAKE,
+                        FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    # null rank pointer
+    tab2 = (ctypes.c_void_p * 8)(*([FAKE] * 7 + [None]))
+    assert L.moe_layout(ctypes.byref(s), ctypes.byref(p), None, ctypes.cast(tab2, ctypes.c_void_p), FAKE,
+                        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    # misaligned rank pointer / workspace / row buffer
+    tab3 = (ctypes.c_void_p * 8)(*([FAKE] * 7 + [FAKE + 4]))
+    assert L.moe_dispatch_pull(ctypes.byref(s), ctypes.byref(p), ctypes.cast(tab3, ctypes.c_void_p), FAKE,
+                               FAKE, FAKE, FAKE, big, None) == -2
+    assert L.moe_layout(ctypes.byref(s), ctypes.byref(p), None, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE + 64, big, None) == -2
+    assert L.moe_dispatch_pull(ctypes.byref(s), ctypes.byref(p), tabp, FAKE, FAKE, FAKE + 8, FAKE, big,
+                               None) == -2
+    # workspace too small
+    assert L.moe_layout(ctypes.byref(s), ctypes.byref(p), None, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, 1024, None) == -3
+    assert L.moe_expert_ffn(ctypes.byref(s), ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, 1024, None) == -3
+    assert L.moe_combine_push(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, tabp, None,
+                              FAKE, big, None) == -1
+    # negative minibatch
+    ex = moe.Exec(-1, 0, 0, 0, 0)
+    assert L.moe_layout(ctypes.byref(s), ctypes.byref(p), ctypes.byref(ex), tabp, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, FAKE, FAKE, big, None) == -1
+    assert L.moe_read_status(None, None) == -1
+
+
+def test_forward_checks_every_stage_before_launching():
+    s, p = _shape(), _pl()
+    L = moe.lib()
+    tab = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    tabp = ctypes.cast(tab, ctypes.c_void_p)
+    # y table missing: must fail up front, not after launching the layout
+    rc = L.moe_forward(ctypes.byref(s), ctypes.byref(p), None, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE,
+                       tabp, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert rc == -1
