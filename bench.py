@@ -1,0 +1,183 @@
+"""Benchmark of one GPU's share of a MoE layer forward (HIP path on MI355X).
+
+One step = one whole forward over one batch of synthetic inputs already resident
+in HBM: top-k routing, sort-free layout, pull dispatch, grouped SwiGLU expert FFN,
+push combine and the final weighted merge.  Prints ONE JSON line on stdout.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config dsv3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from mixture_experts_layer_histogram_amd import configs, inputs  # noqa: E402
+
+METRIC = "MoE layer fwd tokens/s; grouped-GEMM % MFMA peak; gather/combine % HBM peak"
+PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
+PEAK_F32_FLOPS = 157.3e12    # MI355X fp32 matrix
+PEAK_HBM = 8.0e12            # MI355X HBM3E bytes/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_grouped_gemm_dsv3.json")
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_histogram_amd", "csrc", "gemm.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="dsv3", choices=sorted(configs.CONFIGS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-ranks", type=int, default=0, help="0 = all ranks (the whole step)")
+    return ap.parse_args()
+
+
+def gemm_source_sha() -> str:
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_bytes():
+    """HBM bytes per FFN launch pair from the committed rocprofv3 counter runs, or
+    None when the GEMM source has changed since they were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != gemm_source_sha():
+        return None
+    return rec.get("bytes_per_step")
+
+
+def cpu_baseline(cfg, inp, ranks):
+    """The oracle as it stands, on a bounded sample: the first `ranks` source ranks of
+    the same inputs (all of them by default, i.e. the whole step) through the share."""
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    ranks = max(1, min(ranks, cfg.R))
+    t0 = time.perf_counter()
+    O.forward(inp.logits[:ranks], inp.x_f32[:ranks], inp.w1_f32, inp.w3_f32, inp.w2_f32,
+              inp.expert_to_local, cfg.E_local, cfg.k, cfg.minibatch)
+    dt = time.perf_counter() - t0
+    tokens = ranks * cfg.T / cfg.G
+    frac = "the whole step" if ranks == cfg.R else f"{ranks}/{cfg.R} of the step"
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"source ranks 0..{ranks - 1} of the same inputs ({frac}); fp64 NumPy oracle "
+                      f"(route, layout, pull, SwiGLU experts, push, merge); {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the multi-GPU expert-parallel path is not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mixture_experts_layer_histogram_amd.device import DeviceProblem
+
+    cfg = configs.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating inputs for {cfg.name}")
+    t0 = time.time()
+    inp = inputs.make_inputs(cfg, seed=args.seed)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s; uploading")
+    P = DeviceProblem(cfg, inp, device=dev)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        P.forward()
+    torch.cuda.synchronize()
+    st = P.status()
+    if st != 0:
+        raise SystemExit(f"device status {st} after warmup")
+    N = P.N()
+    log(f"[bench] warmup done, N={N} local pairs")
+
+    names = ["layout", "dispatch", "ffn", "combine"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        P.layout()
+        e[1].record(stream)
+        P.dispatch()
+        e[2].record(stream)
+        P.ffn()
+        e[3].record(stream)
+        P.combine()
+        e[4].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    stage_ms = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+                for j, n in enumerate(names)}
+    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; stages {stage_ms}")
+
+    esz = 4 if cfg.dtype == "f32" else 2
+    row = cfg.d * esz
+    flops = 6.0 * cfg.d * cfg.F * N
+    peak = PEAK_F32_FLOPS if cfg.dtype == "f32" else PEAK_BF16_FLOPS
+    t_ffn = stage_ms["ffn"] * 1e-3
+    gather_bytes = 2.0 * N * row + N * 8
+    push_bytes = 2.0 * N * row
+    merge_bytes = 1.0 * N * row + cfg.R * cfg.T * row
+    tokens = cfg.R * cfg.T / cfg.G
+    value = tokens / (ms_step * 1e-3)
+    traffic = traffic_bytes()
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype != "f32" else "f32",
+        "data": "synthetic (seeded N(0,1) tokens, fan-in scaled random expert weights, router logits x@W_r)",
+        "config": {"workload": cfg.name, "R": cfg.R, "T": cfg.T, "d": cfg.d, "E": cfg.E,
+                   "E_local": cfg.E_local, "k": cfg.k, "F": cfg.F, "local_pairs": N,
+                   "path": "unfused (layout, dispatch, ffn, combine+merge kernels on one stream)"},
+        "roofline": {"bound": "mfma", "kernel": "grouped SwiGLU FFN (gate/up+SwiGLU, down GEMMs)",
+                     "achieved": flops / t_ffn / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
+                     "frac": flops / t_ffn / peak, "traffic": traffic},
+        "stages_ms": stage_ms,
+        "stages_hbm_frac": {
+            "dispatch": gather_bytes / (stage_ms["dispatch"] * 1e-3) / PEAK_HBM,
+            "combine+merge": (push_bytes + merge_bytes) / (stage_ms["combine"] * 1e-3) / PEAK_HBM,
+        },
+        "pairs_per_s": N / (ms_step * 1e-3),
+        "source_tokens_per_s": cfg.R * cfg.T / (ms_step * 1e-3),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_ranks or cfg.R)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

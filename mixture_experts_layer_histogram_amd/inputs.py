@@ -60,9 +60,9 @@ class MoEInputs:
     cfg: object
     logits: np.ndarray                 # [R][T][E] float32
     x_f32: np.ndarray                  # [R][T][d] float32 (exact values of x)
-    w1_f32: np.ndarray                 # [E_l][F][d]
-    w3_f32: np.ndarray                 # [E_l][F][d]
-    w2_f32: np.ndarray                 # [E_l][d][F]
+    w1_f32: object                     # [E_l][F][d]; indexable per expert (see Widened)
+    w3_f32: object                     # [E_l][F][d]
+    w2_f32: object                     # [E_l][d][F]
     expert_to_local: np.ndarray        # [E] int32, -1 = not on this GPU
     x_store: np.ndarray = field(repr=False, default=None)   # storage payload of x
     w1_store: np.ndarray = field(repr=False, default=None)
@@ -74,23 +74,45 @@ def _rng(seed: int, tag: int, i: int = 0) -> np.random.Generator:
     return np.random.default_rng([int(seed), int(tag), int(i)])
 
 
-def _normal_store(seed, tag, i, shape, std, dtype):
-    """One N(0, std^2) tensor in the storage type; returns (store, f32 values)."""
-    a = _rng(seed, tag, i).standard_normal(int(np.prod(shape)), dtype=np.float32)
+def _normal_into(out: np.ndarray, seed, tag, i, std, dtype):
+    """Fill ``out`` (storage type) with one N(0, std^2) tensor."""
+    a = _rng(seed, tag, i).standard_normal(out.size, dtype=np.float32)
     a *= np.float32(std)
-    a = a.reshape(shape)
     if dtype == "f32":
-        return a, a
-    bits = f32_to_bf16_bits(a)
-    return bits, bf16_bits_to_f32(bits)
+        out.reshape(-1)[:] = a
+    else:
+        out.reshape(-1)[:] = f32_to_bf16_bits(a)
 
 
-def _stack_experts(seed, tag, n, shape, std, dtype, threads):
+def _normal_stack(seed, tag, n, shape, std, dtype, threads):
+    """n independent tensors of ``shape`` (stream i = tensor i), filled in parallel."""
+    out = np.empty((n, *shape), dtype=np.float32 if dtype == "f32" else np.uint16)
     with ThreadPoolExecutor(max(1, threads)) as ex:
-        parts = list(ex.map(lambda i: _normal_store(seed, tag, i, shape, std, dtype), range(n)))
-    store = np.stack([p[0] for p in parts])
-    vals = store if dtype == "f32" else None
-    return store, vals, parts
+        list(ex.map(lambda i: _normal_into(out[i], seed, tag, i, std, dtype), range(n)))
+    return out
+
+
+class Widened:
+    """Per-index exact float32 view of a bf16-bit tensor (widened on access)."""
+
+    def __init__(self, bits: np.ndarray):
+        self.bits = bits
+        self.shape = bits.shape
+        self.dtype = np.float32
+
+    def __len__(self):
+        return self.shape[0]
+
+    def __getitem__(self, i):
+        return bf16_bits_to_f32(self.bits[i])
+
+    def __array__(self, dtype=None, copy=None):
+        a = bf16_bits_to_f32(self.bits)
+        return a if dtype is None else a.astype(dtype)
+
+
+def _values(store: np.ndarray, dtype: str):
+    return store if dtype == "f32" else Widened(store)
 
 
 def make_inputs(cfg, seed: int = 0, want_f32_weights: bool = True,
@@ -105,9 +127,8 @@ def make_inputs(cfg, seed: int = 0, want_f32_weights: bool = True,
     e2l[local_ids] = np.arange(El, dtype=np.int32)
 
     # token rows, one buffer per source rank
-    x_parts = [_normal_store(seed, TAG_X, r, (T, d), 1.0, st) for r in range(R)]
-    x_store = np.stack([p[0] for p in x_parts])
-    x_f32 = np.stack([p[1] for p in x_parts])
+    x_store = _normal_stack(seed, TAG_X, R, (T, d), 1.0, st, threads)
+    x_f32 = x_store if st == "f32" else bf16_bits_to_f32(x_store)
 
     if cfg.load == "skew":
         logits = skewed_logits(cfg, seed, e2l)
@@ -117,16 +138,13 @@ def make_inputs(cfg, seed: int = 0, want_f32_weights: bool = True,
         for r in range(R):
             logits[r] = (x_f32[r].astype(np.float64) @ wr).astype(np.float32)
 
-    w1_store, _, p1 = _stack_experts(seed, TAG_W1, El, (F, d), 1.0 / np.sqrt(d), st, threads)
-    w3_store, _, p3 = _stack_experts(seed, TAG_W3, El, (F, d), 1.0 / np.sqrt(d), st, threads)
-    w2_store, _, p2 = _stack_experts(seed, TAG_W2, El, (d, F), 1.0 / np.sqrt(F), st, threads)
+    w1_store = _normal_stack(seed, TAG_W1, El, (F, d), 1.0 / np.sqrt(d), st, threads)
+    w3_store = _normal_stack(seed, TAG_W3, El, (F, d), 1.0 / np.sqrt(d), st, threads)
+    w2_store = _normal_stack(seed, TAG_W2, El, (d, F), 1.0 / np.sqrt(F), st, threads)
     if want_f32_weights:
-        w1_f32 = np.stack([p[1] for p in p1])
-        w3_f32 = np.stack([p[1] for p in p3])
-        w2_f32 = np.stack([p[1] for p in p2])
+        w1_f32, w3_f32, w2_f32 = (_values(w, st) for w in (w1_store, w3_store, w2_store))
     else:
         w1_f32 = w3_f32 = w2_f32 = None
-    del p1, p3, p2
 
     return MoEInputs(cfg=cfg, logits=logits, x_f32=x_f32, w1_f32=w1_f32, w3_f32=w3_f32,
                      w2_f32=w2_f32, expert_to_local=e2l, x_store=x_store,
