@@ -78,11 +78,13 @@ typedef struct {
 
 /* Execution knobs.  Zero selects the default of each field. */
 typedef struct {
-  int32_t minibatch_rows;   /* rows of one expert released to compute at once (default 128) */
+  int32_t minibatch_rows;   /* rows of one expert released to compute at once (default 128;
+                               the persistent path takes 64, 128 or 256) */
   int32_t comm_cus;         /* persistent path: workgroups doing data movement (default 32) */
-  int32_t ring_slots;       /* persistent path: ring slots (default: as many as ring_bytes holds) */
-  int32_t trace;            /* reserved */
-  uint64_t watchdog_cycles; /* persistent path: spin budget of every device wait (default ~2 s) */
+  int32_t ring_slots;       /* persistent path: cap on ring slots (default: as many as ring_bytes holds) */
+  int32_t trace;            /* reserved, must be 0 */
+  uint64_t watchdog_us;     /* persistent path: wall-clock budget of every device wait in
+                               microseconds (default 2,000,000) */
 } moe_exec_t;
 
 /* Limits checked by every call: 1 <= k <= 16, k <= E <= 1024, 1 <= E_local <= E. */
@@ -171,6 +173,45 @@ int moe_forward(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t
                 const void* w2, void* xe, void* ye, void* const* recv, void* const* y,
                 int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
                 int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_forward_persistent -- the whole share with dispatch, expert FFN and combine in one
+ * persistent kernel [kucoin §02: one megakernel; the SMs are split into a communication
+ * part (dispatch, combine, state) and a compute part (expert FFN) that notify each other
+ * through GPU-local counters; tokens reach the experts a minibatch at a time through a
+ * fixed-size ring buffer whose slots are reused right after combine, so the combine of one
+ * macrobatch overlaps the dispatch of the next; qubstore, ring buffer and megakernel
+ * paragraphs: no CPU in the loop, no worst-case buffers].
+ * Same inputs and outputs as moe_forward (bf16 only), plus:
+ *   ring, ring_bytes: caller-owned device buffer, 256-byte aligned, of at least
+ *     256 / minibatch_rows slots of moe_ring_slot_bytes() each.  A slot holds one
+ *     minibatch of token rows (overwritten in place by their expert outputs) and their h
+ *     rows.  Fewer slots mean more back-pressure, never a different result.
+ *   ws: at least moe_persistent_workspace_bytes() bytes (no worst-case staging).
+ * Launch sequence on `stream`: the layout kernels, one cooperative persistent kernel
+ * (grid = one workgroup per CU), the weighted merge.  The CUs split into ex->comm_cus
+ * data-movement workgroups and the rest for the expert GEMMs; with eight XCDs and enough
+ * ring slots there is one pipeline per XCD so every hand-off stays inside one L2.  Every
+ * device wait is bounded by ex->watchdog_us; on expiry the kernel exits and
+ * moe_read_status() returns MOE_ETIMEOUT.  Bit-identical to moe_forward's outputs for the
+ * same inputs (same tile arithmetic, same merge order).
+ * Status: currently switched off -- after its argument checks it returns MOE_EUNSUP and
+ * launches nothing (its first GPU run did not complete; the cause is under study).
+ * Errors: MOE_EUNSUP for a non-bf16 dtype or minibatch_rows not in {64, 128, 256};
+ * MOE_ENOSPC for a ring below one 256-row tile or a small workspace; MOE_EINVAL when
+ * comm_cus leaves no CU for compute.
+ */
+int moe_forward_persistent(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+                           const float* const* logits, const void* const* x, const void* w1, const void* w3,
+                           const void* w2, void* ring, size_t ring_bytes, void* const* recv, void* const* y,
+                           int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                           int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of one ring slot of moe_forward_persistent (0 if unsupported). */
+size_t moe_ring_slot_bytes(const moe_shape_t* s, const moe_exec_t* ex);
+
+/* Workspace bytes moe_forward_persistent needs (smaller than moe_workspace_bytes). */
+size_t moe_persistent_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex);
 
 /* Syncs `stream` and returns the device status word (0, MOE_EINVAL or MOE_ETIMEOUT). */
 int moe_read_status(const void* ws, void* stream);

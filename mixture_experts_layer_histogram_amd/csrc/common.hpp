@@ -29,8 +29,10 @@ enum CtrlSlot {
   kCtrlWords = 64
 };
 
+constexpr int kMaxRingSlots = 65536;
+
 struct WsLayout {
-  size_t ctrl, l2g, mtile_base, chunk_base, blockhist, blockbase, hbuf, total;
+  size_t ctrl, l2g, mtile_base, chunk_base, blockhist, blockbase, pctrl, hbuf, total;
   int32_t nb;        // layout blocks
   int64_t max_pairs;
   int32_t max_mtiles;
@@ -53,6 +55,8 @@ inline WsLayout ws_layout(const moe_shape_t& s, int32_t E_local) {
   w.chunk_base = o;  o = align256(o + size_t(E_local + 1) * 4);
   w.blockhist = o;   o = align256(o + size_t(w.nb) * s.E * 4);
   w.blockbase = o;   o = align256(o + size_t(w.nb) * E_local * 4);
+  // persistent-path control block: 128 words + 6 per row tile + one per ring slot
+  w.pctrl = o;       o = align256(o + (size_t(128) + size_t(w.max_mtiles) * 6 + kMaxRingSlots) * 4);
   w.hbuf = o;        o = align256(o + size_t(w.max_pairs) * s.F * esz);
   w.total = o;
   return w;

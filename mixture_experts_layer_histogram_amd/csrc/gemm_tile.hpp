@@ -1,0 +1,188 @@
+// One 256-row x 256-column tile of the grouped SwiGLU FFN on gfx950 (bf16 MFMA).
+// Shared by the standalone grouped GEMM kernels and the persistent forward kernel.
+//
+// GEMM1 (MODE 0): h = silu(X W1^T) * (X W3^T); GEMM2 (MODE 1): y = h W2^T.  Every
+// operand is K-contiguous (row-major X and h, weights stored [out][in]), so each MFMA
+// lane's 8 consecutive K values are one 16-byte LDS read.
+//
+// 8 waves (two per SIMD) as 4 (rows) x 2 (cols); each wave owns a 64 x 128 block = 2 x 4
+// tiles of v_mfma_f32_32x32x16_bf16.  K is staged 64 at a time through two LDS buffers
+// (2 x 64 KiB) filled by direct global->LDS loads (global_load_lds_dwordx4, no VGPR
+// staging).  GEMM1's B tile interleaves 32-row blocks of W1 and W3 for the same f values,
+// so a lane holds the gate and the up accumulator of one (row, f) and applies SwiGLU in
+// registers.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kStageBytes = (kGemmBM + kGemmBN) * kGemmBK * 2;   // 64 KiB
+constexpr int kGemmLds = 2 * kStageBytes;                          // 128 KiB
+constexpr int kGemmThreads = 512;                                  // 8 waves, 2 per SIMD
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// LDS byte offset of 16-byte chunk `chunk` of tile row `row` (128-byte rows).  The chunk
+// index is XORed with bits 1..3 of the row so that the 16 lanes one ds_read_b128 serves
+// per cycle (rows r..r+15 of one chunk column) hit 16 distinct bank groups of the 64-bank
+// LDS (row parity picks the half, (row >> 1) & 7 the chunk).
+__device__ __forceinline__ int swz_off(int row, int chunk) {
+  return row * (kGemmBK * 2) + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+// Where the tile's rows live: up to 4 blocks of (1 << blk_log2) consecutive rows each
+// (one block = one ring slot in the persistent kernel; blocks of 128 rows back to back in
+// the standalone GEMM).  Rows >= rows are not stored; their loads re-read row rows-1.
+struct TileIO {
+  const uint16_t* a0;
+  const uint16_t* a1;
+  const uint16_t* a2;
+  const uint16_t* a3;
+  uint16_t* o0;
+  uint16_t* o1;
+  uint16_t* o2;
+  uint16_t* o3;
+  int a_ld, o_ld;      // row strides in elements
+  int blk_log2;        // 6, 7 or 8
+  int rows;            // valid rows, 1..256
+};
+
+template <typename P>
+__device__ __forceinline__ P pick4(int i, P p0, P p1, P p2, P p3) {
+  return i == 0 ? p0 : (i == 1 ? p1 : (i == 2 ? p2 : p3));
+}
+
+// b0/b1: this expert's weight matrices ([Nout][K]); c0: first output column of the tile.
+template <int MODE>
+__device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __restrict__ b0,
+                                          const uint16_t* __restrict__ b1, int c0, int Nout, int K,
+                                          char* smem) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r32 = lane & 31, hi = lane >> 5;
+  // LDS fill geometry: lane -> row lrow of an 8-row group, LDS chunk position lpos, which
+  // holds logical chunk lpos ^ (((g & 1) * 4 + (lrow >> 1)) & 7) for group g
+  const int lrow = lane >> 3, lpos = lane & 7;
+  const int lch_even = lpos ^ (lrow >> 1);
+  const int lch_odd = lpos ^ (4 + (lrow >> 1));
+  const int nk = K / kGemmBK;
+  const int rows = io.rows;
+  const int bmask = (1 << io.blk_log2) - 1;
+
+  // this wave fills row groups g = wave*4 + i (rows g*8 + lrow) of the A and B tiles
+  const uint16_t* ap[4];
+  const uint16_t* bp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wave * 4 + i) * 8 + lrow;
+    const int lch = (i & 1) ? lch_odd : lch_even;
+    const int rr = min(row, rows - 1);
+    ap[i] = pick4(rr >> io.blk_log2, io.a0, io.a1, io.a2, io.a3) + size_t(rr & bmask) * io.a_ld + lch * 8;
+    if (MODE == 0) {
+      // 32-row blocks alternate W1 / W3 rows of the same 32 f values
+      const int n = min(c0 + (row >> 6) * 32 + (row & 31), Nout - 1);
+      bp[i] = (((row >> 5) & 1) ? b1 : b0) + size_t(n) * K + lch * 8;
+    } else {
+      const int n = min(c0 + row, Nout - 1);
+      bp[i] = b0 + size_t(n) * K + lch * 8;
+    }
+  }
+  auto issue = [&](int ks) {
+    char* sa = smem + (ks & 1) * kStageBytes;
+    char* sb = sa + kGemmBM * kGemmBK * 2;
+    const int koff = ks * kGemmBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = wave * 4 + i;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(ap[i] + koff), (lds_void_ptr)(sa + g * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bp[i] + koff), (lds_void_ptr)(sb + g * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
+
+  issue(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int ks = 0; ks < nk; ++ks) {
+    if (ks + 1 < nk) issue(ks + 1);     // other stage: everyone finished reading it
+    const char* sa = smem + (ks & 1) * kStageBytes;
+    const char* sb = sa + kGemmBM * kGemmBK * 2;
+    bf16x8 fa[2][2], fb[2][4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) fa[0][m] = *reinterpret_cast<const bf16x8*>(sa + swz_off(wm * 64 + m * 32 + r32, hi));
+#pragma unroll
+    for (int n = 0; n < 4; ++n) fb[0][n] = *reinterpret_cast<const bf16x8*>(sb + swz_off(wn * 128 + n * 32 + r32, hi));
+#pragma unroll
+    for (int sub = 0; sub < kGemmBK / 16; ++sub) {
+      const int cur = sub & 1;
+      if (sub + 1 < kGemmBK / 16) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          fa[cur ^ 1][m] = *reinterpret_cast<const bf16x8*>(sa + swz_off(wm * 64 + m * 32 + r32, (sub + 1) * 2 + hi));
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          fb[cur ^ 1][n] = *reinterpret_cast<const bf16x8*>(sb + swz_off(wn * 128 + n * 32 + r32, (sub + 1) * 2 + hi));
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][m], fb[cur][n], acc[m][n], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);      // this wave's fills of the next stage landed
+    __syncthreads();                    // ... and everyone's
+  }
+
+  // epilogue: lane holds column r32 and rows 8*(e/4) + 4*hi + e%4 of each 32x32 block
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int rb = wm * 64 + m * 32;                     // 32-row block, inside one row block
+    uint16_t* orow = pick4(rb >> io.blk_log2, io.o0, io.o1, io.o2, io.o3) + size_t(rb & bmask) * io.o_ld;
+    if (MODE == 0) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int f = c0 + (wn * 2 + q) * 32 + r32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = 8 * (e >> 2) + 4 * hi + (e & 3);
+          if (rb + row < rows && f < Nout) {
+            const float h = silu_f32(acc[m][2 * q][e]) * acc[m][2 * q + 1][e];
+            orow[size_t(row) * io.o_ld + f] = f32_to_bf16(h);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int col = c0 + wn * 128 + n * 32 + r32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = 8 * (e >> 2) + 4 * hi + (e & 3);
+          if (rb + row < rows && col < Nout) orow[size_t(row) * io.o_ld + col] = f32_to_bf16(acc[m][n][e]);
+        }
+      }
+    }
+  }
+}
+
+// which local expert owns global row tile mt (binary search on the tile prefix)
+__device__ __forceinline__ int find_expert(const int32_t* __restrict__ mtile_base, int El, int mt) {
+  int lo = 0, hi = El - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (mtile_base[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace moe

@@ -152,28 +152,39 @@ hipError_t launch_dispatch(const moe_shape_t& s, const void* const* x, const int
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const moe_shape_t& s, const char* ye, const int32_t* pull_src,
-                          const int32_t* slot_of, const float* topk_w, void* const* recv, void* const* y,
-                          const int32_t* ctrl, int cus, hipStream_t st) {
+hipError_t launch_push(const moe_shape_t& s, const char* ye, const int32_t* pull_src, const int32_t* slot_of,
+                       void* const* recv, const int32_t* ctrl, int cus, hipStream_t st) {
   RankPtrs<char*> rp{};
+  for (int r = 0; r < s.R; ++r) rp.p[r] = static_cast<char*>(recv[r]);
+  const int row_bytes = s.d * (s.dtype == MOE_F32 ? 4 : 2);
+  hipLaunchKernelGGL(combine_push_kernel, dim3(mover_grid(cus)), dim3(256), 0, st, ye, pull_src, slot_of, ctrl, rp,
+                     s.T, s.k, row_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const moe_shape_t& s, const int32_t* slot_of, const float* topk_w, void* const* recv,
+                        void* const* y, int cus, hipStream_t st) {
   RankPtrs<const char*> rcp{};
   RankPtrs<char*> yp{};
   for (int r = 0; r < s.R; ++r) {
-    rp.p[r] = static_cast<char*>(recv[r]);
     rcp.p[r] = static_cast<const char*>(recv[r]);
     yp.p[r] = static_cast<char*>(y[r]);
   }
-  const bool bf = s.dtype != MOE_F32;
-  const int row_bytes = s.d * (bf ? 2 : 4);
-  hipLaunchKernelGGL(combine_push_kernel, dim3(mover_grid(cus)), dim3(256), 0, st, ye, pull_src, slot_of,
-                     ctrl, rp, s.T, s.k, row_bytes);
-  if (bf)
-    hipLaunchKernelGGL(weighted_merge_kernel<true>, dim3(mover_grid(cus)), dim3(256), 0, st, rcp, yp,
-                       slot_of, topk_w, s.R, s.T, s.k, s.d);
+  if (s.dtype != MOE_F32)
+    hipLaunchKernelGGL(weighted_merge_kernel<true>, dim3(mover_grid(cus)), dim3(256), 0, st, rcp, yp, slot_of, topk_w,
+                       s.R, s.T, s.k, s.d);
   else
-    hipLaunchKernelGGL(weighted_merge_kernel<false>, dim3(mover_grid(cus)), dim3(256), 0, st, rcp, yp,
-                       slot_of, topk_w, s.R, s.T, s.k, s.d);
+    hipLaunchKernelGGL(weighted_merge_kernel<false>, dim3(mover_grid(cus)), dim3(256), 0, st, rcp, yp, slot_of, topk_w,
+                       s.R, s.T, s.k, s.d);
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const moe_shape_t& s, const char* ye, const int32_t* pull_src,
+                          const int32_t* slot_of, const float* topk_w, void* const* recv, void* const* y,
+                          const int32_t* ctrl, int cus, hipStream_t st) {
+  const hipError_t e = launch_push(s, ye, pull_src, slot_of, recv, ctrl, cus, st);
+  if (e != hipSuccess) return e;
+  return launch_merge(s, slot_of, topk_w, recv, y, cus, st);
 }
 
 }  // namespace moe

@@ -81,6 +81,22 @@ class DeviceProblem:
                         self.xe, self.ye, self.recv, self.y, self.topk_idx, self.topk_w, self.counts,
                         self.offsets, self.pull_src, self.slot_of, self.ws, stream=stream)
 
+    def alloc_ring(self, ring_mib=None, ex=None):
+        """Ring buffer for the persistent path (ring_mib MiB, default the config's)."""
+        torch = self.torch
+        mib = self.cfg.ring_mib if ring_mib is None else ring_mib
+        self.ring = torch.empty(int(mib * (1 << 20)), dtype=torch.uint8, device=self.device)
+        self.pex = ex if ex is not None else self.ex
+        return self.ring
+
+    def forward_persistent(self, ex=None, stream=None, check=True):
+        if not hasattr(self, "ring"):
+            self.alloc_ring()
+        return moe.moe_forward_persistent(self.shape, self.placement, ex if ex is not None else self.pex,
+                                          self.logits, self.x, self.w1, self.w3, self.w2, self.ring, self.recv,
+                                          self.y, self.topk_idx, self.topk_w, self.counts, self.offsets,
+                                          self.pull_src, self.slot_of, self.ws, stream=stream, check=check)
+
     def status(self, stream=None) -> int:
         return moe.moe_read_status(self.ws, stream)
 

@@ -22,7 +22,8 @@ ERRORS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_ENOSPC", -4:
 
 # every symbol include/moe.h declares
 EXPORTS = ["moe_max_pairs", "moe_workspace_bytes", "moe_layout", "moe_dispatch_pull",
-           "moe_expert_ffn", "moe_combine_push", "moe_forward", "moe_read_status",
+           "moe_expert_ffn", "moe_combine_push", "moe_forward", "moe_forward_persistent",
+           "moe_ring_slot_bytes", "moe_persistent_workspace_bytes", "moe_read_status",
            "moe_strerror", "moe_version"]
 
 
@@ -45,7 +46,7 @@ class Placement(ctypes.Structure):
 class Exec(ctypes.Structure):
     _fields_ = [("minibatch_rows", ctypes.c_int32), ("comm_cus", ctypes.c_int32),
                 ("ring_slots", ctypes.c_int32), ("trace", ctypes.c_int32),
-                ("watchdog_cycles", ctypes.c_uint64)]
+                ("watchdog_us", ctypes.c_uint64)]
 
 
 _lib = None
@@ -70,12 +71,18 @@ def lib() -> ctypes.CDLL:
         L.moe_combine_push.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_forward.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, VP, VP, VP,
                                   VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_forward_persistent.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, SZ, VP, VP,
+                                             VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_ring_slot_bytes.argtypes = [S, EX]
+        L.moe_ring_slot_bytes.restype = SZ
+        L.moe_persistent_workspace_bytes.argtypes = [S, PL, EX]
+        L.moe_persistent_workspace_bytes.restype = SZ
         L.moe_read_status.argtypes = [VP, VP]
         L.moe_strerror.argtypes = [I32]
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_version.restype = ctypes.c_char_p
         for f in ("moe_layout", "moe_dispatch_pull", "moe_expert_ffn", "moe_combine_push",
-                  "moe_forward", "moe_read_status"):
+                  "moe_forward", "moe_forward_persistent", "moe_read_status"):
             getattr(L, f).restype = I32
         _lib = L
     return _lib
@@ -173,6 +180,28 @@ def moe_forward(shape, placement, ex, logits, x, w1, w3, w2, xe, ye, recv, y, to
                            _p(topk_w), _p(counts), _p(offsets), _p(pull_src), _p(slot_of), _p(ws),
                            ws.numel() if ws_bytes is None else ws_bytes, _stream(stream))
     return _check(rc, "moe_forward") if check else rc
+
+
+def moe_forward_persistent(shape, placement, ex, logits, x, w1, w3, w2, ring, recv, y, topk_idx, topk_w,
+                           counts, offsets, pull_src, slot_of, ws, ring_bytes=None, ws_bytes=None, stream=None,
+                           check=True):
+    rc = lib().moe_forward_persistent(ctypes.byref(shape), ctypes.byref(placement),
+                                      ctypes.byref(ex) if ex is not None else None, _table(logits), _table(x),
+                                      _p(w1), _p(w3), _p(w2), _p(ring),
+                                      ring.numel() if ring_bytes is None else ring_bytes, _table(recv),
+                                      _table(y), _p(topk_idx), _p(topk_w), _p(counts), _p(offsets),
+                                      _p(pull_src), _p(slot_of), _p(ws),
+                                      ws.numel() if ws_bytes is None else ws_bytes, _stream(stream))
+    return _check(rc, "moe_forward_persistent") if check else rc
+
+
+def moe_ring_slot_bytes(shape: Shape, ex: Exec | None = None) -> int:
+    return int(lib().moe_ring_slot_bytes(ctypes.byref(shape), ctypes.byref(ex) if ex is not None else None))
+
+
+def moe_persistent_workspace_bytes(shape: Shape, placement: Placement, ex: Exec | None = None) -> int:
+    return int(lib().moe_persistent_workspace_bytes(ctypes.byref(shape), ctypes.byref(placement),
+                                                    ctypes.byref(ex) if ex is not None else None))
 
 
 def moe_read_status(ws, stream=None) -> int:

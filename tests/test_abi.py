@@ -128,3 +128,37 @@ def test_forward_checks_every_stage_before_launching():
     rc = L.moe_forward(ctypes.byref(s), ctypes.byref(p), None, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE,
                        tabp, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
     assert rc == -1
+
+
+def test_persistent_entry_rejects_bad_arguments_before_launch():
+    L = moe.lib()
+    s, p = _shape(), _pl()
+    tab = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    tabp = ctypes.cast(tab, ctypes.c_void_p)
+    big = 1 << 40
+    slot = moe.moe_ring_slot_bytes(s, moe.Exec(128, 0, 0, 0, 0))
+    assert slot == 128 * (7168 + 2048) * 2
+    assert moe.moe_ring_slot_bytes(s, moe.Exec(96, 0, 0, 0, 0)) == 0
+    assert 0 < moe.moe_persistent_workspace_bytes(s, p) < moe.moe_workspace_bytes(s, p)
+
+    def call(shape=s, ex=None, ring_bytes=big, ring=FAKE, ws_bytes=big):
+        return L.moe_forward_persistent(ctypes.byref(shape), ctypes.byref(p), ctypes.byref(ex) if ex else None,
+                                        tabp, tabp, FAKE, FAKE, FAKE, ring, ring_bytes, tabp, tabp, FAKE, FAKE,
+                                        FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+    assert call(shape=_shape(dtype=moe.MOE_F32)) == -6                 # bf16 only
+    assert call(ex=moe.Exec(96, 0, 0, 0, 0)) == -6                      # chunk must divide 256
+    assert call(ring_bytes=slot) == -3                                  # below one 256-row tile
+    assert call(ring=FAKE + 16) == -2                                   # ring alignment
+    assert call(ws_bytes=1024) == -3
+    assert call(ring=None) == -1
+
+
+def test_persistent_entry_is_switched_off():
+    """The persistent path returns MOE_EUNSUP after its checks and launches nothing."""
+    L = moe.lib()
+    s, p = _shape(), _pl()
+    tab = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    tabp = ctypes.cast(tab, ctypes.c_void_p)
+    rc = L.moe_forward_persistent(ctypes.byref(s), ctypes.byref(p), None, tabp, tabp, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 40, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert rc == -6
