@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-ranks", type=int, default=0, help="0 = all ranks (the whole step)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run three plain 1 GiB device copies (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) "
+                         "into the committed traffic record, then exit")
     return ap.parse_args()
 
 
@@ -60,6 +65,40 @@ def traffic_bytes():
     if rec.get("source_sha") != gemm_source_sha():
         return None
     return rec.get("bytes_per_step")
+
+
+CAL_BYTES = 1 << 30
+
+
+def _per_dispatch(csv_path, counter):
+    import csv
+    out = []
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter:
+            out.append((r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0))
+    return out
+
+
+def write_traffic(fetch_csv, write_csv):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the two FFN GEMM kernels, each scaled
+    by (known bytes / counter) of a plain 1 GiB device copy in the same run."""
+    rec = {"source_sha": gemm_source_sha()}
+    for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rows = _per_dispatch(path, counter)
+        cal = [v for k, v in rows if "copyBuffer" in k and 0.5 * CAL_BYTES < v < 2.0 * CAL_BYTES]
+        if not cal:
+            raise SystemExit(f"no 1 GiB copy dispatch found in {path}")
+        factor = CAL_BYTES / float(np.median(cal))
+        g = {}
+        for mode in (0, 1):
+            vals = [v for k, v in rows if f"grouped_gemm_bf16_kernel<{mode}>" in k]
+            g[mode] = float(np.median(vals)) * factor
+        rec[name] = {"copy_factor": factor, "gemm1_bytes": g[0], "gemm2_bytes": g[1]}
+    rec["bytes_per_step"] = (rec["fetch"]["gemm1_bytes"] + rec["fetch"]["gemm2_bytes"] +
+                             rec["write"]["gemm1_bytes"] + rec["write"]["gemm2_bytes"])
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(rec))
 
 
 def cpu_baseline(cfg, inp, ranks):
@@ -85,6 +124,9 @@ def cpu_baseline(cfg, inp, ranks):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(the multi-GPU expert-parallel path is not built)", file=sys.stderr)
@@ -134,6 +176,13 @@ def main():
     stage_ms = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j, n in enumerate(names)}
     log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; stages {stage_ms}")
+    if args.copy_calibration:
+        src = torch.empty(CAL_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     esz = 4 if cfg.dtype == "f32" else 2
     row = cfg.d * esz
