@@ -13,19 +13,22 @@
 
 namespace moe {
 
-constexpr int kMoveUnroll = 8;   // 16-byte vectors in flight per lane
-
+// UNROLL = 16-byte vectors in flight per lane (16: a 16 KiB row in one round trip).
+// Measured on MI355X at the DeepSeek-V3 share: the gather (random source rows, sequential
+// destination) is fastest with 16 in flight and 4 resident blocks per CU; the push
+// (sequential source, scattered destination) with 8 in flight and 8 blocks per CU.
+template <int UNROLL>
 __device__ __forceinline__ void copy_row(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int n16,
                                          int lane) {
-  for (int base = 0; base < n16; base += 64 * kMoveUnroll) {
-    u32x4 v[kMoveUnroll];
+  for (int base = 0; base < n16; base += 64 * UNROLL) {
+    u32x4 v[UNROLL];
 #pragma unroll
-    for (int u = 0; u < kMoveUnroll; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const int i = base + u * 64 + lane;
       if (i < n16) v[u] = __builtin_nontemporal_load(src + i);
     }
 #pragma unroll
-    for (int u = 0; u < kMoveUnroll; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const int i = base + u * 64 + lane;
       if (i < n16) dst[i] = v[u];
     }
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(256) void dispatch_pull_kernel(RankPtrs<const char*
   for (int s = blockIdx.x * 4 + (threadIdx.x >> 6); s < N; s += nw) {
     const int r = pull_src[2 * int64_t(s)];
     const int t = pull_src[2 * int64_t(s) + 1];
-    copy_row(reinterpret_cast<const u32x4*>(x.p[r] + int64_t(t) * row_bytes),
+    copy_row<16>(reinterpret_cast<const u32x4*>(x.p[r] + int64_t(t) * row_bytes),
              reinterpret_cast<u32x4*>(xe + int64_t(s) * row_bytes), n16, lane);
   }
 }
@@ -63,16 +66,19 @@ __global__ __launch_bounds__(256) void combine_push_kernel(const char* __restric
   for (int s = blockIdx.x * 4 + (threadIdx.x >> 6); s < N; s += nw) {
     const int r = pull_src[2 * int64_t(s)];
     const int t = pull_src[2 * int64_t(s) + 1];
+    // the pair's j: lanes 0..k-1 compare their slot_of entry at once (k <= 16)
     const int32_t* so = slot_of + (int64_t(r) * T + t) * k;
-    int j = 0;
-    for (int jj = 0; jj < k; ++jj)
-      if (so[jj] == s) j = jj;
-    copy_row(reinterpret_cast<const u32x4*>(ye + int64_t(s) * row_bytes),
+    const unsigned long long hit = __ballot(lane < k && so[lane < k ? lane : 0] == s);
+    const int j = hit ? __builtin_ctzll(hit) : 0;
+    copy_row<8>(reinterpret_cast<const u32x4*>(ye + int64_t(s) * row_bytes),
              reinterpret_cast<u32x4*>(recv.p[r] + (int64_t(t) * k + j) * row_bytes), n16, lane);
   }
 }
 
 // y[r][t] = sum over ascending j with a local expert of g[r][t][j] * recv[r][t][j]
+// A wave task is one column segment (64 * VPL 16-byte vectors) of one token row.  The
+// token's local j are compacted into a mask; for each local j all VPL loads of the
+// segment are issued before any is used, so a task costs one memory round trip per j.
 template <bool BF16>
 __global__ __launch_bounds__(256) void weighted_merge_kernel(RankPtrs<const char*> recv,
                                                              RankPtrs<char*> y,
@@ -80,74 +86,83 @@ __global__ __launch_bounds__(256) void weighted_merge_kernel(RankPtrs<const char
                                                              const float* __restrict__ topk_w, int R,
                                                              int T, int k, int d) {
   constexpr int EPV = BF16 ? 8 : 4;      // elements per 16-byte vector
-  constexpr int VPL = 4;                 // vectors per lane per column batch
+  constexpr int VPL = 8;                 // vectors per lane per segment
   const int lane = threadIdx.x & 63;
   const int row_bytes = d * (BF16 ? 2 : 4);
   const int n16 = row_bytes >> 4;
-  const int64_t RT = int64_t(R) * T;
+  const int nseg = (n16 + 64 * VPL - 1) / (64 * VPL);
+  const int64_t tasks = int64_t(R) * T * nseg;
   const int64_t nw = int64_t(gridDim.x) * 4;
-  for (int64_t g = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); g < RT; g += nw) {
+  for (int64_t task = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); task < tasks; task += nw) {
+    const int64_t g = task / nseg;
+    const int cb = int(task - g * nseg) * 64 * VPL;
     const int r = int(g / T);
     const int t = int(g - int64_t(r) * T);
     const int32_t* so = slot_of + g * k;
     const float* gw = topk_w + g * k;
+    // the token's local j (ascending) as a bit mask: lanes 0..k-1 test their entry at once
+    const unsigned long long lm = __ballot(lane < k && so[lane < k ? lane : 0] >= 0);
+    uint32_t local = uint32_t(lm);
     const char* rrow = recv.p[r] + int64_t(t) * k * row_bytes;
     u32x4* yrow = reinterpret_cast<u32x4*>(y.p[r] + int64_t(t) * row_bytes);
-    for (int cb = 0; cb < n16; cb += 64 * VPL) {
-      float acc[VPL][EPV];
+    float acc[VPL][EPV];
 #pragma unroll
-      for (int u = 0; u < VPL; ++u)
+    for (int u = 0; u < VPL; ++u)
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) acc[u][e] = 0.0f;
-      for (int j = 0; j < k; ++j) {
-        if (so[j] < 0) continue;
-        const float gj = gw[j];
-        const u32x4* src = reinterpret_cast<const u32x4*>(rrow + int64_t(j) * row_bytes);
+      for (int e = 0; e < EPV; ++e) acc[u][e] = 0.0f;
+    for (uint32_t m = local; m; m &= m - 1) {
+      const int j = __builtin_ctz(m);
+      const float gj = gw[j];
+      const u32x4* src = reinterpret_cast<const u32x4*>(rrow + int64_t(j) * row_bytes);
+      u32x4 v[VPL];
 #pragma unroll
-        for (int u = 0; u < VPL; ++u) {
-          const int i = cb + u * 64 + lane;
-          if (i < n16) {
-            const u32x4 v = __builtin_nontemporal_load(src + i);
-            if (BF16) {
-#pragma unroll
-              for (int w = 0; w < 4; ++w) {
-                acc[u][2 * w] = fmaf(gj, __uint_as_float(v[w] << 16), acc[u][2 * w]);
-                acc[u][2 * w + 1] = fmaf(gj, __uint_as_float(v[w] & 0xFFFF0000u), acc[u][2 * w + 1]);
-              }
-            } else {
-#pragma unroll
-              for (int w = 0; w < 4; ++w) acc[u][w] = fmaf(gj, __uint_as_float(v[w]), acc[u][w]);
-            }
-          }
-        }
+      for (int u = 0; u < VPL; ++u) {
+        const int i = cb + u * 64 + lane;
+        if (i < n16) v[u] = __builtin_nontemporal_load(src + i);
       }
 #pragma unroll
       for (int u = 0; u < VPL; ++u) {
         const int i = cb + u * 64 + lane;
         if (i < n16) {
-          u32x4 o;
           if (BF16) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(acc[u][2 * w], acc[u][2 * w + 1]);
+            for (int w = 0; w < 4; ++w) {
+              acc[u][2 * w] = fmaf(gj, __uint_as_float(v[u][w] << 16), acc[u][2 * w]);
+              acc[u][2 * w + 1] = fmaf(gj, __uint_as_float(v[u][w] & 0xFFFF0000u), acc[u][2 * w + 1]);
+            }
           } else {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) o[w] = __float_as_uint(acc[u][w]);
+            for (int w = 0; w < 4; ++w) acc[u][w] = fmaf(gj, __uint_as_float(v[u][w]), acc[u][w]);
           }
-          yrow[i] = o;
         }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) {
+      const int i = cb + u * 64 + lane;
+      if (i < n16) {
+        u32x4 o;
+        if (BF16) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(acc[u][2 * w], acc[u][2 * w + 1]);
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) o[w] = __float_as_uint(acc[u][w]);
+        }
+        __builtin_nontemporal_store(o, yrow + i);
       }
     }
   }
 }
 
-static int mover_grid(int cus) { return cus * 8; }
+constexpr int kGatherBlocksPerCU = 4, kPushBlocksPerCU = 8, kMergeBlocksPerCU = 4;
 
 hipError_t launch_dispatch(const moe_shape_t& s, const void* const* x, const int32_t* pull_src, char* xe,
                            const int32_t* ctrl, int cus, hipStream_t st) {
   RankPtrs<const char*> xp{};
   for (int r = 0; r < s.R; ++r) xp.p[r] = static_cast<const char*>(x[r]);
   const int row_bytes = s.d * (s.dtype == MOE_F32 ? 4 : 2);
-  hipLaunchKernelGGL(dispatch_pull_kernel, dim3(mover_grid(cus)), dim3(256), 0, st, xp, pull_src, ctrl, xe,
+  hipLaunchKernelGGL(dispatch_pull_kernel, dim3(cus * kGatherBlocksPerCU), dim3(256), 0, st, xp, pull_src, ctrl, xe,
                      row_bytes);
   return hipGetLastError();
 }
@@ -157,7 +172,7 @@ hipError_t launch_push(const moe_shape_t& s, const char* ye, const int32_t* pull
   RankPtrs<char*> rp{};
   for (int r = 0; r < s.R; ++r) rp.p[r] = static_cast<char*>(recv[r]);
   const int row_bytes = s.d * (s.dtype == MOE_F32 ? 4 : 2);
-  hipLaunchKernelGGL(combine_push_kernel, dim3(mover_grid(cus)), dim3(256), 0, st, ye, pull_src, slot_of, ctrl, rp,
+  hipLaunchKernelGGL(combine_push_kernel, dim3(cus * kPushBlocksPerCU), dim3(256), 0, st, ye, pull_src, slot_of, ctrl, rp,
                      s.T, s.k, row_bytes);
   return hipGetLastError();
 }
@@ -171,10 +186,10 @@ hipError_t launch_merge(const moe_shape_t& s, const int32_t* slot_of, const floa
     yp.p[r] = static_cast<char*>(y[r]);
   }
   if (s.dtype != MOE_F32)
-    hipLaunchKernelGGL(weighted_merge_kernel<true>, dim3(mover_grid(cus)), dim3(256), 0, st, rcp, yp, slot_of, topk_w,
+    hipLaunchKernelGGL(weighted_merge_kernel<true>, dim3(cus * kMergeBlocksPerCU), dim3(256), 0, st, rcp, yp, slot_of, topk_w,
                        s.R, s.T, s.k, s.d);
   else
-    hipLaunchKernelGGL(weighted_merge_kernel<false>, dim3(mover_grid(cus)), dim3(256), 0, st, rcp, yp, slot_of, topk_w,
+    hipLaunchKernelGGL(weighted_merge_kernel<false>, dim3(cus * kMergeBlocksPerCU), dim3(256), 0, st, rcp, yp, slot_of, topk_w,
                        s.R, s.T, s.k, s.d);
   return hipGetLastError();
 }
