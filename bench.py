@@ -24,6 +24,7 @@ from mixture_experts_layer_histogram_amd import configs, inputs  # noqa: E402
 
 METRIC = "MoE layer fwd tokens/s; grouped-GEMM % MFMA peak; gather/combine % HBM peak"
 PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
+PEAK_FP8_FLOPS = 5.0e15      # MI355X dense fp8 / MXFP8 MFMA
 PEAK_F32_FLOPS = 157.3e12    # MI355X fp32 matrix
 PEAK_HBM = 8.0e12            # MI355X HBM3E bytes/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_grouped_gemm_dsv3.json")
@@ -42,7 +43,8 @@ def parse():
     ap.add_argument("--config", default="dsv3", choices=sorted(configs.CONFIGS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-ranks", type=int, default=0, help="0 = all ranks (the whole step)")
+    ap.add_argument("--cpu-sample-ranks", type=int, default=0,
+                    help="0 = all ranks (the whole step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run three plain 1 GiB device copies (counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -55,9 +57,12 @@ def gemm_source_sha() -> str:
     return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
 
 
-def traffic_bytes():
-    """HBM bytes per FFN launch pair from the committed rocprofv3 counter runs, or
-    None when the GEMM source has changed since they were taken."""
+def traffic_bytes(cfg):
+    """HBM bytes per FFN launch pair of the bf16 DeepSeek-V3 share from the committed
+    rocprofv3 counter runs, or None for another workload or when the GEMM source has
+    changed since they were taken."""
+    if cfg.name != configs.DSV3.name:
+        return None
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -101,25 +106,50 @@ def write_traffic(fetch_csv, write_csv):
     print(json.dumps(rec))
 
 
+def _oracle_mx_weights(cfg, inp):
+    """Offline step of the MXFP8 oracle (untimed): every local expert's weights quantised."""
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import mx_oracle as MX
+    jobs = [(i, l) for i in range(3) for l in range(cfg.E_local)]
+    src = (inp.w1_f32, inp.w3_f32, inp.w2_f32)
+    out = [[None] * cfg.E_local for _ in range(3)]
+
+    def one(job):
+        i, l = job
+        out[i][l] = MX.quantize(np.asarray(src[i][l], dtype=np.float64))[2]
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(one, jobs))
+    return out
+
+
 def cpu_baseline(cfg, inp, ranks):
     """The oracle as it stands, on a bounded sample: the first `ranks` source ranks of
-    the same inputs (all of them by default, i.e. the whole step) through the share."""
+    the same inputs through the share (all of them by default, i.e. the whole step)."""
     from oracle import moe_oracle as O
+    from oracle import mx_oracle as MX
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     ranks = max(1, min(ranks, cfg.R))
-    t0 = time.perf_counter()
-    O.forward(inp.logits[:ranks], inp.x_f32[:ranks], inp.w1_f32, inp.w3_f32, inp.w2_f32,
-              inp.expert_to_local, cfg.E_local, cfg.k, cfg.minibatch)
+    if cfg.dtype == "mxfp8":
+        wq = _oracle_mx_weights(cfg, inp)
+        t0 = time.perf_counter()
+        MX.forward_q(inp.logits[:ranks], inp.x_f32[:ranks], *wq, inp.expert_to_local, cfg.E_local, cfg.k,
+                     cfg.minibatch)
+        what = ("fp64 NumPy quantised oracle (route, layout, pull with MX quantisation of x, SwiGLU experts "
+                "with h quantised, push, merge; weights quantised beforehand, untimed)")
+    else:
+        t0 = time.perf_counter()
+        O.forward(inp.logits[:ranks], inp.x_f32[:ranks], inp.w1_f32, inp.w3_f32, inp.w2_f32,
+                  inp.expert_to_local, cfg.E_local, cfg.k, cfg.minibatch)
+        what = "fp64 NumPy oracle (route, layout, pull, SwiGLU experts, push, merge)"
     dt = time.perf_counter() - t0
     tokens = ranks * cfg.T / cfg.G
     frac = "the whole step" if ranks == cfg.R else f"{ranks}/{cfg.R} of the step"
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"source ranks 0..{ranks - 1} of the same inputs ({frac}); fp64 NumPy oracle "
-                      f"(route, layout, pull, SwiGLU experts, push, merge); {dt:.2f} s wall"}
+            "sample": f"source ranks 0..{ranks - 1} of the same inputs ({frac}); {what}; {dt:.2f} s wall"}
 
 
 def main():
@@ -187,14 +217,17 @@ def main():
     esz = 4 if cfg.dtype == "f32" else 2
     row = cfg.d * esz
     flops = 6.0 * cfg.d * cfg.F * N
-    peak = PEAK_F32_FLOPS if cfg.dtype == "f32" else PEAK_BF16_FLOPS
+    peak = {"f32": PEAK_F32_FLOPS, "bf16": PEAK_BF16_FLOPS, "mxfp8": PEAK_FP8_FLOPS}[cfg.dtype]
     t_ffn = stage_ms["ffn"] * 1e-3
-    gather_bytes = 2.0 * N * row + N * 8
+    if cfg.dtype == "mxfp8":     # bf16 row in, E4M3 codes + one scale byte per 32 out
+        gather_bytes = N * row + N * (cfg.d + cfg.d // 32) + N * 8
+    else:
+        gather_bytes = 2.0 * N * row + N * 8
     push_bytes = 2.0 * N * row
     merge_bytes = 1.0 * N * row + cfg.R * cfg.T * row
     tokens = cfg.R * cfg.T / cfg.G
     value = tokens / (ms_step * 1e-3)
-    traffic = traffic_bytes()
+    traffic = traffic_bytes(cfg)
     result = {
         "metric": METRIC,
         "value": value,
@@ -206,7 +239,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype != "f32" else "f32",
+        "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) tokens, fan-in scaled random expert weights, router logits x@W_r)",
         "config": {"workload": cfg.name, "R": cfg.R, "T": cfg.T, "d": cfg.d, "E": cfg.E,
                    "E_local": cfg.E_local, "k": cfg.k, "F": cfg.F, "local_pairs": N,

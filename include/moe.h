@@ -59,7 +59,8 @@ extern "C" {
 typedef enum {
   MOE_F32 = 0,   /* fp32 rows and weights, fp32 arithmetic */
   MOE_BF16 = 1,  /* bf16 rows and weights, fp32 accumulation, bf16 h and outputs */
-  MOE_MXFP8 = 2  /* reserved: E4M3 elements with E8M0 scales per 32 along K */
+  MOE_MXFP8 = 2  /* bf16 token rows and outputs; the expert GEMMs in MXFP8: E4M3 elements
+                    with one E8M0 scale per 32 consecutive K values (see moe_mx_quantize) */
 } moe_dtype_t;
 
 typedef struct {
@@ -75,6 +76,16 @@ typedef struct {
   const int32_t* expert_to_local;
   int32_t E_local;
 } moe_placement_t;
+
+/* Block scales of MXFP8 expert weights (moe_mx_quantize of the bf16 weights), DEVICE
+ * pointers of E8M0 codes, 4-byte aligned.  Used only when dtype is MOE_MXFP8, where the
+ * weight pointers w1, w3, w2 hold E4M3 codes of the same [E_local][F][d] / [E_local][d][F]
+ * shapes (one byte per value). */
+typedef struct {
+  const uint8_t* w1;   /* [E_local][F][d/32] */
+  const uint8_t* w3;   /* [E_local][F][d/32] */
+  const uint8_t* w2;   /* [E_local][d][F/32] */
+} moe_mx_scales_t;
 
 /* Execution knobs.  Zero selects the default of each field. */
 typedef struct {
@@ -94,6 +105,22 @@ int64_t moe_max_pairs(const moe_shape_t* s, const moe_placement_t* p);
 
 /* Workspace bytes needed by every call below for this shape (a pure host function). */
 size_t moe_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex);
+
+/*
+ * moe_mx_quantize -- MXFP8 quantisation of `rows` rows of K values [kucoin §02: MXFP8 in
+ * the expert data path; the pages give no rule, the one used is OCP Microscaling v1.0]:
+ * for every block of 32 consecutive values v of a row, amax = max |v|;
+ *   amax == 0: scale code 0 and 32 zero codes;
+ *   otherwise e = clamp(floor(log2 amax) - 8, -127, 127), scale code e + 127, and
+ *   code_i = E4M3(v_i / 2^e) rounded to nearest (ties to even), saturated to +-448.
+ * src: [rows][K] of src_dtype (MOE_BF16 or MOE_F32), 16-byte aligned; codes: [rows][K]
+ * bytes, 16-byte aligned; scales: [rows][K/32] bytes.  K % 32 == 0 (else MOE_EALIGN).
+ * Used offline on expert weights; moe_dispatch_pull and the GEMM1 epilogue apply the
+ * same rule to token rows and h.  Bit-exact (integer decisions, exact power-of-two
+ * scaling).
+ */
+int moe_mx_quantize(const void* src, int32_t src_dtype, int64_t rows, int32_t K, uint8_t* codes,
+                    uint8_t* scales, void* stream);
 
 /*
  * moe_layout -- routing and sort-free layout generation.
@@ -128,10 +155,14 @@ int moe_layout(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t*
  *   xe[s][:] = x[pull_src[s].rank][pull_src[s].token][:]  for s in [0, N)
  * x: R device pointers, each [T][d] rows.  xe: [moe_max_pairs][d] rows.
  * offsets/ws: from moe_layout (N is read on the device).  Bit-exact copy.
+ * MOE_MXFP8 [kucoin §02: quantisation fused into the dispatch]: x is bf16 and each row
+ * is quantised on its way (the moe_mx_quantize rule): xe receives [moe_max_pairs][d]
+ * E4M3 codes and xe_scales [moe_max_pairs][d/32] scale codes (4-byte aligned).
+ * xe_scales is ignored for the other dtypes.
  */
 int moe_dispatch_pull(const moe_shape_t* s, const moe_placement_t* p, const void* const* x,
-                      const int32_t* pull_src, const int32_t* offsets, void* xe, void* ws,
-                      size_t ws_bytes, void* stream);
+                      const int32_t* pull_src, const int32_t* offsets, void* xe, uint8_t* xe_scales,
+                      void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_expert_ffn -- grouped SwiGLU expert FFN [kucoin §01: grouped GEMM over
@@ -142,10 +173,17 @@ int moe_dispatch_pull(const moe_shape_t* s, const moe_placement_t* p, const void
  * w1, w3: [E_local][F][d]; w2: [E_local][d][F]; xe, ye: [moe_max_pairs][d].
  * bf16: d and F must be multiples of 64.  Accuracy: see moe_forward tolerances
  * in the tests (bf16 max row-relative error <= 2e-2 against an fp64 oracle).
+ * MOE_MXFP8 [kucoin §02: quantisation fused into the grouped GEMM and SwiGLU]: xe and
+ * xe_scales as moe_dispatch_pull writes them, weights as E4M3 codes with w_scales
+ * (moe_mx_quantize of the bf16 weights); h is quantised along F in GEMM1's epilogue
+ * (fp32 h, the same rule); ye is bf16 with fp32 accumulation.  d and F must be
+ * multiples of 128.  Accuracy: max row-relative error <= 1e-2 against the fp64 forward
+ * on the dequantised operands.  xe_scales and w_scales are ignored for other dtypes.
  */
 int moe_expert_ffn(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
-                   const void* xe, const int32_t* offsets, const void* w1, const void* w3,
-                   const void* w2, void* ye, void* ws, size_t ws_bytes, void* stream);
+                   const void* xe, const uint8_t* xe_scales, const int32_t* offsets, const void* w1,
+                   const void* w3, const void* w2, const moe_mx_scales_t* w_scales, void* ye, void* ws,
+                   size_t ws_bytes, void* stream);
 
 /*
  * moe_combine_push -- push combine then the final weighted merge
@@ -166,11 +204,14 @@ int moe_combine_push(const moe_shape_t* s, const moe_placement_t* p, const void*
 
 /*
  * moe_forward -- the four calls above in order on one stream (the unfused,
- * multi-kernel path).  xe and ye are [moe_max_pairs][d] staging rows.
+ * multi-kernel path).  xe and ye are [moe_max_pairs][d] staging rows (xe holds E4M3
+ * codes and xe_scales their scales for MOE_MXFP8; xe_scales and w_scales are ignored
+ * for the other dtypes).
  */
 int moe_forward(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
                 const float* const* logits, const void* const* x, const void* w1, const void* w3,
-                const void* w2, void* xe, void* ye, void* const* recv, void* const* y,
+                const void* w2, const moe_mx_scales_t* w_scales, void* xe, uint8_t* xe_scales, void* ye,
+                void* const* recv, void* const* y,
                 int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
                 int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes, void* stream);
 

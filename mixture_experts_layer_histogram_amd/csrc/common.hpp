@@ -57,7 +57,11 @@ inline WsLayout ws_layout(const moe_shape_t& s, int32_t E_local) {
   w.blockbase = o;   o = align256(o + size_t(w.nb) * E_local * 4);
   // persistent-path control block: 128 words + 6 per row tile + one per ring slot
   w.pctrl = o;       o = align256(o + (size_t(128) + size_t(w.max_mtiles) * 6 + kMaxRingSlots) * 4);
-  w.hbuf = o;        o = align256(o + size_t(w.max_pairs) * s.F * esz);
+  // h staging: fp32/bf16 rows, or MXFP8 codes followed (256-aligned) by their block scales
+  const size_t hbytes = (s.dtype == MOE_MXFP8)
+                            ? align256(size_t(w.max_pairs) * s.F) + size_t(w.max_pairs) * (s.F / 32)
+                            : size_t(w.max_pairs) * s.F * esz;
+  w.hbuf = o;        o = align256(o + hbytes);
   w.total = o;
   return w;
 }

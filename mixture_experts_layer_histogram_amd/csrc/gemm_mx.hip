@@ -1,0 +1,276 @@
+// Grouped SwiGLU expert FFN in MXFP8 on gfx950 (v_mfma_scale_f32_32x32x64_f8f6f4).
+//
+// Operation (MoK article, kucoin.com/es "Cursor's MoK logra un aumento del 2.37x ...",
+// section 01: grouped GEMM over expert-contiguous rows; section 02: SwiGLU, and MXFP8
+// quantisation fused into the grouped-GEMM and SwiGLU data paths):
+//   GEMM1: h = MX(silu(X W1^T) * (X W3^T))   X, W1, W3 in MXFP8 (blocks of 32 along d)
+//   GEMM2: y = h W2^T (bf16 out)              h, W2 in MXFP8 (blocks of 32 along F)
+// h is quantised in GEMM1's epilogue, so it reaches HBM once, at one byte per value.
+//
+// The tile mirrors the bf16 one (256 x 256, 8 waves as 4 x 2, direct global->LDS fills,
+// the same XOR swizzle of 16-byte chunks in 128-byte LDS rows) with 128 K values per
+// stage, plus one 32-bit word of four E8M0 scales per tile row and stage, fetched into LDS
+// by one more direct load per wave.  Lane layout of the scaled MFMA (checked on the
+// device): lane (row r32, half hi) supplies K chunks hi and 2 + hi (16 values each) of
+// the 64-value step, and the scale of block hi of that step; so a lane shifts its row's
+// scale word right by 8 * hi and selects byte 0 or 2 with op_sel for the two steps.
+#include "gemm_tile.hpp"
+#include "mx.hpp"
+
+namespace moe {
+
+constexpr int kMxBK = 128;                                              // K values (bytes) per stage
+constexpr int kMxDataBytes = (kGemmBM + kGemmBN) * kMxBK;               // 64 KiB
+constexpr int kMxStageBytes = kMxDataBytes + (kGemmBM + kGemmBN) * 4;   // + a scale word per row
+constexpr int kMxLds = 2 * kMxStageBytes;                               // 132 KiB
+
+struct TileMX {
+  const uint8_t* a;     // the tile's first A row; row stride K
+  const uint8_t* as;    // its scales; row stride K / 32
+  void* o;              // MODE 0: h codes, MODE 1: bf16 rows; row stride Nout elements
+  uint8_t* os;          // MODE 0: h scales; row stride Nout / 32
+  int rows;             // valid rows, 1..256; rows beyond re-read row rows-1 and are not stored
+};
+
+__device__ __forceinline__ i32x8 ld_frag(const char* s, int row, int c0) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(s + swz_off(row, c0));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(s + swz_off(row, c0 + 2));
+  return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+}
+
+// max over the 32 lanes of each wave half, by XOR swizzles (bit-mask mode of ds_swizzle)
+__device__ __forceinline__ uint32_t half_max(uint32_t m) {
+  m = max(m, uint32_t(__builtin_amdgcn_ds_swizzle(int(m), (1 << 10) | 0x1F)));
+  m = max(m, uint32_t(__builtin_amdgcn_ds_swizzle(int(m), (2 << 10) | 0x1F)));
+  m = max(m, uint32_t(__builtin_amdgcn_ds_swizzle(int(m), (4 << 10) | 0x1F)));
+  m = max(m, uint32_t(__builtin_amdgcn_ds_swizzle(int(m), (8 << 10) | 0x1F)));
+  return max(m, uint32_t(__builtin_amdgcn_ds_swizzle(int(m), (16 << 10) | 0x1F)));
+}
+
+// b0/b1: this expert's weight codes ([Nout][K]); bs0/bs1 their scales ([Nout][K/32]).
+template <int MODE>
+__device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __restrict__ b0,
+                                             const uint8_t* __restrict__ b1, const uint8_t* __restrict__ bs0,
+                                             const uint8_t* __restrict__ bs1, int c0, int Nout, int K,
+                                             char* smem) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int lrow = lane >> 3, lpos = lane & 7;
+  const int lch_even = lpos ^ (lrow >> 1);
+  const int lch_odd = lpos ^ (4 + (lrow >> 1));
+  const int nk = K / kMxBK;
+  const int ksc = K / kMxBlock;
+  const int rows = io.rows;
+
+  // fills: this wave's row groups g = wave*4 + i (rows g*8 + lrow) of the A and B tiles
+  const uint8_t* ap[4];
+  const uint8_t* bp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wave * 4 + i) * 8 + lrow;
+    const int lch = (i & 1) ? lch_odd : lch_even;
+    ap[i] = io.a + size_t(min(row, rows - 1)) * K + lch * 16;
+    if (MODE == 0) {
+      const int n = min(c0 + (row >> 6) * 32 + (row & 31), Nout - 1);
+      bp[i] = (((row >> 5) & 1) ? b1 : b0) + size_t(n) * K + lch * 16;
+    } else {
+      bp[i] = b0 + size_t(min(c0 + row, Nout - 1)) * K + lch * 16;
+    }
+  }
+  // scale words: waves 0-3 fetch A rows 64*wave + lane, waves 4-7 B rows 64*(wave-4) + lane
+  const uint8_t* sp;
+  {
+    const int row = (wave & 3) * 64 + lane;
+    if (wave < 4) {
+      sp = io.as + size_t(min(row, rows - 1)) * ksc;
+    } else if (MODE == 0) {
+      const int n = min(c0 + (row >> 6) * 32 + (row & 31), Nout - 1);
+      sp = (((row >> 5) & 1) ? bs1 : bs0) + size_t(n) * ksc;
+    } else {
+      sp = bs0 + size_t(min(c0 + row, Nout - 1)) * ksc;
+    }
+  }
+  auto issue = [&](int ks) {
+    char* sa = smem + (ks & 1) * kMxStageBytes;
+    char* sb = sa + kGemmBM * kMxBK;
+    char* ss = sa + kMxDataBytes;
+    const int koff = ks * kMxBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = wave * 4 + i;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(ap[i] + koff), (lds_void_ptr)(sa + g * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bp[i] + koff), (lds_void_ptr)(sb + g * 1024), 16, 0, 0);
+    }
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(sp + ks * 4), (lds_void_ptr)(ss + wave * 256), 4, 0, 0);
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
+
+  issue(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int ks = 0; ks < nk; ++ks) {
+    if (ks + 1 < nk) issue(ks + 1);     // other stage: everyone finished reading it
+    const char* sa = smem + (ks & 1) * kMxStageBytes;
+    const char* sb = sa + kGemmBM * kMxBK;
+    const uint32_t* ss = reinterpret_cast<const uint32_t*>(sa + kMxDataBytes);
+    int wa[2], wb[4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) wa[m] = int(ss[wm * 64 + m * 32 + r32] >> (8 * hi));
+#pragma unroll
+    for (int n = 0; n < 4; ++n) wb[n] = int(ss[kGemmBM + wn * 128 + n * 32 + r32] >> (8 * hi));
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      i32x8 fa[2], fb[4];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) fa[m] = ld_frag(sa, wm * 64 + m * 32 + r32, 4 * st + hi);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) fb[n] = ld_frag(sb, wn * 128 + n * 32 + r32, 4 * st + hi);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          acc[m][n] = (st == 0)
+              ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[m], fb[n], acc[m][n], 0, 0, 0, wa[m], 0, wb[n])
+              : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[m], fb[n], acc[m][n], 0, 0, 2, wa[m], 2, wb[n]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);      // this wave's fills of the next stage landed
+    __syncthreads();                    // ... and everyone's
+  }
+
+  // epilogue: lane holds column r32 and rows 8*(e/4) + 4*hi + e%4 of each 32x32 block
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int rb = wm * 64 + m * 32;
+    if (MODE == 0) {
+      uint8_t* hq = static_cast<uint8_t*>(io.o) + size_t(rb) * Nout;
+      uint8_t* hs = io.os + size_t(rb) * (Nout / kMxBlock);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int f0 = c0 + (wn * 2 + q) * 32;      // this 32-value block of h (inside [0, Nout))
+        float h[16];
+        uint32_t mx[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          h[e] = silu_f32(acc[m][2 * q][e]) * acc[m][2 * q + 1][e];
+          mx[e] = half_max(__float_as_uint(h[e]) & 0x7FFFFFFFu);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = 8 * (e >> 2) + 4 * hi + (e & 3);
+          if (rb + row < rows) {
+            uint32_t code = 0, sc = 0;
+            if (mx[e] != 0) {
+              const int ex = mx_block_exp(mx[e]);
+              code = mx_code1(h[e], mx_inv_scale(ex));
+              sc = uint32_t(ex + 127);
+            }
+            hq[size_t(row) * Nout + f0 + r32] = uint8_t(code);
+            if (r32 == 0) hs[size_t(row) * (Nout / kMxBlock) + f0 / kMxBlock] = uint8_t(sc);
+          }
+        }
+      }
+    } else {
+      uint16_t* orow = static_cast<uint16_t*>(io.o) + size_t(rb) * Nout;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int col = c0 + wn * 128 + n * 32 + r32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = 8 * (e >> 2) + 4 * hi + (e & 3);
+          if (rb + row < rows && col < Nout) orow[size_t(row) * Nout + col] = f32_to_bf16(acc[m][n][e]);
+        }
+      }
+    }
+  }
+}
+
+// MODE 0: A = xe codes [*][d], B0/B1 = W1/W3 -> h codes [*][F] + scales   (256 rows x 128 f)
+// MODE 1: A = h codes [*][F],  B0 = W2       -> ye bf16 [*][d]            (256 rows x 256 cols)
+// Tile enumeration as in the bf16 grouped GEMM: a persistent grid walks 8 contiguous
+// per-XCD ranges of the expert-major tile list.
+template <int MODE>
+__global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_mx_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B0,
+    const uint8_t* __restrict__ B1, const uint8_t* __restrict__ Bs0, const uint8_t* __restrict__ Bs1,
+    void* __restrict__ C, uint8_t* __restrict__ Cs, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ mtile_base, const int32_t* __restrict__ ctrl, int El, int K, int Nout) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int cols_per_tile = (MODE == 0) ? kGemmBN / 2 : kGemmBN;
+  const int NT = (Nout + cols_per_tile - 1) / cols_per_tile;
+  const int total = ctrl[kCtrlMTiles] * NT;
+  const int per_xcd = (total + 7) >> 3;
+  const int xcd = blockIdx.x & 7;
+  const int wg_per_xcd = gridDim.x >> 3;
+  const int ksc = K / kMxBlock;
+
+  for (int tt = blockIdx.x >> 3; tt < per_xcd; tt += wg_per_xcd) {
+    const int tau = xcd * per_xcd + tt;
+    if (tau >= total) break;
+    const int mtg = tau / NT;
+    const int l = find_expert(mtile_base, El, mtg);
+    const int mt0 = mtile_base[l];
+    const int mtl = mtile_base[l + 1] - mt0;
+    const int i_in = tau - mt0 * NT;
+    const int nt = i_in / mtl, mt = i_in - nt * mtl;
+    const int row0 = offsets[l] + mt * kGemmBM;
+    TileMX io;
+    io.a = A + size_t(row0) * K;
+    io.as = As + size_t(row0) * ksc;
+    if (MODE == 0) {
+      io.o = static_cast<uint8_t*>(C) + size_t(row0) * Nout;
+      io.os = Cs + size_t(row0) * (Nout / kMxBlock);
+    } else {
+      io.o = static_cast<uint16_t*>(C) + size_t(row0) * Nout;
+      io.os = nullptr;
+    }
+    io.rows = min(kGemmBM, offsets[l + 1] - row0);
+    const uint8_t* b0 = B0 + size_t(l) * Nout * K;
+    const uint8_t* b1 = (MODE == 0) ? B1 + size_t(l) * Nout * K : b0;
+    const uint8_t* bs0 = Bs0 + size_t(l) * Nout * ksc;
+    const uint8_t* bs1 = (MODE == 0) ? Bs1 + size_t(l) * Nout * ksc : bs0;
+    gemm_mx_tile<MODE>(io, b0, b1, bs0, bs1, nt * cols_per_tile, Nout, K, smem);
+  }
+}
+
+// h codes at hbuf, h scales after them (both within the workspace's h staging region)
+size_t mx_h_scales_offset(const WsLayout& L, const moe_shape_t& s) {
+  return L.hbuf + align256(size_t(L.max_pairs) * s.F);
+}
+
+hipError_t launch_ffn_mx(const moe_shape_t& s, int El, const uint8_t* xe, const uint8_t* xe_scales,
+                         const int32_t* offsets, const uint8_t* w1, const uint8_t* w3, const uint8_t* w2,
+                         const uint8_t* w1s, const uint8_t* w3s, const uint8_t* w2s, void* ye, char* ws,
+                         const WsLayout& L, int cus, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_mx_kernel<0>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_mx_kernel<1>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int32_t* ctrl = reinterpret_cast<const int32_t*>(ws + L.ctrl);
+  const int32_t* mtb = reinterpret_cast<const int32_t*>(ws + L.mtile_base);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hbuf);
+  uint8_t* hs = reinterpret_cast<uint8_t*>(ws + mx_h_scales_offset(L, s));
+  const int grid = (cus / 8) * 8;
+  hipLaunchKernelGGL(grouped_gemm_mx_kernel<0>, dim3(grid), dim3(kGemmThreads), kMxLds, st, xe, xe_scales, w1, w3,
+                     w1s, w3s, static_cast<void*>(hq), hs, offsets, mtb, ctrl, El, s.d, s.F);
+  hipLaunchKernelGGL(grouped_gemm_mx_kernel<1>, dim3(grid), dim3(kGemmThreads), kMxLds, st, hq, hs, w2, nullptr,
+                     w2s, nullptr, ye, nullptr, offsets, mtb, ctrl, El, s.F, s.d);
+  return hipGetLastError();
+}
+
+}  // namespace moe

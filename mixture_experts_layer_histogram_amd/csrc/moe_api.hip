@@ -16,6 +16,14 @@ hipError_t launch_ffn(const moe_shape_t& s, int El, const void* xe, const int32_
 hipError_t launch_combine(const moe_shape_t& s, const char* ye, const int32_t* pull_src,
                           const int32_t* slot_of, const float* topk_w, void* const* recv, void* const* y,
                           const int32_t* ctrl, int cus, hipStream_t st);
+hipError_t launch_mx_quantize(const void* src, int src_dtype, int64_t rows, int K, uint8_t* codes,
+                              uint8_t* scales, int cus, hipStream_t st);
+hipError_t launch_dispatch_mx(const moe_shape_t& s, const void* const* x, const int32_t* pull_src, uint8_t* xe,
+                              uint8_t* xe_scales, const int32_t* ctrl, int cus, hipStream_t st);
+hipError_t launch_ffn_mx(const moe_shape_t& s, int El, const uint8_t* xe, const uint8_t* xe_scales,
+                         const int32_t* offsets, const uint8_t* w1, const uint8_t* w3, const uint8_t* w2,
+                         const uint8_t* w1s, const uint8_t* w3s, const uint8_t* w2s, void* ye, char* ws,
+                         const WsLayout& L, int cus, hipStream_t st);
 hipError_t launch_merge(const moe_shape_t& s, const int32_t* slot_of, const float* topk_w, void* const* recv,
                         void* const* y, int cus, hipStream_t st);
 hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x, const void* w1, const void* w3,
@@ -37,11 +45,11 @@ int check_shape(const moe_shape_t* s, const moe_placement_t* p) {
   if (s->E < 1 || s->E > 1024 || s->k < 1 || s->k > 16 || s->k > s->E) return MOE_EINVAL;
   if (p->E_local < 1 || p->E_local > s->E) return MOE_EINVAL;
   if (int64_t(s->R) * s->T * s->k >= (int64_t(1) << 31)) return MOE_EINVAL;
-  if (s->dtype == MOE_MXFP8) return MOE_EUNSUP;
-  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_EINVAL;
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16 && s->dtype != MOE_MXFP8) return MOE_EINVAL;
   const int esz = s->dtype == MOE_F32 ? 4 : 2;
   if ((int64_t(s->d) * esz) % 16 || (int64_t(s->F) * esz) % 16) return MOE_EALIGN;
   if (s->dtype == MOE_BF16 && (s->d % kGemmBK || s->F % kGemmBK)) return MOE_EALIGN;
+  if (s->dtype == MOE_MXFP8 && (s->d % 128 || s->F % 128)) return MOE_EALIGN;   // one 128-value GEMM stage
   return MOE_OK;
 }
 
@@ -61,6 +69,19 @@ int check_ptr_table(const T* const* tab, int R) {
 }
 
 int aligned16(const void* q) { return q && !(reinterpret_cast<uintptr_t>(q) & 15); }
+
+// non-null and 4-byte aligned (scale arrays, read as 32-bit words)
+int check_scales(const void* q) {
+  if (!q) return MOE_EINVAL;
+  return (reinterpret_cast<uintptr_t>(q) & 3) ? MOE_EALIGN : MOE_OK;
+}
+
+int check_w_scales(const moe_mx_scales_t* w) {
+  if (!w) return MOE_EINVAL;
+  int rc;
+  if ((rc = check_scales(w->w1)) || (rc = check_scales(w->w3)) || (rc = check_scales(w->w2))) return rc;
+  return MOE_OK;
+}
 
 int cu_count() {
   int dev = 0;
@@ -111,6 +132,17 @@ size_t moe_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p, const
   return ws_layout(*s, p->E_local).total;
 }
 
+int moe_mx_quantize(const void* src, int32_t src_dtype, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                    void* stream) {
+  if (src_dtype != MOE_BF16 && src_dtype != MOE_F32) return MOE_EINVAL;
+  if (rows < 0 || K < 1 || rows > (int64_t(1) << 40) / K) return MOE_EINVAL;
+  if (K % 32) return MOE_EALIGN;
+  if (!src || !codes || !scales) return MOE_EINVAL;
+  if (!aligned16(src) || !aligned16(codes)) return MOE_EALIGN;
+  return hip_rc(launch_mx_quantize(src, src_dtype, rows, K, codes, scales, cu_count(),
+                                   static_cast<hipStream_t>(stream)));
+}
+
 int moe_layout(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
                const float* const* logits, int32_t* topk_idx, float* topk_w, int32_t* counts,
                int32_t* offsets, int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes,
@@ -129,23 +161,27 @@ int moe_layout(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t*
 }
 
 int moe_dispatch_pull(const moe_shape_t* s, const moe_placement_t* p, const void* const* x,
-                      const int32_t* pull_src, const int32_t* offsets, void* xe, void* ws, size_t ws_bytes,
-                      void* stream) {
+                      const int32_t* pull_src, const int32_t* offsets, void* xe, uint8_t* xe_scales, void* ws,
+                      size_t ws_bytes, void* stream) {
   int rc = check_shape(s, p);
   if (rc) return rc;
   if (!pull_src || !offsets) return MOE_EINVAL;
   if (!aligned16(xe)) return xe ? MOE_EALIGN : MOE_EINVAL;
+  if (s->dtype == MOE_MXFP8 && (rc = check_scales(xe_scales))) return rc;
   if ((rc = check_ptr_table(x, s->R))) return rc;
   if ((rc = check_ws(s, p, ws, ws_bytes))) return rc;
   const WsLayout L = ws_layout(*s, p->E_local);
-  return hip_rc(launch_dispatch(*s, x, pull_src, static_cast<char*>(xe),
-                                reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + L.ctrl), cu_count(),
+  const int32_t* ctrl = reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + L.ctrl);
+  if (s->dtype == MOE_MXFP8)
+    return hip_rc(launch_dispatch_mx(*s, x, pull_src, static_cast<uint8_t*>(xe), xe_scales, ctrl, cu_count(),
+                                     static_cast<hipStream_t>(stream)));
+  return hip_rc(launch_dispatch(*s, x, pull_src, static_cast<char*>(xe), ctrl, cu_count(),
                                 static_cast<hipStream_t>(stream)));
 }
 
 int moe_expert_ffn(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex, const void* xe,
-                   const int32_t* offsets, const void* w1, const void* w3, const void* w2, void* ye, void* ws,
-                   size_t ws_bytes, void* stream) {
+                   const uint8_t* xe_scales, const int32_t* offsets, const void* w1, const void* w3, const void* w2,
+                   const moe_mx_scales_t* w_scales, void* ye, void* ws, size_t ws_bytes, void* stream) {
   (void)ex;
   int rc = check_shape(s, p);
   if (rc) return rc;
@@ -153,8 +189,14 @@ int moe_expert_ffn(const moe_shape_t* s, const moe_placement_t* p, const moe_exe
   const void* bufs[] = {xe, w1, w3, w2, ye};
   for (const void* b : bufs)
     if (!aligned16(b)) return b ? MOE_EALIGN : MOE_EINVAL;
+  if (s->dtype == MOE_MXFP8 && ((rc = check_scales(xe_scales)) || (rc = check_w_scales(w_scales)))) return rc;
   if ((rc = check_ws(s, p, ws, ws_bytes))) return rc;
   const WsLayout L = ws_layout(*s, p->E_local);
+  if (s->dtype == MOE_MXFP8)
+    return hip_rc(launch_ffn_mx(*s, p->E_local, static_cast<const uint8_t*>(xe), xe_scales, offsets,
+                                static_cast<const uint8_t*>(w1), static_cast<const uint8_t*>(w3),
+                                static_cast<const uint8_t*>(w2), w_scales->w1, w_scales->w3, w_scales->w2, ye,
+                                static_cast<char*>(ws), L, cu_count(), static_cast<hipStream_t>(stream)));
   return hip_rc(launch_ffn(*s, p->E_local, xe, offsets, w1, w3, w2, ye, static_cast<char*>(ws), L, cu_count(),
                            static_cast<hipStream_t>(stream)));
 }
@@ -176,8 +218,8 @@ int moe_combine_push(const moe_shape_t* s, const moe_placement_t* p, const void*
 }
 
 int moe_forward(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex, const float* const* logits,
-                const void* const* x, const void* w1, const void* w3, const void* w2, void* xe, void* ye,
-                void* const* recv, void* const* y, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                const void* const* x, const void* w1, const void* w3, const void* w2, const moe_mx_scales_t* w_scales,
+                void* xe, uint8_t* xe_scales, void* ye, void* const* recv, void* const* y, int32_t* topk_idx, float* topk_w, int32_t* counts,
                 int32_t* offsets, int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes,
                 void* stream) {
   int rc = check_shape(s, p);
@@ -188,6 +230,7 @@ int moe_forward(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t
   const void* bufs[] = {xe, ye, w1, w3, w2};
   for (const void* b : bufs)
     if (!aligned16(b)) return b ? MOE_EALIGN : MOE_EINVAL;
+  if (s->dtype == MOE_MXFP8 && ((rc = check_scales(xe_scales)) || (rc = check_w_scales(w_scales)))) return rc;
   if ((rc = check_ptr_table(logits, s->R)) || (rc = check_ptr_table(x, s->R)) ||
       (rc = check_ptr_table(recv, s->R)) || (rc = check_ptr_table(y, s->R)))
     return rc;
@@ -195,8 +238,9 @@ int moe_forward(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t
   if ((rc = moe_layout(s, p, ex, logits, topk_idx, topk_w, counts, offsets, pull_src, slot_of, ws, ws_bytes,
                        stream)))
     return rc;
-  if ((rc = moe_dispatch_pull(s, p, x, pull_src, offsets, xe, ws, ws_bytes, stream))) return rc;
-  if ((rc = moe_expert_ffn(s, p, ex, xe, offsets, w1, w3, w2, ye, ws, ws_bytes, stream))) return rc;
+  if ((rc = moe_dispatch_pull(s, p, x, pull_src, offsets, xe, xe_scales, ws, ws_bytes, stream))) return rc;
+  if ((rc = moe_expert_ffn(s, p, ex, xe, xe_scales, offsets, w1, w3, w2, w_scales, ye, ws, ws_bytes, stream)))
+    return rc;
   return moe_combine_push(s, p, ye, pull_src, slot_of, topk_w, offsets, recv, y, ws, ws_bytes, stream);
 }
 
@@ -298,6 +342,6 @@ const char* moe_strerror(int code) {
   }
 }
 
-const char* moe_version(void) { return "libmoe 0.1 gfx950"; }
+const char* moe_version(void) { return "libmoe 0.2 gfx950"; }
 
 }  // extern "C"

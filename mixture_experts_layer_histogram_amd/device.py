@@ -36,6 +36,9 @@ class DeviceProblem:
         self.w1 = _to_device_store(inp.w1_store, dt, self.device)
         self.w3 = _to_device_store(inp.w3_store, dt, self.device)
         self.w2 = _to_device_store(inp.w2_store, dt, self.device)
+        self.w_scales = None
+        if dt == "mxfp8":
+            self.quantize_weights()
         self.nmax = moe.moe_max_pairs(self.shape, self.placement)
         self.ws_bytes = moe.moe_workspace_bytes(self.shape, self.placement, self.ex)
         if self.ws_bytes == 0:
@@ -43,6 +46,24 @@ class DeviceProblem:
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         if alloc_outputs:
             self.alloc_outputs()
+
+    def quantize_weights(self, stream=None):
+        """MXFP8 codes and block scales of the bf16 expert weights (the offline step, on the device)."""
+        torch = self.torch
+        self.wq, self.ws_codes = [], []
+        for w in (self.w1, self.w3, self.w2):
+            K = w.shape[-1]
+            rows = w.numel() // K
+            q = torch.empty(w.shape, dtype=torch.uint8, device=self.device)
+            sc = torch.empty((*w.shape[:-1], K // 32), dtype=torch.uint8, device=self.device)
+            moe.moe_mx_quantize(w, moe.MOE_BF16, rows, K, q, sc, stream=stream)
+            self.wq.append(q)
+            self.ws_codes.append(sc)
+        self.w_scales = moe.MXScales(*(t.data_ptr() for t in self.ws_codes))
+
+    def weights(self):
+        """The weight tensors the FFN reads: bf16/fp32 rows, or MXFP8 codes."""
+        return self.wq if self.cfg.dtype == "mxfp8" else (self.w1, self.w3, self.w2)
 
     def alloc_outputs(self):
         torch, cfg, dev = self.torch, self.cfg, self.device
@@ -54,7 +75,12 @@ class DeviceProblem:
         self.offsets = torch.empty(cfg.E_local + 1, dtype=torch.int32, device=dev)
         self.pull_src = torch.empty((self.nmax, 2), dtype=torch.int32, device=dev)
         self.slot_of = torch.empty((R, T, k), dtype=torch.int32, device=dev)
-        self.xe = torch.empty((self.nmax, d), dtype=ed, device=dev)
+        if cfg.dtype == "mxfp8":
+            self.xe = torch.empty((self.nmax, d), dtype=torch.uint8, device=dev)
+            self.xe_scales = torch.empty((self.nmax, d // 32), dtype=torch.uint8, device=dev)
+        else:
+            self.xe = torch.empty((self.nmax, d), dtype=ed, device=dev)
+            self.xe_scales = None
         self.ye = torch.empty((self.nmax, d), dtype=ed, device=dev)
         self.recv = [torch.zeros((T, k, d), dtype=ed, device=dev) for _ in range(R)]
         self.y = [torch.empty((T, d), dtype=ed, device=dev) for _ in range(R)]
@@ -66,20 +92,22 @@ class DeviceProblem:
 
     def dispatch(self, stream=None):
         moe.moe_dispatch_pull(self.shape, self.placement, self.x, self.pull_src, self.offsets, self.xe,
-                              self.ws, stream=stream)
+                              self.ws, stream=stream, xe_scales=self.xe_scales)
 
     def ffn(self, stream=None):
-        moe.moe_expert_ffn(self.shape, self.placement, self.ex, self.xe, self.offsets, self.w1, self.w3,
-                           self.w2, self.ye, self.ws, stream=stream)
+        w1, w3, w2 = self.weights()
+        moe.moe_expert_ffn(self.shape, self.placement, self.ex, self.xe, self.offsets, w1, w3, w2, self.ye,
+                           self.ws, stream=stream, xe_scales=self.xe_scales, w_scales=self.w_scales)
 
     def combine(self, stream=None):
         moe.moe_combine_push(self.shape, self.placement, self.ye, self.pull_src, self.slot_of, self.topk_w,
                              self.offsets, self.recv, self.y, self.ws, stream=stream)
 
     def forward(self, stream=None):
-        moe.moe_forward(self.shape, self.placement, self.ex, self.logits, self.x, self.w1, self.w3, self.w2,
-                        self.xe, self.ye, self.recv, self.y, self.topk_idx, self.topk_w, self.counts,
-                        self.offsets, self.pull_src, self.slot_of, self.ws, stream=stream)
+        w1, w3, w2 = self.weights()
+        moe.moe_forward(self.shape, self.placement, self.ex, self.logits, self.x, w1, w3, w2, self.xe, self.ye,
+                        self.recv, self.y, self.topk_idx, self.topk_w, self.counts, self.offsets, self.pull_src,
+                        self.slot_of, self.ws, stream=stream, w_scales=self.w_scales, xe_scales=self.xe_scales)
 
     def alloc_ring(self, ring_mib=None, ex=None):
         """Ring buffer for the persistent path (ring_mib MiB, default the config's)."""

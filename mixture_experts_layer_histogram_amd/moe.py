@@ -21,7 +21,7 @@ ERRORS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_ENOSPC", -4:
           -5: "MOE_ETIMEOUT", -6: "MOE_EUNSUP"}
 
 # every symbol include/moe.h declares
-EXPORTS = ["moe_max_pairs", "moe_workspace_bytes", "moe_layout", "moe_dispatch_pull",
+EXPORTS = ["moe_max_pairs", "moe_workspace_bytes", "moe_mx_quantize", "moe_layout", "moe_dispatch_pull",
            "moe_expert_ffn", "moe_combine_push", "moe_forward", "moe_forward_persistent",
            "moe_ring_slot_bytes", "moe_persistent_workspace_bytes", "moe_read_status",
            "moe_strerror", "moe_version"]
@@ -43,6 +43,11 @@ class Placement(ctypes.Structure):
     _fields_ = [("expert_to_local", ctypes.c_void_p), ("E_local", ctypes.c_int32)]
 
 
+class MXScales(ctypes.Structure):
+    """moe_mx_scales_t: device pointers of the E8M0 block scales of w1, w3, w2."""
+    _fields_ = [("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p)]
+
+
 class Exec(ctypes.Structure):
     _fields_ = [("minibatch_rows", ctypes.c_int32), ("comm_cus", ctypes.c_int32),
                 ("ring_slots", ctypes.c_int32), ("trace", ctypes.c_int32),
@@ -60,16 +65,17 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(f"libmoe.so not built: {LIB_PATH} (run __graft_entry__.build())")
         L = ctypes.CDLL(LIB_PATH)
         P, VP, I32, SZ = ctypes.POINTER, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
-        S, PL, EX = P(Shape), P(Placement), P(Exec)
+        S, PL, EX, MS = P(Shape), P(Placement), P(Exec), P(MXScales)
         L.moe_max_pairs.argtypes = [S, PL]
         L.moe_max_pairs.restype = ctypes.c_int64
         L.moe_workspace_bytes.argtypes = [S, PL, EX]
         L.moe_workspace_bytes.restype = SZ
+        L.moe_mx_quantize.argtypes = [VP, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, VP, VP, VP]
         L.moe_layout.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
-        L.moe_dispatch_pull.argtypes = [S, PL, VP, VP, VP, VP, VP, SZ, VP]
-        L.moe_expert_ffn.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_dispatch_pull.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_expert_ffn.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, MS, VP, VP, SZ, VP]
         L.moe_combine_push.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
-        L.moe_forward.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, VP, VP, VP,
+        L.moe_forward.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, MS, VP, VP, VP, VP, VP,
                                   VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_forward_persistent.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, SZ, VP, VP,
                                              VP, VP, VP, VP, VP, VP, VP, SZ, VP]
@@ -81,7 +87,7 @@ def lib() -> ctypes.CDLL:
         L.moe_strerror.argtypes = [I32]
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_version.restype = ctypes.c_char_p
-        for f in ("moe_layout", "moe_dispatch_pull", "moe_expert_ffn", "moe_combine_push",
+        for f in ("moe_mx_quantize", "moe_layout", "moe_dispatch_pull", "moe_expert_ffn", "moe_combine_push",
                   "moe_forward", "moe_forward_persistent", "moe_read_status"):
             getattr(L, f).restype = I32
         _lib = L
@@ -138,6 +144,15 @@ def moe_workspace_bytes(shape: Shape, placement: Placement, ex: Exec | None = No
                                          ctypes.byref(ex) if ex is not None else None))
 
 
+def _ref(st):
+    return ctypes.byref(st) if st is not None else None
+
+
+def moe_mx_quantize(src, src_dtype, rows, K, codes, scales, stream=None, check=True):
+    rc = lib().moe_mx_quantize(_p(src), int(src_dtype), int(rows), int(K), _p(codes), _p(scales), _stream(stream))
+    return _check(rc, "moe_mx_quantize") if check else rc
+
+
 def moe_layout(shape, placement, ex, logits, topk_idx, topk_w, counts, offsets, pull_src, slot_of,
                ws, ws_bytes=None, stream=None, check=True):
     rc = lib().moe_layout(ctypes.byref(shape), ctypes.byref(placement),
@@ -148,19 +163,18 @@ def moe_layout(shape, placement, ex, logits, topk_idx, topk_w, counts, offsets, 
 
 
 def moe_dispatch_pull(shape, placement, x, pull_src, offsets, xe, ws, ws_bytes=None, stream=None,
-                      check=True):
+                      check=True, xe_scales=None):
     rc = lib().moe_dispatch_pull(ctypes.byref(shape), ctypes.byref(placement), _table(x), _p(pull_src),
-                                 _p(offsets), _p(xe), _p(ws), ws.numel() if ws_bytes is None else ws_bytes,
-                                 _stream(stream))
+                                 _p(offsets), _p(xe), _p(xe_scales), _p(ws),
+                                 ws.numel() if ws_bytes is None else ws_bytes, _stream(stream))
     return _check(rc, "moe_dispatch_pull") if check else rc
 
 
 def moe_expert_ffn(shape, placement, ex, xe, offsets, w1, w3, w2, ye, ws, ws_bytes=None, stream=None,
-                   check=True):
-    rc = lib().moe_expert_ffn(ctypes.byref(shape), ctypes.byref(placement),
-                              ctypes.byref(ex) if ex is not None else None, _p(xe), _p(offsets), _p(w1),
-                              _p(w3), _p(w2), _p(ye), _p(ws), ws.numel() if ws_bytes is None else ws_bytes,
-                              _stream(stream))
+                   check=True, xe_scales=None, w_scales=None):
+    rc = lib().moe_expert_ffn(ctypes.byref(shape), ctypes.byref(placement), _ref(ex), _p(xe), _p(xe_scales),
+                              _p(offsets), _p(w1), _p(w3), _p(w2), _ref(w_scales), _p(ye), _p(ws),
+                              ws.numel() if ws_bytes is None else ws_bytes, _stream(stream))
     return _check(rc, "moe_expert_ffn") if check else rc
 
 
@@ -173,10 +187,11 @@ def moe_combine_push(shape, placement, ye, pull_src, slot_of, topk_w, offsets, r
 
 
 def moe_forward(shape, placement, ex, logits, x, w1, w3, w2, xe, ye, recv, y, topk_idx, topk_w, counts,
-                offsets, pull_src, slot_of, ws, ws_bytes=None, stream=None, check=True):
-    rc = lib().moe_forward(ctypes.byref(shape), ctypes.byref(placement),
-                           ctypes.byref(ex) if ex is not None else None, _table(logits), _table(x), _p(w1),
-                           _p(w3), _p(w2), _p(xe), _p(ye), _table(recv), _table(y), _p(topk_idx),
+                offsets, pull_src, slot_of, ws, ws_bytes=None, stream=None, check=True, w_scales=None,
+                xe_scales=None):
+    rc = lib().moe_forward(ctypes.byref(shape), ctypes.byref(placement), _ref(ex), _table(logits), _table(x),
+                           _p(w1), _p(w3), _p(w2), _ref(w_scales), _p(xe), _p(xe_scales), _p(ye), _table(recv),
+                           _table(y), _p(topk_idx),
                            _p(topk_w), _p(counts), _p(offsets), _p(pull_src), _p(slot_of), _p(ws),
                            ws.numel() if ws_bytes is None else ws_bytes, _stream(stream))
     return _check(rc, "moe_forward") if check else rc

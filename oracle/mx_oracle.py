@@ -37,40 +37,31 @@ E4M3_MIN_NORMAL_EXP = -6
 E4M3_MANT_BITS = 3
 
 
-def _rne(v: np.ndarray) -> np.ndarray:
-    """Round half to even (NumPy's rint uses the current mode, nearest-even)."""
-    return np.rint(v)
-
-
 def e4m3_round(y: np.ndarray) -> np.ndarray:
-    """Nearest E4M3 value of y (ties to even), saturated to +-448; float64 in and out."""
+    """Nearest E4M3 value of y (ties to even), saturated to +-448; float64 in and out.
+
+    The grid step at |y| is 2^(max(floor(log2 |y|), -6) - 3): 3 mantissa bits in a normal
+    binade, the subnormal step 2^-9 below 2^-6.  np.rint rounds half to even."""
     y = np.asarray(y, dtype=np.float64)
     a = np.abs(y)
-    out = np.zeros_like(a)
-    nz = a > 0
-    # exponent of each value, floored at the subnormal exponent
-    e = np.full_like(a, E4M3_MIN_NORMAL_EXP)
-    e[nz] = np.maximum(np.floor(np.log2(a[nz])), E4M3_MIN_NORMAL_EXP)
-    ulp = np.exp2(e - E4M3_MANT_BITS)
-    q = _rne(a / ulp) * ulp
-    q = np.minimum(q, E4M3_MAX)
-    out[nz] = q[nz]
-    return np.copysign(out, y)
+    _, ex = np.frexp(a)                        # a = m * 2^ex with m in [0.5, 1): floor(log2 a) = ex - 1
+    step = np.ldexp(1.0, np.maximum(ex - 1, E4M3_MIN_NORMAL_EXP) - E4M3_MANT_BITS)
+    q = np.minimum(np.rint(a / step) * step, E4M3_MAX)
+    return np.copysign(q, y)
 
 
 def e4m3_encode(q: np.ndarray) -> np.ndarray:
-    """Bit pattern (uint8) of E4M3 values q (already on the E4M3 grid)."""
+    """Bit pattern (uint8) of E4M3 values q (already on the E4M3 grid): S.EEEE.MMM with
+    bias 7; exponent field 0 holds the subnormals m * 2^-9."""
     q = np.asarray(q, dtype=np.float64)
-    s = (np.signbit(q)).astype(np.uint8) << 7
     a = np.abs(q)
-    code = np.zeros(a.shape, dtype=np.uint8)
-    sub = (a > 0) & (a < 2.0 ** E4M3_MIN_NORMAL_EXP)
-    code[sub] = np.rint(a[sub] / 2.0 ** -9).astype(np.uint8)
-    nrm = a >= 2.0 ** E4M3_MIN_NORMAL_EXP
-    e = np.floor(np.log2(a[nrm]))
-    m = np.rint((a[nrm] / np.exp2(e) - 1.0) * 8).astype(np.int64)
-    code[nrm] = ((e.astype(np.int64) + 7) << 3 | m).astype(np.uint8)
-    return code | s
+    _, ex = np.frexp(a)
+    e = ex - 1
+    normal = a >= 2.0 ** E4M3_MIN_NORMAL_EXP
+    code_norm = ((e + 7) << 3) + np.rint((np.ldexp(a, -e) - 1.0) * 8).astype(np.int64)
+    code_sub = np.rint(a / 2.0 ** -9).astype(np.int64)
+    code = np.where(normal, code_norm, code_sub).astype(np.uint8)
+    return code | (np.signbit(q).astype(np.uint8) << 7)
 
 
 def e4m3_decode(code: np.ndarray) -> np.ndarray:
@@ -87,11 +78,9 @@ def e4m3_decode(code: np.ndarray) -> np.ndarray:
 def block_scale_code(amax: np.ndarray) -> np.ndarray:
     """E8M0 code of the shared scale of blocks with max magnitude amax (0 -> code 0)."""
     amax = np.asarray(amax, dtype=np.float64)
-    code = np.zeros(amax.shape, dtype=np.int64)
-    nz = amax > 0
-    e = np.floor(np.log2(amax[nz])) - E4M3_EMAX
-    code[nz] = np.clip(e + 127, 0, 254).astype(np.int64)
-    return code.astype(np.uint8)
+    _, ex = np.frexp(amax)
+    code = np.clip(ex - 1 - E4M3_EMAX + 127, 0, 254)
+    return np.where(amax > 0, code, 0).astype(np.uint8)
 
 
 def quantize(x: np.ndarray):
@@ -102,14 +91,24 @@ def quantize(x: np.ndarray):
     K = x.shape[-1]
     if K % BLOCK:
         raise ValueError("K must be a multiple of 32")
-    xb = x.reshape(*x.shape[:-1], K // BLOCK, BLOCK)
-    sc = block_scale_code(np.abs(xb).max(axis=-1))
-    scale = np.exp2(sc.astype(np.float64) - 127.0)[..., None]
-    zero = (np.abs(xb).max(axis=-1) == 0)[..., None]
-    q = np.where(zero, 0.0, e4m3_round(xb / scale))
-    codes = e4m3_encode(q).reshape(x.shape)
-    deq = (q * np.where(zero, 0.0, scale)).reshape(x.shape)
-    return codes, sc, deq
+    lead = x.shape[:-1]
+    rows = x.reshape(-1, K)
+    codes = np.empty(rows.shape, dtype=np.uint8)
+    sc = np.empty((rows.shape[0], K // BLOCK), dtype=np.uint8)
+    deq = np.empty(rows.shape, dtype=np.float64)
+    # every block is independent; rows go through in groups only to keep temporaries small
+    step = max(1, (1 << 20) // K)
+    for r0 in range(0, rows.shape[0], step):
+        xb = rows[r0:r0 + step].reshape(-1, K // BLOCK, BLOCK)
+        amax = np.abs(xb).max(axis=-1)
+        s = block_scale_code(amax)
+        scale = np.ldexp(1.0, s.astype(np.int64) - 127)[..., None]
+        q = np.where((amax == 0)[..., None], 0.0, e4m3_round(xb / scale))
+        n = xb.shape[0]
+        codes[r0:r0 + n] = e4m3_encode(q).reshape(n, K)
+        sc[r0:r0 + n] = s
+        deq[r0:r0 + n] = (q * scale).reshape(n, K)
+    return codes.reshape(x.shape), sc.reshape(*lead, K // BLOCK), deq.reshape(x.shape)
 
 
 def dequantize(codes: np.ndarray, scale_codes: np.ndarray) -> np.ndarray:

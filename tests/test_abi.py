@@ -68,7 +68,8 @@ def test_max_pairs_and_workspace():
     (dict(), 0, -1),
     (dict(), 300, -1),
     (dict(dtype=7), 32, -1),
-    (dict(dtype=moe.MOE_MXFP8), 32, -6),
+    (dict(dtype=moe.MOE_MXFP8, d=7168 + 64), 32, -2),   # MXFP8 GEMM stage needs d % 128 == 0
+    (dict(dtype=moe.MOE_MXFP8, F=2048 + 64), 32, -2),
     (dict(d=7160), 32, -2),                         # bf16 K step needs d % 64 == 0
     (dict(F=2000), 32, -2),
     (dict(d=130, dtype=moe.MOE_F32), 32, -2),       # fp32 row of 520 B is not 16-byte aligned
@@ -100,16 +101,16 @@ def test_null_and_misaligned_pointers_rejected():
     # misaligned rank pointer / workspace / row buffer
     tab3 = (ctypes.c_void_p * 8)(*([FAKE] * 7 + [FAKE + 4]))
     assert L.moe_dispatch_pull(ctypes.byref(s), ctypes.byref(p), ctypes.cast(tab3, ctypes.c_void_p), FAKE,
-                               FAKE, FAKE, FAKE, big, None) == -2
+                               FAKE, FAKE, None, FAKE, big, None) == -2
     assert L.moe_layout(ctypes.byref(s), ctypes.byref(p), None, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                         FAKE + 64, big, None) == -2
-    assert L.moe_dispatch_pull(ctypes.byref(s), ctypes.byref(p), tabp, FAKE, FAKE, FAKE + 8, FAKE, big,
+    assert L.moe_dispatch_pull(ctypes.byref(s), ctypes.byref(p), tabp, FAKE, FAKE, FAKE + 8, None, FAKE, big,
                                None) == -2
     # workspace too small
     assert L.moe_layout(ctypes.byref(s), ctypes.byref(p), None, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                         FAKE, 1024, None) == -3
-    assert L.moe_expert_ffn(ctypes.byref(s), ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                            FAKE, 1024, None) == -3
+    assert L.moe_expert_ffn(ctypes.byref(s), ctypes.byref(p), None, FAKE, None, FAKE, FAKE, FAKE, FAKE, None,
+                            FAKE, FAKE, 1024, None) == -3
     assert L.moe_combine_push(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, tabp, None,
                               FAKE, big, None) == -1
     # negative minibatch
@@ -125,9 +126,53 @@ def test_forward_checks_every_stage_before_launching():
     tab = (ctypes.c_void_p * 8)(*([FAKE] * 8))
     tabp = ctypes.cast(tab, ctypes.c_void_p)
     # y table missing: must fail up front, not after launching the layout
-    rc = L.moe_forward(ctypes.byref(s), ctypes.byref(p), None, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE,
-                       tabp, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    rc = L.moe_forward(ctypes.byref(s), ctypes.byref(p), None, tabp, tabp, FAKE, FAKE, FAKE, None, FAKE, None,
+                       FAKE, tabp, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
     assert rc == -1
+
+
+def test_mx_quantize_rejects_bad_arguments_before_launch():
+    L = moe.lib()
+    q = L.moe_mx_quantize
+    assert q(FAKE, moe.MOE_MXFP8, 4, 64, FAKE, FAKE, None) == -1        # source must be bf16 or fp32
+    assert q(FAKE, moe.MOE_BF16, -1, 64, FAKE, FAKE, None) == -1
+    assert q(FAKE, moe.MOE_BF16, 4, 0, FAKE, FAKE, None) == -1
+    assert q(FAKE, moe.MOE_BF16, 4, 48, FAKE, FAKE, None) == -2         # K % 32
+    assert q(None, moe.MOE_BF16, 4, 64, FAKE, FAKE, None) == -1
+    assert q(FAKE, moe.MOE_BF16, 4, 64, FAKE, None, None) == -1
+    assert q(FAKE + 8, moe.MOE_BF16, 4, 64, FAKE, FAKE, None) == -2
+    assert q(FAKE, moe.MOE_F32, 4, 64, FAKE + 4, FAKE, None) == -2
+    assert q(FAKE, moe.MOE_BF16, 0, 64, FAKE, FAKE, None) == 0          # nothing to do, nothing launched
+
+
+def test_mx_entry_points_need_their_scales():
+    L = moe.lib()
+    s, p = _shape(dtype=moe.MOE_MXFP8), _pl()
+    tab = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    tabp = ctypes.cast(tab, ctypes.c_void_p)
+    big = 1 << 40
+    ws = moe.moe_workspace_bytes(s, p)
+    assert 0 < ws < moe.moe_workspace_bytes(_shape(), p)                # h is one byte per value
+    ok = moe.MXScales(FAKE, FAKE, FAKE)
+    assert L.moe_dispatch_pull(ctypes.byref(s), ctypes.byref(p), tabp, FAKE, FAKE, FAKE, None, FAKE, big,
+                               None) == -1
+    assert L.moe_dispatch_pull(ctypes.byref(s), ctypes.byref(p), tabp, FAKE, FAKE, FAKE, FAKE + 2, FAKE, big,
+                               None) == -2
+
+    def ffn(xs, wsc):
+        return L.moe_expert_ffn(ctypes.byref(s), ctypes.byref(p), None, FAKE, xs, FAKE, FAKE, FAKE, FAKE,
+                                ctypes.byref(wsc) if wsc is not None else None, FAKE, FAKE, 1024, None)
+    assert ffn(FAKE, None) == -1
+    assert ffn(None, ok) == -1
+    assert ffn(FAKE, moe.MXScales(FAKE, None, FAKE)) == -1
+    assert ffn(FAKE, moe.MXScales(FAKE, FAKE, FAKE + 1)) == -2
+    assert ffn(FAKE, ok) == -3                                          # then the workspace check
+    rc = L.moe_forward(ctypes.byref(s), ctypes.byref(p), None, tabp, tabp, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                       FAKE, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None)
+    assert rc == -1
+    # the persistent path is bf16 only
+    assert L.moe_forward_persistent(ctypes.byref(s), ctypes.byref(p), None, tabp, tabp, FAKE, FAKE, FAKE, FAKE,
+                                    big, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == -6
 
 
 def test_persistent_entry_rejects_bad_arguments_before_launch():

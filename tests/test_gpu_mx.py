@@ -1,0 +1,257 @@
+"""GPU parity of the MXFP8 path against the oracle's MX codec and quantised forward.
+
+Bar: codes and scale codes bit-exact (moe_mx_quantize over every bf16 value and over
+fp32 values on and next to every rounding midpoint; the quantise-on-gather of
+moe_dispatch_pull; the offline weight codes); layout bit-exact; outputs against
+Oracle-Q, the fp64 forward on the dequantised operands: max row-relative error <= 6e-2
+(the stated MXFP8 bound) and relative Frobenius error <= 5e-3; rows with no local expert
+exactly 0.
+
+Why two bars: h is quantised from fp32 on the GPU and from fp64 in the oracle, so a few
+of its rounding decisions differ (the fp32 h carries ~1e-6 relative error); one flipped
+element moves a whole output row by up to one E4M3 step of its block (about 2^-3 of the
+block maximum) times a W2 column, 1-3 % of the row maximum in the worst row at these
+widths.  Such flips are rare, so over all rows they add ~5e-4 (relative Frobenius) to the
+~1.6e-3 of the two bf16 roundings (ye and y); a systematic slip (a wrong rounding mode, a
+misplaced scale) moves the Frobenius figure by percent.  The distance to the unquantised
+fp64 forward is printed for information: E4M3's 3 mantissa bits alone put it near 8 %.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from oracle import mx_oracle as MX
+from mixture_experts_layer_histogram_amd import configs, inputs, moe
+
+pytestmark = pytest.mark.gpu
+
+TOL_Q_ROW = 6e-2
+TOL_Q_FRO = 5e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _row_rel_err(yg, yr, has):
+    num = np.abs(yg - yr).max(axis=-1)
+    den = np.abs(yr).max(axis=-1)
+    return float((num[has] / np.maximum(den[has], 1e-30)).max()) if has.any() else 0.0
+
+
+def _fro_rel_err(yg, yr, has):
+    return float(np.linalg.norm(yg[has] - yr[has]) / max(np.linalg.norm(yr[has]), 1e-300))
+
+
+def _gpu_quantize(vals_f32, K, src="bf16"):
+    """moe_mx_quantize on rows of K values; returns (codes, scales) as numpy uint8."""
+    torch = _torch()
+    dev = torch.device("cuda:0")
+    rows = vals_f32.size // K
+    if src == "bf16":
+        bits = inputs.f32_to_bf16_bits(vals_f32.reshape(rows, K))
+        t = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        code = moe.MOE_BF16
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(vals_f32.reshape(rows, K), dtype=np.float32)).to(dev)
+        code = moe.MOE_F32
+    q = torch.full((rows, K), 0x55, dtype=torch.uint8, device=dev)
+    s = torch.full((rows, K // 32), 0x55, dtype=torch.uint8, device=dev)
+    moe.moe_mx_quantize(t, code, rows, K, q, s)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def _all_bf16_values():
+    p = np.arange(65536, dtype=np.uint32)
+    v = (p << 16).view(np.float32).copy()
+    v[~np.isfinite(v)] = 0.0
+    return v
+
+
+# --------------------------------------------------------------------------- codec
+@pytest.mark.parametrize("order", ["natural", "shuffled", "shuffled-moderate"])
+def test_mx_quantize_every_bf16_value(order):
+    _say(f"[mx-codec] every bf16 value, {order} blocks")
+    v = _all_bf16_values()
+    if order == "shuffled":
+        v = v[np.random.default_rng(1).permutation(v.size)]
+    elif order == "shuffled-moderate":
+        # blocks of 32 neighbouring magnitudes (sorted), in shuffled block order: most
+        # elements land on normal E4M3 codes instead of underflowing next to a large one
+        mag = np.abs(v)
+        v = v[np.argsort(mag, kind="stable")]
+        blocks = v.reshape(-1, 32)
+        blocks = blocks[np.random.default_rng(2).permutation(len(blocks))]
+        v = blocks.reshape(-1)
+    codes, scales = _gpu_quantize(v, 4096, "bf16")
+    rc, rs, _ = MX.quantize(v.astype(np.float64).reshape(-1, 4096))
+    assert np.array_equal(scales, rs)
+    bad = np.argwhere(codes != rc)
+    assert len(bad) == 0, (bad[:5], v.reshape(-1, 4096)[tuple(bad[0])] if len(bad) else None)
+
+
+def test_mx_quantize_f32_midpoints_and_neighbours():
+    """fp32 values exactly on, just below and just above every E4M3 rounding midpoint
+    (the h path quantises fp32 values), at several block scales, plus saturating ones."""
+    _say("[mx-codec] fp32 midpoints")
+    grid = np.sort(np.unique(np.abs(MX.e4m3_decode(np.arange(0, 127, dtype=np.uint8)))))
+    mids = (grid[:-1] + grid[1:]) / 2                      # 126 midpoints, exact in fp32
+    base = np.concatenate([mids, np.nextafter(mids.astype(np.float32), np.float32(0)).astype(np.float64),
+                           np.nextafter(mids.astype(np.float32), np.float32(1e9)).astype(np.float64),
+                           grid, [449.0, 463.99, 464.0, 470.0, 500.0, 511.9]])
+    rng = np.random.default_rng(3)
+    blocks = []
+    for e in (-20, -3, 0, 7, 40):
+        b = np.array(base)
+        rng.shuffle(b)
+        b = b[: (len(b) // 31) * 31].reshape(-1, 31)
+        # one element per block fixes amax in [256, 512) * 2^e: the scale is exactly 2^e
+        lead = np.full((len(b), 1), 256.0 + 16.0 * rng.integers(0, 16))
+        blk = np.concatenate([lead, b], axis=1) * 2.0 ** e
+        blk *= np.where(rng.random(blk.shape) < 0.5, -1.0, 1.0)
+        blocks.append(blk)
+    v = np.concatenate(blocks).astype(np.float32)
+    pad = (-v.shape[0]) % 4
+    v = np.concatenate([v, np.zeros((pad, 32), np.float32)]).reshape(-1, 128)
+    codes, scales = _gpu_quantize(v, 128, "f32")
+    rc, rs, _ = MX.quantize(v.astype(np.float64))
+    assert np.array_equal(scales, rs)
+    assert np.array_equal(codes, rc)
+
+
+# --------------------------------------------------------------------------- path
+def _problem(cfg, seed=0):
+    from mixture_experts_layer_histogram_amd.device import DeviceProblem
+    inp = inputs.make_inputs(cfg, seed=seed)
+    return inp, DeviceProblem(cfg, inp)
+
+
+def _oracle_weights(inp, experts):
+    """Oracle MX codes, scale codes and dequantised values of the listed local experts
+    (one thread per matrix; NumPy releases the GIL in its loops)."""
+    from concurrent.futures import ThreadPoolExecutor
+    src = (inp.w1_f32, inp.w3_f32, inp.w2_f32)
+    jobs = [(l, i) for l in experts for i in range(3)]
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        res = list(ex.map(lambda j: MX.quantize(np.asarray(src[j[1]][j[0]], dtype=np.float64)), jobs))
+    out = {}
+    for (l, i), r in zip(jobs, res):
+        out.setdefault(l, [None] * 3)[i] = r
+    return out
+
+
+MX_SMALL = configs.DSV3_MX.scaled(name="mx-small R2 T600 d1024 E16/8 k4 F512", R=2, T=600, d=1024, E=16,
+                                  E_local=8, k=4, F=512)
+MX_SLICE = configs.DSV3_MX.scaled(name="mx-dsv3-slice R2 T256 d7168 E64/4 k8 F2048", R=2, T=256, E=64,
+                                  E_local=4)
+MX_SKEW = configs.DSV3_MX.scaled(name="mx-slice-zipf R2 T512 d1024 E64/8 k8 F768", R=2, T=512, d=1024, E=64,
+                                 E_local=8, F=768, load="skew")
+MX_CASES = {"mx-small": MX_SMALL, "mx-dsv3-slice": MX_SLICE, "mx-slice-zipf": MX_SKEW}
+
+
+@pytest.mark.parametrize("name", list(MX_CASES))
+def test_mx_forward_parity(name):
+    torch = _torch()
+    cfg = MX_CASES[name]
+    _say(f"[mx-forward] {cfg.name}")
+    inp, P = _problem(cfg)
+    P.forward()
+    assert P.status() == 0
+    torch.cuda.synchronize()
+    qw = _oracle_weights(inp, range(cfg.E_local))
+    # offline weight quantisation: bit-exact codes and scales
+    for l in range(cfg.E_local):
+        for i in range(3):
+            assert np.array_equal(P.wq[i][l].cpu().numpy(), qw[l][i][0]), (l, i)
+            assert np.array_equal(P.ws_codes[i][l].cpu().numpy(), qw[l][i][1]), (l, i)
+    wq = [[qw[l][i][2] for l in range(cfg.E_local)] for i in range(3)]
+    ref = MX.forward_q(inp.logits, inp.x_f32, *wq, inp.expert_to_local, cfg.E_local, cfg.k)
+    N = ref["N"]
+    np.testing.assert_array_equal(P.offsets.cpu().numpy(), ref["offsets"])
+    np.testing.assert_array_equal(P.pull_src[:N].cpu().numpy(), ref["pull_src"])
+    np.testing.assert_array_equal(P.slot_of.cpu().numpy(), ref["slot_of"])
+    # quantise-on-gather: codes and scales bit-exact
+    xc, xs, _ = MX.quantize(O.dispatch(inp.x_f32, ref["pull_src"]))
+    assert np.array_equal(P.xe[:N].cpu().numpy(), xc)
+    assert np.array_equal(P.xe_scales[:N].cpu().numpy(), xs)
+    ye = P.rows_f64(P.ye[:N])
+    allr = np.ones(N, dtype=bool)
+    err_ffn, fro_ffn = _row_rel_err(ye, ref["ye"], allr), _fro_rel_err(ye, ref["ye"], allr)
+    so = ref["slot_of"]
+    y = np.stack([P.rows_f64(P.y[r]) for r in range(cfg.R)])
+    has = (so >= 0).any(-1)
+    err = _row_rel_err(y.reshape(-1, cfg.d), ref["y"].reshape(-1, cfg.d), has.reshape(-1))
+    fro_y = _fro_rel_err(y.reshape(-1, cfg.d), ref["y"].reshape(-1, cfg.d), has.reshape(-1))
+    exact = O.forward(inp.logits, inp.x_f32, inp.w1_f32, inp.w3_f32, inp.w2_f32, inp.expert_to_local,
+                      cfg.E_local, cfg.k)["y"]
+    live = has.reshape(-1)
+    yl, el = y.reshape(-1, cfg.d)[live], exact.reshape(-1, cfg.d)[live]
+    fro = float(np.linalg.norm(yl - el) / np.linalg.norm(el))
+    _say(f"  N={N} vs Oracle-Q: ffn row={err_ffn:.3e} fro={fro_ffn:.3e}; y row={err:.3e} fro={fro_y:.3e} "
+         f"(vs unquantised: fro={fro:.3e} row={_row_rel_err(y.reshape(-1, cfg.d), exact.reshape(-1, cfg.d), live):.3e})")
+    assert err_ffn <= TOL_Q_ROW and fro_ffn <= TOL_Q_FRO
+    assert err <= TOL_Q_ROW and fro_y <= TOL_Q_FRO
+    assert (y[~has] == 0).all()
+
+
+def test_mx_forward_deterministic_and_stagewise_equals_fused_call():
+    torch = _torch()
+    cfg = MX_SKEW
+    _say(f"[mx-determinism] {cfg.name}")
+    inp, P = _problem(cfg, seed=1)
+    P.forward()
+    y1 = [t.clone() for t in P.y]
+    P.layout()
+    P.dispatch()
+    P.ffn()
+    P.combine()
+    torch.cuda.synchronize()
+    for a, b in zip(y1, P.y):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.slow
+def test_mx_forward_full_dsv3_sampled():
+    """Full DeepSeek-V3-shaped share in MXFP8 in the launch configuration the bench
+    times: layout compared whole; sampled tokens (those whose local experts are among the
+    first six, so the oracle quantises six experts' weights) computed one by one."""
+    torch = _torch()
+    cfg = configs.DSV3_MX
+    _say(f"[mx-forward-full] {cfg.name}")
+    inp, P = _problem(cfg)
+    P.forward()
+    assert P.status() == 0
+    torch.cuda.synchronize()
+    idx, g = O.route(inp.logits, cfg.k)
+    lay = O.layout(idx, inp.expert_to_local, cfg.E_local)
+    np.testing.assert_array_equal(P.offsets.cpu().numpy(), lay["offsets"])
+    np.testing.assert_array_equal(P.slot_of.cpu().numpy(), lay["slot_of"])
+    np.testing.assert_array_equal(P.pull_src[:lay["N"]].cpu().numpy(), lay["pull_src"])
+    loc = inp.expert_to_local[idx]                       # [R][T][k] local id or -1
+    has = (loc >= 0).any(-1)
+    ok = has & np.where(loc >= 0, loc < 6, True).all(-1)
+    cand = np.argwhere(ok)
+    pick = cand[np.random.default_rng(0).choice(len(cand), 24, replace=False)]
+    qw = _oracle_weights(inp, range(6))
+    for l in range(6):
+        assert np.array_equal(P.wq[0][l].cpu().numpy(), qw[l][0][0])
+        assert np.array_equal(P.ws_codes[2][l].cpu().numpy(), qw[l][2][1])
+    wq = [[qw[l][i][2] if l < 6 else None for l in range(cfg.E_local)] for i in range(3)]
+    yr = np.stack([MX.token_output_q(inp.x_f32[r, t], idx[r, t], g[r, t], inp.expert_to_local, *wq)
+                   for r, t in pick])
+    yg = np.stack([P.y[r][t].float().cpu().numpy().astype(np.float64) for r, t in pick])
+    allr = np.ones(len(pick), dtype=bool)
+    worst, fro = _row_rel_err(yg, yr, allr), _fro_rel_err(yg, yr, allr)
+    zr, zt = np.argwhere(~has)[0]
+    assert (P.y[zr][zt].float().cpu().numpy() == 0).all()
+    _say(f"  N={lay['N']} sampled vs Oracle-Q: row={worst:.3e} fro={fro:.3e}")
+    assert worst <= TOL_Q_ROW and fro <= TOL_Q_FRO
