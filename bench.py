@@ -27,8 +27,14 @@ PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
 PEAK_FP8_FLOPS = 5.0e15      # MI355X dense fp8 / MXFP8 MFMA
 PEAK_F32_FLOPS = 157.3e12    # MI355X fp32 matrix
 PEAK_HBM = 8.0e12            # MI355X HBM3E bytes/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_grouped_gemm_dsv3.json")
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_histogram_amd", "csrc", "gemm.hip")
+CSRC = os.path.join(ROOT, "mixture_experts_layer_histogram_amd", "csrc")
+# per workload: committed traffic record, GEMM kernel name, and the sources the kernels are built from
+TRAFFIC = {
+    "dsv3": ("traffic_grouped_gemm_dsv3_bf16.json", "grouped_gemm_bf16_kernel",
+             ("gemm.hip", "gemm_tile.hpp", "common.hpp")),
+    "dsv3_mx": ("traffic_grouped_gemm_dsv3_mxfp8.json", "grouped_gemm_mx_kernel",
+                ("gemm_mx.hip", "gemm_tile.hpp", "mx.hpp", "common.hpp")),
+}
 
 
 def log(msg):
@@ -43,31 +49,36 @@ def parse():
     ap.add_argument("--config", default="dsv3", choices=sorted(configs.CONFIGS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-ranks", type=int, default=0,
-                    help="0 = all ranks (the whole step)")
+    ap.add_argument("--cpu-sample-ranks", type=int, default=0, help="0 = all ranks (the whole step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run three plain 1 GiB device copies (counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) "
-                         "into the committed traffic record, then exit")
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of "
+                         "this --config into its committed traffic record, then exit")
     return ap.parse_args()
 
 
-def gemm_source_sha() -> str:
-    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+def gemm_source_sha(config) -> str:
+    h = hashlib.sha256()
+    for f in TRAFFIC[config][2]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
-def traffic_bytes(cfg):
-    """HBM bytes per FFN launch pair of the bf16 DeepSeek-V3 share from the committed
-    rocprofv3 counter runs, or None for another workload or when the GEMM source has
-    changed since they were taken."""
-    if cfg.name != configs.DSV3.name:
+def traffic_file(config):
+    return os.path.join(ROOT, "profiles", TRAFFIC[config][0])
+
+
+def traffic_bytes(config):
+    """HBM bytes per FFN launch pair of this workload from the committed rocprofv3 counter
+    runs, or None when there is none or the GEMM sources changed since they were taken."""
+    if config not in TRAFFIC:
         return None
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(traffic_file(config)))
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha") != gemm_source_sha():
+    if rec.get("source_sha") != gemm_source_sha(config):
         return None
     return rec.get("bytes_per_step")
 
@@ -84,10 +95,11 @@ def _per_dispatch(csv_path, counter):
     return out
 
 
-def write_traffic(fetch_csv, write_csv):
+def write_traffic(config, fetch_csv, write_csv):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the two FFN GEMM kernels, each scaled
     by (known bytes / counter) of a plain 1 GiB device copy in the same run."""
-    rec = {"source_sha": gemm_source_sha()}
+    kname = TRAFFIC[config][1]
+    rec = {"workload": configs.CONFIGS[config].name, "source_sha": gemm_source_sha(config)}
     for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = _per_dispatch(path, counter)
         cal = [v for k, v in rows if "copyBuffer" in k and 0.5 * CAL_BYTES < v < 2.0 * CAL_BYTES]
@@ -96,13 +108,13 @@ def write_traffic(fetch_csv, write_csv):
         factor = CAL_BYTES / float(np.median(cal))
         g = {}
         for mode in (0, 1):
-            vals = [v for k, v in rows if f"grouped_gemm_bf16_kernel<{mode}>" in k]
+            vals = [v for k, v in rows if f"{kname}<{mode}>" in k]
             g[mode] = float(np.median(vals)) * factor
         rec[name] = {"copy_factor": factor, "gemm1_bytes": g[0], "gemm2_bytes": g[1]}
     rec["bytes_per_step"] = (rec["fetch"]["gemm1_bytes"] + rec["fetch"]["gemm2_bytes"] +
                              rec["write"]["gemm1_bytes"] + rec["write"]["gemm2_bytes"])
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+    os.makedirs(os.path.dirname(traffic_file(config)), exist_ok=True)
+    json.dump(rec, open(traffic_file(config), "w"), indent=1)
     print(json.dumps(rec))
 
 
@@ -155,7 +167,7 @@ def cpu_baseline(cfg, inp, ranks):
 def main():
     args = parse()
     if args.write_traffic:
-        write_traffic(*args.write_traffic)
+        write_traffic(args.config, *args.write_traffic)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -227,7 +239,7 @@ def main():
     merge_bytes = 1.0 * N * row + cfg.R * cfg.T * row
     tokens = cfg.R * cfg.T / cfg.G
     value = tokens / (ms_step * 1e-3)
-    traffic = traffic_bytes(cfg)
+    traffic = traffic_bytes(args.config)
     result = {
         "metric": METRIC,
         "value": value,
