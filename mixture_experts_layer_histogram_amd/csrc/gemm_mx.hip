@@ -38,15 +38,6 @@ __device__ __forceinline__ i32x8 ld_frag(const char* s, int row, int c0) {
   return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
 }
 
-// max over the 32 lanes of each wave half, by XOR swizzles (bit-mask mode of ds_swizzle)
-__device__ __forceinline__ uint32_t half_max(uint32_t m) {
-  m = max(m, uint32_t(__builtin_amdgcn_ds_swizzle(int(m), (1 << 10) | 0x1F)));
-  m = max(m, uint32_t(__builtin_amdgcn_ds_swizzle(int(m), (2 << 10) | 0x1F)));
-  m = max(m, uint32_t(__builtin_amdgcn_ds_swizzle(int(m), (4 << 10) | 0x1F)));
-  m = max(m, uint32_t(__builtin_amdgcn_ds_swizzle(int(m), (8 << 10) | 0x1F)));
-  return max(m, uint32_t(__builtin_amdgcn_ds_swizzle(int(m), (16 << 10) | 0x1F)));
-}
-
 // b0/b1: this expert's weight codes ([Nout][K]); bs0/bs1 their scales ([Nout][K/32]).
 template <int MODE>
 __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __restrict__ b0,
@@ -147,51 +138,83 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
     __syncthreads();                    // ... and everyone's
   }
 
-  // epilogue: lane holds column r32 and rows 8*(e/4) + 4*hi + e%4 of each 32x32 block
+  // Epilogue through LDS (the stages are free after the last barrier).  Each wave writes
+  // its results into a row-major tile whose rows are padded by 16 bytes; the lane layout of
+  // the accumulators is column r32, rows 8*(e/4) + 4*hi + e%4 of each 32x32 block.
+  //  MODE 0: the fp32 h tile [256][128]; then every thread quantises whole 32-value blocks
+  //          of it on its own and writes 32 code bytes as two 16-byte vectors plus the scale.
+  //  MODE 1: the bf16 output tile [256][256]; then 16-byte row segments go to global memory.
+  constexpr int kPitch = 528;                                   // 512 bytes of data + 16
+  static_assert(kGemmBM * kPitch <= kMxLds, "staged tile exceeds the LDS stages");
+  char* ot = smem;
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int rb = wm * 64 + m * 32;
     if (MODE == 0) {
-      uint8_t* hq = static_cast<uint8_t*>(io.o) + size_t(rb) * Nout;
-      uint8_t* hs = io.os + size_t(rb) * (Nout / kMxBlock);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int f0 = c0 + (wn * 2 + q) * 32;      // this 32-value block of h (inside [0, Nout))
-        float h[16];
-        uint32_t mx[16];
+        const int fc = (wn * 2 + q) * 32 + r32;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          h[e] = silu_f32(acc[m][2 * q][e]) * acc[m][2 * q + 1][e];
-          mx[e] = half_max(__float_as_uint(h[e]) & 0x7FFFFFFFu);
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = 8 * (e >> 2) + 4 * hi + (e & 3);
-          if (rb + row < rows) {
-            uint32_t code = 0, sc = 0;
-            if (mx[e] != 0) {
-              const int ex = mx_block_exp(mx[e]);
-              code = mx_code1(h[e], mx_inv_scale(ex));
-              sc = uint32_t(ex + 127);
-            }
-            hq[size_t(row) * Nout + f0 + r32] = uint8_t(code);
-            if (r32 == 0) hs[size_t(row) * (Nout / kMxBlock) + f0 / kMxBlock] = uint8_t(sc);
-          }
+          const int row = rb + 8 * (e >> 2) + 4 * hi + (e & 3);
+          *reinterpret_cast<float*>(ot + row * kPitch + fc * 4) = silu_f32(acc[m][2 * q][e]) * acc[m][2 * q + 1][e];
         }
       }
     } else {
-      uint16_t* orow = static_cast<uint16_t*>(io.o) + size_t(rb) * Nout;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const int col = c0 + wn * 128 + n * 32 + r32;
+        const int cc = wn * 128 + n * 32 + r32;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int row = 8 * (e >> 2) + 4 * hi + (e & 3);
-          if (rb + row < rows && col < Nout) orow[size_t(row) * Nout + col] = f32_to_bf16(acc[m][n][e]);
+          const int row = rb + 8 * (e >> 2) + 4 * hi + (e & 3);
+          *reinterpret_cast<uint16_t*>(ot + row * kPitch + cc * 2) = f32_to_bf16(acc[m][n][e]);
         }
       }
     }
   }
+  __syncthreads();
+  if (MODE == 0) {
+    uint8_t* hq = static_cast<uint8_t*>(io.o);
+    for (int b = tid; b < kGemmBM * 4; b += kGemmThreads) {    // 4 blocks of 32 f per row
+      const int row = b >> 2, blk = b & 3;
+      if (row >= rows) continue;
+      const f32x4* src = reinterpret_cast<const f32x4*>(ot + row * kPitch + blk * 128);
+      f32x4 v[8];
+      uint32_t mx = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[i] = src[i];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) mx = max(mx, __float_as_uint(v[i][w]) & 0x7FFFFFFFu);
+      }
+      u32x4 c0v = {0, 0, 0, 0}, c1v = {0, 0, 0, 0};
+      uint32_t sc = 0;
+      if (mx != 0) {
+        const int ex = mx_block_exp(mx);
+        const float inv = mx_inv_scale(ex);
+        sc = uint32_t(ex + 127);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          c0v[w] = mx_pack4(v[w][0], v[w][1], v[w][2], v[w][3], inv);
+          c1v[w] = mx_pack4(v[4 + w][0], v[4 + w][1], v[4 + w][2], v[4 + w][3], inv);
+        }
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(hq + size_t(row) * Nout + c0 + blk * 32);
+      dst[0] = c0v;
+      dst[1] = c1v;
+      io.os[size_t(row) * (Nout / kMxBlock) + (c0 >> 5) + blk] = uint8_t(sc);
+    }
+  } else {
+    uint16_t* orow0 = static_cast<uint16_t*>(io.o);
+    const int ncols = min(kGemmBN, Nout - c0);
+    for (int v = tid; v < kGemmBM * (kGemmBN / 8); v += kGemmThreads) {
+      const int row = v >> 5, cv = v & 31;                   // 32 vectors of 8 bf16 per row
+      if (row < rows && cv * 8 < ncols)
+        *reinterpret_cast<u32x4*>(orow0 + size_t(row) * Nout + c0 + cv * 8) =
+            *reinterpret_cast<const u32x4*>(ot + row * kPitch + cv * 16);
+    }
+  }
+  __syncthreads();     // the next tile's fills reuse the stages
 }
 
 // MODE 0: A = xe codes [*][d], B0/B1 = W1/W3 -> h codes [*][F] + scales   (256 rows x 128 f)

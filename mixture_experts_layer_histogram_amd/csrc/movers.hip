@@ -79,6 +79,9 @@ __global__ __launch_bounds__(256) void combine_push_kernel(const char* __restric
 // A wave task is one column segment (64 * VPL 16-byte vectors) of one token row.  The
 // token's local j are compacted into a mask; for each local j all VPL loads of the
 // segment are issued before any is used, so a task costs one memory round trip per j.
+// Measured on MI355X at the DeepSeek-V3 share: short segments (VPL 4) and a grid of 16
+// blocks per CU keep the most rows in flight (180 us against 199 us for VPL 8 with 4
+// blocks per CU); prefetching the next task's metadata changed less than 1 %.
 template <bool BF16>
 __global__ __launch_bounds__(256) void weighted_merge_kernel(RankPtrs<const char*> recv,
                                                              RankPtrs<char*> y,
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(256) void weighted_merge_kernel(RankPtrs<const char
                                                              const float* __restrict__ topk_w, int R,
                                                              int T, int k, int d) {
   constexpr int EPV = BF16 ? 8 : 4;      // elements per 16-byte vector
-  constexpr int VPL = 8;                 // vectors per lane per segment
+  constexpr int VPL = 4;                 // vectors per lane per segment
   const int lane = threadIdx.x & 63;
   const int row_bytes = d * (BF16 ? 2 : 4);
   const int n16 = row_bytes >> 4;
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(256) void weighted_merge_kernel(RankPtrs<const char
   }
 }
 
-constexpr int kGatherBlocksPerCU = 4, kPushBlocksPerCU = 8, kMergeBlocksPerCU = 4;
+constexpr int kGatherBlocksPerCU = 4, kPushBlocksPerCU = 8, kMergeBlocksPerCU = 16;
 
 hipError_t launch_dispatch(const moe_shape_t& s, const void* const* x, const int32_t* pull_src, char* xe,
                            const int32_t* ctrl, int cus, hipStream_t st) {

@@ -38,10 +38,6 @@ __device__ __forceinline__ uint32_t mx_pack4(float a, float b, float c, float d,
   return uint32_t(r);
 }
 
-__device__ __forceinline__ uint32_t mx_code1(float a, float inv) {
-  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(mx_clamp(a * inv), 0.0f, 0, false)) & 0xFFu;
-}
-
 // Max over the 4 lanes of an aligned lane quad (the 4 lanes holding one 32-value block).
 __device__ __forceinline__ uint32_t quad_max(uint32_t m) {
   m = max(m, uint32_t(__shfl_xor(int(m), 1)));
