@@ -77,14 +77,21 @@ typedef struct {
   int32_t E_local;
 } moe_placement_t;
 
-/* Block scales of MXFP8 expert weights (moe_mx_quantize of the bf16 weights), DEVICE
- * pointers of E8M0 codes, 4-byte aligned.  Used only when dtype is MOE_MXFP8, where the
- * weight pointers w1, w3, w2 hold E4M3 codes of the same [E_local][F][d] / [E_local][d][F]
- * shapes (one byte per value). */
+/* MXFP8 scale layout (every scale array below): for a matrix of `rows` rows of K values
+ * (K a multiple of 128), the E8M0 code of 32-value block b of row r is the byte at offset
+ *     4 * (rows * (b / 4) + r) + b % 4,
+ * i.e. one 32-bit word per (128-value K tile, row), K tiles outermost: [K/128][rows][4].
+ * The grouped GEMM reads the words of 64 consecutive rows of one K tile at once.
+ *
+ * Block scales of MXFP8 expert weights (moe_mx_quantize of the bf16 weights), DEVICE
+ * pointers, 4-byte aligned.  Used only when dtype is MOE_MXFP8, where the weight pointers
+ * w1, w3, w2 hold E4M3 codes of the same [E_local][F][d] / [E_local][d][F] shapes (one byte
+ * per value); each scale array covers the whole tensor as one matrix of E_local*F (or
+ * E_local*d) rows. */
 typedef struct {
-  const uint8_t* w1;   /* [E_local][F][d/32] */
-  const uint8_t* w3;   /* [E_local][F][d/32] */
-  const uint8_t* w2;   /* [E_local][d][F/32] */
+  const uint8_t* w1;   /* [d/128][E_local*F][4] */
+  const uint8_t* w3;   /* [d/128][E_local*F][4] */
+  const uint8_t* w2;   /* [F/128][E_local*d][4] */
 } moe_mx_scales_t;
 
 /* Execution knobs.  Zero selects the default of each field. */
@@ -114,7 +121,8 @@ size_t moe_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p, const
  *   otherwise e = clamp(floor(log2 amax) - 8, -127, 127), scale code e + 127, and
  *   code_i = E4M3(v_i / 2^e) rounded to nearest (ties to even), saturated to +-448.
  * src: [rows][K] of src_dtype (MOE_BF16 or MOE_F32), 16-byte aligned; codes: [rows][K]
- * bytes, 16-byte aligned; scales: [rows][K/32] bytes.  K % 32 == 0 (else MOE_EALIGN).
+ * bytes, 16-byte aligned; scales: rows*K/32 bytes in the MXFP8 scale layout above
+ * ([K/128][rows][4]).  K % 128 == 0 (else MOE_EALIGN).
  * Used offline on expert weights; moe_dispatch_pull and the GEMM1 epilogue apply the
  * same rule to token rows and h.  Bit-exact (integer decisions, exact power-of-two
  * scaling).
@@ -157,7 +165,8 @@ int moe_layout(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t*
  * offsets/ws: from moe_layout (N is read on the device).  Bit-exact copy.
  * MOE_MXFP8 [kucoin §02: quantisation fused into the dispatch]: x is bf16 and each row
  * is quantised on its way (the moe_mx_quantize rule): xe receives [moe_max_pairs][d]
- * E4M3 codes and xe_scales [moe_max_pairs][d/32] scale codes (4-byte aligned).
+ * E4M3 codes and xe_scales their scale codes in the MXFP8 scale layout with
+ * rows = moe_max_pairs ([d/128][moe_max_pairs][4], 4-byte aligned).
  * xe_scales is ignored for the other dtypes.
  */
 int moe_dispatch_pull(const moe_shape_t* s, const moe_placement_t* p, const void* const* x,

@@ -10,7 +10,10 @@
 // The tile mirrors the bf16 one (256 x 256, 8 waves as 4 x 2, direct global->LDS fills,
 // the same XOR swizzle of 16-byte chunks in 128-byte LDS rows) with 128 K values per
 // stage, plus one 32-bit word of four E8M0 scales per tile row and stage, fetched into LDS
-// by one more direct load per wave.  Lane layout of the scaled MFMA (checked on the
+// by one more direct load per wave.  Scale arrays are K-tile-major (one plane of 32-bit
+// words per 128-value K tile, rows consecutive inside a plane), so that load reads 256
+// contiguous bytes; with row-major scales the same load touched 64 lines and cost a quarter
+// of GEMM1's time.  Lane layout of the scaled MFMA (checked on the
 // device): lane (row r32, half hi) supplies K chunks hi and 2 + hi (16 values each) of
 // the 64-value step, and the scale of block hi of that step; so a lane shifts its row's
 // scale word right by 8 * hi and selects byte 0 or 2 with op_sel for the two steps.
@@ -26,9 +29,11 @@ constexpr int kMxLds = 2 * kMxStageBytes;                               // 132 K
 
 struct TileMX {
   const uint8_t* a;     // the tile's first A row; row stride K
-  const uint8_t* as;    // its scales; row stride K / 32
+  const uint8_t* as;    // the scale word of its first row in K-tile plane 0
+  int64_t as_plane;     // bytes between K-tile planes of the A scales (4 * total A rows)
   void* o;              // MODE 0: h codes, MODE 1: bf16 rows; row stride Nout elements
-  uint8_t* os;          // MODE 0: h scales; row stride Nout / 32
+  uint8_t* os;          // MODE 0: the h scale word of the tile's first row in plane 0
+  int64_t os_plane;     // MODE 0: bytes between planes of the h scales
   int rows;             // valid rows, 1..256; rows beyond re-read row rows-1 and are not stored
 };
 
@@ -38,12 +43,13 @@ __device__ __forceinline__ i32x8 ld_frag(const char* s, int row, int c0) {
   return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
 }
 
-// b0/b1: this expert's weight codes ([Nout][K]); bs0/bs1 their scales ([Nout][K/32]).
+// b0/b1: this expert's weight codes ([Nout][K]); bs0/bs1: the scale word of its row 0 in
+// plane 0; bs_plane: bytes between the weights' K-tile planes.
 template <int MODE>
 __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __restrict__ b0,
                                              const uint8_t* __restrict__ b1, const uint8_t* __restrict__ bs0,
-                                             const uint8_t* __restrict__ bs1, int c0, int Nout, int K,
-                                             char* smem) {
+                                             const uint8_t* __restrict__ bs1, int64_t bs_plane, int c0, int Nout,
+                                             int K, char* smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -52,7 +58,6 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
   const int lch_even = lpos ^ (lrow >> 1);
   const int lch_odd = lpos ^ (4 + (lrow >> 1));
   const int nk = K / kMxBK;
-  const int ksc = K / kMxBlock;
   const int rows = io.rows;
 
   // fills: this wave's row groups g = wave*4 + i (rows g*8 + lrow) of the A and B tiles
@@ -72,15 +77,19 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
   }
   // scale words: waves 0-3 fetch A rows 64*wave + lane, waves 4-7 B rows 64*(wave-4) + lane
   const uint8_t* sp;
+  int64_t splane;
   {
     const int row = (wave & 3) * 64 + lane;
     if (wave < 4) {
-      sp = io.as + size_t(min(row, rows - 1)) * ksc;
+      sp = io.as + 4 * size_t(min(row, rows - 1));
+      splane = io.as_plane;
     } else if (MODE == 0) {
       const int n = min(c0 + (row >> 6) * 32 + (row & 31), Nout - 1);
-      sp = (((row >> 5) & 1) ? bs1 : bs0) + size_t(n) * ksc;
+      sp = (((row >> 5) & 1) ? bs1 : bs0) + 4 * size_t(n);
+      splane = bs_plane;
     } else {
-      sp = bs0 + size_t(min(c0 + row, Nout - 1)) * ksc;
+      sp = bs0 + 4 * size_t(min(c0 + row, Nout - 1));
+      splane = bs_plane;
     }
   }
   auto issue = [&](int ks) {
@@ -94,7 +103,7 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(ap[i] + koff), (lds_void_ptr)(sa + g * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(bp[i] + koff), (lds_void_ptr)(sb + g * 1024), 16, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(sp + ks * 4), (lds_void_ptr)(ss + wave * 256), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(sp + ks * splane), (lds_void_ptr)(ss + wave * 256), 4, 0, 0);
   };
 
   f32x16 acc[2][4];
@@ -202,7 +211,7 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
       u32x4* dst = reinterpret_cast<u32x4*>(hq + size_t(row) * Nout + c0 + blk * 32);
       dst[0] = c0v;
       dst[1] = c1v;
-      io.os[size_t(row) * (Nout / kMxBlock) + (c0 >> 5) + blk] = uint8_t(sc);
+      io.os[(c0 >> 7) * io.os_plane + 4 * size_t(row) + blk] = uint8_t(sc);
     }
   } else {
     uint16_t* orow0 = static_cast<uint16_t*>(io.o);
@@ -226,7 +235,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_mx_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B0,
     const uint8_t* __restrict__ B1, const uint8_t* __restrict__ Bs0, const uint8_t* __restrict__ Bs1,
     void* __restrict__ C, uint8_t* __restrict__ Cs, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ mtile_base, const int32_t* __restrict__ ctrl, int El, int K, int Nout) {
+    const int32_t* __restrict__ mtile_base, const int32_t* __restrict__ ctrl, int El, int K, int Nout,
+    int64_t nmax) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int cols_per_tile = (MODE == 0) ? kGemmBN / 2 : kGemmBN;
   const int NT = (Nout + cols_per_tile - 1) / cols_per_tile;
@@ -234,7 +244,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_mx_kernel(
   const int per_xcd = (total + 7) >> 3;
   const int xcd = blockIdx.x & 7;
   const int wg_per_xcd = gridDim.x >> 3;
-  const int ksc = K / kMxBlock;
+  const int64_t bs_plane = 4 * int64_t(El) * Nout;    // weight scale planes hold every expert's rows
 
   for (int tt = blockIdx.x >> 3; tt < per_xcd; tt += wg_per_xcd) {
     const int tau = xcd * per_xcd + tt;
@@ -248,20 +258,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_mx_kernel(
     const int row0 = offsets[l] + mt * kGemmBM;
     TileMX io;
     io.a = A + size_t(row0) * K;
-    io.as = As + size_t(row0) * ksc;
+    io.as = As + 4 * size_t(row0);
+    io.as_plane = 4 * nmax;
     if (MODE == 0) {
       io.o = static_cast<uint8_t*>(C) + size_t(row0) * Nout;
-      io.os = Cs + size_t(row0) * (Nout / kMxBlock);
+      io.os = Cs + 4 * size_t(row0);
+      io.os_plane = 4 * nmax;
     } else {
       io.o = static_cast<uint16_t*>(C) + size_t(row0) * Nout;
       io.os = nullptr;
+      io.os_plane = 0;
     }
     io.rows = min(kGemmBM, offsets[l + 1] - row0);
     const uint8_t* b0 = B0 + size_t(l) * Nout * K;
     const uint8_t* b1 = (MODE == 0) ? B1 + size_t(l) * Nout * K : b0;
-    const uint8_t* bs0 = Bs0 + size_t(l) * Nout * ksc;
-    const uint8_t* bs1 = (MODE == 0) ? Bs1 + size_t(l) * Nout * ksc : bs0;
-    gemm_mx_tile<MODE>(io, b0, b1, bs0, bs1, nt * cols_per_tile, Nout, K, smem);
+    const uint8_t* bs0 = Bs0 + 4 * size_t(l) * Nout;
+    const uint8_t* bs1 = (MODE == 0) ? Bs1 + 4 * size_t(l) * Nout : bs0;
+    gemm_mx_tile<MODE>(io, b0, b1, bs0, bs1, bs_plane, nt * cols_per_tile, Nout, K, smem);
   }
 }
 
@@ -290,9 +303,9 @@ hipError_t launch_ffn_mx(const moe_shape_t& s, int El, const uint8_t* xe, const 
   uint8_t* hs = reinterpret_cast<uint8_t*>(ws + mx_h_scales_offset(L, s));
   const int grid = (cus / 8) * 8;
   hipLaunchKernelGGL(grouped_gemm_mx_kernel<0>, dim3(grid), dim3(kGemmThreads), kMxLds, st, xe, xe_scales, w1, w3,
-                     w1s, w3s, static_cast<void*>(hq), hs, offsets, mtb, ctrl, El, s.d, s.F);
+                     w1s, w3s, static_cast<void*>(hq), hs, offsets, mtb, ctrl, El, s.d, s.F, int64_t(L.max_pairs));
   hipLaunchKernelGGL(grouped_gemm_mx_kernel<1>, dim3(grid), dim3(kGemmThreads), kMxLds, st, hq, hs, w2, nullptr,
-                     w2s, nullptr, ye, nullptr, offsets, mtb, ctrl, El, s.F, s.d);
+                     w2s, nullptr, ye, nullptr, offsets, mtb, ctrl, El, s.F, s.d, int64_t(L.max_pairs));
   return hipGetLastError();
 }
 

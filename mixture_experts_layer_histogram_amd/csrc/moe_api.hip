@@ -19,7 +19,7 @@ hipError_t launch_combine(const moe_shape_t& s, const char* ye, const int32_t* p
 hipError_t launch_mx_quantize(const void* src, int src_dtype, int64_t rows, int K, uint8_t* codes,
                               uint8_t* scales, int cus, hipStream_t st);
 hipError_t launch_dispatch_mx(const moe_shape_t& s, const void* const* x, const int32_t* pull_src, uint8_t* xe,
-                              uint8_t* xe_scales, const int32_t* ctrl, int cus, hipStream_t st);
+                              uint8_t* xe_scales, int64_t nmax, const int32_t* ctrl, int cus, hipStream_t st);
 hipError_t launch_ffn_mx(const moe_shape_t& s, int El, const uint8_t* xe, const uint8_t* xe_scales,
                          const int32_t* offsets, const uint8_t* w1, const uint8_t* w3, const uint8_t* w2,
                          const uint8_t* w1s, const uint8_t* w3s, const uint8_t* w2s, void* ye, char* ws,
@@ -136,7 +136,7 @@ int moe_mx_quantize(const void* src, int32_t src_dtype, int64_t rows, int32_t K,
                     void* stream) {
   if (src_dtype != MOE_BF16 && src_dtype != MOE_F32) return MOE_EINVAL;
   if (rows < 0 || K < 1 || rows > (int64_t(1) << 40) / K) return MOE_EINVAL;
-  if (K % 32) return MOE_EALIGN;
+  if (K % 128) return MOE_EALIGN;                // whole 32-bit scale words per row
   if (!src || !codes || !scales) return MOE_EINVAL;
   if (!aligned16(src) || !aligned16(codes)) return MOE_EALIGN;
   return hip_rc(launch_mx_quantize(src, src_dtype, rows, K, codes, scales, cu_count(),
@@ -173,8 +173,8 @@ int moe_dispatch_pull(const moe_shape_t* s, const moe_placement_t* p, const void
   const WsLayout L = ws_layout(*s, p->E_local);
   const int32_t* ctrl = reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + L.ctrl);
   if (s->dtype == MOE_MXFP8)
-    return hip_rc(launch_dispatch_mx(*s, x, pull_src, static_cast<uint8_t*>(xe), xe_scales, ctrl, cu_count(),
-                                     static_cast<hipStream_t>(stream)));
+    return hip_rc(launch_dispatch_mx(*s, x, pull_src, static_cast<uint8_t*>(xe), xe_scales, L.max_pairs, ctrl,
+                                     cu_count(), static_cast<hipStream_t>(stream)));
   return hip_rc(launch_dispatch(*s, x, pull_src, static_cast<char*>(xe), ctrl, cu_count(),
                                 static_cast<hipStream_t>(stream)));
 }

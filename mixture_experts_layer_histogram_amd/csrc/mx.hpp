@@ -13,6 +13,15 @@
 namespace moe {
 
 constexpr int kMxBlock = 32;
+constexpr int kMxTileK = 128;     // K values of one scale word (four blocks)
+
+// Scale layout shared by every MXFP8 operand: for a matrix of `rows` rows, the scale code of
+// block b of row r sits at byte 4 * (rows * (b / 4) + r) + b % 4 -- one 32-bit word per
+// (128-value K tile, row), K tiles outermost.  A wave reading the words of 64 consecutive
+// rows for one K tile then touches 256 contiguous bytes instead of 64 scattered lines.
+__device__ __forceinline__ int64_t mx_scale_index(int64_t rows, int64_t r, int b) {
+  return 4 * (rows * (b >> 2) + r) + (b & 3);
+}
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 

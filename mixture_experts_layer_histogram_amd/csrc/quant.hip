@@ -11,11 +11,13 @@
 
 namespace moe {
 
-// codes[i] / scales[i / 32] for the n8 groups of 8 consecutive values of src
+// codes[i] for the n8 groups of 8 consecutive values of src ([rows][K]); the scale of each
+// 32-value block goes to its place in the K-tile-major scale layout
 template <bool BF16>
-__global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict__ src, int64_t n8,
-                                                          uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict__ src, int64_t n8, int64_t rows,
+                                                          int K, uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales) {
+  const int g8 = K >> 3;             // groups of 8 per row
   // n8 is a multiple of 4, so every lane quad is either wholly inside or wholly outside
   const int64_t stride = int64_t(gridDim.x) * 256;
   for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < n8; t += stride) {
@@ -29,7 +31,10 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict
       q = mx_quant8_f32(__builtin_nontemporal_load(p), __builtin_nontemporal_load(p + 1), &sc);
     }
     reinterpret_cast<uint2*>(codes)[t] = q;
-    if ((t & 3) == 0) scales[t >> 2] = uint8_t(sc);
+    if ((t & 3) == 0) {
+      const int64_t r = t / g8;
+      scales[mx_scale_index(rows, r, int(t - r * g8) >> 2)] = uint8_t(sc);
+    }
   }
 }
 
@@ -39,7 +44,7 @@ __global__ __launch_bounds__(256) void dispatch_pull_mx_kernel(RankPtrs<const ch
                                                                const int32_t* __restrict__ pull_src,
                                                                const int32_t* __restrict__ ctrl,
                                                                uint8_t* __restrict__ xe,
-                                                               uint8_t* __restrict__ xes, int d) {
+                                                               uint8_t* __restrict__ xes, int d, int64_t nmax) {
   constexpr int UNROLL = 16;
   const int N = ctrl[kCtrlN];
   const int lane = threadIdx.x & 63;
@@ -50,7 +55,6 @@ __global__ __launch_bounds__(256) void dispatch_pull_mx_kernel(RankPtrs<const ch
     const int t = pull_src[2 * int64_t(s) + 1];
     const u32x4* src = reinterpret_cast<const u32x4*>(x.p[r] + int64_t(t) * d * 2);
     uint2* dst = reinterpret_cast<uint2*>(xe + int64_t(s) * d);
-    uint8_t* dsc = xes + int64_t(s) * (d / kMxBlock);
     for (int base = 0; base < n16; base += 64 * UNROLL) {
       u32x4 v[UNROLL];
 #pragma unroll
@@ -66,7 +70,7 @@ __global__ __launch_bounds__(256) void dispatch_pull_mx_kernel(RankPtrs<const ch
         const uint2 q = mx_quant8_bf16(v[u], &sc);     // all lanes: quad shuffles inside
         if (i < n16) {
           dst[i] = q;
-          if ((i & 3) == 0) dsc[i >> 2] = uint8_t(sc);
+          if ((i & 3) == 0) xes[mx_scale_index(nmax, s, i >> 2)] = uint8_t(sc);
         }
       }
     }
@@ -82,18 +86,18 @@ hipError_t launch_mx_quantize(const void* src, int src_dtype, int64_t rows, int 
   const int64_t need = (n8 + 255) / 256;
   const int grid = int(need < int64_t(cus) * kQuantBlocksPerCU ? need : int64_t(cus) * kQuantBlocksPerCU);
   if (src_dtype == MOE_BF16)
-    hipLaunchKernelGGL(mx_quantize_kernel<true>, dim3(grid), dim3(256), 0, st, src, n8, codes, scales);
+    hipLaunchKernelGGL(mx_quantize_kernel<true>, dim3(grid), dim3(256), 0, st, src, n8, rows, K, codes, scales);
   else
-    hipLaunchKernelGGL(mx_quantize_kernel<false>, dim3(grid), dim3(256), 0, st, src, n8, codes, scales);
+    hipLaunchKernelGGL(mx_quantize_kernel<false>, dim3(grid), dim3(256), 0, st, src, n8, rows, K, codes, scales);
   return hipGetLastError();
 }
 
 hipError_t launch_dispatch_mx(const moe_shape_t& s, const void* const* x, const int32_t* pull_src, uint8_t* xe,
-                              uint8_t* xe_scales, const int32_t* ctrl, int cus, hipStream_t st) {
+                              uint8_t* xe_scales, int64_t nmax, const int32_t* ctrl, int cus, hipStream_t st) {
   RankPtrs<const char*> xp{};
   for (int r = 0; r < s.R; ++r) xp.p[r] = static_cast<const char*>(x[r]);
   hipLaunchKernelGGL(dispatch_pull_mx_kernel, dim3(cus * kGatherMxBlocksPerCU), dim3(256), 0, st, xp, pull_src, ctrl,
-                     xe, xe_scales, s.d);
+                     xe, xe_scales, s.d, nmax);
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ class DeviceProblem:
             K = w.shape[-1]
             rows = w.numel() // K
             q = torch.empty(w.shape, dtype=torch.uint8, device=self.device)
-            sc = torch.empty((*w.shape[:-1], K // 32), dtype=torch.uint8, device=self.device)
+            sc = torch.empty((K // 128, rows, 4), dtype=torch.uint8, device=self.device)   # K-tile-major
             moe.moe_mx_quantize(w, moe.MOE_BF16, rows, K, q, sc, stream=stream)
             self.wq.append(q)
             self.ws_codes.append(sc)
@@ -77,7 +77,7 @@ class DeviceProblem:
         self.slot_of = torch.empty((R, T, k), dtype=torch.int32, device=dev)
         if cfg.dtype == "mxfp8":
             self.xe = torch.empty((self.nmax, d), dtype=torch.uint8, device=dev)
-            self.xe_scales = torch.empty((self.nmax, d // 32), dtype=torch.uint8, device=dev)
+            self.xe_scales = torch.empty((d // 128, self.nmax, 4), dtype=torch.uint8, device=dev)
         else:
             self.xe = torch.empty((self.nmax, d), dtype=ed, device=dev)
             self.xe_scales = None
@@ -129,6 +129,14 @@ class DeviceProblem:
         return moe.moe_read_status(self.ws, stream)
 
     # ---- host copies ----
+    @staticmethod
+    def scales_rowmajor(t, rows=None) -> np.ndarray:
+        """[rows][K/32] scale codes from a [K/128][rows][4] device array (first `rows` rows)."""
+        a = t.cpu().numpy()
+        kt, n, _ = a.shape
+        rows = n if rows is None else rows
+        return np.ascontiguousarray(a[:, :rows, :].transpose(1, 0, 2).reshape(rows, kt * 4))
+
     def N(self) -> int:
         return int(self.offsets[-1].item())
 

@@ -134,15 +134,16 @@ def test_forward_checks_every_stage_before_launching():
 def test_mx_quantize_rejects_bad_arguments_before_launch():
     L = moe.lib()
     q = L.moe_mx_quantize
-    assert q(FAKE, moe.MOE_MXFP8, 4, 64, FAKE, FAKE, None) == -1        # source must be bf16 or fp32
-    assert q(FAKE, moe.MOE_BF16, -1, 64, FAKE, FAKE, None) == -1
+    assert q(FAKE, moe.MOE_MXFP8, 4, 128, FAKE, FAKE, None) == -1       # source must be bf16 or fp32
+    assert q(FAKE, moe.MOE_BF16, -1, 128, FAKE, FAKE, None) == -1
     assert q(FAKE, moe.MOE_BF16, 4, 0, FAKE, FAKE, None) == -1
-    assert q(FAKE, moe.MOE_BF16, 4, 48, FAKE, FAKE, None) == -2         # K % 32
-    assert q(None, moe.MOE_BF16, 4, 64, FAKE, FAKE, None) == -1
-    assert q(FAKE, moe.MOE_BF16, 4, 64, FAKE, None, None) == -1
-    assert q(FAKE + 8, moe.MOE_BF16, 4, 64, FAKE, FAKE, None) == -2
-    assert q(FAKE, moe.MOE_F32, 4, 64, FAKE + 4, FAKE, None) == -2
-    assert q(FAKE, moe.MOE_BF16, 0, 64, FAKE, FAKE, None) == 0          # nothing to do, nothing launched
+    assert q(FAKE, moe.MOE_BF16, 4, 48, FAKE, FAKE, None) == -2         # K % 128: whole scale words
+    assert q(FAKE, moe.MOE_BF16, 4, 64, FAKE, FAKE, None) == -2
+    assert q(None, moe.MOE_BF16, 4, 128, FAKE, FAKE, None) == -1
+    assert q(FAKE, moe.MOE_BF16, 4, 128, FAKE, None, None) == -1
+    assert q(FAKE + 8, moe.MOE_BF16, 4, 128, FAKE, FAKE, None) == -2
+    assert q(FAKE, moe.MOE_F32, 4, 128, FAKE + 4, FAKE, None) == -2
+    assert q(FAKE, moe.MOE_BF16, 0, 128, FAKE, FAKE, None) == 0         # nothing to do, nothing launched
 
 
 def test_mx_entry_points_need_their_scales():

@@ -64,10 +64,11 @@ def _gpu_quantize(vals_f32, K, src="bf16"):
         t = torch.from_numpy(np.ascontiguousarray(vals_f32.reshape(rows, K), dtype=np.float32)).to(dev)
         code = moe.MOE_F32
     q = torch.full((rows, K), 0x55, dtype=torch.uint8, device=dev)
-    s = torch.full((rows, K // 32), 0x55, dtype=torch.uint8, device=dev)
+    s = torch.full((K // 128, rows, 4), 0x55, dtype=torch.uint8, device=dev)    # K-tile-major scales
     moe.moe_mx_quantize(t, code, rows, K, q, s)
     torch.cuda.synchronize()
-    return q.cpu().numpy(), s.cpu().numpy()
+    from mixture_experts_layer_histogram_amd.device import DeviceProblem
+    return q.cpu().numpy(), DeviceProblem.scales_rowmajor(s)
 
 
 def _all_bf16_values():
@@ -169,10 +170,11 @@ def test_mx_forward_parity(name):
     torch.cuda.synchronize()
     qw = _oracle_weights(inp, range(cfg.E_local))
     # offline weight quantisation: bit-exact codes and scales
+    wsc = [P.scales_rowmajor(t).reshape(cfg.E_local, -1, t.shape[0] * 4) for t in P.ws_codes]
     for l in range(cfg.E_local):
         for i in range(3):
             assert np.array_equal(P.wq[i][l].cpu().numpy(), qw[l][i][0]), (l, i)
-            assert np.array_equal(P.ws_codes[i][l].cpu().numpy(), qw[l][i][1]), (l, i)
+            assert np.array_equal(wsc[i][l], qw[l][i][1]), (l, i)
     wq = [[qw[l][i][2] for l in range(cfg.E_local)] for i in range(3)]
     ref = MX.forward_q(inp.logits, inp.x_f32, *wq, inp.expert_to_local, cfg.E_local, cfg.k)
     N = ref["N"]
@@ -182,7 +184,7 @@ def test_mx_forward_parity(name):
     # quantise-on-gather: codes and scales bit-exact
     xc, xs, _ = MX.quantize(O.dispatch(inp.x_f32, ref["pull_src"]))
     assert np.array_equal(P.xe[:N].cpu().numpy(), xc)
-    assert np.array_equal(P.xe_scales[:N].cpu().numpy(), xs)
+    assert np.array_equal(P.scales_rowmajor(P.xe_scales, N), xs)
     ye = P.rows_f64(P.ye[:N])
     allr = np.ones(N, dtype=bool)
     err_ffn, fro_ffn = _row_rel_err(ye, ref["ye"], allr), _fro_rel_err(ye, ref["ye"], allr)
@@ -242,9 +244,10 @@ def test_mx_forward_full_dsv3_sampled():
     cand = np.argwhere(ok)
     pick = cand[np.random.default_rng(0).choice(len(cand), 24, replace=False)]
     qw = _oracle_weights(inp, range(6))
+    w2s = P.scales_rowmajor(P.ws_codes[2]).reshape(cfg.E_local, cfg.d, cfg.F // 32)
     for l in range(6):
         assert np.array_equal(P.wq[0][l].cpu().numpy(), qw[l][0][0])
-        assert np.array_equal(P.ws_codes[2][l].cpu().numpy(), qw[l][2][1])
+        assert np.array_equal(w2s[l], qw[l][2][1])
     wq = [[qw[l][i][2] if l < 6 else None for l in range(cfg.E_local)] for i in range(3)]
     yr = np.stack([MX.token_output_q(inp.x_f32[r, t], idx[r, t], g[r, t], inp.expert_to_local, *wq)
                    for r, t in pick])
