@@ -5,6 +5,11 @@ in HBM: top-k routing, sort-free layout, pull dispatch, grouped SwiGLU expert FF
 push combine and the final weighted merge.  Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config dsv3]
+
+With --backward (bf16 configs) a step is instead the whole backward of the share after
+one forward: the weight transposes (moe_backward_prepare, once per weight update) and
+moe_backward's three stages (pull reverse-combine, expert SwiGLU backward with the
+weight-gradient GEMMs, push reverse-dispatch with the ordered sum and the gate gradient).
 """
 from __future__ import annotations
 
@@ -23,6 +28,7 @@ sys.path.insert(0, ROOT)
 from mixture_experts_layer_histogram_amd import configs, inputs  # noqa: E402
 
 METRIC = "MoE layer fwd tokens/s; grouped-GEMM % MFMA peak; gather/combine % HBM peak"
+METRIC_BWD = "MoE layer bwd tokens/s; expert-backward GEMMs % MFMA peak; reverse pull/push % HBM peak"
 PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
 PEAK_FP8_FLOPS = 5.0e15      # MI355X dense fp8 / MXFP8 MFMA
 PEAK_F32_FLOPS = 157.3e12    # MI355X fp32 matrix
@@ -49,6 +55,8 @@ def parse():
     ap.add_argument("--config", default="dsv3", choices=sorted(configs.CONFIGS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (bf16) instead of the forward; prints its own JSON line")
     ap.add_argument("--cpu-sample-ranks", type=int, default=0, help="0 = all ranks (the whole step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run three plain 1 GiB device copies (counter calibration)")
@@ -164,6 +172,103 @@ def cpu_baseline(cfg, inp, ranks):
             "sample": f"source ranks 0..{ranks - 1} of the same inputs ({frac}); {what}; {dt:.2f} s wall"}
 
 
+def cpu_baseline_bwd(cfg, inp, dy, ranks):
+    """The backward oracle as it stands (it recomputes its forward) on the first `ranks`
+    source ranks of the same inputs."""
+    from oracle import moe_oracle_bwd as B
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    ranks = max(1, min(ranks, cfg.R))
+    t0 = time.perf_counter()
+    B.backward(inp.logits[:ranks], inp.x_f32[:ranks], inp.w1_f32, inp.w3_f32, inp.w2_f32, inp.expert_to_local,
+               cfg.E_local, cfg.k, dy[:ranks], cfg.minibatch)
+    dt = time.perf_counter() - t0
+    tokens = ranks * cfg.T / cfg.G
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"source ranks 0..{ranks - 1} of {cfg.R} of the same inputs; fp64 NumPy backward oracle "
+                      f"(its forward, pull reverse-combine, SwiGLU backward, weight gradients, push, gate "
+                      f"gradients); {dt:.2f} s wall"}
+
+
+def run_backward(args, cfg, inp, P, stream, N):
+    import torch
+    if cfg.dtype != "bf16":
+        raise SystemExit("--backward: the backward is built for bf16 configs only")
+    dy_bits, dy = inputs.make_dy(cfg, seed=args.seed)
+    P.alloc_backward(dy_bits)
+    for _ in range(args.warmup):
+        P.prepare_backward()
+        P.backward()
+    torch.cuda.synchronize()
+    names = ["prepare", "pull_reverse", "ffn_backward", "push_reverse"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        P.prepare_backward()
+        e[1].record(stream)
+        P.combine_reverse()
+        e[2].record(stream)
+        P.ffn_backward()
+        e[3].record(stream)
+        P.dispatch_reverse()
+        e[4].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    stage_ms = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+                for j, n in enumerate(names)}
+    log(f"[bench] backward {args.steps} steps: {ms_step:.3f} ms/step; stages {stage_ms}")
+    row = cfg.d * 2
+    # dh = dO W2 (2dFN), GEMM1 again (4dFN), dX (4dFN), dW1 + dW3 + dW2 (6dFN)
+    flops = 16.0 * cfg.d * cfg.F * N
+    t_ffn = stage_ms["ffn_backward"] * 1e-3
+    pull_bytes = 3.0 * N * row + N * 12            # dy and ye rows in, dO out; schedule, gate, dg
+    push_bytes = 2.0 * N * row + N * 12            # dX rows to recv, dg beside them
+    merge_bytes = 1.0 * N * row + cfg.R * cfg.T * row
+    gate_bytes = cfg.R * cfg.T * (cfg.k * 16 + cfg.E * 4)
+    prep_bytes = 2.0 * 3 * cfg.E_local * cfg.F * cfg.d * 2
+    tokens = cfg.R * cfg.T / cfg.G
+    result = {
+        "metric": METRIC_BWD,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) tokens and incoming gradients, fan-in scaled random expert weights, "
+                "router logits x@W_r)",
+        "config": {"workload": cfg.name, "R": cfg.R, "T": cfg.T, "d": cfg.d, "E": cfg.E, "E_local": cfg.E_local,
+                   "k": cfg.k, "F": cfg.F, "local_pairs": N,
+                   "path": "backward after one forward: weight transposes + three stage calls on one stream"},
+        "roofline": {"bound": "mfma", "kernel": "expert SwiGLU backward stage (dh, GEMM1+SwiGLU backward, dX, "
+                                                 "dW1/dW3/dW2 GEMMs, operand transposes)",
+                     "achieved": flops / t_ffn / 1e12, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": flops / t_ffn / PEAK_BF16_FLOPS, "traffic": None},
+        "stages_ms": stage_ms,
+        "stages_hbm_frac": {
+            "prepare": prep_bytes / (stage_ms["prepare"] * 1e-3) / PEAK_HBM,
+            "pull_reverse": pull_bytes / (stage_ms["pull_reverse"] * 1e-3) / PEAK_HBM,
+            "push_reverse": (push_bytes + merge_bytes + gate_bytes) / (stage_ms["push_reverse"] * 1e-3) / PEAK_HBM,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU backward oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline_bwd(cfg, inp, dy, args.cpu_sample_ranks or 1)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -193,6 +298,9 @@ def main():
         raise SystemExit(f"device status {st} after warmup")
     N = P.N()
     log(f"[bench] warmup done, N={N} local pairs")
+    if args.backward:
+        run_backward(args, cfg, inp, P, stream, N)
+        return
 
     names = ["layout", "dispatch", "ffn", "combine"]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]

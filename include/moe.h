@@ -263,6 +263,93 @@ size_t moe_ring_slot_bytes(const moe_shape_t* s, const moe_exec_t* ex);
 /* Workspace bytes moe_forward_persistent needs (smaller than moe_workspace_bytes). */
 size_t moe_persistent_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex);
 
+/*
+ * Backward of the share (bf16 only; other dtypes return MOE_EUNSUP)
+ *   [kucoin §01: training adds a backward pass with two more communication rounds in the
+ *   opposite direction; kucoin §02: the backward uses a pull reverse-combine and a push
+ *   reverse-dispatch; kucoin §03: the backward is sped up as well].
+ * The pages give the two rounds, not the arithmetic; what follows is the derivative of the
+ * forward above for the loss L = sum over (r, t) of <dy[r][t], y[r][t]>.
+ */
+
+/* Bytes of the backward workspace `bws` (0 if the shape is invalid or not bf16). */
+size_t moe_backward_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p);
+
+/*
+ * moe_backward_prepare -- the transposed expert weights the backward's row GEMMs read,
+ * built once per weight update:
+ *   w13t[l][n][f] = w1[l][f][n],  w13t[l][n][F + f] = w3[l][f][n]   [E_local][d][2F]
+ *   w2t[l][f][n]  = w2[l][n][f]                                     [E_local][F][d]
+ * w1, w3: [E_local][F][d]; w2: [E_local][d][F]; all bf16, 16-byte aligned.  Bit-exact.
+ */
+int moe_backward_prepare(const moe_shape_t* s, const moe_placement_t* p, const void* w1, const void* w3,
+                         const void* w2, void* w13t, void* w2t, void* stream);
+
+/*
+ * The backward in three stages (moe_backward runs them in order).  Inputs common to all:
+ * the forward's outputs (xe and ye as moe_forward left them, [moe_max_pairs][d];
+ * topk_idx, topk_w, offsets, pull_src, slot_of from moe_layout), ws = the workspace the
+ * forward ran with (read only: row count and row tiles), and bws, the backward workspace
+ * (at least moe_backward_workspace_bytes(), 256-byte aligned), which carries the per-row
+ * gradients from one stage to the next.  With g the pair's gate and, per row of a local
+ * expert, a = x W1^T, b = x W3^T, h = silu(a) * b.  Deterministic.
+ * Accuracy against the fp64 oracle: dx per token and every row of dw1, dw3, dw2 within
+ * the bf16 row-relative 2e-2; dlogits of a token within 2e-2 of max_j g_j |dy| |o_j|.
+ */
+
+/*
+ * moe_combine_pull_reverse -- pull reverse-combine [kucoin §02]: row s of pair (r, t, j)
+ * pulls dO_s = g_j dy[r][t] (bf16, into bws) by the forward's pull schedule, and the
+ * pair's gate gradient dg_s = <dy[r][t], ye[s]> (fp32 accumulation, into bws).
+ * dy: R device pointers, each [T][d] bf16 (the incoming gradient of y).
+ */
+int moe_combine_pull_reverse(const moe_shape_t* s, const moe_placement_t* p, const void* const* dy, const void* ye,
+                             const int32_t* pull_src, const int32_t* slot_of, const float* topk_w, const void* ws,
+                             size_t ws_bytes, void* bws, size_t bws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn_backward -- grouped SwiGLU backward of every local expert from the dO
+ * rows in bws [kucoin §03: the backward is sped up as well]:
+ *   dh = dO W2; da = dh * b * silu'(a); db = dh * silu(a), silu'(a) = sigma(a) (1 + a (1 - sigma(a)));
+ *   dX = da W1 + db W3 (fp32 accumulate, bf16 rows, into bws);
+ *   dw1[l] = sum_s da_s^T x_s, dw3[l] = sum_s db_s^T x_s ([E_local][F][d] bf16),
+ *   dw2[l] = sum_s dO_s^T h_s ([E_local][d][F] bf16), summed over the expert's rows in
+ *   ascending order; an expert with no rows gets zeros.
+ * w1, w3: [E_local][F][d]; w13t, w2t: moe_backward_prepare's outputs.
+ */
+int moe_expert_ffn_backward(const moe_shape_t* s, const moe_placement_t* p, const void* xe, const int32_t* offsets,
+                            const void* w1, const void* w3, const void* w13t, const void* w2t, const void* ws,
+                            size_t ws_bytes, void* dw1, void* dw3, void* dw2, void* bws, size_t bws_bytes,
+                            void* stream);
+
+/*
+ * moe_dispatch_push_reverse -- push reverse-dispatch [kucoin §02], then the ordered sum and
+ * the gate gradient:
+ *   recv[r][t][j] = dX_s (R pointers, each [T][k][d] bf16; the forward's recv may be reused);
+ *   dx[r][t] = sum over ascending j with a local expert of recv[r][t][j] (R pointers, each
+ *     [T][d] bf16; exactly 0 for a token with no local pair);
+ *   dlogits[r][t][e_j] = g_j (dg_j - sum_i g_i dg_i) for the k kept experts e_j, with
+ *     dg = 0 for a pair whose expert is not local; 0 for every other e (R pointers,
+ *     each [T][E] fp32).
+ */
+int moe_dispatch_push_reverse(const moe_shape_t* s, const moe_placement_t* p, const int32_t* pull_src,
+                              const int32_t* slot_of, const int32_t* topk_idx, const float* topk_w, const void* ws,
+                              size_t ws_bytes, void* const* recv, void* const* dx, float* const* dlogits, void* bws,
+                              size_t bws_bytes, void* stream);
+
+/*
+ * moe_backward -- the three calls above in order on one stream, after moe_forward ran with
+ * the same arguments: gradients of L with respect to the token rows (dx), the local
+ * experts' weights (dw1, dw3, dw2) and the logits (dlogits).  Every stage's arguments are
+ * checked before the first launch.
+ */
+int moe_backward(const moe_shape_t* s, const moe_placement_t* p, const void* const* dy, const void* xe,
+                 const void* ye, const void* w1, const void* w3, const void* w13t, const void* w2t,
+                 const int32_t* topk_idx, const float* topk_w, const int32_t* offsets, const int32_t* pull_src,
+                 const int32_t* slot_of, const void* ws, size_t ws_bytes, void* const* recv, void* const* dx,
+                 float* const* dlogits, void* dw1, void* dw3, void* dw2, void* bws, size_t bws_bytes,
+                 void* stream);
+
 /* Syncs `stream` and returns the device status word (0, MOE_EINVAL or MOE_ETIMEOUT). */
 int moe_read_status(const void* ws, void* stream);
 

@@ -1,9 +1,12 @@
 // One 256-row x 256-column tile of the grouped SwiGLU FFN on gfx950 (bf16 MFMA).
 // Shared by the standalone grouped GEMM kernels and the persistent forward kernel.
 //
-// GEMM1 (MODE 0): h = silu(X W1^T) * (X W3^T); GEMM2 (MODE 1): y = h W2^T.  Every
-// operand is K-contiguous (row-major X and h, weights stored [out][in]), so each MFMA
-// lane's 8 consecutive K values are one 16-byte LDS read.
+// GEMM1 (MODE 0): h = silu(X W1^T) * (X W3^T); GEMM2 (MODE 1): y = h W2^T.  MODE 2 is
+// GEMM1 of the backward: the same products a = X W1^T, b = X W3^T, then from the incoming
+// dh of each (row, f) the epilogue writes h, da = dh * b * silu'(a) and db = dh * silu(a),
+// silu'(a) = sigma(a) (1 + a (1 - sigma(a))) (needs F % 8 == 0).  Every operand is
+// K-contiguous (row-major X and h, weights stored [out][in]), so each MFMA lane's 8
+// consecutive K values are one 16-byte LDS read.
 //
 // 8 waves (two per SIMD) as 4 (rows) x 2 (cols); each wave owns a 64 x 128 block = 2 x 4
 // tiles of v_mfma_f32_32x32x16_bf16.  K is staged 64 at a time through two LDS buffers
@@ -46,6 +49,8 @@ struct TileIO {
   int a_ld, o_ld;      // row strides in elements
   int blk_log2;        // 6, 7 or 8
   int rows;            // valid rows, 1..256
+  const uint16_t* dh;  // MODE 2: incoming dh of the tile's first row ([rows][Nout] contiguous)
+  uint16_t* dab;       // MODE 2: [da | db] rows of 2 * Nout from the tile's first row
 };
 
 template <typename P>
@@ -53,11 +58,12 @@ __device__ __forceinline__ P pick4(int i, P p0, P p1, P p2, P p3) {
   return i == 0 ? p0 : (i == 1 ? p1 : (i == 2 ? p2 : p3));
 }
 
-// b0/b1: this expert's weight matrices ([Nout][K]); c0: first output column of the tile.
+// b0/b1: this expert's weight matrices ([Nout][K], row stride b_ld); c0: first output
+// column of the tile.
 template <int MODE>
 __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __restrict__ b0,
                                           const uint16_t* __restrict__ b1, int c0, int Nout, int K,
-                                          char* smem) {
+                                          char* smem, int b_ld) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -80,13 +86,13 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
     const int lch = (i & 1) ? lch_odd : lch_even;
     const int rr = min(row, rows - 1);
     ap[i] = pick4(rr >> io.blk_log2, io.a0, io.a1, io.a2, io.a3) + size_t(rr & bmask) * io.a_ld + lch * 8;
-    if (MODE == 0) {
+    if (MODE != 1) {
       // 32-row blocks alternate W1 / W3 rows of the same 32 f values
       const int n = min(c0 + (row >> 6) * 32 + (row & 31), Nout - 1);
-      bp[i] = (((row >> 5) & 1) ? b1 : b0) + size_t(n) * K + lch * 8;
+      bp[i] = (((row >> 5) & 1) ? b1 : b0) + size_t(n) * b_ld + lch * 8;
     } else {
       const int n = min(c0 + row, Nout - 1);
-      bp[i] = b0 + size_t(n) * K + lch * 8;
+      bp[i] = b0 + size_t(n) * b_ld + lch * 8;
     }
   }
   auto issue = [&](int ks) {
@@ -141,6 +147,62 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
     }
     __builtin_amdgcn_s_waitcnt(0);      // this wave's fills of the next stage landed
     __syncthreads();                    // ... and everyone's
+  }
+
+  if (MODE == 2) {
+    // Backward epilogue, in two passes of 128 tile rows (m = 0, 1): every wave stages its
+    // (a, b) pairs as fp32 in LDS ([128 rows][128 f] float2 = the whole 128 KiB), then each
+    // thread finishes 8 consecutive f of one row -- one 16-byte load of dh, 16-byte stores
+    // of h, da and db.  The main loop ended on a barrier, so the stages are free.
+    float2* stg = reinterpret_cast<float2*>(smem);
+#pragma unroll   // acc[m] must stay in registers: a run-time m would move acc to scratch
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int lr = wm * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+          stg[lr * 128 + (wn * 2 + q) * 32 + r32] = make_float2(acc[m][2 * q][e], acc[m][2 * q + 1][e]);
+        }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int u = tid + i * kGemmThreads;             // 128 rows x 16 vectors of 8 f
+        const int lr = u >> 4, f8 = (u & 15) * 8;
+        const int trow = (lr >> 5) * 64 + m * 32 + (lr & 31);
+        const int f = c0 + f8;
+        if (trow < rows && f < Nout) {
+          const u32x4 dv = *reinterpret_cast<const u32x4*>(io.dh + size_t(trow) * Nout + f);
+          const f32x4* sp = reinterpret_cast<const f32x4*>(stg + lr * 128 + f8);
+          u32x4 hv, dav, dbv;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const f32x4 ab = sp[w];                       // a, b of f8 + 2w and f8 + 2w + 1
+            float hh[2], ga[2], gb[2];
+#pragma unroll
+            for (int z = 0; z < 2; ++z) {
+              const float a = ab[2 * z], b = ab[2 * z + 1];
+              const float dh = __uint_as_float(z ? (dv[w] & 0xFFFF0000u) : (dv[w] << 16));
+              const float sg = 1.0f / (1.0f + __expf(-a));
+              const float sa = a * sg;
+              hh[z] = sa * b;
+              ga[z] = dh * b * (sg * (1.0f + a * (1.0f - sg)));
+              gb[z] = dh * sa;
+            }
+            hv[w] = pack_bf16x2(hh[0], hh[1]);
+            dav[w] = pack_bf16x2(ga[0], ga[1]);
+            dbv[w] = pack_bf16x2(gb[0], gb[1]);
+          }
+          uint16_t* orow = pick4(trow >> io.blk_log2, io.o0, io.o1, io.o2, io.o3) + size_t(trow & bmask) * io.o_ld;
+          *reinterpret_cast<u32x4*>(orow + f) = hv;
+          uint16_t* drow = io.dab + size_t(trow) * (2 * Nout);
+          *reinterpret_cast<u32x4*>(drow + f) = dav;
+          *reinterpret_cast<u32x4*>(drow + Nout + f) = dbv;
+        }
+      }
+      __syncthreads();
+    }
+    return;
   }
 
   // epilogue: lane holds column r32 and rows 8*(e/4) + 4*hi + e%4 of each 32x32 block

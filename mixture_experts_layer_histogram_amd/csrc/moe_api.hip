@@ -31,6 +31,26 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
                              const int32_t* offsets, char* ring, long long slot_bytes, int slots, int blk_log2,
                              int comm_cus, int n_part, int cus, long long budget, void* const* recv, char* ws,
                              const WsLayout& L, hipStream_t st);
+hipError_t launch_rows_gemm(const uint16_t* A, const uint16_t* B, uint16_t* C, int K, int Nout, const int32_t* offsets,
+                            const int32_t* mtb, const int32_t* ctrl, int El, int cus, hipStream_t st);
+hipError_t launch_gemm1_bwd(const uint16_t* xe, const uint16_t* w1, const uint16_t* w3, const uint16_t* dh,
+                            uint16_t* h, uint16_t* dab, int d, int F, const int32_t* offsets, const int32_t* mtb,
+                            const int32_t* ctrl, int El, int cus, hipStream_t st);
+hipError_t launch_wgrad(const uint16_t* At, const uint16_t* Bt, const int32_t* poff, uint16_t* C, int El, int M, int Nc,
+                        int cus, hipStream_t st);
+hipError_t launch_pull_reverse(const moe_shape_t& s, const void* const* dy, const uint16_t* ye,
+                               const int32_t* pull_src, const int32_t* slot_of, const float* topk_w,
+                               const int32_t* ctrl, uint16_t* dO, float* dg, int cus, hipStream_t st);
+hipError_t launch_pad_offsets(const int32_t* offsets, int El, int32_t* poff, hipStream_t st);
+hipError_t launch_transpose_rows(const uint16_t* src, int64_t ld_src, uint16_t* dst, int C, const int32_t* offsets,
+                                 const int32_t* poff, int El, int cus, hipStream_t st);
+hipError_t launch_transpose_batched(const uint16_t* src, int64_t src_bstride, uint16_t* dst, int64_t ldt,
+                                    int64_t dst_bstride, int P, int C, int batches, int cus, hipStream_t st);
+hipError_t launch_gate_grad(const moe_shape_t& s, const float* topk_w, const int32_t* topk_idx, const int32_t* slot_of,
+                            const float* dgp, float* const* dlogits, int cus, hipStream_t st);
+hipError_t launch_push_grad(const moe_shape_t& s, const char* dX, const float* dg, const int32_t* pull_src,
+                            const int32_t* slot_of, void* const* recv, float* dgp, const int32_t* ctrl, int cus,
+                            hipStream_t st);
 }  // namespace moe
 
 using namespace moe;
@@ -116,6 +136,21 @@ long long wall_ticks_per_us() {
 }
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+// backward calls: bf16 shape, the forward's workspace, and the backward workspace
+int check_bwd(const moe_shape_t* s, const moe_placement_t* p, const void* ws, size_t ws_bytes, const void* bws,
+              size_t bws_bytes) {
+  int rc = check_shape(s, p);
+  if (rc) return rc;
+  if (s->dtype != MOE_BF16) return MOE_EUNSUP;
+  if ((rc = check_ws(s, p, ws, ws_bytes))) return rc;
+  if (!bws) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(bws) & 255) return MOE_EALIGN;
+  const BwdLayout B = bwd_layout(*s, p->E_local);
+  if (bws_bytes < B.total) return MOE_ENOSPC;
+  if (B.ldt >= (int64_t(1) << 31)) return MOE_EINVAL;
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -320,6 +355,151 @@ int moe_forward_persistent(const moe_shape_t* s, const moe_placement_t* p, const
   return hip_rc(launch_merge(*s, slot_of, topk_w, recv, y, cu_count(), st));
 }
 
+size_t moe_backward_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p) {
+  if (check_shape(s, p) != MOE_OK || s->dtype != MOE_BF16) return 0;
+  return bwd_layout(*s, p->E_local).total;
+}
+
+int moe_backward_prepare(const moe_shape_t* s, const moe_placement_t* p, const void* w1, const void* w3,
+                         const void* w2, void* w13t, void* w2t, void* stream) {
+  int rc = check_shape(s, p);
+  if (rc) return rc;
+  if (s->dtype != MOE_BF16) return MOE_EUNSUP;
+  const void* bufs[] = {w1, w3, w2, w13t, w2t};
+  for (const void* b : bufs)
+    if (!aligned16(b)) return b ? MOE_EALIGN : MOE_EINVAL;
+  const int El = p->E_local, d = s->d, F = s->F, cus = cu_count();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* w13 = static_cast<uint16_t*>(w13t);
+  const int64_t fd = int64_t(F) * d;
+  // W13T[l][n][f] = W1[l][f][n], W13T[l][n][F + f] = W3[l][f][n]; W2T[l][f][n] = W2[l][n][f]
+  hipError_t e = launch_transpose_batched(static_cast<const uint16_t*>(w1), fd, w13, 2 * F, 2 * fd, F, d, El, cus, st);
+  if (e == hipSuccess)
+    e = launch_transpose_batched(static_cast<const uint16_t*>(w3), fd, w13 + F, 2 * F, 2 * fd, F, d, El, cus, st);
+  if (e == hipSuccess)
+    e = launch_transpose_batched(static_cast<const uint16_t*>(w2), fd, static_cast<uint16_t*>(w2t), d, fd, d, F, El,
+                                 cus, st);
+  return hip_rc(e);
+}
+
+int moe_combine_pull_reverse(const moe_shape_t* s, const moe_placement_t* p, const void* const* dy, const void* ye,
+                             const int32_t* pull_src, const int32_t* slot_of, const float* topk_w, const void* ws,
+                             size_t ws_bytes, void* bws, size_t bws_bytes, void* stream) {
+  int rc = check_bwd(s, p, ws, ws_bytes, bws, bws_bytes);
+  if (rc) return rc;
+  if (!pull_src || !slot_of || !topk_w) return MOE_EINVAL;
+  if (!aligned16(ye)) return ye ? MOE_EALIGN : MOE_EINVAL;
+  if ((rc = check_ptr_table(dy, s->R))) return rc;
+  const WsLayout L = ws_layout(*s, p->E_local);
+  const BwdLayout B = bwd_layout(*s, p->E_local);
+  char* b = static_cast<char*>(bws);
+  return hip_rc(launch_pull_reverse(*s, dy, static_cast<const uint16_t*>(ye), pull_src, slot_of, topk_w,
+                                    reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + L.ctrl),
+                                    reinterpret_cast<uint16_t*>(b + B.dO), reinterpret_cast<float*>(b + B.dg),
+                                    cu_count(), static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_ffn_backward(const moe_shape_t* s, const moe_placement_t* p, const void* xe, const int32_t* offsets,
+                            const void* w1, const void* w3, const void* w13t, const void* w2t, const void* ws,
+                            size_t ws_bytes, void* dw1, void* dw3, void* dw2, void* bws, size_t bws_bytes,
+                            void* stream) {
+  int rc = check_bwd(s, p, ws, ws_bytes, bws, bws_bytes);
+  if (rc) return rc;
+  if (!offsets) return MOE_EINVAL;
+  const void* bufs[] = {xe, w1, w3, w13t, w2t, dw1, dw3, dw2};
+  for (const void* q : bufs)
+    if (!aligned16(q)) return q ? MOE_EALIGN : MOE_EINVAL;
+  const WsLayout L = ws_layout(*s, p->E_local);
+  const BwdLayout B = bwd_layout(*s, p->E_local);
+  const char* w = static_cast<const char*>(ws);
+  const int32_t* ctrl = reinterpret_cast<const int32_t*>(w + L.ctrl);
+  const int32_t* mtb = reinterpret_cast<const int32_t*>(w + L.mtile_base);
+  char* b = static_cast<char*>(bws);
+  uint16_t* dO = reinterpret_cast<uint16_t*>(b + B.dO);
+  uint16_t* dh = reinterpret_cast<uint16_t*>(b + B.dh);
+  uint16_t* h = reinterpret_cast<uint16_t*>(b + B.h);
+  uint16_t* dab = reinterpret_cast<uint16_t*>(b + B.dab);
+  uint16_t* dX = reinterpret_cast<uint16_t*>(b + B.dX);
+  int32_t* poff = reinterpret_cast<int32_t*>(b + B.poff);
+  uint16_t* xeT = reinterpret_cast<uint16_t*>(b + B.xeT);
+  uint16_t* dOT = reinterpret_cast<uint16_t*>(b + B.dOT);
+  uint16_t* daT = reinterpret_cast<uint16_t*>(b + B.daT);
+  uint16_t* dbT = reinterpret_cast<uint16_t*>(b + B.dbT);
+  uint16_t* hT = reinterpret_cast<uint16_t*>(b + B.hT);
+  const uint16_t* xeb = static_cast<const uint16_t*>(xe);
+  const int El = p->E_local, d = s->d, F = s->F, cus = cu_count();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // dh = dO W2, then (h, da, db) in GEMM1's backward epilogue, then dX = [da|db] [W1|W3]
+  hipError_t e = launch_rows_gemm(dO, static_cast<const uint16_t*>(w2t), dh, d, F, offsets, mtb, ctrl, El, cus, st);
+  if (e == hipSuccess)
+    e = launch_gemm1_bwd(xeb, static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), dh, h, dab, d, F,
+                         offsets, mtb, ctrl, El, cus, st);
+  if (e == hipSuccess)
+    e = launch_rows_gemm(dab, static_cast<const uint16_t*>(w13t), dX, 2 * F, d, offsets, mtb, ctrl, El, cus, st);
+  // weight gradients over each expert's rows (transposed, zero-padded operands)
+  if (e == hipSuccess) e = launch_pad_offsets(offsets, El, poff, st);
+  if (e == hipSuccess) e = launch_transpose_rows(xeb, d, xeT, d, offsets, poff, El, cus, st);
+  if (e == hipSuccess) e = launch_transpose_rows(dO, d, dOT, d, offsets, poff, El, cus, st);
+  if (e == hipSuccess) e = launch_transpose_rows(dab, 2 * F, daT, F, offsets, poff, El, cus, st);
+  if (e == hipSuccess) e = launch_transpose_rows(dab + F, 2 * F, dbT, F, offsets, poff, El, cus, st);
+  if (e == hipSuccess) e = launch_transpose_rows(h, F, hT, F, offsets, poff, El, cus, st);
+  if (e == hipSuccess) e = launch_wgrad(daT, xeT, poff, static_cast<uint16_t*>(dw1), El, F, d, cus, st);
+  if (e == hipSuccess) e = launch_wgrad(dbT, xeT, poff, static_cast<uint16_t*>(dw3), El, F, d, cus, st);
+  if (e == hipSuccess) e = launch_wgrad(dOT, hT, poff, static_cast<uint16_t*>(dw2), El, d, F, cus, st);
+  return hip_rc(e);
+}
+
+int moe_dispatch_push_reverse(const moe_shape_t* s, const moe_placement_t* p, const int32_t* pull_src,
+                              const int32_t* slot_of, const int32_t* topk_idx, const float* topk_w, const void* ws,
+                              size_t ws_bytes, void* const* recv, void* const* dx, float* const* dlogits, void* bws,
+                              size_t bws_bytes, void* stream) {
+  int rc = check_bwd(s, p, ws, ws_bytes, bws, bws_bytes);
+  if (rc) return rc;
+  if (!pull_src || !slot_of || !topk_idx || !topk_w) return MOE_EINVAL;
+  if ((rc = check_ptr_table(recv, s->R)) || (rc = check_ptr_table(dx, s->R))) return rc;
+  if (!dlogits) return MOE_EINVAL;
+  for (int r = 0; r < s->R; ++r)
+    if (!dlogits[r]) return MOE_EINVAL;
+  const WsLayout L = ws_layout(*s, p->E_local);
+  const BwdLayout B = bwd_layout(*s, p->E_local);
+  char* b = static_cast<char*>(bws);
+  const int32_t* ctrl = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + L.ctrl);
+  float* dgp = reinterpret_cast<float*>(b + B.dgp);
+  const int cus = cu_count();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_push_grad(*s, b + B.dX, reinterpret_cast<const float*>(b + B.dg), pull_src, slot_of, recv,
+                                  dgp, ctrl, cus, st);
+  if (e == hipSuccess) e = launch_merge(*s, slot_of, nullptr, recv, dx, cus, st);
+  if (e == hipSuccess) e = launch_gate_grad(*s, topk_w, topk_idx, slot_of, dgp, dlogits, cus, st);
+  return hip_rc(e);
+}
+
+int moe_backward(const moe_shape_t* s, const moe_placement_t* p, const void* const* dy, const void* xe, const void* ye,
+                 const void* w1, const void* w3, const void* w13t, const void* w2t, const int32_t* topk_idx,
+                 const float* topk_w, const int32_t* offsets, const int32_t* pull_src, const int32_t* slot_of,
+                 const void* ws, size_t ws_bytes, void* const* recv, void* const* dx, float* const* dlogits, void* dw1,
+                 void* dw3, void* dw2, void* bws, size_t bws_bytes, void* stream) {
+  int rc = check_bwd(s, p, ws, ws_bytes, bws, bws_bytes);
+  if (rc) return rc;
+  // validate every stage's arguments before launching any of them
+  if (!topk_idx || !topk_w || !offsets || !pull_src || !slot_of) return MOE_EINVAL;
+  const void* bufs[] = {xe, ye, w1, w3, w13t, w2t, dw1, dw3, dw2};
+  for (const void* q : bufs)
+    if (!aligned16(q)) return q ? MOE_EALIGN : MOE_EINVAL;
+  if ((rc = check_ptr_table(dy, s->R)) || (rc = check_ptr_table(recv, s->R)) || (rc = check_ptr_table(dx, s->R)))
+    return rc;
+  if (!dlogits) return MOE_EINVAL;
+  for (int r = 0; r < s->R; ++r)
+    if (!dlogits[r]) return MOE_EINVAL;
+  if ((rc = moe_combine_pull_reverse(s, p, dy, ye, pull_src, slot_of, topk_w, ws, ws_bytes, bws, bws_bytes, stream)))
+    return rc;
+  if ((rc = moe_expert_ffn_backward(s, p, xe, offsets, w1, w3, w13t, w2t, ws, ws_bytes, dw1, dw3, dw2, bws, bws_bytes,
+                                    stream)))
+    return rc;
+  return moe_dispatch_push_reverse(s, p, pull_src, slot_of, topk_idx, topk_w, ws, ws_bytes, recv, dx, dlogits, bws,
+                                   bws_bytes, stream);
+}
+
 int moe_read_status(const void* ws, void* stream) {
   if (!ws) return MOE_EINVAL;
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_EHIP;
@@ -342,6 +522,6 @@ const char* moe_strerror(int code) {
   }
 }
 
-const char* moe_version(void) { return "libmoe 0.2 gfx950"; }
+const char* moe_version(void) { return "libmoe 0.3 gfx950"; }
 
 }  // extern "C"

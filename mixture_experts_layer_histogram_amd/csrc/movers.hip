@@ -52,13 +52,16 @@ __global__ __launch_bounds__(256) void dispatch_pull_kernel(RankPtrs<const char*
   }
 }
 
-// recv[r][t][j] = ye[s] for the pair (r, t, j) whose row is s
+// recv[r][t][j] = ye[s] for the pair (r, t, j) whose row is s.  In the backward (push
+// reverse-dispatch) ye holds dX and the row's gate gradient dg[s] travels with it into
+// dgp[r][t][j] (dg == nullptr in the forward).
 __global__ __launch_bounds__(256) void combine_push_kernel(const char* __restrict__ ye,
                                                            const int32_t* __restrict__ pull_src,
                                                            const int32_t* __restrict__ slot_of,
                                                            const int32_t* __restrict__ ctrl,
                                                            RankPtrs<char*> recv, int T, int k,
-                                                           int row_bytes) {
+                                                           int row_bytes, const float* __restrict__ dg,
+                                                           float* __restrict__ dgp) {
   const int N = ctrl[kCtrlN];
   const int lane = threadIdx.x & 63;
   const int n16 = row_bytes >> 4;
@@ -70,12 +73,14 @@ __global__ __launch_bounds__(256) void combine_push_kernel(const char* __restric
     const int32_t* so = slot_of + (int64_t(r) * T + t) * k;
     const unsigned long long hit = __ballot(lane < k && so[lane < k ? lane : 0] == s);
     const int j = hit ? __builtin_ctzll(hit) : 0;
+    if (dg && lane == 0) dgp[(int64_t(r) * T + t) * k + j] = dg[s];
     copy_row<8>(reinterpret_cast<const u32x4*>(ye + int64_t(s) * row_bytes),
              reinterpret_cast<u32x4*>(recv.p[r] + (int64_t(t) * k + j) * row_bytes), n16, lane);
   }
 }
 
 // y[r][t] = sum over ascending j with a local expert of g[r][t][j] * recv[r][t][j]
+// (g = 1 when topk_w is null: the backward's ordered sum of the pushed dX rows)
 // A wave task is one column segment (64 * VPL 16-byte vectors) of one token row.  The
 // token's local j are compacted into a mask; for each local j all VPL loads of the
 // segment are issued before any is used, so a task costs one memory round trip per j.
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(256) void weighted_merge_kernel(RankPtrs<const char
     const int r = int(g / T);
     const int t = int(g - int64_t(r) * T);
     const int32_t* so = slot_of + g * k;
-    const float* gw = topk_w + g * k;
+    const float* gw = topk_w ? topk_w + g * k : nullptr;
     // the token's local j (ascending) as a bit mask: lanes 0..k-1 test their entry at once
     const unsigned long long lm = __ballot(lane < k && so[lane < k ? lane : 0] >= 0);
     uint32_t local = uint32_t(lm);
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(256) void weighted_merge_kernel(RankPtrs<const char
       for (int e = 0; e < EPV; ++e) acc[u][e] = 0.0f;
     for (uint32_t m = local; m; m &= m - 1) {
       const int j = __builtin_ctz(m);
-      const float gj = gw[j];
+      const float gj = gw ? gw[j] : 1.0f;
       const u32x4* src = reinterpret_cast<const u32x4*>(rrow + int64_t(j) * row_bytes);
       u32x4 v[VPL];
 #pragma unroll
@@ -176,7 +181,18 @@ hipError_t launch_push(const moe_shape_t& s, const char* ye, const int32_t* pull
   for (int r = 0; r < s.R; ++r) rp.p[r] = static_cast<char*>(recv[r]);
   const int row_bytes = s.d * (s.dtype == MOE_F32 ? 4 : 2);
   hipLaunchKernelGGL(combine_push_kernel, dim3(cus * kPushBlocksPerCU), dim3(256), 0, st, ye, pull_src, slot_of, ctrl, rp,
-                     s.T, s.k, row_bytes);
+                     s.T, s.k, row_bytes, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+// push reverse-dispatch: dX rows to recv[r][t][j], their dg to dgp[r][t][j]
+hipError_t launch_push_grad(const moe_shape_t& s, const char* dX, const float* dg, const int32_t* pull_src,
+                            const int32_t* slot_of, void* const* recv, float* dgp, const int32_t* ctrl, int cus,
+                            hipStream_t st) {
+  RankPtrs<char*> rp{};
+  for (int r = 0; r < s.R; ++r) rp.p[r] = static_cast<char*>(recv[r]);
+  hipLaunchKernelGGL(combine_push_kernel, dim3(cus * kPushBlocksPerCU), dim3(256), 0, st, dX, pull_src, slot_of, ctrl, rp,
+                     s.T, s.k, s.d * 2, dg, dgp);
   return hipGetLastError();
 }
 

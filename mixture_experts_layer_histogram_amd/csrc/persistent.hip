@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
         io.o_ld = A.F;
         const uint16_t* b0 = A.w1 + size_t(l) * A.F * A.d;
         const uint16_t* b1 = A.w3 + size_t(l) * A.F * A.d;
-        gemm_tile<0>(io, b0, b1, j * (kGemmBN / 2), A.F, A.d, smem);
+        gemm_tile<0>(io, b0, b1, j * (kGemmBN / 2), A.F, A.d, smem, A.d);
         release_add(g1_done + m, 1, light);
       } else {
         io.a0 = reinterpret_cast<const uint16_t*>(s0 + xpart);
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
         io.a_ld = A.F;
         io.o_ld = A.d;
         const uint16_t* b0 = A.w2 + size_t(l) * A.d * A.F;
-        gemm_tile<1>(io, b0, b0, (j - NT1) * kGemmBN, A.d, A.F, smem);
+        gemm_tile<1>(io, b0, b0, (j - NT1) * kGemmBN, A.d, A.F, smem, A.F);
         release_add(g2_done + m, 1, light);
       }
     }

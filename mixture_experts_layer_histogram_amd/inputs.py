@@ -13,6 +13,8 @@ Recipe (one generator per tensor, NumPy PCG64 seeded with ``[seed, tag, i]``):
   because logits are an *input* of the layer's boundary (the caller owns the
   router projection).
 * ``W1, W3``   ~ N(0, 1/d), ``[E_local][F][d]``;  ``W2`` ~ N(0, 1/F), ``[E_local][d][F]``.
+* ``dY_r``     ~ N(0, 1), one ``[T][d]`` buffer per rank: the incoming gradient of the
+  layer output for the backward (``make_dy``).
 * skewed load: ``logit[t, e] = tau * ln p[pi(e)] + Gumbel(0, 1)`` with ``p`` the
   Zipf(s) distribution over popularity ranks 1..E and ``pi`` a seeded
   permutation, swapped so that the most popular expert is local.
@@ -30,7 +32,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # tensor tags for the seed sequence (fixed per tensor kind)
-TAG_X, TAG_WR, TAG_W1, TAG_W3, TAG_W2, TAG_GUMBEL, TAG_PERM = range(7)
+TAG_X, TAG_WR, TAG_W1, TAG_W3, TAG_W2, TAG_GUMBEL, TAG_PERM, TAG_DY = range(8)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -149,6 +151,13 @@ def make_inputs(cfg, seed: int = 0, want_f32_weights: bool = True,
     return MoEInputs(cfg=cfg, logits=logits, x_f32=x_f32, w1_f32=w1_f32, w3_f32=w3_f32,
                      w2_f32=w2_f32, expert_to_local=e2l, x_store=x_store,
                      w1_store=w1_store, w3_store=w3_store, w2_store=w2_store)
+
+
+def make_dy(cfg, seed: int = 0, threads: int | None = None):
+    """Incoming gradient of y: ([R][T][d] bf16 bits, their exact float32 values)."""
+    threads = threads or min(16, os.cpu_count() or 1)
+    bits = _normal_stack(seed, TAG_DY, cfg.R, (cfg.T, cfg.d), 1.0, "bf16", threads)
+    return bits, bf16_bits_to_f32(bits)
 
 
 def zipf_probs(E: int, s: float) -> np.ndarray:

@@ -208,3 +208,75 @@ def test_persistent_entry_is_switched_off():
     rc = L.moe_forward_persistent(ctypes.byref(s), ctypes.byref(p), None, tabp, tabp, FAKE, FAKE, FAKE, FAKE,
                                   1 << 40, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
     assert rc == -6
+
+
+def test_backward_entry_points_reject_bad_arguments_before_launch():
+    L = moe.lib()
+    s, p = _shape(), _pl()
+    tab = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    tabp = ctypes.cast(tab, ctypes.c_void_p)
+    big = 1 << 40
+    bws = moe.moe_backward_workspace_bytes(s, p)
+    assert bws > 0 and bws % 256 == 0
+    # per-row gradients plus the transposed operands dominate
+    assert bws >= 8 * 4096 * 8 * (7168 * 4 + 2048 * 7) * 2
+    assert moe.moe_backward_workspace_bytes(_shape(dtype=moe.MOE_MXFP8), p) == 0     # bf16 only
+    assert moe.moe_backward_workspace_bytes(_shape(dtype=moe.MOE_F32), p) == 0
+
+    def prep(shape=s, w=FAKE, out=FAKE):
+        return L.moe_backward_prepare(ctypes.byref(shape), ctypes.byref(p), w, FAKE, FAKE, out, FAKE, None)
+    assert prep(shape=_shape(dtype=moe.MOE_MXFP8)) == -6
+    assert prep(shape=_shape(dtype=moe.MOE_F32)) == -6
+    assert prep(shape=_shape(d=100)) == -2
+    assert prep(w=None) == -1
+    assert prep(out=FAKE + 2) == -2
+
+    def bwd(shape=s, xe=FAKE, dy=tabp, dlog=tabp, ws_bytes=big, bws_ptr=FAKE, bws_bytes=big, dw2=FAKE):
+        return L.moe_backward(ctypes.byref(shape), ctypes.byref(p), dy, xe, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, tabp, tabp, dlog, FAKE, FAKE, dw2, bws_ptr,
+                              bws_bytes, None)
+    assert bwd(shape=_shape(dtype=moe.MOE_MXFP8)) == -6
+    assert bwd(shape=_shape(k=0)) == -1
+    assert bwd(xe=None) == -1
+    assert bwd(xe=FAKE + 8) == -2
+    assert bwd(dw2=None) == -1
+    assert bwd(dy=None) == -1
+    assert bwd(dlog=None) == -1
+    assert bwd(ws_bytes=1024) == -3                                     # the forward's workspace
+    assert bwd(bws_ptr=None) == -1
+    assert bwd(bws_ptr=FAKE + 16) == -2
+    assert bwd(bws_bytes=bws - 1) == -3
+
+
+def test_backward_stage_entries_reject_bad_arguments_before_launch():
+    L = moe.lib()
+    s, p = _shape(), _pl()
+    tab = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    tabp = ctypes.cast(tab, ctypes.c_void_p)
+    big = 1 << 40
+    bws = moe.moe_backward_workspace_bytes(s, p)
+    mx = _shape(dtype=moe.MOE_MXFP8)
+
+    def pull(shape=s, dy=tabp, ye=FAKE, bb=big):
+        return L.moe_combine_pull_reverse(ctypes.byref(shape), ctypes.byref(p), dy, ye, FAKE, FAKE, FAKE, FAKE, big,
+                                          FAKE, bb, None)
+    assert pull(shape=mx) == -6
+    assert pull(dy=None) == -1
+    assert pull(ye=FAKE + 2) == -2
+    assert pull(bb=bws - 256) == -3
+
+    def ffn(shape=s, xe=FAKE, dw1=FAKE, ws_bytes=big):
+        return L.moe_expert_ffn_backward(ctypes.byref(shape), ctypes.byref(p), xe, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                         FAKE, ws_bytes, dw1, FAKE, FAKE, FAKE, big, None)
+    assert ffn(shape=mx) == -6
+    assert ffn(xe=None) == -1
+    assert ffn(dw1=FAKE + 4) == -2
+    assert ffn(ws_bytes=0) == -3
+
+    def push(shape=s, recv=tabp, dlog=tabp, bptr=FAKE):
+        return L.moe_dispatch_push_reverse(ctypes.byref(shape), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, big,
+                                           recv, tabp, dlog, bptr, big, None)
+    assert push(shape=mx) == -6
+    assert push(recv=None) == -1
+    assert push(dlog=None) == -1
+    assert push(bptr=FAKE + 128) == -2

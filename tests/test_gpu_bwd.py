@@ -1,0 +1,162 @@
+"""GPU parity of the backward (bf16): moe_backward, after moe_forward, against the fp64
+backward oracle on the same seeded inputs.
+
+Bar: dx per token and every row of dw1 / dw3 / dw2 within the bf16 row-relative 2e-2
+(max |err| / max |ref| over the row); the logit gradient of a token within 2e-2 of
+max_j g_j |dY| |o_j|: dl_j is built from the dot products dg_j = <dY, o_j>, which can
+cancel to any size, while their error is bounded by |dY| |o_j - o_j'| (Cauchy-Schwarz),
+so the bar is relative to that bound rather than to dl itself;
+tokens with no local pair get exactly zero dx and dlogits, logits that were not kept
+get exactly 0, an expert with no rows gets exactly zero weight gradients;
+moe_backward_prepare's transposes are bit-exact; two runs, and the three stage calls,
+are bit-identical.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle_bwd as B
+from mixture_experts_layer_histogram_amd import configs, inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+CASES = [
+    # several row tiles per expert, ragged; 2 column tiles in dX; 2 row tiles (ragged) in dW2
+    ("bwd-ragged R1 T1024 d512 E8/8 k2 F384", dict(R=1, T=1024, d=512, E=8, E_local=8, k=2, F=384), None),
+    # remote experts, top-4 of 16
+    ("bwd-remote R2 T256 d256 E16/8 k4 F256", dict(R=2, T=256, d=256, E=16, E_local=8, k=4, F=256), None),
+    # one local expert never chosen (its logit pushed down): zero weight gradients
+    ("bwd-empty-expert R2 T512 d384 E32/8 k4 F320", dict(R=2, T=512, d=384, E=32, E_local=8, k=4, F=320), 3),
+]
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _bf16_to_f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _row_rel(g, r):
+    num = np.abs(g - r).max(axis=-1)
+    den = np.abs(r).max(axis=-1)
+    return float((num / np.maximum(den, 1e-30)).max()) if num.size else 0.0
+
+
+def _dl_scale(ref, dy):
+    """Per token: max over its local pairs of g_j |dY[r][t]| |o_j| (fp64 oracle values)."""
+    so = ref["slot_of"]
+    on = np.linalg.norm(ref["ye"], axis=-1)                  # |o_s| per row
+    dyn = np.linalg.norm(dy.astype(np.float64), axis=-1)     # [R][T]
+    t = np.where(so >= 0, ref["gates"] * on[np.maximum(so, 0)], 0.0)
+    return t.max(axis=-1) * dyn
+
+
+def _run(name, dims, dead_expert, seed=0):
+    from mixture_experts_layer_histogram_amd.device import DeviceProblem
+    cfg = configs.MoEConfig(name, dtype="bf16", **dims)
+    inp = inputs.make_inputs(cfg, seed=seed)
+    if dead_expert is not None:
+        inp.logits[..., dead_expert] -= 100.0        # global id == local id here
+    dy_bits, dy = inputs.make_dy(cfg, seed=seed)
+    _say(f"[bwd] {name}: forward + backward on cuda:0")
+    dp = DeviceProblem(cfg, inp)
+    dp.alloc_backward(dy_bits)
+    dp.forward()
+    dp.prepare_backward()
+    dp.backward()
+    dp.torch.cuda.synchronize()
+    assert dp.status() == 0
+    got = dict(dx=np.stack([_bf16_to_f64(t) for t in dp.dx]),
+               dlogits=np.stack([t.cpu().numpy().astype(np.float64) for t in dp.dlogits]),
+               dw1=_bf16_to_f64(dp.dw1), dw3=_bf16_to_f64(dp.dw3), dw2=_bf16_to_f64(dp.dw2))
+    _say(f"[bwd] {name}: oracle")
+    ref = B.backward(inp.logits, inp.x_f32, inp.w1_f32, inp.w3_f32, inp.w2_f32, inp.expert_to_local,
+                     cfg.E_local, cfg.k, dy, minibatch=cfg.minibatch)
+    return cfg, dp, got, dict(ref, dy=dy)
+
+
+@pytest.mark.parametrize("name,dims,dead", CASES, ids=[c[0].split()[0] for c in CASES])
+def test_backward_matches_oracle(name, dims, dead):
+    cfg, dp, got, ref = _run(name, dims, dead)
+    so = ref["slot_of"]
+    has = (so >= 0).any(-1)
+    assert has.any() and (~has).any() or cfg.E_local == cfg.E
+    # dx
+    e_dx = _row_rel(got["dx"][has], ref["dx"][has])
+    _say(f"[bwd] {name}: dx row-rel {e_dx:.3e}")
+    assert e_dx <= TOL
+    assert np.all(got["dx"][~has] == 0.0)
+    # weight gradients, per row; experts without rows exactly zero
+    off = ref["offsets"]
+    worst = {}
+    for key in ("dw1", "dw3", "dw2"):
+        for l in range(cfg.E_local):
+            if off[l + 1] == off[l]:
+                assert np.all(got[key][l] == 0.0), (key, l)
+            else:
+                e = _row_rel(got[key][l], ref[key][l])
+                worst[key] = max(worst.get(key, 0.0), e)
+                assert e <= TOL, (key, l, e)
+    _say(f"[bwd] {name}: weight gradients row-rel " + ", ".join(f"{k_} {v:.3e}" for k_, v in worst.items()))
+    if dead is not None:
+        assert off[dead + 1] == off[dead]
+    # logit gradients: kept positions against the Cauchy-Schwarz scale, the rest exactly 0
+    scale = _dl_scale(ref, ref["dy"])
+    idx = ref["idx"]
+    kept = np.zeros(got["dlogits"].shape, dtype=bool)
+    np.put_along_axis(kept, idx.astype(np.int64), True, axis=-1)
+    assert np.all(got["dlogits"][~kept] == 0.0)
+    err = np.abs(got["dlogits"] - ref["dlogits"]).max(axis=-1)
+    assert np.all(got["dlogits"][~has] == 0.0)
+    e_dl = float((err[has] / np.maximum(scale[has], 1e-30)).max())
+    _say(f"[bwd] {name}: dlogits scaled error {e_dl:.3e}")
+    assert e_dl <= TOL
+
+
+def test_prepare_transposes_bit_exact():
+    from mixture_experts_layer_histogram_amd.device import DeviceProblem
+    name, dims, _ = CASES[2]
+    cfg = configs.MoEConfig(name, dtype="bf16", **dims)
+    inp = inputs.make_inputs(cfg, seed=1)
+    _say("[bwd] prepare transposes")
+    dp = DeviceProblem(cfg, inp, alloc_outputs=False)
+    dp.alloc_backward()
+    dp.prepare_backward()
+    torch = dp.torch
+    torch.cuda.synchronize()
+    F = cfg.F
+    assert torch.equal(dp.w13t[:, :, :F], dp.w1.transpose(1, 2))
+    assert torch.equal(dp.w13t[:, :, F:], dp.w3.transpose(1, 2))
+    assert torch.equal(dp.w2t, dp.w2.transpose(1, 2))
+
+
+def test_backward_deterministic():
+    name, dims, dead = CASES[1]
+    _, dp, _, _ = _run(name, dims, dead, seed=2)
+    torch = dp.torch
+    first = [t.clone() for t in dp.dx + dp.dlogits + [dp.dw1, dp.dw3, dp.dw2]]
+    _say("[bwd] second backward")
+    dp.backward()
+    torch.cuda.synchronize()
+    again = [t.clone() for t in dp.dx + dp.dlogits + [dp.dw1, dp.dw3, dp.dw2]]
+    # the three stage entry points in order give the same bits as moe_backward
+    _say("[bwd] three stage calls")
+    for t in dp.dx + dp.dlogits + [dp.dw1, dp.dw3, dp.dw2]:
+        t.fill_(7)
+    dp.combine_reverse()
+    dp.ffn_backward()
+    dp.dispatch_reverse()
+    torch.cuda.synchronize()
+    staged = dp.dx + dp.dlogits + [dp.dw1, dp.dw3, dp.dw2]
+
+    def bits(t):
+        return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+    for a, b, c in zip(first, again, staged):
+        assert torch.equal(bits(a), bits(b))
+        assert torch.equal(bits(a), bits(c))
