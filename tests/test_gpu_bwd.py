@@ -160,3 +160,87 @@ def test_backward_deterministic():
     for a, b, c in zip(first, again, staged):
         assert torch.equal(bits(a), bits(b))
         assert torch.equal(bits(a), bits(c))
+
+
+@pytest.mark.slow
+def test_backward_full_dsv3_sampled():
+    """Full DeepSeek-V3-shaped share, in the launch configuration `bench.py --backward` times.
+
+    dx and dlogits on sampled tokens, each from the oracle run on that token alone with the
+    local experts it chose (its routing and its backward depend on no other token or
+    expert); the whole dw1, dw3 and dw2 of the most and the least loaded local expert, each
+    from the oracle run on exactly the tokens that chose it with that expert alone local
+    (the same rows, in the same order).  Sampled tokens are drawn among those whose local
+    experts fall in a set of at most 8, so the oracle widens few weight matrices."""
+    from oracle import moe_oracle as O
+    from mixture_experts_layer_histogram_amd.device import DeviceProblem
+    cfg = configs.DSV3
+    _say(f"[bwd-full] {cfg.name}: inputs")
+    inp = inputs.make_inputs(cfg, seed=0)
+    dy_bits, dy = inputs.make_dy(cfg, seed=0)
+    _say("[bwd-full] forward + backward on cuda:0")
+    dp = DeviceProblem(cfg, inp)
+    dp.alloc_backward(dy_bits)
+    dp.forward()
+    dp.prepare_backward()
+    dp.backward()
+    dp.torch.cuda.synchronize()
+    assert dp.status() == 0
+    idx, _ = O.route(inp.logits, cfg.k)
+    e2l = inp.expert_to_local
+    lay = O.layout(idx, e2l, cfg.E_local)
+    counts = np.diff(lay["offsets"])
+    hot, cold = int(np.argmax(counts)), int(np.argmin(counts))
+    cache = {}
+
+    def weights(ls):
+        for l in ls:
+            if l not in cache:
+                cache[l] = (inp.w1_f32[l], inp.w3_f32[l], inp.w2_f32[l])
+        return [np.stack([cache[l][i] for l in ls]) for i in range(3)]
+
+    # sampled tokens: local experts within a set of at most 8 (hot and cold included)
+    has = (lay["slot_of"] >= 0).any(-1)
+    tok = np.argwhere(has)
+    rng = np.random.default_rng(0)
+    allowed, picked = {hot, cold}, []
+    for i in rng.permutation(len(tok)):
+        r, t = tok[i]
+        ls = {int(e2l[e]) for e in idx[r, t] if e2l[e] >= 0}
+        if len(allowed | ls) <= 8:
+            allowed |= ls
+            picked.append((r, t))
+        if len(picked) == 8:
+            break
+    worst_dx = worst_dl = 0.0
+    for r, t in picked:
+        ls = [int(e2l[e]) for e in idx[r, t] if e2l[e] >= 0]            # the token's local experts, j order
+        e2l_t = np.full(cfg.E, -1, dtype=np.int32)
+        for i, l in enumerate(ls):
+            e2l_t[int(np.flatnonzero(e2l == l)[0])] = i
+        w1, w3, w2 = weights(ls)
+        ref = B.backward(inp.logits[r:r + 1, t:t + 1], inp.x_f32[r:r + 1, t:t + 1], w1, w3, w2, e2l_t, len(ls),
+                         cfg.k, dy[r:r + 1, t:t + 1], minibatch=cfg.minibatch)
+        worst_dx = max(worst_dx, _row_rel(_bf16_to_f64(dp.dx[r][t])[None], ref["dx"][0]))
+        dlg = dp.dlogits[r][t].cpu().numpy().astype(np.float64)
+        kept = np.zeros(cfg.E, dtype=bool)
+        kept[idx[r, t]] = True
+        assert np.all(dlg[~kept] == 0.0)
+        scale = _dl_scale(ref, dy[r:r + 1, t:t + 1])[0, 0]
+        worst_dl = max(worst_dl, float(np.abs(dlg - ref["dlogits"][0, 0]).max() / scale))
+    zr, zt = np.argwhere(~has)[0]
+    assert (dp.dx[zr][zt].float() == 0).all() and (dp.dlogits[zr][zt] == 0).all()
+    _say(f"[bwd-full] {len(picked)} sampled tokens: dx row-rel {worst_dx:.3e}, dlogits scaled {worst_dl:.3e}")
+    assert len(picked) >= 4 and worst_dx <= TOL and worst_dl <= TOL
+    for l in (hot, cold):
+        e = int(np.flatnonzero(e2l == l)[0])
+        rr, tt = np.nonzero((idx == e).any(-1))                       # ascending (r, t)
+        e2l1 = np.full(cfg.E, -1, dtype=np.int32)
+        e2l1[e] = 0
+        _say(f"[bwd-full] expert {e} (local {l}, {len(rr)} rows): oracle")
+        ref = B.backward(inp.logits[rr, tt][None], inp.x_f32[rr, tt][None], *weights([l]), e2l1, 1, cfg.k,
+                         dy[rr, tt][None], minibatch=cfg.minibatch)
+        assert ref["N"] == counts[l]
+        errs = {key: _row_rel(_bf16_to_f64(getattr(dp, key)[l]), ref[key][0]) for key in ("dw1", "dw3", "dw2")}
+        _say(f"[bwd-full] expert {e}: " + ", ".join(f"{k_} row-rel {v:.3e}" for k_, v in errs.items()))
+        assert max(errs.values()) <= TOL
