@@ -7,9 +7,9 @@ push combine and the final weighted merge.  Prints ONE JSON line on stdout.
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config dsv3]
 
 With --backward (bf16 configs) a step is instead the whole backward of the share after
-one forward: the weight transposes (moe_backward_prepare, once per weight update) and
-moe_backward's three stages (pull reverse-combine, expert SwiGLU backward with the
-weight-gradient GEMMs, push reverse-dispatch with the ordered sum and the gate gradient).
+one forward: moe_backward's three stages (pull reverse-combine, expert SwiGLU backward with
+the weight-gradient GEMMs, push reverse-dispatch with the ordered sum and the gate
+gradient).
 """
 from __future__ import annotations
 
@@ -200,10 +200,9 @@ def run_backward(args, cfg, inp, P, stream, N):
     dy_bits, dy = inputs.make_dy(cfg, seed=args.seed)
     P.alloc_backward(dy_bits)
     for _ in range(args.warmup):
-        P.prepare_backward()
         P.backward()
     torch.cuda.synchronize()
-    names = ["prepare", "pull_reverse", "ffn_backward", "push_reverse"]
+    names = ["pull_reverse", "ffn_backward", "push_reverse"]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -211,14 +210,12 @@ def run_backward(args, cfg, inp, P, stream, N):
     for i in range(args.steps):
         e = ev[i]
         e[0].record(stream)
-        P.prepare_backward()
-        e[1].record(stream)
         P.combine_reverse()
-        e[2].record(stream)
+        e[1].record(stream)
         P.ffn_backward()
-        e[3].record(stream)
+        e[2].record(stream)
         P.dispatch_reverse()
-        e[4].record(stream)
+        e[3].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
@@ -233,7 +230,6 @@ def run_backward(args, cfg, inp, P, stream, N):
     push_bytes = 2.0 * N * row + N * 12            # dX rows to recv, dg beside them
     merge_bytes = 1.0 * N * row + cfg.R * cfg.T * row
     gate_bytes = cfg.R * cfg.T * (cfg.k * 16 + cfg.E * 4)
-    prep_bytes = 2.0 * 3 * cfg.E_local * cfg.F * cfg.d * 2
     tokens = cfg.R * cfg.T / cfg.G
     result = {
         "metric": METRIC_BWD,
@@ -251,14 +247,13 @@ def run_backward(args, cfg, inp, P, stream, N):
                 "router logits x@W_r)",
         "config": {"workload": cfg.name, "R": cfg.R, "T": cfg.T, "d": cfg.d, "E": cfg.E, "E_local": cfg.E_local,
                    "k": cfg.k, "F": cfg.F, "local_pairs": N,
-                   "path": "backward after one forward: weight transposes + three stage calls on one stream"},
+                   "path": "backward after one forward: three stage calls on one stream"},
         "roofline": {"bound": "mfma", "kernel": "expert SwiGLU backward stage (dh, GEMM1+SwiGLU backward, dX, "
-                                                 "dW1/dW3/dW2 GEMMs, operand transposes)",
+                                                 "dW1/dW3/dW2 GEMMs)",
                      "achieved": flops / t_ffn / 1e12, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": flops / t_ffn / PEAK_BF16_FLOPS, "traffic": None},
         "stages_ms": stage_ms,
         "stages_hbm_frac": {
-            "prepare": prep_bytes / (stage_ms["prepare"] * 1e-3) / PEAK_HBM,
             "pull_reverse": pull_bytes / (stage_ms["pull_reverse"] * 1e-3) / PEAK_HBM,
             "push_reverse": (push_bytes + merge_bytes + gate_bytes) / (stage_ms["push_reverse"] * 1e-3) / PEAK_HBM,
         },

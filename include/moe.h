@@ -276,16 +276,6 @@ size_t moe_persistent_workspace_bytes(const moe_shape_t* s, const moe_placement_
 size_t moe_backward_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p);
 
 /*
- * moe_backward_prepare -- the transposed expert weights the backward's row GEMMs read,
- * built once per weight update:
- *   w13t[l][n][f] = w1[l][f][n],  w13t[l][n][F + f] = w3[l][f][n]   [E_local][d][2F]
- *   w2t[l][f][n]  = w2[l][n][f]                                     [E_local][F][d]
- * w1, w3: [E_local][F][d]; w2: [E_local][d][F]; all bf16, 16-byte aligned.  Bit-exact.
- */
-int moe_backward_prepare(const moe_shape_t* s, const moe_placement_t* p, const void* w1, const void* w3,
-                         const void* w2, void* w13t, void* w2t, void* stream);
-
-/*
  * The backward in three stages (moe_backward runs them in order).  Inputs common to all:
  * the forward's outputs (xe and ye as moe_forward left them, [moe_max_pairs][d];
  * topk_idx, topk_w, offsets, pull_src, slot_of from moe_layout), ws = the workspace the
@@ -309,18 +299,18 @@ int moe_combine_pull_reverse(const moe_shape_t* s, const moe_placement_t* p, con
 
 /*
  * moe_expert_ffn_backward -- grouped SwiGLU backward of every local expert from the dO
- * rows in bws [kucoin §03: the backward is sped up as well]:
+ * rows in bws [kucoin §03: the backward is sped up as well].  Every operand is read as
+ * stored (no transposed copies of weights or rows):
  *   dh = dO W2; da = dh * b * silu'(a); db = dh * silu(a), silu'(a) = sigma(a) (1 + a (1 - sigma(a)));
  *   dX = da W1 + db W3 (fp32 accumulate, bf16 rows, into bws);
  *   dw1[l] = sum_s da_s^T x_s, dw3[l] = sum_s db_s^T x_s ([E_local][F][d] bf16),
  *   dw2[l] = sum_s dO_s^T h_s ([E_local][d][F] bf16), summed over the expert's rows in
  *   ascending order; an expert with no rows gets zeros.
- * w1, w3: [E_local][F][d]; w13t, w2t: moe_backward_prepare's outputs.
+ * w1, w3: [E_local][F][d]; w2: [E_local][d][F] (the forward's bf16 weights).
  */
 int moe_expert_ffn_backward(const moe_shape_t* s, const moe_placement_t* p, const void* xe, const int32_t* offsets,
-                            const void* w1, const void* w3, const void* w13t, const void* w2t, const void* ws,
-                            size_t ws_bytes, void* dw1, void* dw3, void* dw2, void* bws, size_t bws_bytes,
-                            void* stream);
+                            const void* w1, const void* w3, const void* w2, const void* ws, size_t ws_bytes, void* dw1,
+                            void* dw3, void* dw2, void* bws, size_t bws_bytes, void* stream);
 
 /*
  * moe_dispatch_push_reverse -- push reverse-dispatch [kucoin §02], then the ordered sum and
@@ -344,8 +334,7 @@ int moe_dispatch_push_reverse(const moe_shape_t* s, const moe_placement_t* p, co
  * checked before the first launch.
  */
 int moe_backward(const moe_shape_t* s, const moe_placement_t* p, const void* const* dy, const void* xe,
-                 const void* ye, const void* w1, const void* w3, const void* w13t, const void* w2t,
-                 const int32_t* topk_idx, const float* topk_w, const int32_t* offsets, const int32_t* pull_src,
+                 const void* ye, const void* w1, const void* w3, const void* w2, const int32_t* topk_idx, const float* topk_w, const int32_t* offsets, const int32_t* pull_src,
                  const int32_t* slot_of, const void* ws, size_t ws_bytes, void* const* recv, void* const* dx,
                  float* const* dlogits, void* dw1, void* dw3, void* dw2, void* bws, size_t bws_bytes,
                  void* stream);

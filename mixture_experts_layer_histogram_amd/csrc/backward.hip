@@ -11,11 +11,8 @@
 //     ordered sum over ascending j gives dx[r][t];
 //   gate gradient: for the k kept experts of a token dl_j = g_j (dg_j - sum_i g_i dg_i),
 //     the other logits get 0; a pair whose expert is not local has dg = 0 here.
-// The weight-gradient GEMMs contract over an expert's rows, so their operands are the
-// expert rows transposed, one contiguous [cols][K_l] block per expert with K_l its row
-// count rounded up to 64 (one K step) and the padding zero; transpose_kernel builds them
-// (and the transposed weights the backward's row GEMMs read).  Everything here is
-// HBM-bound: 16-byte vectors per lane.
+// The grouped GEMMs of the backward are in gemm_bwd.hip (and GEMM1's backward epilogue in
+// gemm_tile.hpp).  Everything here is HBM-bound: 16-byte vectors per lane.
 #include "common.hpp"
 
 namespace moe {
@@ -75,89 +72,6 @@ __global__ __launch_bounds__(256) void pull_reverse_kernel(RankPtrs<const char*>
   }
 }
 
-// poff[l] = sum over l' < l of round_up(offsets[l'+1] - offsets[l'], 64); poff[El] = Np.
-// One wave, 64 experts per step.
-__global__ __launch_bounds__(64) void pad_offsets_kernel(const int32_t* __restrict__ offsets, int El,
-                                                         int32_t* __restrict__ poff) {
-  const int lane = threadIdx.x;
-  int run = 0;
-  for (int base = 0; base < El; base += 64) {
-    const int l = base + lane;
-    const int v = l < El ? ((offsets[l + 1] - offsets[l] + 63) & ~63) : 0;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    if (l < El) poff[l] = run + incl - v;
-    run += __shfl(incl, 63);
-  }
-  if (lane == 0) poff[El] = run;
-}
-
-// Transposes in 64 x 64 tiles through LDS.
-//   poff != nullptr (expert rows): p runs over [0, poff[El]); for p in expert l's padded
-//     range, q = p - poff[l] < K_l = poff[l+1] - poff[l], the expert's block [C][K_l] at
-//     dst + C * poff[l] gets dst_l[c][q] = src[offsets[l] + q][c], or 0 past its last row.
-//     One expert's block is contiguous, so the weight-gradient GEMM reads rows K_l apart.
-//   poff == nullptr (weights): `batches` matrices of P rows each (P % 64 == 0),
-//     dst[c][p] = src[p][c] with row stride ldt.
-// C % 64 == 0; rows of src and dst are 16-byte aligned.
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src, int64_t ld_src,
-                                                        int64_t src_bstride, uint16_t* __restrict__ dst, int64_t ldt,
-                                                        int64_t dst_bstride, int C, int P, int batches,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ poff, int El) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];   // 144-byte rows: 16-byte aligned
-  const int ncb = C >> 6;
-  const int npb = poff ? (poff[El] >> 6) : (P >> 6);
-  const int64_t tasks = int64_t(poff ? 1 : batches) * npb * ncb;
-  for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
-    const int bt = int(task / (int64_t(npb) * ncb));
-    const int rem = int(task - int64_t(bt) * npb * ncb);
-    const int pb = rem / ncb, cb = rem - pb * ncb;
-    const int p0 = pb * 64, c0 = cb * 64;
-    int s0 = p0, s_end = P;
-    int64_t dbase = int64_t(bt) * dst_bstride + p0, dld = ldt;
-    if (poff) {
-      // the expert owning columns [p0, p0 + 64): the last l with poff[l] <= p0
-      int lo = 0, hi = El - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (poff[mid] <= p0) lo = mid; else hi = mid - 1;
-      }
-      s0 = offsets[lo] + (p0 - poff[lo]);
-      s_end = offsets[lo + 1];
-      dld = poff[lo + 1] - poff[lo];
-      dbase = int64_t(C) * poff[lo] + (p0 - poff[lo]);
-    }
-    const uint16_t* sb = src + int64_t(bt) * src_bstride;
-    uint16_t* db = dst + dbase;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int v = threadIdx.x + 256 * i;        // 64 rows x 8 vectors
-      const int pr = v >> 3, cv = v & 7;
-      const int s = s0 + pr;
-      u32x4 val = u32x4{0, 0, 0, 0};
-      if (s < s_end) val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sb + int64_t(s) * ld_src + c0) + cv);
-      *reinterpret_cast<u32x4*>(&tile[pr][cv * 8]) = val;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int v = threadIdx.x + 256 * i;        // 64 output rows x 8 vectors of 8 p
-      const int c = v >> 3, pv = v & 7;
-      u32x4 o;
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        o[w] = uint32_t(tile[pv * 8 + 2 * w][c]) | (uint32_t(tile[pv * 8 + 2 * w + 1][c]) << 16);
-      *reinterpret_cast<u32x4*>(db + int64_t(c0 + c) * dld + pv * 8) = o;
-    }
-    __syncthreads();
-  }
-}
-
 // dlogits[r][t][:] = 0 except dl_j at the k kept experts; one wave per token
 __global__ __launch_bounds__(256) void gate_grad_kernel(const float* __restrict__ topk_w,
                                                         const int32_t* __restrict__ topk_idx,
@@ -195,7 +109,7 @@ __global__ __launch_bounds__(256) void gate_grad_kernel(const float* __restrict_
   }
 }
 
-constexpr int kPullRevBlocksPerCU = 4, kTransposeBlocksPerCU = 8, kGateBlocksPerCU = 4;
+constexpr int kPullRevBlocksPerCU = 4, kGateBlocksPerCU = 4;
 
 hipError_t launch_pull_reverse(const moe_shape_t& s, const void* const* dy, const uint16_t* ye,
                                const int32_t* pull_src, const int32_t* slot_of, const float* topk_w,
@@ -204,25 +118,6 @@ hipError_t launch_pull_reverse(const moe_shape_t& s, const void* const* dy, cons
   for (int r = 0; r < s.R; ++r) dp.p[r] = static_cast<const char*>(dy[r]);
   hipLaunchKernelGGL(pull_reverse_kernel, dim3(cus * kPullRevBlocksPerCU), dim3(256), 0, st, dp, ye, pull_src, slot_of,
                      topk_w, ctrl, dO, dg, s.T, s.k, s.d);
-  return hipGetLastError();
-}
-
-hipError_t launch_pad_offsets(const int32_t* offsets, int El, int32_t* poff, hipStream_t st) {
-  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(64), 0, st, offsets, El, poff);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_rows(const uint16_t* src, int64_t ld_src, uint16_t* dst, int C, const int32_t* offsets,
-                                 const int32_t* poff, int El, int cus, hipStream_t st) {
-  hipLaunchKernelGGL(transpose_kernel, dim3(cus * kTransposeBlocksPerCU), dim3(256), 0, st, src, ld_src, int64_t(0), dst,
-                     int64_t(0), int64_t(0), C, 0, 1, offsets, poff, El);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_batched(const uint16_t* src, int64_t src_bstride, uint16_t* dst, int64_t ldt,
-                                    int64_t dst_bstride, int P, int C, int batches, int cus, hipStream_t st) {
-  hipLaunchKernelGGL(transpose_kernel, dim3(cus * kTransposeBlocksPerCU), dim3(256), 0, st, src, int64_t(C),
-                     src_bstride, dst, ldt, dst_bstride, C, P, batches, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 

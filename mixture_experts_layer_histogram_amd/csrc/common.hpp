@@ -66,19 +66,16 @@ inline WsLayout ws_layout(const moe_shape_t& s, int32_t E_local) {
   return w;
 }
 
-// Backward workspace (bf16): per-row gradients and the transposed, per-expert zero-padded
-// operands of the weight-gradient GEMMs (one [cols][K_l] block per expert; ldt bounds the
-// sum of the padded row counts K_l).
+// Backward workspace (bf16): the per-row gradients handed from one backward stage to the
+// next, and the per-pair gate gradients of the push.
 struct BwdLayout {
-  size_t dO, dg, dh, h, dab, dX, poff, dgp, xeT, dOT, daT, dbT, hT, total;
-  int64_t ldt;
+  size_t dO, dg, dh, h, dab, dX, dgp, total;
 };
 
 inline BwdLayout bwd_layout(const moe_shape_t& s, int32_t E_local) {
   BwdLayout b{};
   const int64_t mp = int64_t(s.R) * s.T * (s.k < E_local ? s.k : E_local);
-  b.ldt = (mp + int64_t(63) * E_local + 63) & ~int64_t(63);
-  const size_t d = size_t(s.d), F = size_t(s.F), n = size_t(mp), lt = size_t(b.ldt);
+  const size_t d = size_t(s.d), F = size_t(s.F), n = size_t(mp);
   size_t o = 0;
   b.dO = o;   o = align256(o + n * d * 2);
   b.dg = o;   o = align256(o + n * 4);
@@ -86,13 +83,7 @@ inline BwdLayout bwd_layout(const moe_shape_t& s, int32_t E_local) {
   b.h = o;    o = align256(o + n * F * 2);
   b.dab = o;  o = align256(o + n * F * 4);
   b.dX = o;   o = align256(o + n * d * 2);
-  b.poff = o; o = align256(o + size_t(E_local + 1) * 4);
   b.dgp = o;  o = align256(o + size_t(s.R) * s.T * s.k * 4);
-  b.xeT = o;  o = align256(o + d * lt * 2);
-  b.dOT = o;  o = align256(o + d * lt * 2);
-  b.daT = o;  o = align256(o + F * lt * 2);
-  b.dbT = o;  o = align256(o + F * lt * 2);
-  b.hT = o;   o = align256(o + F * lt * 2);
   b.total = o;
   return b;
 }

@@ -17,8 +17,7 @@
 namespace moe {
 
 // MODE 0: A = xe [*][d], B0 = W1, B1 = W3 -> C = h [*][F]   (tile = 256 rows x 128 f)
-// MODE 1: A = [*][K],    B0 = [Nout][K]   -> C = [*][Nout]   (tile = 256 rows x 256 cols)
-//         (GEMM2 y = h W2^T; in the backward dh = dO W2 and dX = [da | db] [W1 | W3])
+// MODE 1: A = h [*][F],  B0 = W2          -> C = ye [*][d]  (tile = 256 rows x 256 cols)
 // MODE 2: as MODE 0, with the backward epilogue: DH in, C = h, DAB = [da | db] out
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
@@ -60,55 +59,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t* b0 = B0 + size_t(l) * Nout * K;
     const uint16_t* b1 = (MODE != 1) ? B1 + size_t(l) * Nout * K : b0;
     gemm_tile<MODE>(io, b0, b1, nt * cols_per_tile, Nout, K, smem, K);
-  }
-}
-
-// Weight gradients of every local expert: C_l [M][Nc] = A_l [M][K_l] * B_l [Nc][K_l]^T,
-// where A_l (at A + M * poff[l]) and B_l (at Bm + Nc * poff[l]) hold the expert's rows
-// transposed, zero-padded to K_l = poff[l+1] - poff[l], a multiple of 64 -- whole K steps
-// (the K of these GEMMs is the expert's rows; they run in ascending order, so the sum
-// order is fixed).
-// dW1 = daT xeT^T, dW3 = dbT xeT^T, dW2 = dOT hT^T.  An expert with no rows gets zeros.
-__global__ __launch_bounds__(kGemmThreads, 1) void grouped_wgrad_bf16_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm, const int32_t* __restrict__ poff,
-    uint16_t* __restrict__ C, int El, int M, int Nc) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int MT = (M + kGemmBM - 1) / kGemmBM, NT = (Nc + kGemmBN - 1) / kGemmBN;
-  const int total = El * MT * NT;
-  const int per_xcd = (total + 7) >> 3;
-  const int xcd = blockIdx.x & 7;
-  const int wg_per_xcd = gridDim.x >> 3;
-  for (int tt = blockIdx.x >> 3; tt < per_xcd; tt += wg_per_xcd) {
-    const int tau = xcd * per_xcd + tt;
-    if (tau >= total) break;
-    const int l = tau / (MT * NT);
-    const int rem = tau - l * MT * NT;
-    const int nt = rem / MT, mt = rem - nt * MT;    // row tiles innermost: shared B panel
-    const int m0 = mt * kGemmBM, c0 = nt * kGemmBN;
-    const int rows = min(kGemmBM, M - m0);
-    uint16_t* out = C + (size_t(l) * M + m0) * Nc;
-    const int p0 = poff[l];
-    const int K = poff[l + 1] - p0;
-    if (K == 0) {
-      const int ncols = min(kGemmBN, Nc - c0);
-      for (int v = threadIdx.x; v < kGemmBM * (kGemmBN / 8); v += kGemmThreads) {
-        const int row = v >> 5, cv = v & 31;
-        if (row < rows && cv * 8 < ncols)
-          *reinterpret_cast<u32x4*>(out + size_t(row) * Nc + c0 + cv * 8) = u32x4{0, 0, 0, 0};
-      }
-      continue;
-    }
-    TileIO io;
-    io.a0 = io.a1 = io.a2 = io.a3 = A + size_t(M) * p0 + size_t(m0) * K;
-    io.o0 = io.o1 = io.o2 = io.o3 = out;
-    io.a_ld = K;
-    io.o_ld = Nc;
-    io.blk_log2 = 8;
-    io.rows = rows;
-    io.dh = nullptr;
-    io.dab = nullptr;
-    const uint16_t* bl = Bm + size_t(Nc) * p0;
-    gemm_tile<1>(io, bl, bl, c0, Nc, K, smem, K);
   }
 }
 
@@ -159,8 +109,7 @@ hipError_t set_gemm_lds_attrs() {
   if (done) return hipSuccess;
   const void* ks[] = {reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<0>),
                       reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<1>),
-                      reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<2>),
-                      reinterpret_cast<const void*>(grouped_wgrad_bf16_kernel)};
+                      reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<2>)};
   for (const void* k : ks) {
     const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
     if (e != hipSuccess) return e;
@@ -197,17 +146,7 @@ hipError_t launch_ffn(const moe_shape_t& s, int El, const void* xe, const int32_
   return hipGetLastError();
 }
 
-// ---- backward GEMMs (bf16) ----
-// C[s] = A[s] B_l^T for the rows of every local expert (B_l: [Nout][K] per expert)
-hipError_t launch_rows_gemm(const uint16_t* A, const uint16_t* B, uint16_t* C, int K, int Nout, const int32_t* offsets,
-                            const int32_t* mtb, const int32_t* ctrl, int El, int cus, hipStream_t st) {
-  hipError_t e = set_gemm_lds_attrs();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<1>, dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st, A, B,
-                     nullptr, C, offsets, mtb, ctrl, El, K, Nout, nullptr, nullptr);
-  return hipGetLastError();
-}
-
+// ---- backward (bf16) ----
 // GEMM1 again with the backward epilogue: h and [da | db] from xe, W1, W3 and dh
 hipError_t launch_gemm1_bwd(const uint16_t* xe, const uint16_t* w1, const uint16_t* w3, const uint16_t* dh,
                             uint16_t* h, uint16_t* dab, int d, int F, const int32_t* offsets, const int32_t* mtb,
@@ -216,15 +155,6 @@ hipError_t launch_gemm1_bwd(const uint16_t* xe, const uint16_t* w1, const uint16
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<2>, dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st, xe, w1, w3,
                      h, offsets, mtb, ctrl, El, d, F, dh, dab);
-  return hipGetLastError();
-}
-
-hipError_t launch_wgrad(const uint16_t* At, const uint16_t* Bt, const int32_t* poff, uint16_t* C, int El, int M, int Nc,
-                        int cus, hipStream_t st) {
-  hipError_t e = set_gemm_lds_attrs();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(grouped_wgrad_bf16_kernel, dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st, At, Bt, poff, C,
-                     El, M, Nc);
   return hipGetLastError();
 }
 

@@ -31,21 +31,17 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
                              const int32_t* offsets, char* ring, long long slot_bytes, int slots, int blk_log2,
                              int comm_cus, int n_part, int cus, long long budget, void* const* recv, char* ws,
                              const WsLayout& L, hipStream_t st);
-hipError_t launch_rows_gemm(const uint16_t* A, const uint16_t* B, uint16_t* C, int K, int Nout, const int32_t* offsets,
-                            const int32_t* mtb, const int32_t* ctrl, int El, int cus, hipStream_t st);
+hipError_t launch_rows_bmn(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, int ksplit, uint16_t* C, int K,
+                           int Nout, const int32_t* offsets, const int32_t* mtb, const int32_t* ctrl, int El, int cus,
+                           hipStream_t st);
 hipError_t launch_gemm1_bwd(const uint16_t* xe, const uint16_t* w1, const uint16_t* w3, const uint16_t* dh,
                             uint16_t* h, uint16_t* dab, int d, int F, const int32_t* offsets, const int32_t* mtb,
                             const int32_t* ctrl, int El, int cus, hipStream_t st);
-hipError_t launch_wgrad(const uint16_t* At, const uint16_t* Bt, const int32_t* poff, uint16_t* C, int El, int M, int Nc,
-                        int cus, hipStream_t st);
+hipError_t launch_wgrad(const uint16_t* A, int lda, const uint16_t* B, int ldb, const int32_t* offsets, uint16_t* C,
+                        int El, int M, int Nc, int cus, hipStream_t st);
 hipError_t launch_pull_reverse(const moe_shape_t& s, const void* const* dy, const uint16_t* ye,
                                const int32_t* pull_src, const int32_t* slot_of, const float* topk_w,
                                const int32_t* ctrl, uint16_t* dO, float* dg, int cus, hipStream_t st);
-hipError_t launch_pad_offsets(const int32_t* offsets, int El, int32_t* poff, hipStream_t st);
-hipError_t launch_transpose_rows(const uint16_t* src, int64_t ld_src, uint16_t* dst, int C, const int32_t* offsets,
-                                 const int32_t* poff, int El, int cus, hipStream_t st);
-hipError_t launch_transpose_batched(const uint16_t* src, int64_t src_bstride, uint16_t* dst, int64_t ldt,
-                                    int64_t dst_bstride, int P, int C, int batches, int cus, hipStream_t st);
 hipError_t launch_gate_grad(const moe_shape_t& s, const float* topk_w, const int32_t* topk_idx, const int32_t* slot_of,
                             const float* dgp, float* const* dlogits, int cus, hipStream_t st);
 hipError_t launch_push_grad(const moe_shape_t& s, const char* dX, const float* dg, const int32_t* pull_src,
@@ -146,9 +142,7 @@ int check_bwd(const moe_shape_t* s, const moe_placement_t* p, const void* ws, si
   if ((rc = check_ws(s, p, ws, ws_bytes))) return rc;
   if (!bws) return MOE_EINVAL;
   if (reinterpret_cast<uintptr_t>(bws) & 255) return MOE_EALIGN;
-  const BwdLayout B = bwd_layout(*s, p->E_local);
-  if (bws_bytes < B.total) return MOE_ENOSPC;
-  if (B.ldt >= (int64_t(1) << 31)) return MOE_EINVAL;
+  if (bws_bytes < bwd_layout(*s, p->E_local).total) return MOE_ENOSPC;
   return MOE_OK;
 }
 
@@ -360,28 +354,6 @@ size_t moe_backward_workspace_bytes(const moe_shape_t* s, const moe_placement_t*
   return bwd_layout(*s, p->E_local).total;
 }
 
-int moe_backward_prepare(const moe_shape_t* s, const moe_placement_t* p, const void* w1, const void* w3,
-                         const void* w2, void* w13t, void* w2t, void* stream) {
-  int rc = check_shape(s, p);
-  if (rc) return rc;
-  if (s->dtype != MOE_BF16) return MOE_EUNSUP;
-  const void* bufs[] = {w1, w3, w2, w13t, w2t};
-  for (const void* b : bufs)
-    if (!aligned16(b)) return b ? MOE_EALIGN : MOE_EINVAL;
-  const int El = p->E_local, d = s->d, F = s->F, cus = cu_count();
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  uint16_t* w13 = static_cast<uint16_t*>(w13t);
-  const int64_t fd = int64_t(F) * d;
-  // W13T[l][n][f] = W1[l][f][n], W13T[l][n][F + f] = W3[l][f][n]; W2T[l][f][n] = W2[l][n][f]
-  hipError_t e = launch_transpose_batched(static_cast<const uint16_t*>(w1), fd, w13, 2 * F, 2 * fd, F, d, El, cus, st);
-  if (e == hipSuccess)
-    e = launch_transpose_batched(static_cast<const uint16_t*>(w3), fd, w13 + F, 2 * F, 2 * fd, F, d, El, cus, st);
-  if (e == hipSuccess)
-    e = launch_transpose_batched(static_cast<const uint16_t*>(w2), fd, static_cast<uint16_t*>(w2t), d, fd, d, F, El,
-                                 cus, st);
-  return hip_rc(e);
-}
-
 int moe_combine_pull_reverse(const moe_shape_t* s, const moe_placement_t* p, const void* const* dy, const void* ye,
                              const int32_t* pull_src, const int32_t* slot_of, const float* topk_w, const void* ws,
                              size_t ws_bytes, void* bws, size_t bws_bytes, void* stream) {
@@ -400,13 +372,12 @@ int moe_combine_pull_reverse(const moe_shape_t* s, const moe_placement_t* p, con
 }
 
 int moe_expert_ffn_backward(const moe_shape_t* s, const moe_placement_t* p, const void* xe, const int32_t* offsets,
-                            const void* w1, const void* w3, const void* w13t, const void* w2t, const void* ws,
-                            size_t ws_bytes, void* dw1, void* dw3, void* dw2, void* bws, size_t bws_bytes,
-                            void* stream) {
+                            const void* w1, const void* w3, const void* w2, const void* ws, size_t ws_bytes, void* dw1,
+                            void* dw3, void* dw2, void* bws, size_t bws_bytes, void* stream) {
   int rc = check_bwd(s, p, ws, ws_bytes, bws, bws_bytes);
   if (rc) return rc;
   if (!offsets) return MOE_EINVAL;
-  const void* bufs[] = {xe, w1, w3, w13t, w2t, dw1, dw3, dw2};
+  const void* bufs[] = {xe, w1, w3, w2, dw1, dw3, dw2};
   for (const void* q : bufs)
     if (!aligned16(q)) return q ? MOE_EALIGN : MOE_EINVAL;
   const WsLayout L = ws_layout(*s, p->E_local);
@@ -420,32 +391,21 @@ int moe_expert_ffn_backward(const moe_shape_t* s, const moe_placement_t* p, cons
   uint16_t* h = reinterpret_cast<uint16_t*>(b + B.h);
   uint16_t* dab = reinterpret_cast<uint16_t*>(b + B.dab);
   uint16_t* dX = reinterpret_cast<uint16_t*>(b + B.dX);
-  int32_t* poff = reinterpret_cast<int32_t*>(b + B.poff);
-  uint16_t* xeT = reinterpret_cast<uint16_t*>(b + B.xeT);
-  uint16_t* dOT = reinterpret_cast<uint16_t*>(b + B.dOT);
-  uint16_t* daT = reinterpret_cast<uint16_t*>(b + B.daT);
-  uint16_t* dbT = reinterpret_cast<uint16_t*>(b + B.dbT);
-  uint16_t* hT = reinterpret_cast<uint16_t*>(b + B.hT);
   const uint16_t* xeb = static_cast<const uint16_t*>(xe);
+  const uint16_t* w1b = static_cast<const uint16_t*>(w1);
+  const uint16_t* w3b = static_cast<const uint16_t*>(w3);
+  const uint16_t* w2b = static_cast<const uint16_t*>(w2);
   const int El = p->E_local, d = s->d, F = s->F, cus = cu_count();
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // dh = dO W2, then (h, da, db) in GEMM1's backward epilogue, then dX = [da|db] [W1|W3]
-  hipError_t e = launch_rows_gemm(dO, static_cast<const uint16_t*>(w2t), dh, d, F, offsets, mtb, ctrl, El, cus, st);
+  // dh = dO W2; then h, da, db in GEMM1's backward epilogue; dX = [da|db] [W1; W3]
+  hipError_t e = launch_rows_bmn(dO, w2b, nullptr, d, dh, d, F, offsets, mtb, ctrl, El, cus, st);
+  if (e == hipSuccess) e = launch_gemm1_bwd(xeb, w1b, w3b, dh, h, dab, d, F, offsets, mtb, ctrl, El, cus, st);
+  if (e == hipSuccess) e = launch_rows_bmn(dab, w1b, w3b, F, dX, 2 * F, d, offsets, mtb, ctrl, El, cus, st);
+  // weight gradients over each expert's rows: dW1 = da^T x, dW3 = db^T x, dW2 = dO^T h
+  if (e == hipSuccess) e = launch_wgrad(dab, 2 * F, xeb, d, offsets, static_cast<uint16_t*>(dw1), El, F, d, cus, st);
   if (e == hipSuccess)
-    e = launch_gemm1_bwd(xeb, static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), dh, h, dab, d, F,
-                         offsets, mtb, ctrl, El, cus, st);
-  if (e == hipSuccess)
-    e = launch_rows_gemm(dab, static_cast<const uint16_t*>(w13t), dX, 2 * F, d, offsets, mtb, ctrl, El, cus, st);
-  // weight gradients over each expert's rows (transposed, zero-padded operands)
-  if (e == hipSuccess) e = launch_pad_offsets(offsets, El, poff, st);
-  if (e == hipSuccess) e = launch_transpose_rows(xeb, d, xeT, d, offsets, poff, El, cus, st);
-  if (e == hipSuccess) e = launch_transpose_rows(dO, d, dOT, d, offsets, poff, El, cus, st);
-  if (e == hipSuccess) e = launch_transpose_rows(dab, 2 * F, daT, F, offsets, poff, El, cus, st);
-  if (e == hipSuccess) e = launch_transpose_rows(dab + F, 2 * F, dbT, F, offsets, poff, El, cus, st);
-  if (e == hipSuccess) e = launch_transpose_rows(h, F, hT, F, offsets, poff, El, cus, st);
-  if (e == hipSuccess) e = launch_wgrad(daT, xeT, poff, static_cast<uint16_t*>(dw1), El, F, d, cus, st);
-  if (e == hipSuccess) e = launch_wgrad(dbT, xeT, poff, static_cast<uint16_t*>(dw3), El, F, d, cus, st);
-  if (e == hipSuccess) e = launch_wgrad(dOT, hT, poff, static_cast<uint16_t*>(dw2), El, d, F, cus, st);
+    e = launch_wgrad(dab + F, 2 * F, xeb, d, offsets, static_cast<uint16_t*>(dw3), El, F, d, cus, st);
+  if (e == hipSuccess) e = launch_wgrad(dO, d, h, F, offsets, static_cast<uint16_t*>(dw2), El, d, F, cus, st);
   return hip_rc(e);
 }
 
@@ -475,7 +435,7 @@ int moe_dispatch_push_reverse(const moe_shape_t* s, const moe_placement_t* p, co
 }
 
 int moe_backward(const moe_shape_t* s, const moe_placement_t* p, const void* const* dy, const void* xe, const void* ye,
-                 const void* w1, const void* w3, const void* w13t, const void* w2t, const int32_t* topk_idx,
+                 const void* w1, const void* w3, const void* w2, const int32_t* topk_idx,
                  const float* topk_w, const int32_t* offsets, const int32_t* pull_src, const int32_t* slot_of,
                  const void* ws, size_t ws_bytes, void* const* recv, void* const* dx, float* const* dlogits, void* dw1,
                  void* dw3, void* dw2, void* bws, size_t bws_bytes, void* stream) {
@@ -483,7 +443,7 @@ int moe_backward(const moe_shape_t* s, const moe_placement_t* p, const void* con
   if (rc) return rc;
   // validate every stage's arguments before launching any of them
   if (!topk_idx || !topk_w || !offsets || !pull_src || !slot_of) return MOE_EINVAL;
-  const void* bufs[] = {xe, ye, w1, w3, w13t, w2t, dw1, dw3, dw2};
+  const void* bufs[] = {xe, ye, w1, w3, w2, dw1, dw3, dw2};
   for (const void* q : bufs)
     if (!aligned16(q)) return q ? MOE_EALIGN : MOE_EINVAL;
   if ((rc = check_ptr_table(dy, s->R)) || (rc = check_ptr_table(recv, s->R)) || (rc = check_ptr_table(dx, s->R)))
@@ -493,7 +453,7 @@ int moe_backward(const moe_shape_t* s, const moe_placement_t* p, const void* con
     if (!dlogits[r]) return MOE_EINVAL;
   if ((rc = moe_combine_pull_reverse(s, p, dy, ye, pull_src, slot_of, topk_w, ws, ws_bytes, bws, bws_bytes, stream)))
     return rc;
-  if ((rc = moe_expert_ffn_backward(s, p, xe, offsets, w1, w3, w13t, w2t, ws, ws_bytes, dw1, dw3, dw2, bws, bws_bytes,
+  if ((rc = moe_expert_ffn_backward(s, p, xe, offsets, w1, w3, w2, ws, ws_bytes, dw1, dw3, dw2, bws, bws_bytes,
                                     stream)))
     return rc;
   return moe_dispatch_push_reverse(s, p, pull_src, slot_of, topk_idx, topk_w, ws, ws_bytes, recv, dx, dlogits, bws,

@@ -111,12 +111,10 @@ class DeviceProblem:
 
     # ---- backward (bf16) ----
     def alloc_backward(self, dy_bits=None):
-        """Backward buffers: transposed weights, gradients, the backward workspace, and dy."""
+        """Backward buffers: gradients, the backward workspace, and dy."""
         torch, cfg, dev = self.torch, self.cfg, self.device
         R, T, d, E, El, F, k = cfg.R, cfg.T, cfg.d, cfg.E, cfg.E_local, cfg.F, cfg.k
         bf = torch.bfloat16
-        self.w13t = torch.empty((El, d, 2 * F), dtype=bf, device=dev)
-        self.w2t = torch.empty((El, F, d), dtype=bf, device=dev)
         self.dx = [torch.empty((T, d), dtype=bf, device=dev) for _ in range(R)]
         self.dlogits = [torch.empty((T, E), dtype=torch.float32, device=dev) for _ in range(R)]
         self.dw1 = torch.empty((El, F, d), dtype=bf, device=dev)
@@ -129,25 +127,21 @@ class DeviceProblem:
         if dy_bits is not None:
             self.dy = [_to_device_store(dy_bits[r], "bf16", dev) for r in range(R)]
 
-    def prepare_backward(self, stream=None):
-        moe.moe_backward_prepare(self.shape, self.placement, self.w1, self.w3, self.w2, self.w13t, self.w2t,
-                                 stream=stream)
-
     def combine_reverse(self, stream=None):
         moe.moe_combine_pull_reverse(self.shape, self.placement, self.dy, self.ye, self.pull_src, self.slot_of,
                                      self.topk_w, self.ws, self.bws, stream=stream)
 
     def ffn_backward(self, stream=None):
-        moe.moe_expert_ffn_backward(self.shape, self.placement, self.xe, self.offsets, self.w1, self.w3, self.w13t,
-                                    self.w2t, self.ws, self.dw1, self.dw3, self.dw2, self.bws, stream=stream)
+        moe.moe_expert_ffn_backward(self.shape, self.placement, self.xe, self.offsets, self.w1, self.w3, self.w2,
+                                    self.ws, self.dw1, self.dw3, self.dw2, self.bws, stream=stream)
 
     def dispatch_reverse(self, stream=None):
         moe.moe_dispatch_push_reverse(self.shape, self.placement, self.pull_src, self.slot_of, self.topk_idx,
                                       self.topk_w, self.ws, self.recv, self.dx, self.dlogits, self.bws, stream=stream)
 
     def backward(self, stream=None, check=True):
-        return moe.moe_backward(self.shape, self.placement, self.dy, self.xe, self.ye, self.w1, self.w3, self.w13t,
-                                self.w2t, self.topk_idx, self.topk_w, self.offsets, self.pull_src, self.slot_of,
+        return moe.moe_backward(self.shape, self.placement, self.dy, self.xe, self.ye, self.w1, self.w3, self.w2,
+                                self.topk_idx, self.topk_w, self.offsets, self.pull_src, self.slot_of,
                                 self.ws, self.recv, self.dx, self.dlogits, self.dw1, self.dw3, self.dw2, self.bws,
                                 stream=stream, check=check)
 

@@ -24,7 +24,7 @@ ERRORS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_ENOSPC", -4:
 EXPORTS = ["moe_max_pairs", "moe_workspace_bytes", "moe_mx_quantize", "moe_layout", "moe_dispatch_pull",
            "moe_expert_ffn", "moe_combine_push", "moe_forward", "moe_forward_persistent",
            "moe_ring_slot_bytes", "moe_persistent_workspace_bytes", "moe_backward_workspace_bytes",
-           "moe_backward_prepare", "moe_combine_pull_reverse", "moe_expert_ffn_backward",
+           "moe_combine_pull_reverse", "moe_expert_ffn_backward",
            "moe_dispatch_push_reverse", "moe_backward", "moe_read_status", "moe_strerror", "moe_version"]
 
 
@@ -86,19 +86,17 @@ def lib() -> ctypes.CDLL:
         L.moe_persistent_workspace_bytes.restype = SZ
         L.moe_backward_workspace_bytes.argtypes = [S, PL]
         L.moe_backward_workspace_bytes.restype = SZ
-        L.moe_backward_prepare.argtypes = [S, PL, VP, VP, VP, VP, VP, VP]
         L.moe_combine_pull_reverse.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, SZ, VP, SZ, VP]
-        L.moe_expert_ffn_backward.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, SZ, VP, VP, VP, VP, SZ, VP]
+        L.moe_expert_ffn_backward.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, SZ, VP, VP, VP, VP, SZ, VP]
         L.moe_dispatch_push_reverse.argtypes = [S, PL, VP, VP, VP, VP, VP, SZ, VP, VP, VP, VP, SZ, VP]
-        L.moe_backward.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ,
+        L.moe_backward.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ,
                                    VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_read_status.argtypes = [VP, VP]
         L.moe_strerror.argtypes = [I32]
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_version.restype = ctypes.c_char_p
         for f in ("moe_mx_quantize", "moe_layout", "moe_dispatch_pull", "moe_expert_ffn", "moe_combine_push",
-                  "moe_forward", "moe_forward_persistent", "moe_backward_prepare", "moe_combine_pull_reverse",
-                  "moe_expert_ffn_backward", "moe_dispatch_push_reverse", "moe_backward", "moe_read_status"):
+                  "moe_forward", "moe_forward_persistent", "moe_combine_pull_reverse", "moe_expert_ffn_backward", "moe_dispatch_push_reverse", "moe_backward", "moe_read_status"):
             getattr(L, f).restype = I32
         _lib = L
     return _lib
@@ -233,12 +231,6 @@ def moe_backward_workspace_bytes(shape: Shape, placement: Placement) -> int:
     return int(lib().moe_backward_workspace_bytes(ctypes.byref(shape), ctypes.byref(placement)))
 
 
-def moe_backward_prepare(shape, placement, w1, w3, w2, w13t, w2t, stream=None, check=True):
-    rc = lib().moe_backward_prepare(ctypes.byref(shape), ctypes.byref(placement), _p(w1), _p(w3), _p(w2),
-                                    _p(w13t), _p(w2t), _stream(stream))
-    return _check(rc, "moe_backward_prepare") if check else rc
-
-
 def moe_combine_pull_reverse(shape, placement, dy, ye, pull_src, slot_of, topk_w, ws, bws, ws_bytes=None,
                              bws_bytes=None, stream=None, check=True):
     rc = lib().moe_combine_pull_reverse(ctypes.byref(shape), ctypes.byref(placement), _table(dy), _p(ye),
@@ -248,10 +240,10 @@ def moe_combine_pull_reverse(shape, placement, dy, ye, pull_src, slot_of, topk_w
     return _check(rc, "moe_combine_pull_reverse") if check else rc
 
 
-def moe_expert_ffn_backward(shape, placement, xe, offsets, w1, w3, w13t, w2t, ws, dw1, dw3, dw2, bws,
+def moe_expert_ffn_backward(shape, placement, xe, offsets, w1, w3, w2, ws, dw1, dw3, dw2, bws,
                             ws_bytes=None, bws_bytes=None, stream=None, check=True):
     rc = lib().moe_expert_ffn_backward(ctypes.byref(shape), ctypes.byref(placement), _p(xe), _p(offsets), _p(w1),
-                                       _p(w3), _p(w13t), _p(w2t), _p(ws),
+                                       _p(w3), _p(w2), _p(ws),
                                        ws.numel() if ws_bytes is None else ws_bytes, _p(dw1), _p(dw3), _p(dw2),
                                        _p(bws), bws.numel() if bws_bytes is None else bws_bytes, _stream(stream))
     return _check(rc, "moe_expert_ffn_backward") if check else rc
@@ -267,10 +259,10 @@ def moe_dispatch_push_reverse(shape, placement, pull_src, slot_of, topk_idx, top
     return _check(rc, "moe_dispatch_push_reverse") if check else rc
 
 
-def moe_backward(shape, placement, dy, xe, ye, w1, w3, w13t, w2t, topk_idx, topk_w, offsets, pull_src, slot_of,
+def moe_backward(shape, placement, dy, xe, ye, w1, w3, w2, topk_idx, topk_w, offsets, pull_src, slot_of,
                  ws, recv, dx, dlogits, dw1, dw3, dw2, bws, ws_bytes=None, bws_bytes=None, stream=None, check=True):
     rc = lib().moe_backward(ctypes.byref(shape), ctypes.byref(placement), _table(dy), _p(xe), _p(ye), _p(w1),
-                            _p(w3), _p(w13t), _p(w2t), _p(topk_idx), _p(topk_w), _p(offsets), _p(pull_src),
+                            _p(w3), _p(w2), _p(topk_idx), _p(topk_w), _p(offsets), _p(pull_src),
                             _p(slot_of), _p(ws), ws.numel() if ws_bytes is None else ws_bytes, _table(recv),
                             _table(dx), _table(dlogits), _p(dw1), _p(dw3), _p(dw2), _p(bws),
                             bws.numel() if bws_bytes is None else bws_bytes, _stream(stream))

@@ -8,8 +8,7 @@ cancel to any size, while their error is bounded by |dY| |o_j - o_j'| (Cauchy-Sc
 so the bar is relative to that bound rather than to dl itself;
 tokens with no local pair get exactly zero dx and dlogits, logits that were not kept
 get exactly 0, an expert with no rows gets exactly zero weight gradients;
-moe_backward_prepare's transposes are bit-exact; two runs, and the three stage calls,
-are bit-identical.
+two runs, and the three stage calls, are bit-identical.
 """
 import sys
 
@@ -68,7 +67,6 @@ def _run(name, dims, dead_expert, seed=0):
     dp = DeviceProblem(cfg, inp)
     dp.alloc_backward(dy_bits)
     dp.forward()
-    dp.prepare_backward()
     dp.backward()
     dp.torch.cuda.synchronize()
     assert dp.status() == 0
@@ -119,23 +117,6 @@ def test_backward_matches_oracle(name, dims, dead):
     assert e_dl <= TOL
 
 
-def test_prepare_transposes_bit_exact():
-    from mixture_experts_layer_histogram_amd.device import DeviceProblem
-    name, dims, _ = CASES[2]
-    cfg = configs.MoEConfig(name, dtype="bf16", **dims)
-    inp = inputs.make_inputs(cfg, seed=1)
-    _say("[bwd] prepare transposes")
-    dp = DeviceProblem(cfg, inp, alloc_outputs=False)
-    dp.alloc_backward()
-    dp.prepare_backward()
-    torch = dp.torch
-    torch.cuda.synchronize()
-    F = cfg.F
-    assert torch.equal(dp.w13t[:, :, :F], dp.w1.transpose(1, 2))
-    assert torch.equal(dp.w13t[:, :, F:], dp.w3.transpose(1, 2))
-    assert torch.equal(dp.w2t, dp.w2.transpose(1, 2))
-
-
 def test_backward_deterministic():
     name, dims, dead = CASES[1]
     _, dp, _, _ = _run(name, dims, dead, seed=2)
@@ -182,7 +163,6 @@ def test_backward_full_dsv3_sampled():
     dp = DeviceProblem(cfg, inp)
     dp.alloc_backward(dy_bits)
     dp.forward()
-    dp.prepare_backward()
     dp.backward()
     dp.torch.cuda.synchronize()
     assert dp.status() == 0
