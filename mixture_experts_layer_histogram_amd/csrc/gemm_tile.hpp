@@ -123,6 +123,66 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
     if (ks + 1 < nk) issue(ks + 1);     // other stage: everyone finished reading it
     const char* sa = smem + (ks & 1) * kStageBytes;
     const char* sb = sa + kGemmBM * kGemmBK * 2;
+#ifndef MOE_GEMM_NO_ASM
+    {
+      // Each sub-step is one block: its 8 MFMAs with the next sub-step's 6 fragment reads
+      // between them, then one lgkmcnt(0).  The next fragments are early-clobber outputs,
+      // so they live in registers of their own (double buffering the compiler's schedule
+      // does not keep).  Per accumulator the MFMAs run in the same order as below.
+      auto lds_addr = [](const char* q) -> uint32_t {
+        return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)q));
+      };
+      i32x4 ca0, ca1, cb0, cb1, cb2, cb3;
+      ca0 = *reinterpret_cast<const i32x4*>(sa + swz_off(wm * 64 + r32, hi));
+      ca1 = *reinterpret_cast<const i32x4*>(sa + swz_off(wm * 64 + 32 + r32, hi));
+      cb0 = *reinterpret_cast<const i32x4*>(sb + swz_off(wn * 128 + r32, hi));
+      cb1 = *reinterpret_cast<const i32x4*>(sb + swz_off(wn * 128 + 32 + r32, hi));
+      cb2 = *reinterpret_cast<const i32x4*>(sb + swz_off(wn * 128 + 64 + r32, hi));
+      cb3 = *reinterpret_cast<const i32x4*>(sb + swz_off(wn * 128 + 96 + r32, hi));
+#pragma unroll
+      for (int sub = 0; sub < kGemmBK / 16; ++sub) {
+        if (sub + 1 < kGemmBK / 16) {
+          const uint32_t aa = lds_addr(sa + swz_off(wm * 64 + r32, (sub + 1) * 2 + hi));
+          const uint32_t ba = lds_addr(sb + swz_off(wn * 128 + r32, (sub + 1) * 2 + hi));
+          i32x4 na0, na1, nb0, nb1, nb2, nb3;
+          asm volatile(
+              "v_mfma_f32_32x32x16_bf16 %0, %14, %16, %0\n\t"
+              "ds_read_b128 %8, %20\n\t"
+              "v_mfma_f32_32x32x16_bf16 %1, %14, %17, %1\n\t"
+              "ds_read_b128 %9, %20 offset:4096\n\t"
+              "v_mfma_f32_32x32x16_bf16 %2, %14, %18, %2\n\t"
+              "ds_read_b128 %10, %21\n\t"
+              "v_mfma_f32_32x32x16_bf16 %3, %14, %19, %3\n\t"
+              "ds_read_b128 %11, %21 offset:4096\n\t"
+              "v_mfma_f32_32x32x16_bf16 %4, %15, %16, %4\n\t"
+              "ds_read_b128 %12, %21 offset:8192\n\t"
+              "v_mfma_f32_32x32x16_bf16 %5, %15, %17, %5\n\t"
+              "ds_read_b128 %13, %21 offset:12288\n\t"
+              "v_mfma_f32_32x32x16_bf16 %6, %15, %18, %6\n\t"
+              "v_mfma_f32_32x32x16_bf16 %7, %15, %19, %7\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]), "+v"(acc[1][0]),
+                "+v"(acc[1][1]), "+v"(acc[1][2]), "+v"(acc[1][3]), "=&v"(na0), "=&v"(na1), "=&v"(nb0),
+                "=&v"(nb1), "=&v"(nb2), "=&v"(nb3)
+              : "v"(ca0), "v"(ca1), "v"(cb0), "v"(cb1), "v"(cb2), "v"(cb3), "v"(aa), "v"(ba));
+          ca0 = na0; ca1 = na1; cb0 = nb0; cb1 = nb1; cb2 = nb2; cb3 = nb3;
+        } else {
+          asm volatile(
+              "v_mfma_f32_32x32x16_bf16 %0, %8, %10, %0\n\t"
+              "v_mfma_f32_32x32x16_bf16 %1, %8, %11, %1\n\t"
+              "v_mfma_f32_32x32x16_bf16 %2, %8, %12, %2\n\t"
+              "v_mfma_f32_32x32x16_bf16 %3, %8, %13, %3\n\t"
+              "v_mfma_f32_32x32x16_bf16 %4, %9, %10, %4\n\t"
+              "v_mfma_f32_32x32x16_bf16 %5, %9, %11, %5\n\t"
+              "v_mfma_f32_32x32x16_bf16 %6, %9, %12, %6\n\t"
+              "v_mfma_f32_32x32x16_bf16 %7, %9, %13, %7"
+              : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]), "+v"(acc[1][0]),
+                "+v"(acc[1][1]), "+v"(acc[1][2]), "+v"(acc[1][3])
+              : "v"(ca0), "v"(ca1), "v"(cb0), "v"(cb1), "v"(cb2), "v"(cb3));
+        }
+      }
+    }
+#else
     bf16x8 fa[2][2], fb[2][4];
 #pragma unroll
     for (int m = 0; m < 2; ++m) fa[0][m] = *reinterpret_cast<const bf16x8*>(sa + swz_off(wm * 64 + m * 32 + r32, hi));
@@ -145,9 +205,17 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
         for (int n = 0; n < 4; ++n)
           acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][m], fb[cur][n], acc[m][n], 0, 0, 0);
     }
+#endif
     __builtin_amdgcn_s_waitcnt(0);      // this wave's fills of the next stage landed
     __syncthreads();                    // ... and everyone's
   }
+
+  // The epilogue's lane indices are re-derived through an opaque copy, so the compiler
+  // cannot hoist its per-row store offsets above the main loop, where they would hold
+  // registers the loop needs for double-buffered fragments.
+  int lane_o = lane;
+  asm volatile("" : "+v"(lane_o));
+  const int r32o = lane_o & 31, hio = lane_o >> 5;
 
   if (MODE == 2) {
     // Backward epilogue, in two passes of 128 tile rows (m = 0, 1): every wave stages its
@@ -161,8 +229,8 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
       for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int lr = wm * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-          stg[lr * 128 + (wn * 2 + q) * 32 + r32] = make_float2(acc[m][2 * q][e], acc[m][2 * q + 1][e]);
+          const int lr = wm * 32 + 8 * (e >> 2) + 4 * hio + (e & 3);
+          stg[lr * 128 + (wn * 2 + q) * 32 + r32o] = make_float2(acc[m][2 * q][e], acc[m][2 * q + 1][e]);
         }
       __syncthreads();
 #pragma unroll
@@ -213,10 +281,10 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
     if (MODE == 0) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int f = c0 + (wn * 2 + q) * 32 + r32;
+        const int f = c0 + (wn * 2 + q) * 32 + r32o;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int row = 8 * (e >> 2) + 4 * hi + (e & 3);
+          const int row = 8 * (e >> 2) + 4 * hio + (e & 3);
           if (rb + row < rows && f < Nout) {
             const float h = silu_f32(acc[m][2 * q][e]) * acc[m][2 * q + 1][e];
             orow[size_t(row) * io.o_ld + f] = f32_to_bf16(h);
@@ -226,10 +294,10 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
     } else {
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const int col = c0 + wn * 128 + n * 32 + r32;
+        const int col = c0 + wn * 128 + n * 32 + r32o;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int row = 8 * (e >> 2) + 4 * hi + (e & 3);
+          const int row = 8 * (e >> 2) + 4 * hio + (e & 3);
           if (rb + row < rows && col < Nout) orow[size_t(row) * io.o_ld + col] = f32_to_bf16(acc[m][n][e]);
         }
       }
