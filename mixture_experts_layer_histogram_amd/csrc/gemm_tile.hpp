@@ -58,6 +58,42 @@ __device__ __forceinline__ P pick4(int i, P p0, P p1, P p2, P p3) {
   return i == 0 ? p0 : (i == 1 ? p1 : (i == 2 ? p2 : p3));
 }
 
+// MFMA operand fragments of one sub-step (16 K values): two A blocks, four B blocks
+struct Frags {
+  i32x4 a0, a1, b0, b1, b2, b3;
+};
+
+__device__ __forceinline__ uint32_t lds_addr(const char* q) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)q));
+}
+
+// ACC[m][n] += A_m B_n for one sub-step (fragments C), with the 6 fragments of the next
+// sub-step read into N from LDS (A blocks at AA, AA + 4096; B blocks at BA + n * 4096)
+// between the MFMAs (reads spread over the block keep the eight waves' LDS requests from
+// arriving in one burst), then one lgkmcnt(0).  A macro, so that ACC stays a register
+// array of the caller.
+#define MOE_MFMA_SUBSTEP_READ(ACC, C, N, AA, BA)                                                          \
+  asm volatile(                                                                                           \
+      "v_mfma_f32_32x32x16_bf16 %0, %14, %16, %0\n\t"                                                     \
+      "ds_read_b128 %8, %20\n\t"                                                                          \
+      "v_mfma_f32_32x32x16_bf16 %1, %14, %17, %1\n\t"                                                     \
+      "ds_read_b128 %9, %20 offset:4096\n\t"                                                              \
+      "v_mfma_f32_32x32x16_bf16 %2, %14, %18, %2\n\t"                                                     \
+      "ds_read_b128 %10, %21\n\t"                                                                         \
+      "v_mfma_f32_32x32x16_bf16 %3, %14, %19, %3\n\t"                                                     \
+      "ds_read_b128 %11, %21 offset:4096\n\t"                                                             \
+      "v_mfma_f32_32x32x16_bf16 %4, %15, %16, %4\n\t"                                                     \
+      "ds_read_b128 %12, %21 offset:8192\n\t"                                                             \
+      "v_mfma_f32_32x32x16_bf16 %5, %15, %17, %5\n\t"                                                     \
+      "ds_read_b128 %13, %21 offset:12288\n\t"                                                            \
+      "v_mfma_f32_32x32x16_bf16 %6, %15, %18, %6\n\t"                                                     \
+      "v_mfma_f32_32x32x16_bf16 %7, %15, %19, %7\n\t"                                                     \
+      "s_waitcnt lgkmcnt(0)"                                                                              \
+      : "+v"(ACC[0][0]), "+v"(ACC[0][1]), "+v"(ACC[0][2]), "+v"(ACC[0][3]), "+v"(ACC[1][0]),              \
+        "+v"(ACC[1][1]), "+v"(ACC[1][2]), "+v"(ACC[1][3]), "=&v"(N.a0), "=&v"(N.a1), "=&v"(N.b0),          \
+        "=&v"(N.b1), "=&v"(N.b2), "=&v"(N.b3)                                                             \
+      : "v"(C.a0), "v"(C.a1), "v"(C.b0), "v"(C.b1), "v"(C.b2), "v"(C.b3), "v"(AA), "v"(BA))
+
 // b0/b1: this expert's weight matrices ([Nout][K], row stride b_ld); c0: first output
 // column of the tile.
 template <int MODE>
@@ -115,99 +151,52 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
 
+  // Software pipeline over K.  Each sub-step is one block: its 8 MFMAs with the next
+  // sub-step's 6 fragment reads between them, then one lgkmcnt(0); the next fragments are
+  // early-clobber outputs, so they sit in registers of their own.  The barrier of a K step
+  // comes after sub-step 2, whose block already read sub-step 3's fragments: by then every
+  // wave is done with this stage, so the fill two steps ahead goes into it right away and
+  // sub-step 3's MFMAs cover the reads of the next stage's first fragments.  A fill is
+  // issued four sub-steps before the barrier that waits for it.  Per accumulator the MFMAs
+  // run in K order, so the result does not depend on this schedule.
+  auto a_at = [&](const char* st, int sub) -> uint32_t {
+    return lds_addr(st + swz_off(wm * 64 + r32, sub * 2 + hi));
+  };
+  auto b_at = [&](const char* st, int sub) -> uint32_t {
+    return lds_addr(st + kGemmBM * kGemmBK * 2 + swz_off(wn * 128 + r32, sub * 2 + hi));
+  };
+  Frags cur;
+
   issue(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (nk > 1) issue(1);
+  cur.a0 = *reinterpret_cast<const i32x4*>(smem + swz_off(wm * 64 + r32, hi));
+  cur.a1 = *reinterpret_cast<const i32x4*>(smem + swz_off(wm * 64 + 32 + r32, hi));
+  cur.b0 = *reinterpret_cast<const i32x4*>(smem + kGemmBM * kGemmBK * 2 + swz_off(wn * 128 + r32, hi));
+  cur.b1 = *reinterpret_cast<const i32x4*>(smem + kGemmBM * kGemmBK * 2 + swz_off(wn * 128 + 32 + r32, hi));
+  cur.b2 = *reinterpret_cast<const i32x4*>(smem + kGemmBM * kGemmBK * 2 + swz_off(wn * 128 + 64 + r32, hi));
+  cur.b3 = *reinterpret_cast<const i32x4*>(smem + kGemmBM * kGemmBK * 2 + swz_off(wn * 128 + 96 + r32, hi));
 
   for (int ks = 0; ks < nk; ++ks) {
-    if (ks + 1 < nk) issue(ks + 1);     // other stage: everyone finished reading it
-    const char* sa = smem + (ks & 1) * kStageBytes;
-    const char* sb = sa + kGemmBM * kGemmBK * 2;
-#ifndef MOE_GEMM_NO_ASM
-    {
-      // Each sub-step is one block: its 8 MFMAs with the next sub-step's 6 fragment reads
-      // between them, then one lgkmcnt(0).  The next fragments are early-clobber outputs,
-      // so they live in registers of their own (double buffering the compiler's schedule
-      // does not keep).  Per accumulator the MFMAs run in the same order as below.
-      auto lds_addr = [](const char* q) -> uint32_t {
-        return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)q));
-      };
-      i32x4 ca0, ca1, cb0, cb1, cb2, cb3;
-      ca0 = *reinterpret_cast<const i32x4*>(sa + swz_off(wm * 64 + r32, hi));
-      ca1 = *reinterpret_cast<const i32x4*>(sa + swz_off(wm * 64 + 32 + r32, hi));
-      cb0 = *reinterpret_cast<const i32x4*>(sb + swz_off(wn * 128 + r32, hi));
-      cb1 = *reinterpret_cast<const i32x4*>(sb + swz_off(wn * 128 + 32 + r32, hi));
-      cb2 = *reinterpret_cast<const i32x4*>(sb + swz_off(wn * 128 + 64 + r32, hi));
-      cb3 = *reinterpret_cast<const i32x4*>(sb + swz_off(wn * 128 + 96 + r32, hi));
+    const char* st = smem + (ks & 1) * kStageBytes;
 #pragma unroll
-      for (int sub = 0; sub < kGemmBK / 16; ++sub) {
-        if (sub + 1 < kGemmBK / 16) {
-          const uint32_t aa = lds_addr(sa + swz_off(wm * 64 + r32, (sub + 1) * 2 + hi));
-          const uint32_t ba = lds_addr(sb + swz_off(wn * 128 + r32, (sub + 1) * 2 + hi));
-          i32x4 na0, na1, nb0, nb1, nb2, nb3;
-          asm volatile(
-              "v_mfma_f32_32x32x16_bf16 %0, %14, %16, %0\n\t"
-              "ds_read_b128 %8, %20\n\t"
-              "v_mfma_f32_32x32x16_bf16 %1, %14, %17, %1\n\t"
-              "ds_read_b128 %9, %20 offset:4096\n\t"
-              "v_mfma_f32_32x32x16_bf16 %2, %14, %18, %2\n\t"
-              "ds_read_b128 %10, %21\n\t"
-              "v_mfma_f32_32x32x16_bf16 %3, %14, %19, %3\n\t"
-              "ds_read_b128 %11, %21 offset:4096\n\t"
-              "v_mfma_f32_32x32x16_bf16 %4, %15, %16, %4\n\t"
-              "ds_read_b128 %12, %21 offset:8192\n\t"
-              "v_mfma_f32_32x32x16_bf16 %5, %15, %17, %5\n\t"
-              "ds_read_b128 %13, %21 offset:12288\n\t"
-              "v_mfma_f32_32x32x16_bf16 %6, %15, %18, %6\n\t"
-              "v_mfma_f32_32x32x16_bf16 %7, %15, %19, %7\n\t"
-              "s_waitcnt lgkmcnt(0)"
-              : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]), "+v"(acc[1][0]),
-                "+v"(acc[1][1]), "+v"(acc[1][2]), "+v"(acc[1][3]), "=&v"(na0), "=&v"(na1), "=&v"(nb0),
-                "=&v"(nb1), "=&v"(nb2), "=&v"(nb3)
-              : "v"(ca0), "v"(ca1), "v"(cb0), "v"(cb1), "v"(cb2), "v"(cb3), "v"(aa), "v"(ba));
-          ca0 = na0; ca1 = na1; cb0 = nb0; cb1 = nb1; cb2 = nb2; cb3 = nb3;
-        } else {
-          asm volatile(
-              "v_mfma_f32_32x32x16_bf16 %0, %8, %10, %0\n\t"
-              "v_mfma_f32_32x32x16_bf16 %1, %8, %11, %1\n\t"
-              "v_mfma_f32_32x32x16_bf16 %2, %8, %12, %2\n\t"
-              "v_mfma_f32_32x32x16_bf16 %3, %8, %13, %3\n\t"
-              "v_mfma_f32_32x32x16_bf16 %4, %9, %10, %4\n\t"
-              "v_mfma_f32_32x32x16_bf16 %5, %9, %11, %5\n\t"
-              "v_mfma_f32_32x32x16_bf16 %6, %9, %12, %6\n\t"
-              "v_mfma_f32_32x32x16_bf16 %7, %9, %13, %7"
-              : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]), "+v"(acc[1][0]),
-                "+v"(acc[1][1]), "+v"(acc[1][2]), "+v"(acc[1][3])
-              : "v"(ca0), "v"(ca1), "v"(cb0), "v"(cb1), "v"(cb2), "v"(cb3));
-        }
-      }
+    for (int sub = 0; sub < kGemmBK / 16 - 1; ++sub) {
+      Frags nxt;
+      const uint32_t aa = a_at(st, sub + 1), ba = b_at(st, sub + 1);
+      MOE_MFMA_SUBSTEP_READ(acc, cur, nxt, aa, ba);
+      cur = nxt;
     }
-#else
-    bf16x8 fa[2][2], fb[2][4];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) fa[0][m] = *reinterpret_cast<const bf16x8*>(sa + swz_off(wm * 64 + m * 32 + r32, hi));
-#pragma unroll
-    for (int n = 0; n < 4; ++n) fb[0][n] = *reinterpret_cast<const bf16x8*>(sb + swz_off(wn * 128 + n * 32 + r32, hi));
-#pragma unroll
-    for (int sub = 0; sub < kGemmBK / 16; ++sub) {
-      const int cur = sub & 1;
-      if (sub + 1 < kGemmBK / 16) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-          fa[cur ^ 1][m] = *reinterpret_cast<const bf16x8*>(sa + swz_off(wm * 64 + m * 32 + r32, (sub + 1) * 2 + hi));
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-          fb[cur ^ 1][n] = *reinterpret_cast<const bf16x8*>(sb + swz_off(wn * 128 + n * 32 + r32, (sub + 1) * 2 + hi));
-      }
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][m], fb[cur][n], acc[m][n], 0, 0, 0);
-    }
-#endif
     __builtin_amdgcn_s_waitcnt(0);      // this wave's fills of the next stage landed
-    __syncthreads();                    // ... and everyone's
+    __syncthreads();                    // ... and everyone's; every wave is done with this stage
+    if (ks + 2 < nk) issue(ks + 2);     // into this stage
+    // the next stage's first fragments (after the last K step these reads land in the
+    // other stage, inside the LDS allocation, and are not used)
+    const char* sn = smem + ((ks + 1) & 1) * kStageBytes;
+    Frags nxt;
+    const uint32_t aa = a_at(sn, 0), ba = b_at(sn, 0);
+    MOE_MFMA_SUBSTEP_READ(acc, cur, nxt, aa, ba);
+    cur = nxt;
   }
 
   // The epilogue's lane indices are re-derived through an opaque copy, so the compiler
