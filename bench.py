@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (bf16) instead of the forward; prints its own JSON line")
+    ap.add_argument("--sweep-tokens", default="",
+                    help="comma-separated tokens per rank: time the forward at each (one JSON line per value; "
+                         "the minibatch-size curve of the unfused path)"),
     ap.add_argument("--cpu-sample-ranks", type=int, default=0, help="0 = all ranks (the whole step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run three plain 1 GiB device copies (counter calibration)")
@@ -264,6 +267,41 @@ def run_backward(args, cfg, inp, P, stream, N):
     print(json.dumps(result), flush=True)
 
 
+def run_sweep(args, cfg, P, stream):
+    """Forward time against tokens handed to the layer at once.  The problem's buffers are
+    sized for T tokens per rank; each point lowers the shape's T in place (every call reads
+    the first T rows of each rank's token and logit buffers) and times `args.steps` steps."""
+    import torch
+    T_full = P.shape.T
+    for t in [int(v) for v in args.sweep_tokens.split(",")]:
+        if not 1 <= t <= T_full:
+            raise SystemExit(f"--sweep-tokens: {t} outside 1..{T_full}")
+        P.shape.T = t
+        for _ in range(args.warmup):
+            P.forward()
+        torch.cuda.synchronize()
+        if P.status() != 0:
+            raise SystemExit(f"device status {P.status()} at T={t}")
+        n = P.N()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            P.forward()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        offs = P.offsets.cpu().numpy()
+        tiles1 = int(sum((int(offs[l + 1] - offs[l]) + 255) // 256 for l in range(cfg.E_local))) * ((cfg.F + 127) // 128)
+        line = {"metric": "MoE layer fwd ms per call vs tokens per call", "tokens_per_rank": t,
+                "source_tokens": cfg.R * t, "local_pairs": n, "ms_per_call": ms,
+                "us_per_source_token": ms * 1e3 / (cfg.R * t), "gemm1_tiles": tiles1,
+                "gemm1_waves": tiles1 / 256.0, "workload": cfg.name}
+        print(json.dumps(line), flush=True)
+        log(f"[sweep] T={t}: {ms:.3f} ms, N={n}, GEMM1 tiles {tiles1} ({tiles1 / 256:.2f} waves)")
+    P.shape.T = T_full
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -295,6 +333,9 @@ def main():
     log(f"[bench] warmup done, N={N} local pairs")
     if args.backward:
         run_backward(args, cfg, inp, P, stream, N)
+        return
+    if args.sweep_tokens:
+        run_sweep(args, cfg, P, stream)
         return
 
     names = ["layout", "dispatch", "ffn", "combine"]
