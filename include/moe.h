@@ -272,7 +272,7 @@ size_t moe_persistent_workspace_bytes(const moe_shape_t* s, const moe_placement_
  * forward above for the loss L = sum over (r, t) of <dy[r][t], y[r][t]>.
  */
 
-/* Bytes of the backward workspace `bws` (0 if the shape is invalid or not bf16). */
+/* Bytes of the backward workspace `bws` for a bf16 or MXFP8 shape (0 otherwise). */
 size_t moe_backward_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p);
 
 /*
@@ -338,6 +338,49 @@ int moe_backward(const moe_shape_t* s, const moe_placement_t* p, const void* con
                  const int32_t* slot_of, const void* ws, size_t ws_bytes, void* const* recv, void* const* dx,
                  float* const* dlogits, void* dw1, void* dw3, void* dw2, void* bws, size_t bws_bytes,
                  void* stream);
+
+/*
+ * MXFP8 backward [kucoin §02: MXFP8 in the expert data path; the pages give neither the
+ * backward's quantisation points nor its rule].  Its two data-gradient GEMMs run in MXFP8 with
+ * every operand quantised (the moe_mx_quantize rule) in blocks of 32 along that GEMM's K:
+ *   dh = dO W2:           dO along d, W2 along d;
+ *   dX = da W1 + db W3:   da and db along F, W1 and W3 along F;
+ * a = x W1^T and b = x W3^T are recomputed from the forward's MXFP8 operands.  The weight
+ * gradients contract over each expert's rows (32-row blocks would straddle experts) and
+ * run in bf16 on bf16 dO, da, db, h and the bf16 token rows.
+ */
+
+/*
+ * moe_backward_prepare_mx -- the weights in the backward's orientation, quantised from the
+ * bf16 weights w1, w3 ([E_local][F][d]) and w2 ([E_local][d][F]), once per weight update:
+ *   w2t:  [E_local][F][d] codes, row l*F + f = W2[l][:, f] quantised along d;
+ *         w2t_scales: [d/128][E_local*F][4] (MXFP8 scale layout);
+ *   w13t: [E_local][d][2F] codes, row l*d + n = [W1[l][:, n] | W3[l][:, n]] quantised along F;
+ *         w13t_scales: [2F/128][E_local*d][4].
+ * dtype must be MOE_MXFP8 (else MOE_EUNSUP).  Bit-exact (the moe_mx_quantize rule).
+ */
+int moe_backward_prepare_mx(const moe_shape_t* s, const moe_placement_t* p, const void* w1, const void* w3,
+                            const void* w2, uint8_t* w2t, uint8_t* w2t_scales, uint8_t* w13t, uint8_t* w13t_scales,
+                            void* stream);
+
+/*
+ * moe_backward_mx -- moe_backward for MOE_MXFP8, after moe_forward ran with the same
+ * arguments.  Inputs as moe_backward, plus: x (R pointers, the bf16 token rows, for the
+ * weight gradients), xe / xe_scales and w1q / w3q / w_scales as moe_forward read them, and
+ * moe_backward_prepare_mx's outputs.  Outputs as moe_backward (dx, dlogits, and dw1, dw3,
+ * dw2 in bf16).  bws: at least moe_backward_workspace_bytes() of this shape.
+ * Accuracy against the MXFP8 backward oracle (the same quantisation points in fp64):
+ * dx within 1e-1 of the largest row value per token and 2.5e-2 in Frobenius norm (rounding
+ * decisions on fp32 / bf16 intermediates flip against fp64); weight gradients per row
+ * within the bf16 row-relative 2e-2; dlogits as moe_backward.
+ */
+int moe_backward_mx(const moe_shape_t* s, const moe_placement_t* p, const void* const* dy, const void* const* x,
+                    const uint8_t* xe, const uint8_t* xe_scales, const void* ye, const uint8_t* w1q, const uint8_t* w3q,
+                    const moe_mx_scales_t* w_scales, const uint8_t* w2t, const uint8_t* w2t_scales, const uint8_t* w13t,
+                    const uint8_t* w13t_scales, const int32_t* topk_idx, const float* topk_w, const int32_t* offsets,
+                    const int32_t* pull_src, const int32_t* slot_of, const void* ws, size_t ws_bytes,
+                    void* const* recv, void* const* dx, float* const* dlogits, void* dw1, void* dw3, void* dw2,
+                    void* bws, size_t bws_bytes, void* stream);
 
 /* Syncs `stream` and returns the device status word (0, MOE_EINVAL or MOE_ETIMEOUT). */
 int moe_read_status(const void* ws, void* stream);

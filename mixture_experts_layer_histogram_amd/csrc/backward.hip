@@ -13,7 +13,7 @@
 //     the other logits get 0; a pair whose expert is not local has dg = 0 here.
 // The grouped GEMMs of the backward are in gemm_bwd.hip (and GEMM1's backward epilogue in
 // gemm_tile.hpp).  Everything here is HBM-bound: 16-byte vectors per lane.
-#include "common.hpp"
+#include "mx.hpp"
 
 namespace moe {
 
@@ -72,6 +72,76 @@ __global__ __launch_bounds__(256) void pull_reverse_kernel(RankPtrs<const char*>
   }
 }
 
+// The MXFP8 variant: dO[s] = g dY[r][t] as bf16 (for the weight gradients) and as MX codes
+// of the fp32 products in blocks of 32 along d (for dh = dO W2; scales in the MXFP8 scale
+// layout of nmax rows), and dg[s] = <dY[r][t], ye[s]>.  One wave per row, every lane in the
+// quad shuffles of the quantiser (lanes past the row end carry zeros).
+__global__ __launch_bounds__(256) void pull_reverse_mx_kernel(RankPtrs<const char*> dy, const uint16_t* __restrict__ ye,
+                                                              const int32_t* __restrict__ pull_src,
+                                                              const int32_t* __restrict__ slot_of,
+                                                              const float* __restrict__ topk_w,
+                                                              const int32_t* __restrict__ ctrl,
+                                                              uint16_t* __restrict__ dO, uint8_t* __restrict__ dOq,
+                                                              uint8_t* __restrict__ dOs, float* __restrict__ dg, int T,
+                                                              int k, int d, int64_t nmax) {
+  constexpr int UNROLL = 4;
+  const int N = ctrl[kCtrlN];
+  const int lane = threadIdx.x & 63;
+  const int n16 = d >> 3;                 // 16-byte vectors of 8 bf16 (d % 32 == 0: whole quads)
+  const int nw = gridDim.x * 4;
+  for (int s = blockIdx.x * 4 + (threadIdx.x >> 6); s < N; s += nw) {
+    const int r = pull_src[2 * int64_t(s)];
+    const int t = pull_src[2 * int64_t(s) + 1];
+    const int64_t pair0 = (int64_t(r) * T + t) * k;
+    const unsigned long long hit = __ballot(lane < k && slot_of[pair0 + (lane < k ? lane : 0)] == s);
+    const int j = hit ? __builtin_ctzll(hit) : 0;
+    const float g = topk_w[pair0 + j];
+    const u32x4* src = reinterpret_cast<const u32x4*>(dy.p[r] + int64_t(t) * d * 2);
+    const u32x4* yr = reinterpret_cast<const u32x4*>(ye + int64_t(s) * d);
+    u32x4* out = reinterpret_cast<u32x4*>(dO + int64_t(s) * d);
+    uint2* qout = reinterpret_cast<uint2*>(dOq + int64_t(s) * d);
+    float acc = 0.0f;
+    for (int base = 0; base < n16; base += 64 * UNROLL) {
+      u32x4 a[UNROLL], b[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int i = base + u * 64 + lane;
+        a[u] = u32x4{0, 0, 0, 0};
+        b[u] = u32x4{0, 0, 0, 0};
+        if (i < n16) {
+          a[u] = __builtin_nontemporal_load(src + i);
+          b[u] = __builtin_nontemporal_load(yr + i);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int i = base + u * 64 + lane;
+        f32x4 p0, p1;
+        u32x4 o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float lo = __uint_as_float(a[u][w] << 16), hi = __uint_as_float(a[u][w] & 0xFFFF0000u);
+          acc = fmaf(lo, __uint_as_float(b[u][w] << 16), acc);
+          acc = fmaf(hi, __uint_as_float(b[u][w] & 0xFFFF0000u), acc);
+          const float glo = g * lo, ghi = g * hi;
+          if (w < 2) { p0[2 * w] = glo; p0[2 * w + 1] = ghi; } else { p1[2 * w - 4] = glo; p1[2 * w - 3] = ghi; }
+          o[w] = pack_bf16x2(glo, ghi);
+        }
+        uint32_t sc;
+        const uint2 q = mx_quant8_f32(p0, p1, &sc);          // all lanes: quad shuffles inside
+        if (i < n16) {
+          out[i] = o;
+          qout[i] = q;
+          if ((i & 3) == 0) dOs[mx_scale_index(nmax, s, i >> 2)] = uint8_t(sc);
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) dg[s] = acc;
+  }
+}
+
 // dlogits[r][t][:] = 0 except dl_j at the k kept experts; one wave per token
 __global__ __launch_bounds__(256) void gate_grad_kernel(const float* __restrict__ topk_w,
                                                         const int32_t* __restrict__ topk_idx,
@@ -118,6 +188,17 @@ hipError_t launch_pull_reverse(const moe_shape_t& s, const void* const* dy, cons
   for (int r = 0; r < s.R; ++r) dp.p[r] = static_cast<const char*>(dy[r]);
   hipLaunchKernelGGL(pull_reverse_kernel, dim3(cus * kPullRevBlocksPerCU), dim3(256), 0, st, dp, ye, pull_src, slot_of,
                      topk_w, ctrl, dO, dg, s.T, s.k, s.d);
+  return hipGetLastError();
+}
+
+hipError_t launch_pull_reverse_mx(const moe_shape_t& s, const void* const* dy, const uint16_t* ye,
+                                  const int32_t* pull_src, const int32_t* slot_of, const float* topk_w,
+                                  const int32_t* ctrl, uint16_t* dO, uint8_t* dOq, uint8_t* dOs, float* dg, int64_t nmax,
+                                  int cus, hipStream_t st) {
+  RankPtrs<const char*> dp{};
+  for (int r = 0; r < s.R; ++r) dp.p[r] = static_cast<const char*>(dy[r]);
+  hipLaunchKernelGGL(pull_reverse_mx_kernel, dim3(cus * kPullRevBlocksPerCU), dim3(256), 0, st, dp, ye, pull_src,
+                     slot_of, topk_w, ctrl, dO, dOq, dOs, dg, s.T, s.k, s.d, nmax);
   return hipGetLastError();
 }
 

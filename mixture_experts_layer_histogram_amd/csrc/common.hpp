@@ -66,10 +66,14 @@ inline WsLayout ws_layout(const moe_shape_t& s, int32_t E_local) {
   return w;
 }
 
-// Backward workspace (bf16): the per-row gradients handed from one backward stage to the
-// next, and the per-pair gate gradients of the push.
+// Backward workspace: the per-row gradients handed from one backward stage to the next,
+// and the per-pair gate gradients of the push.  MXFP8 adds the MX codes and block scales
+// of dO (along d) and of [da | db] (along F) for the data-gradient GEMMs, and bf16 copies
+// of the dispatched token rows for the weight gradients.
 struct BwdLayout {
-  size_t dO, dg, dh, h, dab, dX, dgp, total;
+  size_t dO, dg, dh, h, dab, dX, dgp;
+  size_t dOq, dOs, dabq, dabs, xeb;   // MXFP8 only (0 otherwise)
+  size_t total;
 };
 
 inline BwdLayout bwd_layout(const moe_shape_t& s, int32_t E_local) {
@@ -84,6 +88,13 @@ inline BwdLayout bwd_layout(const moe_shape_t& s, int32_t E_local) {
   b.dab = o;  o = align256(o + n * F * 4);
   b.dX = o;   o = align256(o + n * d * 2);
   b.dgp = o;  o = align256(o + size_t(s.R) * s.T * s.k * 4);
+  if (s.dtype == MOE_MXFP8) {
+    b.dOq = o;  o = align256(o + n * d);
+    b.dOs = o;  o = align256(o + n * (d / 32));
+    b.dabq = o; o = align256(o + n * 2 * F);
+    b.dabs = o; o = align256(o + n * (2 * F / 32));
+    b.xeb = o;  o = align256(o + n * d * 2);
+  }
   b.total = o;
   return b;
 }

@@ -35,6 +35,13 @@ struct TileMX {
   uint8_t* os;          // MODE 0: the h scale word of the tile's first row in plane 0
   int64_t os_plane;     // MODE 0: bytes between planes of the h scales
   int rows;             // valid rows, 1..256; rows beyond re-read row rows-1 and are not stored
+  // MODE 2 (backward GEMM1): dh in, h and [da | db] out as bf16, [da | db] as MX codes
+  const uint16_t* dh;   // [rows][Nout] from the tile's first row
+  uint16_t* hb;         // [rows][Nout]
+  uint16_t* dab;        // [rows][2 Nout]
+  uint8_t* dabq;        // [rows][2 Nout] codes
+  uint8_t* dabs;        // scales of the whole [nmax][2 Nout] code matrix (MXFP8 scale layout)
+  int64_t row0, nmax;   // global index of the tile's first row; rows of the scale layout
 };
 
 __device__ __forceinline__ i32x8 ld_frag(const char* s, int row, int c0) {
@@ -68,7 +75,7 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
     const int row = (wave * 4 + i) * 8 + lrow;
     const int lch = (i & 1) ? lch_odd : lch_even;
     ap[i] = io.a + size_t(min(row, rows - 1)) * K + lch * 16;
-    if (MODE == 0) {
+    if (MODE != 1) {
       const int n = min(c0 + (row >> 6) * 32 + (row & 31), Nout - 1);
       bp[i] = (((row >> 5) & 1) ? b1 : b0) + size_t(n) * K + lch * 16;
     } else {
@@ -83,7 +90,7 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
     if (wave < 4) {
       sp = io.as + 4 * size_t(min(row, rows - 1));
       splane = io.as_plane;
-    } else if (MODE == 0) {
+    } else if (MODE != 1) {
       const int n = min(c0 + (row >> 6) * 32 + (row & 31), Nout - 1);
       sp = (((row >> 5) & 1) ? bs1 : bs0) + 4 * size_t(n);
       splane = bs_plane;
@@ -145,6 +152,87 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
     }
     __builtin_amdgcn_s_waitcnt(0);      // this wave's fills of the next stage landed
     __syncthreads();                    // ... and everyone's
+  }
+
+  if (MODE == 2) {
+    // Backward epilogue, two passes of 128 tile rows: stage (a, b) as fp32 pairs in LDS
+    // ([128][128] float2 = 128 KiB), then each thread takes one 32-value f block of one
+    // row: h = silu(a) b, da = dh b silu'(a), db = dh silu(a) as bf16, and da, db quantised
+    // along F (MX blocks of 32; the block maximum is taken over a first pass, the codes
+    // over a second that recomputes the values).
+    float2* stg = reinterpret_cast<float2*>(smem);
+    const int F2 = 2 * Nout;
+#pragma unroll   // acc[m] must stay in registers
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int lr = wm * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+          stg[lr * 128 + (wn * 2 + q) * 32 + r32] = make_float2(acc[m][2 * q][e], acc[m][2 * q + 1][e]);
+        }
+      __syncthreads();
+      const int lr = tid >> 2, q32 = tid & 3;                    // 128 rows x 4 blocks = 512 threads
+      const int trow = (lr >> 5) * 64 + m * 32 + (lr & 31);
+      const int f0 = c0 + q32 * 32;
+      if (trow < rows && f0 < Nout) {
+        const float2* sp = stg + lr * 128 + q32 * 32;
+        u32x4 dv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dv[c] = reinterpret_cast<const u32x4*>(io.dh + size_t(trow) * Nout + f0)[c];
+        auto grad = [&](int i, float* hh, float* ga, float* gb) {
+          const float2 ab = sp[i];
+          const uint32_t w = dv[i >> 3][(i & 7) >> 1];
+          const float dhv = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+          const float sg = 1.0f / (1.0f + __expf(-ab.x));
+          const float sa = ab.x * sg;
+          *hh = sa * ab.y;
+          *ga = dhv * ab.y * (sg * (1.0f + ab.x * (1.0f - sg)));
+          *gb = dhv * sa;
+        };
+        uint32_t mda = 0, mdb = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          u32x4 hv, dav, dbv;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            float hh[2], ga[2], gb[2];
+            grad(c * 8 + 2 * w, &hh[0], &ga[0], &gb[0]);
+            grad(c * 8 + 2 * w + 1, &hh[1], &ga[1], &gb[1]);
+            mda = max(mda, max(__float_as_uint(ga[0]) & 0x7FFFFFFFu, __float_as_uint(ga[1]) & 0x7FFFFFFFu));
+            mdb = max(mdb, max(__float_as_uint(gb[0]) & 0x7FFFFFFFu, __float_as_uint(gb[1]) & 0x7FFFFFFFu));
+            hv[w] = pack_bf16x2(hh[0], hh[1]);
+            dav[w] = pack_bf16x2(ga[0], ga[1]);
+            dbv[w] = pack_bf16x2(gb[0], gb[1]);
+          }
+          reinterpret_cast<u32x4*>(io.hb + size_t(trow) * Nout + f0)[c] = hv;
+          reinterpret_cast<u32x4*>(io.dab + size_t(trow) * F2 + f0)[c] = dav;
+          reinterpret_cast<u32x4*>(io.dab + size_t(trow) * F2 + Nout + f0)[c] = dbv;
+        }
+        const int ea = mda ? mx_block_exp(mda) : 0, eb = mdb ? mx_block_exp(mdb) : 0;
+        const float ia = mx_inv_scale(ea), ib = mx_inv_scale(eb);
+        uint32_t qa[8], qb[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float hh[4], ga[4], gb[4];
+#pragma unroll
+          for (int z = 0; z < 4; ++z) grad(c * 4 + z, &hh[z], &ga[z], &gb[z]);
+          qa[c] = mda ? mx_pack4(ga[0], ga[1], ga[2], ga[3], ia) : 0u;
+          qb[c] = mdb ? mx_pack4(gb[0], gb[1], gb[2], gb[3], ib) : 0u;
+        }
+        u32x4* qd = reinterpret_cast<u32x4*>(io.dabq + size_t(trow) * F2 + f0);
+        qd[0] = u32x4{qa[0], qa[1], qa[2], qa[3]};
+        qd[1] = u32x4{qa[4], qa[5], qa[6], qa[7]};
+        u32x4* qe = reinterpret_cast<u32x4*>(io.dabq + size_t(trow) * F2 + Nout + f0);
+        qe[0] = u32x4{qb[0], qb[1], qb[2], qb[3]};
+        qe[1] = u32x4{qb[4], qb[5], qb[6], qb[7]};
+        const int64_t grow = io.row0 + trow;
+        io.dabs[mx_scale_index(io.nmax, grow, f0 >> 5)] = uint8_t(mda ? ea + 127 : 0);
+        io.dabs[mx_scale_index(io.nmax, grow, (Nout + f0) >> 5)] = uint8_t(mdb ? eb + 127 : 0);
+      }
+      __syncthreads();
+    }
+    return;
   }
 
   // Epilogue through LDS (the stages are free after the last barrier).  Each wave writes
@@ -227,7 +315,10 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
 }
 
 // MODE 0: A = xe codes [*][d], B0/B1 = W1/W3 -> h codes [*][F] + scales   (256 rows x 128 f)
-// MODE 1: A = h codes [*][F],  B0 = W2       -> ye bf16 [*][d]            (256 rows x 256 cols)
+// MODE 1: A = codes [*][K],    B0 = codes [Nout][K] per expert -> bf16 [*][Nout]   (256 x 256)
+//         (GEMM2 y = h W2^T; in the backward dh = dO W2 and dX = [da | db] [W1; W3], with
+//         the weights quantised along the backward's K)
+// MODE 2: as MODE 0 with the backward epilogue: DH in; HB, DAB (bf16) and DABQ/DABS out
 // Tile enumeration as in the bf16 grouped GEMM: a persistent grid walks 8 contiguous
 // per-XCD ranges of the expert-major tile list.
 template <int MODE>
@@ -236,9 +327,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_mx_kernel(
     const uint8_t* __restrict__ B1, const uint8_t* __restrict__ Bs0, const uint8_t* __restrict__ Bs1,
     void* __restrict__ C, uint8_t* __restrict__ Cs, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ mtile_base, const int32_t* __restrict__ ctrl, int El, int K, int Nout,
-    int64_t nmax) {
+    int64_t nmax, const uint16_t* __restrict__ DH, uint16_t* __restrict__ DAB, uint8_t* __restrict__ DABQ,
+    uint8_t* __restrict__ DABS) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int cols_per_tile = (MODE == 0) ? kGemmBN / 2 : kGemmBN;
+  const int cols_per_tile = (MODE != 1) ? kGemmBN / 2 : kGemmBN;
   const int NT = (Nout + cols_per_tile - 1) / cols_per_tile;
   const int total = ctrl[kCtrlMTiles] * NT;
   const int per_xcd = (total + 7) >> 3;
@@ -270,10 +362,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_mx_kernel(
       io.os_plane = 0;
     }
     io.rows = min(kGemmBM, offsets[l + 1] - row0);
+    io.dh = (MODE == 2) ? DH + size_t(row0) * Nout : nullptr;
+    io.hb = (MODE == 2) ? static_cast<uint16_t*>(C) + size_t(row0) * Nout : nullptr;
+    io.dab = (MODE == 2) ? DAB + size_t(row0) * 2 * Nout : nullptr;
+    io.dabq = (MODE == 2) ? DABQ + size_t(row0) * 2 * Nout : nullptr;
+    io.dabs = DABS;
+    io.row0 = row0;
+    io.nmax = nmax;
     const uint8_t* b0 = B0 + size_t(l) * Nout * K;
-    const uint8_t* b1 = (MODE == 0) ? B1 + size_t(l) * Nout * K : b0;
+    const uint8_t* b1 = (MODE != 1) ? B1 + size_t(l) * Nout * K : b0;
     const uint8_t* bs0 = Bs0 + 4 * size_t(l) * Nout;
-    const uint8_t* bs1 = (MODE == 0) ? Bs1 + 4 * size_t(l) * Nout : bs0;
+    const uint8_t* bs1 = (MODE != 1) ? Bs1 + 4 * size_t(l) * Nout : bs0;
     gemm_mx_tile<MODE>(io, b0, b1, bs0, bs1, bs_plane, nt * cols_per_tile, Nout, K, smem);
   }
 }
@@ -303,9 +402,49 @@ hipError_t launch_ffn_mx(const moe_shape_t& s, int El, const uint8_t* xe, const 
   uint8_t* hs = reinterpret_cast<uint8_t*>(ws + mx_h_scales_offset(L, s));
   const int grid = (cus / 8) * 8;
   hipLaunchKernelGGL(grouped_gemm_mx_kernel<0>, dim3(grid), dim3(kGemmThreads), kMxLds, st, xe, xe_scales, w1, w3,
-                     w1s, w3s, static_cast<void*>(hq), hs, offsets, mtb, ctrl, El, s.d, s.F, int64_t(L.max_pairs));
+                     w1s, w3s, static_cast<void*>(hq), hs, offsets, mtb, ctrl, El, s.d, s.F, int64_t(L.max_pairs),
+                     nullptr, nullptr, nullptr, nullptr);
   hipLaunchKernelGGL(grouped_gemm_mx_kernel<1>, dim3(grid), dim3(kGemmThreads), kMxLds, st, hq, hs, w2, nullptr,
-                     w2s, nullptr, ye, nullptr, offsets, mtb, ctrl, El, s.F, s.d, int64_t(L.max_pairs));
+                     w2s, nullptr, ye, nullptr, offsets, mtb, ctrl, El, s.F, s.d, int64_t(L.max_pairs), nullptr, nullptr,
+                     nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t set_mx_bwd_lds_attrs() {
+  static bool done = false;
+  if (done) return hipSuccess;
+  const void* ks[] = {reinterpret_cast<const void*>(grouped_gemm_mx_kernel<1>),
+                      reinterpret_cast<const void*>(grouped_gemm_mx_kernel<2>)};
+  for (const void* k : ks) {
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
+    if (e != hipSuccess) return e;
+  }
+  done = true;
+  return hipSuccess;
+}
+
+// C[s] = A[s] B_l^T in MXFP8 for the rows of every local expert: A codes [*][K] with scales
+// of nmax rows, B codes [E_local][Nout][K] with scales of E_local * Nout rows; bf16 out.
+hipError_t launch_rows_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, uint16_t* C, int K,
+                          int Nout, int64_t nmax, const int32_t* offsets, const int32_t* mtb, const int32_t* ctrl,
+                          int El, int cus, hipStream_t st) {
+  hipError_t e = set_mx_bwd_lds_attrs();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(grouped_gemm_mx_kernel<1>, dim3((cus / 8) * 8), dim3(kGemmThreads), kMxLds, st, A, As, B, nullptr,
+                     Bs, nullptr, static_cast<void*>(C), nullptr, offsets, mtb, ctrl, El, K, Nout, nmax, nullptr,
+                     nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+// GEMM1 again in MXFP8 with the backward epilogue: h, [da | db] (bf16) and [da | db] codes
+hipError_t launch_gemm1_bwd_mx(const uint8_t* xe, const uint8_t* xes, const uint8_t* w1, const uint8_t* w3,
+                               const uint8_t* w1s, const uint8_t* w3s, const uint16_t* dh, uint16_t* h, uint16_t* dab,
+                               uint8_t* dabq, uint8_t* dabs, int d, int F, int64_t nmax, const int32_t* offsets,
+                               const int32_t* mtb, const int32_t* ctrl, int El, int cus, hipStream_t st) {
+  hipError_t e = set_mx_bwd_lds_attrs();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(grouped_gemm_mx_kernel<2>, dim3((cus / 8) * 8), dim3(kGemmThreads), kMxLds, st, xe, xes, w1, w3,
+                     w1s, w3s, static_cast<void*>(h), nullptr, offsets, mtb, ctrl, El, d, F, nmax, dh, dab, dabq, dabs);
   return hipGetLastError();
 }
 

@@ -47,6 +47,19 @@ hipError_t launch_gate_grad(const moe_shape_t& s, const float* topk_w, const int
 hipError_t launch_push_grad(const moe_shape_t& s, const char* dX, const float* dg, const int32_t* pull_src,
                             const int32_t* slot_of, void* const* recv, float* dgp, const int32_t* ctrl, int cus,
                             hipStream_t st);
+hipError_t launch_mx_quantize_t(const uint16_t* src, int P, int C, int batches, uint8_t* codes, int64_t ldk, int k0,
+                                uint8_t* scales, int64_t rows_total, int cus, hipStream_t st);
+hipError_t launch_pull_reverse_mx(const moe_shape_t& s, const void* const* dy, const uint16_t* ye,
+                                  const int32_t* pull_src, const int32_t* slot_of, const float* topk_w,
+                                  const int32_t* ctrl, uint16_t* dO, uint8_t* dOq, uint8_t* dOs, float* dg, int64_t nmax,
+                                  int cus, hipStream_t st);
+hipError_t launch_rows_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, uint16_t* C, int K,
+                          int Nout, int64_t nmax, const int32_t* offsets, const int32_t* mtb, const int32_t* ctrl,
+                          int El, int cus, hipStream_t st);
+hipError_t launch_gemm1_bwd_mx(const uint8_t* xe, const uint8_t* xes, const uint8_t* w1, const uint8_t* w3,
+                               const uint8_t* w1s, const uint8_t* w3s, const uint16_t* dh, uint16_t* h, uint16_t* dab,
+                               uint8_t* dabq, uint8_t* dabs, int d, int F, int64_t nmax, const int32_t* offsets,
+                               const int32_t* mtb, const int32_t* ctrl, int El, int cus, hipStream_t st);
 }  // namespace moe
 
 using namespace moe;
@@ -133,12 +146,12 @@ long long wall_ticks_per_us() {
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
-// backward calls: bf16 shape, the forward's workspace, and the backward workspace
+// backward calls: a shape of the given dtype, the forward's workspace, and the backward workspace
 int check_bwd(const moe_shape_t* s, const moe_placement_t* p, const void* ws, size_t ws_bytes, const void* bws,
-              size_t bws_bytes) {
+              size_t bws_bytes, int dtype = MOE_BF16) {
   int rc = check_shape(s, p);
   if (rc) return rc;
-  if (s->dtype != MOE_BF16) return MOE_EUNSUP;
+  if (s->dtype != dtype) return MOE_EUNSUP;
   if ((rc = check_ws(s, p, ws, ws_bytes))) return rc;
   if (!bws) return MOE_EINVAL;
   if (reinterpret_cast<uintptr_t>(bws) & 255) return MOE_EALIGN;
@@ -350,8 +363,100 @@ int moe_forward_persistent(const moe_shape_t* s, const moe_placement_t* p, const
 }
 
 size_t moe_backward_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p) {
-  if (check_shape(s, p) != MOE_OK || s->dtype != MOE_BF16) return 0;
+  if (check_shape(s, p) != MOE_OK || (s->dtype != MOE_BF16 && s->dtype != MOE_MXFP8)) return 0;
   return bwd_layout(*s, p->E_local).total;
+}
+
+int moe_backward_prepare_mx(const moe_shape_t* s, const moe_placement_t* p, const void* w1, const void* w3,
+                            const void* w2, uint8_t* w2t, uint8_t* w2t_scales, uint8_t* w13t, uint8_t* w13t_scales,
+                            void* stream) {
+  int rc = check_shape(s, p);
+  if (rc) return rc;
+  if (s->dtype != MOE_MXFP8) return MOE_EUNSUP;
+  const void* bufs[] = {w1, w3, w2, w2t, w13t};
+  for (const void* q : bufs)
+    if (!aligned16(q)) return q ? MOE_EALIGN : MOE_EINVAL;
+  if ((rc = check_scales(w2t_scales)) || (rc = check_scales(w13t_scales))) return rc;
+  const int El = p->E_local, d = s->d, F = s->F, cus = cu_count();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // W2 along d -> [E_local][F][d] codes; W1 and W3 along F -> [E_local][d][2F] codes
+  hipError_t e = launch_mx_quantize_t(static_cast<const uint16_t*>(w2), d, F, El, w2t, d, 0, w2t_scales,
+                                      int64_t(El) * F, cus, st);
+  if (e == hipSuccess)
+    e = launch_mx_quantize_t(static_cast<const uint16_t*>(w1), F, d, El, w13t, 2 * F, 0, w13t_scales, int64_t(El) * d,
+                             cus, st);
+  if (e == hipSuccess)
+    e = launch_mx_quantize_t(static_cast<const uint16_t*>(w3), F, d, El, w13t, 2 * F, F, w13t_scales, int64_t(El) * d,
+                             cus, st);
+  return hip_rc(e);
+}
+
+int moe_backward_mx(const moe_shape_t* s, const moe_placement_t* p, const void* const* dy, const void* const* x,
+                    const uint8_t* xe, const uint8_t* xe_scales, const void* ye, const uint8_t* w1q, const uint8_t* w3q,
+                    const moe_mx_scales_t* w_scales, const uint8_t* w2t, const uint8_t* w2t_scales, const uint8_t* w13t,
+                    const uint8_t* w13t_scales, const int32_t* topk_idx, const float* topk_w, const int32_t* offsets,
+                    const int32_t* pull_src, const int32_t* slot_of, const void* ws, size_t ws_bytes,
+                    void* const* recv, void* const* dx, float* const* dlogits, void* dw1, void* dw3, void* dw2,
+                    void* bws, size_t bws_bytes, void* stream) {
+  int rc = check_bwd(s, p, ws, ws_bytes, bws, bws_bytes, MOE_MXFP8);
+  if (rc) return rc;
+  if (!topk_idx || !topk_w || !offsets || !pull_src || !slot_of) return MOE_EINVAL;
+  const void* bufs[] = {xe, ye, w1q, w3q, w2t, w13t, dw1, dw3, dw2};
+  for (const void* q : bufs)
+    if (!aligned16(q)) return q ? MOE_EALIGN : MOE_EINVAL;
+  if ((rc = check_scales(xe_scales)) || (rc = check_w_scales(w_scales)) || (rc = check_scales(w2t_scales)) ||
+      (rc = check_scales(w13t_scales)))
+    return rc;
+  if ((rc = check_ptr_table(dy, s->R)) || (rc = check_ptr_table(x, s->R)) || (rc = check_ptr_table(recv, s->R)) ||
+      (rc = check_ptr_table(dx, s->R)))
+    return rc;
+  if (!dlogits) return MOE_EINVAL;
+  for (int r = 0; r < s->R; ++r)
+    if (!dlogits[r]) return MOE_EINVAL;
+
+  const WsLayout L = ws_layout(*s, p->E_local);
+  const BwdLayout B = bwd_layout(*s, p->E_local);
+  const char* w = static_cast<const char*>(ws);
+  const int32_t* ctrl = reinterpret_cast<const int32_t*>(w + L.ctrl);
+  const int32_t* mtb = reinterpret_cast<const int32_t*>(w + L.mtile_base);
+  char* b = static_cast<char*>(bws);
+  uint16_t* dO = reinterpret_cast<uint16_t*>(b + B.dO);
+  float* dg = reinterpret_cast<float*>(b + B.dg);
+  uint16_t* dh = reinterpret_cast<uint16_t*>(b + B.dh);
+  uint16_t* h = reinterpret_cast<uint16_t*>(b + B.h);
+  uint16_t* dab = reinterpret_cast<uint16_t*>(b + B.dab);
+  uint16_t* dX = reinterpret_cast<uint16_t*>(b + B.dX);
+  float* dgp = reinterpret_cast<float*>(b + B.dgp);
+  uint8_t* dOq = reinterpret_cast<uint8_t*>(b + B.dOq);
+  uint8_t* dOs = reinterpret_cast<uint8_t*>(b + B.dOs);
+  uint8_t* dabq = reinterpret_cast<uint8_t*>(b + B.dabq);
+  uint8_t* dabs = reinterpret_cast<uint8_t*>(b + B.dabs);
+  uint16_t* xeb = reinterpret_cast<uint16_t*>(b + B.xeb);
+  const int El = p->E_local, d = s->d, F = s->F, cus = cu_count();
+  const int64_t nmax = L.max_pairs;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // pull reverse-combine (dO bf16 and MX codes along d, dg)
+  hipError_t e = launch_pull_reverse_mx(*s, dy, static_cast<const uint16_t*>(ye), pull_src, slot_of, topk_w, ctrl, dO,
+                                        dOq, dOs, dg, nmax, cus, st);
+  // MX data-gradient GEMMs: dh = dO W2; GEMM1 again with the backward epilogue; dX = [da|db] [W1; W3]
+  if (e == hipSuccess) e = launch_rows_mx(dOq, dOs, w2t, w2t_scales, dh, d, F, nmax, offsets, mtb, ctrl, El, cus, st);
+  if (e == hipSuccess)
+    e = launch_gemm1_bwd_mx(xe, xe_scales, w1q, w3q, w_scales->w1, w_scales->w3, dh, h, dab, dabq, dabs, d, F, nmax,
+                            offsets, mtb, ctrl, El, cus, st);
+  if (e == hipSuccess)
+    e = launch_rows_mx(dabq, dabs, w13t, w13t_scales, dX, 2 * F, d, nmax, offsets, mtb, ctrl, El, cus, st);
+  // bf16 weight gradients over each expert's rows (the token rows gathered again in bf16)
+  if (e == hipSuccess) e = launch_dispatch(*s, x, pull_src, reinterpret_cast<char*>(xeb), ctrl, cus, st);
+  if (e == hipSuccess) e = launch_wgrad(dab, 2 * F, xeb, d, offsets, static_cast<uint16_t*>(dw1), El, F, d, cus, st);
+  if (e == hipSuccess)
+    e = launch_wgrad(dab + F, 2 * F, xeb, d, offsets, static_cast<uint16_t*>(dw3), El, F, d, cus, st);
+  if (e == hipSuccess) e = launch_wgrad(dO, d, h, F, offsets, static_cast<uint16_t*>(dw2), El, d, F, cus, st);
+  // push reverse-dispatch, ordered sum, gate gradients
+  if (e == hipSuccess)
+    e = launch_push_grad(*s, reinterpret_cast<const char*>(dX), dg, pull_src, slot_of, recv, dgp, ctrl, cus, st);
+  if (e == hipSuccess) e = launch_merge(*s, slot_of, nullptr, recv, dx, cus, st);
+  if (e == hipSuccess) e = launch_gate_grad(*s, topk_w, topk_idx, slot_of, dgp, dlogits, cus, st);
+  return hip_rc(e);
 }
 
 int moe_combine_pull_reverse(const moe_shape_t* s, const moe_placement_t* p, const void* const* dy, const void* ye,

@@ -124,6 +124,12 @@ class DeviceProblem:
         if self.bws_bytes == 0:
             raise ValueError("shape rejected by moe_backward_workspace_bytes")
         self.bws = torch.empty(self.bws_bytes, dtype=torch.uint8, device=dev)
+        if cfg.dtype == "mxfp8":
+            u8 = torch.uint8
+            self.w2t = torch.empty((El, F, d), dtype=u8, device=dev)
+            self.w2t_scales = torch.empty((d // 128, El * F, 4), dtype=u8, device=dev)
+            self.w13t = torch.empty((El, d, 2 * F), dtype=u8, device=dev)
+            self.w13t_scales = torch.empty((2 * F // 128, El * d, 4), dtype=u8, device=dev)
         if dy_bits is not None:
             self.dy = [_to_device_store(dy_bits[r], "bf16", dev) for r in range(R)]
 
@@ -138,6 +144,19 @@ class DeviceProblem:
     def dispatch_reverse(self, stream=None):
         moe.moe_dispatch_push_reverse(self.shape, self.placement, self.pull_src, self.slot_of, self.topk_idx,
                                       self.topk_w, self.ws, self.recv, self.dx, self.dlogits, self.bws, stream=stream)
+
+    def prepare_backward_mx(self, stream=None):
+        """The weights in the backward's orientation, MX-quantised (once per weight update)."""
+        moe.moe_backward_prepare_mx(self.shape, self.placement, self.w1, self.w3, self.w2, self.w2t, self.w2t_scales,
+                                    self.w13t, self.w13t_scales, stream=stream)
+
+    def backward_mx(self, stream=None, check=True):
+        w1q, w3q, _ = self.weights()
+        return moe.moe_backward_mx(self.shape, self.placement, self.dy, self.x, self.xe, self.xe_scales, self.ye, w1q,
+                                   w3q, self.w_scales, self.w2t, self.w2t_scales, self.w13t, self.w13t_scales,
+                                   self.topk_idx, self.topk_w, self.offsets, self.pull_src, self.slot_of, self.ws,
+                                   self.recv, self.dx, self.dlogits, self.dw1, self.dw3, self.dw2, self.bws,
+                                   stream=stream, check=check)
 
     def backward(self, stream=None, check=True):
         return moe.moe_backward(self.shape, self.placement, self.dy, self.xe, self.ye, self.w1, self.w3, self.w2,

@@ -25,7 +25,8 @@ EXPORTS = ["moe_max_pairs", "moe_workspace_bytes", "moe_mx_quantize", "moe_layou
            "moe_expert_ffn", "moe_combine_push", "moe_forward", "moe_forward_persistent",
            "moe_ring_slot_bytes", "moe_persistent_workspace_bytes", "moe_backward_workspace_bytes",
            "moe_combine_pull_reverse", "moe_expert_ffn_backward",
-           "moe_dispatch_push_reverse", "moe_backward", "moe_read_status", "moe_strerror", "moe_version"]
+           "moe_dispatch_push_reverse", "moe_backward", "moe_backward_prepare_mx", "moe_backward_mx",
+           "moe_read_status", "moe_strerror", "moe_version"]
 
 
 class MoEError(RuntimeError):
@@ -91,12 +92,16 @@ def lib() -> ctypes.CDLL:
         L.moe_dispatch_push_reverse.argtypes = [S, PL, VP, VP, VP, VP, VP, SZ, VP, VP, VP, VP, SZ, VP]
         L.moe_backward.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ,
                                    VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_backward_prepare_mx.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, VP]
+        L.moe_backward_mx.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, MS, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP,
+                                      SZ, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_read_status.argtypes = [VP, VP]
         L.moe_strerror.argtypes = [I32]
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_version.restype = ctypes.c_char_p
         for f in ("moe_mx_quantize", "moe_layout", "moe_dispatch_pull", "moe_expert_ffn", "moe_combine_push",
-                  "moe_forward", "moe_forward_persistent", "moe_combine_pull_reverse", "moe_expert_ffn_backward", "moe_dispatch_push_reverse", "moe_backward", "moe_read_status"):
+                  "moe_forward", "moe_forward_persistent", "moe_combine_pull_reverse", "moe_expert_ffn_backward", "moe_dispatch_push_reverse", "moe_backward", "moe_backward_prepare_mx",
+                  "moe_backward_mx", "moe_read_status"):
             getattr(L, f).restype = I32
         _lib = L
     return _lib
@@ -267,6 +272,25 @@ def moe_backward(shape, placement, dy, xe, ye, w1, w3, w2, topk_idx, topk_w, off
                             _table(dx), _table(dlogits), _p(dw1), _p(dw3), _p(dw2), _p(bws),
                             bws.numel() if bws_bytes is None else bws_bytes, _stream(stream))
     return _check(rc, "moe_backward") if check else rc
+
+
+def moe_backward_prepare_mx(shape, placement, w1, w3, w2, w2t, w2t_scales, w13t, w13t_scales, stream=None,
+                            check=True):
+    rc = lib().moe_backward_prepare_mx(ctypes.byref(shape), ctypes.byref(placement), _p(w1), _p(w3), _p(w2), _p(w2t),
+                                       _p(w2t_scales), _p(w13t), _p(w13t_scales), _stream(stream))
+    return _check(rc, "moe_backward_prepare_mx") if check else rc
+
+
+def moe_backward_mx(shape, placement, dy, x, xe, xe_scales, ye, w1q, w3q, w_scales, w2t, w2t_scales, w13t,
+                    w13t_scales, topk_idx, topk_w, offsets, pull_src, slot_of, ws, recv, dx, dlogits, dw1, dw3, dw2,
+                    bws, ws_bytes=None, bws_bytes=None, stream=None, check=True):
+    rc = lib().moe_backward_mx(ctypes.byref(shape), ctypes.byref(placement), _table(dy), _table(x), _p(xe),
+                               _p(xe_scales), _p(ye), _p(w1q), _p(w3q), _ref(w_scales), _p(w2t), _p(w2t_scales),
+                               _p(w13t), _p(w13t_scales), _p(topk_idx), _p(topk_w), _p(offsets), _p(pull_src),
+                               _p(slot_of), _p(ws), ws.numel() if ws_bytes is None else ws_bytes, _table(recv),
+                               _table(dx), _table(dlogits), _p(dw1), _p(dw3), _p(dw2), _p(bws),
+                               bws.numel() if bws_bytes is None else bws_bytes, _stream(stream))
+    return _check(rc, "moe_backward_mx") if check else rc
 
 
 def moe_read_status(ws, stream=None) -> int:

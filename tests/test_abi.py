@@ -220,7 +220,8 @@ def test_backward_entry_points_reject_bad_arguments_before_launch():
     assert bws > 0 and bws % 256 == 0
     # the per-row gradients (dO, dX [d]; dh, h [F]; [da|db] [2F]) dominate
     assert bws >= 8 * 4096 * 8 * (7168 * 2 + 2048 * 4) * 2
-    assert moe.moe_backward_workspace_bytes(_shape(dtype=moe.MOE_MXFP8), p) == 0     # bf16 only
+    # MXFP8 adds its codes, scales and the bf16 token rows; fp32 has no backward
+    assert moe.moe_backward_workspace_bytes(_shape(dtype=moe.MOE_MXFP8), p) > bws
     assert moe.moe_backward_workspace_bytes(_shape(dtype=moe.MOE_F32), p) == 0
 
     def bwd(shape=s, xe=FAKE, dy=tabp, dlog=tabp, ws_bytes=big, bws_ptr=FAKE, bws_bytes=big, dw2=FAKE):
@@ -272,3 +273,34 @@ def test_backward_stage_entries_reject_bad_arguments_before_launch():
     assert push(recv=None) == -1
     assert push(dlog=None) == -1
     assert push(bptr=FAKE + 128) == -2
+
+
+def test_mx_backward_entries_reject_bad_arguments_before_launch():
+    L = moe.lib()
+    s, p = _shape(dtype=moe.MOE_MXFP8), _pl()
+    tab = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    tabp = ctypes.cast(tab, ctypes.c_void_p)
+    big = 1 << 40
+    bws = moe.moe_backward_workspace_bytes(s, p)
+    ok = moe.MXScales(FAKE, FAKE, FAKE)
+
+    def prep(shape=s, w=FAKE, sc=FAKE):
+        return L.moe_backward_prepare_mx(ctypes.byref(shape), ctypes.byref(p), w, FAKE, FAKE, FAKE, sc, FAKE, FAKE,
+                                         None)
+    assert prep(shape=_shape()) == -6                                    # MXFP8 only
+    assert prep(w=None) == -1
+    assert prep(w=FAKE + 8) == -2
+    assert prep(sc=FAKE + 1) == -2
+    assert prep(shape=_shape(dtype=moe.MOE_MXFP8, d=7168 + 64)) == -2   # d % 128
+
+    def bwd(shape=s, x=tabp, xs=FAKE, wsc=ok, bb=big, dw1=FAKE):
+        return L.moe_backward_mx(ctypes.byref(shape), ctypes.byref(p), tabp, x, FAKE, xs, FAKE, FAKE, FAKE,
+                                 ctypes.byref(wsc) if wsc is not None else None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, FAKE, FAKE, FAKE, big, tabp, tabp, tabp, dw1, FAKE, FAKE, FAKE, bb, None)
+    assert bwd(shape=_shape()) == -6                                     # bf16 uses moe_backward
+    assert bwd(x=None) == -1
+    assert bwd(xs=None) == -1
+    assert bwd(wsc=None) == -1
+    assert bwd(wsc=moe.MXScales(FAKE, FAKE + 2, FAKE)) == -2
+    assert bwd(dw1=FAKE + 4) == -2
+    assert bwd(bb=bws - 256) == -3
