@@ -6,10 +6,11 @@ push combine and the final weighted merge.  Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config dsv3]
 
-With --backward (bf16 configs) a step is instead the whole backward of the share after
-one forward: moe_backward's three stages (pull reverse-combine, expert SwiGLU backward with
-the weight-gradient GEMMs, push reverse-dispatch with the ordered sum and the gate
-gradient).
+With --backward a step is instead the whole backward of the share after one forward:
+bf16 configs time moe_backward's three stages (pull reverse-combine, expert SwiGLU
+backward with the weight-gradient GEMMs, push reverse-dispatch with the ordered sum and
+the gate gradient); MXFP8 configs time moe_backward_prepare_mx (the weights re-quantised
+along the backward's K, once per weight update) and moe_backward_mx.
 """
 from __future__ import annotations
 
@@ -196,10 +197,96 @@ def cpu_baseline_bwd(cfg, inp, dy, ranks):
                       f"gradients); {dt:.2f} s wall"}
 
 
+def _oracle_mx_bwd_weights(cfg, inp):
+    """The MXFP8 backward oracle's quantised weights (both orientations), per expert in
+    threads: untimed setup, like the weights' offline quantisation on the GPU."""
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import mx_oracle_bwd as QB
+    def one(l):
+        return QB.weights_q([inp.w1_f32[l]], [inp.w3_f32[l]], [inp.w2_f32[l]], 1)
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        parts = list(ex.map(one, range(cfg.E_local)))
+    return {key: [p[key][0] for p in parts] for key in parts[0]}
+
+
+def cpu_baseline_bwd_mx(cfg, inp, dy, ranks):
+    """The MXFP8 backward oracle as it stands on the first `ranks` source ranks (weights
+    quantised beforehand, untimed)."""
+    from oracle import mx_oracle_bwd as QB
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    ranks = max(1, min(ranks, cfg.R))
+    W = _oracle_mx_bwd_weights(cfg, inp)
+    t0 = time.perf_counter()
+    QB.backward_q(inp.logits[:ranks], inp.x_f32[:ranks], inp.w1_f32, inp.w3_f32, inp.w2_f32, inp.expert_to_local,
+                  cfg.E_local, cfg.k, dy[:ranks], cfg.minibatch, W=W)
+    dt = time.perf_counter() - t0
+    tokens = ranks * cfg.T / cfg.G
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"source ranks 0..{ranks - 1} of {cfg.R} of the same inputs; fp64 NumPy MXFP8 backward oracle "
+                      f"(its quantised forward, pull reverse-combine, MX data-gradient GEMMs, weight gradients, push, "
+                      f"gate gradients; weights quantised beforehand, untimed); {dt:.2f} s wall"}
+
+
+def run_backward_mx(args, cfg, inp, P, stream, N):
+    import torch
+    dy_bits, dy = inputs.make_dy(cfg, seed=args.seed)
+    P.alloc_backward(dy_bits)
+    for _ in range(args.warmup):
+        P.prepare_backward_mx()
+        P.backward_mx()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        P.prepare_backward_mx()
+        ev[i][1].record(stream)
+        P.backward_mx()
+        ev[i][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    stage_ms = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+                for j, n in enumerate(["prepare", "backward"])}
+    log(f"[bench] MXFP8 backward {args.steps} steps: {ms_step:.3f} ms/step; stages {stage_ms}")
+    dfn = float(cfg.d) * cfg.F * N
+    fl_mx, fl_bf = 10.0 * dfn, 6.0 * dfn          # dh, GEMM1 again, dX in MXFP8; three weight gradients in bf16
+    peak = (fl_mx + fl_bf) / (fl_mx / PEAK_FP8_FLOPS + fl_bf / PEAK_BF16_FLOPS)
+    t_b = stage_ms["backward"] * 1e-3
+    tokens = cfg.R * cfg.T / cfg.G
+    result = {
+        "metric": METRIC_BWD, "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) tokens and incoming gradients, fan-in scaled random expert weights, "
+                "router logits x@W_r)",
+        "config": {"workload": cfg.name, "R": cfg.R, "T": cfg.T, "d": cfg.d, "E": cfg.E, "E_local": cfg.E_local,
+                   "k": cfg.k, "F": cfg.F, "local_pairs": N,
+                   "path": "MXFP8 backward after one forward: weight re-quantisation + moe_backward_mx"},
+        "roofline": {"bound": "mfma", "kernel": "moe_backward_mx (10dFN MXFP8 data-gradient FLOP + 6dFN bf16 "
+                                                 "weight-gradient FLOP; peak = that mix at 5.0 and 2.5 PFLOP/s)",
+                     "achieved": (fl_mx + fl_bf) / t_b / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
+                     "frac": (fl_mx + fl_bf) / t_b / peak, "traffic": None},
+        "stages_ms": stage_ms,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU MXFP8 backward oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline_bwd_mx(cfg, inp, dy, args.cpu_sample_ranks or 1)
+    print(json.dumps(result), flush=True)
+
+
 def run_backward(args, cfg, inp, P, stream, N):
     import torch
+    if cfg.dtype == "mxfp8":
+        return run_backward_mx(args, cfg, inp, P, stream, N)
     if cfg.dtype != "bf16":
-        raise SystemExit("--backward: the backward is built for bf16 configs only")
+        raise SystemExit("--backward: the backward is built for bf16 and MXFP8 configs")
     dy_bits, dy = inputs.make_dy(cfg, seed=args.seed)
     P.alloc_backward(dy_bits)
     for _ in range(args.warmup):

@@ -110,58 +110,58 @@ namespace moe {
 // stride ldk), quantised in blocks of 32 along p; the block scale goes to the MXFP8 scale
 // layout of a matrix of `rows_total` rows.  Used for the weights of the backward's
 // data-gradient GEMMs, whose K runs along the other axis (W2 along d, W1 and W3 along F).
-// 64 x 64 tiles through LDS; a thread quantises one 32-value column block.  P, C % 64 == 0.
+// 64 (p) x 128 (c) tiles through LDS, filled with 16-byte loads; each of the 256 threads
+// then quantises one 32-value column block.  P % 64 == 0, C % 128 == 0.
 __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const uint16_t* __restrict__ src, int P, int C, int batches,
                                                             uint8_t* __restrict__ codes, int64_t ldk, int k0,
                                                             uint8_t* __restrict__ scales, int64_t rows_total) {
-  __shared__ uint16_t tile[64][66];
-  const int npb = P >> 6, ncb = C >> 6;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][136];   // 272-byte rows: 16-byte aligned
+  const int npb = P >> 6, ncb = C >> 7;
   const int64_t tasks = int64_t(batches) * npb * ncb;
   for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
     const int bt = int(task / (int64_t(npb) * ncb));
     const int rem = int(task - int64_t(bt) * npb * ncb);
     const int pb = rem / ncb, cb = rem - pb * ncb;
-    const uint16_t* s0 = src + (int64_t(bt) * P + pb * 64) * C + cb * 64;
-    for (int v = threadIdx.x; v < 64 * 64 / 2; v += 256) {       // 32-bit loads: 2 values each
-      const int r = v >> 5, c2 = (v & 31) * 2;
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(s0 + int64_t(r) * C + c2);
-      tile[r][c2] = uint16_t(w & 0xFFFFu);
-      tile[r][c2 + 1] = uint16_t(w >> 16);
+    const uint16_t* s0 = src + (int64_t(bt) * P + pb * 64) * C + cb * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = threadIdx.x + 256 * i;           // 64 rows x 16 vectors of 8 values
+      const int r = v >> 4, cv = v & 15;
+      *reinterpret_cast<u32x4*>(&tile[r][cv * 8]) =
+          __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(s0 + int64_t(r) * C) + cv);
     }
     __syncthreads();
-    if (threadIdx.x < 128) {
-      const int c = threadIdx.x & 63, half = threadIdx.x >> 6;    // column c, p block half
-      float v[32];
-      uint32_t mx = 0;
+    const int c = threadIdx.x & 127, half = threadIdx.x >> 7;   // column c, p block half
+    float v[32];
+    uint32_t mx = 0;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const uint32_t b = tile[half * 32 + i][c];
-        v[i] = bf16_to_f32(uint16_t(b));
-        mx = max(mx, (b << 16) & 0x7FFFFFFFu);
-      }
-      uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      uint32_t sc = 0;
-      if (mx != 0) {
-        const int e = mx_block_exp(mx);
-        const float inv = mx_inv_scale(e);
-        sc = uint32_t(e + 127);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) w[q] = mx_pack4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], inv);
-      }
-      const int64_t row = int64_t(bt) * C + cb * 64 + c;
-      const int k = k0 + pb * 64 + half * 32;
-      u32x4* dst = reinterpret_cast<u32x4*>(codes + row * ldk + k);
-      dst[0] = u32x4{w[0], w[1], w[2], w[3]};
-      dst[1] = u32x4{w[4], w[5], w[6], w[7]};
-      scales[mx_scale_index(rows_total, row, k >> 5)] = uint8_t(sc);
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t b = tile[half * 32 + i][c];
+      v[i] = bf16_to_f32(uint16_t(b));
+      mx = max(mx, (b << 16) & 0x7FFFFFFFu);
     }
+    uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t sc = 0;
+    if (mx != 0) {
+      const int e = mx_block_exp(mx);
+      const float inv = mx_inv_scale(e);
+      sc = uint32_t(e + 127);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) w[q] = mx_pack4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], inv);
+    }
+    const int64_t row = int64_t(bt) * C + cb * 128 + c;
+    const int k = k0 + pb * 64 + half * 32;
+    u32x4* dst = reinterpret_cast<u32x4*>(codes + row * ldk + k);
+    dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+    dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+    scales[mx_scale_index(rows_total, row, k >> 5)] = uint8_t(sc);
     __syncthreads();
   }
 }
 
 hipError_t launch_mx_quantize_t(const uint16_t* src, int P, int C, int batches, uint8_t* codes, int64_t ldk, int k0,
                                 uint8_t* scales, int64_t rows_total, int cus, hipStream_t st) {
-  hipLaunchKernelGGL(mx_quantize_t_kernel, dim3(cus * 4), dim3(256), 0, st, src, P, C, batches, codes, ldk, k0, scales,
+  hipLaunchKernelGGL(mx_quantize_t_kernel, dim3(cus * 8), dim3(256), 0, st, src, P, C, batches, codes, ldk, k0, scales,
                      rows_total);
   return hipGetLastError();
 }

@@ -60,12 +60,14 @@ def weights_q(w1, w3, w2, E_local, q=mx_rows):
     return out
 
 
-def backward_q(logits, x, w1, w3, w2, expert_to_local, E_local, k, dy, minibatch=128, q=mx_rows) -> dict:
+def backward_q(logits, x, w1, w3, w2, expert_to_local, E_local, k, dy, minibatch=128, q=mx_rows, W=None) -> dict:
     """Gradients of L = sum <dy, y> through the MXFP8 share (see the module notes).
 
     w1, w3 [E_local][F][d] and w2 [E_local][d][F] are the unquantised (bf16) weights; q is
-    the row quantiser (MX by default; the identity reduces this to the bf16 backward)."""
-    W = weights_q(w1, w3, w2, E_local, q)
+    the row quantiser (MX by default; the identity reduces this to the bf16 backward).  W,
+    if given, is weights_q(w1, w3, w2, E_local, q) computed beforehand."""
+    if W is None:
+        W = weights_q(w1, w3, w2, E_local, q)
     # forward: routing, layout, MX x, SwiGLU with MX h, merge
     idx, gates = O.route(logits, k)
     lay = O.layout(idx, expert_to_local, E_local, minibatch)

@@ -134,3 +134,89 @@ def test_prepare_mx_bit_exact():
         torch.cuda.synchronize()
         assert torch.equal(q, codes)
         assert torch.equal(sc, scales)
+
+
+@pytest.mark.slow
+def test_mx_backward_full_dsv3_sampled():
+    """Full DeepSeek-V3-shaped MXFP8 share, in the launch configuration `bench.py --backward
+    --config dsv3_mx` times.  dx and dlogits of sampled tokens from the oracle on each token
+    alone (with the local experts it chose); the whole dw1, dw3, dw2 of the most loaded
+    expert from the oracle on exactly the tokens that chose it with that expert alone local.
+    Sampled tokens are drawn among those whose local experts fall in a set of at most 4,
+    whose weights the oracle quantises once."""
+    from oracle import moe_oracle as O
+    from mixture_experts_layer_histogram_amd.device import DeviceProblem
+    cfg = configs.DSV3_MX
+    _say(f"[mx-bwd-full] {cfg.name}: inputs")
+    inp = inputs.make_inputs(cfg, seed=0)
+    dy_bits, dy = inputs.make_dy(cfg, seed=0)
+    _say("[mx-bwd-full] forward + backward on cuda:0")
+    dp = DeviceProblem(cfg, inp)
+    dp.alloc_backward(dy_bits)
+    dp.forward()
+    dp.prepare_backward_mx()
+    dp.backward_mx()
+    dp.torch.cuda.synchronize()
+    assert dp.status() == 0
+    idx, _ = O.route(inp.logits, cfg.k)
+    e2l = inp.expert_to_local
+    lay = O.layout(idx, e2l, cfg.E_local)
+    counts = np.diff(lay["offsets"])
+    hot = int(np.argmax(counts))
+    has = (lay["slot_of"] >= 0).any(-1)
+    tok = np.argwhere(has)
+    rng = np.random.default_rng(0)
+    allowed, picked = {hot}, []
+    for i in rng.permutation(len(tok)):
+        r, t = tok[i]
+        ls = {int(e2l[e]) for e in idx[r, t] if e2l[e] >= 0}
+        if len(allowed | ls) <= 4:
+            allowed |= ls
+            picked.append((r, t))
+        if len(picked) == 6:
+            break
+    _say(f"[mx-bwd-full] quantising the weights of experts {sorted(allowed)} for the oracle")
+    Wl = {l: QB.weights_q([inp.w1_f32[l]], [inp.w3_f32[l]], [inp.w2_f32[l]], 1) for l in allowed}
+
+    def W_of(ls):
+        return {key: [Wl[l][key][0] for l in ls] for key in Wl[ls[0]]}
+
+    def w_of(ls):
+        return ([inp.w1_f32[l] for l in ls], [inp.w3_f32[l] for l in ls], [inp.w2_f32[l] for l in ls])
+    gx, rx = [], []
+    worst_dl = 0.0
+    for r, t in picked:
+        ls = [int(e2l[e]) for e in idx[r, t] if e2l[e] >= 0]
+        e2l_t = np.full(cfg.E, -1, dtype=np.int32)
+        for i, l in enumerate(ls):
+            e2l_t[int(np.flatnonzero(e2l == l)[0])] = i
+        ref = QB.backward_q(inp.logits[r:r + 1, t:t + 1], inp.x_f32[r:r + 1, t:t + 1], *w_of(ls), e2l_t, len(ls),
+                            cfg.k, dy[r:r + 1, t:t + 1], minibatch=cfg.minibatch, W=W_of(ls))
+        gx.append(_f64(dp.dx[r][t]))
+        rx.append(ref["dx"][0, 0])
+        dlg = dp.dlogits[r][t].cpu().numpy().astype(np.float64)
+        kept = np.zeros(cfg.E, dtype=bool)
+        kept[idx[r, t]] = True
+        assert np.all(dlg[~kept] == 0.0)
+        on = np.linalg.norm(ref["ye"], axis=-1)
+        so = ref["slot_of"][0, 0]
+        scale = max(float(ref["gates"][0, 0, j] * on[so[j]]) for j in range(cfg.k) if so[j] >= 0) * \
+            float(np.linalg.norm(dy[r, t].astype(np.float64)))
+        worst_dl = max(worst_dl, float(np.abs(dlg - ref["dlogits"][0, 0]).max() / scale))
+    gx, rx = np.stack(gx), np.stack(rx)
+    row = _row_rel(gx, rx)
+    fro = float(np.linalg.norm(gx - rx) / np.linalg.norm(rx))
+    _say(f"[mx-bwd-full] {len(picked)} sampled tokens: dx row-max {row:.3e}, Frobenius {fro:.3e}, "
+         f"dlogits scaled {worst_dl:.3e}")
+    assert len(picked) >= 3 and row <= DX_ROW and fro <= DX_FRO and worst_dl <= DL_TOL
+    e = int(np.flatnonzero(e2l == hot)[0])
+    rr, tt = np.nonzero((idx == e).any(-1))
+    e2l1 = np.full(cfg.E, -1, dtype=np.int32)
+    e2l1[e] = 0
+    _say(f"[mx-bwd-full] expert {e} ({len(rr)} rows): oracle")
+    ref = QB.backward_q(inp.logits[rr, tt][None], inp.x_f32[rr, tt][None], *w_of([hot]), e2l1, 1, cfg.k,
+                        dy[rr, tt][None], minibatch=cfg.minibatch, W=W_of([hot]))
+    assert ref["N"] == counts[hot]
+    errs = {key: _row_rel(_f64(getattr(dp, key)[hot]), ref[key][0]) for key in ("dw1", "dw3", "dw2")}
+    _say(f"[mx-bwd-full] expert {e}: " + ", ".join(f"{k_} row-rel {v:.3e}" for k_, v in errs.items()))
+    assert max(errs.values()) <= W_TOL
