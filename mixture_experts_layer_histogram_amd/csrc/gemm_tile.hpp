@@ -199,6 +199,15 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
     cur = nxt;
   }
 
+  // The MFMAs above are inline assembly, which the compiler's hazard recognizer does not
+  // see: a read of an accumulator right after the MFMA that writes it would see the old
+  // value (MFMA results are not interlocked for dependent reads).  24 wait states cover the
+  // longest MFMA->read distance; taking every accumulator as an operand keeps all reads
+  // of them after this point.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]), "+v"(acc[1][0]),
+                 "+v"(acc[1][1]), "+v"(acc[1][2]), "+v"(acc[1][3]));
+
   // The epilogue's lane indices are re-derived through an opaque copy, so the compiler
   // cannot hoist its per-row store offsets above the main loop, where they would hold
   // registers the loop needs for double-buffered fragments.
