@@ -62,6 +62,9 @@ def parse():
                     help="comma-separated tokens per rank: time the forward at each (one JSON line per value; "
                          "the minibatch-size curve of the unfused path)"),
     ap.add_argument("--cpu-sample-ranks", type=int, default=0, help="0 = all ranks (the whole step)")
+    ap.add_argument("--sample-clocks", action="store_true",
+                    help="sample the GPU's gfx clocks and socket power with amd-smi during the timed steps "
+                         "(use enough --steps for a few seconds) and report their means")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run three plain 1 GiB device copies (counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -96,6 +99,53 @@ def traffic_bytes(config):
 
 
 CAL_BYTES = 1 << 30
+
+
+class ClockSampler:
+    """Polls `amd-smi metric -c -p` (a child process per sample) while the timed steps run:
+    the sustained gfx clock under load sets the MFMA peak actually reachable (the published
+    peaks assume 2.4 GHz)."""
+
+    def __init__(self, period=0.25):
+        import threading
+        self.period, self.clk, self.pw, self.n = period, [], [], 0
+        self.stop_ev = threading.Event()
+        self.th = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import re
+        import subprocess
+        while not self.stop_ev.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"], capture_output=True,
+                                   text=True, timeout=20)
+                txt = r.stdout
+            except (OSError, subprocess.SubprocessError):
+                return
+            c = [int(v) for v in re.findall(r'"gfx_\d+": \{\s*"clk": \{\s*"value": (\d+)', txt)]
+            w = re.search(r'"socket_power": \{\s*"value": (\d+)', txt)
+            if c and not self.stop_ev.is_set() and min(c) >= 500:      # idle readings before the load starts
+                self.clk.append(float(np.mean(c)))
+                self.n += 1
+                if w:
+                    self.pw.append(float(w.group(1)))
+            self.stop_ev.wait(self.period)
+
+    def __enter__(self):
+        self.th.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop_ev.set()
+        self.th.join(timeout=30)
+
+    def summary(self, peak):
+        if not self.clk:
+            return None
+        mhz = float(np.mean(self.clk))
+        return {"gfx_mhz_mean": mhz, "gfx_mhz_min": float(np.min(self.clk)), "gfx_mhz_max": float(np.max(self.clk)),
+                "socket_w_mean": float(np.mean(self.pw)) if self.pw else None, "samples": self.n,
+                "peak_at_mean_clock": peak * mhz / 2400.0 / 1e12, "peak_unit": "TFLOP/s"}
 
 
 def _per_dispatch(csv_path, counter):
@@ -430,6 +480,9 @@ def main():
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    sampler = ClockSampler() if args.sample_clocks else None
+    if sampler:
+        sampler.__enter__()
     t_start.record(stream)
     for i in range(args.steps):
         e = ev[i]
@@ -444,6 +497,8 @@ def main():
         e[4].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
+    if sampler:
+        sampler.__exit__()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
     stage_ms = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
@@ -498,6 +553,8 @@ def main():
         "pairs_per_s": N / (ms_step * 1e-3),
         "source_tokens_per_s": cfg.R * cfg.T / (ms_step * 1e-3),
     }
+    if sampler:
+        result["clocks"] = sampler.summary(peak)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_ranks or cfg.R)
