@@ -16,6 +16,8 @@
 // registers.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -93,6 +95,24 @@ __device__ __forceinline__ uint32_t lds_addr(const char* q) {
         "+v"(ACC[1][1]), "+v"(ACC[1][2]), "+v"(ACC[1][3]), "=&v"(N.a0), "=&v"(N.a1), "=&v"(N.b0),          \
         "=&v"(N.b1), "=&v"(N.b2), "=&v"(N.b3)                                                             \
       : "v"(C.a0), "v"(C.a1), "v"(C.b0), "v"(C.b1), "v"(C.b2), "v"(C.b3), "v"(AA), "v"(BA))
+
+// The same sub-step for a wave whose second 32-row block lies wholly past the tile's valid
+// rows: only the m = 0 MFMAs, and no read of the second A block.
+#define MOE_MFMA_SUBSTEP_READ_M1(ACC, C, N, AA, BA)                                                       \
+  asm volatile(                                                                                           \
+      "v_mfma_f32_32x32x16_bf16 %0, %9, %10, %0\n\t"                                                      \
+      "ds_read_b128 %4, %14\n\t"                                                                          \
+      "v_mfma_f32_32x32x16_bf16 %1, %9, %11, %1\n\t"                                                      \
+      "ds_read_b128 %5, %15\n\t"                                                                          \
+      "ds_read_b128 %6, %15 offset:4096\n\t"                                                              \
+      "v_mfma_f32_32x32x16_bf16 %2, %9, %12, %2\n\t"                                                      \
+      "ds_read_b128 %7, %15 offset:8192\n\t"                                                              \
+      "ds_read_b128 %8, %15 offset:12288\n\t"                                                             \
+      "v_mfma_f32_32x32x16_bf16 %3, %9, %13, %3\n\t"                                                      \
+      "s_waitcnt lgkmcnt(0)"                                                                              \
+      : "+v"(ACC[0][0]), "+v"(ACC[0][1]), "+v"(ACC[0][2]), "+v"(ACC[0][3]), "=&v"(N.a0), "=&v"(N.b0),     \
+        "=&v"(N.b1), "=&v"(N.b2), "=&v"(N.b3)                                                             \
+      : "v"(C.a0), "v"(C.b0), "v"(C.b1), "v"(C.b2), "v"(C.b3), "v"(AA), "v"(BA))
 
 // b0/b1: this expert's weight matrices ([Nout][K], row stride b_ld); c0: first output
 // column of the tile.
@@ -178,26 +198,45 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
   cur.b2 = *reinterpret_cast<const i32x4*>(smem + kGemmBM * kGemmBK * 2 + swz_off(wn * 128 + 64 + r32, hi));
   cur.b3 = *reinterpret_cast<const i32x4*>(smem + kGemmBM * kGemmBK * 2 + swz_off(wn * 128 + 96 + r32, hi));
 
-  for (int ks = 0; ks < nk; ++ks) {
-    const char* st = smem + (ks & 1) * kStageBytes;
-#pragma unroll
-    for (int sub = 0; sub < kGemmBK / 16 - 1; ++sub) {
+  // Row padding: the last row tile of an expert is usually partial.  A wave whose 32-row
+  // blocks lie wholly past the valid rows skips their MFMAs (and fragment reads); it still
+  // fills and meets every barrier.  Waves w and w + 4 share a SIMD and own rows 64(w/2) and
+  // 64(w/2) + 128, so a tile of at most 128 valid rows keeps each SIMD at most half busy.
+  // Skipped MFMAs only ever accumulate into rows that are never stored.
+  const int mv = __builtin_amdgcn_readfirstlane(min(2, max(0, (rows - wm * 64 + 31) >> 5)));
+  auto substep = [&](auto mvc, uint32_t aa, uint32_t ba) {
+    constexpr int MV = decltype(mvc)::value;
+    if constexpr (MV == 2) {
       Frags nxt;
-      const uint32_t aa = a_at(st, sub + 1), ba = b_at(st, sub + 1);
       MOE_MFMA_SUBSTEP_READ(acc, cur, nxt, aa, ba);
       cur = nxt;
+    } else if constexpr (MV == 1) {
+      Frags nxt;
+      MOE_MFMA_SUBSTEP_READ_M1(acc, cur, nxt, aa, ba);
+      cur.a0 = nxt.a0;
+      cur.b0 = nxt.b0;
+      cur.b1 = nxt.b1;
+      cur.b2 = nxt.b2;
+      cur.b3 = nxt.b3;
     }
-    __builtin_amdgcn_s_waitcnt(0);      // this wave's fills of the next stage landed
-    __syncthreads();                    // ... and everyone's; every wave is done with this stage
-    if (ks + 2 < nk) issue(ks + 2);     // into this stage
-    // the next stage's first fragments (after the last K step these reads land in the
-    // other stage, inside the LDS allocation, and are not used)
-    const char* sn = smem + ((ks + 1) & 1) * kStageBytes;
-    Frags nxt;
-    const uint32_t aa = a_at(sn, 0), ba = b_at(sn, 0);
-    MOE_MFMA_SUBSTEP_READ(acc, cur, nxt, aa, ba);
-    cur = nxt;
-  }
+  };
+  auto kloop = [&](auto mvc) {
+    for (int ks = 0; ks < nk; ++ks) {
+      const char* st = smem + (ks & 1) * kStageBytes;
+#pragma unroll
+      for (int sub = 0; sub < kGemmBK / 16 - 1; ++sub) substep(mvc, a_at(st, sub + 1), b_at(st, sub + 1));
+      __builtin_amdgcn_s_waitcnt(0);      // this wave's fills of the next stage landed
+      __syncthreads();                    // ... and everyone's; every wave is done with this stage
+      if (ks + 2 < nk) issue(ks + 2);     // into this stage
+      // the next stage's first fragments (after the last K step these reads land in the
+      // other stage, inside the LDS allocation, and are not used)
+      const char* sn = smem + ((ks + 1) & 1) * kStageBytes;
+      substep(mvc, a_at(sn, 0), b_at(sn, 0));
+    }
+  };
+  if (mv == 2) kloop(std::integral_constant<int, 2>{});
+  else if (mv == 1) kloop(std::integral_constant<int, 1>{});
+  else kloop(std::integral_constant<int, 0>{});
 
   // The MFMAs above are inline assembly, which the compiler's hazard recognizer does not
   // see: a read of an accumulator right after the MFMA that writes it would see the old
