@@ -125,34 +125,46 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int ks = 0; ks < nk; ++ks) {
-    if (ks + 1 < nk) issue(ks + 1);     // other stage: everyone finished reading it
-    const char* sa = smem + (ks & 1) * kMxStageBytes;
-    const char* sb = sa + kGemmBM * kMxBK;
-    const uint32_t* ss = reinterpret_cast<const uint32_t*>(sa + kMxDataBytes);
-    int wa[2], wb[4];
+  // Row padding: a wave whose 32-row blocks lie wholly past the tile's valid rows skips
+  // their fragment reads and MFMAs (they only feed rows that are never stored); it still
+  // fills and meets every barrier.
+  const int mv = __builtin_amdgcn_readfirstlane(min(2, max(0, (rows - wm * 64 + 31) >> 5)));
+  auto kloop = [&](auto mvc) {
+    constexpr int MV = decltype(mvc)::value;
+    for (int ks = 0; ks < nk; ++ks) {
+      if (ks + 1 < nk) issue(ks + 1);     // other stage: everyone finished reading it
+      const char* sa = smem + (ks & 1) * kMxStageBytes;
+      const char* sb = sa + kGemmBM * kMxBK;
+      const uint32_t* ss = reinterpret_cast<const uint32_t*>(sa + kMxDataBytes);
+      if constexpr (MV > 0) {
+        int wa[2], wb[4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) wa[m] = int(ss[wm * 64 + m * 32 + r32] >> (8 * hi));
+        for (int m = 0; m < MV; ++m) wa[m] = int(ss[wm * 64 + m * 32 + r32] >> (8 * hi));
 #pragma unroll
-    for (int n = 0; n < 4; ++n) wb[n] = int(ss[kGemmBM + wn * 128 + n * 32 + r32] >> (8 * hi));
+        for (int n = 0; n < 4; ++n) wb[n] = int(ss[kGemmBM + wn * 128 + n * 32 + r32] >> (8 * hi));
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      i32x8 fa[2], fb[4];
+        for (int st = 0; st < 2; ++st) {
+          i32x8 fa[2], fb[4];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) fa[m] = ld_frag(sa, wm * 64 + m * 32 + r32, 4 * st + hi);
+          for (int m = 0; m < MV; ++m) fa[m] = ld_frag(sa, wm * 64 + m * 32 + r32, 4 * st + hi);
 #pragma unroll
-      for (int n = 0; n < 4; ++n) fb[n] = ld_frag(sb, wn * 128 + n * 32 + r32, 4 * st + hi);
+          for (int n = 0; n < 4; ++n) fb[n] = ld_frag(sb, wn * 128 + n * 32 + r32, 4 * st + hi);
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+          for (int m = 0; m < MV; ++m)
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
-          acc[m][n] = (st == 0)
-              ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[m], fb[n], acc[m][n], 0, 0, 0, wa[m], 0, wb[n])
-              : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[m], fb[n], acc[m][n], 0, 0, 2, wa[m], 2, wb[n]);
+            for (int n = 0; n < 4; ++n)
+              acc[m][n] = (st == 0)
+                  ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[m], fb[n], acc[m][n], 0, 0, 0, wa[m], 0, wb[n])
+                  : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[m], fb[n], acc[m][n], 0, 0, 2, wa[m], 2, wb[n]);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);      // this wave's fills of the next stage landed
+      __syncthreads();                    // ... and everyone's
     }
-    __builtin_amdgcn_s_waitcnt(0);      // this wave's fills of the next stage landed
-    __syncthreads();                    // ... and everyone's
-  }
+  };
+  if (mv == 2) kloop(std::integral_constant<int, 2>{});
+  else if (mv == 1) kloop(std::integral_constant<int, 1>{});
+  else kloop(std::integral_constant<int, 0>{});
 
   if (MODE == 2) {
     // Backward epilogue, two passes of 128 tile rows: stage (a, b) as fp32 pairs in LDS
