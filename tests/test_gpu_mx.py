@@ -130,9 +130,13 @@ def test_mx_quantize_f32_midpoints_and_neighbours():
 
 
 # --------------------------------------------------------------------------- path
-def _problem(cfg, seed=0):
+def _problem(cfg, seed=0, never=None):
+    """Seeded inputs on the device; experts listed in `never` get their logits lowered by
+    100 so that no token selects them."""
     from mixture_experts_layer_histogram_amd.device import DeviceProblem
     inp = inputs.make_inputs(cfg, seed=seed)
+    if never:
+        inp.logits[..., list(never)] -= 100.0
     return inp, DeviceProblem(cfg, inp)
 
 
@@ -159,12 +163,40 @@ MX_SKEW = configs.DSV3_MX.scaled(name="mx-slice-zipf R2 T512 d1024 E64/8 k8 F768
 MX_CASES = {"mx-small": MX_SMALL, "mx-dsv3-slice": MX_SLICE, "mx-slice-zipf": MX_SKEW}
 
 
+# Degenerate shapes: (config, experts never selected)
+MX_EDGE = {
+    # a single token: 2 rows in the whole GEMM (254 padded rows per tile skipped)
+    "mx-single-token": (configs.DSV3_MX.scaled(name="mx-one-token R1 T1 d256 E8/8 k2 F128", R=1, T=1, d=256, E=8,
+                                               E_local=8, k=2, F=128), None),
+    # one resident expert of 16
+    "mx-one-local-expert": (configs.DSV3_MX.scaled(name="mx-one-local R2 T300 d384 E16/1 k4 F256", R=2, T=300,
+                                                   d=384, E=16, E_local=1, k=4, F=256), None),
+    # no token selects a local expert: N = 0, y exactly zero everywhere
+    "mx-no-local-pairs": (configs.DSV3_MX.scaled(name="mx-no-local R2 T200 d256 E16/4 k4 F128", R=2, T=200,
+                                                 d=256, E=16, E_local=4, k=4, F=128), (0, 1, 2, 3)),
+}
+
+
 @pytest.mark.parametrize("name", list(MX_CASES))
 def test_mx_forward_parity(name):
-    torch = _torch()
     cfg = MX_CASES[name]
     _say(f"[mx-forward] {cfg.name}")
     inp, P = _problem(cfg)
+    _check_mx_forward(cfg, inp, P)
+
+
+@pytest.mark.parametrize("name", list(MX_EDGE))
+def test_mx_forward_edge_cases(name):
+    cfg, never = MX_EDGE[name]
+    _say(f"[mx-forward-edge] {cfg.name}")
+    inp, P = _problem(cfg, never=never)
+    N = _check_mx_forward(cfg, inp, P)
+    if never:
+        assert N == 0
+
+
+def _check_mx_forward(cfg, inp, P):
+    torch = _torch()
     P.forward()
     assert P.status() == 0
     torch.cuda.synchronize()
@@ -185,12 +217,15 @@ def test_mx_forward_parity(name):
     xc, xs, _ = MX.quantize(O.dispatch(inp.x_f32, ref["pull_src"]))
     assert np.array_equal(P.xe[:N].cpu().numpy(), xc)
     assert np.array_equal(P.scales_rowmajor(P.xe_scales, N), xs)
-    ye = P.rows_f64(P.ye[:N])
-    allr = np.ones(N, dtype=bool)
-    err_ffn, fro_ffn = _row_rel_err(ye, ref["ye"], allr), _fro_rel_err(ye, ref["ye"], allr)
     so = ref["slot_of"]
     y = np.stack([P.rows_f64(P.y[r]) for r in range(cfg.R)])
     has = (so >= 0).any(-1)
+    assert (y[~has] == 0).all()
+    if N == 0:
+        return N
+    ye = P.rows_f64(P.ye[:N])
+    allr = np.ones(N, dtype=bool)
+    err_ffn, fro_ffn = _row_rel_err(ye, ref["ye"], allr), _fro_rel_err(ye, ref["ye"], allr)
     err = _row_rel_err(y.reshape(-1, cfg.d), ref["y"].reshape(-1, cfg.d), has.reshape(-1))
     fro_y = _fro_rel_err(y.reshape(-1, cfg.d), ref["y"].reshape(-1, cfg.d), has.reshape(-1))
     exact = O.forward(inp.logits, inp.x_f32, inp.w1_f32, inp.w3_f32, inp.w2_f32, inp.expert_to_local,
@@ -202,7 +237,7 @@ def test_mx_forward_parity(name):
          f"(vs unquantised: fro={fro:.3e} row={_row_rel_err(y.reshape(-1, cfg.d), exact.reshape(-1, cfg.d), live):.3e})")
     assert err_ffn <= TOL_Q_ROW and fro_ffn <= TOL_Q_FRO
     assert err <= TOL_Q_ROW and fro_y <= TOL_Q_FRO
-    assert (y[~has] == 0).all()
+    return N
 
 
 def test_mx_forward_deterministic_and_stagewise_equals_fused_call():

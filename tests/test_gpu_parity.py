@@ -152,9 +152,13 @@ def test_layout_rejects_bad_placement_on_device():
 
 
 # --------------------------------------------------------------------------- full path
-def _problem(cfg, seed=0):
+def _problem(cfg, seed=0, never=None):
+    """Seeded inputs on the device; experts listed in `never` get their logits lowered by
+    100 so that no token selects them."""
     from mixture_experts_layer_histogram_amd.device import DeviceProblem
     inp = inputs.make_inputs(cfg, seed=seed)
+    if never:
+        inp.logits[..., list(never)] -= 100.0
     return inp, DeviceProblem(cfg, inp)
 
 
@@ -166,12 +170,50 @@ FORWARD_CASES = {"tiny": configs.TINY, "mid": configs.MID, "mid-ragged": MID_SMA
                  "dsv3-slice-zipf": SLICE_SKEW}
 
 
+# Degenerate and boundary shapes: (config, experts never selected)
+EDGE_CASES = {
+    # one expert, top-1: the layer is the plain SwiGLU FFN of every token; F = 192 leaves
+    # a half-empty column tile in GEMM1 and d = 128 a half-empty one in GEMM2
+    "E1-k1": (configs.MoEConfig("e1-k1 R1 T100 d128 E1 k1 F192", R=1, T=100, d=128, E=1, E_local=1, k=1,
+                                F=192, dtype="bf16"), None),
+    # k = E, all local: every token uses every expert
+    "k-equals-E": (configs.MoEConfig("k=E R2 T130 d256 E16/16 k16 F256", R=2, T=130, d=256, E=16, E_local=16,
+                                     k=16, F=256, dtype="bf16"), None),
+    # a single token (2 rows in the whole GEMM)
+    "single-token": (configs.MoEConfig("one-token R1 T1 d512 E8/8 k2 F256", R=1, T=1, d=512, E=8, E_local=8,
+                                       k=2, F=256, dtype="bf16"), None),
+    # one resident expert of 32: most tokens have no local pair
+    "one-local-expert": (configs.MoEConfig("one-local R3 T200 d256 E32/1 k4 F128", R=3, T=200, d=256, E=32,
+                                           E_local=1, k=4, F=128, dtype="bf16"), None),
+    # no token selects a local expert: N = 0, empty GEMMs, y exactly zero everywhere
+    "no-local-pairs": (configs.MoEConfig("no-local R2 T300 d256 E16/4 k4 F256", R=2, T=300, d=256, E=16,
+                                         E_local=4, k=4, F=256, dtype="bf16"), (0, 1, 2, 3)),
+    # fp32 with ragged d, F and T
+    "fp32-ragged": (configs.MoEConfig("fp32-ragged R3 T333 d96 E8/6 k3 F80", R=3, T=333, d=96, E=8, E_local=6,
+                                      k=3, F=80, dtype="f32"), None),
+}
+
+
 @pytest.mark.parametrize("name", list(FORWARD_CASES))
 def test_forward_parity(name):
-    torch = _torch()
     cfg = FORWARD_CASES[name]
     _say(f"[forward] {cfg.name}")
     inp, P = _problem(cfg)
+    _check_forward(cfg, inp, P)
+
+
+@pytest.mark.parametrize("name", list(EDGE_CASES))
+def test_forward_edge_cases(name):
+    cfg, never = EDGE_CASES[name]
+    _say(f"[forward-edge] {cfg.name}")
+    inp, P = _problem(cfg, never=never)
+    N = _check_forward(cfg, inp, P)
+    if never:
+        assert N == 0
+
+
+def _check_forward(cfg, inp, P):
+    torch = _torch()
     P.forward()
     assert P.status() == 0
     torch.cuda.synchronize()
@@ -206,6 +248,7 @@ def test_forward_parity(name):
     assert err_ffn <= TOL[cfg.dtype]
     assert err <= TOL[cfg.dtype]
     assert (y[~has] == 0).all()
+    return N
 
 
 def test_forward_deterministic_and_stagewise_equals_fused_call():
