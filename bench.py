@@ -62,6 +62,9 @@ def parse():
                     help="comma-separated tokens per rank: time the forward at each (one JSON line per value; "
                          "the minibatch-size curve of the unfused path)"),
     ap.add_argument("--cpu-sample-ranks", type=int, default=0, help="0 = all ranks (the whole step)")
+    ap.add_argument("--signal-latency", action="store_true",
+                    help="time the inter-partition hand-off (flag round trip between workgroup pairs, same XCD and "
+                         "across XCDs, L2-local and agent-scope) instead of the layer; prints its own JSON line")
     ap.add_argument("--sample-clocks", action="store_true",
                     help="sample the GPU's gfx clocks and socket power with amd-smi during the timed steps "
                          "(use enough --steps for a few seconds) and report their means")
@@ -404,6 +407,30 @@ def run_backward(args, cfg, inp, P, stream, N):
     print(json.dumps(result), flush=True)
 
 
+def run_signal_latency(args):
+    """Round trip of a flag (and of a 64 KiB payload) between two workgroups, the one-GPU
+    analogue of the pages' push/pull signalling latency.  128 pairs run concurrently; a
+    round is one flag plus one acknowledgement per pair."""
+    import torch
+    from mixture_experts_layer_histogram_amd import moe
+    rounds = max(100, args.steps * 25)
+    res = []
+    for words in (0, 16384):
+        scratch = torch.empty(moe.moe_signal_probe_bytes(words), dtype=torch.uint8, device="cuda:0")
+        for cross in (0, 1):
+            for scope in (0, 1):
+                moe.moe_signal_probe(cross, scope, words, 20, scratch, check=False)     # warm-up
+                rc, us, stale, tmo, same = moe.moe_signal_probe(cross, scope, words, rounds, scratch, check=False)
+                res.append({"payload_bytes": words * 4, "partners": "different XCDs" if cross else "same XCD",
+                            "handoff": "agent-scope release/acquire" if scope else "L2-local (L1 invalidate)",
+                            "us_per_round_trip": us, "stale_words": stale, "timeouts": tmo, "rc": rc,
+                            "pairs_on_one_xcd": same})
+                log(f"[signal] payload {words * 4} B, {'cross' if cross else 'same'}-XCD, scope {scope}: "
+                    f"{us:.2f} us/round, stale {stale}, timeouts {tmo}")
+    print(json.dumps({"metric": "inter-partition signal round trip (one GPU)", "unit": "us", "n_gpus": 1,
+                      "rounds": rounds, "pairs": 128, "higher_is_better": False, "results": res}), flush=True)
+
+
 def run_sweep(args, cfg, P, stream):
     """Forward time against tokens handed to the layer at once.  The problem's buffers are
     sized for T tokens per rank; each point lowers the shape's T in place (every call reads
@@ -451,6 +478,9 @@ def main():
     import torch
     from mixture_experts_layer_histogram_amd.device import DeviceProblem
 
+    if args.signal_latency:
+        run_signal_latency(args)
+        return
     cfg = configs.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     log(f"[bench] generating inputs for {cfg.name}")

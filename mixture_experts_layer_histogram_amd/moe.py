@@ -26,7 +26,7 @@ EXPORTS = ["moe_max_pairs", "moe_workspace_bytes", "moe_mx_quantize", "moe_layou
            "moe_ring_slot_bytes", "moe_persistent_workspace_bytes", "moe_backward_workspace_bytes",
            "moe_combine_pull_reverse", "moe_expert_ffn_backward",
            "moe_dispatch_push_reverse", "moe_backward", "moe_backward_prepare_mx", "moe_backward_mx",
-           "moe_read_status", "moe_strerror", "moe_version"]
+           "moe_signal_probe_bytes", "moe_signal_probe", "moe_read_status", "moe_strerror", "moe_version"]
 
 
 class MoEError(RuntimeError):
@@ -95,6 +95,9 @@ def lib() -> ctypes.CDLL:
         L.moe_backward_prepare_mx.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, VP]
         L.moe_backward_mx.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, MS, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP,
                                       SZ, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_signal_probe_bytes.argtypes = [I32]
+        L.moe_signal_probe_bytes.restype = SZ
+        L.moe_signal_probe.argtypes = [I32, I32, I32, I32, VP, SZ, VP, VP, VP, VP, VP]
         L.moe_read_status.argtypes = [VP, VP]
         L.moe_strerror.argtypes = [I32]
         L.moe_strerror.restype = ctypes.c_char_p
@@ -295,3 +298,20 @@ def moe_backward_mx(shape, placement, dy, x, xe, xe_scales, ye, w1q, w3q, w_scal
 
 def moe_read_status(ws, stream=None) -> int:
     return int(lib().moe_read_status(_p(ws), _stream(stream)))
+
+
+def moe_signal_probe_bytes(payload_words: int) -> int:
+    return int(lib().moe_signal_probe_bytes(int(payload_words)))
+
+
+def moe_signal_probe(cross_xcd: int, scope: int, payload_words: int, rounds: int, scratch, scratch_bytes=None,
+                     stream=None, check=True):
+    """Returns (rc, us_per_round, stale_words, timeouts, pairs_same_xcd)."""
+    us = ctypes.c_float(0.0)
+    stale, tmo, same = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    rc = lib().moe_signal_probe(int(cross_xcd), int(scope), int(payload_words), int(rounds), _p(scratch),
+                                scratch.numel() if scratch_bytes is None else scratch_bytes, ctypes.byref(us),
+                                ctypes.byref(stale), ctypes.byref(tmo), ctypes.byref(same), _stream(stream))
+    if check:
+        _check(rc, "moe_signal_probe")
+    return rc, float(us.value), int(stale.value), int(tmo.value), int(same.value)

@@ -304,3 +304,25 @@ def test_mx_backward_entries_reject_bad_arguments_before_launch():
     assert bwd(wsc=moe.MXScales(FAKE, FAKE + 2, FAKE)) == -2
     assert bwd(dw1=FAKE + 4) == -2
     assert bwd(bb=bws - 256) == -3
+
+
+def test_signal_probe_sizes_and_rejects_bad_arguments_before_launch():
+    L = moe.lib()
+    assert moe.moe_signal_probe_bytes(0) > 0
+    assert moe.moe_signal_probe_bytes(16384) >= 128 * 16384 * 4
+    assert moe.moe_signal_probe_bytes(-1) == 0 and moe.moe_signal_probe_bytes(1 << 21) == 0
+    need = moe.moe_signal_probe_bytes(1024)
+    us, n1, n2, n3 = ctypes.c_float(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    outs = [ctypes.byref(us), ctypes.byref(n1), ctypes.byref(n2), ctypes.byref(n3)]
+
+    def call(cross=0, scope=1, words=1024, rounds=10, scratch=FAKE, nbytes=need, out=outs):
+        return L.moe_signal_probe(cross, scope, words, rounds, scratch, nbytes, *out, None)
+    assert call(cross=2) == -1
+    assert call(scope=-1) == -1
+    assert call(words=-5) == -1
+    assert call(rounds=0) == -1
+    assert call(rounds=100001) == -1
+    assert call(scratch=None) == -1
+    assert call(out=[None] + outs[1:]) == -1
+    assert call(scratch=FAKE + 64) == -2
+    assert call(nbytes=need - 1) == -3
