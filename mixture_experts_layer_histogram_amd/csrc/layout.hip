@@ -8,9 +8,10 @@
 // two-column pull schedule built without sorting.
 //
 // Three launches:
-//   1. topk_hist   : one 16-lane group per token (4 tokens per wave); k rounds of a
-//                    16-lane max over packed (logit, ~id) keys; gate = softmax over
-//                    the kept logits; per-block expert histogram in LDS.
+//   1. topk_hist   : one 16-lane group per token (4 tokens per wave, a block's 64
+//                    tokens at once for E <= 256); k rounds of a 16-lane max over
+//                    packed (logit, ~id) keys; gate = softmax over the kept logits;
+//                    per-block expert histogram in LDS.
 //   2. layout_scan : block 0 validates the placement, scans the local experts'
 //                    block histograms (flattened exclusive scan = offsets and
 //                    per-block bases at once) and the GEMM-tile / chunk tables;
@@ -42,25 +43,29 @@ __device__ __forceinline__ int key_expert(unsigned long long key) {
   return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
 }
 
-// VPL = logits held per lane (E <= 16 * VPL)
-template <int VPL>
-__global__ __launch_bounds__(256) void topk_hist_kernel(RankPtrs<const float*> logits, int R, int T,
-                                                        int E, int k, int32_t* __restrict__ topk_idx,
-                                                        float* __restrict__ topk_w,
-                                                        int32_t* __restrict__ blockhist) {
+// VPL = logits held per lane (E <= 16 * VPL); NT threads per block, so NT / 16 tokens in
+// flight per pass over the block's kTokPerLayoutBlock tokens.  With up to 256 experts the
+// block has 1024 threads (every token of the block in one pass) and the ordering keys are
+// built once per token; wider rows keep 256 threads and rebuild the keys every round.
+template <int VPL, int NT>
+__global__ __launch_bounds__(NT) void topk_hist_kernel(RankPtrs<const float*> logits, int R, int T,
+                                                       int E, int k, int32_t* __restrict__ topk_idx,
+                                                       float* __restrict__ topk_w,
+                                                       int32_t* __restrict__ blockhist) {
+  constexpr bool kKeys = VPL <= 16;        // keys kept in registers
+  constexpr int kGroups = NT / 16;         // tokens in flight per pass
   __shared__ int hist[1024];
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 256) hist[e] = 0;
+  for (int e = tid; e < E; e += NT) hist[e] = 0;
   __syncthreads();
 
-  const int lane = tid & 63, wave = tid >> 6;
-  const int grp = lane >> 4, sl = lane & 15;
+  const int grp = tid >> 4, sl = tid & 15;
   const int64_t RT = int64_t(R) * T;
   const int64_t tok0 = int64_t(blockIdx.x) * kTokPerLayoutBlock;
 
 #pragma unroll 1
-  for (int pass = 0; pass < kTokPerLayoutBlock / 16; ++pass) {
-    const int64_t g = tok0 + wave * (kTokPerLayoutBlock / 4) + pass * 4 + grp;
+  for (int pass = 0; pass < kTokPerLayoutBlock / kGroups; ++pass) {
+    const int64_t g = tok0 + pass * kGroups + grp;
     const bool valid = g < RT;
     float v[VPL];
     if (valid) {
@@ -76,6 +81,14 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(RankPtrs<const float*> l
 #pragma unroll
       for (int i = 0; i < VPL; ++i) v[i] = 0.0f;
     }
+    unsigned long long keys[kKeys ? VPL : 1];
+    if constexpr (kKeys) {
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int e = sl + 16 * i;
+        keys[i] = (e < E) ? make_key(v[i], e) : 0ull;       // 0 is below every real key
+      }
+    }
 
     unsigned long long taken = 0ull;
     int my_idx = 0;
@@ -85,7 +98,7 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(RankPtrs<const float*> l
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
         const int e = sl + 16 * i;
-        const unsigned long long key = make_key(v[i], e);
+        const unsigned long long key = kKeys ? keys[i] : make_key(v[i], e);
         const bool ok = (e < E) && !((taken >> i) & 1ull);
         best = (ok && key > best) ? key : best;
       }
@@ -114,7 +127,7 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(RankPtrs<const float*> l
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) blockhist[size_t(blockIdx.x) * E + e] = hist[e];
+  for (int e = tid; e < E; e += NT) blockhist[size_t(blockIdx.x) * E + e] = hist[e];
 }
 
 // exclusive scan over a 1024-thread block; returns the thread's exclusive prefix
@@ -155,6 +168,7 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(
     const int e = (blockIdx.x - 1) * 64 + (tid >> 4), q = tid & 15;
     int sum = 0;
     if (e < E) {
+#pragma unroll 8
       for (int b = q; b < nb; b += 16) sum += blockhist[size_t(b) * E + e];
     }
 #pragma unroll
@@ -209,17 +223,41 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(
   const int c = tid / tpc, q = tid - c * tpc;
   const int seg = (nb + tpc - 1) / tpc;
   const int b0 = q * seg, b1 = min(nb, b0 + seg);
+  // a thread's segment of at most kSegRegs blocks is loaded once, all loads in flight
+  // together, and kept in registers for the second pass
+  constexpr int kSegRegs = 16;
+  int hv[kSegRegs];
   int mysum = 0;
   const int col = (c < El) ? l2g_s[c] : 0;
-  if (c < El)
-    for (int b = b0; b < b1; ++b) mysum += blockhist[size_t(b) * E + col];
+  if (c < El) {
+    if (seg <= kSegRegs) {
+#pragma unroll
+      for (int i = 0; i < kSegRegs; ++i) {
+        const int b = b0 + i;
+        hv[i] = (b < b1) ? blockhist[size_t(b) * E + col] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < kSegRegs; ++i) mysum += hv[i];
+    } else {
+      for (int b = b0; b < b1; ++b) mysum += blockhist[size_t(b) * E + col];
+    }
+  }
   int N = 0;
   const int ex = block_excl_scan_1024(mysum, tmp16, &N);
   if (c < El) {
     int run = ex;
-    for (int b = b0; b < b1; ++b) {
-      blockbase[size_t(b) * El + c] = run;
-      run += blockhist[size_t(b) * E + col];
+    if (seg <= kSegRegs) {
+#pragma unroll
+      for (int i = 0; i < kSegRegs; ++i) {
+        const int b = b0 + i;
+        if (b < b1) blockbase[size_t(b) * El + c] = run;
+        run += hv[i];
+      }
+    } else {
+      for (int b = b0; b < b1; ++b) {
+        blockbase[size_t(b) * El + c] = run;
+        run += blockhist[size_t(b) * E + col];
+      }
     }
     if (q == 0) col_off[c] = ex;
   }
@@ -298,7 +336,8 @@ __global__ __launch_bounds__(64) void slot_assign_kernel(
 template <int VPL>
 static void launch_topk(dim3 grid, hipStream_t st, const RankPtrs<const float*>& lp, const moe_shape_t& s,
                         int32_t* topk_idx, float* topk_w, int32_t* blockhist) {
-  hipLaunchKernelGGL(topk_hist_kernel<VPL>, grid, dim3(256), 0, st, lp, s.R, s.T, s.E, s.k, topk_idx,
+  constexpr int NT = VPL <= 16 ? 1024 : 256;
+  hipLaunchKernelGGL((topk_hist_kernel<VPL, NT>), grid, dim3(NT), 0, st, lp, s.R, s.T, s.E, s.k, topk_idx,
                      topk_w, blockhist);
 }
 
