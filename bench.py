@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--sample-clocks", action="store_true",
                     help="sample the GPU's gfx clocks and socket power with amd-smi during the timed steps "
                          "(use enough --steps for a few seconds) and report their means")
+    ap.add_argument("--cold-cache", action="store_true",
+                    help="after the timed steps, time as many again, each after writing a 1 GiB buffer "
+                         "(evicts the 4 MB L2s and the 256 MB MALL); reported as 'cold'")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run three plain 1 GiB device copies (counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -396,6 +399,7 @@ def run_backward(args, cfg, inp, P, stream, N):
                      "achieved": flops / t_ffn / 1e12, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": flops / t_ffn / PEAK_BF16_FLOPS, "traffic": None},
         "stages_ms": stage_ms,
+        "step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step))},
         "stages_hbm_frac": {
             "pull_reverse": pull_bytes / (stage_ms["pull_reverse"] * 1e-3) / PEAK_HBM,
             "push_reverse": (push_bytes + merge_bytes + gate_bytes) / (stage_ms["push_reverse"] * 1e-3) / PEAK_HBM,
@@ -533,7 +537,32 @@ def main():
     ms_step = total_ms / args.steps
     stage_ms = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j, n in enumerate(names)}
+    per_step = [ev[i][0].elapsed_time(ev[i][len(names)]) for i in range(args.steps)]
     log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; stages {stage_ms}")
+    cold = None
+    if args.cold_cache:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush.fill_(i & 255)
+            e = cev[i]
+            e[0].record(stream)
+            P.layout()
+            e[1].record(stream)
+            P.dispatch()
+            e[2].record(stream)
+            P.ffn()
+            e[3].record(stream)
+            P.combine()
+            e[4].record(stream)
+        torch.cuda.synchronize()
+        del flush
+        cs = [cev[i][0].elapsed_time(cev[i][len(names)]) for i in range(args.steps)]
+        cold = {"note": "each step after a 1 GiB buffer write; flush not timed",
+                "ms_per_step": {"median": float(np.median(cs)), "min": float(np.min(cs)), "mean": float(np.mean(cs))},
+                "stages_ms": {n: float(np.median([cev[i][j].elapsed_time(cev[i][j + 1]) for i in range(args.steps)]))
+                              for j, n in enumerate(names)}}
+        log(f"[bench] cold cache: {cold}")
     if args.copy_calibration:
         src = torch.empty(CAL_BYTES, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -542,6 +571,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    counts = P.counts.cpu().numpy().astype(np.int64)
+    local_counts = counts[np.asarray(inp.expert_to_local) >= 0]
+    mean_load = cfg.R * cfg.T * cfg.k / cfg.E
+    load = {"kind": cfg.load, "mean_pairs_per_expert": mean_load,
+            "local_max_pairs": int(local_counts.max()) if local_counts.size else 0,
+            "local_max_over_mean": float(local_counts.max() / mean_load) if local_counts.size else 0.0}
     esz = 4 if cfg.dtype == "f32" else 2
     row = cfg.d * esz
     flops = 6.0 * cfg.d * cfg.F * N
@@ -570,12 +605,13 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) tokens, fan-in scaled random expert weights, router logits x@W_r)",
         "config": {"workload": cfg.name, "R": cfg.R, "T": cfg.T, "d": cfg.d, "E": cfg.E,
-                   "E_local": cfg.E_local, "k": cfg.k, "F": cfg.F, "local_pairs": N,
+                   "E_local": cfg.E_local, "k": cfg.k, "F": cfg.F, "local_pairs": N, "load": load,
                    "path": "unfused (layout, dispatch, ffn, combine+merge kernels on one stream)"},
         "roofline": {"bound": "mfma", "kernel": "grouped SwiGLU FFN (gate/up+SwiGLU, down GEMMs)",
                      "achieved": flops / t_ffn / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
                      "frac": flops / t_ffn / peak, "traffic": traffic},
         "stages_ms": stage_ms,
+        "step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step))},
         "stages_hbm_frac": {
             "dispatch": gather_bytes / (stage_ms["dispatch"] * 1e-3) / PEAK_HBM,
             "combine+merge": (push_bytes + merge_bytes) / (stage_ms["combine"] * 1e-3) / PEAK_HBM,
@@ -583,6 +619,8 @@ def main():
         "pairs_per_s": N / (ms_step * 1e-3),
         "source_tokens_per_s": cfg.R * cfg.T / (ms_step * 1e-3),
     }
+    if cold:
+        result["cold"] = cold
     if sampler:
         result["clocks"] = sampler.summary(peak)
     if not args.no_cpu_baseline:
