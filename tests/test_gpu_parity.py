@@ -298,3 +298,98 @@ def test_forward_full_dsv3_sampled():
     assert (P.y[zr][zt].float().cpu().numpy() == 0).all()
     _say(f"  N={lay['N']} sampled y_rel={worst:.3e}")
     assert worst <= TOL["bf16"]
+
+
+# --------------------------------------------------------------------------- metamorphic
+# Relations the HIP path must satisfy bit for bit, whatever the oracle says: each output
+# row's arithmetic (MFMA K order, fp32 merge in ascending j) does not depend on where the
+# row lands in the expert segments or GEMM tiles.
+META_CASES = {
+    "bf16": configs.MoEConfig("meta-bf16 R2 T1100 d384 E16/8 k4 F320", R=2, T=1100, d=384, E=16, E_local=8, k=4,
+                              F=320, dtype="bf16"),
+    "fp32": configs.MoEConfig("meta-fp32 R2 T300 d96 E8/6 k3 F80", R=2, T=300, d=96, E=8, E_local=6, k=3, F=80,
+                              dtype="f32"),
+    # MXFP8: scaling W2 by 2^m moves each block's E8M0 scale by m and leaves the codes alone
+    "mxfp8": configs.MoEConfig("meta-mx R2 T1100 d384 E16/8 k4 F384", R=2, T=1100, d=384, E=16, E_local=8, k=4,
+                               F=384, dtype="mxfp8"),
+}
+
+
+def _run(cfg, inp):
+    from mixture_experts_layer_histogram_amd.device import DeviceProblem
+    torch = _torch()
+    P = DeviceProblem(cfg, inp)
+    P.forward()
+    assert P.status() == 0
+    torch.cuda.synchronize()
+    return [P.y[r].float().cpu().numpy() for r in range(cfg.R)], P.N()
+
+
+def _assert_no_topk_ties(logits, k):
+    """The relations below change expert ids or token order; with an exact tie among a
+    token's k + 1 largest logits the lower-id rule could pick or order differently."""
+    top = -np.sort(-logits, axis=-1)[..., :min(k + 1, logits.shape[-1])]
+    assert (np.diff(top, axis=-1) < 0).all()
+
+
+def _replace(inp, **kw):
+    import dataclasses
+    return dataclasses.replace(inp, **kw)
+
+
+def _scale_store(store, dtype, m):
+    v = store if dtype == "f32" else inputs.bf16_bits_to_f32(store)
+    s = (v.astype(np.float32) * np.float32(2.0 ** m)).astype(np.float32)
+    return s if dtype == "f32" else inputs.f32_to_bf16_bits(s)
+
+
+@pytest.mark.parametrize("name", list(META_CASES))
+def test_forward_w2_power_of_two_scales_output_exactly(name):
+    cfg = META_CASES[name]
+    _say(f"[meta-w2-scale] {cfg.name}")
+    inp = inputs.make_inputs(cfg, seed=5)
+    y0, n0 = _run(cfg, inp)
+    assert n0 > 0
+    for m in (3, -2):
+        yi, _ = _run(cfg, _replace(inp, w2_store=_scale_store(inp.w2_store, cfg.dtype, m)))
+        for a, b in zip(y0, yi):
+            np.testing.assert_array_equal(b, a * np.float32(2.0 ** m))
+
+
+@pytest.mark.parametrize("name", list(META_CASES))
+def test_forward_token_permutation_permutes_output(name):
+    cfg = META_CASES[name]
+    _say(f"[meta-token-perm] {cfg.name}")
+    inp = inputs.make_inputs(cfg, seed=6)
+    _assert_no_topk_ties(inp.logits, cfg.k)
+    y0, _ = _run(cfg, inp)
+    rng = np.random.default_rng(60)
+    perm = np.stack([rng.permutation(cfg.T) for _ in range(cfg.R)])
+    x_p = np.stack([inp.x_store[r][perm[r]] for r in range(cfg.R)])
+    lg_p = np.stack([inp.logits[r][perm[r]] for r in range(cfg.R)])
+    yp, _ = _run(cfg, _replace(inp, x_store=x_p, logits=lg_p))
+    for r in range(cfg.R):
+        np.testing.assert_array_equal(yp[r], y0[r][perm[r]])
+
+
+@pytest.mark.parametrize("name", list(META_CASES))
+def test_forward_expert_relabelling_leaves_output_unchanged(name):
+    cfg = META_CASES[name]
+    _say(f"[meta-relabel] {cfg.name}")
+    inp = inputs.make_inputs(cfg, seed=7)
+    _assert_no_topk_ties(inp.logits, cfg.k)
+    y0, n0 = _run(cfg, inp)
+    rng = np.random.default_rng(70)
+    sigma = rng.permutation(cfg.E)              # old global id e -> new id sigma[e]
+    pl = rng.permutation(cfg.E_local)           # old local id l -> new local id pl[l]
+    logits = np.empty_like(inp.logits)
+    logits[..., sigma] = inp.logits
+    e2l = np.full(cfg.E, -1, dtype=np.int32)
+    loc = inp.expert_to_local >= 0
+    e2l[sigma[loc]] = pl[inp.expert_to_local[loc]]
+    inv = np.argsort(pl)                        # new local id -> old local id
+    w = {k: getattr(inp, k)[inv] for k in ("w1_store", "w3_store", "w2_store")}
+    y1, n1 = _run(cfg, _replace(inp, logits=logits, expert_to_local=e2l, **w))
+    assert n1 == n0
+    for a, b in zip(y0, y1):
+        np.testing.assert_array_equal(b, a)
