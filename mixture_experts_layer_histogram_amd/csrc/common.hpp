@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/moe.h"
 
 namespace moe {
@@ -17,6 +19,22 @@ constexpr int kGemmBN = 256;             // output columns of one tile
 constexpr int kGemmBK = 64;              // K step staged in LDS
 constexpr int kSimtBM = 64;              // fp32 SIMT path tile
 constexpr int kSimtBN = 64;
+
+// ---------------------------------------------------------------------------
+// host: a kernel-attribute grant (hipFuncSetAttribute acts on the current device), done
+// once per device; safe from several host threads (a grant repeated in a race is harmless)
+// ---------------------------------------------------------------------------
+template <typename F>
+inline hipError_t once_per_device(std::atomic<uint64_t>& done, F grant) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = grant();
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // ---------------------------------------------------------------------------
 // workspace layout (computed on the host from the shape; every region 256-byte aligned)

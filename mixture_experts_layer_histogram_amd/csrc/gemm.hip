@@ -105,17 +105,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
 
 // the tile's 128 KiB of dynamic LDS, granted once per kernel
 hipError_t set_gemm_lds_attrs() {
-  static bool done = false;
-  if (done) return hipSuccess;
-  const void* ks[] = {reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<0>),
-                      reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<1>),
-                      reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<2>)};
-  for (const void* k : ks) {
-    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-    if (e != hipSuccess) return e;
-  }
-  done = true;
-  return hipSuccess;
+  static std::atomic<uint64_t> done{0};
+  return once_per_device(done, [] {
+    const void* ks[] = {reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<0>),
+                        reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<1>),
+                        reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<2>)};
+    for (const void* k : ks) {
+      const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  });
 }
 
 hipError_t launch_ffn(const moe_shape_t& s, int El, const void* xe, const int32_t* offsets, const void* w1,

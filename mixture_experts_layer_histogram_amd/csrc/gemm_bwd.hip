@@ -252,16 +252,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_wgrad_bf16_kernel(
 }
 
 hipError_t set_bwd_gemm_lds_attrs() {
-  static bool done = false;
-  if (done) return hipSuccess;
-  const void* ks[] = {reinterpret_cast<const void*>(grouped_rows_bmn_kernel),
-                      reinterpret_cast<const void*>(grouped_wgrad_bf16_kernel)};
-  for (const void* k : ks) {
-    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-    if (e != hipSuccess) return e;
-  }
-  done = true;
-  return hipSuccess;
+  static std::atomic<uint64_t> done{0};
+  return once_per_device(done, [] {
+    const void* ks[] = {reinterpret_cast<const void*>(grouped_rows_bmn_kernel),
+                        reinterpret_cast<const void*>(grouped_wgrad_bf16_kernel)};
+    for (const void* k : ks) {
+      const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  });
 }
 
 hipError_t launch_rows_bmn(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, int ksplit, uint16_t* C, int K,

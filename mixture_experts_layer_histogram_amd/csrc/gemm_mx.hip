@@ -398,16 +398,16 @@ hipError_t launch_ffn_mx(const moe_shape_t& s, int El, const uint8_t* xe, const 
                          const int32_t* offsets, const uint8_t* w1, const uint8_t* w3, const uint8_t* w2,
                          const uint8_t* w1s, const uint8_t* w3s, const uint8_t* w2s, void* ye, char* ws,
                          const WsLayout& L, int cus, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
+  static std::atomic<uint64_t> attr_set{0};
+  const hipError_t ea = once_per_device(attr_set, [] {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_mx_kernel<0>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
     if (e == hipSuccess)
       e = hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_mx_kernel<1>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    return e;
+  });
+  if (ea != hipSuccess) return ea;
   const int32_t* ctrl = reinterpret_cast<const int32_t*>(ws + L.ctrl);
   const int32_t* mtb = reinterpret_cast<const int32_t*>(ws + L.mtile_base);
   uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hbuf);
@@ -423,16 +423,16 @@ hipError_t launch_ffn_mx(const moe_shape_t& s, int El, const uint8_t* xe, const 
 }
 
 hipError_t set_mx_bwd_lds_attrs() {
-  static bool done = false;
-  if (done) return hipSuccess;
-  const void* ks[] = {reinterpret_cast<const void*>(grouped_gemm_mx_kernel<1>),
-                      reinterpret_cast<const void*>(grouped_gemm_mx_kernel<2>)};
-  for (const void* k : ks) {
-    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
-    if (e != hipSuccess) return e;
-  }
-  done = true;
-  return hipSuccess;
+  static std::atomic<uint64_t> done{0};
+  return once_per_device(done, [] {
+    const void* ks[] = {reinterpret_cast<const void*>(grouped_gemm_mx_kernel<1>),
+                        reinterpret_cast<const void*>(grouped_gemm_mx_kernel<2>)};
+    for (const void* k : ks) {
+      const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  });
 }
 
 // C[s] = A[s] B_l^T in MXFP8 for the rows of every local expert: A codes [*][K] with scales

@@ -115,12 +115,16 @@ int check_w_scales(const moe_mx_scales_t* w) {
 int cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
-  static int cached[64] = {0};
-  if (dev < 64 && cached[dev]) return cached[dev];
+  static std::atomic<int> cached[64];       // zero-initialised (static storage)
+  const bool slot = dev >= 0 && dev < 64;
+  if (slot) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
   if (n < 8) n = 8;
-  if (dev < 64) cached[dev] = n;
+  if (slot) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 

@@ -380,13 +380,12 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
   A.max_mtiles = L.max_mtiles;
   A.lookahead = (A.slots_per_part >= 2 * A.cpm) ? 1 : 0;
 
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_persistent_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> attr_set{0};
+  const hipError_t ea = once_per_device(attr_set, [] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(moe_persistent_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+  });
+  if (ea != hipSuccess) return ea;
   const int words = persist_ctrl_words(L.max_mtiles, slots);
   hipLaunchKernelGGL(persist_init_kernel, dim3((words + 255) / 256), dim3(256), 0, st, pc, words);
   hipError_t e = hipGetLastError();
