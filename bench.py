@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--sample-clocks", action="store_true",
                     help="sample the GPU's gfx clocks and socket power with amd-smi during the timed steps "
                          "(use enough --steps for a few seconds) and report their means")
+    ap.add_argument("--graph", action="store_true",
+                    help="after the timed steps, capture one forward in a HIP graph and time as many replays; "
+                         "reported as 'graph' (value stays the eager figure)")
     ap.add_argument("--cold-cache", action="store_true",
                     help="after the timed steps, time as many again, each after writing a 1 GiB buffer "
                          "(evicts the 4 MB L2s and the 256 MB MALL); reported as 'cold'")
@@ -539,6 +542,31 @@ def main():
                 for j, n in enumerate(names)}
     per_step = [ev[i][0].elapsed_time(ev[i][len(names)]) for i in range(args.steps)]
     log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; stages {stage_ms}")
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            P.forward()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            P.forward()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / args.steps
+        graph = {"ms_per_step": gms, "tokens_per_s": cfg.R * cfg.T / cfg.G / (gms * 1e-3),
+                 "note": "one moe_forward captured in a HIP graph, replayed back to back"}
+        log(f"[bench] graph replay: {gms:.3f} ms/step")
     cold = None
     if args.cold_cache:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -619,6 +647,8 @@ def main():
         "pairs_per_s": N / (ms_step * 1e-3),
         "source_tokens_per_s": cfg.R * cfg.T / (ms_step * 1e-3),
     }
+    if graph:
+        result["graph"] = graph
     if cold:
         result["cold"] = cold
     if sampler:
