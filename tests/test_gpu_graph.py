@@ -66,3 +66,52 @@ def test_forward_graph_replay_equals_eager(name):
         for a, b in zip(P.y, ref_y):
             assert torch.equal(a, b), f"replay {rep} differs"
     _say(f"  4 replays bit-identical, N={P.N()}")
+
+
+@pytest.mark.parametrize("name", ["bf16", "mxfp8"])
+def test_backward_graph_replay_equals_eager(name):
+    """The whole backward (moe_backward, or moe_backward_mx after its once-per-update
+    weight preparation) captured after an eager forward; replays equal the eager call."""
+    import torch
+    from mixture_experts_layer_histogram_amd.device import DeviceProblem
+    cfg = CASES[name]
+    _say(f"[graph-bwd] {cfg.name}")
+    inp = inputs.make_inputs(cfg, seed=12)
+    P = DeviceProblem(cfg, inp)
+    P.forward()
+    dy_bits, _ = inputs.make_dy(cfg, seed=12)
+    P.alloc_backward(dy_bits)
+    mx = cfg.dtype == "mxfp8"
+    if mx:
+        P.prepare_backward_mx()
+    run = P.backward_mx if mx else P.backward
+    run()
+    assert P.status() == 0
+    torch.cuda.synchronize()
+    outs = lambda: P.dx + P.dlogits + [P.dw1, P.dw3, P.dw2]      # noqa: E731
+    bits = lambda t: t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)  # noqa: E731
+    ref = [bits(t).clone() for t in outs()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs():
+            t.fill_(7)
+        if rep == 1:
+            run()
+            torch.cuda.synchronize()
+            for t in outs():
+                t.fill_(7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert P.status() == 0
+        for a, b in zip(outs(), ref):
+            assert torch.equal(bits(a), b), f"replay {rep} differs"
+    _say("  3 replays bit-identical")
