@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--sample-clocks", action="store_true",
                     help="sample the GPU's gfx clocks and socket power with amd-smi during the timed steps "
                          "(use enough --steps for a few seconds) and report their means")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the unfused path (ye staged, separate push kernel) instead of the fused push")
     ap.add_argument("--graph", action="store_true",
                     help="after the timed steps, capture one forward in a HIP graph and time as many replays; "
                          "reported as 'graph' (value stays the eager figure)")
@@ -497,8 +499,9 @@ def main():
     P = DeviceProblem(cfg, inp, device=dev)
     stream = torch.cuda.current_stream()
 
+    warm = P.forward if (args.unfused or args.backward or args.sweep_tokens) else P.forward_fused
     for _ in range(args.warmup):
-        P.forward()
+        warm()
     torch.cuda.synchronize()
     st = P.status()
     if st != 0:
@@ -512,7 +515,15 @@ def main():
         run_sweep(args, cfg, P, stream)
         return
 
-    names = ["layout", "dispatch", "ffn", "combine"]
+    if args.unfused:
+        names = ["layout", "dispatch", "ffn", "combine"]
+        calls = [P.layout, P.dispatch, P.ffn, P.combine]
+        fwd = P.forward
+    else:
+        # the push fused into the down GEMM: "ffn" writes each result row to its recv slot
+        names = ["layout", "dispatch", "ffn", "merge"]
+        calls = [P.layout, P.dispatch, P.ffn_push, P.merge]
+        fwd = P.forward_fused
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
@@ -524,14 +535,9 @@ def main():
     for i in range(args.steps):
         e = ev[i]
         e[0].record(stream)
-        P.layout()
-        e[1].record(stream)
-        P.dispatch()
-        e[2].record(stream)
-        P.ffn()
-        e[3].record(stream)
-        P.combine()
-        e[4].record(stream)
+        for c, call in enumerate(calls):
+            call()
+            e[c + 1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     if sampler:
@@ -547,12 +553,12 @@ def main():
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
-            P.forward()
+            fwd()
         stream.wait_stream(side)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
-            P.forward()
+            fwd()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -575,14 +581,9 @@ def main():
             flush.fill_(i & 255)
             e = cev[i]
             e[0].record(stream)
-            P.layout()
-            e[1].record(stream)
-            P.dispatch()
-            e[2].record(stream)
-            P.ffn()
-            e[3].record(stream)
-            P.combine()
-            e[4].record(stream)
+            for c, call in enumerate(calls):
+                call()
+                e[c + 1].record(stream)
         torch.cuda.synchronize()
         del flush
         cs = [cev[i][0].elapsed_time(cev[i][len(names)]) for i in range(args.steps)]
@@ -634,7 +635,10 @@ def main():
         "data": "synthetic (seeded N(0,1) tokens, fan-in scaled random expert weights, router logits x@W_r)",
         "config": {"workload": cfg.name, "R": cfg.R, "T": cfg.T, "d": cfg.d, "E": cfg.E,
                    "E_local": cfg.E_local, "k": cfg.k, "F": cfg.F, "local_pairs": N, "load": load,
-                   "path": "unfused (layout, dispatch, ffn, combine+merge kernels on one stream)"},
+                   "path": ("unfused (layout, dispatch, ffn writing ye, push + merge kernels on one stream)"
+                            if args.unfused else
+                            "fused push (layout, dispatch, ffn whose down GEMM writes each row to its recv slot, "
+                            "merge; kernels on one stream)")},
         "roofline": {"bound": "mfma", "kernel": "grouped SwiGLU FFN (gate/up+SwiGLU, down GEMMs)",
                      "achieved": flops / t_ffn / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
                      "frac": flops / t_ffn / peak, "traffic": traffic},
@@ -642,7 +646,8 @@ def main():
         "step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step))},
         "stages_hbm_frac": {
             "dispatch": gather_bytes / (stage_ms["dispatch"] * 1e-3) / PEAK_HBM,
-            "combine+merge": (push_bytes + merge_bytes) / (stage_ms["combine"] * 1e-3) / PEAK_HBM,
+            **({"combine+merge": (push_bytes + merge_bytes) / (stage_ms["combine"] * 1e-3) / PEAK_HBM}
+               if args.unfused else {"merge": merge_bytes / (stage_ms["merge"] * 1e-3) / PEAK_HBM}),
         },
         "pairs_per_s": N / (ms_step * 1e-3),
         "source_tokens_per_s": cfg.R * cfg.T / (ms_step * 1e-3),

@@ -195,6 +195,38 @@ int moe_expert_ffn(const moe_shape_t* s, const moe_placement_t* p, const moe_exe
                    size_t ws_bytes, void* stream);
 
 /*
+ * moe_expert_ffn_push -- moe_expert_ffn with the push combine fused into the down GEMM's
+ *   epilogue [kucoin §02: combine is a push because the destination of every result row is
+ *   already known].  Same arithmetic as moe_expert_ffn; instead of ye[s] the down GEMM
+ *   writes each result row straight to recv[r][t][j], where (r, t) = pull_src[s] and
+ *   slot_of[r][t][j] == s.  recv rows are then bit-identical to moe_expert_ffn followed by
+ *   the push of moe_combine_push; entries of recv without a local pair are not written.
+ *   No ye buffer is needed.  A per-pair table of destination addresses is built in the
+ *   workspace first (8 bytes per pair, counted by moe_workspace_bytes).
+ * recv: R device pointers, each [T][k][d], 16-byte aligned.  Other arguments, alignment
+ *   and dtype rules as moe_expert_ffn.
+ * Errors: MOE_EINVAL for a missing pull_src, slot_of or recv entry; otherwise as
+ *   moe_expert_ffn.
+ */
+int moe_expert_ffn_push(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+                        const void* xe, const uint8_t* xe_scales, const int32_t* offsets, const void* w1,
+                        const void* w3, const void* w2, const moe_mx_scales_t* w_scales,
+                        const int32_t* pull_src, const int32_t* slot_of, void* const* recv, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/*
+ * moe_weighted_merge -- the final weighted merge alone [kucoin §03: the final weighted merge
+ *   is a step of its own]: y[r][t][:] = sum over ascending j with slot_of[r][t][j] >= 0 of
+ *   topk_w[r][t][j] * recv[r][t][j][:], fp32 accumulation, rounded once to the row dtype;
+ *   exactly 0 for a token with no local pair.  Deterministic.  Reads only the recv entries of
+ *   local pairs.  recv: R pointers [T][k][d]; y: R pointers [T][d]; both 16-byte aligned.
+ * Errors: MOE_EINVAL for a missing slot_of, topk_w or table entry; MOE_EALIGN for a
+ *   misaligned row buffer.
+ */
+int moe_weighted_merge(const moe_shape_t* s, const moe_placement_t* p, const int32_t* slot_of,
+                       const float* topk_w, void* const* recv, void* const* y, void* stream);
+
+/*
  * moe_combine_push -- push combine then the final weighted merge
  *   [kucoin §01: combine returns each result to the token's original position;
  *   kucoin §02: combine is a push since the destination is known; kucoin §03: the
@@ -223,6 +255,20 @@ int moe_forward(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t
                 void* const* recv, void* const* y,
                 int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
                 int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_forward_fused -- moe_layout, moe_dispatch_pull, moe_expert_ffn_push and
+ *   moe_weighted_merge in order on one stream: the multi-kernel path with the push fused
+ *   into the down GEMM, so no expert-output staging rows (ye) are written or read back.
+ *   recv (local-pair entries) and y are bit-identical to moe_forward's.  Arguments as
+ *   moe_forward without ye.
+ */
+int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+                      const float* const* logits, const void* const* x, const void* w1, const void* w3,
+                      const void* w2, const moe_mx_scales_t* w_scales, void* xe, uint8_t* xe_scales,
+                      void* const* recv, void* const* y, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                      int32_t* offsets, int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /*
  * moe_forward_persistent -- the whole share with dispatch, expert FFN and combine in one

@@ -50,7 +50,7 @@ enum CtrlSlot {
 constexpr int kMaxRingSlots = 65536;
 
 struct WsLayout {
-  size_t ctrl, l2g, mtile_base, chunk_base, blockhist, blockbase, pctrl, hbuf, total;
+  size_t ctrl, l2g, mtile_base, chunk_base, blockhist, blockbase, pctrl, hbuf, push_dst, total;
   int32_t nb;        // layout blocks
   int64_t max_pairs;
   int32_t max_mtiles;
@@ -80,6 +80,8 @@ inline WsLayout ws_layout(const moe_shape_t& s, int32_t E_local) {
                             ? align256(size_t(w.max_pairs) * s.F) + size_t(w.max_pairs) * (s.F / 32)
                             : size_t(w.max_pairs) * s.F * esz;
   w.hbuf = o;        o = align256(o + hbytes);
+  // per local pair: the address of its recv row (the push fused into the down GEMM)
+  w.push_dst = o;    o = align256(o + size_t(w.max_pairs) * 8);
   w.total = o;
   return w;
 }

@@ -42,6 +42,7 @@ struct TileMX {
   uint8_t* dabq;        // [rows][2 Nout] codes
   uint8_t* dabs;        // scales of the whole [nmax][2 Nout] code matrix (MXFP8 scale layout)
   int64_t row0, nmax;   // global index of the tile's first row; rows of the scale layout
+  const uint64_t* row_dst;  // MODE 1: null, or per tile row the address its output row goes to
 };
 
 __device__ __forceinline__ i32x8 ld_frag(const char* s, int row, int c0) {
@@ -318,9 +319,10 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
     const int ncols = min(kGemmBN, Nout - c0);
     for (int v = tid; v < kGemmBM * (kGemmBN / 8); v += kGemmThreads) {
       const int row = v >> 5, cv = v & 31;                   // 32 vectors of 8 bf16 per row
-      if (row < rows && cv * 8 < ncols)
-        *reinterpret_cast<u32x4*>(orow0 + size_t(row) * Nout + c0 + cv * 8) =
-            *reinterpret_cast<const u32x4*>(ot + row * kPitch + cv * 16);
+      if (row < rows && cv * 8 < ncols) {
+        uint16_t* orow = io.row_dst ? reinterpret_cast<uint16_t*>(io.row_dst[row]) : orow0 + size_t(row) * Nout;
+        *reinterpret_cast<u32x4*>(orow + c0 + cv * 8) = *reinterpret_cast<const u32x4*>(ot + row * kPitch + cv * 16);
+      }
     }
   }
   __syncthreads();     // the next tile's fills reuse the stages
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_mx_kernel(
     void* __restrict__ C, uint8_t* __restrict__ Cs, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ mtile_base, const int32_t* __restrict__ ctrl, int El, int K, int Nout,
     int64_t nmax, const uint16_t* __restrict__ DH, uint16_t* __restrict__ DAB, uint8_t* __restrict__ DABQ,
-    uint8_t* __restrict__ DABS) {
+    uint8_t* __restrict__ DABS, const uint64_t* __restrict__ RowDst) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int cols_per_tile = (MODE != 1) ? kGemmBN / 2 : kGemmBN;
   const int NT = (Nout + cols_per_tile - 1) / cols_per_tile;
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_mx_kernel(
       io.os = Cs + 4 * size_t(row0);
       io.os_plane = 4 * nmax;
     } else {
-      io.o = static_cast<uint16_t*>(C) + size_t(row0) * Nout;
+      io.o = C ? static_cast<uint16_t*>(C) + size_t(row0) * Nout : nullptr;   // null C: MODE 1 with RowDst
       io.os = nullptr;
       io.os_plane = 0;
     }
@@ -381,6 +383,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_mx_kernel(
     io.dabs = DABS;
     io.row0 = row0;
     io.nmax = nmax;
+    io.row_dst = (MODE == 1 && RowDst) ? RowDst + row0 : nullptr;
     const uint8_t* b0 = B0 + size_t(l) * Nout * K;
     const uint8_t* b1 = (MODE != 1) ? B1 + size_t(l) * Nout * K : b0;
     const uint8_t* bs0 = Bs0 + 4 * size_t(l) * Nout;
@@ -397,7 +400,7 @@ size_t mx_h_scales_offset(const WsLayout& L, const moe_shape_t& s) {
 hipError_t launch_ffn_mx(const moe_shape_t& s, int El, const uint8_t* xe, const uint8_t* xe_scales,
                          const int32_t* offsets, const uint8_t* w1, const uint8_t* w3, const uint8_t* w2,
                          const uint8_t* w1s, const uint8_t* w3s, const uint8_t* w2s, void* ye, char* ws,
-                         const WsLayout& L, int cus, hipStream_t st) {
+                         const WsLayout& L, int cus, hipStream_t st, const uint64_t* row_dst) {
   static std::atomic<uint64_t> attr_set{0};
   const hipError_t ea = once_per_device(attr_set, [] {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_mx_kernel<0>),
@@ -415,10 +418,10 @@ hipError_t launch_ffn_mx(const moe_shape_t& s, int El, const uint8_t* xe, const 
   const int grid = (cus / 8) * 8;
   hipLaunchKernelGGL(grouped_gemm_mx_kernel<0>, dim3(grid), dim3(kGemmThreads), kMxLds, st, xe, xe_scales, w1, w3,
                      w1s, w3s, static_cast<void*>(hq), hs, offsets, mtb, ctrl, El, s.d, s.F, int64_t(L.max_pairs),
-                     nullptr, nullptr, nullptr, nullptr);
+                     nullptr, nullptr, nullptr, nullptr, nullptr);
   hipLaunchKernelGGL(grouped_gemm_mx_kernel<1>, dim3(grid), dim3(kGemmThreads), kMxLds, st, hq, hs, w2, nullptr,
                      w2s, nullptr, ye, nullptr, offsets, mtb, ctrl, El, s.F, s.d, int64_t(L.max_pairs), nullptr, nullptr,
-                     nullptr, nullptr);
+                     nullptr, nullptr, row_dst);
   return hipGetLastError();
 }
 
@@ -444,7 +447,7 @@ hipError_t launch_rows_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B,
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(grouped_gemm_mx_kernel<1>, dim3((cus / 8) * 8), dim3(kGemmThreads), kMxLds, st, A, As, B, nullptr,
                      Bs, nullptr, static_cast<void*>(C), nullptr, offsets, mtb, ctrl, El, K, Nout, nmax, nullptr,
-                     nullptr, nullptr, nullptr);
+                     nullptr, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -456,7 +459,8 @@ hipError_t launch_gemm1_bwd_mx(const uint8_t* xe, const uint8_t* xes, const uint
   hipError_t e = set_mx_bwd_lds_attrs();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(grouped_gemm_mx_kernel<2>, dim3((cus / 8) * 8), dim3(kGemmThreads), kMxLds, st, xe, xes, w1, w3,
-                     w1s, w3s, static_cast<void*>(h), nullptr, offsets, mtb, ctrl, El, d, F, nmax, dh, dab, dabq, dabs);
+                     w1s, w3s, static_cast<void*>(h), nullptr, offsets, mtb, ctrl, El, d, F, nmax, dh, dab, dabq, dabs,
+                     nullptr);
   return hipGetLastError();
 }
 

@@ -53,6 +53,7 @@ struct TileIO {
   int rows;            // valid rows, 1..256
   const uint16_t* dh;  // MODE 2: incoming dh of the tile's first row ([rows][Nout] contiguous)
   uint16_t* dab;       // MODE 2: [da | db] rows of 2 * Nout from the tile's first row
+  const uint64_t* row_dst;  // MODE 1: null, or per tile row the address its output row goes to
 };
 
 template <typename P>
@@ -253,6 +254,36 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
   int lane_o = lane;
   asm volatile("" : "+v"(lane_o));
   const int r32o = lane_o & 31, hio = lane_o >> 5;
+
+  if (MODE == 1 && io.row_dst) {
+    // Fused push: every output row goes to its own destination (a recv row).  The tile is
+    // staged as bf16 in LDS ([256 rows][256 cols], 16-byte chunks XOR-swizzled by row), then
+    // written back row by row in 16-byte vectors, so each destination row receives whole
+    // 128-byte lines.  The main loop ended on a barrier, so the stages are free.
+    char* stg = smem;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int col = wn * 128 + n * 32 + r32o;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = wm * 64 + m * 32 + 8 * (e >> 2) + 4 * hio + (e & 3);
+          *reinterpret_cast<uint16_t*>(stg + row * 512 + (((col >> 3) ^ (row & 31)) << 4) + (col & 7) * 2) =
+              f32_to_bf16(acc[m][n][e]);
+        }
+      }
+    __syncthreads();
+    const int ncols = min(kGemmBN, Nout - c0);
+    for (int v = tid; v < kGemmBM * (kGemmBN / 8); v += kGemmThreads) {
+      const int row = v >> 5, cv = v & 31;                  // 32 vectors of 8 bf16 per row
+      if (row < rows && cv * 8 < ncols)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(io.row_dst[row]) + c0 + cv * 8) =
+            *reinterpret_cast<const u32x4*>(stg + row * 512 + ((cv ^ (row & 31)) << 4));
+    }
+    __syncthreads();                                        // the next tile's fills reuse the stages
+    return;
+  }
 
   if (MODE == 2) {
     // Backward epilogue, in two passes of 128 tile rows (m = 0, 1): every wave stages its

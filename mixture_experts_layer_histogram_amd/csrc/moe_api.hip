@@ -12,7 +12,9 @@ hipError_t launch_dispatch(const moe_shape_t& s, const void* const* x, const int
                            const int32_t* ctrl, int cus, hipStream_t st);
 hipError_t launch_ffn(const moe_shape_t& s, int El, const void* xe, const int32_t* offsets, const void* w1,
                       const void* w3, const void* w2, void* ye, char* ws, const WsLayout& L, int cus,
-                      hipStream_t st);
+                      hipStream_t st, const uint64_t* row_dst);
+hipError_t launch_push_dst(const moe_shape_t& s, const int32_t* pull_src, const int32_t* slot_of,
+                           void* const* recv, const int32_t* ctrl, uint64_t* push_dst, int cus, hipStream_t st);
 hipError_t launch_combine(const moe_shape_t& s, const char* ye, const int32_t* pull_src,
                           const int32_t* slot_of, const float* topk_w, void* const* recv, void* const* y,
                           const int32_t* ctrl, int cus, hipStream_t st);
@@ -23,7 +25,7 @@ hipError_t launch_dispatch_mx(const moe_shape_t& s, const void* const* x, const 
 hipError_t launch_ffn_mx(const moe_shape_t& s, int El, const uint8_t* xe, const uint8_t* xe_scales,
                          const int32_t* offsets, const uint8_t* w1, const uint8_t* w3, const uint8_t* w2,
                          const uint8_t* w1s, const uint8_t* w3s, const uint8_t* w2s, void* ye, char* ws,
-                         const WsLayout& L, int cus, hipStream_t st);
+                         const WsLayout& L, int cus, hipStream_t st, const uint64_t* row_dst);
 hipError_t launch_merge(const moe_shape_t& s, const int32_t* slot_of, const float* topk_w, void* const* recv,
                         void* const* y, int cus, hipStream_t st);
 hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x, const void* w1, const void* w3,
@@ -242,9 +244,47 @@ int moe_expert_ffn(const moe_shape_t* s, const moe_placement_t* p, const moe_exe
     return hip_rc(launch_ffn_mx(*s, p->E_local, static_cast<const uint8_t*>(xe), xe_scales, offsets,
                                 static_cast<const uint8_t*>(w1), static_cast<const uint8_t*>(w3),
                                 static_cast<const uint8_t*>(w2), w_scales->w1, w_scales->w3, w_scales->w2, ye,
-                                static_cast<char*>(ws), L, cu_count(), static_cast<hipStream_t>(stream)));
+                                static_cast<char*>(ws), L, cu_count(), static_cast<hipStream_t>(stream), nullptr));
   return hip_rc(launch_ffn(*s, p->E_local, xe, offsets, w1, w3, w2, ye, static_cast<char*>(ws), L, cu_count(),
-                           static_cast<hipStream_t>(stream)));
+                           static_cast<hipStream_t>(stream), nullptr));
+}
+
+int moe_expert_ffn_push(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex, const void* xe,
+                        const uint8_t* xe_scales, const int32_t* offsets, const void* w1, const void* w3,
+                        const void* w2, const moe_mx_scales_t* w_scales, const int32_t* pull_src,
+                        const int32_t* slot_of, void* const* recv, void* ws, size_t ws_bytes, void* stream) {
+  (void)ex;
+  int rc = check_shape(s, p);
+  if (rc) return rc;
+  if (!offsets || !pull_src || !slot_of) return MOE_EINVAL;
+  const void* bufs[] = {xe, w1, w3, w2};
+  for (const void* b : bufs)
+    if (!aligned16(b)) return b ? MOE_EALIGN : MOE_EINVAL;
+  if (s->dtype == MOE_MXFP8 && ((rc = check_scales(xe_scales)) || (rc = check_w_scales(w_scales)))) return rc;
+  if ((rc = check_ptr_table(recv, s->R))) return rc;
+  if ((rc = check_ws(s, p, ws, ws_bytes))) return rc;
+  const WsLayout L = ws_layout(*s, p->E_local);
+  char* w = static_cast<char*>(ws);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  uint64_t* dst = reinterpret_cast<uint64_t*>(w + L.push_dst);
+  const hipError_t e = launch_push_dst(*s, pull_src, slot_of, recv, reinterpret_cast<const int32_t*>(w + L.ctrl), dst,
+                                       cu_count(), st);
+  if (e != hipSuccess) return MOE_EHIP;
+  if (s->dtype == MOE_MXFP8)
+    return hip_rc(launch_ffn_mx(*s, p->E_local, static_cast<const uint8_t*>(xe), xe_scales, offsets,
+                                static_cast<const uint8_t*>(w1), static_cast<const uint8_t*>(w3),
+                                static_cast<const uint8_t*>(w2), w_scales->w1, w_scales->w3, w_scales->w2, nullptr,
+                                w, L, cu_count(), st, dst));
+  return hip_rc(launch_ffn(*s, p->E_local, xe, offsets, w1, w3, w2, nullptr, w, L, cu_count(), st, dst));
+}
+
+int moe_weighted_merge(const moe_shape_t* s, const moe_placement_t* p, const int32_t* slot_of, const float* topk_w,
+                       void* const* recv, void* const* y, void* stream) {
+  int rc = check_shape(s, p);
+  if (rc) return rc;
+  if (!slot_of || !topk_w) return MOE_EINVAL;
+  if ((rc = check_ptr_table(recv, s->R)) || (rc = check_ptr_table(y, s->R))) return rc;
+  return hip_rc(launch_merge(*s, slot_of, topk_w, recv, y, cu_count(), static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine_push(const moe_shape_t* s, const moe_placement_t* p, const void* ye, const int32_t* pull_src,
@@ -288,6 +328,35 @@ int moe_forward(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t
   if ((rc = moe_expert_ffn(s, p, ex, xe, xe_scales, offsets, w1, w3, w2, w_scales, ye, ws, ws_bytes, stream)))
     return rc;
   return moe_combine_push(s, p, ye, pull_src, slot_of, topk_w, offsets, recv, y, ws, ws_bytes, stream);
+}
+
+int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+                      const float* const* logits, const void* const* x, const void* w1, const void* w3,
+                      const void* w2, const moe_mx_scales_t* w_scales, void* xe, uint8_t* xe_scales,
+                      void* const* recv, void* const* y, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                      int32_t* offsets, int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes,
+                      void* stream) {
+  int rc = check_shape(s, p);
+  if (rc) return rc;
+  // validate every stage's arguments before launching any of them
+  if (!p->expert_to_local || !topk_idx || !topk_w || !counts || !offsets || !pull_src || !slot_of)
+    return MOE_EINVAL;
+  const void* bufs[] = {xe, w1, w3, w2};
+  for (const void* b : bufs)
+    if (!aligned16(b)) return b ? MOE_EALIGN : MOE_EINVAL;
+  if (s->dtype == MOE_MXFP8 && ((rc = check_scales(xe_scales)) || (rc = check_w_scales(w_scales)))) return rc;
+  if ((rc = check_ptr_table(logits, s->R)) || (rc = check_ptr_table(x, s->R)) ||
+      (rc = check_ptr_table(recv, s->R)) || (rc = check_ptr_table(y, s->R)))
+    return rc;
+  if ((rc = check_ws(s, p, ws, ws_bytes))) return rc;
+  if ((rc = moe_layout(s, p, ex, logits, topk_idx, topk_w, counts, offsets, pull_src, slot_of, ws, ws_bytes,
+                       stream)))
+    return rc;
+  if ((rc = moe_dispatch_pull(s, p, x, pull_src, offsets, xe, xe_scales, ws, ws_bytes, stream))) return rc;
+  if ((rc = moe_expert_ffn_push(s, p, ex, xe, xe_scales, offsets, w1, w3, w2, w_scales, pull_src, slot_of, recv, ws,
+                                ws_bytes, stream)))
+    return rc;
+  return moe_weighted_merge(s, p, slot_of, topk_w, recv, y, stream);
 }
 
 size_t moe_ring_slot_bytes(const moe_shape_t* s, const moe_exec_t* ex) {

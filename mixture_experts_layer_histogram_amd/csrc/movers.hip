@@ -79,6 +79,24 @@ __global__ __launch_bounds__(256) void combine_push_kernel(const char* __restric
   }
 }
 
+// The recv row of every local pair, for the push fused into the down GEMM's epilogue:
+// push_dst[s] = address of recv[r][t][j] with (r, t) = pull_src[s] and slot_of[r][t][j] = s.
+__global__ __launch_bounds__(256) void push_dst_kernel(const int32_t* __restrict__ pull_src,
+                                                       const int32_t* __restrict__ slot_of,
+                                                       const int32_t* __restrict__ ctrl, RankPtrs<char*> recv,
+                                                       int T, int k, int row_bytes, uint64_t* __restrict__ push_dst) {
+  const int N = ctrl[kCtrlN];
+  for (int s = blockIdx.x * 256 + threadIdx.x; s < N; s += gridDim.x * 256) {
+    const int r = pull_src[2 * int64_t(s)];
+    const int t = pull_src[2 * int64_t(s) + 1];
+    const int32_t* so = slot_of + (int64_t(r) * T + t) * k;
+    int j = 0;
+    for (int jj = 0; jj < k; ++jj)
+      if (so[jj] == s) j = jj;
+    push_dst[s] = reinterpret_cast<uint64_t>(recv.p[r] + (int64_t(t) * k + j) * row_bytes);
+  }
+}
+
 // y[r][t] = sum over ascending j with a local expert of g[r][t][j] * recv[r][t][j]
 // (g = 1 when topk_w is null: the backward's ordered sum of the pushed dX rows)
 // A wave task is one column segment (64 * VPL 16-byte vectors) of one token row.  The
@@ -193,6 +211,16 @@ hipError_t launch_push_grad(const moe_shape_t& s, const char* dX, const float* d
   for (int r = 0; r < s.R; ++r) rp.p[r] = static_cast<char*>(recv[r]);
   hipLaunchKernelGGL(combine_push_kernel, dim3(cus * kPushBlocksPerCU), dim3(256), 0, st, dX, pull_src, slot_of, ctrl, rp,
                      s.T, s.k, s.d * 2, dg, dgp);
+  return hipGetLastError();
+}
+
+hipError_t launch_push_dst(const moe_shape_t& s, const int32_t* pull_src, const int32_t* slot_of,
+                           void* const* recv, const int32_t* ctrl, uint64_t* push_dst, int cus, hipStream_t st) {
+  RankPtrs<char*> rp{};
+  for (int r = 0; r < s.R; ++r) rp.p[r] = static_cast<char*>(recv[r]);
+  const int row_bytes = s.d * (s.dtype == MOE_F32 ? 4 : 2);
+  hipLaunchKernelGGL(push_dst_kernel, dim3(cus * 2), dim3(256), 0, st, pull_src, slot_of, ctrl, rp, s.T, s.k, row_bytes,
+                     push_dst);
   return hipGetLastError();
 }
 

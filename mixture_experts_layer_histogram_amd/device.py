@@ -103,6 +103,24 @@ class DeviceProblem:
         moe.moe_combine_push(self.shape, self.placement, self.ye, self.pull_src, self.slot_of, self.topk_w,
                              self.offsets, self.recv, self.y, self.ws, stream=stream)
 
+    def ffn_push(self, stream=None):
+        """The FFN with the push fused into the down GEMM (writes recv, not ye)."""
+        w1, w3, w2 = self.weights()
+        moe.moe_expert_ffn_push(self.shape, self.placement, self.ex, self.xe, self.offsets, w1, w3, w2,
+                                self.pull_src, self.slot_of, self.recv, self.ws, stream=stream,
+                                xe_scales=self.xe_scales, w_scales=self.w_scales)
+
+    def merge(self, stream=None):
+        moe.moe_weighted_merge(self.shape, self.placement, self.slot_of, self.topk_w, self.recv, self.y,
+                               stream=stream)
+
+    def forward_fused(self, stream=None):
+        w1, w3, w2 = self.weights()
+        moe.moe_forward_fused(self.shape, self.placement, self.ex, self.logits, self.x, w1, w3, w2, self.xe,
+                              self.recv, self.y, self.topk_idx, self.topk_w, self.counts, self.offsets,
+                              self.pull_src, self.slot_of, self.ws, stream=stream, w_scales=self.w_scales,
+                              xe_scales=self.xe_scales)
+
     def forward(self, stream=None):
         w1, w3, w2 = self.weights()
         moe.moe_forward(self.shape, self.placement, self.ex, self.logits, self.x, w1, w3, w2, self.xe, self.ye,

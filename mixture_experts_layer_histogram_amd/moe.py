@@ -22,7 +22,8 @@ ERRORS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_ENOSPC", -4:
 
 # every symbol include/moe.h declares
 EXPORTS = ["moe_max_pairs", "moe_workspace_bytes", "moe_mx_quantize", "moe_layout", "moe_dispatch_pull",
-           "moe_expert_ffn", "moe_combine_push", "moe_forward", "moe_forward_persistent",
+           "moe_expert_ffn", "moe_expert_ffn_push", "moe_weighted_merge", "moe_combine_push", "moe_forward",
+           "moe_forward_fused", "moe_forward_persistent",
            "moe_ring_slot_bytes", "moe_persistent_workspace_bytes", "moe_backward_workspace_bytes",
            "moe_combine_pull_reverse", "moe_expert_ffn_backward",
            "moe_dispatch_push_reverse", "moe_backward", "moe_backward_prepare_mx", "moe_backward_mx",
@@ -76,7 +77,11 @@ def lib() -> ctypes.CDLL:
         L.moe_layout.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_dispatch_pull.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_expert_ffn.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, MS, VP, VP, SZ, VP]
+        L.moe_expert_ffn_push.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, MS, VP, VP, VP, VP, SZ, VP]
+        L.moe_weighted_merge.argtypes = [S, PL, VP, VP, VP, VP, VP]
         L.moe_combine_push.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_forward_fused.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, MS, VP, VP, VP, VP,
+                                        VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_forward.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, MS, VP, VP, VP, VP, VP,
                                   VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_forward_persistent.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, SZ, VP, VP,
@@ -103,6 +108,7 @@ def lib() -> ctypes.CDLL:
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_version.restype = ctypes.c_char_p
         for f in ("moe_mx_quantize", "moe_layout", "moe_dispatch_pull", "moe_expert_ffn", "moe_combine_push",
+                  "moe_expert_ffn_push", "moe_weighted_merge", "moe_forward_fused",
                   "moe_forward", "moe_forward_persistent", "moe_combine_pull_reverse", "moe_expert_ffn_backward", "moe_dispatch_push_reverse", "moe_backward", "moe_backward_prepare_mx",
                   "moe_backward_mx", "moe_read_status"):
             getattr(L, f).restype = I32
@@ -194,6 +200,21 @@ def moe_expert_ffn(shape, placement, ex, xe, offsets, w1, w3, w2, ye, ws, ws_byt
     return _check(rc, "moe_expert_ffn") if check else rc
 
 
+def moe_expert_ffn_push(shape, placement, ex, xe, offsets, w1, w3, w2, pull_src, slot_of, recv, ws, ws_bytes=None,
+                        stream=None, check=True, xe_scales=None, w_scales=None):
+    rc = lib().moe_expert_ffn_push(ctypes.byref(shape), ctypes.byref(placement), _ref(ex), _p(xe), _p(xe_scales),
+                                   _p(offsets), _p(w1), _p(w3), _p(w2), _ref(w_scales), _p(pull_src), _p(slot_of),
+                                   _table(recv), _p(ws), ws.numel() if ws_bytes is None else ws_bytes,
+                                   _stream(stream))
+    return _check(rc, "moe_expert_ffn_push") if check else rc
+
+
+def moe_weighted_merge(shape, placement, slot_of, topk_w, recv, y, stream=None, check=True):
+    rc = lib().moe_weighted_merge(ctypes.byref(shape), ctypes.byref(placement), _p(slot_of), _p(topk_w),
+                                  _table(recv), _table(y), _stream(stream))
+    return _check(rc, "moe_weighted_merge") if check else rc
+
+
 def moe_combine_push(shape, placement, ye, pull_src, slot_of, topk_w, offsets, recv, y, ws, ws_bytes=None,
                      stream=None, check=True):
     rc = lib().moe_combine_push(ctypes.byref(shape), ctypes.byref(placement), _p(ye), _p(pull_src),
@@ -211,6 +232,16 @@ def moe_forward(shape, placement, ex, logits, x, w1, w3, w2, xe, ye, recv, y, to
                            _p(topk_w), _p(counts), _p(offsets), _p(pull_src), _p(slot_of), _p(ws),
                            ws.numel() if ws_bytes is None else ws_bytes, _stream(stream))
     return _check(rc, "moe_forward") if check else rc
+
+
+def moe_forward_fused(shape, placement, ex, logits, x, w1, w3, w2, xe, recv, y, topk_idx, topk_w, counts,
+                      offsets, pull_src, slot_of, ws, ws_bytes=None, stream=None, check=True, w_scales=None,
+                      xe_scales=None):
+    rc = lib().moe_forward_fused(ctypes.byref(shape), ctypes.byref(placement), _ref(ex), _table(logits), _table(x),
+                                 _p(w1), _p(w3), _p(w2), _ref(w_scales), _p(xe), _p(xe_scales), _table(recv),
+                                 _table(y), _p(topk_idx), _p(topk_w), _p(counts), _p(offsets), _p(pull_src),
+                                 _p(slot_of), _p(ws), ws.numel() if ws_bytes is None else ws_bytes, _stream(stream))
+    return _check(rc, "moe_forward_fused") if check else rc
 
 
 def moe_forward_persistent(shape, placement, ex, logits, x, w1, w3, w2, ring, recv, y, topk_idx, topk_w,

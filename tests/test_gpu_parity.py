@@ -393,3 +393,59 @@ def test_forward_expert_relabelling_leaves_output_unchanged(name):
     assert n1 == n0
     for a, b in zip(y0, y1):
         np.testing.assert_array_equal(b, a)
+
+
+# --------------------------------------------------------------------------- fused push
+# moe_forward_fused / moe_expert_ffn_push: the push is fused into the down GEMM's epilogue.
+# The fused path must reproduce the unfused path (pinned to the oracle above) bit for bit:
+# recv on every local-pair entry, and y everywhere.
+def _fused_cases():
+    from tests.test_gpu_mx import MX_CASES, MX_EDGE
+    cases = dict(FORWARD_CASES)
+    cases.update({f"edge-{k}": v[0] for k, v in EDGE_CASES.items()})
+    cases.update(MX_CASES)
+    cases.update({k: v[0] for k, v in MX_EDGE.items()})
+    nevers = {f"edge-{k}": v[1] for k, v in EDGE_CASES.items()}
+    nevers.update({k: v[1] for k, v in MX_EDGE.items()})
+    return cases, nevers
+
+
+FUSED_CASES, FUSED_NEVER = _fused_cases()
+
+
+@pytest.mark.parametrize("name", list(FUSED_CASES))
+def test_forward_fused_push_equals_unfused(name):
+    torch = _torch()
+    cfg = FUSED_CASES[name]
+    _say(f"[fused] {cfg.name}")
+    inp, P = _problem(cfg, seed=3, never=FUSED_NEVER.get(name))
+    P.forward()
+    assert P.status() == 0
+    torch.cuda.synchronize()
+    so = P.slot_of.clone()
+    mask = [so[r] >= 0 for r in range(cfg.R)]
+    ref_recv = [P.recv[r][mask[r]].clone() for r in range(cfg.R)]
+    ref_y = [t.clone() for t in P.y]
+
+    def clear():
+        for r in range(cfg.R):
+            P.recv[r].fill_(float("nan"))
+            P.y[r].fill_(float("nan"))
+
+    def check(tag):
+        torch.cuda.synchronize()
+        assert P.status() == 0
+        for r in range(cfg.R):
+            assert torch.equal(P.recv[r][mask[r]], ref_recv[r]), f"{tag}: recv rank {r}"
+            assert torch.equal(P.y[r], ref_y[r]), f"{tag}: y rank {r}"
+
+    clear()
+    P.forward_fused()
+    check("moe_forward_fused")
+    clear()
+    P.layout()
+    P.dispatch()
+    P.ffn_push()
+    P.merge()
+    check("staged fused calls")
+    _say(f"  N={P.N()} bit-identical")
