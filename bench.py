@@ -519,10 +519,17 @@ def main():
         names = ["layout", "dispatch", "ffn", "combine"]
         calls = [P.layout, P.dispatch, P.ffn, P.combine]
         fwd = P.forward
-    else:
+    elif cfg.dtype == "mxfp8":
         # the push fused into the down GEMM: "ffn" writes each result row to its recv slot
+        # (the gather stays: it quantises the rows)
         names = ["layout", "dispatch", "ffn", "merge"]
         calls = [P.layout, P.dispatch, P.ffn_push, P.merge]
+        fwd = P.forward_fused
+    else:
+        # pull and push fused: "ffn" reads each pair's token row from x and writes its result
+        # row to its recv slot
+        names = ["layout", "ffn", "merge"]
+        calls = [P.layout, lambda: P.ffn_push(pull=True), P.merge]
         fwd = P.forward_fused
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -637,15 +644,18 @@ def main():
                    "E_local": cfg.E_local, "k": cfg.k, "F": cfg.F, "local_pairs": N, "load": load,
                    "path": ("unfused (layout, dispatch, ffn writing ye, push + merge kernels on one stream)"
                             if args.unfused else
-                            "fused push (layout, dispatch, ffn whose down GEMM writes each row to its recv slot, "
-                            "merge; kernels on one stream)")},
+                            ("fused push (layout, dispatch, ffn whose down GEMM writes each row to its recv slot, "
+                             "merge; kernels on one stream)" if cfg.dtype == "mxfp8" else
+                             "fused pull and push (layout, ffn whose gate/up GEMM reads each pair's token row from "
+                             "its source buffer and whose down GEMM writes each row to its recv slot, merge; "
+                             "kernels on one stream)"))},
         "roofline": {"bound": "mfma", "kernel": "grouped SwiGLU FFN (gate/up+SwiGLU, down GEMMs)",
                      "achieved": flops / t_ffn / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
                      "frac": flops / t_ffn / peak, "traffic": traffic},
         "stages_ms": stage_ms,
         "step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step))},
         "stages_hbm_frac": {
-            "dispatch": gather_bytes / (stage_ms["dispatch"] * 1e-3) / PEAK_HBM,
+            **({"dispatch": gather_bytes / (stage_ms["dispatch"] * 1e-3) / PEAK_HBM} if "dispatch" in stage_ms else {}),
             **({"combine+merge": (push_bytes + merge_bytes) / (stage_ms["combine"] * 1e-3) / PEAK_HBM}
                if args.unfused else {"merge": merge_bytes / (stage_ms["merge"] * 1e-3) / PEAK_HBM}),
         },

@@ -195,22 +195,29 @@ int moe_expert_ffn(const moe_shape_t* s, const moe_placement_t* p, const moe_exe
                    size_t ws_bytes, void* stream);
 
 /*
- * moe_expert_ffn_push -- moe_expert_ffn with the push combine fused into the down GEMM's
+ * moe_expert_ffn_push -- the expert FFN with the combine's push fused into the down GEMM's
  *   epilogue [kucoin §02: combine is a push because the destination of every result row is
- *   already known].  Same arithmetic as moe_expert_ffn; instead of ye[s] the down GEMM
- *   writes each result row straight to recv[r][t][j], where (r, t) = pull_src[s] and
- *   slot_of[r][t][j] == s.  recv rows are then bit-identical to moe_expert_ffn followed by
- *   the push of moe_combine_push; entries of recv without a local pair are not written.
- *   No ye buffer is needed.  A per-pair table of destination addresses is built in the
- *   workspace first (8 bytes per pair, counted by moe_workspace_bytes).
- * recv: R device pointers, each [T][k][d], 16-byte aligned.  Other arguments, alignment
- *   and dtype rules as moe_expert_ffn.
- * Errors: MOE_EINVAL for a missing pull_src, slot_of or recv entry; otherwise as
- *   moe_expert_ffn.
+ *   already known] and, for fp32 and bf16, optionally the pull fused into the gate/up GEMM's
+ *   operand loads [kucoin §02: the expert side reads the token rows it needs from their
+ *   source buffers].
+ *   Same arithmetic as moe_expert_ffn.  Instead of ye[s] the down GEMM writes each result
+ *   row straight to recv[r][t][j], where (r, t) = pull_src[s] and slot_of[r][t][j] == s.
+ *   With x != NULL (fp32, bf16) the gate/up GEMM reads row s straight from x[r][t] instead
+ *   of xe[s], so no dispatch (moe_dispatch_pull) is needed and xe is neither read nor
+ *   written (may be NULL); with x == NULL it reads xe as moe_dispatch_pull wrote it.
+ *   recv entries of local pairs are bit-identical to moe_dispatch_pull + moe_expert_ffn +
+ *   the push of moe_combine_push; entries without a local pair are not written.  Per-pair
+ *   address tables are built in the workspace first (16 bytes per pair, counted by
+ *   moe_workspace_bytes).
+ * x: NULL or R device pointers [T][d]; recv: R device pointers, each [T][k][d]; both
+ *   16-byte aligned.  Other arguments, alignment and dtype rules as moe_expert_ffn.
+ * Errors: MOE_EINVAL for a missing pull_src, slot_of or recv entry (or xe when x is NULL);
+ *   MOE_EUNSUP for x != NULL with MOE_MXFP8 (its rows are quantised by the gather);
+ *   otherwise as moe_expert_ffn.
  */
 int moe_expert_ffn_push(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
-                        const void* xe, const uint8_t* xe_scales, const int32_t* offsets, const void* w1,
-                        const void* w3, const void* w2, const moe_mx_scales_t* w_scales,
+                        const void* const* x, const void* xe, const uint8_t* xe_scales, const int32_t* offsets,
+                        const void* w1, const void* w3, const void* w2, const moe_mx_scales_t* w_scales,
                         const int32_t* pull_src, const int32_t* slot_of, void* const* recv, void* ws,
                         size_t ws_bytes, void* stream);
 
@@ -257,11 +264,13 @@ int moe_forward(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t
                 int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * moe_forward_fused -- moe_layout, moe_dispatch_pull, moe_expert_ffn_push and
- *   moe_weighted_merge in order on one stream: the multi-kernel path with the push fused
- *   into the down GEMM, so no expert-output staging rows (ye) are written or read back.
- *   recv (local-pair entries) and y are bit-identical to moe_forward's.  Arguments as
- *   moe_forward without ye.
+ * moe_forward_fused -- moe_layout, moe_expert_ffn_push and moe_weighted_merge in order on one
+ *   stream: for fp32 and bf16 the pull is fused into the gate/up GEMM and the push into the
+ *   down GEMM, so neither the dispatched rows (xe) nor the expert outputs (ye) are staged;
+ *   for MXFP8, moe_dispatch_pull (which quantises the rows) runs first and only the push is
+ *   fused.  recv (local-pair entries) and y are bit-identical to moe_forward's.  Arguments
+ *   as moe_forward without ye; xe and xe_scales are only used (and required) for MXFP8.
+ *   A caller that needs xe for moe_backward runs moe_dispatch_pull (or moe_forward).
  */
 int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
                       const float* const* logits, const void* const* x, const void* w1, const void* w3,

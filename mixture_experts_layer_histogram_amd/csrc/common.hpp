@@ -50,7 +50,7 @@ enum CtrlSlot {
 constexpr int kMaxRingSlots = 65536;
 
 struct WsLayout {
-  size_t ctrl, l2g, mtile_base, chunk_base, blockhist, blockbase, pctrl, hbuf, push_dst, total;
+  size_t ctrl, l2g, mtile_base, chunk_base, blockhist, blockbase, pctrl, hbuf, push_dst, pull_addr, total;
   int32_t nb;        // layout blocks
   int64_t max_pairs;
   int32_t max_mtiles;
@@ -82,6 +82,8 @@ inline WsLayout ws_layout(const moe_shape_t& s, int32_t E_local) {
   w.hbuf = o;        o = align256(o + hbytes);
   // per local pair: the address of its recv row (the push fused into the down GEMM)
   w.push_dst = o;    o = align256(o + size_t(w.max_pairs) * 8);
+  // per local pair: the address of its source token row (the pull fused into the gate/up GEMM)
+  w.pull_addr = o;   o = align256(o + size_t(w.max_pairs) * 8);
   w.total = o;
   return w;
 }

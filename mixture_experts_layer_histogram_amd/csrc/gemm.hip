@@ -19,13 +19,14 @@ namespace moe {
 // MODE 0: A = xe [*][d], B0 = W1, B1 = W3 -> C = h [*][F]   (tile = 256 rows x 128 f)
 // MODE 1: A = h [*][F],  B0 = W2          -> C = ye [*][d]  (tile = 256 rows x 256 cols), or
 //         with RowDst each row s to the address RowDst[s] instead (the push fused in)
+// RowSrc (any MODE): A row s read from the address RowSrc[s] instead (the pull fused in)
 // MODE 2: as MODE 0, with the backward epilogue: DH in, C = h, DAB = [da | db] out
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
     uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, const int32_t* __restrict__ mtile_base,
     const int32_t* __restrict__ ctrl, int El, int K, int Nout, const uint16_t* __restrict__ DH,
-    uint16_t* __restrict__ DAB, const uint64_t* __restrict__ RowDst) {
+    uint16_t* __restrict__ DAB, const uint64_t* __restrict__ RowDst, const uint64_t* __restrict__ RowSrc) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int cols_per_tile = (MODE != 1) ? kGemmBN / 2 : kGemmBN;
   const int NT = (Nout + cols_per_tile - 1) / cols_per_tile;
@@ -45,8 +46,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     const int nt = i_in / mtl, mt = i_in - nt * mtl;
     const int row0 = offsets[l] + mt * kGemmBM;
     TileIO io;
-    io.a0 = A + size_t(row0) * K;
-    io.a1 = io.a0 + size_t(128) * K;
+    io.a0 = A ? A + size_t(row0) * K : nullptr;        // null A: rows come from RowSrc
+    io.a1 = A ? io.a0 + size_t(128) * K : nullptr;
     io.a2 = io.a3 = io.a1;
     io.o0 = C ? C + size_t(row0) * Nout : nullptr;     // null C: MODE 1 with RowDst
     io.o1 = C ? io.o0 + size_t(128) * Nout : nullptr;
@@ -58,6 +59,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     io.dh = (MODE == 2) ? DH + size_t(row0) * Nout : nullptr;
     io.dab = (MODE == 2) ? DAB + size_t(row0) * 2 * Nout : nullptr;
     io.row_dst = (MODE == 1 && RowDst) ? RowDst + row0 : nullptr;
+    io.row_src = RowSrc ? RowSrc + row0 : nullptr;
     const uint16_t* b0 = B0 + size_t(l) * Nout * K;
     const uint16_t* b1 = (MODE != 1) ? B1 + size_t(l) * Nout * K : b0;
     gemm_tile<MODE>(io, b0, b1, nt * cols_per_tile, Nout, K, smem, K);
@@ -69,7 +71,8 @@ template <int MODE>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     const float* __restrict__ A, const float* __restrict__ B0, const float* __restrict__ B1,
     float* __restrict__ C, const int32_t* __restrict__ offsets, const int32_t* __restrict__ mtile_base,
-    const int32_t* __restrict__ ctrl, int El, int K, int Nout, const uint64_t* __restrict__ RowDst) {
+    const int32_t* __restrict__ ctrl, int El, int K, int Nout, const uint64_t* __restrict__ RowDst,
+    const uint64_t* __restrict__ RowSrc) {
   const int NT = (Nout + kSimtBN - 1) / kSimtBN;
   const int total = ctrl[kCtrlMTiles] * NT;
   const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = min(rg * 16 + r, rows - 1);
-        const float xv = A[size_t(row0 + row) * K + kk];
+        const float xv = RowSrc ? reinterpret_cast<const float*>(RowSrc[row0 + row])[kk] : A[size_t(row0 + row) * K + kk];
         a[r] = fmaf(xv, u0, a[r]);
         if (MODE == 0) b[r] = fmaf(xv, u1, b[r]);
       }
@@ -123,20 +126,21 @@ hipError_t set_gemm_lds_attrs() {
   });
 }
 
-// row_dst: null (GEMM2 writes ye), or per local pair the address of its output row
+// row_dst: null (GEMM2 writes ye), or per local pair the address of its output row;
+// row_src: null (GEMM1 reads xe), or per local pair the address of its source token row
 hipError_t launch_ffn(const moe_shape_t& s, int El, const void* xe, const int32_t* offsets, const void* w1,
                       const void* w3, const void* w2, void* ye, char* ws, const WsLayout& L, int cus,
-                      hipStream_t st, const uint64_t* row_dst) {
+                      hipStream_t st, const uint64_t* row_dst, const uint64_t* row_src) {
   const int32_t* ctrl = reinterpret_cast<const int32_t*>(ws + L.ctrl);
   const int32_t* mtb = reinterpret_cast<const int32_t*>(ws + L.mtile_base);
   if (s.dtype == MOE_F32) {
     float* h = reinterpret_cast<float*>(ws + L.hbuf);
     hipLaunchKernelGGL(grouped_gemm_f32_kernel<0>, dim3(cus * 4), dim3(256), 0, st,
                        static_cast<const float*>(xe), static_cast<const float*>(w1),
-                       static_cast<const float*>(w3), h, offsets, mtb, ctrl, El, s.d, s.F, nullptr);
+                       static_cast<const float*>(w3), h, offsets, mtb, ctrl, El, s.d, s.F, nullptr, row_src);
     hipLaunchKernelGGL(grouped_gemm_f32_kernel<1>, dim3(cus * 4), dim3(256), 0, st,
                        static_cast<const float*>(h), static_cast<const float*>(w2), nullptr,
-                       static_cast<float*>(ye), offsets, mtb, ctrl, El, s.F, s.d, row_dst);
+                       static_cast<float*>(ye), offsets, mtb, ctrl, El, s.F, s.d, row_dst, nullptr);
     return hipGetLastError();
   }
   hipError_t e = set_gemm_lds_attrs();
@@ -145,10 +149,10 @@ hipError_t launch_ffn(const moe_shape_t& s, int El, const void* xe, const int32_
   const int grid = (cus / 8) * 8;
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<0>, dim3(grid), dim3(kGemmThreads), kGemmLds, st,
                      static_cast<const uint16_t*>(xe), static_cast<const uint16_t*>(w1),
-                     static_cast<const uint16_t*>(w3), h, offsets, mtb, ctrl, El, s.d, s.F, nullptr, nullptr, nullptr);
+                     static_cast<const uint16_t*>(w3), h, offsets, mtb, ctrl, El, s.d, s.F, nullptr, nullptr, nullptr, row_src);
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<1>, dim3(grid), dim3(kGemmThreads), kGemmLds, st,
                      static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w2), nullptr,
-                     static_cast<uint16_t*>(ye), offsets, mtb, ctrl, El, s.F, s.d, nullptr, nullptr, row_dst);
+                     static_cast<uint16_t*>(ye), offsets, mtb, ctrl, El, s.F, s.d, nullptr, nullptr, row_dst, nullptr);
   return hipGetLastError();
 }
 
@@ -160,7 +164,7 @@ hipError_t launch_gemm1_bwd(const uint16_t* xe, const uint16_t* w1, const uint16
   hipError_t e = set_gemm_lds_attrs();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<2>, dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st, xe, w1, w3,
-                     h, offsets, mtb, ctrl, El, d, F, dh, dab, nullptr);
+                     h, offsets, mtb, ctrl, El, d, F, dh, dab, nullptr, nullptr);
   return hipGetLastError();
 }
 

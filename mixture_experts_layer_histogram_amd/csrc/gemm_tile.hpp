@@ -54,6 +54,7 @@ struct TileIO {
   const uint16_t* dh;  // MODE 2: incoming dh of the tile's first row ([rows][Nout] contiguous)
   uint16_t* dab;       // MODE 2: [da | db] rows of 2 * Nout from the tile's first row
   const uint64_t* row_dst;  // MODE 1: null, or per tile row the address its output row goes to
+  const uint64_t* row_src;  // null, or per tile row the address of its A row (replaces a0..a3)
 };
 
 template <typename P>
@@ -142,7 +143,9 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
     const int row = (wave * 4 + i) * 8 + lrow;
     const int lch = (i & 1) ? lch_odd : lch_even;
     const int rr = min(row, rows - 1);
-    ap[i] = pick4(rr >> io.blk_log2, io.a0, io.a1, io.a2, io.a3) + size_t(rr & bmask) * io.a_ld + lch * 8;
+    ap[i] = (io.row_src ? reinterpret_cast<const uint16_t*>(io.row_src[rr])
+                        : pick4(rr >> io.blk_log2, io.a0, io.a1, io.a2, io.a3) + size_t(rr & bmask) * io.a_ld) +
+            lch * 8;
     if (MODE != 1) {
       // 32-row blocks alternate W1 / W3 rows of the same 32 f values
       const int n = min(c0 + (row >> 6) * 32 + (row & 31), Nout - 1);

@@ -12,9 +12,10 @@ hipError_t launch_dispatch(const moe_shape_t& s, const void* const* x, const int
                            const int32_t* ctrl, int cus, hipStream_t st);
 hipError_t launch_ffn(const moe_shape_t& s, int El, const void* xe, const int32_t* offsets, const void* w1,
                       const void* w3, const void* w2, void* ye, char* ws, const WsLayout& L, int cus,
-                      hipStream_t st, const uint64_t* row_dst);
-hipError_t launch_push_dst(const moe_shape_t& s, const int32_t* pull_src, const int32_t* slot_of,
-                           void* const* recv, const int32_t* ctrl, uint64_t* push_dst, int cus, hipStream_t st);
+                      hipStream_t st, const uint64_t* row_dst, const uint64_t* row_src);
+hipError_t launch_pair_addr(const moe_shape_t& s, const int32_t* pull_src, const int32_t* slot_of,
+                            void* const* recv, const void* const* x, const int32_t* ctrl, uint64_t* push_dst,
+                            uint64_t* pull_addr, int cus, hipStream_t st);
 hipError_t launch_combine(const moe_shape_t& s, const char* ye, const int32_t* pull_src,
                           const int32_t* slot_of, const float* topk_w, void* const* recv, void* const* y,
                           const int32_t* ctrl, int cus, hipStream_t st);
@@ -246,20 +247,23 @@ int moe_expert_ffn(const moe_shape_t* s, const moe_placement_t* p, const moe_exe
                                 static_cast<const uint8_t*>(w2), w_scales->w1, w_scales->w3, w_scales->w2, ye,
                                 static_cast<char*>(ws), L, cu_count(), static_cast<hipStream_t>(stream), nullptr));
   return hip_rc(launch_ffn(*s, p->E_local, xe, offsets, w1, w3, w2, ye, static_cast<char*>(ws), L, cu_count(),
-                           static_cast<hipStream_t>(stream), nullptr));
+                           static_cast<hipStream_t>(stream), nullptr, nullptr));
 }
 
-int moe_expert_ffn_push(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex, const void* xe,
-                        const uint8_t* xe_scales, const int32_t* offsets, const void* w1, const void* w3,
-                        const void* w2, const moe_mx_scales_t* w_scales, const int32_t* pull_src,
-                        const int32_t* slot_of, void* const* recv, void* ws, size_t ws_bytes, void* stream) {
+int moe_expert_ffn_push(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+                        const void* const* x, const void* xe, const uint8_t* xe_scales, const int32_t* offsets,
+                        const void* w1, const void* w3, const void* w2, const moe_mx_scales_t* w_scales,
+                        const int32_t* pull_src, const int32_t* slot_of, void* const* recv, void* ws, size_t ws_bytes,
+                        void* stream) {
   (void)ex;
   int rc = check_shape(s, p);
   if (rc) return rc;
   if (!offsets || !pull_src || !slot_of) return MOE_EINVAL;
-  const void* bufs[] = {xe, w1, w3, w2};
+  if (x && s->dtype == MOE_MXFP8) return MOE_EUNSUP;      // MXFP8 rows are quantised by the gather
+  const void* bufs[] = {x ? w1 : xe, w1, w3, w2};
   for (const void* b : bufs)
     if (!aligned16(b)) return b ? MOE_EALIGN : MOE_EINVAL;
+  if (x && (rc = check_ptr_table(x, s->R))) return rc;
   if (s->dtype == MOE_MXFP8 && ((rc = check_scales(xe_scales)) || (rc = check_w_scales(w_scales)))) return rc;
   if ((rc = check_ptr_table(recv, s->R))) return rc;
   if ((rc = check_ws(s, p, ws, ws_bytes))) return rc;
@@ -267,15 +271,17 @@ int moe_expert_ffn_push(const moe_shape_t* s, const moe_placement_t* p, const mo
   char* w = static_cast<char*>(ws);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   uint64_t* dst = reinterpret_cast<uint64_t*>(w + L.push_dst);
-  const hipError_t e = launch_push_dst(*s, pull_src, slot_of, recv, reinterpret_cast<const int32_t*>(w + L.ctrl), dst,
-                                       cu_count(), st);
+  uint64_t* src = x ? reinterpret_cast<uint64_t*>(w + L.pull_addr) : nullptr;
+  const hipError_t e = launch_pair_addr(*s, pull_src, slot_of, recv, x, reinterpret_cast<const int32_t*>(w + L.ctrl),
+                                        dst, src, cu_count(), st);
   if (e != hipSuccess) return MOE_EHIP;
   if (s->dtype == MOE_MXFP8)
     return hip_rc(launch_ffn_mx(*s, p->E_local, static_cast<const uint8_t*>(xe), xe_scales, offsets,
                                 static_cast<const uint8_t*>(w1), static_cast<const uint8_t*>(w3),
                                 static_cast<const uint8_t*>(w2), w_scales->w1, w_scales->w3, w_scales->w2, nullptr,
                                 w, L, cu_count(), st, dst));
-  return hip_rc(launch_ffn(*s, p->E_local, xe, offsets, w1, w3, w2, nullptr, w, L, cu_count(), st, dst));
+  return hip_rc(launch_ffn(*s, p->E_local, x ? nullptr : xe, offsets, w1, w3, w2, nullptr, w, L, cu_count(), st, dst,
+                           src));
 }
 
 int moe_weighted_merge(const moe_shape_t* s, const moe_placement_t* p, const int32_t* slot_of, const float* topk_w,
@@ -341,10 +347,11 @@ int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_
   // validate every stage's arguments before launching any of them
   if (!p->expert_to_local || !topk_idx || !topk_w || !counts || !offsets || !pull_src || !slot_of)
     return MOE_EINVAL;
-  const void* bufs[] = {xe, w1, w3, w2};
+  const bool mx = s->dtype == MOE_MXFP8;      // only MXFP8 stages its rows (the gather quantises them)
+  const void* bufs[] = {mx ? xe : w1, w1, w3, w2};
   for (const void* b : bufs)
     if (!aligned16(b)) return b ? MOE_EALIGN : MOE_EINVAL;
-  if (s->dtype == MOE_MXFP8 && ((rc = check_scales(xe_scales)) || (rc = check_w_scales(w_scales)))) return rc;
+  if (mx && ((rc = check_scales(xe_scales)) || (rc = check_w_scales(w_scales)))) return rc;
   if ((rc = check_ptr_table(logits, s->R)) || (rc = check_ptr_table(x, s->R)) ||
       (rc = check_ptr_table(recv, s->R)) || (rc = check_ptr_table(y, s->R)))
     return rc;
@@ -352,9 +359,9 @@ int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_
   if ((rc = moe_layout(s, p, ex, logits, topk_idx, topk_w, counts, offsets, pull_src, slot_of, ws, ws_bytes,
                        stream)))
     return rc;
-  if ((rc = moe_dispatch_pull(s, p, x, pull_src, offsets, xe, xe_scales, ws, ws_bytes, stream))) return rc;
-  if ((rc = moe_expert_ffn_push(s, p, ex, xe, xe_scales, offsets, w1, w3, w2, w_scales, pull_src, slot_of, recv, ws,
-                                ws_bytes, stream)))
+  if (mx && (rc = moe_dispatch_pull(s, p, x, pull_src, offsets, xe, xe_scales, ws, ws_bytes, stream))) return rc;
+  if ((rc = moe_expert_ffn_push(s, p, ex, mx ? nullptr : x, xe, xe_scales, offsets, w1, w3, w2, w_scales, pull_src,
+                                slot_of, recv, ws, ws_bytes, stream)))
     return rc;
   return moe_weighted_merge(s, p, slot_of, topk_w, recv, y, stream);
 }

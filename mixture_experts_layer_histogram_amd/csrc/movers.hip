@@ -79,12 +79,16 @@ __global__ __launch_bounds__(256) void combine_push_kernel(const char* __restric
   }
 }
 
-// The recv row of every local pair, for the push fused into the down GEMM's epilogue:
-// push_dst[s] = address of recv[r][t][j] with (r, t) = pull_src[s] and slot_of[r][t][j] = s.
-__global__ __launch_bounds__(256) void push_dst_kernel(const int32_t* __restrict__ pull_src,
-                                                       const int32_t* __restrict__ slot_of,
-                                                       const int32_t* __restrict__ ctrl, RankPtrs<char*> recv,
-                                                       int T, int k, int row_bytes, uint64_t* __restrict__ push_dst) {
+// Per-pair address tables for the fused FFN: push_dst[s] = address of recv[r][t][j] (the
+// push fused into the down GEMM), and, when pull_addr is not null, pull_addr[s] = address of
+// x_r[t] (the pull fused into the gate/up GEMM), with (r, t) = pull_src[s] and
+// slot_of[r][t][j] = s.
+__global__ __launch_bounds__(256) void pair_addr_kernel(const int32_t* __restrict__ pull_src,
+                                                        const int32_t* __restrict__ slot_of,
+                                                        const int32_t* __restrict__ ctrl, RankPtrs<char*> recv,
+                                                        RankPtrs<const char*> x, int T, int k, int row_bytes,
+                                                        uint64_t* __restrict__ push_dst,
+                                                        uint64_t* __restrict__ pull_addr) {
   const int N = ctrl[kCtrlN];
   for (int s = blockIdx.x * 256 + threadIdx.x; s < N; s += gridDim.x * 256) {
     const int r = pull_src[2 * int64_t(s)];
@@ -94,6 +98,7 @@ __global__ __launch_bounds__(256) void push_dst_kernel(const int32_t* __restrict
     for (int jj = 0; jj < k; ++jj)
       if (so[jj] == s) j = jj;
     push_dst[s] = reinterpret_cast<uint64_t>(recv.p[r] + (int64_t(t) * k + j) * row_bytes);
+    if (pull_addr) pull_addr[s] = reinterpret_cast<uint64_t>(x.p[r] + int64_t(t) * row_bytes);
   }
 }
 
@@ -214,13 +219,19 @@ hipError_t launch_push_grad(const moe_shape_t& s, const char* dX, const float* d
   return hipGetLastError();
 }
 
-hipError_t launch_push_dst(const moe_shape_t& s, const int32_t* pull_src, const int32_t* slot_of,
-                           void* const* recv, const int32_t* ctrl, uint64_t* push_dst, int cus, hipStream_t st) {
+// x: null (no pull table), or the R source buffers
+hipError_t launch_pair_addr(const moe_shape_t& s, const int32_t* pull_src, const int32_t* slot_of,
+                            void* const* recv, const void* const* x, const int32_t* ctrl, uint64_t* push_dst,
+                            uint64_t* pull_addr, int cus, hipStream_t st) {
   RankPtrs<char*> rp{};
-  for (int r = 0; r < s.R; ++r) rp.p[r] = static_cast<char*>(recv[r]);
+  RankPtrs<const char*> xp{};
+  for (int r = 0; r < s.R; ++r) {
+    rp.p[r] = static_cast<char*>(recv[r]);
+    if (x) xp.p[r] = static_cast<const char*>(x[r]);
+  }
   const int row_bytes = s.d * (s.dtype == MOE_F32 ? 4 : 2);
-  hipLaunchKernelGGL(push_dst_kernel, dim3(cus * 2), dim3(256), 0, st, pull_src, slot_of, ctrl, rp, s.T, s.k, row_bytes,
-                     push_dst);
+  hipLaunchKernelGGL(pair_addr_kernel, dim3(cus * 2), dim3(256), 0, st, pull_src, slot_of, ctrl, rp, xp, s.T, s.k,
+                     row_bytes, push_dst, x ? pull_addr : nullptr);
   return hipGetLastError();
 }
 

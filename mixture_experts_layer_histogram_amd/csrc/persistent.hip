@@ -305,6 +305,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
       io.blk_log2 = A.blk_log2;
       io.rows = rows;
       io.row_dst = nullptr;
+      io.row_src = nullptr;
       if (j < NT1) {
         io.a0 = reinterpret_cast<const uint16_t*>(s0);
         io.a1 = reinterpret_cast<const uint16_t*>(s1);

@@ -103,12 +103,13 @@ class DeviceProblem:
         moe.moe_combine_push(self.shape, self.placement, self.ye, self.pull_src, self.slot_of, self.topk_w,
                              self.offsets, self.recv, self.y, self.ws, stream=stream)
 
-    def ffn_push(self, stream=None):
-        """The FFN with the push fused into the down GEMM (writes recv, not ye)."""
+    def ffn_push(self, stream=None, pull=False):
+        """The FFN with the push fused into the down GEMM (writes recv, not ye); with pull=True
+        (fp32, bf16) the gate/up GEMM also reads its rows straight from x (no xe)."""
         w1, w3, w2 = self.weights()
         moe.moe_expert_ffn_push(self.shape, self.placement, self.ex, self.xe, self.offsets, w1, w3, w2,
                                 self.pull_src, self.slot_of, self.recv, self.ws, stream=stream,
-                                xe_scales=self.xe_scales, w_scales=self.w_scales)
+                                xe_scales=self.xe_scales, w_scales=self.w_scales, x=self.x if pull else None)
 
     def merge(self, stream=None):
         moe.moe_weighted_merge(self.shape, self.placement, self.slot_of, self.topk_w, self.recv, self.y,

@@ -77,7 +77,7 @@ def lib() -> ctypes.CDLL:
         L.moe_layout.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_dispatch_pull.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_expert_ffn.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, MS, VP, VP, SZ, VP]
-        L.moe_expert_ffn_push.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, MS, VP, VP, VP, VP, SZ, VP]
+        L.moe_expert_ffn_push.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, VP, MS, VP, VP, VP, VP, SZ, VP]
         L.moe_weighted_merge.argtypes = [S, PL, VP, VP, VP, VP, VP]
         L.moe_combine_push.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_forward_fused.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, MS, VP, VP, VP, VP,
@@ -201,8 +201,9 @@ def moe_expert_ffn(shape, placement, ex, xe, offsets, w1, w3, w2, ye, ws, ws_byt
 
 
 def moe_expert_ffn_push(shape, placement, ex, xe, offsets, w1, w3, w2, pull_src, slot_of, recv, ws, ws_bytes=None,
-                        stream=None, check=True, xe_scales=None, w_scales=None):
-    rc = lib().moe_expert_ffn_push(ctypes.byref(shape), ctypes.byref(placement), _ref(ex), _p(xe), _p(xe_scales),
+                        stream=None, check=True, xe_scales=None, w_scales=None, x=None):
+    rc = lib().moe_expert_ffn_push(ctypes.byref(shape), ctypes.byref(placement), _ref(ex), _table(x), _p(xe),
+                                   _p(xe_scales),
                                    _p(offsets), _p(w1), _p(w3), _p(w2), _ref(w_scales), _p(pull_src), _p(slot_of),
                                    _table(recv), _p(ws), ws.numel() if ws_bytes is None else ws_bytes,
                                    _stream(stream))

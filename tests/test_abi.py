@@ -335,14 +335,18 @@ def test_fused_push_entries_reject_bad_arguments_before_launch():
     tabp = ctypes.cast(tab, ctypes.c_void_p)
     big = 1 << 40
     # moe_expert_ffn_push: missing pull_src, slot_of or recv table; misaligned recv row; small workspace
-    args = lambda pull, so, rv, ws_bytes: (ctypes.byref(s), ctypes.byref(p), None, FAKE, None, FAKE, FAKE, FAKE,  # noqa: E731
-                                           FAKE, None, pull, so, rv, FAKE, ws_bytes, None)
+    args = lambda pull, so, rv, ws_bytes, x=None: (ctypes.byref(s), ctypes.byref(p), None, x, FAKE, None, FAKE,  # noqa: E731
+                                                   FAKE, FAKE, FAKE, None, pull, so, rv, FAKE, ws_bytes, None)
     assert L.moe_expert_ffn_push(*args(None, FAKE, tabp, big)) == -1
     assert L.moe_expert_ffn_push(*args(FAKE, None, tabp, big)) == -1
     assert L.moe_expert_ffn_push(*args(FAKE, FAKE, None, big)) == -1
     tab3 = (ctypes.c_void_p * 8)(*([FAKE] * 7 + [FAKE + 4]))
     assert L.moe_expert_ffn_push(*args(FAKE, FAKE, ctypes.cast(tab3, ctypes.c_void_p), big)) == -2
     assert L.moe_expert_ffn_push(*args(FAKE, FAKE, tabp, 1024)) == -3
+    # the fused pull: a null or misaligned x entry
+    tab2 = (ctypes.c_void_p * 8)(*([FAKE] * 7 + [None]))
+    assert L.moe_expert_ffn_push(*args(FAKE, FAKE, tabp, big, ctypes.cast(tab2, ctypes.c_void_p))) == -1
+    assert L.moe_expert_ffn_push(*args(FAKE, FAKE, tabp, big, ctypes.cast(tab3, ctypes.c_void_p))) == -2
     # moe_weighted_merge: missing topk_w, missing y table
     assert L.moe_weighted_merge(ctypes.byref(s), ctypes.byref(p), FAKE, None, tabp, tabp, None) == -1
     assert L.moe_weighted_merge(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, tabp, None, None) == -1
@@ -352,5 +356,9 @@ def test_fused_push_entries_reject_bad_arguments_before_launch():
     assert rc == -1
     # MXFP8 without scales
     smx = moe.Shape(8, 4096, 7168, 256, 8, 2048, moe.MOE_MXFP8)
-    assert L.moe_expert_ffn_push(ctypes.byref(smx), ctypes.byref(p), None, FAKE, None, FAKE, FAKE, FAKE, FAKE, None,
-                                 FAKE, FAKE, tabp, FAKE, big, None) == -1
+    assert L.moe_expert_ffn_push(ctypes.byref(smx), ctypes.byref(p), None, None, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                 None, FAKE, FAKE, tabp, FAKE, big, None) == -1
+    # MXFP8 cannot fuse the pull (its rows are quantised by the gather)
+    sc = moe.MXScales(FAKE, FAKE, FAKE)
+    assert L.moe_expert_ffn_push(ctypes.byref(smx), ctypes.byref(p), None, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 ctypes.byref(sc), FAKE, FAKE, tabp, FAKE, big, None) == -6

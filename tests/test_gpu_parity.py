@@ -396,7 +396,8 @@ def test_forward_expert_relabelling_leaves_output_unchanged(name):
 
 
 # --------------------------------------------------------------------------- fused push
-# moe_forward_fused / moe_expert_ffn_push: the push is fused into the down GEMM's epilogue.
+# moe_forward_fused / moe_expert_ffn_push: the push is fused into the down GEMM's epilogue
+# and (fp32, bf16) the pull into the gate/up GEMM's row loads.
 # The fused path must reproduce the unfused path (pinned to the oracle above) bit for bit:
 # recv on every local-pair entry, and y everywhere.
 def _fused_cases():
@@ -447,5 +448,12 @@ def test_forward_fused_push_equals_unfused(name):
     P.dispatch()
     P.ffn_push()
     P.merge()
-    check("staged fused calls")
+    check("staged calls, push fused")
+    if cfg.dtype != "mxfp8":
+        clear()
+        P.xe.fill_(0)                     # the fused pull must not read xe
+        P.layout()
+        P.ffn_push(pull=True)
+        P.merge()
+        check("staged calls, pull and push fused")
     _say(f"  N={P.N()} bit-identical")
