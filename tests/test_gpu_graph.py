@@ -27,15 +27,17 @@ def _say(msg):
     sys.stdout.flush()
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["unfused", "fused"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_forward_graph_replay_equals_eager(name):
+def test_forward_graph_replay_equals_eager(name, fused):
     import torch
     from mixture_experts_layer_histogram_amd.device import DeviceProblem
     cfg = CASES[name]
-    _say(f"[graph] {cfg.name}")
+    _say(f"[graph] {cfg.name} {'fused' if fused else 'unfused'}")
     inp = inputs.make_inputs(cfg, seed=11)
     P = DeviceProblem(cfg, inp)
-    P.forward()
+    fwd = P.forward_fused if fused else P.forward
+    fwd()
     assert P.status() == 0
     torch.cuda.synchronize()
     ref_y = [t.clone() for t in P.y]
@@ -43,19 +45,19 @@ def test_forward_graph_replay_equals_eager(name):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        P.forward()                      # warm-up on the capture stream
+        fwd()                            # warm-up on the capture stream
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
-        P.forward()
+        fwd()
     torch.cuda.synchronize()
     for rep in range(4):
         for t in P.y:
             t.fill_(float("nan"))
         P.slot_of.fill_(-7)
         if rep == 2:                     # eager work between replays
-            P.forward()
+            fwd()
             torch.cuda.synchronize()
             for t in P.y:
                 t.fill_(float("nan"))
