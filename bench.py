@@ -445,13 +445,14 @@ def run_sweep(args, cfg, P, stream):
     sized for T tokens per rank; each point lowers the shape's T in place (every call reads
     the first T rows of each rank's token and logit buffers) and times `args.steps` steps."""
     import torch
+    fwd = P.forward if args.unfused else P.forward_fused
     T_full = P.shape.T
     for t in [int(v) for v in args.sweep_tokens.split(",")]:
         if not 1 <= t <= T_full:
             raise SystemExit(f"--sweep-tokens: {t} outside 1..{T_full}")
         P.shape.T = t
         for _ in range(args.warmup):
-            P.forward()
+            fwd()
         torch.cuda.synchronize()
         if P.status() != 0:
             raise SystemExit(f"device status {P.status()} at T={t}")
@@ -460,7 +461,7 @@ def run_sweep(args, cfg, P, stream):
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
-            P.forward()
+            fwd()
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
@@ -469,7 +470,8 @@ def run_sweep(args, cfg, P, stream):
         line = {"metric": "MoE layer fwd ms per call vs tokens per call", "tokens_per_rank": t,
                 "source_tokens": cfg.R * t, "local_pairs": n, "ms_per_call": ms,
                 "us_per_source_token": ms * 1e3 / (cfg.R * t), "gemm1_tiles": tiles1,
-                "gemm1_waves": tiles1 / 256.0, "workload": cfg.name}
+                "gemm1_waves": tiles1 / 256.0, "workload": cfg.name,
+                "path": "unfused" if args.unfused else "fused pull and push"}
         print(json.dumps(line), flush=True)
         log(f"[sweep] T={t}: {ms:.3f} ms, N={n}, GEMM1 tiles {tiles1} ({tiles1 / 256:.2f} waves)")
     P.shape.T = T_full
