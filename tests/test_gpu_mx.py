@@ -293,3 +293,15 @@ def test_mx_forward_full_dsv3_sampled():
     assert (P.y[zr][zt].float().cpu().numpy() == 0).all()
     _say(f"  N={lay['N']} sampled vs Oracle-Q: row={worst:.3e} fro={fro:.3e}")
     assert worst <= TOL_Q_ROW and fro <= TOL_Q_FRO
+    # the launch configuration the bench times (push fused into the down GEMM): bit for bit
+    # the same y as the unfused path just checked
+    torch = _torch()
+    y_ref = [t.clone() for t in P.y]
+    for t in P.y:
+        t.fill_(float("nan"))
+    P.forward_fused()
+    assert P.status() == 0
+    torch.cuda.synchronize()
+    for a, b in zip(P.y, y_ref):
+        assert torch.equal(a, b)
+    _say("  fused push: y bit-identical")

@@ -298,6 +298,17 @@ def test_forward_full_dsv3_sampled():
     assert (P.y[zr][zt].float().cpu().numpy() == 0).all()
     _say(f"  N={lay['N']} sampled y_rel={worst:.3e}")
     assert worst <= TOL["bf16"]
+    # the launch configuration the bench times (pull and push fused into the GEMMs): bit for
+    # bit the same y as the unfused path just checked
+    y_ref = [t.clone() for t in P.y]
+    for t in P.y:
+        t.fill_(float("nan"))
+    P.forward_fused()
+    assert P.status() == 0
+    torch.cuda.synchronize()
+    for a, b in zip(P.y, y_ref):
+        assert torch.equal(a, b)
+    _say("  fused pull and push: y bit-identical")
 
 
 # --------------------------------------------------------------------------- metamorphic
