@@ -116,6 +116,48 @@ __device__ __forceinline__ uint32_t lds_addr(const char* q) {
         "=&v"(N.b1), "=&v"(N.b2), "=&v"(N.b3)                                                             \
       : "v"(C.a0), "v"(C.b0), "v"(C.b1), "v"(C.b2), "v"(C.b3), "v"(AA), "v"(BA))
 
+// The same two sub-steps with the MFMA operands swapped (B block first): each accumulator
+// then holds the transposed 32 x 32 block, so a lane owns one output row and 4
+// consecutive columns per group of 4 values (the down GEMM's epilogue stores 8 bytes at a
+// time).  Every output element is the same dot product over the same K values.
+#define MOE_MFMA_SUBSTEP_READ_T(ACC, C, N, AA, BA)                                                          \
+  asm volatile(                                                                                           \
+      "v_mfma_f32_32x32x16_bf16 %0, %16, %14, %0\n\t"                                                     \
+      "ds_read_b128 %8, %20\n\t"                                                                          \
+      "v_mfma_f32_32x32x16_bf16 %1, %17, %14, %1\n\t"                                                     \
+      "ds_read_b128 %9, %20 offset:4096\n\t"                                                              \
+      "v_mfma_f32_32x32x16_bf16 %2, %18, %14, %2\n\t"                                                     \
+      "ds_read_b128 %10, %21\n\t"                                                                         \
+      "v_mfma_f32_32x32x16_bf16 %3, %19, %14, %3\n\t"                                                     \
+      "ds_read_b128 %11, %21 offset:4096\n\t"                                                             \
+      "v_mfma_f32_32x32x16_bf16 %4, %16, %15, %4\n\t"                                                     \
+      "ds_read_b128 %12, %21 offset:8192\n\t"                                                             \
+      "v_mfma_f32_32x32x16_bf16 %5, %17, %15, %5\n\t"                                                     \
+      "ds_read_b128 %13, %21 offset:12288\n\t"                                                            \
+      "v_mfma_f32_32x32x16_bf16 %6, %18, %15, %6\n\t"                                                     \
+      "v_mfma_f32_32x32x16_bf16 %7, %19, %15, %7\n\t"                                                     \
+      "s_waitcnt lgkmcnt(0)"                                                                              \
+      : "+v"(ACC[0][0]), "+v"(ACC[0][1]), "+v"(ACC[0][2]), "+v"(ACC[0][3]), "+v"(ACC[1][0]),              \
+        "+v"(ACC[1][1]), "+v"(ACC[1][2]), "+v"(ACC[1][3]), "=&v"(N.a0), "=&v"(N.a1), "=&v"(N.b0),          \
+        "=&v"(N.b1), "=&v"(N.b2), "=&v"(N.b3)                                                             \
+      : "v"(C.a0), "v"(C.a1), "v"(C.b0), "v"(C.b1), "v"(C.b2), "v"(C.b3), "v"(AA), "v"(BA))
+
+#define MOE_MFMA_SUBSTEP_READ_M1_T(ACC, C, N, AA, BA)                                                       \
+  asm volatile(                                                                                           \
+      "v_mfma_f32_32x32x16_bf16 %0, %10, %9, %0\n\t"                                                      \
+      "ds_read_b128 %4, %14\n\t"                                                                          \
+      "v_mfma_f32_32x32x16_bf16 %1, %11, %9, %1\n\t"                                                      \
+      "ds_read_b128 %5, %15\n\t"                                                                          \
+      "ds_read_b128 %6, %15 offset:4096\n\t"                                                              \
+      "v_mfma_f32_32x32x16_bf16 %2, %12, %9, %2\n\t"                                                      \
+      "ds_read_b128 %7, %15 offset:8192\n\t"                                                              \
+      "ds_read_b128 %8, %15 offset:12288\n\t"                                                             \
+      "v_mfma_f32_32x32x16_bf16 %3, %13, %9, %3\n\t"                                                      \
+      "s_waitcnt lgkmcnt(0)"                                                                              \
+      : "+v"(ACC[0][0]), "+v"(ACC[0][1]), "+v"(ACC[0][2]), "+v"(ACC[0][3]), "=&v"(N.a0), "=&v"(N.b0),     \
+        "=&v"(N.b1), "=&v"(N.b2), "=&v"(N.b3)                                                             \
+      : "v"(C.a0), "v"(C.b0), "v"(C.b1), "v"(C.b2), "v"(C.b3), "v"(AA), "v"(BA))
+
 // b0/b1: this expert's weight matrices ([Nout][K], row stride b_ld); c0: first output
 // column of the tile.
 template <int MODE>
@@ -212,11 +254,13 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
     constexpr int MV = decltype(mvc)::value;
     if constexpr (MV == 2) {
       Frags nxt;
-      MOE_MFMA_SUBSTEP_READ(acc, cur, nxt, aa, ba);
+      if constexpr (MODE == 1) MOE_MFMA_SUBSTEP_READ_T(acc, cur, nxt, aa, ba);
+      else MOE_MFMA_SUBSTEP_READ(acc, cur, nxt, aa, ba);
       cur = nxt;
     } else if constexpr (MV == 1) {
       Frags nxt;
-      MOE_MFMA_SUBSTEP_READ_M1(acc, cur, nxt, aa, ba);
+      if constexpr (MODE == 1) MOE_MFMA_SUBSTEP_READ_M1_T(acc, cur, nxt, aa, ba);
+      else MOE_MFMA_SUBSTEP_READ_M1(acc, cur, nxt, aa, ba);
       cur.a0 = nxt.a0;
       cur.b0 = nxt.b0;
       cur.b1 = nxt.b1;
@@ -264,18 +308,21 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
     // written back row by row in 16-byte vectors, so each destination row receives whole
     // 128-byte lines.  The main loop ended on a barrier, so the stages are free.
     char* stg = smem;
+    // (transposed blocks: lane owns row r32 and columns 8 j + 4 hi + 0..3 of each 32 x 32 block)
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < 2; ++m) {
+      const int row = wm * 64 + m * 32 + r32o;
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int col = wn * 128 + n * 32 + r32o;
+      for (int n = 0; n < 4; ++n)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = wm * 64 + m * 32 + 8 * (e >> 2) + 4 * hio + (e & 3);
-          *reinterpret_cast<uint16_t*>(stg + row * 512 + (((col >> 3) ^ (row & 31)) << 4) + (col & 7) * 2) =
-              f32_to_bf16(acc[m][n][e]);
+        for (int j = 0; j < 4; ++j) {
+          const int col = wn * 128 + n * 32 + 8 * j + 4 * hio;
+          uint2 v;
+          v.x = pack_bf16x2(acc[m][n][4 * j], acc[m][n][4 * j + 1]);
+          v.y = pack_bf16x2(acc[m][n][4 * j + 2], acc[m][n][4 * j + 3]);
+          *reinterpret_cast<uint2*>(stg + row * 512 + (((col >> 3) ^ (row & 31)) << 4) + (col & 7) * 2) = v;
         }
-      }
+    }
     __syncthreads();
     const int ncols = min(kGemmBN, Nout - c0);
     for (int v = tid; v < kGemmBM * (kGemmBN / 8); v += kGemmThreads) {
@@ -362,16 +409,21 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
           }
         }
       }
-    } else {
+    } else if (rb + r32o < rows) {
+      // transposed blocks: lane owns row r32 and columns 8 j + 4 hi + 0..3 of each block
+      uint16_t* prow = orow + size_t(r32o) * io.o_ld;
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int col = c0 + wn * 128 + n * 32 + r32o;
+      for (int n = 0; n < 4; ++n)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = 8 * (e >> 2) + 4 * hio + (e & 3);
-          if (rb + row < rows && col < Nout) orow[size_t(row) * io.o_ld + col] = f32_to_bf16(acc[m][n][e]);
+        for (int j = 0; j < 4; ++j) {
+          const int col = c0 + wn * 128 + n * 32 + 8 * j + 4 * hio;
+          if (col < Nout) {
+            uint2 v;
+            v.x = pack_bf16x2(acc[m][n][4 * j], acc[m][n][4 * j + 1]);
+            v.y = pack_bf16x2(acc[m][n][4 * j + 2], acc[m][n][4 * j + 3]);
+            *reinterpret_cast<uint2*>(prow + col) = v;
+          }
         }
-      }
     }
   }
 }
