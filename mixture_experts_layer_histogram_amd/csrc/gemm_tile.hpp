@@ -118,8 +118,9 @@ __device__ __forceinline__ uint32_t lds_addr(const char* q) {
 
 // The same two sub-steps with the MFMA operands swapped (B block first): each accumulator
 // then holds the transposed 32 x 32 block, so a lane owns one output row and 4
-// consecutive columns per group of 4 values (the down GEMM's epilogue stores 8 bytes at a
-// time).  Every output element is the same dot product over the same K values.
+// consecutive columns per group of 4 values (the forward epilogues store 8 bytes at a
+// time; the backward's GEMM1, MODE 2, keeps the original orientation).  Every output
+// element is the same dot product over the same K values.
 #define MOE_MFMA_SUBSTEP_READ_T(ACC, C, N, AA, BA)                                                          \
   asm volatile(                                                                                           \
       "v_mfma_f32_32x32x16_bf16 %0, %16, %14, %0\n\t"                                                     \
@@ -254,12 +255,12 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
     constexpr int MV = decltype(mvc)::value;
     if constexpr (MV == 2) {
       Frags nxt;
-      if constexpr (MODE == 1) MOE_MFMA_SUBSTEP_READ_T(acc, cur, nxt, aa, ba);
+      if constexpr (MODE <= 1) MOE_MFMA_SUBSTEP_READ_T(acc, cur, nxt, aa, ba);
       else MOE_MFMA_SUBSTEP_READ(acc, cur, nxt, aa, ba);
       cur = nxt;
     } else if constexpr (MV == 1) {
       Frags nxt;
-      if constexpr (MODE == 1) MOE_MFMA_SUBSTEP_READ_M1_T(acc, cur, nxt, aa, ba);
+      if constexpr (MODE <= 1) MOE_MFMA_SUBSTEP_READ_M1_T(acc, cur, nxt, aa, ba);
       else MOE_MFMA_SUBSTEP_READ_M1(acc, cur, nxt, aa, ba);
       cur.a0 = nxt.a0;
       cur.b0 = nxt.b0;
@@ -397,17 +398,24 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
     const int rb = wm * 64 + m * 32;                     // 32-row block, inside one row block
     uint16_t* orow = pick4(rb >> io.blk_log2, io.o0, io.o1, io.o2, io.o3) + size_t(rb & bmask) * io.o_ld;
     if (MODE == 0) {
+      // transposed blocks: lane owns row r32 and f = 8 j + 4 hi + 0..3 of each 32-f block
+      if (rb + r32o < rows) {
+        uint16_t* prow = orow + size_t(r32o) * io.o_ld;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int f = c0 + (wn * 2 + q) * 32 + r32o;
+        for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = 8 * (e >> 2) + 4 * hio + (e & 3);
-          if (rb + row < rows && f < Nout) {
-            const float h = silu_f32(acc[m][2 * q][e]) * acc[m][2 * q + 1][e];
-            orow[size_t(row) * io.o_ld + f] = f32_to_bf16(h);
+          for (int j = 0; j < 4; ++j) {
+            const int f = c0 + (wn * 2 + q) * 32 + 8 * j + 4 * hio;
+            if (f < Nout) {
+              float h[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) h[i] = silu_f32(acc[m][2 * q][4 * j + i]) * acc[m][2 * q + 1][4 * j + i];
+              uint2 v;
+              v.x = pack_bf16x2(h[0], h[1]);
+              v.y = pack_bf16x2(h[2], h[3]);
+              *reinterpret_cast<uint2*>(prow + f) = v;
+            }
           }
-        }
       }
     } else if (rb + r32o < rows) {
       // transposed blocks: lane owns row r32 and columns 8 j + 4 hi + 0..3 of each block
