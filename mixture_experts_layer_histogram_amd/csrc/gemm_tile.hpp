@@ -303,11 +303,11 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
   asm volatile("" : "+v"(lane_o));
   const int r32o = lane_o & 31, hio = lane_o >> 5;
 
-  if (MODE == 1 && io.row_dst) {
-    // Fused push: every output row goes to its own destination (a recv row).  The tile is
-    // staged as bf16 in LDS ([256 rows][256 cols], 16-byte chunks XOR-swizzled by row), then
-    // written back row by row in 16-byte vectors, so each destination row receives whole
-    // 128-byte lines.  The main loop ended on a barrier, so the stages are free.
+  if (MODE == 1) {
+    // The tile is staged as bf16 in LDS ([256 rows][256 cols], 16-byte chunks XOR-swizzled
+    // by row), then written back row by row in 16-byte vectors, so every output row receives
+    // whole 128-byte lines: rows of ye, or with row_dst (the fused push) each row at its own
+    // destination (a recv row).  The main loop ended on a barrier, so the stages are free.
     char* stg = smem;
     // (transposed blocks: lane owns row r32 and columns 8 j + 4 hi + 0..3 of each 32 x 32 block)
 #pragma unroll
@@ -328,9 +328,11 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
     const int ncols = min(kGemmBN, Nout - c0);
     for (int v = tid; v < kGemmBM * (kGemmBN / 8); v += kGemmThreads) {
       const int row = v >> 5, cv = v & 31;                  // 32 vectors of 8 bf16 per row
-      if (row < rows && cv * 8 < ncols)
-        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(io.row_dst[row]) + c0 + cv * 8) =
-            *reinterpret_cast<const u32x4*>(stg + row * 512 + ((cv ^ (row & 31)) << 4));
+      if (row < rows && cv * 8 < ncols) {
+        uint16_t* orow = io.row_dst ? reinterpret_cast<uint16_t*>(io.row_dst[row])
+                                    : pick4(row >> io.blk_log2, io.o0, io.o1, io.o2, io.o3) + size_t(row & bmask) * io.o_ld;
+        *reinterpret_cast<u32x4*>(orow + c0 + cv * 8) = *reinterpret_cast<const u32x4*>(stg + row * 512 + ((cv ^ (row & 31)) << 4));
+      }
     }
     __syncthreads();                                        // the next tile's fills reuse the stages
     return;
@@ -392,7 +394,7 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
     return;
   }
 
-  // epilogue: lane holds column r32 and rows 8*(e/4) + 4*hi + e%4 of each 32x32 block
+  // SwiGLU epilogue (MODE 0; MODE 1 and 2 returned above)
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int rb = wm * 64 + m * 32;                     // 32-row block, inside one row block
@@ -417,21 +419,6 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
             }
           }
       }
-    } else if (rb + r32o < rows) {
-      // transposed blocks: lane owns row r32 and columns 8 j + 4 hi + 0..3 of each block
-      uint16_t* prow = orow + size_t(r32o) * io.o_ld;
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = c0 + wn * 128 + n * 32 + 8 * j + 4 * hio;
-          if (col < Nout) {
-            uint2 v;
-            v.x = pack_bf16x2(acc[m][n][4 * j], acc[m][n][4 * j + 1]);
-            v.y = pack_bf16x2(acc[m][n][4 * j + 2], acc[m][n][4 * j + 3]);
-            *reinterpret_cast<uint2*>(prow + col) = v;
-          }
-        }
     }
   }
 }
