@@ -135,7 +135,7 @@ class ClockSampler:
                 return
             c = [int(v) for v in re.findall(r'"gfx_\d+": \{\s*"clk": \{\s*"value": (\d+)', txt)]
             w = re.search(r'"socket_power": \{\s*"value": (\d+)', txt)
-            if c and not self.stop_ev.is_set() and min(c) >= 500:      # idle readings before the load starts
+            if c and not self.stop_ev.is_set() and min(c) >= 1000:     # idle or ramping readings at the edges of the load
                 self.clk.append(float(np.mean(c)))
                 self.n += 1
                 if w:
