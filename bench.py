@@ -369,10 +369,24 @@ def run_backward(args, cfg, inp, P, stream, N):
         e[3].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_staged = t_start.elapsed_time(t_end) / args.steps
     stage_ms = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j, n in enumerate(names)}
-    log(f"[bench] backward {args.steps} steps: {ms_step:.3f} ms/step; stages {stage_ms}")
+    per_step = [ev[i][0].elapsed_time(ev[i][len(names)]) for i in range(args.steps)]
+    log(f"[bench] backward, three stage calls, {args.steps} steps: {ms_staged:.3f} ms/step; stages {stage_ms}")
+    # the single call (moe_backward), whose dX GEMM writes its rows straight to recv
+    fev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    fev[0].record(stream)
+    for i in range(args.steps):
+        P.backward()
+        fev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    fused_step = [fev[i].elapsed_time(fev[i + 1]) for i in range(args.steps)]
+    ms_fused = fev[0].elapsed_time(fev[args.steps]) / args.steps
+    log(f"[bench] backward, moe_backward (dX push fused), {args.steps} steps: {ms_fused:.3f} ms/step")
+    ms_step = ms_staged
+    if not args.unfused:
+        ms_step, per_step = ms_fused, fused_step
     row = cfg.d * 2
     # dh = dO W2 (2dFN), GEMM1 again (4dFN), dX (4dFN), dW1 + dW3 + dW2 (6dFN)
     flops = 16.0 * cfg.d * cfg.F * N
@@ -398,13 +412,16 @@ def run_backward(args, cfg, inp, P, stream, N):
                 "router logits x@W_r)",
         "config": {"workload": cfg.name, "R": cfg.R, "T": cfg.T, "d": cfg.d, "E": cfg.E, "E_local": cfg.E_local,
                    "k": cfg.k, "F": cfg.F, "local_pairs": N,
-                   "path": "backward after one forward: three stage calls on one stream"},
+                   "path": ("backward after one forward: three stage calls on one stream" if args.unfused else
+                            "backward after one forward: moe_backward, the push of dX fused into its GEMM")},
         "roofline": {"bound": "mfma", "kernel": "expert SwiGLU backward stage (dh, GEMM1+SwiGLU backward, dX, "
                                                  "dW1/dW3/dW2 GEMMs)",
                      "achieved": flops / t_ffn / 1e12, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": flops / t_ffn / PEAK_BF16_FLOPS, "traffic": None},
         "stages_ms": stage_ms,
         "step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step))},
+        "ms_per_step_staged": ms_staged,
+        "ms_per_step_fused": ms_fused,
         "stages_hbm_frac": {
             "pull_reverse": pull_bytes / (stage_ms["pull_reverse"] * 1e-3) / PEAK_HBM,
             "push_reverse": (push_bytes + merge_bytes + gate_bytes) / (stage_ms["push_reverse"] * 1e-3) / PEAK_HBM,
@@ -656,6 +673,8 @@ def main():
                      "frac": flops / t_ffn / peak, "traffic": traffic},
         "stages_ms": stage_ms,
         "step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step))},
+        "ms_per_step_staged": ms_staged,
+        "ms_per_step_fused": ms_fused,
         "stages_hbm_frac": {
             **({"dispatch": gather_bytes / (stage_ms["dispatch"] * 1e-3) / PEAK_HBM} if "dispatch" in stage_ms else {}),
             **({"combine+merge": (push_bytes + merge_bytes) / (stage_ms["combine"] * 1e-3) / PEAK_HBM}

@@ -67,9 +67,13 @@ __device__ __forceinline__ bf16x8 ld_frag_mn(const char* tile, int kb, int c0, i
 
 // out[r][c] = sum_k A[r][k] B[c][k] for r < orows, c < ocols of one 256 x 256 tile, in the
 // orientation each operand is stored.  K % 64 == 0.  MASK_K zeroes A's values at k >= A.kvalid.
-template <bool A_MN, bool B_MN, bool MASK_K>
+// ROW_DST: row_dst[r] is the address output row r goes to (then `out` is unused and col0 is
+// the tile's first output column); the tile is staged in LDS and stored row by row in 16-byte
+// vectors (ocols % 8 == 0).  A compile-time switch, so the other instantiations keep their code.
+template <bool A_MN, bool B_MN, bool MASK_K, bool ROW_DST = false>
 __device__ __forceinline__ void gemm_tile_t(const Operand& A, const Operand& B, uint16_t* __restrict__ out, int o_ld,
-                                            int orows, int ocols, int K, char* smem) {
+                                            int orows, int ocols, int K, char* smem,
+                                            const uint64_t* __restrict__ row_dst = nullptr, int col0 = 0) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -163,6 +167,31 @@ __device__ __forceinline__ void gemm_tile_t(const Operand& A, const Operand& B, 
   }
 
   // lane holds column r32 and rows 8*(e/4) + 4*hi + e%4 of each 32 x 32 block
+  if constexpr (ROW_DST) {
+    // [256 rows][256 cols] bf16 in LDS, 16-byte chunks XOR-swizzled by row; the K loop ended
+    // on a barrier, so the stages are free
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int col = wn * 128 + n * 32 + r32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = wm * 64 + m * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+          *reinterpret_cast<uint16_t*>(smem + row * 512 + (((col >> 3) ^ (row & 31)) << 4) + (col & 7) * 2) =
+              f32_to_bf16(acc[m][n][e]);
+        }
+      }
+    __syncthreads();
+    for (int v = tid; v < kGemmBM * (kGemmBN / 8); v += kGemmThreads) {
+      const int row = v >> 5, cv = v & 31;
+      if (row < orows && cv * 8 < ocols)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(row_dst[row]) + col0 + cv * 8) =
+            *reinterpret_cast<const u32x4*>(smem + row * 512 + ((cv ^ (row & 31)) << 4));
+    }
+    __syncthreads();                      // the next tile's fills reuse the stages
+    return;
+  }
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -181,10 +210,11 @@ __device__ __forceinline__ void gemm_tile_t(const Operand& A, const Operand& B, 
 //   dh = dO W2    (B0 = W2 [E_local][d][F], K = d, Nout = F);
 //   dX = [da|db] [W1; W3]   (B0 = W1, B1 = W3 [E_local][F][d], K = 2F, ksplit = F, Nout = d).
 // Tiles walk as the forward's grouped GEMM: 8 contiguous ranges, one per XCD, expert-major.
+template <bool ROW_DST>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_rows_bmn_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int ksplit,
     uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, const int32_t* __restrict__ mtile_base,
-    const int32_t* __restrict__ ctrl, int El, int K, int Nout) {
+    const int32_t* __restrict__ ctrl, int El, int K, int Nout, const uint64_t* __restrict__ RowDst) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int NT = (Nout + kGemmBN - 1) / kGemmBN;
   const int total = ctrl[kCtrlMTiles] * NT;
@@ -206,7 +236,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_rows_bmn_kernel(
     const Operand a{A + size_t(row0) * K, nullptr, K, rows, 0, 0};
     const Operand b{B0 + size_t(l) * ksplit * Nout + c0,
                     B1 ? B1 + size_t(l) * (K - ksplit) * Nout + c0 : nullptr, Nout, Nout - c0, ksplit, K};
-    gemm_tile_t<false, true, false>(a, b, C + size_t(row0) * Nout + c0, Nout, rows, Nout - c0, K, smem);
+    gemm_tile_t<false, true, false, ROW_DST>(a, b, ROW_DST ? nullptr : C + size_t(row0) * Nout + c0, Nout, rows,
+                                             Nout - c0, K, smem, ROW_DST ? RowDst + row0 : nullptr, c0);
   }
 }
 
@@ -254,7 +285,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_wgrad_bf16_kernel(
 hipError_t set_bwd_gemm_lds_attrs() {
   static std::atomic<uint64_t> done{0};
   return once_per_device(done, [] {
-    const void* ks[] = {reinterpret_cast<const void*>(grouped_rows_bmn_kernel),
+    const void* ks[] = {reinterpret_cast<const void*>(grouped_rows_bmn_kernel<false>),
+                        reinterpret_cast<const void*>(grouped_rows_bmn_kernel<true>),
                         reinterpret_cast<const void*>(grouped_wgrad_bf16_kernel)};
     for (const void* k : ks) {
       const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
@@ -264,13 +296,18 @@ hipError_t set_bwd_gemm_lds_attrs() {
   });
 }
 
+// row_dst: null (rows to C), or per pair the address its output row goes to
 hipError_t launch_rows_bmn(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, int ksplit, uint16_t* C, int K,
                            int Nout, const int32_t* offsets, const int32_t* mtb, const int32_t* ctrl, int El, int cus,
-                           hipStream_t st) {
+                           hipStream_t st, const uint64_t* row_dst) {
   hipError_t e = set_bwd_gemm_lds_attrs();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(grouped_rows_bmn_kernel, dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st, A, B0, B1, ksplit,
-                     C, offsets, mtb, ctrl, El, K, Nout);
+  if (row_dst)
+    hipLaunchKernelGGL(grouped_rows_bmn_kernel<true>, dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st, A, B0, B1,
+                       ksplit, C, offsets, mtb, ctrl, El, K, Nout, row_dst);
+  else
+    hipLaunchKernelGGL(grouped_rows_bmn_kernel<false>, dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st, A, B0,
+                       B1, ksplit, C, offsets, mtb, ctrl, El, K, Nout, row_dst);
   return hipGetLastError();
 }
 

@@ -442,12 +442,12 @@ hipError_t set_mx_bwd_lds_attrs() {
 // of nmax rows, B codes [E_local][Nout][K] with scales of E_local * Nout rows; bf16 out.
 hipError_t launch_rows_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, uint16_t* C, int K,
                           int Nout, int64_t nmax, const int32_t* offsets, const int32_t* mtb, const int32_t* ctrl,
-                          int El, int cus, hipStream_t st) {
+                          int El, int cus, hipStream_t st, const uint64_t* row_dst) {
   hipError_t e = set_mx_bwd_lds_attrs();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(grouped_gemm_mx_kernel<1>, dim3((cus / 8) * 8), dim3(kGemmThreads), kMxLds, st, A, As, B, nullptr,
                      Bs, nullptr, static_cast<void*>(C), nullptr, offsets, mtb, ctrl, El, K, Nout, nmax, nullptr,
-                     nullptr, nullptr, nullptr, nullptr);
+                     nullptr, nullptr, nullptr, row_dst);
   return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@ hipError_t launch_ffn(const moe_shape_t& s, int El, const void* xe, const int32_
                       hipStream_t st, const uint64_t* row_dst, const uint64_t* row_src);
 hipError_t launch_pair_addr(const moe_shape_t& s, const int32_t* pull_src, const int32_t* slot_of,
                             void* const* recv, const void* const* x, const int32_t* ctrl, uint64_t* push_dst,
-                            uint64_t* pull_addr, int cus, hipStream_t st);
+                            uint64_t* pull_addr, int cus, hipStream_t st, const float* dg, float* dgp);
 hipError_t launch_combine(const moe_shape_t& s, const char* ye, const int32_t* pull_src,
                           const int32_t* slot_of, const float* topk_w, void* const* recv, void* const* y,
                           const int32_t* ctrl, int cus, hipStream_t st);
@@ -36,7 +36,7 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
                              const WsLayout& L, hipStream_t st);
 hipError_t launch_rows_bmn(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, int ksplit, uint16_t* C, int K,
                            int Nout, const int32_t* offsets, const int32_t* mtb, const int32_t* ctrl, int El, int cus,
-                           hipStream_t st);
+                           hipStream_t st, const uint64_t* row_dst);
 hipError_t launch_gemm1_bwd(const uint16_t* xe, const uint16_t* w1, const uint16_t* w3, const uint16_t* dh,
                             uint16_t* h, uint16_t* dab, int d, int F, const int32_t* offsets, const int32_t* mtb,
                             const int32_t* ctrl, int El, int cus, hipStream_t st);
@@ -58,7 +58,7 @@ hipError_t launch_pull_reverse_mx(const moe_shape_t& s, const void* const* dy, c
                                   int cus, hipStream_t st);
 hipError_t launch_rows_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, uint16_t* C, int K,
                           int Nout, int64_t nmax, const int32_t* offsets, const int32_t* mtb, const int32_t* ctrl,
-                          int El, int cus, hipStream_t st);
+                          int El, int cus, hipStream_t st, const uint64_t* row_dst);
 hipError_t launch_gemm1_bwd_mx(const uint8_t* xe, const uint8_t* xes, const uint8_t* w1, const uint8_t* w3,
                                const uint8_t* w1s, const uint8_t* w3s, const uint16_t* dh, uint16_t* h, uint16_t* dab,
                                uint8_t* dabq, uint8_t* dabs, int d, int F, int64_t nmax, const int32_t* offsets,
@@ -273,7 +273,7 @@ int moe_expert_ffn_push(const moe_shape_t* s, const moe_placement_t* p, const mo
   uint64_t* dst = reinterpret_cast<uint64_t*>(w + L.push_dst);
   uint64_t* src = x ? reinterpret_cast<uint64_t*>(w + L.pull_addr) : nullptr;
   const hipError_t e = launch_pair_addr(*s, pull_src, slot_of, recv, x, reinterpret_cast<const int32_t*>(w + L.ctrl),
-                                        dst, src, cu_count(), st);
+                                        dst, src, cu_count(), st, nullptr, nullptr);
   if (e != hipSuccess) return MOE_EHIP;
   if (s->dtype == MOE_MXFP8)
     return hip_rc(launch_ffn_mx(*s, p->E_local, static_cast<const uint8_t*>(xe), xe_scales, offsets,
@@ -519,21 +519,26 @@ int moe_backward_mx(const moe_shape_t* s, const moe_placement_t* p, const void* 
   hipError_t e = launch_pull_reverse_mx(*s, dy, static_cast<const uint16_t*>(ye), pull_src, slot_of, topk_w, ctrl, dO,
                                         dOq, dOs, dg, nmax, cus, st);
   // MX data-gradient GEMMs: dh = dO W2; GEMM1 again with the backward epilogue; dX = [da|db] [W1; W3]
-  if (e == hipSuccess) e = launch_rows_mx(dOq, dOs, w2t, w2t_scales, dh, d, F, nmax, offsets, mtb, ctrl, El, cus, st);
+  if (e == hipSuccess)
+    e = launch_rows_mx(dOq, dOs, w2t, w2t_scales, dh, d, F, nmax, offsets, mtb, ctrl, El, cus, st, nullptr);
   if (e == hipSuccess)
     e = launch_gemm1_bwd_mx(xe, xe_scales, w1q, w3q, w_scales->w1, w_scales->w3, dh, h, dab, dabq, dabs, d, F, nmax,
                             offsets, mtb, ctrl, El, cus, st);
+  // the push of dX fused into its GEMM: each dX row goes straight to recv[r][t][j] (the per-pair
+  // address table lives in the dX staging region, which the fused GEMM leaves unused), and the
+  // table kernel pushes the gate gradients dg to dgp
+  uint64_t* dx_dst = reinterpret_cast<uint64_t*>(dX);
   if (e == hipSuccess)
-    e = launch_rows_mx(dabq, dabs, w13t, w13t_scales, dX, 2 * F, d, nmax, offsets, mtb, ctrl, El, cus, st);
+    e = launch_pair_addr(*s, pull_src, slot_of, recv, nullptr, ctrl, dx_dst, nullptr, cus, st, dg, dgp);
+  if (e == hipSuccess)
+    e = launch_rows_mx(dabq, dabs, w13t, w13t_scales, nullptr, 2 * F, d, nmax, offsets, mtb, ctrl, El, cus, st, dx_dst);
   // bf16 weight gradients over each expert's rows (the token rows gathered again in bf16)
   if (e == hipSuccess) e = launch_dispatch(*s, x, pull_src, reinterpret_cast<char*>(xeb), ctrl, cus, st);
   if (e == hipSuccess) e = launch_wgrad(dab, 2 * F, xeb, d, offsets, static_cast<uint16_t*>(dw1), El, F, d, cus, st);
   if (e == hipSuccess)
     e = launch_wgrad(dab + F, 2 * F, xeb, d, offsets, static_cast<uint16_t*>(dw3), El, F, d, cus, st);
   if (e == hipSuccess) e = launch_wgrad(dO, d, h, F, offsets, static_cast<uint16_t*>(dw2), El, d, F, cus, st);
-  // push reverse-dispatch, ordered sum, gate gradients
-  if (e == hipSuccess)
-    e = launch_push_grad(*s, reinterpret_cast<const char*>(dX), dg, pull_src, slot_of, recv, dgp, ctrl, cus, st);
+  // ordered sum of the pushed dX rows, gate gradients
   if (e == hipSuccess) e = launch_merge(*s, slot_of, nullptr, recv, dx, cus, st);
   if (e == hipSuccess) e = launch_gate_grad(*s, topk_w, topk_idx, slot_of, dgp, dlogits, cus, st);
   return hip_rc(e);
@@ -556,15 +561,12 @@ int moe_combine_pull_reverse(const moe_shape_t* s, const moe_placement_t* p, con
                                     cu_count(), static_cast<hipStream_t>(stream)));
 }
 
-int moe_expert_ffn_backward(const moe_shape_t* s, const moe_placement_t* p, const void* xe, const int32_t* offsets,
-                            const void* w1, const void* w3, const void* w2, const void* ws, size_t ws_bytes, void* dw1,
-                            void* dw3, void* dw2, void* bws, size_t bws_bytes, void* stream) {
-  int rc = check_bwd(s, p, ws, ws_bytes, bws, bws_bytes);
-  if (rc) return rc;
-  if (!offsets) return MOE_EINVAL;
-  const void* bufs[] = {xe, w1, w3, w2, dw1, dw3, dw2};
-  for (const void* q : bufs)
-    if (!aligned16(q)) return q ? MOE_EALIGN : MOE_EINVAL;
+// recv == null: dX rows to the backward workspace (the staged API); else the push of dX fused
+// into its GEMM (rows straight to recv, the gate gradients pushed to dgp by the table kernel)
+static int ffn_backward_impl(const moe_shape_t* s, const moe_placement_t* p, const void* xe, const int32_t* offsets,
+                             const void* w1, const void* w3, const void* w2, const void* ws, void* dw1, void* dw3,
+                             void* dw2, void* bws, const int32_t* pull_src, const int32_t* slot_of, void* const* recv,
+                             void* stream) {
   const WsLayout L = ws_layout(*s, p->E_local);
   const BwdLayout B = bwd_layout(*s, p->E_local);
   const char* w = static_cast<const char*>(ws);
@@ -583,15 +585,35 @@ int moe_expert_ffn_backward(const moe_shape_t* s, const moe_placement_t* p, cons
   const int El = p->E_local, d = s->d, F = s->F, cus = cu_count();
   hipStream_t st = static_cast<hipStream_t>(stream);
   // dh = dO W2; then h, da, db in GEMM1's backward epilogue; dX = [da|db] [W1; W3]
-  hipError_t e = launch_rows_bmn(dO, w2b, nullptr, d, dh, d, F, offsets, mtb, ctrl, El, cus, st);
+  hipError_t e = launch_rows_bmn(dO, w2b, nullptr, d, dh, d, F, offsets, mtb, ctrl, El, cus, st, nullptr);
   if (e == hipSuccess) e = launch_gemm1_bwd(xeb, w1b, w3b, dh, h, dab, d, F, offsets, mtb, ctrl, El, cus, st);
-  if (e == hipSuccess) e = launch_rows_bmn(dab, w1b, w3b, F, dX, 2 * F, d, offsets, mtb, ctrl, El, cus, st);
+  uint64_t* dx_dst = nullptr;
+  if (recv) {             // the address table lives in the dX staging region, unused when fused
+    dx_dst = reinterpret_cast<uint64_t*>(dX);
+    if (e == hipSuccess)
+      e = launch_pair_addr(*s, pull_src, slot_of, recv, nullptr, ctrl, dx_dst, nullptr, cus, st,
+                           reinterpret_cast<const float*>(b + B.dg), reinterpret_cast<float*>(b + B.dgp));
+  }
+  if (e == hipSuccess)
+    e = launch_rows_bmn(dab, w1b, w3b, F, recv ? nullptr : dX, 2 * F, d, offsets, mtb, ctrl, El, cus, st, dx_dst);
   // weight gradients over each expert's rows: dW1 = da^T x, dW3 = db^T x, dW2 = dO^T h
   if (e == hipSuccess) e = launch_wgrad(dab, 2 * F, xeb, d, offsets, static_cast<uint16_t*>(dw1), El, F, d, cus, st);
   if (e == hipSuccess)
     e = launch_wgrad(dab + F, 2 * F, xeb, d, offsets, static_cast<uint16_t*>(dw3), El, F, d, cus, st);
   if (e == hipSuccess) e = launch_wgrad(dO, d, h, F, offsets, static_cast<uint16_t*>(dw2), El, d, F, cus, st);
   return hip_rc(e);
+}
+
+int moe_expert_ffn_backward(const moe_shape_t* s, const moe_placement_t* p, const void* xe, const int32_t* offsets,
+                            const void* w1, const void* w3, const void* w2, const void* ws, size_t ws_bytes, void* dw1,
+                            void* dw3, void* dw2, void* bws, size_t bws_bytes, void* stream) {
+  int rc = check_bwd(s, p, ws, ws_bytes, bws, bws_bytes);
+  if (rc) return rc;
+  if (!offsets) return MOE_EINVAL;
+  const void* bufs[] = {xe, w1, w3, w2, dw1, dw3, dw2};
+  for (const void* q : bufs)
+    if (!aligned16(q)) return q ? MOE_EALIGN : MOE_EINVAL;
+  return ffn_backward_impl(s, p, xe, offsets, w1, w3, w2, ws, dw1, dw3, dw2, bws, nullptr, nullptr, nullptr, stream);
 }
 
 int moe_dispatch_push_reverse(const moe_shape_t* s, const moe_placement_t* p, const int32_t* pull_src,
@@ -638,11 +660,17 @@ int moe_backward(const moe_shape_t* s, const moe_placement_t* p, const void* con
     if (!dlogits[r]) return MOE_EINVAL;
   if ((rc = moe_combine_pull_reverse(s, p, dy, ye, pull_src, slot_of, topk_w, ws, ws_bytes, bws, bws_bytes, stream)))
     return rc;
-  if ((rc = moe_expert_ffn_backward(s, p, xe, offsets, w1, w3, w2, ws, ws_bytes, dw1, dw3, dw2, bws, bws_bytes,
-                                    stream)))
+  // the expert backward with the push of dX fused into its GEMM, then the ordered sum and the
+  // gate gradients (moe_dispatch_push_reverse without its push)
+  if ((rc = ffn_backward_impl(s, p, xe, offsets, w1, w3, w2, ws, dw1, dw3, dw2, bws, pull_src, slot_of, recv, stream)))
     return rc;
-  return moe_dispatch_push_reverse(s, p, pull_src, slot_of, topk_idx, topk_w, ws, ws_bytes, recv, dx, dlogits, bws,
-                                   bws_bytes, stream);
+  const BwdLayout B = bwd_layout(*s, p->E_local);
+  float* dgp = reinterpret_cast<float*>(static_cast<char*>(bws) + B.dgp);
+  const int cus = cu_count();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_merge(*s, slot_of, nullptr, recv, dx, cus, st);
+  if (e == hipSuccess) e = launch_gate_grad(*s, topk_w, topk_idx, slot_of, dgp, dlogits, cus, st);
+  return hip_rc(e);
 }
 
 int moe_read_status(const void* ws, void* stream) {

@@ -82,13 +82,15 @@ __global__ __launch_bounds__(256) void combine_push_kernel(const char* __restric
 // Per-pair address tables for the fused FFN: push_dst[s] = address of recv[r][t][j] (the
 // push fused into the down GEMM), and, when pull_addr is not null, pull_addr[s] = address of
 // x_r[t] (the pull fused into the gate/up GEMM), with (r, t) = pull_src[s] and
-// slot_of[r][t][j] = s.
+// slot_of[r][t][j] = s; in the backward, dgp[r][t][j] = dg[s] as well (the push of the gate
+// gradients, whose dX rows the dX GEMM pushes itself).
 __global__ __launch_bounds__(256) void pair_addr_kernel(const int32_t* __restrict__ pull_src,
                                                         const int32_t* __restrict__ slot_of,
                                                         const int32_t* __restrict__ ctrl, RankPtrs<char*> recv,
                                                         RankPtrs<const char*> x, int T, int k, int row_bytes,
                                                         uint64_t* __restrict__ push_dst,
-                                                        uint64_t* __restrict__ pull_addr) {
+                                                        uint64_t* __restrict__ pull_addr,
+                                                        const float* __restrict__ dg, float* __restrict__ dgp) {
   const int N = ctrl[kCtrlN];
   for (int s = blockIdx.x * 256 + threadIdx.x; s < N; s += gridDim.x * 256) {
     const int r = pull_src[2 * int64_t(s)];
@@ -99,6 +101,7 @@ __global__ __launch_bounds__(256) void pair_addr_kernel(const int32_t* __restric
       if (so[jj] == s) j = jj;
     push_dst[s] = reinterpret_cast<uint64_t>(recv.p[r] + (int64_t(t) * k + j) * row_bytes);
     if (pull_addr) pull_addr[s] = reinterpret_cast<uint64_t>(x.p[r] + int64_t(t) * row_bytes);
+    if (dgp) dgp[(int64_t(r) * T + t) * k + j] = dg[s];     // backward: the pair's gate gradient
   }
 }
 
@@ -222,7 +225,7 @@ hipError_t launch_push_grad(const moe_shape_t& s, const char* dX, const float* d
 // x: null (no pull table), or the R source buffers
 hipError_t launch_pair_addr(const moe_shape_t& s, const int32_t* pull_src, const int32_t* slot_of,
                             void* const* recv, const void* const* x, const int32_t* ctrl, uint64_t* push_dst,
-                            uint64_t* pull_addr, int cus, hipStream_t st) {
+                            uint64_t* pull_addr, int cus, hipStream_t st, const float* dg, float* dgp) {
   RankPtrs<char*> rp{};
   RankPtrs<const char*> xp{};
   for (int r = 0; r < s.R; ++r) {
@@ -231,7 +234,7 @@ hipError_t launch_pair_addr(const moe_shape_t& s, const int32_t* pull_src, const
   }
   const int row_bytes = s.d * (s.dtype == MOE_F32 ? 4 : 2);
   hipLaunchKernelGGL(pair_addr_kernel, dim3(cus * 2), dim3(256), 0, st, pull_src, slot_of, ctrl, rp, xp, s.T, s.k,
-                     row_bytes, push_dst, x ? pull_addr : nullptr);
+                     row_bytes, push_dst, x ? pull_addr : nullptr, dg, dgp);
   return hipGetLastError();
 }
 
