@@ -673,8 +673,6 @@ def main():
                      "frac": flops / t_ffn / peak, "traffic": traffic},
         "stages_ms": stage_ms,
         "step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step))},
-        "ms_per_step_staged": ms_staged,
-        "ms_per_step_fused": ms_fused,
         "stages_hbm_frac": {
             **({"dispatch": gather_bytes / (stage_ms["dispatch"] * 1e-3) / PEAK_HBM} if "dispatch" in stage_ms else {}),
             **({"combine+merge": (push_bytes + merge_bytes) / (stage_ms["combine"] * 1e-3) / PEAK_HBM}
