@@ -386,7 +386,10 @@ int moe_dispatch_push_reverse(const moe_shape_t* s, const moe_placement_t* p, co
  * moe_backward -- the three calls above in order on one stream, after moe_forward ran with
  * the same arguments: gradients of L with respect to the token rows (dx), the local
  * experts' weights (dw1, dw3, dw2) and the logits (dlogits).  Every stage's arguments are
- * checked before the first launch.
+ * checked before the first launch.  The results are bit-identical to the three calls; the
+ * push of dX is fused into its GEMM here (each dX row is stored straight to recv[r][t][j]),
+ * so bws's dX staging rows are not written (its first 8 N bytes hold the per-pair recv
+ * addresses instead).
  */
 int moe_backward(const moe_shape_t* s, const moe_placement_t* p, const void* const* dy, const void* xe,
                  const void* ye, const void* w1, const void* w3, const void* w2, const int32_t* topk_idx, const float* topk_w, const int32_t* offsets, const int32_t* pull_src,
@@ -427,7 +430,8 @@ int moe_backward_prepare_mx(const moe_shape_t* s, const moe_placement_t* p, cons
  * Accuracy against the MXFP8 backward oracle (the same quantisation points in fp64):
  * dx within 1e-1 of the largest row value per token and 2.5e-2 in Frobenius norm (rounding
  * decisions on fp32 / bf16 intermediates flip against fp64); weight gradients per row
- * within the bf16 row-relative 2e-2; dlogits as moe_backward.
+ * within the bf16 row-relative 2e-2; dlogits as moe_backward.  As in moe_backward, the dX
+ * GEMM stores each row straight to recv[r][t][j] (recv is written, then summed into dx).
  */
 int moe_backward_mx(const moe_shape_t* s, const moe_placement_t* p, const void* const* dy, const void* const* x,
                     const uint8_t* xe, const uint8_t* xe_scales, const void* ye, const uint8_t* w1q, const uint8_t* w3q,
