@@ -78,6 +78,19 @@ def parse():
                          "(evicts the 4 MB L2s and the 256 MB MALL); reported as 'cold'")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run three plain 1 GiB device copies (counter calibration)")
+    ap.add_argument("--persistent", action="store_true",
+                    help="time the persistent megakernel path (layout, one persistent kernel for pull dispatch into "
+                         "the ring, expert FFN and push combine, merge) instead of the fused multi-kernel path")
+    ap.add_argument("--fused", action="store_true",
+                    help="time the fused multi-kernel path (layout, FFN with the pull and push fused in, merge)")
+    ap.add_argument("--comm-cus", type=int, default=16, help="persistent path: data-movement workgroups")
+    ap.add_argument("--minibatch", type=int, default=0, help="persistent path: rows per chunk (64, 128, 256)")
+    ap.add_argument("--ring-mib", type=int, default=0, help="persistent path: ring size (default: the config's)")
+    ap.add_argument("--trace", action="store_true",
+                    help="persistent path: after the timed steps, one traced call; per-role busy and wait summary")
+    ap.add_argument("--sweep-persistent", default="",
+                    help="persistent path: 'C1,C2,...:M1,M2,...' -- time every comm_cus C x minibatch M "
+                         "(one JSON line per point)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of "
                          "this --config into its committed traffic record, then exit")
@@ -494,6 +507,77 @@ def run_sweep(args, cfg, P, stream):
     P.shape.T = T_full
 
 
+def persistent_exec(args, cfg, comm=None, mb=None, trace=0):
+    from mixture_experts_layer_histogram_amd import moe
+    return moe.Exec(mb or args.minibatch or cfg.minibatch, args.comm_cus if comm is None else comm, 0, trace, 0)
+
+
+def trace_summary(ev, tpu, grid):
+    """Per-role figures of one traced persistent call: span, busy and waiting fractions of
+    the data-movement and compute workgroups, task counts, and the overlap of combine
+    (pushes) with dispatch (gathers)."""
+    import numpy as np
+    t0 = int(ev["t_begin"].min())
+    span = float(ev["t_end"].max() - t0)
+    out = {"span_us": span / tpu, "events": int(len(ev))}
+    starts = ev[ev["kind"] == 0]
+    role_of = {int(w): int(r) for w, r in zip(starts["workgroup"], starts["index"])}
+    for role, name, kinds in ((0, "data_movement", (1, 2)), (1, "compute", (3, 4))):
+        wgs = [w for w, r in role_of.items() if r == role]
+        sel = ev[np.isin(ev["kind"], kinds)]
+        busy = float((sel["t_end"] - sel["t_begin"]).sum())
+        wait = float(sel["t_wait"].sum())
+        out[name] = {"workgroups": len(wgs), "tasks": int(len(sel)),
+                     "busy_frac": busy / (span * max(1, len(wgs))),
+                     "wait_frac": wait / (span * max(1, len(wgs)))}
+    g, pu = ev[ev["kind"] == 1], ev[ev["kind"] == 2]
+    if len(g) and len(pu):
+        last_gather = float(g["t_end"].max() - t0)
+        first_push = float(pu["t_begin"].min() - t0)
+        pushes_before = int((pu["t_begin"] < g["t_end"].max()).sum())
+        out["overlap"] = {"first_push_us": first_push / tpu, "last_gather_end_us": last_gather / tpu,
+                          "pushes_started_before_last_gather": pushes_before, "pushes": int(len(pu))}
+    ff = ev[np.isin(ev["kind"], (3, 4))]
+    if len(ff):
+        out["first_gemm_us"] = float(ff["t_begin"].min() - t0) / tpu
+        out["last_gemm_end_us"] = float(ff["t_end"].max() - t0) / tpu
+    return out
+
+
+def run_persistent_sweep(args, cfg, P, stream):
+    """comm_cus x minibatch grid on the persistent kernel (layout once per minibatch)."""
+    import torch
+    from mixture_experts_layer_histogram_amd import moe
+    comms, mbs = args.sweep_persistent.split(":")
+    N = P.N()
+    flops = 6.0 * cfg.d * cfg.F * N
+    for mb in [int(v) for v in mbs.split(",")]:
+        P.ex = moe.Exec(mb, 0, 0, 0, 0)
+        P.layout()
+        for comm in [int(v) for v in comms.split(",")]:
+            ex = persistent_exec(args, cfg, comm=comm, mb=mb)
+            P.alloc_ring(args.ring_mib or cfg.ring_mib, ex)
+            for _ in range(args.warmup):
+                P.persistent_dfc(ex)
+            torch.cuda.synchronize()
+            st = P.status()
+            if st != 0:
+                raise SystemExit(f"device status {st} at comm_cus={comm} minibatch={mb}")
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                P.persistent_dfc(ex)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            line = {"metric": "persistent kernel ms (dispatch + FFN + combine)", "workload": cfg.name,
+                    "comm_cus": comm, "minibatch": mb, "ring_mib": args.ring_mib or cfg.ring_mib, "ms": ms,
+                    "ffn_tflops": flops / (ms * 1e-3) / 1e12, "frac_bf16_peak": flops / (ms * 1e-3) / PEAK_BF16_FLOPS}
+            print(json.dumps(line), flush=True)
+            log(f"[sweep-persistent] comm={comm} mb={mb}: {ms:.3f} ms")
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -504,6 +588,7 @@ def main():
               f"(the multi-GPU expert-parallel path is not built)", file=sys.stderr)
         sys.exit(2)
     import torch
+    from mixture_experts_layer_histogram_amd import moe
     from mixture_experts_layer_histogram_amd.device import DeviceProblem
 
     if args.signal_latency:
@@ -518,7 +603,12 @@ def main():
     P = DeviceProblem(cfg, inp, device=dev)
     stream = torch.cuda.current_stream()
 
-    warm = P.forward if (args.unfused or args.backward or args.sweep_tokens) else P.forward_fused
+    if args.persistent or args.sweep_persistent:
+        P.ex = moe.Exec(args.minibatch or cfg.minibatch, 0, 0, 0, 0)
+        P.alloc_ring(args.ring_mib or cfg.ring_mib, persistent_exec(args, cfg))
+        warm = P.forward_persistent
+    else:
+        warm = P.forward if (args.unfused or args.backward or args.sweep_tokens) else P.forward_fused
     for _ in range(args.warmup):
         warm()
     torch.cuda.synchronize()
@@ -533,8 +623,16 @@ def main():
     if args.sweep_tokens:
         run_sweep(args, cfg, P, stream)
         return
+    if args.sweep_persistent:
+        run_persistent_sweep(args, cfg, P, stream)
+        return
 
-    if args.unfused:
+    if args.persistent:
+        # one persistent kernel for the pull into the ring, the expert FFN and the push
+        names = ["layout", "ffn", "merge"]
+        calls = [P.layout, P.persistent_dfc, P.merge]
+        fwd = P.forward_persistent
+    elif args.unfused:
         names = ["layout", "dispatch", "ffn", "combine"]
         calls = [P.layout, P.dispatch, P.ffn, P.combine]
         fwd = P.forward
@@ -661,7 +759,10 @@ def main():
         "data": "synthetic (seeded N(0,1) tokens, fan-in scaled random expert weights, router logits x@W_r)",
         "config": {"workload": cfg.name, "R": cfg.R, "T": cfg.T, "d": cfg.d, "E": cfg.E,
                    "E_local": cfg.E_local, "k": cfg.k, "F": cfg.F, "local_pairs": N, "load": load,
-                   "path": ("unfused (layout, dispatch, ffn writing ye, push + merge kernels on one stream)"
+                   "path": ("persistent megakernel (layout; one persistent kernel whose data-movement "
+                            "workgroups pull token rows into the ring and push finished rows to recv while its "
+                            "compute workgroups run the grouped SwiGLU GEMMs; merge)" if args.persistent else
+                            "unfused (layout, dispatch, ffn writing ye, push + merge kernels on one stream)"
                             if args.unfused else
                             ("fused push (layout, dispatch, ffn whose down GEMM writes each row to its recv slot, "
                              "merge; kernels on one stream)" if cfg.dtype == "mxfp8" else
@@ -681,6 +782,32 @@ def main():
         "pairs_per_s": N / (ms_step * 1e-3),
         "source_tokens_per_s": cfg.R * cfg.T / (ms_step * 1e-3),
     }
+    if args.persistent:
+        pex = persistent_exec(args, cfg)
+        result["config"].update({"ring_mib": args.ring_mib or cfg.ring_mib, "minibatch": pex.minibatch_rows,
+                                 "comm_cus": pex.comm_cus})
+        result["roofline"]["kernel"] = ("persistent kernel (pull into the ring, gate/up+SwiGLU and down GEMMs, "
+                                        "push), FLOPs of the GEMMs")
+        # the movers' algorithmic bytes inside the persistent kernel: rows in and out of the ring
+        result["stages_hbm_frac"]["dispatch+combine in the persistent kernel"] = (
+            (gather_bytes + push_bytes) / t_ffn / PEAK_HBM)
+        if args.trace:
+            tex = persistent_exec(args, cfg, trace=1)
+            wsb = moe.moe_persistent_workspace_bytes(P.shape, P.placement, tex)
+            tws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+            moe.moe_forward_persistent(P.shape, P.placement, tex, P.logits, P.x, P.w1, P.w3, P.w2, P.ring,
+                                       P.recv, P.y, P.topk_idx, P.topk_w, P.counts, P.offsets, P.pull_src,
+                                       P.slot_of, tws)
+            if moe.moe_read_status(tws) != 0:
+                raise SystemExit("device status after the traced call")
+            ev, tpu = moe.read_trace(tws, P.shape, P.placement, tex)
+            result["trace"] = trace_summary(ev, tpu, P.cu_grid() if hasattr(P, "cu_grid") else 0)
+            log(f"[bench] trace: {result['trace']}")
+            del tws
+    else:
+        # the fused path: the pull and push bytes moved inside the FFN kernels, over the FFN time
+        if not args.unfused and cfg.dtype != "mxfp8":
+            result["stages_hbm_frac"]["dispatch+combine fused in the FFN"] = (gather_bytes + push_bytes) / t_ffn / PEAK_HBM
     if graph:
         result["graph"] = graph
     if cold:

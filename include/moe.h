@@ -55,6 +55,8 @@ extern "C" {
 #define MOE_EHIP (-4)     /* a HIP launch failed */
 #define MOE_ETIMEOUT (-5) /* a device-side wait exceeded its watchdog budget */
 #define MOE_EUNSUP (-6)   /* combination not built (e.g. dtype for this entry point) */
+#define MOE_EINCOMPLETE (-7) /* the persistent kernel ended with work left undone (a pipeline
+                                received no data-movement or no compute workgroup) */
 
 typedef enum {
   MOE_F32 = 0,   /* fp32 rows and weights, fp32 arithmetic */
@@ -100,7 +102,9 @@ typedef struct {
                                the persistent path takes 64, 128 or 256) */
   int32_t comm_cus;         /* persistent path: workgroups doing data movement (default 32) */
   int32_t ring_slots;       /* persistent path: cap on ring slots (default: as many as ring_bytes holds) */
-  int32_t trace;            /* reserved, must be 0 */
+  int32_t trace;            /* persistent path: 1 = record a per-workgroup event trace into the
+                               workspace (moe_persistent_trace_info); every other entry point
+                               requires 0 (else MOE_EINVAL) */
   uint64_t watchdog_us;     /* persistent path: wall-clock budget of every device wait in
                                microseconds (default 2,000,000) */
 } moe_exec_t;
@@ -285,26 +289,35 @@ int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_
  * part (dispatch, combine, state) and a compute part (expert FFN) that notify each other
  * through GPU-local counters; tokens reach the experts a minibatch at a time through a
  * fixed-size ring buffer whose slots are reused right after combine, so the combine of one
- * macrobatch overlaps the dispatch of the next; qubstore, ring buffer and megakernel
+ * batch overlaps the dispatch of the next; qubstore, ring buffer and megakernel
  * paragraphs: no CPU in the loop, no worst-case buffers].
  * Same inputs and outputs as moe_forward (bf16 only), plus:
  *   ring, ring_bytes: caller-owned device buffer, 256-byte aligned, of at least
  *     256 / minibatch_rows slots of moe_ring_slot_bytes() each.  A slot holds one
  *     minibatch of token rows (overwritten in place by their expert outputs) and their h
  *     rows.  Fewer slots mean more back-pressure, never a different result.
- *   ws: at least moe_persistent_workspace_bytes() bytes (no worst-case staging).
- * Launch sequence on `stream`: the layout kernels, one cooperative persistent kernel
- * (grid = one workgroup per CU), the weighted merge.  The CUs split into ex->comm_cus
- * data-movement workgroups and the rest for the expert GEMMs; with eight XCDs and enough
- * ring slots there is one pipeline per XCD so every hand-off stays inside one L2.  Every
- * device wait is bounded by ex->watchdog_us; on expiry the kernel exits and
- * moe_read_status() returns MOE_ETIMEOUT.  Bit-identical to moe_forward's outputs for the
- * same inputs (same tile arithmetic, same merge order).
- * Status: currently switched off -- after its argument checks it returns MOE_EUNSUP and
- * launches nothing (its first GPU run did not complete; the cause is under study).
- * Errors: MOE_EUNSUP for a non-bf16 dtype or minibatch_rows not in {64, 128, 256};
- * MOE_ENOSPC for a ring below one 256-row tile or a small workspace; MOE_EINVAL when
- * comm_cus leaves no CU for compute.
+ *   ws: at least moe_persistent_workspace_bytes() bytes (no worst-case row staging).
+ * Launch sequence on `stream`: the layout kernels, a preparation kernel (clears the control
+ * words, builds the per-pipeline task tables), the persistent kernel (one 512-thread
+ * workgroup per CU, ordinary launch), a completion check, the weighted merge.
+ * Roles: in each pipeline the first comm_cus / pipelines workgroups to start move data --
+ * they gather chunks of token rows from the source buffers into free ring slots and push
+ * finished output rows to recv, freeing the slots -- and the others take GEMM tasks in
+ * ticket order.  Row tiles (256 rows of one expert) are split evenly over the pipelines:
+ * eight (one per XCD, every hand-off inside one L2) when each XCD's share of the ring holds
+ * two groups, else fewer, with agent-scope hand-offs.  Up to G consecutive row tiles of one
+ * expert form a group whose GEMM tasks run weight-panel-major, so concurrent tasks share
+ * each weight panel (G = slots per pipeline / (2 * chunks per row tile), at most 8).
+ * Every device wait is bounded by ex->watchdog_us; on expiry all workgroups exit and
+ * moe_read_status() returns MOE_ETIMEOUT.  If a pipeline's work was left undone (no
+ * workgroup reached it) moe_read_status() returns MOE_EINCOMPLETE.
+ * recv (local-pair entries) and y are bit-identical to moe_forward's for the same inputs
+ * (same tile arithmetic, same merge order).
+ * With ex->trace = 1 the kernel records one moe_trace_event_t per task and per workgroup
+ * start / end into the workspace (moe_persistent_trace_info).
+ * Errors: MOE_EUNSUP for a non-bf16 dtype, minibatch_rows not in {64, 128, 256}, or a
+ * device where one workgroup per CU cannot be resident; MOE_ENOSPC for a ring below one
+ * 256-row tile or a small workspace; MOE_EINVAL when comm_cus leaves no CU for compute.
  */
 int moe_forward_persistent(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
                            const float* const* logits, const void* const* x, const void* w1, const void* w3,
@@ -312,11 +325,55 @@ int moe_forward_persistent(const moe_shape_t* s, const moe_placement_t* p, const
                            int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
                            int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moe_persistent_dispatch_ffn_combine -- the persistent kernel of moe_forward_persistent alone
+ * (with its preparation and completion-check kernels): pull dispatch into the ring, the
+ * grouped SwiGLU FFN and the push combine into recv, from the outputs of moe_layout (run
+ * before, on the same stream, with the same shape, placement and ws).  recv's local-pair
+ * entries are bit-identical to moe_dispatch_pull + moe_expert_ffn + the push of
+ * moe_combine_push; the weighted merge (moe_weighted_merge) is not included.  Arguments,
+ * errors and status as moe_forward_persistent.
+ */
+int moe_persistent_dispatch_ffn_combine(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+                                        const void* const* x, const void* w1, const void* w3, const void* w2,
+                                        void* ring, size_t ring_bytes, const int32_t* pull_src,
+                                        const int32_t* slot_of, const int32_t* offsets, void* const* recv, void* ws,
+                                        size_t ws_bytes, void* stream);
+
 /* Bytes of one ring slot of moe_forward_persistent (0 if unsupported). */
 size_t moe_ring_slot_bytes(const moe_shape_t* s, const moe_exec_t* ex);
 
-/* Workspace bytes moe_forward_persistent needs (smaller than moe_workspace_bytes). */
+/* Workspace bytes moe_forward_persistent needs (smaller than moe_workspace_bytes); includes
+ * the trace region when ex->trace is 1. */
 size_t moe_persistent_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex);
+
+/* One event of the persistent kernel's trace.  Times are wall-clock ticks of the GPU's
+ * constant-rate counter (ticks_per_us from moe_persistent_trace_info). */
+typedef struct {
+  int64_t t_begin;   /* task start (after its waits) */
+  int64_t t_end;     /* task end (its completion signal sent) */
+  int32_t t_wait;    /* ticks spent waiting (or, for a mover, idle) before t_begin */
+  int32_t index;     /* gather: pipeline-local chunk; push: row tile; GEMM: row_tile * 256 + column tile;
+                        start / end: 0 = data movement, 1 = compute */
+  int32_t workgroup; /* blockIdx.x */
+  int16_t kind;      /* MOE_TRACE_* */
+  int16_t pipeline;
+} moe_trace_event_t;
+
+#define MOE_TRACE_START 0
+#define MOE_TRACE_GATHER 1
+#define MOE_TRACE_PUSH 2
+#define MOE_TRACE_GATE_UP 3
+#define MOE_TRACE_DOWN 4
+#define MOE_TRACE_END 5
+
+/* Where the trace of moe_forward_persistent (ex->trace = 1) lies in its workspace: an int32
+ * event count at byte `offset`, then up to `capacity` events from byte offset + 256 (events
+ * beyond the capacity are dropped; the count still counts them).  Also the wall-clock tick
+ * rate of the current device (100 per us if it cannot be queried).  No kernel is launched;
+ * MOE_EINVAL for a bad shape, a null pointer or ex->trace != 1. */
+int moe_persistent_trace_info(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+                              size_t* offset, int32_t* capacity, int32_t* ticks_per_us);
 
 /*
  * Backward of the share (bf16 only; other dtypes return MOE_EUNSUP)

@@ -7,6 +7,7 @@
 #include <atomic>
 
 #include "../../include/moe.h"
+#include "persist_sched.hpp"
 
 namespace moe {
 
@@ -73,8 +74,8 @@ inline WsLayout ws_layout(const moe_shape_t& s, int32_t E_local) {
   w.chunk_base = o;  o = align256(o + size_t(E_local + 1) * 4);
   w.blockhist = o;   o = align256(o + size_t(w.nb) * s.E * 4);
   w.blockbase = o;   o = align256(o + size_t(w.nb) * E_local * 4);
-  // persistent-path control block: 128 words + 6 per row tile + one per ring slot
-  w.pctrl = o;       o = align256(o + (size_t(128) + size_t(w.max_mtiles) * 6 + kMaxRingSlots) * 4);
+  // persistent-path control block (counters, task tables, one epoch word per ring slot)
+  w.pctrl = o;       o = align256(o + size_t(sched::ctrl_layout(w.max_mtiles, kMaxRingSlots).words) * 4);
   // h staging: fp32/bf16 rows, or MXFP8 codes followed (256-aligned) by their block scales
   const size_t hbytes = (s.dtype == MOE_MXFP8)
                             ? align256(size_t(w.max_pairs) * s.F) + size_t(w.max_pairs) * (s.F / 32)

@@ -31,9 +31,11 @@ hipError_t launch_merge(const moe_shape_t& s, const int32_t* slot_of, const floa
                         void* const* y, int cus, hipStream_t st);
 hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x, const void* w1, const void* w3,
                              const void* w2, const int32_t* pull_src, const int32_t* slot_of,
-                             const int32_t* offsets, char* ring, long long slot_bytes, int slots, int blk_log2,
-                             int comm_cus, int n_part, int cus, long long budget, void* const* recv, char* ws,
-                             const WsLayout& L, hipStream_t st);
+                             const int32_t* offsets, char* ring, long long slot_bytes, int blk_log2,
+                             const sched::Plan& plan, int grid, long long budget, void* const* recv, char* ws,
+                             const WsLayout& L, moe_trace_event_t* trace, int32_t* trace_count, int trace_cap,
+                             hipStream_t st);
+hipError_t persistent_occupancy(int* blocks_per_cu);
 hipError_t launch_rows_bmn(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, int ksplit, uint16_t* C, int K,
                            int Nout, const int32_t* offsets, const int32_t* mtb, const int32_t* ctrl, int El, int cus,
                            hipStream_t st, const uint64_t* row_dst);
@@ -68,8 +70,6 @@ hipError_t launch_gemm1_bwd_mx(const uint8_t* xe, const uint8_t* xes, const uint
 using namespace moe;
 
 namespace {
-
-constexpr bool kPersistentEnabled = false;
 
 int check_shape(const moe_shape_t* s, const moe_placement_t* p) {
   if (!s || !p) return MOE_EINVAL;
@@ -153,6 +153,12 @@ long long wall_ticks_per_us() {
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// execution knobs of the multi-kernel entry points: the trace is the persistent path's only
+int check_ex(const moe_exec_t* ex) {
+  if (ex && (ex->trace != 0 || ex->minibatch_rows < 0)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
 // backward calls: a shape of the given dtype, the forward's workspace, and the backward workspace
 int check_bwd(const moe_shape_t* s, const moe_placement_t* p, const void* ws, size_t ws_bytes, const void* bws,
               size_t bws_bytes, int dtype = MOE_BF16) {
@@ -197,7 +203,7 @@ int moe_layout(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t*
                int32_t* offsets, int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes,
                void* stream) {
   int rc = check_shape(s, p);
-  if (rc) return rc;
+  if (rc || (rc = check_ex(ex))) return rc;
   if (!p->expert_to_local || !topk_idx || !topk_w || !counts || !offsets || !pull_src || !slot_of)
     return MOE_EINVAL;
   if (ex && ex->minibatch_rows < 0) return MOE_EINVAL;
@@ -231,9 +237,8 @@ int moe_dispatch_pull(const moe_shape_t* s, const moe_placement_t* p, const void
 int moe_expert_ffn(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex, const void* xe,
                    const uint8_t* xe_scales, const int32_t* offsets, const void* w1, const void* w3, const void* w2,
                    const moe_mx_scales_t* w_scales, void* ye, void* ws, size_t ws_bytes, void* stream) {
-  (void)ex;
   int rc = check_shape(s, p);
-  if (rc) return rc;
+  if (rc || (rc = check_ex(ex))) return rc;
   if (!offsets) return MOE_EINVAL;
   const void* bufs[] = {xe, w1, w3, w2, ye};
   for (const void* b : bufs)
@@ -255,9 +260,8 @@ int moe_expert_ffn_push(const moe_shape_t* s, const moe_placement_t* p, const mo
                         const void* w1, const void* w3, const void* w2, const moe_mx_scales_t* w_scales,
                         const int32_t* pull_src, const int32_t* slot_of, void* const* recv, void* ws, size_t ws_bytes,
                         void* stream) {
-  (void)ex;
   int rc = check_shape(s, p);
-  if (rc) return rc;
+  if (rc || (rc = check_ex(ex))) return rc;
   if (!offsets || !pull_src || !slot_of) return MOE_EINVAL;
   if (x && s->dtype == MOE_MXFP8) return MOE_EUNSUP;      // MXFP8 rows are quantised by the gather
   const void* bufs[] = {x ? w1 : xe, w1, w3, w2};
@@ -315,7 +319,7 @@ int moe_forward(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t
                 int32_t* offsets, int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes,
                 void* stream) {
   int rc = check_shape(s, p);
-  if (rc) return rc;
+  if (rc || (rc = check_ex(ex))) return rc;
   // validate every stage's arguments before launching any of them
   if (!p->expert_to_local || !topk_idx || !topk_w || !counts || !offsets || !pull_src || !slot_of)
     return MOE_EINVAL;
@@ -343,7 +347,7 @@ int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_
                       int32_t* offsets, int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes,
                       void* stream) {
   int rc = check_shape(s, p);
-  if (rc) return rc;
+  if (rc || (rc = check_ex(ex))) return rc;
   // validate every stage's arguments before launching any of them
   if (!p->expert_to_local || !topk_idx || !topk_w || !counts || !offsets || !pull_src || !slot_of)
     return MOE_EINVAL;
@@ -372,10 +376,117 @@ size_t moe_ring_slot_bytes(const moe_shape_t* s, const moe_exec_t* ex) {
   return b < 0 ? 0 : ring_slot_bytes(*s, b);
 }
 
+namespace {
+// trace region of the persistent workspace: an int32 count, then events from +256
+int trace_capacity(const moe_shape_t& s, const WsLayout& L, const moe_exec_t* ex) {
+  const int b = chunk_log2_of(ex);
+  const int cpm = b < 0 ? 1 : (kGemmBM >> b);
+  const int NT1 = (s.F + kGemmBN / 2 - 1) / (kGemmBN / 2), NT2 = (s.d + kGemmBN - 1) / kGemmBN;
+  const int64_t cap = int64_t(L.max_mtiles) * (cpm + 1 + NT1 + NT2) + 2 * 4096;
+  return cap > (int64_t(1) << 30) ? (1 << 30) : int(cap);
+}
+size_t trace_bytes(const moe_shape_t& s, const WsLayout& L, const moe_exec_t* ex) {
+  return align256(256 + size_t(trace_capacity(s, L, ex)) * sizeof(moe_trace_event_t));
+}
+}  // namespace
+
 size_t moe_persistent_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex) {
-  (void)ex;
   if (check_shape(s, p) != MOE_OK) return 0;
-  return ws_layout(*s, p->E_local).hbuf;      // everything except the unfused h staging
+  const WsLayout L = ws_layout(*s, p->E_local);
+  return L.hbuf + ((ex && ex->trace) ? trace_bytes(*s, L, ex) : 0);   // no h staging
+}
+
+int moe_persistent_trace_info(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex, size_t* offset,
+                              int32_t* capacity, int32_t* ticks_per_us) {
+  if (check_shape(s, p) != MOE_OK || !ex || ex->trace != 1 || !offset || !capacity || !ticks_per_us)
+    return MOE_EINVAL;
+  const WsLayout L = ws_layout(*s, p->E_local);
+  *offset = L.hbuf;
+  *capacity = trace_capacity(*s, L, ex);
+  *ticks_per_us = static_cast<int32_t>(wall_ticks_per_us());
+  return MOE_OK;
+}
+
+namespace {
+// Checks shared by the persistent entry points and the launch plan they derive; every
+// check runs before the first HIP call.
+struct PersistSetup {
+  WsLayout L;
+  sched::Plan plan;
+  long long slot_bytes, budget;
+  int blk_log2, cus;
+  bool tracing;
+};
+
+int persist_setup(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex, const void* const* x,
+                  const void* w1, const void* w3, const void* w2, const void* ring, size_t ring_bytes,
+                  void* const* recv, const void* ws, size_t ws_bytes, PersistSetup* out) {
+  int rc = check_shape(s, p);
+  if (rc) return rc;
+  if (s->dtype != MOE_BF16) return MOE_EUNSUP;
+  const void* bufs[] = {w1, w3, w2};
+  for (const void* b : bufs)
+    if (!aligned16(b)) return b ? MOE_EALIGN : MOE_EINVAL;
+  if (!ring) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(ring) & 255) return MOE_EALIGN;
+  if ((rc = check_ptr_table(x, s->R)) || (rc = check_ptr_table(recv, s->R))) return rc;
+  if (ex && (ex->minibatch_rows < 0 || ex->comm_cus < 0 || ex->ring_slots < 0 || ex->trace < 0 || ex->trace > 1))
+    return MOE_EINVAL;
+  out->blk_log2 = chunk_log2_of(ex);
+  if (out->blk_log2 < 0) return MOE_EUNSUP;
+  out->L = ws_layout(*s, p->E_local);
+  if (!ws) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return MOE_EALIGN;
+  out->tracing = ex && ex->trace == 1;
+  if (ws_bytes < out->L.hbuf + (out->tracing ? trace_bytes(*s, out->L, ex) : 0)) return MOE_ENOSPC;
+  const int cpm = kGemmBM >> out->blk_log2;
+  out->slot_bytes = static_cast<long long>(ring_slot_bytes(*s, out->blk_log2));
+  long long slots = static_cast<long long>(ring_bytes / size_t(out->slot_bytes));
+  if (ex && ex->ring_slots > 0 && ex->ring_slots < slots) slots = ex->ring_slots;
+  if (slots > kMaxRingSlots) slots = kMaxRingSlots;
+  if (slots < cpm) return MOE_ENOSPC;                     // one row tile must fit
+  out->cus = cu_count();
+  const int comm_req = (ex && ex->comm_cus > 0) ? ex->comm_cus : 16;
+  // eight pipelines (one per XCD) only on the whole chip: 256 CUs in eight XCDs, workgroup w
+  // on XCD w mod 8
+  out->plan = sched::plan_persistent(out->cus, out->cus == 256, slots, cpm, comm_req);
+  if (!out->plan.ok) return MOE_EINVAL;                   // no CU left for the expert GEMMs
+  const long long us = (ex && ex->watchdog_us > 0) ? static_cast<long long>(ex->watchdog_us) : 2000000LL;
+  out->budget = us * wall_ticks_per_us();
+  return MOE_OK;
+}
+
+int persist_launch(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex, const PersistSetup& P,
+                   const void* const* x, const void* w1, const void* w3, const void* w2, void* ring,
+                   const int32_t* pull_src, const int32_t* slot_of, const int32_t* offsets, void* const* recv,
+                   void* ws, hipStream_t st) {
+  char* wsc = static_cast<char*>(ws);
+  moe_trace_event_t* trace = P.tracing ? reinterpret_cast<moe_trace_event_t*>(wsc + P.L.hbuf + 256) : nullptr;
+  int32_t* trace_count = P.tracing ? reinterpret_cast<int32_t*>(wsc + P.L.hbuf) : nullptr;
+  return hip_rc(launch_persistent(*s, p->E_local, x, w1, w3, w2, pull_src, slot_of, offsets, static_cast<char*>(ring),
+                                  P.slot_bytes, P.blk_log2, P.plan, P.cus, P.budget, recv, wsc, P.L, trace,
+                                  trace_count, P.tracing ? trace_capacity(*s, P.L, ex) : 0, st));
+}
+
+int persist_occupancy_ok() {
+  int occ = 0;
+  if (persistent_occupancy(&occ) != hipSuccess) return MOE_EHIP;
+  return occ < 1 ? MOE_EUNSUP : MOE_OK;                   // one workgroup per CU must fit
+}
+}  // namespace
+
+int moe_persistent_dispatch_ffn_combine(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+                                        const void* const* x, const void* w1, const void* w3, const void* w2,
+                                        void* ring, size_t ring_bytes, const int32_t* pull_src,
+                                        const int32_t* slot_of, const int32_t* offsets, void* const* recv, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  PersistSetup P;
+  int rc = persist_setup(s, p, ex, x, w1, w3, w2, ring, ring_bytes, recv, ws, ws_bytes, &P);
+  if (rc) return rc;
+  if (!pull_src || !slot_of || !offsets) return MOE_EINVAL;
+  if ((rc = persist_occupancy_ok())) return rc;
+  return persist_launch(s, p, ex, P, x, w1, w3, w2, ring, pull_src, slot_of, offsets, recv, ws,
+                        static_cast<hipStream_t>(stream));
 }
 
 int moe_forward_persistent(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
@@ -383,62 +494,18 @@ int moe_forward_persistent(const moe_shape_t* s, const moe_placement_t* p, const
                            const void* w2, void* ring, size_t ring_bytes, void* const* recv, void* const* y,
                            int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* pull_src,
                            int32_t* slot_of, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_shape(s, p);
+  PersistSetup P;
+  int rc = persist_setup(s, p, ex, x, w1, w3, w2, ring, ring_bytes, recv, ws, ws_bytes, &P);
   if (rc) return rc;
-  if (s->dtype != MOE_BF16) return MOE_EUNSUP;
   if (!p->expert_to_local || !topk_idx || !topk_w || !counts || !offsets || !pull_src || !slot_of)
     return MOE_EINVAL;
-  const void* bufs[] = {w1, w3, w2};
-  for (const void* b : bufs)
-    if (!aligned16(b)) return b ? MOE_EALIGN : MOE_EINVAL;
-  if (!ring) return MOE_EINVAL;
-  if (reinterpret_cast<uintptr_t>(ring) & 255) return MOE_EALIGN;
-  if ((rc = check_ptr_table(logits, s->R)) || (rc = check_ptr_table(x, s->R)) ||
-      (rc = check_ptr_table(recv, s->R)) || (rc = check_ptr_table(y, s->R)))
-    return rc;
-  if (ex && (ex->minibatch_rows < 0 || ex->comm_cus < 0 || ex->ring_slots < 0)) return MOE_EINVAL;
-  const int blk_log2 = chunk_log2_of(ex);
-  if (blk_log2 < 0) return MOE_EUNSUP;
-  const WsLayout L = ws_layout(*s, p->E_local);
-  if (reinterpret_cast<uintptr_t>(ws) & 255) return ws ? MOE_EALIGN : MOE_EINVAL;
-  if (!ws) return MOE_EINVAL;
-  if (ws_bytes < L.hbuf) return MOE_ENOSPC;
-
-  const int cpm = kGemmBM >> blk_log2;
-  const long long slot_bytes = static_cast<long long>(ring_slot_bytes(*s, blk_log2));
-  long long slots = static_cast<long long>(ring_bytes / size_t(slot_bytes));
-  if (ex && ex->ring_slots > 0 && ex->ring_slots < slots) slots = ex->ring_slots;
-  if (slots > kMaxRingSlots) slots = kMaxRingSlots;
-  if (slots < cpm) return MOE_ENOSPC;                     // one row tile must fit
-  const int cus = cu_count();
-  const int comm_req = (ex && ex->comm_cus > 0) ? ex->comm_cus : 32;
-  // pipelines: one per XCD when every XCD gets a slot share that holds a row tile
-  int n_part = 1;
-  if (cus == 256) {
-    for (int np = 8; np >= 1; np >>= 1) {
-      const int comm_pp = comm_req / np > 0 ? comm_req / np : 1;
-      if (slots / np >= cpm && comm_pp < cus / np) { n_part = np; break; }
-    }
-  }
-  const int comm_pp = comm_req / n_part > 0 ? comm_req / n_part : 1;
-  if (comm_pp >= cus / n_part) return MOE_EINVAL;         // no CU left for expert compute
-  const long long us = (ex && ex->watchdog_us > 0) ? static_cast<long long>(ex->watchdog_us) : 2000000LL;
-  const long long budget = us * wall_ticks_per_us();
-
-  // Switched off: the one GPU run of this path (cooperative launch, eight per-XCD
-  // pipelines) did not complete although every device wait is bounded by the watchdog;
-  // the cause is not yet shown, so nothing is launched until it is.
-  if (!kPersistentEnabled) return MOE_EUNSUP;
-
+  if ((rc = check_ptr_table(logits, s->R)) || (rc = check_ptr_table(y, s->R))) return rc;
+  if ((rc = persist_occupancy_ok())) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  char* wsc = static_cast<char*>(ws);
   hipError_t e = launch_layout(*s, p->expert_to_local, p->E_local, minibatch_of(ex), logits, topk_idx, topk_w, counts,
-                               offsets, pull_src, slot_of, wsc, L, st);
+                               offsets, pull_src, slot_of, static_cast<char*>(ws), P.L, st);
   if (e != hipSuccess) return MOE_EHIP;
-  e = launch_persistent(*s, p->E_local, x, w1, w3, w2, pull_src, slot_of, offsets, static_cast<char*>(ring),
-                        slot_bytes, static_cast<int>(slots / n_part * n_part), blk_log2, comm_pp * n_part, n_part, cus,
-                        budget, recv, wsc, L, st);
-  if (e != hipSuccess) return MOE_EHIP;
+  if ((rc = persist_launch(s, p, ex, P, x, w1, w3, w2, ring, pull_src, slot_of, offsets, recv, ws, st))) return rc;
   return hip_rc(launch_merge(*s, slot_of, topk_w, recv, y, cu_count(), st));
 }
 
@@ -691,6 +758,7 @@ const char* moe_strerror(int code) {
     case MOE_EHIP: return "HIP launch failed";
     case MOE_ETIMEOUT: return "device wait exceeded its watchdog budget";
     case MOE_EUNSUP: return "combination not supported by this build";
+    case MOE_EINCOMPLETE: return "persistent kernel ended with work left undone (a pipeline got no workgroup)";
     default: return "unknown error";
   }
 }

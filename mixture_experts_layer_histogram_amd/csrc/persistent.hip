@@ -1,50 +1,42 @@
-// Persistent forward for gfx950: pull dispatch, grouped SwiGLU FFN and push combine in
-// one kernel, with the CUs split into a data-movement partition and a compute partition
-// that signal each other through device-resident counters and a fixed ring of slots.
+// Persistent forward for gfx950: pull dispatch into a fixed ring, the grouped SwiGLU FFN and
+// the push combine in one kernel, with the CUs split into a data-movement partition and a
+// compute partition that signal each other through device-resident counters.
 //
 // Operation (MoK article, kucoin.com/es "Cursor's MoK logra un aumento del 2.37x ...",
 // section 02: one megakernel whose SMs are split between communication and expert
 // compute, GPU-local counters in both directions, tokens released a minibatch at a time,
-// and a fixed-size ring token buffer reused right after combine so the combine of one
-// macrobatch overlaps the dispatch of the next; qubstore.ru "Смесь котят ...", ring buffer
-// and megakernel paragraphs: no CPU in the loop, a buffer of a few hundred MB instead of
-// worst-case staging).
+// and a fixed-size ring token buffer reused right after combine, so the combine of one
+// batch overlaps the dispatch of the next; qubstore.ru "Смесь котят ...", ring buffer and
+// megakernel paragraphs: no CPU in the loop, a buffer of a few hundred MB instead of
+// worst-case staging).  The scheduling rules (pipelines, groups, ticket order, slot reuse,
+// mover claims) are persist_sched.hpp, shared with a host-threaded model of this kernel.
 //
 // MI355X design:
-// * Pipelines per XCD.  The eight XCDs' L2 caches are not coherent with one another, and
-//   an agent-scope release/acquire on gfx950 writes back / invalidates the whole L2
-//   (buffer_wbl2 / buffer_inv sc1).  The row tiles are therefore split into P contiguous
-//   ranges, one pipeline per XCD (workgroup w runs on XCD w mod 8; the kernel reads the
-//   XCC id from the hardware), each with its own ring partition and counters.  Every
-//   producer -> consumer hand-off then stays inside one L2: the producer waits for its
-//   stores (vmcnt 0) and bumps a counter atomically; the consumer polls the counter and
-//   invalidates its CU's L1 (buffer_inv sc0).  When the ring is too small for eight
-//   partitions, pipelines span XCDs and every hand-off uses agent-scope release/acquire.
-// * Roles.  The first comm_per_part workgroups of a pipeline move data: they claim, in
-//   order, the next chunk whose ring slot is free (gather its rows from the source
-//   buffers) or the next row tile whose down GEMM is complete (push its rows to recv and
-//   free its slots), never blocking while holding a claim.  The others take GEMM tasks
-//   from the pipeline's ticket: for each 256-row tile, its gate/up tiles, then its down
-//   tiles.  A gate/up tile waits for its chunks; a down tile waits for all gate/up tiles of
-//   its row tile and writes its output in place over the ring rows it no longer needs.
-// * Ring.  A slot holds one chunk (1 << blk_log2 rows) of token rows (later the expert
-//   output) plus its h rows.  Chunk q of a pipeline uses slot q mod S_p; it may be
-//   gathered once the chunk S_p before it has been pushed.  S_p >= chunks per row tile
-//   makes progress certain: the chunks a task waits for never wait on that task.
+// * Launch.  An ordinary launch of one 512-thread workgroup per CU with 128 KiB of LDS (the
+//   launch shape of the grouped GEMM kernels).  No grid-wide barrier is used, so nothing
+//   needs a cooperative launch.  Roles go by arrival order inside a pipeline, so the first
+//   workgroups to run are the movers; compute workgroups take tickets in order and a task
+//   waits only for movers or smaller tickets, so progress does not depend on every
+//   workgroup being resident at once.
+// * Pipelines per XCD.  The eight XCDs' L2 caches are not coherent with one another, and an
+//   agent-scope release/acquire writes back / invalidates a whole L2.  With a ring large
+//   enough, the row tiles are split into eight pipelines, one per XCD (the kernel reads the
+//   XCC id from the hardware), each with its own ring partition and counters: every
+//   producer -> consumer hand-off stays inside one L2 (stores waited for, then a relaxed
+//   counter bump; the consumer invalidates its CU's L1).  Otherwise pipelines span XCDs and
+//   hand-offs use agent-scope release/acquire.
+// * Ring slot.  One minibatch (chunk) of token rows, overwritten in place by the expert
+//   outputs of those rows, followed by the rows' h.
 // * Watchdog.  Every wait is bounded by a wall-clock budget; on expiry the workgroup sets
-//   the status word (MOE_ETIMEOUT) and an abort flag that every loop checks, so all
-//   workgroups exit.
+//   the status word (MOE_ETIMEOUT) and an abort word that every loop checks, so all
+//   workgroups exit.  A check kernel afterwards reports MOE_EINCOMPLETE if any pipeline's
+//   work was left undone (e.g. a pipeline that received no workgroup).
 #include "gemm_tile.hpp"
+#include "persist_sched.hpp"
 
 namespace moe {
 
-// control block (int32 words, zeroed by persist_init_kernel before every launch)
-enum PersistCtrl {
-  kPcAbort = 0,
-  kPcPipe = 16,          // 8 words per pipeline: join, gather_next, combine_next, task_next
-  kPcPipeStride = 8,
-  kPcArrays = 128,       // then: filled[chunks], g1_done[mtiles], g2_done[mtiles], slot_epoch[slots]
-};
+using sched::CtrlLayout;
 
 struct PersistArgs {
   RankPtrs<const char*> x;
@@ -53,22 +45,30 @@ struct PersistArgs {
   const int32_t* slot_of;
   const int32_t* offsets;
   const int32_t* mtile_base;
-  const int32_t* ctrl;          // layout control words (row tiles)
+  const int32_t* ctrl;          // layout control words (row tile count)
   const uint16_t* w1;
   const uint16_t* w3;
   const uint16_t* w2;
   char* ring;
   int32_t* pc;                  // persistent control block
-  int32_t* ws_status;           // the workspace status word: a watchdog expiry writes MOE_ETIMEOUT
+  int32_t* status;              // the workspace status word
+  moe_trace_event_t* trace;     // null: no trace
+  int32_t* trace_count;
+  int trace_cap;
   long long slot_bytes;
   long long budget;             // wall-clock ticks per wait
   int T, k, d, F, El;
   int blk_log2, cpm;            // chunk rows (log2) and chunks per 256-row tile
-  int n_part, light;            // pipelines; 1 = every pipeline on one XCD
-  int comm_per_part;
-  int slots_per_part;
-  int max_mtiles;
-  int lookahead;                // 1: gate/up tiles of row tile i+1 go before the down tiles of i
+  int n_part, light, comm_pp, S, G, lookahead;
+  CtrlLayout cl;
+};
+
+struct DevOps {
+  int32_t* pc;
+  __device__ int ld(int w) const { return __hip_atomic_load(pc + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+  __device__ bool cas(int w, int expected, int desired) const {
+    return atomicCAS(pc + w, expected, desired) == expected;
+  }
 };
 
 __device__ __forceinline__ int ld_relaxed(const int32_t* p) {
@@ -85,28 +85,29 @@ __device__ __forceinline__ void release_add(int32_t* ctr, int v, bool light) {
   }
 }
 
-// Consumer side, after thread 0 observed the counter: make the producer's data visible.
+// Consumer side, after the workgroup observed the counter: make the producer's data visible.
 __device__ __forceinline__ void acquire_after_poll(bool light) {
-  if (light) {
-    asm volatile("buffer_inv sc0" ::: "memory");      // this CU's L1; the L2 is shared
-  } else {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
+  if (light) asm volatile("buffer_inv sc0" ::: "memory");     // this CU's L1; the L2 is shared
+  else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-// Thread 0 waits until *p >= target (or abort / watchdog); returns false on abort.
-// Block-uniform result via LDS.
+__device__ __forceinline__ void set_abort(const PersistArgs& A, int code) {
+  __hip_atomic_store(A.status, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(A.pc + A.cl.abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0 waits until *p >= target (or abort / watchdog); the result is block-uniform
+// (broadcast through LDS).  Every thread of the workgroup calls it.
 __device__ bool wait_ge(const int32_t* p, int target, const PersistArgs& A, int* sh_flag) {
   if (threadIdx.x == 0) {
     int ok = 1;
     if (ld_relaxed(p) < target) {
       const long long t0 = wall_clock64();
       while (ld_relaxed(p) < target) {
-        if (ld_relaxed(A.pc + kPcAbort)) { ok = 0; break; }
+        if (ld_relaxed(A.pc + A.cl.abort_word)) { ok = 0; break; }
         __builtin_amdgcn_s_sleep(1);
         if (wall_clock64() - t0 > A.budget) {
-          __hip_atomic_store(A.ws_status, MOE_ETIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(A.pc + kPcAbort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          set_abort(A, MOE_ETIMEOUT);
           ok = 0;
           break;
         }
@@ -120,96 +121,153 @@ __device__ bool wait_ge(const int32_t* p, int target, const PersistArgs& A, int*
   return ok;
 }
 
-// 16-byte row copy by one wave
-__device__ __forceinline__ void wave_copy_row(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int n16,
-                                              int lane) {
-  for (int base = 0; base < n16; base += 64 * 8) {
-    u32x4 v[8];
+__device__ __forceinline__ void trace_event(const PersistArgs& A, int kind, int idx, int pipe, long long t_begin,
+                                            long long t_end, long long t_wait) {
+  if (!A.trace || threadIdx.x != 0) return;
+  const int i = atomicAdd(A.trace_count, 1);
+  if (i >= A.trace_cap) return;
+  moe_trace_event_t ev;
+  ev.t_begin = t_begin;
+  ev.t_end = t_end;
+  ev.t_wait = static_cast<int32_t>(t_wait > 0x7fffffffLL ? 0x7fffffffLL : t_wait);
+  ev.index = idx;
+  ev.workgroup = static_cast<int32_t>(blockIdx.x);
+  ev.kind = static_cast<int16_t>(kind);
+  ev.pipeline = static_cast<int16_t>(pipe);
+  A.trace[i] = ev;
+}
+
+// Copy nrows rows of n16 16-byte vectors from src[r] to dst[r] (row addresses staged in
+// LDS) with the whole workgroup, 16 vectors in flight per thread.
+__device__ void wg_copy_rows(const uint64_t* src, const uint64_t* dst, int nrows, int n16) {
+  constexpr int U = 16;
+  const int total = nrows * n16;
+  for (int base = 0; base < total; base += kGemmThreads * U) {
+    u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * 64 + lane;
-      if (i < n16) v[u] = src[i];
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * kGemmThreads + int(threadIdx.x);
+      if (i < total) {
+        const int r = i / n16;
+        v[u] = reinterpret_cast<const u32x4*>(src[r])[i - r * n16];
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * 64 + lane;
-      if (i < n16) dst[i] = v[u];
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * kGemmThreads + int(threadIdx.x);
+      if (i < total) {
+        const int r = i / n16;
+        reinterpret_cast<u32x4*>(dst[r])[i - r * n16] = v[u];
+      }
     }
   }
 }
 
-__global__ void persist_init_kernel(int32_t* pc, int words) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < words; i += gridDim.x * blockDim.x) pc[i] = 0;
+// Zero the control block and build every pipeline's group and phase tables (one block).
+__global__ __launch_bounds__(1024) void persist_prep_kernel(PersistArgs A, int zero_words) {
+  for (int i = threadIdx.x; i < zero_words; i += blockDim.x) A.pc[i] = 0;
+  if (A.trace && threadIdx.x == 0) *A.trace_count = 0;
+  __syncthreads();
+  const int p = threadIdx.x;
+  if (p >= A.n_part) return;
+  const int n_mt = A.ctrl[kCtrlMTiles];
+  int lo, hi;
+  sched::pipe_range(n_mt, A.n_part, p, &lo, &hi);
+  int32_t* gf = A.pc + A.cl.grp_first + lo;
+  int32_t* gl = A.pc + A.cl.grp_len + lo;
+  const int32_t* mtb = A.mtile_base;
+  const int El = A.El;
+  const int n = sched::build_groups(lo, hi, A.G, [&](int m) { return find_expert(mtb, El, m); }, gf, gl);
+  const int NT1 = (A.F + kGemmBN / 2 - 1) / (kGemmBN / 2);
+  const int NT2 = (A.d + kGemmBN - 1) / kGemmBN;
+  const int tickets = n ? sched::build_phases(n, gl, NT1, NT2, A.lookahead != 0, A.pc + A.cl.phase_start + 2 * lo + p)
+                        : 0;
+  int32_t* pw = A.pc + A.cl.pipe0 + p * sched::kPipeWords;
+  pw[sched::kNGroups] = n;
+  pw[sched::kNTickets] = tickets;
+  pw[sched::kLo] = lo;
+  pw[sched::kHi] = hi;
+}
+
+// After the persistent kernel: every pipeline must have claimed all its gathers, pushes and
+// tickets; otherwise (and unless a watchdog already reported) MOE_EINCOMPLETE.
+__global__ void persist_check_kernel(PersistArgs A) {
+  const int p = threadIdx.x;
+  bool bad = false;
+  if (p < A.n_part) {
+    const int32_t* pw = A.pc + A.cl.pipe0 + p * sched::kPipeWords;
+    const int n_m = pw[sched::kHi] - pw[sched::kLo];
+    bad = pw[sched::kGatherNext] < n_m * A.cpm || pw[sched::kPushNext] < n_m ||
+          pw[sched::kTicketNext] < pw[sched::kNTickets];
+  }
+  if (__any(bad) && threadIdx.x == 0 && *A.status == MOE_OK) *A.status = MOE_EINCOMPLETE;
 }
 
 __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(PersistArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int sh[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
+  const long long t_start = wall_clock64();
 
   unsigned xcc;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
   const int p = int(xcc & 7) * A.n_part / 8;
   const bool light = A.light;
-  int32_t* pipe = A.pc + kPcPipe + p * kPcPipeStride;
-  int32_t* filled = A.pc + kPcArrays;
-  int32_t* g1_done = filled + A.max_mtiles * 4;
-  int32_t* g2_done = g1_done + A.max_mtiles;
-  int32_t* slot_epoch = g2_done + A.max_mtiles;
+  const int pbase = A.cl.pipe0 + p * sched::kPipeWords;
+  int32_t* pw = A.pc + pbase;
+  int32_t* filled = A.pc + A.cl.filled;
+  int32_t* g1_done = A.pc + A.cl.g1_done;
+  int32_t* g2_done = A.pc + A.cl.g2_done;
+  int32_t* slot_epoch = A.pc + A.cl.slot_epoch + p * A.S;
 
-  if (tid == 0) sh[0] = __hip_atomic_fetch_add(pipe + 0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) sh[0] = __hip_atomic_fetch_add(pw + sched::kJoin, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int rank = sh[0];
   __syncthreads();
+  const bool mover = rank < A.comm_pp;
+  trace_event(A, 0, mover ? 0 : 1, p, t_start, t_start, 0);
 
-  // this pipeline's row tiles [m_lo, m_hi)
-  const int n_mt = A.ctrl[kCtrlMTiles];
-  const int per = (n_mt + A.n_part - 1) / A.n_part;
-  const int m_lo = min(n_mt, p * per), m_hi = min(n_mt, m_lo + per);
-  const int n_m = m_hi - m_lo;
-  const int n_chunks = n_m * A.cpm;
-  const int S = A.slots_per_part;
+  // this pipeline's row tiles [lo, hi) and tables (written by the preparation kernel)
+  const int lo = pw[sched::kLo], hi = pw[sched::kHi];
+  const int n_m = hi - lo;
+  const int n_groups = pw[sched::kNGroups], n_tickets = pw[sched::kNTickets];
+  const int S = A.S, cpm = A.cpm;
   const int NT1 = (A.F + kGemmBN / 2 - 1) / (kGemmBN / 2);
-  const int NT2 = (A.d + kGemmBN - 1) / kGemmBN;
   const int chunk_rows = 1 << A.blk_log2;
   const int row_bytes = A.d * 2;
   const int n16 = row_bytes >> 4;
-  const long long xpart = (long long)chunk_rows * A.d * 2;   // token/output rows of a slot
+  const long long xpart = (long long)chunk_rows * row_bytes;   // token / output rows of a slot
 
-  auto slot_ptr = [&](int q) -> char* {                       // pipeline-local chunk q
-    return A.ring + (long long)(p * S + q % S) * A.slot_bytes;
+  auto slot_ptr = [&](int q) -> char* {                        // pipeline-local chunk q
+    return A.ring + (long long)(p * S + sched::chunk_slot(q, S)) * A.slot_bytes;
   };
-  auto tile_rows = [&](int m, int* row0, int* l) -> int {     // global row tile m
+  auto tile_rows = [&](int m, int* row0, int* l) -> int {      // global row tile m
     *l = find_expert(A.mtile_base, A.El, m);
     *row0 = A.offsets[*l] + (m - A.mtile_base[*l]) * kGemmBM;
     return min(kGemmBM, A.offsets[*l + 1] - *row0);
   };
 
-  if (rank < A.comm_per_part) {
+  if (mover) {
     // ------------------------------------------------------------ data movement
+    uint64_t* src_tab = reinterpret_cast<uint64_t*>(smem);
+    uint64_t* dst_tab = src_tab + kGemmBM;
+    const DevOps ops{A.pc};
     long long idle_since = wall_clock64();
     while (true) {
       if (tid == 0) {
-        int act = 0, arg = 0;      // 1 = combine row tile arg, 2 = gather chunk arg, 3 = done, 4 = abort
-        if (ld_relaxed(A.pc + kPcAbort)) act = 4;
-        const int ci = ld_relaxed(pipe + 2);
-        if (!act && ci < n_m && ld_relaxed(g2_done + m_lo + ci) == NT2) {
-          if (atomicCAS(pipe + 2, ci, ci + 1) == ci) { act = 1; arg = ci; }
-        }
-        const int qi = ld_relaxed(pipe + 1);
-        if (!act && qi < n_chunks && ld_relaxed(slot_epoch + p * S + qi % S) >= qi / S) {
-          if (atomicCAS(pipe + 1, qi, qi + 1) == qi) { act = 2; arg = qi; }
-        }
-        if (!act && ci >= n_m && qi >= n_chunks) act = 3;
-        if (!act) {
-          __builtin_amdgcn_s_sleep(1);
-          if (wall_clock64() - idle_since > A.budget) {
-            __hip_atomic_store(A.ws_status, MOE_ETIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(A.pc + kPcAbort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            act = 4;
-          }
+        int act = sched::kIdle, arg = 0;
+        if (ld_relaxed(A.pc + A.cl.abort_word)) {
+          act = sched::kDone;
         } else {
-          idle_since = wall_clock64();
+          act = sched::mover_claim(ops, A.cl, pbase, lo, n_m, cpm, S, (A.d + kGemmBN - 1) / kGemmBN,
+                                   A.cl.slot_epoch + p * S, &arg);
+          if (act == sched::kIdle) {
+            __builtin_amdgcn_s_sleep(1);
+            if (wall_clock64() - idle_since > A.budget) {
+              set_abort(A, MOE_ETIMEOUT);
+              act = sched::kDone;
+            }
+          }
         }
         sh[1] = act;
         sh[2] = arg;
@@ -217,15 +275,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
       __syncthreads();
       const int act = sh[1], arg = sh[2];
       __syncthreads();
-      if (act >= 3) break;
-      if (act == 0) continue;          // nothing claimable this round
-      if (act == 1) {
-        // push combine of row tile m_lo + arg: output rows (in place in the ring) -> recv
-        acquire_after_poll(light);
+      if (act == sched::kDone) break;
+      if (act == sched::kIdle) continue;
+      const long long t_b = wall_clock64();
+      acquire_after_poll(light);
+      if (act == sched::kPush) {
+        // row tile lo + arg: its output rows (in place in the ring) -> recv[rank][token][j]
         int row0, l;
-        const int m = m_lo + arg;
+        const int m = lo + arg;
         const int rows = tile_rows(m, &row0, &l);
-        for (int r = wave; r < rows; r += kGemmThreads / 64) {
+        for (int r = tid; r < rows; r += kGemmThreads) {
           const int s = row0 + r;
           const int rk = A.pull_src[2 * (long long)s];
           const int t = A.pull_src[2 * (long long)s + 1];
@@ -233,80 +292,79 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
           int j = 0;
           for (int jj = 0; jj < A.k; ++jj)
             if (so[jj] == s) j = jj;
-          const char* src = slot_ptr(arg * A.cpm + (r >> A.blk_log2)) + (long long)(r & (chunk_rows - 1)) * row_bytes;
-          wave_copy_row(reinterpret_cast<const u32x4*>(src),
-                        reinterpret_cast<u32x4*>(A.recv.p[rk] + ((long long)t * A.k + j) * row_bytes), n16, lane);
+          src_tab[r] = reinterpret_cast<uint64_t>(slot_ptr(arg * cpm + (r >> A.blk_log2)) +
+                                                  (long long)(r & (chunk_rows - 1)) * row_bytes);
+          dst_tab[r] = reinterpret_cast<uint64_t>(A.recv.p[rk] + ((long long)t * A.k + j) * row_bytes);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        wg_copy_rows(src_tab, dst_tab, rows, n16);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // the slot's reads are done
         __syncthreads();
         if (tid == 0)
-          for (int h = 0; h < A.cpm; ++h) {
-            const int q = arg * A.cpm + h;
-            if (light) __hip_atomic_fetch_add(slot_epoch + p * S + q % S, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            else __hip_atomic_fetch_add(slot_epoch + p * S + q % S, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-          }
-      } else {  // act == 2
-        // gather chunk arg: its rows of the row tile, pulled from the source buffers
-        if (!light) acquire_after_poll(light);
+          for (int h = 0; h < cpm; ++h)
+            __hip_atomic_fetch_add(slot_epoch + sched::chunk_slot(arg * cpm + h, S), 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        trace_event(A, 2, m, p, t_b, wall_clock64(), t_b - idle_since);
+      } else {
+        // chunk arg: rows [h * chunk_rows, ...) of row tile lo + arg / cpm, from the sources
         int row0, l;
-        const int m = m_lo + arg / A.cpm, h = arg % A.cpm;
+        const int m = lo + arg / cpm, h = arg % cpm;
         const int rows = tile_rows(m, &row0, &l);
         const int c_lo = h * chunk_rows, c_n = min(chunk_rows, rows - c_lo);
         char* dst = slot_ptr(arg);
-        for (int r = wave; r < c_n; r += kGemmThreads / 64) {
+        for (int r = tid; r < c_n; r += kGemmThreads) {
           const int s = row0 + c_lo + r;
           const int rk = A.pull_src[2 * (long long)s];
           const int t = A.pull_src[2 * (long long)s + 1];
-          wave_copy_row(reinterpret_cast<const u32x4*>(A.x.p[rk] + (long long)t * row_bytes),
-                        reinterpret_cast<u32x4*>(dst + (long long)r * row_bytes), n16, lane);
+          src_tab[r] = reinterpret_cast<uint64_t>(A.x.p[rk] + (long long)t * row_bytes);
+          dst_tab[r] = reinterpret_cast<uint64_t>(dst + (long long)r * row_bytes);
         }
-        release_add(filled + m * A.cpm + h, 1, light);
+        __syncthreads();
+        if (c_n > 0) wg_copy_rows(src_tab, dst_tab, c_n, n16);
+        release_add(filled + m * 4 + h, 1, light);
+        trace_event(A, 1, arg, p, t_b, wall_clock64(), t_b - idle_since);
       }
+      __syncthreads();                                          // the row tables are reused
+      idle_since = wall_clock64();
     }
-  } else {
+  } else if (n_tickets > 0) {
     // ------------------------------------------------------------ expert compute
-    const int n_tasks = n_m * (NT1 + NT2);
+    const int32_t* phase_start = A.pc + A.cl.phase_start + 2 * lo + p;
+    const int32_t* grp_first = A.pc + A.cl.grp_first + lo;
+    const int32_t* grp_len = A.pc + A.cl.grp_len + lo;
     while (true) {
-      if (tid == 0) sh[3] = __hip_atomic_fetch_add(pipe + 3, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) sh[3] = __hip_atomic_fetch_add(pw + sched::kTicketNext, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
-      const int task = sh[3];
+      const int ticket = sh[3];
       __syncthreads();
-      if (task >= n_tasks) break;
-      // task -> (row tile i, j < NT1: gate/up tile j, else down tile j - NT1)
-      int i, j;
-      if (!A.lookahead) {
-        i = task / (NT1 + NT2);
-        j = task % (NT1 + NT2);
-      } else if (task < NT1) {
-        i = 0;
-        j = task;
-      } else {
-        const int u = task - NT1, b = u / (NT1 + NT2), r = u % (NT1 + NT2);
-        if (b < n_m - 1 && r < NT1) { i = b + 1; j = r; }      // gate/up of the next row tile
-        else if (b < n_m - 1) { i = b; j = r; }                 // down of this row tile (r >= NT1)
-        else { i = b; j = NT1 + r; }                            // last block: down tiles only
-      }
-      const int m = m_lo + i;
+      if (ticket >= n_tickets) break;
+      const sched::Task tk = sched::task_of_ticket(ticket, n_groups, phase_start, grp_first, grp_len, A.lookahead != 0);
+      const int m = tk.m;
       int row0, l;
       const int rows = tile_rows(m, &row0, &l);
+      const long long t_w = wall_clock64();
       bool ok = true;
-      if (j < NT1) {
-        for (int h = 0; h < A.cpm && ok; ++h) ok = wait_ge(filled + m * A.cpm + h, 1, A, sh);
+      if (!tk.down) {
+        for (int h = 0; h < cpm && ok; ++h) ok = wait_ge(filled + m * 4 + h, 1, A, sh);
       } else {
         ok = wait_ge(g1_done + m, NT1, A, sh);
       }
       if (!ok) break;
+      const long long t_b = wall_clock64();
       acquire_after_poll(light);
-      char* s0 = slot_ptr(i * A.cpm + 0);
-      char* s1 = slot_ptr(i * A.cpm + min(1, A.cpm - 1));
-      char* s2 = slot_ptr(i * A.cpm + min(2, A.cpm - 1));
-      char* s3 = slot_ptr(i * A.cpm + min(3, A.cpm - 1));
+      const int q0 = (m - lo) * cpm;
+      char* s0 = slot_ptr(q0);
+      char* s1 = slot_ptr(q0 + min(1, cpm - 1));
+      char* s2 = slot_ptr(q0 + min(2, cpm - 1));
+      char* s3 = slot_ptr(q0 + min(3, cpm - 1));
       TileIO io;
       io.blk_log2 = A.blk_log2;
       io.rows = rows;
       io.row_dst = nullptr;
       io.row_src = nullptr;
-      if (j < NT1) {
+      io.dh = nullptr;
+      io.dab = nullptr;
+      if (!tk.down) {
         io.a0 = reinterpret_cast<const uint16_t*>(s0);
         io.a1 = reinterpret_cast<const uint16_t*>(s1);
         io.a2 = reinterpret_cast<const uint16_t*>(s2);
@@ -319,8 +377,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
         io.o_ld = A.F;
         const uint16_t* b0 = A.w1 + size_t(l) * A.F * A.d;
         const uint16_t* b1 = A.w3 + size_t(l) * A.F * A.d;
-        gemm_tile<0>(io, b0, b1, j * (kGemmBN / 2), A.F, A.d, smem, A.d);
+        gemm_tile<0>(io, b0, b1, tk.j * (kGemmBN / 2), A.F, A.d, smem, A.d);
         release_add(g1_done + m, 1, light);
+        trace_event(A, 3, m * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
       } else {
         io.a0 = reinterpret_cast<const uint16_t*>(s0 + xpart);
         io.a1 = reinterpret_cast<const uint16_t*>(s1 + xpart);
@@ -333,23 +392,35 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
         io.a_ld = A.F;
         io.o_ld = A.d;
         const uint16_t* b0 = A.w2 + size_t(l) * A.d * A.F;
-        gemm_tile<1>(io, b0, b0, (j - NT1) * kGemmBN, A.d, A.F, smem, A.F);
+        gemm_tile<1>(io, b0, b0, tk.j * kGemmBN, A.d, A.F, smem, A.F);
         release_add(g2_done + m, 1, light);
+        trace_event(A, 4, m * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
       }
     }
   }
+  trace_event(A, 5, mover ? 0 : 1, p, wall_clock64(), wall_clock64(), 0);
 }
 
 // ---------------------------------------------------------------------------- host side
-int persist_ctrl_words(int max_mtiles, int slots) { return kPcArrays + max_mtiles * 6 + slots; }
-int persist_ctrl_bytes(int max_mtiles) { return persist_ctrl_words(max_mtiles, kMaxRingSlots) * 4; }
+int persist_ctrl_words(int max_mtiles) { return sched::ctrl_layout(max_mtiles, kMaxRingSlots).words; }
+
+hipError_t persistent_occupancy(int* blocks_per_cu) {
+  static std::atomic<uint64_t> attr_set{0};
+  const hipError_t ea = once_per_device(attr_set, [] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(moe_persistent_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+  });
+  if (ea != hipSuccess) return ea;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, reinterpret_cast<const void*>(moe_persistent_kernel),
+                                                      kGemmThreads, kGemmLds);
+}
 
 hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x, const void* w1, const void* w3,
                              const void* w2, const int32_t* pull_src, const int32_t* slot_of,
-                             const int32_t* offsets, char* ring, long long slot_bytes, int slots, int blk_log2,
-                             int comm_cus, int n_part, int cus, long long budget, void* const* recv, char* ws,
-                             const WsLayout& L, hipStream_t st) {
-  int32_t* pc = reinterpret_cast<int32_t*>(ws + L.pctrl);
+                             const int32_t* offsets, char* ring, long long slot_bytes, int blk_log2,
+                             const sched::Plan& plan, int grid, long long budget, void* const* recv, char* ws,
+                             const WsLayout& L, moe_trace_event_t* trace, int32_t* trace_count, int trace_cap,
+                             hipStream_t st) {
   PersistArgs A{};
   for (int r = 0; r < s.R; ++r) {
     A.x.p[r] = static_cast<const char*>(x[r]);
@@ -360,12 +431,15 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
   A.offsets = offsets;
   A.mtile_base = reinterpret_cast<const int32_t*>(ws + L.mtile_base);
   A.ctrl = reinterpret_cast<const int32_t*>(ws + L.ctrl);
-  A.ws_status = reinterpret_cast<int32_t*>(ws + L.ctrl) + kCtrlStatus;
+  A.status = reinterpret_cast<int32_t*>(ws + L.ctrl) + kCtrlStatus;
   A.w1 = static_cast<const uint16_t*>(w1);
   A.w3 = static_cast<const uint16_t*>(w3);
   A.w2 = static_cast<const uint16_t*>(w2);
   A.ring = ring;
-  A.pc = pc;
+  A.pc = reinterpret_cast<int32_t*>(ws + L.pctrl);
+  A.trace = trace;
+  A.trace_count = trace_count;
+  A.trace_cap = trace_cap;
   A.slot_bytes = slot_bytes;
   A.budget = budget;
   A.T = s.T;
@@ -375,26 +449,26 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
   A.El = El;
   A.blk_log2 = blk_log2;
   A.cpm = kGemmBM >> blk_log2;
-  A.n_part = n_part;
-  A.light = (n_part == 8) ? 1 : 0;
-  A.comm_per_part = comm_cus / n_part;
-  A.slots_per_part = slots / n_part;
-  A.max_mtiles = L.max_mtiles;
-  A.lookahead = (A.slots_per_part >= 2 * A.cpm) ? 1 : 0;
+  A.n_part = plan.n_part;
+  A.light = plan.light;
+  A.comm_pp = plan.comm_pp;
+  A.S = plan.S;
+  A.G = plan.G;
+  A.lookahead = plan.lookahead;
+  A.cl = sched::ctrl_layout(L.max_mtiles, kMaxRingSlots);
 
-  static std::atomic<uint64_t> attr_set{0};
-  const hipError_t ea = once_per_device(attr_set, [] {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(moe_persistent_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-  });
-  if (ea != hipSuccess) return ea;
-  const int words = persist_ctrl_words(L.max_mtiles, slots);
-  hipLaunchKernelGGL(persist_init_kernel, dim3((words + 255) / 256), dim3(256), 0, st, pc, words);
-  hipError_t e = hipGetLastError();
+  int occ = 0;
+  hipError_t e = persistent_occupancy(&occ);
   if (e != hipSuccess) return e;
-  void* args[] = {&A};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(moe_persistent_kernel), dim3(cus),
-                                    dim3(kGemmThreads), args, kGemmLds, st);
+  const int zero_words = A.cl.slot_epoch + plan.n_part * plan.S;
+  hipLaunchKernelGGL(persist_prep_kernel, dim3(1), dim3(1024), 0, st, A, zero_words);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(moe_persistent_kernel, dim3(grid), dim3(kGemmThreads), kGemmLds, st, A);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(persist_check_kernel, dim3(1), dim3(64), 0, st, A);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -199,6 +199,15 @@ class DeviceProblem:
                                           self.y, self.topk_idx, self.topk_w, self.counts, self.offsets,
                                           self.pull_src, self.slot_of, self.ws, stream=stream, check=check)
 
+    def persistent_dfc(self, ex=None, stream=None, check=True):
+        """The persistent kernel alone (dispatch, FFN, push) after layout() with the same ex."""
+        if not hasattr(self, "ring"):
+            self.alloc_ring()
+        return moe.moe_persistent_dispatch_ffn_combine(self.shape, self.placement, ex if ex is not None else self.pex,
+                                                       self.x, self.w1, self.w3, self.w2, self.ring, self.pull_src,
+                                                       self.slot_of, self.offsets, self.recv, self.ws, stream=stream,
+                                                       check=check)
+
     def status(self, stream=None) -> int:
         return moe.moe_read_status(self.ws, stream)
 

@@ -18,13 +18,14 @@ MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
 DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
 MOE_MAX_RANKS = 64
 ERRORS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_ENOSPC", -4: "MOE_EHIP",
-          -5: "MOE_ETIMEOUT", -6: "MOE_EUNSUP"}
+          -5: "MOE_ETIMEOUT", -6: "MOE_EUNSUP", -7: "MOE_EINCOMPLETE"}
 
 # every symbol include/moe.h declares
 EXPORTS = ["moe_max_pairs", "moe_workspace_bytes", "moe_mx_quantize", "moe_layout", "moe_dispatch_pull",
            "moe_expert_ffn", "moe_expert_ffn_push", "moe_weighted_merge", "moe_combine_push", "moe_forward",
-           "moe_forward_fused", "moe_forward_persistent",
-           "moe_ring_slot_bytes", "moe_persistent_workspace_bytes", "moe_backward_workspace_bytes",
+           "moe_forward_fused", "moe_forward_persistent", "moe_persistent_dispatch_ffn_combine",
+           "moe_ring_slot_bytes", "moe_persistent_workspace_bytes", "moe_persistent_trace_info",
+           "moe_backward_workspace_bytes",
            "moe_combine_pull_reverse", "moe_expert_ffn_backward",
            "moe_dispatch_push_reverse", "moe_backward", "moe_backward_prepare_mx", "moe_backward_mx",
            "moe_signal_probe_bytes", "moe_signal_probe", "moe_read_status", "moe_strerror", "moe_version"]
@@ -86,10 +87,14 @@ def lib() -> ctypes.CDLL:
                                   VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_forward_persistent.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, SZ, VP, VP,
                                              VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_persistent_dispatch_ffn_combine.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, SZ, VP, VP, VP, VP, VP,
+                                                          SZ, VP]
         L.moe_ring_slot_bytes.argtypes = [S, EX]
         L.moe_ring_slot_bytes.restype = SZ
         L.moe_persistent_workspace_bytes.argtypes = [S, PL, EX]
         L.moe_persistent_workspace_bytes.restype = SZ
+        L.moe_persistent_trace_info.argtypes = [S, PL, EX, P(SZ), P(ctypes.c_int32), P(ctypes.c_int32)]
+        L.moe_persistent_trace_info.restype = I32
         L.moe_backward_workspace_bytes.argtypes = [S, PL]
         L.moe_backward_workspace_bytes.restype = SZ
         L.moe_combine_pull_reverse.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, SZ, VP, SZ, VP]
@@ -109,7 +114,8 @@ def lib() -> ctypes.CDLL:
         L.moe_version.restype = ctypes.c_char_p
         for f in ("moe_mx_quantize", "moe_layout", "moe_dispatch_pull", "moe_expert_ffn", "moe_combine_push",
                   "moe_expert_ffn_push", "moe_weighted_merge", "moe_forward_fused",
-                  "moe_forward", "moe_forward_persistent", "moe_combine_pull_reverse", "moe_expert_ffn_backward", "moe_dispatch_push_reverse", "moe_backward", "moe_backward_prepare_mx",
+                  "moe_forward", "moe_forward_persistent", "moe_persistent_dispatch_ffn_combine",
+                  "moe_combine_pull_reverse", "moe_expert_ffn_backward", "moe_dispatch_push_reverse", "moe_backward", "moe_backward_prepare_mx",
                   "moe_backward_mx", "moe_read_status"):
             getattr(L, f).restype = I32
         _lib = L
@@ -258,6 +264,17 @@ def moe_forward_persistent(shape, placement, ex, logits, x, w1, w3, w2, ring, re
     return _check(rc, "moe_forward_persistent") if check else rc
 
 
+def moe_persistent_dispatch_ffn_combine(shape, placement, ex, x, w1, w3, w2, ring, pull_src, slot_of, offsets, recv,
+                                        ws, ring_bytes=None, ws_bytes=None, stream=None, check=True):
+    rc = lib().moe_persistent_dispatch_ffn_combine(ctypes.byref(shape), ctypes.byref(placement),
+                                                   ctypes.byref(ex) if ex is not None else None, _table(x), _p(w1),
+                                                   _p(w3), _p(w2), _p(ring),
+                                                   ring.numel() if ring_bytes is None else ring_bytes,
+                                                   _p(pull_src), _p(slot_of), _p(offsets), _table(recv), _p(ws),
+                                                   ws.numel() if ws_bytes is None else ws_bytes, _stream(stream))
+    return _check(rc, "moe_persistent_dispatch_ffn_combine") if check else rc
+
+
 def moe_ring_slot_bytes(shape: Shape, ex: Exec | None = None) -> int:
     return int(lib().moe_ring_slot_bytes(ctypes.byref(shape), ctypes.byref(ex) if ex is not None else None))
 
@@ -265,6 +282,33 @@ def moe_ring_slot_bytes(shape: Shape, ex: Exec | None = None) -> int:
 def moe_persistent_workspace_bytes(shape: Shape, placement: Placement, ex: Exec | None = None) -> int:
     return int(lib().moe_persistent_workspace_bytes(ctypes.byref(shape), ctypes.byref(placement),
                                                     ctypes.byref(ex) if ex is not None else None))
+
+
+# one moe_trace_event_t (include/moe.h), as a numpy structured dtype
+TRACE_EVENT_FIELDS = [("t_begin", "<i8"), ("t_end", "<i8"), ("t_wait", "<i4"), ("index", "<i4"),
+                      ("workgroup", "<i4"), ("kind", "<i2"), ("pipeline", "<i2")]
+TRACE_KINDS = {0: "start", 1: "gather", 2: "push", 3: "gate_up", 4: "down", 5: "end"}
+
+
+def moe_persistent_trace_info(shape: Shape, placement: Placement, ex: Exec):
+    """(byte offset of the trace in the workspace, event capacity, ticks per us)."""
+    off, cap, tpu = ctypes.c_size_t(), ctypes.c_int32(), ctypes.c_int32()
+    rc = lib().moe_persistent_trace_info(ctypes.byref(shape), ctypes.byref(placement), ctypes.byref(ex),
+                                         ctypes.byref(off), ctypes.byref(cap), ctypes.byref(tpu))
+    _check(rc, "moe_persistent_trace_info")
+    return int(off.value), int(cap.value), int(tpu.value)
+
+
+def read_trace(ws, shape: Shape, placement: Placement, ex: Exec):
+    """Copy the persistent kernel's trace out of the workspace tensor: (events, ticks per us).
+    Host-side parsing only (numpy structured array of the recorded events)."""
+    import numpy as np
+    off, cap, tpu = moe_persistent_trace_info(shape, placement, ex)
+    n = int(ws[off:off + 4].cpu().numpy().view(np.int32)[0])
+    n = min(n, cap)
+    dt = np.dtype(TRACE_EVENT_FIELDS)
+    raw = ws[off + 256: off + 256 + n * dt.itemsize].cpu().numpy()
+    return raw.view(dt).copy(), tpu
 
 
 def moe_backward_workspace_bytes(shape: Shape, placement: Placement) -> int:

@@ -1,0 +1,388 @@
+// Host-threaded model of the persistent forward kernel (csrc/persistent.hip): one host
+// thread per workgroup runs the kernel's control loop -- join, role by arrival order, the
+// movers' claim step and the compute workgroups' ticket loop with their waits -- through
+// the same scheduling code the device compiles (csrc/persist_sched.hpp), with random
+// delays in place of the copies and GEMM tiles.  Shadow state checks every hazard the
+// counters are meant to exclude:
+//   * a gather writes a slot only after the slot's previous chunk was pushed;
+//   * a gate/up tile starts only when every chunk of its row tile sits in its slot;
+//   * a down tile starts only after every gate/up tile of its row tile finished;
+//   * a push starts only after every down tile of its row tile finished, while the slots
+//     still hold that row tile;
+//   * every chunk, task and push runs exactly once, and every run ends (no deadlock).
+// It also checks the completion rule of the check kernel: a pipeline that receives no
+// workgroup is reported, one that receives workgroups never is.
+//
+// Build: g++ -O2 -std=c++17 -pthread persist_model.cpp -o persist_model
+// Run:   persist_model <seed> <cases>      (prints "OK <cases>" or the first violation)
+#include <atomic>
+#include <chrono>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+#include <random>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../mixture_experts_layer_histogram_amd/csrc/persist_sched.hpp"
+
+using namespace moe::sched;
+
+namespace {
+
+constexpr int kBM = 256;
+
+struct Fail {
+  std::mutex mu;
+  std::string first;
+  std::atomic<int> n{0};
+  void add(const std::string& s) {
+    if (n.fetch_add(1) == 0) {
+      std::lock_guard<std::mutex> g(mu);
+      first = s;
+    }
+  }
+};
+
+struct Case {
+  int El, cpm, NT1, NT2, cus, comm, wg_per_pipe_override;
+  bool eight_xcds;
+  long long slots;
+  std::vector<int> counts;         // rows per local expert
+  bool drop_pipeline;              // give one pipeline no workgroup at all
+};
+
+struct Ops {
+  std::atomic<int>* w;
+  int ld(int i) const { return w[i].load(std::memory_order_relaxed); }
+  bool cas(int i, int e, int d) const { return w[i].compare_exchange_strong(e, d); }
+};
+
+struct Model {
+  Case c;
+  Plan plan;
+  CtrlLayout cl;
+  std::vector<int> offsets, mtb;   // [El + 1]
+  int n_mt = 0, max_mtiles = 0;
+  std::vector<std::atomic<int>> pc;
+  std::atomic<int> abort_flag{0};
+  std::atomic<int> status{0};
+  // shadow state
+  std::vector<std::atomic<int>> slot_occ;     // [n_part * S]: chunk (pipeline-local) in the slot, -1 none
+  std::vector<std::atomic<int>> gathered;     // [n_mt * 4]
+  std::vector<std::atomic<int>> u_done, d_done, pushed, u_runs, d_runs, push_runs;   // per row tile
+  std::vector<std::atomic<int>> gather_runs;  // [n_mt * 4]
+  Fail* fail;
+  unsigned seed;
+
+  int expert_of(int m) const {     // the same binary search as find_expert
+    int lo = 0, hi = c.El - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (mtb[mid] <= m) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  }
+  int tile_rows(int m) const {
+    const int l = expert_of(m);
+    const int row0 = offsets[l] + (m - mtb[l]) * kBM;
+    return std::min(kBM, offsets[l + 1] - row0);
+  }
+
+  void prep() {                    // what persist_prep_kernel does
+    for (auto& a : pc) a.store(0);
+    for (int p = 0; p < plan.n_part; ++p) {
+      int lo, hi;
+      pipe_range(n_mt, plan.n_part, p, &lo, &hi);
+      std::vector<int> gf(std::max(1, hi - lo)), gl(std::max(1, hi - lo));
+      const int n = build_groups(lo, hi, plan.G, [&](int m) { return expert_of(m); }, gf.data(), gl.data());
+      std::vector<int> ps(2 * n + 1);
+      const int tickets = n ? build_phases(n, gl.data(), c.NT1, c.NT2, plan.lookahead != 0, ps.data()) : 0;
+      for (int g = 0; g < n; ++g) {
+        pc[cl.grp_first + lo + g].store(gf[g]);
+        pc[cl.grp_len + lo + g].store(gl[g]);
+      }
+      for (int k = 0; k <= 2 * n && n; ++k) pc[cl.phase_start + 2 * lo + p + k].store(ps[k]);
+      const int b = cl.pipe0 + p * kPipeWords;
+      pc[b + kNGroups].store(n);
+      pc[b + kNTickets].store(tickets);
+      pc[b + kLo].store(lo);
+      pc[b + kHi].store(hi);
+    }
+  }
+
+  void delay(std::mt19937& rng, int max_us) {
+    const int us = int(rng() % (max_us + 1));
+    if (us == 0) std::this_thread::yield();
+    else std::this_thread::sleep_for(std::chrono::microseconds(us));
+  }
+
+  bool wait_ge(int word, int target) {
+    const auto t0 = std::chrono::steady_clock::now();
+    while (pc[word].load(std::memory_order_acquire) < target) {
+      if (abort_flag.load()) return false;
+      std::this_thread::yield();
+      if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(10)) {
+        fail->add("watchdog: a wait did not end within 10 s (deadlock)");
+        abort_flag.store(1);
+        return false;
+      }
+    }
+    return true;
+  }
+
+  void workgroup(int p, unsigned wseed) {
+    std::mt19937 rng(wseed);
+    const int pb = cl.pipe0 + p * kPipeWords;
+    const int rank = pc[pb + kJoin].fetch_add(1);
+    const int lo = pc[pb + kLo].load(), hi = pc[pb + kHi].load();
+    const int n_m = hi - lo, S = plan.S, cpm = c.cpm;
+    const int slot_base = cl.slot_epoch + p * S;
+    Ops ops{pc.data()};
+    if (rank < plan.comm_pp) {
+      auto idle_since = std::chrono::steady_clock::now();
+      while (true) {
+        if (abort_flag.load()) break;
+        int arg = 0;
+        const int act = mover_claim(ops, cl, pb, lo, n_m, cpm, S, c.NT2, p * S, &arg);
+        if (act == kDone) break;
+        if (act == kIdle) {
+          std::this_thread::yield();
+          if (std::chrono::steady_clock::now() - idle_since > std::chrono::seconds(10)) {
+            fail->add("watchdog: a mover idled 10 s (deadlock)");
+            abort_flag.store(1);
+            break;
+          }
+          continue;
+        }
+        if (act == kPush) {
+          const int m = lo + arg;
+          if (d_done[m].load() != c.NT2) fail->add("push before all down tiles finished, tile " + std::to_string(m));
+          for (int h = 0; h < cpm; ++h) {
+            const int q = arg * cpm + h;
+            if (slot_occ[p * S + chunk_slot(q, S)].load() != q)
+              fail->add("push: slot no longer holds chunk " + std::to_string(q));
+          }
+          if (push_runs[m].fetch_add(1) != 0) fail->add("row tile pushed twice");
+          delay(rng, 30);
+          pushed[m].store(1);
+          for (int h = 0; h < cpm; ++h) pc[slot_base + chunk_slot(arg * cpm + h, S)].fetch_add(1);
+        } else {
+          const int q = arg, m = lo + q / cpm, h = q % cpm;
+          const int s = chunk_slot(q, S);
+          const int prev = slot_occ[p * S + s].load();
+          if (q >= S) {
+            if (prev != q - S) fail->add("gather: slot's previous chunk is not q - S");
+            if (!pushed[lo + (q - S) / cpm].load()) fail->add("gather into a slot whose chunk is not pushed yet");
+          } else if (prev != -1) {
+            fail->add("gather: first use of a slot that is occupied");
+          }
+          slot_occ[p * S + s].store(q);
+          if (gather_runs[m * 4 + h].fetch_add(1) != 0) fail->add("chunk gathered twice");
+          delay(rng, 30);
+          gathered[m * 4 + h].store(1);
+          pc[cl.filled + m * 4 + h].fetch_add(1, std::memory_order_release);
+        }
+        idle_since = std::chrono::steady_clock::now();
+      }
+      return;
+    }
+    const int n_groups = pc[pb + kNGroups].load(), n_tickets = pc[pb + kNTickets].load();
+    std::vector<int> ps(2 * n_groups + 1), gf(std::max(1, n_groups)), gl(std::max(1, n_groups));
+    for (int k = 0; k <= 2 * n_groups && n_groups; ++k) ps[k] = pc[cl.phase_start + 2 * lo + p + k].load();
+    for (int g = 0; g < n_groups; ++g) {
+      gf[g] = pc[cl.grp_first + lo + g].load();
+      gl[g] = pc[cl.grp_len + lo + g].load();
+    }
+    while (n_tickets > 0) {
+      const int t = pc[pb + kTicketNext].fetch_add(1);
+      if (t >= n_tickets) break;
+      const Task tk = task_of_ticket(t, n_groups, ps.data(), gf.data(), gl.data(), plan.lookahead != 0);
+      const int m = tk.m;
+      if (m < lo || m >= hi) fail->add("ticket maps outside the pipeline's row tiles");
+      bool ok = true;
+      if (!tk.down) {
+        for (int h = 0; h < cpm && ok; ++h) ok = wait_ge(cl.filled + m * 4 + h, 1);
+      } else {
+        ok = wait_ge(cl.g1_done + m, c.NT1);
+      }
+      if (!ok) break;
+      for (int h = 0; h < cpm; ++h) {
+        const int q = (m - lo) * cpm + h;
+        if (slot_occ[p * S + chunk_slot(q, S)].load() != q || !gathered[m * 4 + h].load())
+          fail->add("GEMM task on a row tile whose chunks are not all in their slots");
+      }
+      if (tk.down && u_done[m].load() != c.NT1) fail->add("down tile before all gate/up tiles finished");
+      if (tk.j < 0 || tk.j >= (tk.down ? c.NT2 : c.NT1)) fail->add("column tile out of range");
+      delay(rng, 20);
+      if (!tk.down) {
+        u_runs[m * 64 + tk.j].fetch_add(1);
+        u_done[m].fetch_add(1);
+        pc[cl.g1_done + m].fetch_add(1, std::memory_order_release);
+      } else {
+        d_runs[m * 64 + tk.j].fetch_add(1);
+        d_done[m].fetch_add(1);
+        pc[cl.g2_done + m].fetch_add(1, std::memory_order_release);
+      }
+    }
+  }
+
+  // the rule of persist_check_kernel
+  bool incomplete() const {
+    for (int p = 0; p < plan.n_part; ++p) {
+      const int b = cl.pipe0 + p * kPipeWords;
+      const int n_m = pc[b + kHi].load() - pc[b + kLo].load();
+      if (pc[b + kGatherNext].load() < n_m * c.cpm || pc[b + kPushNext].load() < n_m ||
+          pc[b + kTicketNext].load() < pc[b + kNTickets].load())
+        return true;
+    }
+    return false;
+  }
+};
+
+Case random_case(std::mt19937& rng) {
+  Case c{};
+  c.El = 1 + int(rng() % 12);
+  const int cpms[3] = {1, 2, 4};
+  c.cpm = cpms[rng() % 3];
+  c.NT1 = 1 + int(rng() % 4);
+  c.NT2 = 1 + int(rng() % 4);
+  c.eight_xcds = rng() % 3 != 0;
+  c.cus = c.eight_xcds ? 8 * (2 + int(rng() % 4)) : 2 + int(rng() % 24);
+  c.comm = 1 + int(rng() % 12);
+  c.slots = c.cpm + int(rng() % 60);
+  c.wg_per_pipe_override = 0;
+  c.drop_pipeline = false;
+  c.counts.resize(c.El);
+  const int hot = int(rng() % c.El);
+  for (int l = 0; l < c.El; ++l) {
+    const int kind = int(rng() % 6);
+    int rows = kind == 0 ? 0 : (kind == 1 ? 1 + int(rng() % 255) : int(rng() % (6 * kBM)));
+    if (l == hot && rng() % 2) rows = int(rng() % (20 * kBM));    // a hot expert: many row tiles
+    c.counts[l] = rows;
+  }
+  return c;
+}
+
+// 0 = fine, 1 = violation (message printed)
+int run_case(const Case& cs, unsigned seed, Fail& fail) {
+  Model M;
+  M.c = cs;
+  M.fail = &fail;
+  M.seed = seed;
+  M.plan = plan_persistent(cs.cus, cs.eight_xcds, cs.slots, cs.cpm, cs.comm);
+  if (!M.plan.ok) return 0;          // rejected on the host: nothing launches
+  M.offsets.assign(cs.El + 1, 0);
+  M.mtb.assign(cs.El + 1, 0);
+  for (int l = 0; l < cs.El; ++l) {
+    M.offsets[l + 1] = M.offsets[l] + cs.counts[l];
+    M.mtb[l + 1] = M.mtb[l] + (cs.counts[l] + kBM - 1) / kBM;
+  }
+  M.n_mt = M.mtb[cs.El];
+  M.max_mtiles = M.n_mt + cs.El + 1;
+  M.cl = ctrl_layout(M.max_mtiles, M.plan.n_part * M.plan.S);
+  M.pc = std::vector<std::atomic<int>>(M.cl.words);
+  M.slot_occ = std::vector<std::atomic<int>>(M.plan.n_part * M.plan.S);
+  for (auto& a : M.slot_occ) a.store(-1);
+  const int nt = std::max(1, M.n_mt);
+  M.gathered = std::vector<std::atomic<int>>(nt * 4);
+  M.gather_runs = std::vector<std::atomic<int>>(nt * 4);
+  M.u_done = std::vector<std::atomic<int>>(nt);
+  M.d_done = std::vector<std::atomic<int>>(nt);
+  M.pushed = std::vector<std::atomic<int>>(nt);
+  M.push_runs = std::vector<std::atomic<int>>(nt);
+  M.u_runs = std::vector<std::atomic<int>>(nt * 64);
+  M.d_runs = std::vector<std::atomic<int>>(nt * 64);
+  M.prep();
+
+  // workgroups: w runs on XCD w mod 8 (eight_xcds) and joins pipeline xcd * n_part / 8
+  std::vector<int> pipe_of;
+  for (int w = 0; w < cs.cus; ++w) {
+    const int p = cs.eight_xcds ? (w % 8) * M.plan.n_part / 8 : 0;
+    if (cs.drop_pipeline && p == M.plan.n_part - 1) continue;
+    pipe_of.push_back(p);
+  }
+  std::vector<std::thread> th;
+  std::mt19937 rng(seed);
+  for (size_t w = 0; w < pipe_of.size(); ++w) th.emplace_back([&M, &pipe_of, w, s = unsigned(rng())] {
+    M.workgroup(pipe_of[w], s);
+  });
+  for (auto& t : th) t.join();
+
+  const bool inc = M.incomplete();
+  // a dropped pipeline with work must be reported; otherwise nothing may be left
+  int lo, hi;
+  pipe_range(M.n_mt, M.plan.n_part, M.plan.n_part - 1, &lo, &hi);
+  const bool dropped_work = cs.drop_pipeline && hi > lo;
+  if (dropped_work != inc) {
+    fail.add(dropped_work ? "a pipeline without workgroups was not reported incomplete"
+                          : "work left undone although every pipeline had workgroups");
+  }
+  if (!cs.drop_pipeline) {
+    for (int m = 0; m < M.n_mt; ++m) {
+      int p = 0;
+      for (int q = 0; q < M.plan.n_part; ++q) {
+        int a, b;
+        pipe_range(M.n_mt, M.plan.n_part, q, &a, &b);
+        if (m >= a && m < b) p = q;
+      }
+      (void)p;
+      if (M.push_runs[m].load() != 1) fail.add("row tile not pushed exactly once");
+      for (int h = 0; h < cs.cpm; ++h)
+        if (M.gather_runs[m * 4 + h].load() != 1) fail.add("chunk not gathered exactly once");
+      for (int j = 0; j < cs.NT1; ++j)
+        if (M.u_runs[m * 64 + j].load() != 1) fail.add("gate/up tile not run exactly once");
+      for (int j = 0; j < cs.NT2; ++j)
+        if (M.d_runs[m * 64 + j].load() != 1) fail.add("down tile not run exactly once");
+    }
+  }
+  return fail.n.load() ? 1 : 0;
+}
+
+std::string describe(const Case& c) {
+  char buf[256];
+  std::snprintf(buf, sizeof buf, "El=%d cpm=%d NT1=%d NT2=%d cus=%d eight_xcds=%d comm=%d slots=%lld drop=%d rows=[",
+                c.El, c.cpm, c.NT1, c.NT2, c.cus, int(c.eight_xcds), c.comm, c.slots, int(c.drop_pipeline));
+  std::string s = buf;
+  for (int v : c.counts) s += std::to_string(v) + ",";
+  return s + "]";
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  const unsigned seed = argc > 1 ? unsigned(std::atoi(argv[1])) : 1u;
+  const int cases = argc > 2 ? std::atoi(argv[2]) : 50;
+  std::mt19937 rng(seed);
+  int run = 0;
+  // fixed cases first: the DeepSeek-V3-shaped share's plan (256 CUs, 113 slots of 128 rows,
+  // 16 movers; 4 row tiles per expert) scaled down to 16 compute tiles per row tile, a ring
+  // of exactly one row tile, and two row tiles
+  std::vector<Case> fixed;
+  {
+    Case c{};
+    c.El = 32; c.cpm = 2; c.NT1 = 4; c.NT2 = 4; c.cus = 256; c.eight_xcds = true; c.comm = 16; c.slots = 113;
+    c.counts.assign(32, 1024);
+    fixed.push_back(c);
+    c.slots = 2;           // one row tile of ring: one pipeline, no look-ahead
+    c.cus = 24;
+    fixed.push_back(c);
+    c.slots = 4;           // two row tiles: one pipeline with look-ahead
+    fixed.push_back(c);
+    c.slots = 113; c.cus = 64; c.drop_pipeline = true;    // one pipeline gets no workgroup
+    fixed.push_back(c);
+  }
+  for (int i = 0; i < cases + int(fixed.size()); ++i) {
+    Case c = i < int(fixed.size()) ? fixed[i] : random_case(rng);
+    if (i >= int(fixed.size()) && c.eight_xcds && rng() % 8 == 0) c.drop_pipeline = true;
+    Fail fail;
+    if (run_case(c, seed * 7919u + unsigned(i), fail)) {
+      std::printf("FAIL case %d: %s\n  %s\n", i, describe(c).c_str(), fail.first.c_str());
+      return 1;
+    }
+    ++run;
+  }
+  std::printf("OK %d\n", run);
+  return 0;
+}

@@ -199,15 +199,58 @@ def test_persistent_entry_rejects_bad_arguments_before_launch():
     assert call(ring=None) == -1
 
 
-def test_persistent_entry_is_switched_off():
-    """The persistent path returns MOE_EUNSUP after its checks and launches nothing."""
+def test_persistent_trace_layout_and_workspace():
+    """The trace region sits after the persistent workspace proper; its record is 32 bytes."""
+    import numpy as np
+    s, p = _shape(), _pl()
+    ex0, ex1 = moe.Exec(128, 16, 0, 0, 0), moe.Exec(128, 16, 0, 1, 0)
+    base = moe.moe_persistent_workspace_bytes(s, p, ex0)
+    with_trace = moe.moe_persistent_workspace_bytes(s, p, ex1)
+    off, cap, tpu = moe.moe_persistent_trace_info(s, p, ex1)
+    assert off == base and off % 256 == 0
+    assert np.dtype(moe.TRACE_EVENT_FIELDS).itemsize == 32
+    assert with_trace >= base + 256 + cap * 32
+    # every task of the worst case fits: gathers (2 per row tile), pushes, 16 + 28 GEMM tiles
+    max_mtiles = (8 * 4096 * 8 + 255) // 256 + 32
+    assert cap >= max_mtiles * (2 + 1 + 16 + 28)
+    assert tpu > 0
+    with pytest.raises(moe.MoEError):
+        moe.moe_persistent_trace_info(s, p, ex0)                       # trace must be on
+
+
+def test_trace_is_rejected_outside_the_persistent_path():
     L = moe.lib()
     s, p = _shape(), _pl()
     tab = (ctypes.c_void_p * 8)(*([FAKE] * 8))
     tabp = ctypes.cast(tab, ctypes.c_void_p)
-    rc = L.moe_forward_persistent(ctypes.byref(s), ctypes.byref(p), None, tabp, tabp, FAKE, FAKE, FAKE, FAKE,
-                                  1 << 40, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
-    assert rc == -6
+    big = 1 << 40
+    ex = moe.Exec(128, 0, 0, 1, 0)
+    assert L.moe_layout(ctypes.byref(s), ctypes.byref(p), ctypes.byref(ex), tabp, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, FAKE, big, None) == -1
+    assert L.moe_expert_ffn(ctypes.byref(s), ctypes.byref(p), ctypes.byref(ex), FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                            None, FAKE, FAKE, big, None) == -1
+    assert L.moe_forward(ctypes.byref(s), ctypes.byref(p), ctypes.byref(ex), tabp, tabp, FAKE, FAKE, FAKE, None,
+                         FAKE, None, FAKE, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    assert L.moe_forward_fused(ctypes.byref(s), ctypes.byref(p), ctypes.byref(ex), tabp, tabp, FAKE, FAKE, FAKE,
+                               None, None, None, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big,
+                               None) == -1
+    # the persistent path takes 0 or 1 only
+    bad = moe.Exec(128, 0, 0, 2, 0)
+    assert L.moe_forward_persistent(ctypes.byref(s), ctypes.byref(p), ctypes.byref(bad), tabp, tabp, FAKE, FAKE,
+                                    FAKE, FAKE, big, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big,
+                                    None) == -1
+
+
+def test_persistent_entry_rejects_a_partition_without_compute():
+    """comm_cus leaving no CU for the expert GEMMs is rejected before any launch."""
+    L = moe.lib()
+    s, p = _shape(), _pl()
+    tab = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    tabp = ctypes.cast(tab, ctypes.c_void_p)
+    ex = moe.Exec(128, 4096, 0, 0, 0)
+    assert L.moe_forward_persistent(ctypes.byref(s), ctypes.byref(p), ctypes.byref(ex), tabp, tabp, FAKE, FAKE,
+                                    FAKE, FAKE, 1 << 40, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    1 << 40, None) == -1
 
 
 def test_backward_entry_points_reject_bad_arguments_before_launch():
