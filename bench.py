@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--ring-mib", type=int, default=0, help="persistent path: ring size (default: the config's)")
     ap.add_argument("--trace", action="store_true",
                     help="persistent path: after the timed steps, one traced call; per-role busy and wait summary")
+    ap.add_argument("--trace-out", default="",
+                    help="with --trace: also save the raw events (numpy .npy) to this path")
     ap.add_argument("--sweep-persistent", default="",
                     help="persistent path: 'C1,C2,...:M1,M2,...' -- time every comm_cus C x minibatch M "
                          "(one JSON line per point)")
@@ -801,6 +803,8 @@ def main():
             if moe.moe_read_status(tws) != 0:
                 raise SystemExit("device status after the traced call")
             ev, tpu = moe.read_trace(tws, P.shape, P.placement, tex)
+            if args.trace_out:
+                np.save(args.trace_out, ev)
             result["trace"] = trace_summary(ev, tpu, P.cu_grid() if hasattr(P, "cu_grid") else 0)
             log(f"[bench] trace: {result['trace']}")
             del tws

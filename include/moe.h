@@ -303,7 +303,7 @@ int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_
  * Roles: in each pipeline the first comm_cus / pipelines workgroups to start move data --
  * they gather chunks of token rows from the source buffers into free ring slots and push
  * finished output rows to recv, freeing the slots -- and the others take GEMM tasks in
- * ticket order.  Row tiles (256 rows of one expert) are split evenly over the pipelines:
+ * ticket order, then join the data movement once their pipeline has no task left.  Row tiles (256 rows of one expert) are split evenly over the pipelines:
  * eight (one per XCD, every hand-off inside one L2) when each XCD's share of the ring holds
  * two groups, else fewer, with agent-scope hand-offs.  Up to G consecutive row tiles of one
  * expert form a group whose GEMM tasks run weight-panel-major, so concurrent tasks share

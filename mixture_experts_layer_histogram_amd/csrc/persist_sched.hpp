@@ -168,6 +168,9 @@ MOE_HD Task task_of_ticket(int t, int n, const int* phase_start, const int* grp_
 // ring slot (pipeline-local) of pipeline-local chunk q, and the epoch it must have reached
 MOE_HD int chunk_slot(int q, int S) { return q % S; }
 MOE_HD int chunk_epoch(int q, int S) { return q / S; }
+// control word holding the epoch of the slot of pipeline p's chunk q (every reader and every
+// writer of a slot epoch goes through this)
+MOE_HD int slot_epoch_word(const CtrlLayout& cl, int p, int S, int q) { return cl.slot_epoch + p * S + chunk_slot(q, S); }
 
 // Mover actions
 enum MoverAct { kIdle = 0, kPush = 1, kGather = 2, kDone = 3 };
@@ -178,8 +181,8 @@ enum MoverAct { kIdle = 0, kPush = 1, kGather = 2, kDone = 3 };
 // pipeline's in-order counters, so every chunk and row tile is claimed exactly once, in
 // order.  Ops: ld(word) -> int (relaxed atomic load), cas(word, expected, desired) -> bool.
 template <class Ops>
-MOE_HD int mover_claim(Ops& ops, const CtrlLayout& cl, int pipe_base, int lo, int n_m, int cpm, int S, int NT2,
-                       int slot_base, int* arg) {
+MOE_HD int mover_claim(Ops& ops, const CtrlLayout& cl, int p, int lo, int n_m, int cpm, int S, int NT2, int* arg) {
+  const int pipe_base = cl.pipe0 + p * kPipeWords;
   const int ci = ops.ld(pipe_base + kPushNext);
   if (ci < n_m && ops.ld(cl.g2_done + lo + ci) >= NT2) {
     if (ops.cas(pipe_base + kPushNext, ci, ci + 1)) {
@@ -189,7 +192,7 @@ MOE_HD int mover_claim(Ops& ops, const CtrlLayout& cl, int pipe_base, int lo, in
     return kIdle;                             // lost the race: try again next round
   }
   const int qi = ops.ld(pipe_base + kGatherNext);
-  if (qi < n_m * cpm && ops.ld(cl.slot_epoch + slot_base + chunk_slot(qi, S)) >= chunk_epoch(qi, S)) {
+  if (qi < n_m * cpm && ops.ld(slot_epoch_word(cl, p, S, qi)) >= chunk_epoch(qi, S)) {
     if (ops.cas(pipe_base + kGatherNext, qi, qi + 1)) {
       *arg = qi;
       return kGather;

@@ -17,7 +17,8 @@
 //   needs a cooperative launch.  Roles go by arrival order inside a pipeline, so the first
 //   workgroups to run are the movers; compute workgroups take tickets in order and a task
 //   waits only for movers or smaller tickets, so progress does not depend on every
-//   workgroup being resident at once.
+//   workgroup being resident at once.  A compute workgroup whose pipeline has no ticket left
+//   joins the movers, so the last pushes (after the last GEMM) are spread over more CUs.
 // * Pipelines per XCD.  The eight XCDs' L2 caches are not coherent with one another, and an
 //   agent-scope release/acquire writes back / invalidates a whole L2.  With a ring large
 //   enough, the row tiles are split into eight pipelines, one per XCD (the kernel reads the
@@ -137,27 +138,41 @@ __device__ __forceinline__ void trace_event(const PersistArgs& A, int kind, int 
   A.trace[i] = ev;
 }
 
+typedef __attribute__((address_space(1))) const u32x4* gsrc_t;
+typedef __attribute__((address_space(1))) u32x4* gdst_t;
+
 // Copy nrows rows of n16 16-byte vectors from src[r] to dst[r] (row addresses staged in
-// LDS) with the whole workgroup, 16 vectors in flight per thread.
+// LDS) with the whole workgroup.  Each wave moves two rows at a time (r and r + 8), 16
+// vectors per lane of each: 32 outstanding 16-byte global loads per lane (224 KiB per
+// workgroup for 14 KiB rows).  The loads are unconditional (columns past the row end are
+// clamped to its last vector; a lone last row reads itself twice) so the compiler issues
+// them back to back; only the stores are predicated.
 __device__ void wg_copy_rows(const uint64_t* src, const uint64_t* dst, int nrows, int n16) {
   constexpr int U = 16;
-  const int total = nrows * n16;
-  for (int base = 0; base < total; base += kGemmThreads * U) {
-    u32x4 v[U];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kWaves = kGemmThreads / 64;
+  for (int r = wave; r < nrows; r += 2 * kWaves) {
+    const int r2 = r + kWaves;
+    const bool two = r2 < nrows;
+    const gsrc_t s0 = reinterpret_cast<gsrc_t>(src[r]);
+    const gdst_t t0 = reinterpret_cast<gdst_t>(dst[r]);
+    const gsrc_t s1 = reinterpret_cast<gsrc_t>(src[two ? r2 : r]);
+    const gdst_t t1 = reinterpret_cast<gdst_t>(dst[two ? r2 : r]);
+    for (int c0 = 0; c0 < n16; c0 += 64 * U) {
+      u32x4 a[U], b[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + u * kGemmThreads + int(threadIdx.x);
-      if (i < total) {
-        const int r = i / n16;
-        v[u] = reinterpret_cast<const u32x4*>(src[r])[i - r * n16];
+      for (int u = 0; u < U; ++u) {
+        const int c = min(c0 + u * 64 + lane, n16 - 1);
+        a[u] = s0[c];
+        b[u] = s1[c];
       }
-    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + u * kGemmThreads + int(threadIdx.x);
-      if (i < total) {
-        const int r = i / n16;
-        reinterpret_cast<u32x4*>(dst[r])[i - r * n16] = v[u];
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < n16) {
+          t0[c] = a[u];
+          if (two) t1[c] = b[u];
+        }
       }
     }
   }
@@ -218,7 +233,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
   int32_t* filled = A.pc + A.cl.filled;
   int32_t* g1_done = A.pc + A.cl.g1_done;
   int32_t* g2_done = A.pc + A.cl.g2_done;
-  int32_t* slot_epoch = A.pc + A.cl.slot_epoch + p * A.S;
 
   if (tid == 0) sh[0] = __hip_atomic_fetch_add(pw + sched::kJoin, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -247,87 +261,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
     return min(kGemmBM, A.offsets[*l + 1] - *row0);
   };
 
-  if (mover) {
-    // ------------------------------------------------------------ data movement
-    uint64_t* src_tab = reinterpret_cast<uint64_t*>(smem);
-    uint64_t* dst_tab = src_tab + kGemmBM;
-    const DevOps ops{A.pc};
-    long long idle_since = wall_clock64();
-    while (true) {
-      if (tid == 0) {
-        int act = sched::kIdle, arg = 0;
-        if (ld_relaxed(A.pc + A.cl.abort_word)) {
-          act = sched::kDone;
-        } else {
-          act = sched::mover_claim(ops, A.cl, pbase, lo, n_m, cpm, S, (A.d + kGemmBN - 1) / kGemmBN,
-                                   A.cl.slot_epoch + p * S, &arg);
-          if (act == sched::kIdle) {
-            __builtin_amdgcn_s_sleep(1);
-            if (wall_clock64() - idle_since > A.budget) {
-              set_abort(A, MOE_ETIMEOUT);
-              act = sched::kDone;
-            }
-          }
-        }
-        sh[1] = act;
-        sh[2] = arg;
-      }
-      __syncthreads();
-      const int act = sh[1], arg = sh[2];
-      __syncthreads();
-      if (act == sched::kDone) break;
-      if (act == sched::kIdle) continue;
-      const long long t_b = wall_clock64();
-      acquire_after_poll(light);
-      if (act == sched::kPush) {
-        // row tile lo + arg: its output rows (in place in the ring) -> recv[rank][token][j]
-        int row0, l;
-        const int m = lo + arg;
-        const int rows = tile_rows(m, &row0, &l);
-        for (int r = tid; r < rows; r += kGemmThreads) {
-          const int s = row0 + r;
-          const int rk = A.pull_src[2 * (long long)s];
-          const int t = A.pull_src[2 * (long long)s + 1];
-          const int32_t* so = A.slot_of + ((long long)rk * A.T + t) * A.k;
-          int j = 0;
-          for (int jj = 0; jj < A.k; ++jj)
-            if (so[jj] == s) j = jj;
-          src_tab[r] = reinterpret_cast<uint64_t>(slot_ptr(arg * cpm + (r >> A.blk_log2)) +
-                                                  (long long)(r & (chunk_rows - 1)) * row_bytes);
-          dst_tab[r] = reinterpret_cast<uint64_t>(A.recv.p[rk] + ((long long)t * A.k + j) * row_bytes);
-        }
-        __syncthreads();
-        wg_copy_rows(src_tab, dst_tab, rows, n16);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // the slot's reads are done
-        __syncthreads();
-        if (tid == 0)
-          for (int h = 0; h < cpm; ++h)
-            __hip_atomic_fetch_add(slot_epoch + sched::chunk_slot(arg * cpm + h, S), 1, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        trace_event(A, 2, m, p, t_b, wall_clock64(), t_b - idle_since);
-      } else {
-        // chunk arg: rows [h * chunk_rows, ...) of row tile lo + arg / cpm, from the sources
-        int row0, l;
-        const int m = lo + arg / cpm, h = arg % cpm;
-        const int rows = tile_rows(m, &row0, &l);
-        const int c_lo = h * chunk_rows, c_n = min(chunk_rows, rows - c_lo);
-        char* dst = slot_ptr(arg);
-        for (int r = tid; r < c_n; r += kGemmThreads) {
-          const int s = row0 + c_lo + r;
-          const int rk = A.pull_src[2 * (long long)s];
-          const int t = A.pull_src[2 * (long long)s + 1];
-          src_tab[r] = reinterpret_cast<uint64_t>(A.x.p[rk] + (long long)t * row_bytes);
-          dst_tab[r] = reinterpret_cast<uint64_t>(dst + (long long)r * row_bytes);
-        }
-        __syncthreads();
-        if (c_n > 0) wg_copy_rows(src_tab, dst_tab, c_n, n16);
-        release_add(filled + m * 4 + h, 1, light);
-        trace_event(A, 1, arg, p, t_b, wall_clock64(), t_b - idle_since);
-      }
-      __syncthreads();                                          // the row tables are reused
-      idle_since = wall_clock64();
-    }
-  } else if (n_tickets > 0) {
+  // Compute workgroups take tickets until none is left, then join the data movement for the
+  // tail (the last pushes); data-movement workgroups move data from the start.
+  bool aborted = false;
+  if (!mover && n_tickets > 0) {
     // ------------------------------------------------------------ expert compute
     const int32_t* phase_start = A.pc + A.cl.phase_start + 2 * lo + p;
     const int32_t* grp_first = A.pc + A.cl.grp_first + lo;
@@ -349,7 +286,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
       } else {
         ok = wait_ge(g1_done + m, NT1, A, sh);
       }
-      if (!ok) break;
+      if (!ok) {
+        aborted = true;
+        break;
+      }
       const long long t_b = wall_clock64();
       acquire_after_poll(light);
       const int q0 = (m - lo) * cpm;
@@ -396,6 +336,86 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
         release_add(g2_done + m, 1, light);
         trace_event(A, 4, m * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
       }
+    }
+  }
+  if (!aborted) {
+    // ------------------------------------------------------------ data movement
+    uint64_t* src_tab = reinterpret_cast<uint64_t*>(smem);
+    uint64_t* dst_tab = src_tab + kGemmBM;
+    const DevOps ops{A.pc};
+    long long idle_since = wall_clock64();
+    while (true) {
+      if (tid == 0) {
+        int act = sched::kIdle, arg = 0;
+        if (ld_relaxed(A.pc + A.cl.abort_word)) {
+          act = sched::kDone;
+        } else {
+          act = sched::mover_claim(ops, A.cl, p, lo, n_m, cpm, S, (A.d + kGemmBN - 1) / kGemmBN, &arg);
+          if (act == sched::kIdle) {
+            __builtin_amdgcn_s_sleep(1);
+            if (wall_clock64() - idle_since > A.budget) {
+              set_abort(A, MOE_ETIMEOUT);
+              act = sched::kDone;
+            }
+          }
+        }
+        sh[1] = act;
+        sh[2] = arg;
+      }
+      __syncthreads();
+      const int act = sh[1], arg = sh[2];
+      __syncthreads();
+      if (act == sched::kDone) break;
+      if (act == sched::kIdle) continue;
+      const long long t_b = wall_clock64();
+      acquire_after_poll(light);
+      if (act == sched::kPush) {
+        // row tile lo + arg: its output rows (in place in the ring) -> recv[rank][token][j]
+        int row0, l;
+        const int m = lo + arg;
+        const int rows = tile_rows(m, &row0, &l);
+        for (int r = tid; r < rows; r += kGemmThreads) {
+          const int s = row0 + r;
+          const int rk = A.pull_src[2 * (long long)s];
+          const int t = A.pull_src[2 * (long long)s + 1];
+          const int32_t* so = A.slot_of + ((long long)rk * A.T + t) * A.k;
+          int j = 0;
+          for (int jj = 0; jj < A.k; ++jj)
+            if (so[jj] == s) j = jj;
+          src_tab[r] = reinterpret_cast<uint64_t>(slot_ptr(arg * cpm + (r >> A.blk_log2)) +
+                                                  (long long)(r & (chunk_rows - 1)) * row_bytes);
+          dst_tab[r] = reinterpret_cast<uint64_t>(A.recv.p[rk] + ((long long)t * A.k + j) * row_bytes);
+        }
+        __syncthreads();
+        wg_copy_rows(src_tab, dst_tab, rows, n16);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // the slot's reads are done
+        __syncthreads();
+        if (tid == 0)
+          for (int h = 0; h < cpm; ++h)
+            __hip_atomic_fetch_add(A.pc + sched::slot_epoch_word(A.cl, p, S, arg * cpm + h), 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        trace_event(A, 2, m, p, t_b, wall_clock64(), t_b - idle_since);
+      } else {
+        // chunk arg: rows [h * chunk_rows, ...) of row tile lo + arg / cpm, from the sources
+        int row0, l;
+        const int m = lo + arg / cpm, h = arg % cpm;
+        const int rows = tile_rows(m, &row0, &l);
+        const int c_lo = h * chunk_rows, c_n = min(chunk_rows, rows - c_lo);
+        char* dst = slot_ptr(arg);
+        for (int r = tid; r < c_n; r += kGemmThreads) {
+          const int s = row0 + c_lo + r;
+          const int rk = A.pull_src[2 * (long long)s];
+          const int t = A.pull_src[2 * (long long)s + 1];
+          src_tab[r] = reinterpret_cast<uint64_t>(A.x.p[rk] + (long long)t * row_bytes);
+          dst_tab[r] = reinterpret_cast<uint64_t>(dst + (long long)r * row_bytes);
+        }
+        __syncthreads();
+        if (c_n > 0) wg_copy_rows(src_tab, dst_tab, c_n, n16);
+        release_add(filled + m * 4 + h, 1, light);
+        trace_event(A, 1, arg, p, t_b, wall_clock64(), t_b - idle_since);
+      }
+      __syncthreads();                                          // the row tables are reused
+      idle_since = wall_clock64();
     }
   }
   trace_event(A, 5, mover ? 0 : 1, p, wall_clock64(), wall_clock64(), 0);

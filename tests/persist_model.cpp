@@ -1,6 +1,7 @@
 // Host-threaded model of the persistent forward kernel (csrc/persistent.hip): one host
 // thread per workgroup runs the kernel's control loop -- join, role by arrival order, the
-// movers' claim step and the compute workgroups' ticket loop with their waits -- through
+// compute workgroups' ticket loop with their waits, and the movers' claim loop, which the
+// compute workgroups also run once their tickets are exhausted -- through
 // the same scheduling code the device compiles (csrc/persist_sched.hpp), with random
 // delays in place of the copies and GEMM tiles.  Shadow state checks every hazard the
 // counters are meant to exclude:
@@ -138,14 +139,53 @@ struct Model {
     const int rank = pc[pb + kJoin].fetch_add(1);
     const int lo = pc[pb + kLo].load(), hi = pc[pb + kHi].load();
     const int n_m = hi - lo, S = plan.S, cpm = c.cpm;
-    const int slot_base = cl.slot_epoch + p * S;
     Ops ops{pc.data()};
-    if (rank < plan.comm_pp) {
+    // compute workgroups take tickets until none is left, then join the data movement
+    if (rank >= plan.comm_pp) {
+      const int n_groups = pc[pb + kNGroups].load(), n_tickets = pc[pb + kNTickets].load();
+      std::vector<int> ps(2 * n_groups + 1), gf(std::max(1, n_groups)), gl(std::max(1, n_groups));
+      for (int k = 0; k <= 2 * n_groups && n_groups; ++k) ps[k] = pc[cl.phase_start + 2 * lo + p + k].load();
+      for (int g = 0; g < n_groups; ++g) {
+        gf[g] = pc[cl.grp_first + lo + g].load();
+        gl[g] = pc[cl.grp_len + lo + g].load();
+      }
+      while (n_tickets > 0) {
+        const int t = pc[pb + kTicketNext].fetch_add(1);
+        if (t >= n_tickets) break;
+        const Task tk = task_of_ticket(t, n_groups, ps.data(), gf.data(), gl.data(), plan.lookahead != 0);
+        const int m = tk.m;
+        if (m < lo || m >= hi) fail->add("ticket maps outside the pipeline's row tiles");
+        bool ok = true;
+        if (!tk.down) {
+          for (int h = 0; h < cpm && ok; ++h) ok = wait_ge(cl.filled + m * 4 + h, 1);
+        } else {
+          ok = wait_ge(cl.g1_done + m, c.NT1);
+        }
+        if (!ok) return;                 // aborted: exit
+        for (int h = 0; h < cpm; ++h) {
+          const int q = (m - lo) * cpm + h;
+          if (slot_occ[p * S + chunk_slot(q, S)].load() != q || !gathered[m * 4 + h].load())
+            fail->add("GEMM task on a row tile whose chunks are not all in their slots");
+        }
+        if (tk.down && u_done[m].load() != c.NT1) fail->add("down tile before all gate/up tiles finished");
+        if (tk.j < 0 || tk.j >= (tk.down ? c.NT2 : c.NT1)) fail->add("column tile out of range");
+        delay(rng, 20);
+        if (!tk.down) {
+          u_runs[m * 64 + tk.j].fetch_add(1);
+          u_done[m].fetch_add(1);
+          pc[cl.g1_done + m].fetch_add(1, std::memory_order_release);
+        } else {
+          d_runs[m * 64 + tk.j].fetch_add(1);
+          d_done[m].fetch_add(1);
+          pc[cl.g2_done + m].fetch_add(1, std::memory_order_release);
+        }
+      }
+    }
       auto idle_since = std::chrono::steady_clock::now();
       while (true) {
         if (abort_flag.load()) break;
         int arg = 0;
-        const int act = mover_claim(ops, cl, pb, lo, n_m, cpm, S, c.NT2, p * S, &arg);
+        const int act = mover_claim(ops, cl, p, lo, n_m, cpm, S, c.NT2, &arg);
         if (act == kDone) break;
         if (act == kIdle) {
           std::this_thread::yield();
@@ -167,7 +207,7 @@ struct Model {
           if (push_runs[m].fetch_add(1) != 0) fail->add("row tile pushed twice");
           delay(rng, 30);
           pushed[m].store(1);
-          for (int h = 0; h < cpm; ++h) pc[slot_base + chunk_slot(arg * cpm + h, S)].fetch_add(1);
+          for (int h = 0; h < cpm; ++h) pc[slot_epoch_word(cl, p, S, arg * cpm + h)].fetch_add(1);
         } else {
           const int q = arg, m = lo + q / cpm, h = q % cpm;
           const int s = chunk_slot(q, S);
@@ -186,46 +226,6 @@ struct Model {
         }
         idle_since = std::chrono::steady_clock::now();
       }
-      return;
-    }
-    const int n_groups = pc[pb + kNGroups].load(), n_tickets = pc[pb + kNTickets].load();
-    std::vector<int> ps(2 * n_groups + 1), gf(std::max(1, n_groups)), gl(std::max(1, n_groups));
-    for (int k = 0; k <= 2 * n_groups && n_groups; ++k) ps[k] = pc[cl.phase_start + 2 * lo + p + k].load();
-    for (int g = 0; g < n_groups; ++g) {
-      gf[g] = pc[cl.grp_first + lo + g].load();
-      gl[g] = pc[cl.grp_len + lo + g].load();
-    }
-    while (n_tickets > 0) {
-      const int t = pc[pb + kTicketNext].fetch_add(1);
-      if (t >= n_tickets) break;
-      const Task tk = task_of_ticket(t, n_groups, ps.data(), gf.data(), gl.data(), plan.lookahead != 0);
-      const int m = tk.m;
-      if (m < lo || m >= hi) fail->add("ticket maps outside the pipeline's row tiles");
-      bool ok = true;
-      if (!tk.down) {
-        for (int h = 0; h < cpm && ok; ++h) ok = wait_ge(cl.filled + m * 4 + h, 1);
-      } else {
-        ok = wait_ge(cl.g1_done + m, c.NT1);
-      }
-      if (!ok) break;
-      for (int h = 0; h < cpm; ++h) {
-        const int q = (m - lo) * cpm + h;
-        if (slot_occ[p * S + chunk_slot(q, S)].load() != q || !gathered[m * 4 + h].load())
-          fail->add("GEMM task on a row tile whose chunks are not all in their slots");
-      }
-      if (tk.down && u_done[m].load() != c.NT1) fail->add("down tile before all gate/up tiles finished");
-      if (tk.j < 0 || tk.j >= (tk.down ? c.NT2 : c.NT1)) fail->add("column tile out of range");
-      delay(rng, 20);
-      if (!tk.down) {
-        u_runs[m * 64 + tk.j].fetch_add(1);
-        u_done[m].fetch_add(1);
-        pc[cl.g1_done + m].fetch_add(1, std::memory_order_release);
-      } else {
-        d_runs[m * 64 + tk.j].fetch_add(1);
-        d_done[m].fetch_add(1);
-        pc[cl.g2_done + m].fetch_add(1, std::memory_order_release);
-      }
-    }
   }
 
   // the rule of persist_check_kernel

@@ -133,12 +133,14 @@ def test_persistent_watchdog_forced_from_host():
 
 def test_persistent_trace():
     """With the trace on: one event per gather, push and GEMM tile and a start and an end per
-    workgroup; outputs unchanged; combine overlaps dispatch (a push begins before the last
-    gather ends)."""
+    workgroup; outputs unchanged.  The ring is capped at 16 slots (four pipelines of 4 slots,
+    fewer than each pipeline's chunks), so slots are reused: some gather must start after a
+    push of the same pipeline ended, and combine overlaps dispatch (a push begins before the
+    last gather ends)."""
     import torch
     inp, P, ref = _reference(SLICE)
     _say("[persistent] trace")
-    ex = moe.Exec(128, 16, 0, 1, WATCHDOG_US)
+    ex = moe.Exec(128, 16, 16, 1, WATCHDOG_US)
     P.alloc_ring(256, ex)
     nbytes = moe.moe_persistent_workspace_bytes(P.shape, P.placement, ex)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=P.device)
@@ -161,6 +163,9 @@ def test_persistent_trace():
     assert (ev["t_end"] >= ev["t_begin"]).all()
     g, pu = ev[ev["kind"] == 1], ev[ev["kind"] == 2]
     assert pu["t_begin"].min() < g["t_end"].max()
+    reused = [p for p in np.unique(g["pipeline"])
+              if g[g["pipeline"] == p]["t_begin"].max() > pu[pu["pipeline"] == p]["t_end"].min()]
+    assert reused
     _say(f"  events={len(ev)} span={(ev['t_end'].max() - ev['t_begin'].min()) / tpu:.0f} us")
 
 
