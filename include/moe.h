@@ -307,7 +307,8 @@ int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_
  * eight (one per XCD, every hand-off inside one L2) when each XCD's share of the ring holds
  * two groups, else fewer, with agent-scope hand-offs.  Up to G consecutive row tiles of one
  * expert form a group whose GEMM tasks run weight-panel-major, so concurrent tasks share
- * each weight panel (G = slots per pipeline / (2 * chunks per row tile), at most 8).
+ * each weight panel (G = slots per pipeline / (3 * chunks per row tile), or / 2 when three
+ * groups do not fit, at most 8).
  * Every device wait is bounded by ex->watchdog_us; on expiry all workgroups exit and
  * moe_read_status() returns MOE_ETIMEOUT.  If a pipeline's work was left undone (no
  * workgroup reached it) moe_read_status() returns MOE_EINCOMPLETE.

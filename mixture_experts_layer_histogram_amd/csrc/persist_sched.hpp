@@ -20,7 +20,7 @@
 //   gate/up phase U(g) of group g runs its tiles column-panel-major (all row tiles of the
 //   group for weight panel 0, then panel 1, ...), so the workgroups that run at the same
 //   time share one weight panel; the down phase D(g) likewise.
-// * Ticket order.  With look-ahead (the ring holds two groups): U0, U1, D0, U2, D1, ...,
+// * Ticket order.  With look-ahead (the ring holds at least two groups): U0, U1, D0, U2, D1, ...,
 //   U(n-1), D(n-2), D(n-1); without: U0, D0, U1, D1, ...  A task waits only for gathers
 //   or for tasks with smaller tickets, and a gather waits only for a push, which waits
 //   only for tasks with smaller tickets than any task that waits for that gather, so the
@@ -243,7 +243,11 @@ inline Plan plan_persistent(int cus, bool eight_xcds, long long slots, int cpm, 
     P.lookahead = 0;
   }
   P.light = (P.n_part == 8) ? 1 : 0;
-  const int g = P.lookahead ? P.S / (2 * cpm) : P.S / cpm;
+  // Group size: with look-ahead the ring should hold three groups, so the gathers of group
+  // g + 1 reuse the slots of group g - 2, pushed long before; else two (then the gathers of
+  // g + 1 wait for the pushes of g - 1, whose down tiles run just before); without
+  // look-ahead, one group.
+  const int g = !P.lookahead ? P.S / cpm : (P.S >= 3 * cpm ? P.S / (3 * cpm) : P.S / (2 * cpm));
   P.G = g < 1 ? 1 : (g > kMaxGroup ? kMaxGroup : g);
   P.ok = 1;
   return P;
