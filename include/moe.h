@@ -341,6 +341,35 @@ int moe_persistent_dispatch_ffn_combine(const moe_shape_t* s, const moe_placemen
                                         const int32_t* slot_of, const int32_t* offsets, void* const* recv, void* ws,
                                         size_t ws_bytes, void* stream);
 
+/*
+ * moe_forward_persistent_noalloc -- for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_forward_persistent with its workspace and its ring in a file-scope device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU, kept by every GPU the library runs on until the process
+ * ends.  The first MOE_NOALLOC_WORKSPACE_BYTES of the array are the workspace, the rest the
+ * ring (as many slots of moe_ring_slot_bytes() as fit, capped by ex->ring_slots).
+ * Same inputs and outputs as moe_forward_persistent, minus ring and ws; the caller still
+ * passes every input and output buffer.  The call makes no allocation (no hipMalloc, no
+ * allocating library routine).
+ * status: NULL, or a 4-byte-aligned DEVICE int32 that receives the device status word
+ *   (what moe_read_status returns for moe_forward_persistent: 0, MOE_EINVAL, MOE_ETIMEOUT,
+ *   MOE_EINCOMPLETE), written on `stream` after the merge.
+ * Every call on one GPU shares that GPU's array and leaves its contents behind; each call
+ * clears what must start at zero, but calls that overlap on one GPU (no ordering between
+ * their streams) race on the array.
+ * Errors: as moe_forward_persistent; MOE_ENOSPC when the shape's workspace
+ * (moe_persistent_workspace_bytes) exceeds MOE_NOALLOC_WORKSPACE_BYTES or the ring part
+ * holds less than one 256-row tile; MOE_EINVAL for ex->trace != 0; MOE_EHIP if the array's
+ * address cannot be looked up.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (128u << 20)
+#define MOE_NOALLOC_WORKSPACE_BYTES (8u << 20)
+int moe_forward_persistent_noalloc(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+                                   const float* const* logits, const void* const* x, const void* w1, const void* w3,
+                                   const void* w2, void* const* recv, void* const* y, int32_t* topk_idx,
+                                   float* topk_w, int32_t* counts, int32_t* offsets, int32_t* pull_src,
+                                   int32_t* slot_of, int32_t* status, void* stream);
+
 /* Bytes of one ring slot of moe_forward_persistent (0 if unsupported). */
 size_t moe_ring_slot_bytes(const moe_shape_t* s, const moe_exec_t* ex);
 

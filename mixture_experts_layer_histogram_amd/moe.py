@@ -24,7 +24,7 @@ ERRORS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_ENOSPC", -4:
 EXPORTS = ["moe_max_pairs", "moe_workspace_bytes", "moe_mx_quantize", "moe_layout", "moe_dispatch_pull",
            "moe_expert_ffn", "moe_expert_ffn_push", "moe_weighted_merge", "moe_combine_push", "moe_forward",
            "moe_forward_fused", "moe_forward_persistent", "moe_persistent_dispatch_ffn_combine",
-           "moe_ring_slot_bytes", "moe_persistent_workspace_bytes", "moe_persistent_trace_info",
+           "moe_forward_persistent_noalloc", "moe_ring_slot_bytes", "moe_persistent_workspace_bytes", "moe_persistent_trace_info",
            "moe_backward_workspace_bytes",
            "moe_combine_pull_reverse", "moe_expert_ffn_backward",
            "moe_dispatch_push_reverse", "moe_backward", "moe_backward_prepare_mx", "moe_backward_mx",
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
                                              VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_persistent_dispatch_ffn_combine.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, SZ, VP, VP, VP, VP, VP,
                                                           SZ, VP]
+        L.moe_forward_persistent_noalloc.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP,
+                                                     VP, VP, VP]
         L.moe_ring_slot_bytes.argtypes = [S, EX]
         L.moe_ring_slot_bytes.restype = SZ
         L.moe_persistent_workspace_bytes.argtypes = [S, PL, EX]
@@ -115,6 +117,7 @@ def lib() -> ctypes.CDLL:
         for f in ("moe_mx_quantize", "moe_layout", "moe_dispatch_pull", "moe_expert_ffn", "moe_combine_push",
                   "moe_expert_ffn_push", "moe_weighted_merge", "moe_forward_fused",
                   "moe_forward", "moe_forward_persistent", "moe_persistent_dispatch_ffn_combine",
+                  "moe_forward_persistent_noalloc",
                   "moe_combine_pull_reverse", "moe_expert_ffn_backward", "moe_dispatch_push_reverse", "moe_backward", "moe_backward_prepare_mx",
                   "moe_backward_mx", "moe_read_status"):
             getattr(L, f).restype = I32
@@ -273,6 +276,20 @@ def moe_persistent_dispatch_ffn_combine(shape, placement, ex, x, w1, w3, w2, rin
                                                    _p(pull_src), _p(slot_of), _p(offsets), _table(recv), _p(ws),
                                                    ws.numel() if ws_bytes is None else ws_bytes, _stream(stream))
     return _check(rc, "moe_persistent_dispatch_ffn_combine") if check else rc
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+NOALLOC_WORKSPACE_BYTES = 8 << 20
+
+
+def moe_forward_persistent_noalloc(shape, placement, ex, logits, x, w1, w3, w2, recv, y, topk_idx, topk_w, counts,
+                                   offsets, pull_src, slot_of, status=None, stream=None, check=True):
+    rc = lib().moe_forward_persistent_noalloc(ctypes.byref(shape), ctypes.byref(placement),
+                                              ctypes.byref(ex) if ex is not None else None, _table(logits), _table(x),
+                                              _p(w1), _p(w3), _p(w2), _table(recv), _table(y), _p(topk_idx),
+                                              _p(topk_w), _p(counts), _p(offsets), _p(pull_src), _p(slot_of),
+                                              _p(status), _stream(stream))
+    return _check(rc, "moe_forward_persistent_noalloc") if check else rc
 
 
 def moe_ring_slot_bytes(shape: Shape, ex: Exec | None = None) -> int:
