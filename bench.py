@@ -37,6 +37,8 @@ PEAK_HBM = 8.0e12            # MI355X HBM3E bytes/s
 CSRC = os.path.join(ROOT, "mixture_experts_layer_histogram_amd", "csrc")
 # per workload: committed traffic record, GEMM kernel name, and the sources the kernels are built from
 TRAFFIC = {
+    "dsv3/persistent": ("traffic_persistent_dsv3_bf16.json", "moe_persistent_kernel",
+                        ("persistent.hip", "persist_sched.hpp", "gemm_tile.hpp", "common.hpp")),
     "dsv3": ("traffic_grouped_gemm_dsv3_bf16.json", "grouped_gemm_bf16_kernel",
              ("gemm.hip", "gemm_tile.hpp", "common.hpp")),
     "dsv3_mx": ("traffic_grouped_gemm_dsv3_mxfp8.json", "grouped_gemm_mx_kernel",
@@ -83,6 +85,8 @@ def parse():
                          "the ring, expert FFN and push combine, merge) instead of the fused multi-kernel path")
     ap.add_argument("--fused", action="store_true",
                     help="time the fused multi-kernel path (layout, FFN with the pull and push fused in, merge)")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="persistent path: skip timing the fused multi-kernel path beside it")
     ap.add_argument("--comm-cus", type=int, default=16, help="persistent path: data-movement workgroups")
     ap.add_argument("--minibatch", type=int, default=0, help="persistent path: rows per chunk (64, 128, 256)")
     ap.add_argument("--ring-mib", type=int, default=0, help="persistent path: ring size (default: the config's)")
@@ -184,23 +188,33 @@ def _per_dispatch(csv_path, counter):
 
 
 def write_traffic(config, fetch_csv, write_csv):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the two FFN GEMM kernels, each scaled
-    by (known bytes / counter) of a plain 1 GiB device copy in the same run."""
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the workload's dominant kernels (the two
+    FFN GEMM kernels, or the persistent kernel), each scaled by (known bytes / counter) of a
+    plain 1 GiB device copy in the same run."""
     kname = TRAFFIC[config][1]
-    rec = {"workload": configs.CONFIGS[config].name, "source_sha": gemm_source_sha(config)}
+    persistent = config.endswith("/persistent")
+    rec = {"workload": configs.CONFIGS[config.split("/")[0]].name, "kernel": kname,
+           "source_sha": gemm_source_sha(config)}
     for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = _per_dispatch(path, counter)
         cal = [v for k, v in rows if "copyBuffer" in k and 0.5 * CAL_BYTES < v < 2.0 * CAL_BYTES]
         if not cal:
             raise SystemExit(f"no 1 GiB copy dispatch found in {path}")
         factor = CAL_BYTES / float(np.median(cal))
-        g = {}
-        for mode in (0, 1):
-            vals = [v for k, v in rows if f"{kname}<{mode}>" in k]
-            g[mode] = float(np.median(vals)) * factor
-        rec[name] = {"copy_factor": factor, "gemm1_bytes": g[0], "gemm2_bytes": g[1]}
-    rec["bytes_per_step"] = (rec["fetch"]["gemm1_bytes"] + rec["fetch"]["gemm2_bytes"] +
-                             rec["write"]["gemm1_bytes"] + rec["write"]["gemm2_bytes"])
+        if persistent:
+            vals = [v for k, v in rows if kname in k]
+            rec[name] = {"copy_factor": factor, "kernel_bytes": float(np.median(vals)) * factor}
+        else:
+            g = {}
+            for mode in (0, 1):
+                vals = [v for k, v in rows if f"{kname}<{mode}>" in k]
+                g[mode] = float(np.median(vals)) * factor
+            rec[name] = {"copy_factor": factor, "gemm1_bytes": g[0], "gemm2_bytes": g[1]}
+    if persistent:
+        rec["bytes_per_step"] = rec["fetch"]["kernel_bytes"] + rec["write"]["kernel_bytes"]
+    else:
+        rec["bytes_per_step"] = (rec["fetch"]["gemm1_bytes"] + rec["fetch"]["gemm2_bytes"] +
+                                 rec["write"]["gemm1_bytes"] + rec["write"]["gemm2_bytes"])
     os.makedirs(os.path.dirname(traffic_file(config)), exist_ok=True)
     json.dump(rec, open(traffic_file(config), "w"), indent=1)
     print(json.dumps(rec))
@@ -583,7 +597,7 @@ def run_persistent_sweep(args, cfg, P, stream):
 def main():
     args = parse()
     if args.write_traffic:
-        write_traffic(args.config, *args.write_traffic)
+        write_traffic(args.config + ("/persistent" if args.persistent else ""), *args.write_traffic)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -605,6 +619,18 @@ def main():
     P = DeviceProblem(cfg, inp, device=dev)
     stream = torch.cuda.current_stream()
 
+    # the timed path: the persistent megakernel for bf16 (every step of the share, the CU
+    # partition and the ring included) unless another is asked for; the fused multi-kernel path
+    # for the other dtypes (the persistent kernel is bf16 only)
+    if args.unfused:
+        path = "unfused"
+    elif args.fused:
+        path = "fused"
+    elif args.persistent or (cfg.dtype == "bf16" and not (args.backward or args.sweep_tokens)):
+        path = "persistent"
+    else:
+        path = "fused"
+    args.persistent = path == "persistent"
     if args.persistent or args.sweep_persistent:
         P.ex = moe.Exec(args.minibatch or cfg.minibatch, 0, 0, 0, 0)
         P.alloc_ring(args.ring_mib or cfg.ring_mib, persistent_exec(args, cfg))
@@ -674,6 +700,30 @@ def main():
                 for j, n in enumerate(names)}
     per_step = [ev[i][0].elapsed_time(ev[i][len(names)]) for i in range(args.steps)]
     log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; stages {stage_ms}")
+    compare = None
+    if args.persistent and not args.no_compare:
+        # context: the fused multi-kernel path on the same inputs (pull fused into the gate/up
+        # GEMM, push into the down GEMM; no CU partition, no ring, h staged at worst-case size)
+        P.forward_fused()
+        torch.cuda.synchronize()
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            cev[i][0].record(stream)
+            P.layout()
+            cev[i][1].record(stream)
+            P.ffn_push(pull=True)
+            cev[i][2].record(stream)
+            P.merge()
+            cev[i][3].record(stream)
+        torch.cuda.synchronize()
+        cst = [cev[i][0].elapsed_time(cev[i][3]) for i in range(args.steps)]
+        cffn = float(np.mean([cev[i][1].elapsed_time(cev[i][2]) for i in range(args.steps)]))
+        cms = float(np.mean(cst))
+        compare = {"path": "fused multi-kernel (layout, FFN with the pull fused into the gate/up GEMM and the push "
+                           "into the down GEMM, merge; no CU partition, no ring, h staged at worst-case size)",
+                   "ms_per_step": cms, "tokens_per_s": cfg.R * cfg.T / cfg.G / (cms * 1e-3), "ffn_ms": cffn,
+                   "ffn_frac_bf16_peak": 6.0 * cfg.d * cfg.F * N / (cffn * 1e-3) / PEAK_BF16_FLOPS}
+        log(f"[bench] fused multi-kernel path for comparison: {cms:.3f} ms/step (FFN {cffn:.3f} ms)")
     graph = None
     if args.graph:
         side = torch.cuda.Stream()
@@ -745,7 +795,7 @@ def main():
     merge_bytes = 1.0 * N * row + cfg.R * cfg.T * row
     tokens = cfg.R * cfg.T / cfg.G
     value = tokens / (ms_step * 1e-3)
-    traffic = traffic_bytes(args.config)
+    traffic = traffic_bytes(args.config + "/persistent" if args.persistent else args.config)
     result = {
         "metric": METRIC,
         "value": value,
@@ -812,6 +862,8 @@ def main():
         # the fused path: the pull and push bytes moved inside the FFN kernels, over the FFN time
         if not args.unfused and cfg.dtype != "mxfp8":
             result["stages_hbm_frac"]["dispatch+combine fused in the FFN"] = (gather_bytes + push_bytes) / t_ffn / PEAK_HBM
+    if compare:
+        result["fused_multi_kernel"] = compare
     if graph:
         result["graph"] = graph
     if cold:
