@@ -190,8 +190,12 @@ int moe_dispatch_pull(const moe_shape_t* s, const moe_placement_t* p, const void
  * xe_scales as moe_dispatch_pull writes them, weights as E4M3 codes with w_scales
  * (moe_mx_quantize of the bf16 weights); h is quantised along F in GEMM1's epilogue
  * (fp32 h, the same rule); ye is bf16 with fp32 accumulation.  d and F must be
- * multiples of 128.  Accuracy: max row-relative error <= 1e-2 against the fp64 forward
- * on the dequantised operands.  xe_scales and w_scales are ignored for other dtypes.
+ * multiples of 128.  Accuracy against the fp64 forward on the dequantised operands (with
+ * h quantised from its fp64 value): max row-relative error <= 6e-2 and relative Frobenius
+ * error <= 5e-3; h is quantised from fp32, so an h code may differ from that reference's
+ * by one E4M3 step where the value lies within fp32 rounding of the midpoint, and each
+ * output element then lies within the effect of those steps plus one bf16 rounding.
+ * xe_scales and w_scales are ignored for other dtypes.
  */
 int moe_expert_ffn(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
                    const void* xe, const uint8_t* xe_scales, const int32_t* offsets, const void* w1,

@@ -112,15 +112,16 @@ __global__ __launch_bounds__(256) void pair_addr_kernel(const int32_t* __restric
 // segment are issued before any is used, so a task costs one memory round trip per j.
 // Measured on MI355X at the DeepSeek-V3 share: short segments (VPL 4) and a grid of 16
 // blocks per CU keep the most rows in flight (180 us against 199 us for VPL 8 with 4
-// blocks per CU); prefetching the next task's metadata changed less than 1 %.
-template <bool BF16>
+// blocks per CU); prefetching the next task's metadata changed less than 1 %.  A row whose
+// vector count is a multiple of 64 * 7 (d = 7168 in bf16: 896 vectors) takes VPL 7, which
+// splits it into two full segments instead of three and a half.
+template <bool BF16, int VPL>
 __global__ __launch_bounds__(256) void weighted_merge_kernel(RankPtrs<const char*> recv,
                                                              RankPtrs<char*> y,
                                                              const int32_t* __restrict__ slot_of,
                                                              const float* __restrict__ topk_w, int R,
                                                              int T, int k, int d) {
   constexpr int EPV = BF16 ? 8 : 4;      // elements per 16-byte vector
-  constexpr int VPL = 4;                 // vectors per lane per segment
   const int lane = threadIdx.x & 63;
   const int row_bytes = d * (BF16 ? 2 : 4);
   const int n16 = row_bytes >> 4;
@@ -246,12 +247,19 @@ hipError_t launch_merge(const moe_shape_t& s, const int32_t* slot_of, const floa
     rcp.p[r] = static_cast<const char*>(recv[r]);
     yp.p[r] = static_cast<char*>(y[r]);
   }
-  if (s.dtype != MOE_F32)
-    hipLaunchKernelGGL(weighted_merge_kernel<true>, dim3(cus * kMergeBlocksPerCU), dim3(256), 0, st, rcp, yp, slot_of, topk_w,
-                       s.R, s.T, s.k, s.d);
-  else
-    hipLaunchKernelGGL(weighted_merge_kernel<false>, dim3(cus * kMergeBlocksPerCU), dim3(256), 0, st, rcp, yp, slot_of, topk_w,
-                       s.R, s.T, s.k, s.d);
+  const int n16 = s.d * (s.dtype == MOE_F32 ? 4 : 2) / 16;
+  const dim3 grid(cus * kMergeBlocksPerCU);
+  if (s.dtype != MOE_F32) {
+    if (n16 % (64 * 7) == 0)
+      hipLaunchKernelGGL((weighted_merge_kernel<true, 7>), grid, dim3(256), 0, st, rcp, yp, slot_of, topk_w, s.R, s.T,
+                         s.k, s.d);
+    else
+      hipLaunchKernelGGL((weighted_merge_kernel<true, 4>), grid, dim3(256), 0, st, rcp, yp, slot_of, topk_w, s.R, s.T,
+                         s.k, s.d);
+  } else {
+    hipLaunchKernelGGL((weighted_merge_kernel<false, 4>), grid, dim3(256), 0, st, rcp, yp, slot_of, topk_w, s.R, s.T,
+                       s.k, s.d);
+  }
   return hipGetLastError();
 }
 

@@ -178,9 +178,12 @@ __device__ void wg_copy_rows(const uint64_t* src, const uint64_t* dst, int nrows
   }
 }
 
-// Zero the control block and build every pipeline's group and phase tables (one block).
+// Zero the control block and build every pipeline's group and phase tables (one block; the
+// per-expert row-tile prefix is staged in LDS first, so the group walk reads no global memory).
 __global__ __launch_bounds__(1024) void persist_prep_kernel(PersistArgs A, int zero_words) {
+  __shared__ int32_t mtb[1025];                 // E_local <= E <= 1024
   for (int i = threadIdx.x; i < zero_words; i += blockDim.x) A.pc[i] = 0;
+  for (int i = threadIdx.x; i <= A.El; i += blockDim.x) mtb[i] = A.mtile_base[i];
   if (A.trace && threadIdx.x == 0) *A.trace_count = 0;
   __syncthreads();
   const int p = threadIdx.x;
@@ -190,7 +193,6 @@ __global__ __launch_bounds__(1024) void persist_prep_kernel(PersistArgs A, int z
   sched::pipe_range(n_mt, A.n_part, p, &lo, &hi);
   int32_t* gf = A.pc + A.cl.grp_first + lo;
   int32_t* gl = A.pc + A.cl.grp_len + lo;
-  const int32_t* mtb = A.mtile_base;
   const int El = A.El;
   const int n = sched::build_groups(lo, hi, A.G, [&](int m) { return find_expert(mtb, El, m); }, gf, gl);
   const int NT1 = (A.F + kGemmBN / 2 - 1) / (kGemmBN / 2);

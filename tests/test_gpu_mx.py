@@ -5,7 +5,11 @@ fp32 values on and next to every rounding midpoint; the quantise-on-gather of
 moe_dispatch_pull; the offline weight codes); layout bit-exact; outputs against
 Oracle-Q, the fp64 forward on the dequantised operands: max row-relative error <= 6e-2
 (the stated MXFP8 bound) and relative Frobenius error <= 5e-3; rows with no local expert
-exactly 0.
+exactly 0.  test_mx_h_decisions_and_output_bound pins what lies between those bars: every
+h code the device chose differently from the oracle's quantisation of the fp64 h is one
+E4M3 step away and its value lies within the fp32 error bound of that step's midpoint, and
+every FFN output element lies within the exact effect of those flips plus one bf16
+rounding (a bound per element, derived, not measured).
 
 Why two bars: h is quantised from fp32 on the GPU and from fp64 in the oracle, so a few
 of its rounding decisions differ (the fp32 h carries ~1e-6 relative error); one flipped
@@ -29,6 +33,12 @@ pytestmark = pytest.mark.gpu
 
 TOL_Q_ROW = 6e-2
 TOL_Q_FRO = 5e-3
+# Accumulation allowance of a scaled FP8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4): its 64
+# products per K step are not summed at full fp32 precision (measured on MI355X: the down
+# GEMM lies up to 2.5e-5 = 2^-15.3 of sum|h w| off the exact product of its own operands
+# beyond one bf16 rounding); the bound allows 2^-13 of the sum of absolute products, which a
+# wrong scale or a dropped K block (percent of that sum) still exceeds by far.
+ACC_MX = 2.0 ** -13
 
 
 def _say(msg):
@@ -305,3 +315,136 @@ def test_mx_forward_full_dsv3_sampled():
     for a, b in zip(P.y, y_ref):
         assert torch.equal(a, b)
     _say("  fused push: y bit-identical")
+
+
+# --------------------------------------------------------------------------- h decisions
+def _h_device(P, cfg, N):
+    """The device's h of the unfused forward (MXFP8 codes [N][F] and block scale codes
+    [N][F/32]) from the workspace's h staging, which starts where the persistent workspace
+    ends (the same layout: control words and tables first, h staging after them)."""
+    F = cfg.F
+    hb = moe.moe_persistent_workspace_bytes(P.shape, P.placement)
+    nmax = P.nmax
+    codes = P.ws[hb: hb + N * F].cpu().numpy().reshape(N, F)
+    soff = hb + ((nmax * F + 255) // 256) * 256
+    sc = P.ws[soff: soff + (F // 128) * nmax * 4].view(F // 128, nmax, 4)
+    return codes, P.scales_rowmajor(sc, N)
+
+
+@pytest.mark.parametrize("name", list(MX_CASES))
+def test_mx_h_decisions_and_output_bound(name):
+    """h decisions and a per-element output bound.
+
+    (1) Scale codes of h equal the oracle's quantisation of the fp64 h, except blocks whose
+    fp64 amax lies within the fp32 error bound of a power of two.  (2) Every E4M3 code that
+    differs is the rounding of a value within the fp32 error bound of the fp64 h (the fp64
+    value lies within that bound of the code's rounding interval: next to a midpoint, or,
+    where cancellation leaves h near zero, on the other side of zero); such flips are rare.
+    The bound
+    on the device's fp32 h: a = x.W1 and b = x.W3 accumulate K / 64 products of exactly
+    representable E4M3 x E4M3 values per scaled MFMA, so each sum is off by at most
+    (K / 32) 2^-24 sum|x w|; silu (hardware exp) and the product add a few ulps of h.
+    (3) Each element of the FFN output (ye, bf16) lies within |hq_dev - hq_oracle| . |W2q|
+    (the effect of the flipped codes, exactly) + one bf16 rounding + the fp32 accumulation
+    bound of the oracle's value; and within one bf16 rounding + accumulation of the fp64
+    product of the device's own dequantised h, which pins the down GEMM alone."""
+    torch = _torch()
+    cfg = MX_CASES[name]
+    _say(f"[mx-h] {cfg.name}")
+    inp, P = _problem(cfg)
+    P.forward()
+    assert P.status() == 0
+    torch.cuda.synchronize()
+    N = P.N()
+    hc_dev, hs_dev = _h_device(P, cfg, N)
+    ye_dev = P.rows_f64(P.ye[:N])
+    qw = _oracle_weights(inp, range(cfg.E_local))
+    ref = MX.forward_q(inp.logits, inp.x_f32, *[[qw[l][i][2] for l in range(cfg.E_local)] for i in range(3)],
+                       inp.expert_to_local, cfg.E_local, cfg.k)
+    xeq, off = ref["xeq"], ref["offsets"]
+    K, F = cfg.d, cfg.F
+    acc = ACC_MX
+    flips = scale_flips = 0
+    worst_acc = worst_row = worst_bar = 0.0
+    allowed = 0.0
+    fin = MX.e4m3_decode(np.arange(256, dtype=np.uint8))
+    grid = np.unique(fin[np.isfinite(fin)])             # the signed E4M3 values, ascending
+    worst_ratio = 0.0
+    for l in range(cfg.E_local):
+        a0, a1 = int(off[l]), int(off[l + 1])
+        if a1 == a0:
+            continue
+        x = xeq[a0:a1]
+        w1, w3, w2 = (qw[l][i][2] for i in range(3))
+        A, B = x @ w1.T, x @ w3.T
+        Sa, Sb = np.abs(x) @ np.abs(w1).T, np.abs(x) @ np.abs(w3).T
+        with np.errstate(over="ignore"):
+            sig = 1.0 / (1.0 + np.exp(-A))
+        H = A * sig * B
+        dsilu = sig * (1.0 + A * (1.0 - sig))
+        err_h = np.abs(dsilu * B) * acc * Sa + np.abs(A * sig) * acc * Sb + 2.0 ** -20 * np.abs(H)
+        rc, rs, rq = MX.quantize(H)
+        dc, ds = hc_dev[a0:a1], hs_dev[a0:a1]
+        # (1) scale codes
+        amax = np.abs(H).reshape(a1 - a0, F // 32, 32).max(-1)
+        eb = err_h.reshape(a1 - a0, F // 32, 32).max(-1)
+        sbad = ds != rs
+        if sbad.any():
+            p2 = 2.0 ** np.round(np.log2(amax[sbad]))
+            assert (np.abs(amax[sbad] - p2) <= eb[sbad]).all(), "a scale code differs away from a power of two"
+            scale_flips += int(sbad.sum())
+        same_scale = np.repeat(~sbad, 32, axis=1)
+        # (2) element codes, where the block scale agrees: the device's code must be the
+        # rounding of some value within the fp32 bound of the fp64 value, i.e. the fp64
+        # value lies within that bound of the code's rounding interval (the midpoints to its
+        # neighbours on the E4M3 grid; the saturated ends are open)
+        bad = (dc != rc) & same_scale
+        # flips the bound allows: a value lies within tol of a midpoint with probability
+        # min(1, 2 tol / step), step the E4M3 grid step at its magnitude
+        e_all = np.ldexp(1.0, np.repeat(ds, 32, axis=1).astype(np.int64) - 127)
+        v_all = np.abs(H) / e_all
+        _, ex_all = np.frexp(np.maximum(v_all, 2.0 ** -9))
+        step_all = np.ldexp(1.0, np.maximum(ex_all - 1, -6) - 3)
+        allowed += float(np.minimum(1.0, 2.0 * (err_h / e_all) / step_all)[same_scale].sum())
+        if bad.any():
+            r_i, f_i = np.nonzero(bad)
+            e = np.ldexp(1.0, ds[r_i, f_i // 32].astype(np.int64) - 127)
+            v = H[r_i, f_i] / e
+            qd = MX.e4m3_decode(dc[r_i, f_i])
+            pos = np.searchsorted(grid, qd)
+            lower = np.where(pos > 0, (grid[np.maximum(pos - 1, 0)] + qd) / 2.0, -np.inf)
+            upper = np.where(pos + 1 < len(grid), (grid[np.minimum(pos + 1, len(grid) - 1)] + qd) / 2.0, np.inf)
+            dist = np.maximum(0.0, np.maximum(lower - v, v - upper))
+            tol = err_h[r_i, f_i] / e
+            ratio = dist / np.maximum(tol, 1e-300)
+            worst = int(np.argmax(ratio))
+            assert (ratio <= 1.0).all(), (f"a flipped code lies {ratio[worst]:.2f} bounds outside its rounding interval: "
+                                          f"value {v[worst]!r}, device code value {qd[worst]!r}, "
+                                          f"oracle code value {MX.e4m3_decode(rc[r_i, f_i])[worst]!r}, bound {tol[worst]!r}")
+            worst_ratio = max(worst_ratio, float(ratio.max()))
+            flips += len(r_i)
+        # (3) the FFN output rows of this expert
+        hq_dev = MX.dequantize(dc, ds)
+        yref_dev = hq_dev @ w2.T
+        yref_q = rq @ w2.T
+        acc2 = ACC_MX * (np.abs(hq_dev) @ np.abs(w2).T)
+        bf = 2.0 ** -8 * np.abs(yref_dev)
+        ye = ye_dev[a0:a1]
+        dev_err = np.abs(ye - yref_dev)
+        over = np.maximum(dev_err - bf, 0.0) / np.maximum(acc2 / ACC_MX, 1e-300)
+        worst_acc = max(worst_acc, float(over.max()))
+        assert (dev_err <= bf + acc2 + 1e-30).all(), "down GEMM off its own h beyond bf16 rounding + accumulation"
+        flip_term = np.abs(hq_dev - rq) @ np.abs(w2).T
+        err_q = np.abs(ye - yref_q)
+        bound_q = flip_term + bf + acc2
+        assert (err_q <= bound_q + 1e-30).all(), "FFN output outside the bound of its h flips"
+        rows_rel = err_q.max(1) / np.abs(yref_q).max(1)
+        bar_rel = bound_q.max(1) / np.abs(yref_q).max(1)
+        worst_row = max(worst_row, float(rows_rel.max()))
+        worst_bar = max(worst_bar, float(bar_rel.max()))
+    frac = flips / max(1, N * F)
+    _say(f"  N={N}: h codes flipped {flips} ({frac:.1e} of all; the bound allows {allowed:.0f}), all within their bound "
+         f"(worst at {worst_ratio:.2f} of it); scale codes flipped {scale_flips}; down-GEMM accumulation "
+         f"{worst_acc:.2e} of sum|h w| beyond one bf16 rounding; FFN rows vs Oracle-Q worst {worst_row:.3e}, "
+         f"their derived bars up to {worst_bar:.3e}")
+    assert flips <= allowed

@@ -268,11 +268,14 @@ def test_forward_deterministic_and_stagewise_equals_fused_call():
 
 
 @pytest.mark.slow
-def test_forward_full_dsv3_sampled():
-    """Full DeepSeek-V3-shaped share, the launch configuration the bench times;
-    layout compared whole, outputs compared on sampled tokens computed one by one."""
+@pytest.mark.parametrize("cfg", [configs.DSV3, configs.DSV3_SKEW], ids=["dsv3", "dsv3-zipf"])
+def test_forward_full_dsv3_sampled(cfg):
+    """Full DeepSeek-V3-shaped share (uniform load, and Zipf(1.2) load whose hottest local
+    expert holds ~10x the mean rows), the launch configuration the bench times; layout
+    compared whole, outputs compared on sampled tokens computed one by one: 40 random tokens
+    with a local pair, plus the tokens of the first, middle and last rows of the hottest local
+    expert's first, middle and last 256-row tiles."""
     torch = _torch()
-    cfg = configs.DSV3
     _say(f"[forward-full] {cfg.name}")
     inp, P = _problem(cfg)
     P.forward()
@@ -287,7 +290,16 @@ def test_forward_full_dsv3_sampled():
     rng = np.random.default_rng(0)
     has = (lay["slot_of"] >= 0).any(-1)
     local_tok = np.argwhere(has)
-    pick = local_tok[rng.choice(len(local_tok), 40, replace=False)]
+    pick = [tuple(v) for v in local_tok[rng.choice(len(local_tok), 40, replace=False)]]
+    off = lay["offsets"]
+    cnt = np.diff(off)
+    hot = int(np.argmax(cnt))
+    tiles = (int(cnt[hot]) + 255) // 256
+    for tile in sorted({0, tiles // 2, tiles - 1}):
+        t0 = int(off[hot]) + 256 * tile
+        t1 = min(t0 + 256, int(off[hot + 1]))
+        for srow in sorted({t0, (t0 + t1) // 2, t1 - 1}):
+            pick.append(tuple(int(v) for v in lay["pull_src"][srow]))
     worst = 0.0
     for r, t in pick:
         yr = O.token_output(inp.x_f32[r, t], idx[r, t], g[r, t], inp.expert_to_local, inp.w1_f32,
@@ -296,10 +308,11 @@ def test_forward_full_dsv3_sampled():
         worst = max(worst, float(np.abs(yg - yr).max() / np.abs(yr).max()))
     zr, zt = np.argwhere(~has)[0]
     assert (P.y[zr][zt].float().cpu().numpy() == 0).all()
-    _say(f"  N={lay['N']} sampled y_rel={worst:.3e}")
+    _say(f"  N={lay['N']} hottest local expert {hot}: {int(cnt[hot])} rows ({cnt[hot] / cnt.mean():.1f}x mean, "
+         f"{tiles} row tiles); {len(pick)} sampled tokens y_rel={worst:.3e}")
     assert worst <= TOL["bf16"]
-    # the launch configuration the bench times (pull and push fused into the GEMMs): bit for
-    # bit the same y as the unfused path just checked
+    # the fused multi-kernel configuration (pull and push fused into the GEMMs) and the
+    # persistent megakernel the bench times: bit for bit the same y as the unfused path
     y_ref = [t.clone() for t in P.y]
     for t in P.y:
         t.fill_(float("nan"))
@@ -308,7 +321,15 @@ def test_forward_full_dsv3_sampled():
     torch.cuda.synchronize()
     for a, b in zip(P.y, y_ref):
         assert torch.equal(a, b)
-    _say("  fused pull and push: y bit-identical")
+    for t in P.y:
+        t.fill_(float("nan"))
+    P.alloc_ring(cfg.ring_mib)
+    P.forward_persistent(moe.Exec(cfg.minibatch, 16, 0, 0, 0))
+    assert P.status() == 0
+    torch.cuda.synchronize()
+    for a, b in zip(P.y, y_ref):
+        assert torch.equal(a, b)
+    _say("  fused pull and push, and the persistent kernel: y bit-identical")
 
 
 # --------------------------------------------------------------------------- metamorphic
