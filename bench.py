@@ -491,7 +491,7 @@ def run_sweep(args, cfg, P, stream):
     sized for T tokens per rank; each point lowers the shape's T in place (every call reads
     the first T rows of each rank's token and logit buffers) and times `args.steps` steps."""
     import torch
-    fwd = P.forward if args.unfused else P.forward_fused
+    fwd = P.forward_persistent if args.persistent else (P.forward if args.unfused else P.forward_fused)
     T_full = P.shape.T
     for t in [int(v) for v in args.sweep_tokens.split(",")]:
         if not 1 <= t <= T_full:
@@ -517,7 +517,7 @@ def run_sweep(args, cfg, P, stream):
                 "source_tokens": cfg.R * t, "local_pairs": n, "ms_per_call": ms,
                 "us_per_source_token": ms * 1e3 / (cfg.R * t), "gemm1_tiles": tiles1,
                 "gemm1_waves": tiles1 / 256.0, "workload": cfg.name,
-                "path": "unfused" if args.unfused else "fused pull and push"}
+                "path": "persistent" if args.persistent else ("unfused" if args.unfused else "fused pull and push")}
         print(json.dumps(line), flush=True)
         log(f"[sweep] T={t}: {ms:.3f} ms, N={n}, GEMM1 tiles {tiles1} ({tiles1 / 256:.2f} waves)")
     P.shape.T = T_full
@@ -557,6 +557,33 @@ def trace_summary(ev, tpu, grid):
     if len(ff):
         out["first_gemm_us"] = float(ff["t_begin"].min() - t0) / tpu
         out["last_gemm_end_us"] = float(ff["t_end"].max() - t0) / tpu
+    # per task kind: mean / max duration and mean wait before it
+    out["tasks"] = {}
+    for k, name in ((1, "gather"), (2, "push"), (3, "gate_up"), (4, "down")):
+        e = ev[ev["kind"] == k]
+        if len(e):
+            d = (e["t_end"] - e["t_begin"]) / tpu
+            out["tasks"][name] = {"n": int(len(e)), "us_mean": float(d.mean()), "us_max": float(d.max()),
+                                  "wait_us_mean": float((e["t_wait"] / tpu).mean())}
+    # per pipeline: row tiles, end of its last GEMM and of its last task
+    out["pipelines"] = []
+    for p in np.unique(ev["pipeline"]):
+        e = ev[ev["pipeline"] == p]
+        c = e[np.isin(e["kind"], (3, 4))]
+        out["pipelines"].append({"pipeline": int(p), "workgroups": int((e["kind"] == 0).sum()),
+                                 "row_tiles": int(len(np.unique(c["index"] // 256))) if len(c) else 0,
+                                 "last_gemm_end_us": float(c["t_end"].max() - t0) / tpu if len(c) else 0.0,
+                                 "end_us": float(e["t_end"].max() - t0) / tpu,
+                                 "compute_wait_ms": float(c["t_wait"].sum()) / tpu / 1e3})
+    # busy compute workgroups per 100 us of the span
+    nb = int(np.ceil(span / tpu / 100.0)) + 1
+    occ = np.zeros(nb)
+    for b0, b1 in zip((ff["t_begin"] - t0) / tpu, (ff["t_end"] - t0) / tpu):
+        for i in range(int(b0 // 100), min(nb, int(b1 // 100) + 1)):
+            lo, hi = max(b0, i * 100.0), min(b1, (i + 1) * 100.0)
+            if hi > lo:
+                occ[i] += (hi - lo) / 100.0
+    out["busy_compute_workgroups_per_100us"] = [round(float(v), 1) for v in occ]
     return out
 
 

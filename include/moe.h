@@ -306,8 +306,9 @@ int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_
  * workgroup per CU, ordinary launch), a completion check, the weighted merge.
  * Roles: in each pipeline the first comm_cus / pipelines workgroups to start move data --
  * they gather chunks of token rows from the source buffers into free ring slots and push
- * finished output rows to recv, freeing the slots -- and the others take GEMM tasks in
- * ticket order, then join the data movement once their pipeline has no task left.  Row tiles (256 rows of one expert) are split evenly over the pipelines:
+ * finished output rows to recv chunk by chunk, freeing the slots -- and the others take
+ * GEMM tasks in ticket order (gathering claimable chunks themselves while a task waits for
+ * its rows), then join the data movement once their pipeline has no task left.  Row tiles (256 rows of one expert) are split evenly over the pipelines:
  * eight (one per XCD, every hand-off inside one L2) when each XCD's share of the ring holds
  * two groups, else fewer, with agent-scope hand-offs.  Up to G consecutive row tiles of one
  * expert form a group whose GEMM tasks run weight-panel-major, so concurrent tasks share
@@ -387,7 +388,7 @@ typedef struct {
   int64_t t_begin;   /* task start (after its waits) */
   int64_t t_end;     /* task end (its completion signal sent) */
   int32_t t_wait;    /* ticks spent waiting (or, for a mover, idle) before t_begin */
-  int32_t index;     /* gather: pipeline-local chunk; push: row tile; GEMM: row_tile * 256 + column tile;
+  int32_t index;     /* gather, push: pipeline-local chunk; GEMM: row_tile * 256 + column tile;
                         start / end: 0 = data movement, 1 = compute */
   int32_t workgroup; /* blockIdx.x */
   int16_t kind;      /* MOE_TRACE_* */

@@ -160,8 +160,9 @@ __device__ __forceinline__ uint32_t lds_addr(const char* q) {
       : "v"(C.a0), "v"(C.b0), "v"(C.b1), "v"(C.b2), "v"(C.b3), "v"(AA), "v"(BA))
 
 // b0/b1: this expert's weight matrices ([Nout][K], row stride b_ld); c0: first output
-// column of the tile.
-template <int MODE>
+// column of the tile.  A_CPOL: cache policy of the A-row loads (0 = default; 16 = sc1, a
+// device-coherent load that does not hit this CU's L1, for rows another CU just wrote).
+template <int MODE, int A_CPOL = 0>
 __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __restrict__ b0,
                                           const uint16_t* __restrict__ b1, int c0, int Nout, int K,
                                           char* smem, int b_ld) {
@@ -205,7 +206,7 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int g = wave * 4 + i;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(ap[i] + koff), (lds_void_ptr)(sa + g * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(ap[i] + koff), (lds_void_ptr)(sa + g * 1024), 16, 0, A_CPOL);
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(bp[i] + koff), (lds_void_ptr)(sb + g * 1024), 16, 0, 0);
     }
   };

@@ -44,7 +44,7 @@ constexpr int kPipeWords = 16;        // control words per pipeline
 enum PipeWord {
   kJoin = 0,        // workgroups that joined (arrival order = rank)
   kGatherNext = 1,  // next chunk to claim for gathering
-  kPushNext = 2,    // next row tile to claim for pushing
+  kPushNext = 2,    // next chunk to claim for pushing
   kTicketNext = 3,  // next compute ticket
   kNGroups = 4,     // groups (written by the preparation kernel)
   kNTickets = 5,    // compute tasks
@@ -176,15 +176,19 @@ MOE_HD int slot_epoch_word(const CtrlLayout& cl, int p, int S, int q) { return c
 enum MoverAct { kIdle = 0, kPush = 1, kGather = 2, kDone = 3 };
 
 // One claim attempt of a data-movement workgroup (thread 0).  Pushes go first: they free
-// ring slots.  A push of row tile lo + c is claimable once all its down tiles finished; a
-// gather of chunk q once its slot's previous occupant was pushed.  Claims are CAS on the
-// pipeline's in-order counters, so every chunk and row tile is claimed exactly once, in
-// order.  Ops: ld(word) -> int (relaxed atomic load), cas(word, expected, desired) -> bool.
+// ring slots.  The push of pipeline-local chunk c is claimable once every down tile of its
+// row tile lo + c / cpm finished; a gather of chunk q once its slot's previous occupant was
+// pushed.  Claims are CAS on the pipeline's in-order counters, so every chunk is gathered
+// and pushed exactly once, in order.  With gather_only, only a gather is tried (a compute
+// workgroup that waits for a chunk helps gathering instead of spinning).  Ops: ld(word) ->
+// int (relaxed atomic load), cas(word, expected, desired) -> bool.
 template <class Ops>
-MOE_HD int mover_claim(Ops& ops, const CtrlLayout& cl, int p, int lo, int n_m, int cpm, int S, int NT2, int* arg) {
+MOE_HD int mover_claim(Ops& ops, const CtrlLayout& cl, int p, int lo, int n_m, int cpm, int S, int NT2, int* arg,
+                       bool gather_only = false) {
   const int pipe_base = cl.pipe0 + p * kPipeWords;
-  const int ci = ops.ld(pipe_base + kPushNext);
-  if (ci < n_m && ops.ld(cl.g2_done + lo + ci) >= NT2) {
+  const int n_chunks = n_m * cpm;
+  const int ci = gather_only ? n_chunks : ops.ld(pipe_base + kPushNext);
+  if (ci < n_chunks && ops.ld(cl.g2_done + lo + ci / cpm) >= NT2) {
     if (ops.cas(pipe_base + kPushNext, ci, ci + 1)) {
       *arg = ci;
       return kPush;
@@ -192,14 +196,14 @@ MOE_HD int mover_claim(Ops& ops, const CtrlLayout& cl, int p, int lo, int n_m, i
     return kIdle;                             // lost the race: try again next round
   }
   const int qi = ops.ld(pipe_base + kGatherNext);
-  if (qi < n_m * cpm && ops.ld(slot_epoch_word(cl, p, S, qi)) >= chunk_epoch(qi, S)) {
+  if (qi < n_chunks && ops.ld(slot_epoch_word(cl, p, S, qi)) >= chunk_epoch(qi, S)) {
     if (ops.cas(pipe_base + kGatherNext, qi, qi + 1)) {
       *arg = qi;
       return kGather;
     }
     return kIdle;
   }
-  if (ci >= n_m && qi >= n_m * cpm) return kDone;
+  if (ci >= n_chunks && qi >= n_chunks) return kDone;
   return kIdle;
 }
 

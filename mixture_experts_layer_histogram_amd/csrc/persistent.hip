@@ -24,8 +24,10 @@
 //   enough, the row tiles are split into eight pipelines, one per XCD (the kernel reads the
 //   XCC id from the hardware), each with its own ring partition and counters: every
 //   producer -> consumer hand-off stays inside one L2 (stores waited for, then a relaxed
-//   counter bump; the consumer invalidates its CU's L1).  Otherwise pipelines span XCDs and
-//   hand-offs use agent-scope release/acquire.
+//   counter bump, no L2 write-back; the consumer reads the data with device-coherent sc1
+//   loads, which bypass its CU's L1).  Otherwise pipelines span XCDs and hand-offs use
+//   agent-scope release/acquire (the producer also writes back its XCD's L2, the consumer
+//   drops stale lines of its own).
 // * Ring slot.  One minibatch (chunk) of token rows, overwritten in place by the expert
 //   outputs of those rows, followed by the rows' h.
 // * Watchdog.  Every wait is bounded by a wall-clock budget; on expiry the workgroup sets
@@ -87,8 +89,16 @@ __device__ __forceinline__ void release_add(int32_t* ctr, int v, bool light) {
 }
 
 // Consumer side, after the workgroup observed the counter: make the producer's data visible.
+// Light (same XCD, one L2): nothing to invalidate, because every read of data another CU
+// wrote during the kernel (ring rows in the GEMMs' A loads and in the push) is a device-
+// coherent sc1 load, which does not hit this CU's L1.  The L1 must be kept out of it: a
+// CU that touched a slot's lines earlier (it gathered into the slot, or read its previous
+// contents) still holds them, and a workgroup-scope invalidate (buffer_inv sc0) leaves them
+// in place (measured on MI355X: a push then copied stale input lines instead of the expert
+// output).  Across XCDs: an agent-scope acquire (buffer_inv sc1) also drops the stale lines
+// of this XCD's L2.
 __device__ __forceinline__ void acquire_after_poll(bool light) {
-  if (light) asm volatile("buffer_inv sc0" ::: "memory");     // this CU's L1; the L2 is shared
+  if (light) asm volatile("" ::: "memory");
   else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
@@ -141,12 +151,27 @@ __device__ __forceinline__ void trace_event(const PersistArgs& A, int kind, int 
 typedef __attribute__((address_space(1))) const u32x4* gsrc_t;
 typedef __attribute__((address_space(1))) u32x4* gdst_t;
 
+// 16 bytes at vector c of the row at `row` (c < n16).  SC1: a device-coherent load (sc1, no
+// L1 hit) through a buffer resource spanning the row.
+template <bool SC1>
+__device__ __forceinline__ u32x4 row_load(uint64_t row, int c, int n16) {
+  if constexpr (SC1) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(row), (short)0, n16 * 16, 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, c * 16, 0, 16);
+  } else {
+    return reinterpret_cast<gsrc_t>(row)[c];
+  }
+}
+
 // Copy nrows rows of n16 16-byte vectors from src[r] to dst[r] (row addresses staged in
 // LDS) with the whole workgroup.  Each wave moves two rows at a time (r and r + 8), 16
-// vectors per lane of each: 32 outstanding 16-byte global loads per lane (224 KiB per
-// workgroup for 14 KiB rows).  The loads are unconditional (columns past the row end are
-// clamped to its last vector; a lone last row reads itself twice) so the compiler issues
-// them back to back; only the stores are predicated.
+// vectors per lane of each: 32 outstanding 16-byte loads per lane (224 KiB per workgroup
+// for 14 KiB rows).  The loads are unconditional (columns past the row end are clamped to
+// its last vector; a lone last row reads itself twice) so the compiler issues them back to
+// back; only the stores are predicated.  SC1_SRC: sources written by other CUs during the
+// kernel (ring rows) are read with device-coherent loads.
+template <bool SC1_SRC>
 __device__ void wg_copy_rows(const uint64_t* src, const uint64_t* dst, int nrows, int n16) {
   constexpr int U = 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -154,17 +179,16 @@ __device__ void wg_copy_rows(const uint64_t* src, const uint64_t* dst, int nrows
   for (int r = wave; r < nrows; r += 2 * kWaves) {
     const int r2 = r + kWaves;
     const bool two = r2 < nrows;
-    const gsrc_t s0 = reinterpret_cast<gsrc_t>(src[r]);
+    const uint64_t s0 = src[r], s1 = src[two ? r2 : r];
     const gdst_t t0 = reinterpret_cast<gdst_t>(dst[r]);
-    const gsrc_t s1 = reinterpret_cast<gsrc_t>(src[two ? r2 : r]);
     const gdst_t t1 = reinterpret_cast<gdst_t>(dst[two ? r2 : r]);
     for (int c0 = 0; c0 < n16; c0 += 64 * U) {
       u32x4 a[U], b[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = min(c0 + u * 64 + lane, n16 - 1);
-        a[u] = s0[c];
-        b[u] = s1[c];
+        a[u] = row_load<SC1_SRC>(s0, c, n16);
+        b[u] = row_load<SC1_SRC>(s1, c, n16);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -214,10 +238,121 @@ __global__ void persist_check_kernel(PersistArgs A) {
   if (p < A.n_part) {
     const int32_t* pw = A.pc + A.cl.pipe0 + p * sched::kPipeWords;
     const int n_m = pw[sched::kHi] - pw[sched::kLo];
-    bad = pw[sched::kGatherNext] < n_m * A.cpm || pw[sched::kPushNext] < n_m ||
+    bad = pw[sched::kGatherNext] < n_m * A.cpm || pw[sched::kPushNext] < n_m * A.cpm ||
           pw[sched::kTicketNext] < pw[sched::kNTickets];
   }
   if (__any(bad) && threadIdx.x == 0 && *A.status == MOE_OK) *A.status = MOE_EINCOMPLETE;
+}
+
+// One workgroup's view of its pipeline.
+struct PipeCtx {
+  int p, lo, n_m, S, cpm, chunk_rows, row_bytes, n16, NT2;
+  bool light;
+};
+
+__device__ __forceinline__ char* slot_ptr(const PersistArgs& A, const PipeCtx& c, int q) {   // pipeline-local chunk q
+  return A.ring + (long long)(c.p * c.S + sched::chunk_slot(q, c.S)) * A.slot_bytes;
+}
+
+__device__ __forceinline__ int tile_rows(const PersistArgs& A, int m, int* row0, int* l) {    // global row tile m
+  *l = find_expert(A.mtile_base, A.El, m);
+  *row0 = A.offsets[*l] + (m - A.mtile_base[*l]) * kGemmBM;
+  return min(kGemmBM, A.offsets[*l + 1] - *row0);
+}
+
+// Gather pipeline-local chunk q (rows of row tile lo + q / cpm) from the source buffers into
+// its slot, then signal it (whole workgroup; the row tables live in LDS).
+__device__ void do_gather(const PersistArgs& A, const PipeCtx& c, int q, char* smem) {
+  uint64_t* src_tab = reinterpret_cast<uint64_t*>(smem);
+  uint64_t* dst_tab = src_tab + kGemmBM;
+  int row0, l;
+  const int m = c.lo + q / c.cpm, h = q % c.cpm;
+  const int rows = tile_rows(A, m, &row0, &l);
+  const int c_lo = h * c.chunk_rows, c_n = min(c.chunk_rows, rows - c_lo);
+  char* dst = slot_ptr(A, c, q);
+  for (int r = threadIdx.x; r < c_n; r += kGemmThreads) {
+    const int s = row0 + c_lo + r;
+    const int rk = A.pull_src[2 * (long long)s];
+    const int t = A.pull_src[2 * (long long)s + 1];
+    src_tab[r] = reinterpret_cast<uint64_t>(A.x.p[rk] + (long long)t * c.row_bytes);
+    dst_tab[r] = reinterpret_cast<uint64_t>(dst + (long long)r * c.row_bytes);
+  }
+  __syncthreads();
+  if (c_n > 0) wg_copy_rows<false>(src_tab, dst_tab, c_n, c.n16);   // the sources never change
+  release_add(A.pc + A.cl.filled + m * 4 + h, 1, c.light);
+  __syncthreads();                                              // the row tables are reused
+}
+
+// Push pipeline-local chunk q: its output rows (in place in the ring) to recv[rank][token][j];
+// then free its slot (whole workgroup).
+__device__ void do_push(const PersistArgs& A, const PipeCtx& c, int q, char* smem) {
+  uint64_t* src_tab = reinterpret_cast<uint64_t*>(smem);
+  uint64_t* dst_tab = src_tab + kGemmBM;
+  int row0, l;
+  const int m = c.lo + q / c.cpm, h = q % c.cpm;
+  const int rows = tile_rows(A, m, &row0, &l);
+  const int c_lo = h * c.chunk_rows, c_n = min(c.chunk_rows, rows - c_lo);
+  const char* src = slot_ptr(A, c, q);
+  for (int r = threadIdx.x; r < c_n; r += kGemmThreads) {
+    const int s = row0 + c_lo + r;
+    const int rk = A.pull_src[2 * (long long)s];
+    const int t = A.pull_src[2 * (long long)s + 1];
+    const int32_t* so = A.slot_of + ((long long)rk * A.T + t) * A.k;
+    int j = 0;
+    for (int jj = 0; jj < A.k; ++jj)
+      if (so[jj] == s) j = jj;
+    src_tab[r] = reinterpret_cast<uint64_t>(src + (long long)r * c.row_bytes);
+    dst_tab[r] = reinterpret_cast<uint64_t>(A.recv.p[rk] + ((long long)t * A.k + j) * c.row_bytes);
+  }
+  __syncthreads();
+  if (c_n > 0) wg_copy_rows<true>(src_tab, dst_tab, c_n, c.n16);    // output rows other CUs wrote
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");             // the slot's reads are done
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(A.pc + sched::slot_epoch_word(A.cl, c.p, c.S, q), 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A compute workgroup waits until every chunk of row tile m is in its slot; meanwhile it
+// gathers claimable chunks of its pipeline itself (a gather never waits, so this cannot
+// deadlock).  Returns false on abort or watchdog expiry.
+__device__ bool wait_chunks(const PersistArgs& A, const PipeCtx& c, int m, char* smem, int* sh) {
+  const DevOps ops{A.pc};
+  long long t0 = wall_clock64();
+  while (true) {
+    if (threadIdx.x == 0) {
+      int st = 0, arg = 0;            // 0 wait, 1 ready, 2 abort, 3 gather chunk arg
+      bool ready = true;
+      for (int h = 0; h < c.cpm; ++h)
+        if (ld_relaxed(A.pc + A.cl.filled + m * 4 + h) < 1) ready = false;
+      if (ready) {
+        st = 1;
+      } else if (ld_relaxed(A.pc + A.cl.abort_word)) {
+        st = 2;
+      } else if (sched::mover_claim(ops, A.cl, c.p, c.lo, c.n_m, c.cpm, c.S, c.NT2, &arg, true) == sched::kGather) {
+        st = 3;
+      } else {
+        __builtin_amdgcn_s_sleep(1);
+        if (wall_clock64() - t0 > A.budget) {
+          set_abort(A, MOE_ETIMEOUT);
+          st = 2;
+        }
+      }
+      sh[1] = st;
+      sh[2] = arg;
+    }
+    __syncthreads();
+    const int st = sh[1], arg = sh[2];
+    __syncthreads();
+    if (st == 1) return true;
+    if (st == 2) return false;
+    if (st == 3) {
+      const long long tb = wall_clock64();
+      do_gather(A, c, arg, smem);
+      trace_event(A, 1, arg, c.p, tb, wall_clock64(), tb - t0);
+      t0 = wall_clock64();
+    }
+  }
 }
 
 __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(PersistArgs A) {
@@ -228,11 +363,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
 
   unsigned xcc;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-  const int p = int(xcc & 7) * A.n_part / 8;
-  const bool light = A.light;
+  PipeCtx c;
+  c.p = int(xcc & 7) * A.n_part / 8;
+  const int p = c.p;
+  c.light = A.light;
   const int pbase = A.cl.pipe0 + p * sched::kPipeWords;
   int32_t* pw = A.pc + pbase;
-  int32_t* filled = A.pc + A.cl.filled;
   int32_t* g1_done = A.pc + A.cl.g1_done;
   int32_t* g2_done = A.pc + A.cl.g2_done;
 
@@ -244,24 +380,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
   trace_event(A, 0, mover ? 0 : 1, p, t_start, t_start, 0);
 
   // this pipeline's row tiles [lo, hi) and tables (written by the preparation kernel)
-  const int lo = pw[sched::kLo], hi = pw[sched::kHi];
-  const int n_m = hi - lo;
+  c.lo = pw[sched::kLo];
+  c.n_m = pw[sched::kHi] - c.lo;
+  const int lo = c.lo;
   const int n_groups = pw[sched::kNGroups], n_tickets = pw[sched::kNTickets];
-  const int S = A.S, cpm = A.cpm;
+  c.S = A.S;
+  c.cpm = A.cpm;
+  c.chunk_rows = 1 << A.blk_log2;
+  c.row_bytes = A.d * 2;
+  c.n16 = c.row_bytes >> 4;
+  c.NT2 = (A.d + kGemmBN - 1) / kGemmBN;
+  const int cpm = c.cpm;
+  const bool light = c.light;
   const int NT1 = (A.F + kGemmBN / 2 - 1) / (kGemmBN / 2);
-  const int chunk_rows = 1 << A.blk_log2;
-  const int row_bytes = A.d * 2;
-  const int n16 = row_bytes >> 4;
-  const long long xpart = (long long)chunk_rows * row_bytes;   // token / output rows of a slot
-
-  auto slot_ptr = [&](int q) -> char* {                        // pipeline-local chunk q
-    return A.ring + (long long)(p * S + sched::chunk_slot(q, S)) * A.slot_bytes;
-  };
-  auto tile_rows = [&](int m, int* row0, int* l) -> int {      // global row tile m
-    *l = find_expert(A.mtile_base, A.El, m);
-    *row0 = A.offsets[*l] + (m - A.mtile_base[*l]) * kGemmBM;
-    return min(kGemmBM, A.offsets[*l + 1] - *row0);
-  };
+  const long long xpart = (long long)c.chunk_rows * c.row_bytes;   // token / output rows of a slot
 
   // Compute workgroups take tickets until none is left, then join the data movement for the
   // tail (the last pushes); data-movement workgroups move data from the start.
@@ -280,14 +412,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
       const sched::Task tk = sched::task_of_ticket(ticket, n_groups, phase_start, grp_first, grp_len, A.lookahead != 0);
       const int m = tk.m;
       int row0, l;
-      const int rows = tile_rows(m, &row0, &l);
+      const int rows = tile_rows(A, m, &row0, &l);
       const long long t_w = wall_clock64();
-      bool ok = true;
-      if (!tk.down) {
-        for (int h = 0; h < cpm && ok; ++h) ok = wait_ge(filled + m * 4 + h, 1, A, sh);
-      } else {
-        ok = wait_ge(g1_done + m, NT1, A, sh);
-      }
+      const bool ok = !tk.down ? wait_chunks(A, c, m, smem, sh) : wait_ge(g1_done + m, NT1, A, sh);
       if (!ok) {
         aborted = true;
         break;
@@ -295,10 +422,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
       const long long t_b = wall_clock64();
       acquire_after_poll(light);
       const int q0 = (m - lo) * cpm;
-      char* s0 = slot_ptr(q0);
-      char* s1 = slot_ptr(q0 + min(1, cpm - 1));
-      char* s2 = slot_ptr(q0 + min(2, cpm - 1));
-      char* s3 = slot_ptr(q0 + min(3, cpm - 1));
+      char* s0 = slot_ptr(A, c, q0);
+      char* s1 = slot_ptr(A, c, q0 + min(1, cpm - 1));
+      char* s2 = slot_ptr(A, c, q0 + min(2, cpm - 1));
+      char* s3 = slot_ptr(A, c, q0 + min(3, cpm - 1));
       TileIO io;
       io.blk_log2 = A.blk_log2;
       io.rows = rows;
@@ -319,7 +446,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
         io.o_ld = A.F;
         const uint16_t* b0 = A.w1 + size_t(l) * A.F * A.d;
         const uint16_t* b1 = A.w3 + size_t(l) * A.F * A.d;
-        gemm_tile<0>(io, b0, b1, tk.j * (kGemmBN / 2), A.F, A.d, smem, A.d);
+        gemm_tile<0, 16>(io, b0, b1, tk.j * (kGemmBN / 2), A.F, A.d, smem, A.d);   // x rows: sc1 loads
         release_add(g1_done + m, 1, light);
         trace_event(A, 3, m * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
       } else {
@@ -334,7 +461,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
         io.a_ld = A.F;
         io.o_ld = A.d;
         const uint16_t* b0 = A.w2 + size_t(l) * A.d * A.F;
-        gemm_tile<1>(io, b0, b0, tk.j * kGemmBN, A.d, A.F, smem, A.F);
+        gemm_tile<1, 16>(io, b0, b0, tk.j * kGemmBN, A.d, A.F, smem, A.F);         // h rows: sc1 loads
         release_add(g2_done + m, 1, light);
         trace_event(A, 4, m * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
       }
@@ -342,8 +469,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
   }
   if (!aborted) {
     // ------------------------------------------------------------ data movement
-    uint64_t* src_tab = reinterpret_cast<uint64_t*>(smem);
-    uint64_t* dst_tab = src_tab + kGemmBM;
     const DevOps ops{A.pc};
     long long idle_since = wall_clock64();
     while (true) {
@@ -352,7 +477,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
         if (ld_relaxed(A.pc + A.cl.abort_word)) {
           act = sched::kDone;
         } else {
-          act = sched::mover_claim(ops, A.cl, p, lo, n_m, cpm, S, (A.d + kGemmBN - 1) / kGemmBN, &arg);
+          act = sched::mover_claim(ops, A.cl, p, lo, c.n_m, cpm, c.S, c.NT2, &arg);
           if (act == sched::kIdle) {
             __builtin_amdgcn_s_sleep(1);
             if (wall_clock64() - idle_since > A.budget) {
@@ -372,51 +497,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
       const long long t_b = wall_clock64();
       acquire_after_poll(light);
       if (act == sched::kPush) {
-        // row tile lo + arg: its output rows (in place in the ring) -> recv[rank][token][j]
-        int row0, l;
-        const int m = lo + arg;
-        const int rows = tile_rows(m, &row0, &l);
-        for (int r = tid; r < rows; r += kGemmThreads) {
-          const int s = row0 + r;
-          const int rk = A.pull_src[2 * (long long)s];
-          const int t = A.pull_src[2 * (long long)s + 1];
-          const int32_t* so = A.slot_of + ((long long)rk * A.T + t) * A.k;
-          int j = 0;
-          for (int jj = 0; jj < A.k; ++jj)
-            if (so[jj] == s) j = jj;
-          src_tab[r] = reinterpret_cast<uint64_t>(slot_ptr(arg * cpm + (r >> A.blk_log2)) +
-                                                  (long long)(r & (chunk_rows - 1)) * row_bytes);
-          dst_tab[r] = reinterpret_cast<uint64_t>(A.recv.p[rk] + ((long long)t * A.k + j) * row_bytes);
-        }
-        __syncthreads();
-        wg_copy_rows(src_tab, dst_tab, rows, n16);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // the slot's reads are done
-        __syncthreads();
-        if (tid == 0)
-          for (int h = 0; h < cpm; ++h)
-            __hip_atomic_fetch_add(A.pc + sched::slot_epoch_word(A.cl, p, S, arg * cpm + h), 1, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        trace_event(A, 2, m, p, t_b, wall_clock64(), t_b - idle_since);
+        do_push(A, c, arg, smem);
+        trace_event(A, 2, arg, p, t_b, wall_clock64(), t_b - idle_since);
       } else {
-        // chunk arg: rows [h * chunk_rows, ...) of row tile lo + arg / cpm, from the sources
-        int row0, l;
-        const int m = lo + arg / cpm, h = arg % cpm;
-        const int rows = tile_rows(m, &row0, &l);
-        const int c_lo = h * chunk_rows, c_n = min(chunk_rows, rows - c_lo);
-        char* dst = slot_ptr(arg);
-        for (int r = tid; r < c_n; r += kGemmThreads) {
-          const int s = row0 + c_lo + r;
-          const int rk = A.pull_src[2 * (long long)s];
-          const int t = A.pull_src[2 * (long long)s + 1];
-          src_tab[r] = reinterpret_cast<uint64_t>(A.x.p[rk] + (long long)t * row_bytes);
-          dst_tab[r] = reinterpret_cast<uint64_t>(dst + (long long)r * row_bytes);
-        }
-        __syncthreads();
-        if (c_n > 0) wg_copy_rows(src_tab, dst_tab, c_n, n16);
-        release_add(filled + m * 4 + h, 1, light);
+        do_gather(A, c, arg, smem);
         trace_event(A, 1, arg, p, t_b, wall_clock64(), t_b - idle_since);
       }
-      __syncthreads();                                          // the row tables are reused
       idle_since = wall_clock64();
     }
   }

@@ -10,8 +10,10 @@
 // depends on where the two workgroups run (one XCD shares an L2; different XCDs do not) and
 // on the visibility protocol:
 //   scope 0 (L2-local): producer stores, waits for them (vmcnt 0), relaxed flag store; the
-//     consumer polls the flag and invalidates its CU's L1 (buffer_inv sc0) before reading.
-//     Sufficient when both sides share one L2; across XCDs the payload may be stale.
+//     consumer polls the flag and invalidates its CU's L1 (buffer_inv sc1; the workgroup-scope
+//     buffer_inv sc0 leaves L1 lines of earlier rounds in place, which a payload smaller than
+//     the L1 exposes) before reading.  Sufficient when both sides share one L2; across XCDs the
+//     payload may be stale.
 //   scope 1 (agent): release store of the flag / acquire load, which on gfx950 write back and
 //     invalidate the XCD's L2 (buffer_wbl2 sc1 / buffer_inv sc1).  Correct anywhere.
 // Every pair runs `rounds` hand-offs; the consumer counts payload words that do not hold the
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(kProbeThreads) void signal_probe_kernel(ProbeArgs A
     if (producer) {
       for (int i = tid; i < A.payload; i += kProbeThreads) buf[i] = r * 1000003 + i;
     } else {
-      if (SCOPE == 0) asm volatile("buffer_inv sc0" ::: "memory");
+      if (SCOPE == 0) asm volatile("buffer_inv sc1" ::: "memory");
       int e = 0;
       for (int i = tid; i < A.payload; i += kProbeThreads) e += buf[i] != r * 1000003 + i;
       if (e) atomicAdd(&bad, e);

@@ -72,7 +72,8 @@ struct Model {
   // shadow state
   std::vector<std::atomic<int>> slot_occ;     // [n_part * S]: chunk (pipeline-local) in the slot, -1 none
   std::vector<std::atomic<int>> gathered;     // [n_mt * 4]
-  std::vector<std::atomic<int>> u_done, d_done, pushed, u_runs, d_runs, push_runs;   // per row tile
+  std::vector<std::atomic<int>> u_done, d_done, u_runs, d_runs;   // per row tile
+  std::vector<std::atomic<int>> pushed_chunk, push_runs;           // per chunk: [n_mt * cpm]
   std::vector<std::atomic<int>> gather_runs;  // [n_mt * 4]
   Fail* fail;
   unsigned seed;
@@ -133,6 +134,62 @@ struct Model {
     return true;
   }
 
+  // what do_gather does, with the shadow checks
+  void gather(int p, int lo, int q, std::mt19937& rng) {
+    const int S = plan.S, cpm = c.cpm;
+    const int m = lo + q / cpm, h = q % cpm;
+    const int s = chunk_slot(q, S);
+    const int prev = slot_occ[p * S + s].load();
+    if (q >= S) {
+      if (prev != q - S) fail->add("gather: slot's previous chunk is not q - S");
+      if (!pushed_chunk[(lo * cpm) + q - S].load()) fail->add("gather into a slot whose chunk is not pushed yet");
+    } else if (prev != -1) {
+      fail->add("gather: first use of a slot that is occupied");
+    }
+    slot_occ[p * S + s].store(q);
+    if (gather_runs[m * 4 + h].fetch_add(1) != 0) fail->add("chunk gathered twice");
+    delay(rng, 30);
+    gathered[m * 4 + h].store(1);
+    pc[cl.filled + m * 4 + h].fetch_add(1, std::memory_order_release);
+  }
+
+  // what do_push does, with the shadow checks
+  void push(int p, int lo, int q, std::mt19937& rng) {
+    const int S = plan.S, cpm = c.cpm;
+    const int m = lo + q / cpm;
+    if (d_done[m].load() != c.NT2) fail->add("push before all down tiles finished, tile " + std::to_string(m));
+    if (slot_occ[p * S + chunk_slot(q, S)].load() != q) fail->add("push: slot no longer holds chunk " + std::to_string(q));
+    if (push_runs[lo * cpm + q].fetch_add(1) != 0) fail->add("chunk pushed twice");
+    delay(rng, 15);
+    pushed_chunk[lo * cpm + q].store(1);
+    pc[slot_epoch_word(cl, p, S, q)].fetch_add(1);
+  }
+
+  // what wait_chunks does: wait for the chunks of row tile m, gathering meanwhile
+  bool wait_chunks(int p, int lo, int n_m, int m, std::mt19937& rng) {
+    Ops ops{pc.data()};
+    auto t0 = std::chrono::steady_clock::now();
+    while (true) {
+      bool ready = true;
+      for (int h = 0; h < c.cpm; ++h)
+        if (pc[cl.filled + m * 4 + h].load(std::memory_order_acquire) < 1) ready = false;
+      if (ready) return true;
+      if (abort_flag.load()) return false;
+      int arg = 0;
+      if (mover_claim(ops, cl, p, lo, n_m, c.cpm, plan.S, c.NT2, &arg, true) == kGather) {
+        gather(p, lo, arg, rng);
+        t0 = std::chrono::steady_clock::now();
+        continue;
+      }
+      std::this_thread::yield();
+      if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(10)) {
+        fail->add("watchdog: a chunk wait did not end within 10 s (deadlock)");
+        abort_flag.store(1);
+        return false;
+      }
+    }
+  }
+
   void workgroup(int p, unsigned wseed) {
     std::mt19937 rng(wseed);
     const int pb = cl.pipe0 + p * kPipeWords;
@@ -155,12 +212,7 @@ struct Model {
         const Task tk = task_of_ticket(t, n_groups, ps.data(), gf.data(), gl.data(), plan.lookahead != 0);
         const int m = tk.m;
         if (m < lo || m >= hi) fail->add("ticket maps outside the pipeline's row tiles");
-        bool ok = true;
-        if (!tk.down) {
-          for (int h = 0; h < cpm && ok; ++h) ok = wait_ge(cl.filled + m * 4 + h, 1);
-        } else {
-          ok = wait_ge(cl.g1_done + m, c.NT1);
-        }
+        const bool ok = !tk.down ? wait_chunks(p, lo, n_m, m, rng) : wait_ge(cl.g1_done + m, c.NT1);
         if (!ok) return;                 // aborted: exit
         for (int h = 0; h < cpm; ++h) {
           const int q = (m - lo) * cpm + h;
@@ -181,51 +233,25 @@ struct Model {
         }
       }
     }
-      auto idle_since = std::chrono::steady_clock::now();
-      while (true) {
-        if (abort_flag.load()) break;
-        int arg = 0;
-        const int act = mover_claim(ops, cl, p, lo, n_m, cpm, S, c.NT2, &arg);
-        if (act == kDone) break;
-        if (act == kIdle) {
-          std::this_thread::yield();
-          if (std::chrono::steady_clock::now() - idle_since > std::chrono::seconds(10)) {
-            fail->add("watchdog: a mover idled 10 s (deadlock)");
-            abort_flag.store(1);
-            break;
-          }
-          continue;
+    auto idle_since = std::chrono::steady_clock::now();
+    while (true) {
+      if (abort_flag.load()) break;
+      int arg = 0;
+      const int act = mover_claim(ops, cl, p, lo, n_m, cpm, S, c.NT2, &arg);
+      if (act == kDone) break;
+      if (act == kIdle) {
+        std::this_thread::yield();
+        if (std::chrono::steady_clock::now() - idle_since > std::chrono::seconds(10)) {
+          fail->add("watchdog: a mover idled 10 s (deadlock)");
+          abort_flag.store(1);
+          break;
         }
-        if (act == kPush) {
-          const int m = lo + arg;
-          if (d_done[m].load() != c.NT2) fail->add("push before all down tiles finished, tile " + std::to_string(m));
-          for (int h = 0; h < cpm; ++h) {
-            const int q = arg * cpm + h;
-            if (slot_occ[p * S + chunk_slot(q, S)].load() != q)
-              fail->add("push: slot no longer holds chunk " + std::to_string(q));
-          }
-          if (push_runs[m].fetch_add(1) != 0) fail->add("row tile pushed twice");
-          delay(rng, 30);
-          pushed[m].store(1);
-          for (int h = 0; h < cpm; ++h) pc[slot_epoch_word(cl, p, S, arg * cpm + h)].fetch_add(1);
-        } else {
-          const int q = arg, m = lo + q / cpm, h = q % cpm;
-          const int s = chunk_slot(q, S);
-          const int prev = slot_occ[p * S + s].load();
-          if (q >= S) {
-            if (prev != q - S) fail->add("gather: slot's previous chunk is not q - S");
-            if (!pushed[lo + (q - S) / cpm].load()) fail->add("gather into a slot whose chunk is not pushed yet");
-          } else if (prev != -1) {
-            fail->add("gather: first use of a slot that is occupied");
-          }
-          slot_occ[p * S + s].store(q);
-          if (gather_runs[m * 4 + h].fetch_add(1) != 0) fail->add("chunk gathered twice");
-          delay(rng, 30);
-          gathered[m * 4 + h].store(1);
-          pc[cl.filled + m * 4 + h].fetch_add(1, std::memory_order_release);
-        }
-        idle_since = std::chrono::steady_clock::now();
+        continue;
       }
+      if (act == kPush) push(p, lo, arg, rng);
+      else gather(p, lo, arg, rng);
+      idle_since = std::chrono::steady_clock::now();
+    }
   }
 
   // the rule of persist_check_kernel
@@ -233,7 +259,7 @@ struct Model {
     for (int p = 0; p < plan.n_part; ++p) {
       const int b = cl.pipe0 + p * kPipeWords;
       const int n_m = pc[b + kHi].load() - pc[b + kLo].load();
-      if (pc[b + kGatherNext].load() < n_m * c.cpm || pc[b + kPushNext].load() < n_m ||
+      if (pc[b + kGatherNext].load() < n_m * c.cpm || pc[b + kPushNext].load() < n_m * c.cpm ||
           pc[b + kTicketNext].load() < pc[b + kNTickets].load())
         return true;
     }
@@ -290,8 +316,8 @@ int run_case(const Case& cs, unsigned seed, Fail& fail) {
   M.gather_runs = std::vector<std::atomic<int>>(nt * 4);
   M.u_done = std::vector<std::atomic<int>>(nt);
   M.d_done = std::vector<std::atomic<int>>(nt);
-  M.pushed = std::vector<std::atomic<int>>(nt);
-  M.push_runs = std::vector<std::atomic<int>>(nt);
+  M.pushed_chunk = std::vector<std::atomic<int>>(nt * 4);
+  M.push_runs = std::vector<std::atomic<int>>(nt * 4);
   M.u_runs = std::vector<std::atomic<int>>(nt * 64);
   M.d_runs = std::vector<std::atomic<int>>(nt * 64);
   M.prep();
@@ -328,9 +354,10 @@ int run_case(const Case& cs, unsigned seed, Fail& fail) {
         if (m >= a && m < b) p = q;
       }
       (void)p;
-      if (M.push_runs[m].load() != 1) fail.add("row tile not pushed exactly once");
-      for (int h = 0; h < cs.cpm; ++h)
+      for (int h = 0; h < cs.cpm; ++h) {
         if (M.gather_runs[m * 4 + h].load() != 1) fail.add("chunk not gathered exactly once");
+        if (M.push_runs[m * cs.cpm + h].load() != 1) fail.add("chunk not pushed exactly once");
+      }
       for (int j = 0; j < cs.NT1; ++j)
         if (M.u_runs[m * 64 + j].load() != 1) fail.add("gate/up tile not run exactly once");
       for (int j = 0; j < cs.NT2; ++j)

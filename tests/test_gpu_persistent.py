@@ -156,7 +156,7 @@ def test_persistent_trace():
     n_mt = int(np.sum((counts + 255) // 256))
     NT1, NT2 = SLICE.F // 128, SLICE.d // 256
     assert kinds[1] == n_mt * 2                      # 128-row chunks: two per row tile
-    assert kinds[2] == n_mt
+    assert kinds[2] == n_mt * 2                      # pushes per chunk as well
     assert kinds[3] == n_mt * NT1
     assert kinds[4] == n_mt * NT2
     assert kinds[0] == kinds[5] and kinds[0] > 0

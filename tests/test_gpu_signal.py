@@ -17,11 +17,15 @@ def _say(msg):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("cross,scope", [(0, 0), (0, 1), (1, 1), (1, 0)],
-                         ids=["same-xcd-l2", "same-xcd-agent", "cross-xcd-agent", "cross-xcd-l2"])
-def test_signal_probe(cross, scope):
+@pytest.mark.parametrize("cross,scope,words", [(0, 0, 16384), (0, 0, 1024), (0, 1, 16384), (0, 1, 1024),
+                                               (1, 1, 16384), (1, 0, 16384)],
+                         ids=["same-xcd-l2", "same-xcd-l2-4KiB", "same-xcd-agent", "same-xcd-agent-4KiB",
+                              "cross-xcd-agent", "cross-xcd-l2"])
+def test_signal_probe(cross, scope, words):
+    """A 4 KiB payload stays in the consumer CU's L1 from one round to the next, so it
+    catches an acquire that does not invalidate the L1 (a 64 KiB payload evicts itself)."""
     import torch
-    words, rounds = 16384, 200
+    rounds = 200
     _say(f"[signal] cross_xcd={cross} scope={scope} payload={words * 4} B rounds={rounds}")
     scratch = torch.empty(moe.moe_signal_probe_bytes(words), dtype=torch.uint8, device="cuda:0")
     rc, us, stale, tmo, same = moe.moe_signal_probe(cross, scope, words, rounds, scratch, check=False)
