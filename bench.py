@@ -463,24 +463,29 @@ def run_backward(args, cfg, inp, P, stream, N):
 
 
 def run_signal_latency(args):
-    """Round trip of a flag (and of a 64 KiB payload) between two workgroups, the one-GPU
-    analogue of the pages' push/pull signalling latency.  128 pairs run concurrently; a
-    round is one flag plus one acknowledgement per pair."""
+    """Round trip of a flag (and of a 64 KiB or 4 KiB payload) between two workgroups, the
+    one-GPU analogue of the pages' push/pull signalling latency.  128 pairs run concurrently;
+    a round is one flag plus one acknowledgement per pair.  Consumer forms: 0 L2-local
+    (buffer_inv sc1), 1 agent-scope release/acquire, 2 workgroup-scope invalidate
+    (buffer_inv sc0, shown stale), 3 no invalidate with sc1 loads (the persistent kernel's)."""
     import torch
     from mixture_experts_layer_histogram_amd import moe
     rounds = max(100, args.steps * 25)
+    names = {0: "L2-local (buffer_inv sc1)", 1: "agent-scope release/acquire",
+             2: "L2-local with buffer_inv sc0 (insufficient)", 3: "L2-local, sc1 loads, no invalidate"}
     res = []
-    for words in (0, 16384):
+    for words in (0, 1024, 16384):
         scratch = torch.empty(moe.moe_signal_probe_bytes(words), dtype=torch.uint8, device="cuda:0")
         for cross in (0, 1):
-            for scope in (0, 1):
+            for scope in (0, 1, 2, 3):
+                if words == 0 and scope > 1:
+                    continue
                 moe.moe_signal_probe(cross, scope, words, 20, scratch, check=False)     # warm-up
                 rc, us, stale, tmo, same = moe.moe_signal_probe(cross, scope, words, rounds, scratch, check=False)
                 res.append({"payload_bytes": words * 4, "partners": "different XCDs" if cross else "same XCD",
-                            "handoff": "agent-scope release/acquire" if scope else "L2-local (L1 invalidate)",
-                            "us_per_round_trip": us, "stale_words": stale, "timeouts": tmo, "rc": rc,
-                            "pairs_on_one_xcd": same})
-                log(f"[signal] payload {words * 4} B, {'cross' if cross else 'same'}-XCD, scope {scope}: "
+                            "handoff": names[scope], "us_per_round_trip": us, "stale_words": stale, "timeouts": tmo,
+                            "rc": rc, "pairs_on_one_xcd": same})
+                log(f"[signal] payload {words * 4} B, {'cross' if cross else 'same'}-XCD, {names[scope]}: "
                     f"{us:.2f} us/round, stale {stale}, timeouts {tmo}")
     print(json.dumps({"metric": "inter-partition signal round trip (one GPU)", "unit": "us", "n_gpus": 1,
                       "rounds": rounds, "pairs": 128, "higher_is_better": False, "results": res}), flush=True)

@@ -545,8 +545,11 @@ int moe_backward_mx(const moe_shape_t* s, const moe_placement_t* p, const void* 
  *   cross_xcd: 0 = partners on the same XCD (workgroups w and w ^ 8; workgroup w runs on
  *     XCD w mod 8), 1 = on different XCDs (w and w ^ 1).
  *   scope: 0 = L2-local hand-off (stores waited for, relaxed flag, the consumer invalidates
- *     its L1 only; not sufficient across XCDs), 1 = agent-scope release/acquire (writes back /
- *     invalidates the XCD's L2; correct anywhere).
+ *     its L1 with buffer_inv sc1; not sufficient across XCDs), 1 = agent-scope release/acquire
+ *     (writes back / invalidates the XCD's L2; correct anywhere), 2 = as 0 with a
+ *     workgroup-scope invalidate (buffer_inv sc0), which leaves the consumer's L1 lines in
+ *     place (shown stale with a payload that fits the L1), 3 = as 0 with no invalidate and the
+ *     payload read by device-coherent sc1 loads (the persistent kernel's same-XCD form).
  *   scratch, scratch_bytes: caller-owned device memory, 256-byte aligned, at least
  *     moe_signal_probe_bytes(payload_words); cleared by the call.
  * Outputs (host): us_per_round = wall time of the launch / rounds (one round = one flag and
@@ -554,7 +557,7 @@ int moe_backward_mx(const moe_shape_t* s, const moe_placement_t* p, const void* 
  * consumer read before they held the round's value (summed); timeouts = waits that hit the
  * 2 s budget; pairs_same_xcd = pairs whose two workgroups reported the same XCC id.
  * Synchronous: returns after the kernel and the copies of the counters finish.  Errors:
- * MOE_EINVAL (bad selector, payload_words outside [0, 2^20], rounds outside [1, 100000],
+ * MOE_EINVAL (cross_xcd not 0/1, scope outside 0..3, payload_words outside [0, 2^20], rounds outside [1, 100000],
  * null pointer), MOE_EALIGN, MOE_ENOSPC, MOE_EHIP; MOE_ETIMEOUT if any wait expired.
  */
 size_t moe_signal_probe_bytes(int32_t payload_words);

@@ -16,6 +16,11 @@
 //     payload may be stale.
 //   scope 1 (agent): release store of the flag / acquire load, which on gfx950 write back and
 //     invalidate the XCD's L2 (buffer_wbl2 sc1 / buffer_inv sc1).  Correct anywhere.
+//   scope 2: as scope 0 with a workgroup-scope invalidate (buffer_inv sc0) instead -- kept to
+//     show that it is not enough: it leaves the consumer CU's L1 lines in place, so a payload
+//     that fits the L1 reads stale from the second round on.
+//   scope 3: as scope 0 without any invalidate, the payload read with device-coherent sc1
+//     loads (no L1 hit) -- the form the persistent kernel's same-XCD hand-offs use.
 // Every pair runs `rounds` hand-offs; the consumer counts payload words that do not hold the
 // round's values.  Every wait is bounded by a wall-clock budget.
 #include "common.hpp"
@@ -75,15 +80,22 @@ __global__ __launch_bounds__(kProbeThreads) void signal_probe_kernel(ProbeArgs A
       for (int i = tid; i < A.payload; i += kProbeThreads) buf[i] = r * 1000003 + i;
     } else {
       if (SCOPE == 0) asm volatile("buffer_inv sc1" ::: "memory");
+      if (SCOPE == 2) asm volatile("buffer_inv sc0" ::: "memory");
       int e = 0;
-      for (int i = tid; i < A.payload; i += kProbeThreads) e += buf[i] != r * 1000003 + i;
+      if (SCOPE == 3) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(buf, (short)0, A.payload * 4, 0x00020000);
+        for (int i = tid; i < A.payload; i += kProbeThreads)
+          e += __builtin_amdgcn_raw_buffer_load_b32(rs, i * 4, 0, 16) != uint32_t(r * 1000003 + i);
+      } else {
+        for (int i = tid; i < A.payload; i += kProbeThreads) e += buf[i] != r * 1000003 + i;
+      }
       if (e) atomicAdd(&bad, e);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
       int* sig = producer ? &A.flag[cpair] : &A.ack[cpair];
-      if (SCOPE == 0) __hip_atomic_store(sig, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (SCOPE != 1) __hip_atomic_store(sig, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else __hip_atomic_store(sig, r, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -119,7 +131,7 @@ extern "C" size_t moe_signal_probe_bytes(int32_t payload_words) {
 extern "C" int moe_signal_probe(int32_t cross_xcd, int32_t scope, int32_t payload_words, int32_t rounds,
                                 void* scratch, size_t scratch_bytes, float* us_per_round, int32_t* stale_words,
                                 int32_t* timeouts, int32_t* pairs_same_xcd, void* stream) {
-  if ((cross_xcd != 0 && cross_xcd != 1) || (scope != 0 && scope != 1)) return MOE_EINVAL;
+  if ((cross_xcd != 0 && cross_xcd != 1) || scope < 0 || scope > 3) return MOE_EINVAL;
   if (payload_words < 0 || payload_words > (1 << 20) || rounds < 1 || rounds > 100000) return MOE_EINVAL;
   if (!scratch || !us_per_round || !stale_words || !timeouts || !pairs_same_xcd) return MOE_EINVAL;
   if (reinterpret_cast<uintptr_t>(scratch) & 255) return MOE_EALIGN;
@@ -153,8 +165,12 @@ extern "C" int moe_signal_probe(int32_t cross_xcd, int32_t scope, int32_t payloa
   if (e == hipSuccess) {
     if (scope == 0)
       hipLaunchKernelGGL(signal_probe_kernel<0>, dim3(kProbeWGs), dim3(kProbeThreads), 0, st, A);
-    else
+    else if (scope == 1)
       hipLaunchKernelGGL(signal_probe_kernel<1>, dim3(kProbeWGs), dim3(kProbeThreads), 0, st, A);
+    else if (scope == 2)
+      hipLaunchKernelGGL(signal_probe_kernel<2>, dim3(kProbeWGs), dim3(kProbeThreads), 0, st, A);
+    else
+      hipLaunchKernelGGL(signal_probe_kernel<3>, dim3(kProbeWGs), dim3(kProbeThreads), 0, st, A);
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = hipEventRecord(e1, st);

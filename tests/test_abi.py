@@ -362,6 +362,7 @@ def test_signal_probe_sizes_and_rejects_bad_arguments_before_launch():
         return L.moe_signal_probe(cross, scope, words, rounds, scratch, nbytes, *out, None)
     assert call(cross=2) == -1
     assert call(scope=-1) == -1
+    assert call(scope=4) == -1
     assert call(words=-5) == -1
     assert call(rounds=0) == -1
     assert call(rounds=100001) == -1

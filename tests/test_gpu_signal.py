@@ -38,6 +38,24 @@ def test_signal_probe(cross, scope, words):
         assert stale == 0
 
 
+def test_signal_probe_consumer_l1():
+    """Same-XCD hand-off of a 4 KiB payload, which stays in the consumer CU's L1 between
+    rounds: a workgroup-scope invalidate (buffer_inv sc0) leaves it there and the consumer
+    reads stale words; device-coherent sc1 loads without any invalidate read none (the
+    persistent kernel's form)."""
+    import torch
+    words, rounds = 1024, 200
+    scratch = torch.empty(moe.moe_signal_probe_bytes(words), dtype=torch.uint8, device="cuda:0")
+    res = {}
+    for scope in (2, 3):
+        rc, us, stale, tmo, same = moe.moe_signal_probe(0, scope, words, rounds, scratch, check=False)
+        _say(f"[signal] 4 KiB same XCD, consumer form {scope}: {us:.2f} us/round, stale words {stale}")
+        assert rc == 0 and tmo == 0 and same == 128
+        res[scope] = stale
+    assert res[2] > 0
+    assert res[3] == 0
+
+
 def test_signal_probe_without_payload():
     import torch
     scratch = torch.empty(moe.moe_signal_probe_bytes(0), dtype=torch.uint8, device="cuda:0")
