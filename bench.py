@@ -236,34 +236,52 @@ def _oracle_mx_weights(cfg, inp):
     return out
 
 
-def cpu_baseline(cfg, inp, ranks):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, inp, ranks, threads=None):
     """The oracle as it stands, on a bounded sample: the first `ranks` source ranks of
-    the same inputs through the share (all of them by default, i.e. the whole step)."""
+    the same inputs through the share (all of them by default, i.e. the whole step).
+    threads: cap of the BLAS thread pool (None = the library's default, all cores)."""
     from oracle import moe_oracle as O
     from oracle import mx_oracle as MX
+    from contextlib import nullcontext
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        threadpool_info = threadpool_limits = None
     ranks = max(1, min(ranks, cfg.R))
-    if cfg.dtype == "mxfp8":
-        wq = _oracle_mx_weights(cfg, inp)
-        t0 = time.perf_counter()
-        MX.forward_q(inp.logits[:ranks], inp.x_f32[:ranks], *wq, inp.expert_to_local, cfg.E_local, cfg.k,
-                     cfg.minibatch)
-        what = ("fp64 NumPy quantised oracle (route, layout, pull with MX quantisation of x, SwiGLU experts "
-                "with h quantised, push, merge; weights quantised beforehand, untimed)")
-    else:
-        t0 = time.perf_counter()
-        O.forward(inp.logits[:ranks], inp.x_f32[:ranks], inp.w1_f32, inp.w3_f32, inp.w2_f32,
-                  inp.expert_to_local, cfg.E_local, cfg.k, cfg.minibatch)
-        what = "fp64 NumPy oracle (route, layout, pull, SwiGLU experts, push, merge)"
-    dt = time.perf_counter() - t0
+    limit = threadpool_limits(limits=threads) if (threads and threadpool_limits) else nullcontext()
+    with limit:
+        if threadpool_info:
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        else:  # pragma: no cover
+            cores = threads or os.cpu_count() or 1
+        if cfg.dtype == "mxfp8":
+            wq = _oracle_mx_weights(cfg, inp)
+            t0 = time.perf_counter()
+            MX.forward_q(inp.logits[:ranks], inp.x_f32[:ranks], *wq, inp.expert_to_local, cfg.E_local, cfg.k,
+                         cfg.minibatch)
+            what = ("fp64 NumPy quantised oracle (route, layout, pull with MX quantisation of x, SwiGLU experts "
+                    "with h quantised, push, merge; weights quantised beforehand, untimed)")
+        else:
+            t0 = time.perf_counter()
+            O.forward(inp.logits[:ranks], inp.x_f32[:ranks], inp.w1_f32, inp.w3_f32, inp.w2_f32,
+                      inp.expert_to_local, cfg.E_local, cfg.k, cfg.minibatch)
+            what = "fp64 NumPy oracle (route, layout, pull, SwiGLU experts, push, merge)"
+        dt = time.perf_counter() - t0
     tokens = ranks * cfg.T / cfg.G
     frac = "the whole step" if ranks == cfg.R else f"{ranks}/{cfg.R} of the step"
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"source ranks 0..{ranks - 1} of the same inputs ({frac}); {what}; {dt:.2f} s wall"}
+            "sample": f"source ranks 0..{ranks - 1} of the same inputs ({frac}); {what}; {dt:.2f} s wall",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count()}
 
 
 def cpu_baseline_bwd(cfg, inp, dy, ranks):
@@ -903,8 +921,9 @@ def main():
     if sampler:
         result["clocks"] = sampler.summary(peak)
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
+        log("[bench] timing the CPU oracle on a bounded sample (all cores, then one thread on one rank)")
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_ranks or cfg.R)
+        result["cpu_baseline_single_thread"] = cpu_baseline(cfg, inp, 1, threads=1)
     print(json.dumps(result), flush=True)
 
 
