@@ -87,7 +87,9 @@ MOE_HD void pipe_range(int n_mt, int n_part, int p, int* lo, int* hi) {
   *hi = int((long long)n_mt * (p + 1) / n_part);
 }
 
-// Group the row tiles [lo, hi) into runs of one expert, at most G row tiles each.
+// Group the row tiles [lo, hi) into runs of one expert, at most G row tiles each; an
+// expert's run is split into the fewest such groups, of near-equal size (5 row tiles with
+// G = 4 become 3 + 2, not 4 + 1: a group of one row tile reads its weight panels alone).
 // expert_of(m) gives the local expert of row tile m.  Returns the number of groups.
 template <class ExpertOf>
 MOE_HD int build_groups(int lo, int hi, int G, ExpertOf expert_of, int* grp_first, int* grp_len) {
@@ -95,12 +97,16 @@ MOE_HD int build_groups(int lo, int hi, int G, ExpertOf expert_of, int* grp_firs
   int m = lo;
   while (m < hi) {
     const int e = expert_of(m);
-    int len = 1;
-    while (m + len < hi && len < G && expert_of(m + len) == e) ++len;
-    grp_first[n] = m;
-    grp_len[n] = len;
-    ++n;
-    m += len;
+    int run = 1;                                   // this expert's row tiles from m on
+    while (m + run < hi && expert_of(m + run) == e) ++run;
+    const int ng = (run + G - 1) / G;              // fewest groups of at most G row tiles,
+    for (int i = 0; i < ng; ++i) {                 // sizes differing by at most one
+      const int len = run / ng + (i < run % ng ? 1 : 0);
+      grp_first[n] = m;
+      grp_len[n] = len;
+      ++n;
+      m += len;
+    }
   }
   return n;
 }
