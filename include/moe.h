@@ -100,13 +100,20 @@ typedef struct {
 typedef struct {
   int32_t minibatch_rows;   /* rows of one expert released to compute at once (default 128;
                                the persistent path takes 64, 128 or 256) */
-  int32_t comm_cus;         /* persistent path: workgroups doing data movement (default 32) */
+  int32_t comm_cus;         /* persistent path: workgroups doing data movement (default 16) */
   int32_t ring_slots;       /* persistent path: cap on ring slots (default: as many as ring_bytes holds) */
   int32_t trace;            /* persistent path: 1 = record a per-workgroup event trace into the
                                workspace (moe_persistent_trace_info); every other entry point
                                requires 0 (else MOE_EINVAL) */
   uint64_t watchdog_us;     /* persistent path: wall-clock budget of every device wait in
                                microseconds (default 2,000,000) */
+  int32_t reverse_ring;     /* persistent path: 1 = walk each pipeline's row tiles in reverse
+                               and keep every chunk's token rows and h rows in its ring slot
+                               (the down GEMM stores the outputs straight to recv), so that
+                               at the end the ring holds the activations of the first chunks,
+                               which moe_backward_ring reads in place; 0 = layout order, the
+                               outputs overwrite the token rows in the ring.  Every other
+                               entry point requires 0 (else MOE_EINVAL) */
 } moe_exec_t;
 
 /* Limits checked by every call: 1 <= k <= 16, k <= E <= 1024, 1 <= E_local <= E. */
@@ -321,6 +328,15 @@ int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_
  * (same tile arithmetic, same merge order).
  * With ex->trace = 1 the kernel records one moe_trace_event_t per task and per workgroup
  * start / end into the workspace (moe_persistent_trace_info).
+ * With ex->reverse_ring = 1 [qubstore, ring buffer paragraph: in the forward the ring is
+ * walked in reverse order, so that at the end it holds the activations the gradient
+ * computation needs and less is recomputed] each pipeline takes its row tiles from last to
+ * first, and the down GEMM writes each output row straight to its recv slot (a per-pair
+ * address table in the workspace), so a slot keeps its chunk's token rows and h rows until
+ * the chunk S slots later (in the pipeline's order) is gathered into it.  At the end the
+ * ring holds each pipeline's first chunks in layout order (all of them when the ring is large
+ * enough), and the workspace records which slot holds which chunk, for moe_backward_ring.
+ * Results are bit-identical to the layout order.
  * Errors: MOE_EUNSUP for a non-bf16 dtype, minibatch_rows not in {64, 128, 256}, or a
  * device where one workgroup per CU cannot be resident; MOE_ENOSPC for a ring below one
  * 256-row tile or a small workspace; MOE_EINVAL when comm_cus leaves no CU for compute.
@@ -379,7 +395,8 @@ int moe_forward_persistent_noalloc(const moe_shape_t* s, const moe_placement_t* 
 size_t moe_ring_slot_bytes(const moe_shape_t* s, const moe_exec_t* ex);
 
 /* Workspace bytes moe_forward_persistent needs (smaller than moe_workspace_bytes); includes
- * the trace region when ex->trace is 1. */
+ * a per-pair recv address table (8 bytes per moe_max_pairs) when ex->reverse_ring is 1 and
+ * the trace region after it when ex->trace is 1. */
 size_t moe_persistent_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex);
 
 /* One event of the persistent kernel's trace.  Times are wall-clock ticks of the GPU's
@@ -388,8 +405,9 @@ typedef struct {
   int64_t t_begin;   /* task start (after its waits) */
   int64_t t_end;     /* task end (its completion signal sent) */
   int32_t t_wait;    /* ticks spent waiting (or, for a mover, idle) before t_begin */
-  int32_t index;     /* gather, push: pipeline-local chunk; GEMM: row_tile * 256 + column tile;
-                        start / end: 0 = data movement, 1 = compute */
+  int32_t index;     /* gather, push: pipeline-local chunk (in the pipeline's order, reversed
+                        with reverse_ring); GEMM: row_tile * 256 + column tile (row tile in
+                        layout order); start / end: 0 = data movement, 1 = compute */
   int32_t workgroup; /* blockIdx.x */
   int16_t kind;      /* MOE_TRACE_* */
   int16_t pipeline;
@@ -409,6 +427,15 @@ typedef struct {
  * MOE_EINVAL for a bad shape, a null pointer or ex->trace != 1. */
 int moe_persistent_trace_info(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
                               size_t* offset, int32_t* capacity, int32_t* ticks_per_us);
+
+/* Where moe_forward_persistent records, in its workspace, which ring slot still holds which
+ * chunk when it returns: `entries` int32 values from byte `offset`.  Entry 4 m + h is 1 + the
+ * index of the ring slot (slot i starts at ring + i * moe_ring_slot_bytes()) that holds chunk
+ * h (its rows minibatch_rows * h onward) of row tile m (256 rows of one expert, the layout's
+ * tiles in expert order), or 0.  Every launch rewrites it: nonzero entries only with
+ * ex->reverse_ring = 1 and a clean run.  No kernel is launched; MOE_EINVAL for a bad shape
+ * or a null pointer. */
+int moe_persistent_resident_info(const moe_shape_t* s, const moe_placement_t* p, size_t* offset, int32_t* entries);
 
 /*
  * Backward of the share (bf16 only; other dtypes return MOE_EUNSUP)
@@ -488,6 +515,34 @@ int moe_backward(const moe_shape_t* s, const moe_placement_t* p, const void* con
                  const int32_t* slot_of, const void* ws, size_t ws_bytes, void* const* recv, void* const* dx,
                  float* const* dlogits, void* dw1, void* dw3, void* dw2, void* bws, size_t bws_bytes,
                  void* stream);
+
+/*
+ * moe_backward_ring -- moe_backward after moe_forward_persistent, reading the forward's
+ * activations where that call left them [qubstore, ring buffer paragraph: the forward walks
+ * the ring in reverse so that at its end the ring holds the activations the gradients need,
+ * and less is recomputed; kucoin §02: pull reverse-combine, push reverse-dispatch].
+ *   - The expert outputs o are read from recv, where the forward pushed them (no ye buffer);
+ *     recv then receives the dX rows, as in moe_backward.
+ *   - The expert-side token rows that the ring still holds (ex->reverse_ring = 1 in the
+ *     forward) are read in place by the GEMMs; only the other rows are pulled again from the
+ *     source buffers x, into xe at their rows.  ring = NULL pulls every row again.
+ *   ex, ring, ring_bytes: exactly as passed to moe_forward_persistent.
+ *   pws, pws_bytes: that call's workspace, unchanged since (its layout tables and the record
+ *     of which ring slot holds which chunk).
+ *   x: R device pointers, [T][d] bf16 (the forward's token rows).
+ *   xe: [moe_max_pairs][d] bf16, rows not in the ring (contents on return unspecified).
+ *   bws: at least moe_backward_workspace_bytes().
+ * Other arguments and results as moe_backward; bit-identical to moe_backward given the same
+ * token rows (xe) and expert outputs (ye).  bf16 only (else MOE_EUNSUP).  A ring that is not
+ * the forward's, or a workspace changed since, gives wrong results, not an error.
+ */
+int moe_backward_ring(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+                      const void* const* dy, const void* const* x, const void* ring, size_t ring_bytes,
+                      const void* pws, size_t pws_bytes, const void* w1, const void* w3, const void* w2,
+                      const int32_t* topk_idx, const float* topk_w, const int32_t* offsets,
+                      const int32_t* pull_src, const int32_t* slot_of, void* const* recv, void* const* dx,
+                      float* const* dlogits, void* dw1, void* dw3, void* dw2, void* xe, void* bws,
+                      size_t bws_bytes, void* stream);
 
 /*
  * MXFP8 backward [kucoin §02: MXFP8 in the expert data path; the pages give neither the

@@ -17,8 +17,11 @@
 
 namespace moe {
 
-// dO[s] = g dY[r][t] (bf16) and dg[s] = <dY[r][t], ye[s]> (fp32), one wave per row
+// dO[s] = g dY[r][t] (bf16) and dg[s] = <dY[r][t], o_s> (fp32), one wave per row; o_s is
+// ye[s], or with FROM_RECV the pair's recv row recv[r][t][j], where the forward pushed it.
+template <bool FROM_RECV>
 __global__ __launch_bounds__(256) void pull_reverse_kernel(RankPtrs<const char*> dy, const uint16_t* __restrict__ ye,
+                                                           RankPtrs<const char*> recv,
                                                            const int32_t* __restrict__ pull_src,
                                                            const int32_t* __restrict__ slot_of,
                                                            const float* __restrict__ topk_w,
@@ -37,7 +40,8 @@ __global__ __launch_bounds__(256) void pull_reverse_kernel(RankPtrs<const char*>
     const int j = hit ? __builtin_ctzll(hit) : 0;
     const float g = topk_w[pair0 + j];
     const u32x4* src = reinterpret_cast<const u32x4*>(dy.p[r] + int64_t(t) * d * 2);
-    const u32x4* yr = reinterpret_cast<const u32x4*>(ye + int64_t(s) * d);
+    const u32x4* yr = FROM_RECV ? reinterpret_cast<const u32x4*>(recv.p[r] + (int64_t(t) * k + j) * d * 2)
+                                : reinterpret_cast<const u32x4*>(ye + int64_t(s) * d);
     u32x4* out = reinterpret_cast<u32x4*>(dO + int64_t(s) * d);
     float acc = 0.0f;
     for (int base = 0; base < n16; base += 64 * UNROLL) {
@@ -181,13 +185,22 @@ __global__ __launch_bounds__(256) void gate_grad_kernel(const float* __restrict_
 
 constexpr int kPullRevBlocksPerCU = 4, kGateBlocksPerCU = 4;
 
+// o rows from ye, or (recv != null) from the forward's recv rows
 hipError_t launch_pull_reverse(const moe_shape_t& s, const void* const* dy, const uint16_t* ye,
                                const int32_t* pull_src, const int32_t* slot_of, const float* topk_w,
-                               const int32_t* ctrl, uint16_t* dO, float* dg, int cus, hipStream_t st) {
-  RankPtrs<const char*> dp{};
-  for (int r = 0; r < s.R; ++r) dp.p[r] = static_cast<const char*>(dy[r]);
-  hipLaunchKernelGGL(pull_reverse_kernel, dim3(cus * kPullRevBlocksPerCU), dim3(256), 0, st, dp, ye, pull_src, slot_of,
-                     topk_w, ctrl, dO, dg, s.T, s.k, s.d);
+                               const int32_t* ctrl, uint16_t* dO, float* dg, int cus, hipStream_t st,
+                               void* const* recv) {
+  RankPtrs<const char*> dp{}, rp{};
+  for (int r = 0; r < s.R; ++r) {
+    dp.p[r] = static_cast<const char*>(dy[r]);
+    if (recv) rp.p[r] = static_cast<const char*>(recv[r]);
+  }
+  if (recv)
+    hipLaunchKernelGGL(pull_reverse_kernel<true>, dim3(cus * kPullRevBlocksPerCU), dim3(256), 0, st, dp, ye, rp,
+                       pull_src, slot_of, topk_w, ctrl, dO, dg, s.T, s.k, s.d);
+  else
+    hipLaunchKernelGGL(pull_reverse_kernel<false>, dim3(cus * kPullRevBlocksPerCU), dim3(256), 0, st, dp, ye, rp,
+                       pull_src, slot_of, topk_w, ctrl, dO, dg, s.T, s.k, s.d);
   return hipGetLastError();
 }
 

@@ -95,6 +95,7 @@ inline WsLayout ws_layout(const moe_shape_t& s, int32_t E_local) {
 // of the dispatched token rows for the weight gradients.
 struct BwdLayout {
   size_t dO, dg, dh, h, dab, dX, dgp;
+  size_t rows, blks;                  // moe_backward_ring: token row addresses (per row, per 64-row block)
   size_t dOq, dOs, dabq, dabs, xeb;   // MXFP8 only (0 otherwise)
   size_t total;
 };
@@ -111,6 +112,9 @@ inline BwdLayout bwd_layout(const moe_shape_t& s, int32_t E_local) {
   b.dab = o;  o = align256(o + n * F * 4);
   b.dX = o;   o = align256(o + n * d * 2);
   b.dgp = o;  o = align256(o + size_t(s.R) * s.T * s.k * 4);
+  const size_t mtiles = size_t((mp + kGemmBM - 1) / kGemmBM + E_local);
+  b.rows = o; o = align256(o + n * 8);
+  b.blks = o; o = align256(o + mtiles * 4 * 8);
   if (s.dtype == MOE_MXFP8) {
     b.dOq = o;  o = align256(o + n * d);
     b.dOs = o;  o = align256(o + n * (d / 32));
@@ -120,6 +124,16 @@ inline BwdLayout bwd_layout(const moe_shape_t& s, int32_t E_local) {
   }
   b.total = o;
   return b;
+}
+
+// which local expert owns global row tile mt (binary search on the tile prefix)
+__device__ __forceinline__ int find_expert(const int32_t* __restrict__ mtile_base, int El, int mt) {
+  int lo = 0, hi = El - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (mtile_base[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  return lo;
 }
 
 // per-rank pointer table passed by value to kernels

@@ -158,13 +158,14 @@ hipError_t launch_ffn(const moe_shape_t& s, int El, const void* xe, const int32_
 
 // ---- backward (bf16) ----
 // GEMM1 again with the backward epilogue: h and [da | db] from xe, W1, W3 and dh
+// row_src: null (token rows from xe), or per local pair the address of its token row
 hipError_t launch_gemm1_bwd(const uint16_t* xe, const uint16_t* w1, const uint16_t* w3, const uint16_t* dh,
                             uint16_t* h, uint16_t* dab, int d, int F, const int32_t* offsets, const int32_t* mtb,
-                            const int32_t* ctrl, int El, int cus, hipStream_t st) {
+                            const int32_t* ctrl, int El, int cus, hipStream_t st, const uint64_t* row_src) {
   hipError_t e = set_gemm_lds_attrs();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<2>, dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st, xe, w1, w3,
-                     h, offsets, mtb, ctrl, El, d, F, dh, dab, nullptr, nullptr);
+  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<2>, dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st,
+                     row_src ? nullptr : xe, w1, w3, h, offsets, mtb, ctrl, El, d, F, dh, dab, nullptr, row_src);
   return hipGetLastError();
 }
 

@@ -35,6 +35,9 @@ typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 //   MN-major: element (k, c) of the tile is at p0 + k * ld + c for k < ksplit and at
 //            p1 + (k - ksplit) * ld + c after; rows = valid tile columns (a multiple of 8);
 //            K rows from kvalid on re-read row kvalid - 1 (and are zeroed when masked).
+//            With kblk (the B operand of a tile instantiated with B_BLK): K rows come in
+//            blocks of 64, block i starting at kblk[i], and element (k, c) is at
+//            kblk[k / 64] + (k % 64) * ld + coff + c.
 struct Operand {
   const uint16_t* p0;
   const uint16_t* p1;
@@ -42,6 +45,8 @@ struct Operand {
   int rows;
   int ksplit;
   int kvalid;
+  const uint64_t* kblk = nullptr;
+  int coff = 0;
 };
 
 __device__ __forceinline__ int mn_off(int row, int col) {
@@ -70,7 +75,7 @@ __device__ __forceinline__ bf16x8 ld_frag_mn(const char* tile, int kb, int c0, i
 // ROW_DST: row_dst[r] is the address output row r goes to (then `out` is unused and col0 is
 // the tile's first output column); the tile is staged in LDS and stored row by row in 16-byte
 // vectors (ocols % 8 == 0).  A compile-time switch, so the other instantiations keep their code.
-template <bool A_MN, bool B_MN, bool MASK_K, bool ROW_DST = false>
+template <bool A_MN, bool B_MN, bool MASK_K, bool ROW_DST = false, bool B_BLK = false>
 __device__ __forceinline__ void gemm_tile_t(const Operand& A, const Operand& B, uint16_t* __restrict__ out, int o_ld,
                                             int orows, int ocols, int K, char* smem,
                                             const uint64_t* __restrict__ row_dst = nullptr, int col0 = 0) {
@@ -102,6 +107,10 @@ __device__ __forceinline__ void gemm_tile_t(const Operand& A, const Operand& B, 
     kg = min(kg, X.kvalid - 1);
     return (kg < X.ksplit ? X.p0 + size_t(kg) * X.ld : X.p1 + size_t(kg - X.ksplit) * X.ld) + col;
   };
+  // B_BLK: the base of B's 64-row block of the K step being issued (bblk), and of the next
+  // one, loaded a K step ahead
+  const uint16_t* bblk = nullptr;
+  uint64_t bnext = 0;
   auto issue = [&](int ks) {
     char* sa = smem + (ks & 1) * kStageBytes;
     char* sb = sa + kGemmBM * kGemmBK * 2;
@@ -111,7 +120,9 @@ __device__ __forceinline__ void gemm_tile_t(const Operand& A, const Operand& B, 
       const int g = wave * 4 + i;
       const int kg = koff + 8 * wave + 2 * i + hi;
       const uint16_t* pa = A_MN ? mn_src(A, kg, acol[i]) : ak[i] + koff;
-      const uint16_t* pb = B_MN ? mn_src(B, kg, bcol[i]) : bk[i] + koff;
+      const uint16_t* pb;
+      if constexpr (B_BLK) pb = bblk + size_t(min(kg, B.kvalid - 1) - koff) * B.ld + B.coff + bcol[i];
+      else pb = B_MN ? mn_src(B, kg, bcol[i]) : bk[i] + koff;
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(pa), (lds_void_ptr)(sa + g * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(pb), (lds_void_ptr)(sb + g * 1024), 16, 0, 0);
     }
@@ -125,12 +136,22 @@ __device__ __forceinline__ void gemm_tile_t(const Operand& A, const Operand& B, 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
 
+  if constexpr (B_BLK) {
+    bblk = reinterpret_cast<const uint16_t*>(B.kblk[0]);
+    if (nk > 1) bnext = B.kblk[1];
+  }
   issue(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int ks = 0; ks < nk; ++ks) {
-    if (ks + 1 < nk) issue(ks + 1);
+    if (ks + 1 < nk) {
+      if constexpr (B_BLK) {
+        bblk = reinterpret_cast<const uint16_t*>(bnext);
+        if (ks + 2 < nk) bnext = B.kblk[ks + 2];
+      }
+      issue(ks + 1);
+    }
     const char* sa = smem + (ks & 1) * kStageBytes;
     const char* sb = sa + kGemmBM * kGemmBK * 2;
     const int klim = MASK_K ? A.kvalid - ks * kGemmBK : kGemmBK;
@@ -248,9 +269,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_rows_bmn_kernel(
 //   dW2 = dO^T h (A = dO, M = d; B = h, Nc = F).
 // K runs over the expert's rows rounded up to 64; A's values past the last row are zeroed.
 // An expert with no rows gets zeros.
+// B_BLK: B's rows are read by 64-row blocks, block b of row tile m starting at
+// BBlk[m * 4 + b] (mtile_base gives each expert's first row tile), instead of from Bm.
+template <bool B_BLK>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_wgrad_bf16_kernel(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ Bm, int ldb,
-    const int32_t* __restrict__ offsets, uint16_t* __restrict__ C, int El, int M, int Nc) {
+    const int32_t* __restrict__ offsets, uint16_t* __restrict__ C, int El, int M, int Nc,
+    const uint64_t* __restrict__ BBlk, const int32_t* __restrict__ mtile_base) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int MT = (M + kGemmBM - 1) / kGemmBM, NT = (Nc + kGemmBN - 1) / kGemmBN;
   const int total = El * MT * NT;
@@ -277,8 +302,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_wgrad_bf16_kernel(
       continue;
     }
     const Operand a{A + size_t(r0) * lda + m0, nullptr, lda, M - m0, 1 << 30, n};
-    const Operand b{Bm + size_t(r0) * ldb + c0, nullptr, ldb, Nc - c0, 1 << 30, n};
-    gemm_tile_t<true, true, true>(a, b, out, Nc, rows, cols, (n + kGemmBK - 1) & ~(kGemmBK - 1), smem);
+    Operand b{B_BLK ? nullptr : Bm + size_t(r0) * ldb + c0, nullptr, ldb, Nc - c0, 1 << 30, n};
+    if constexpr (B_BLK) {
+      b.kblk = BBlk + size_t(mtile_base[l]) * 4;
+      b.coff = c0;
+    }
+    gemm_tile_t<true, true, true, false, B_BLK>(a, b, out, Nc, rows, cols, (n + kGemmBK - 1) & ~(kGemmBK - 1), smem);
   }
 }
 
@@ -287,7 +316,8 @@ hipError_t set_bwd_gemm_lds_attrs() {
   return once_per_device(done, [] {
     const void* ks[] = {reinterpret_cast<const void*>(grouped_rows_bmn_kernel<false>),
                         reinterpret_cast<const void*>(grouped_rows_bmn_kernel<true>),
-                        reinterpret_cast<const void*>(grouped_wgrad_bf16_kernel)};
+                        reinterpret_cast<const void*>(grouped_wgrad_bf16_kernel<false>),
+                        reinterpret_cast<const void*>(grouped_wgrad_bf16_kernel<true>)};
     for (const void* k : ks) {
       const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
       if (e != hipSuccess) return e;
@@ -311,12 +341,18 @@ hipError_t launch_rows_bmn(const uint16_t* A, const uint16_t* B0, const uint16_t
   return hipGetLastError();
 }
 
+// b_blk: null (B rows from B), or the 64-row block table of B's rows (with mtile_base)
 hipError_t launch_wgrad(const uint16_t* A, int lda, const uint16_t* B, int ldb, const int32_t* offsets, uint16_t* C,
-                        int El, int M, int Nc, int cus, hipStream_t st) {
+                        int El, int M, int Nc, int cus, hipStream_t st, const uint64_t* b_blk,
+                        const int32_t* mtile_base) {
   hipError_t e = set_bwd_gemm_lds_attrs();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(grouped_wgrad_bf16_kernel, dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st, A, lda, B, ldb,
-                     offsets, C, El, M, Nc);
+  if (b_blk)
+    hipLaunchKernelGGL(grouped_wgrad_bf16_kernel<true>, dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st, A, lda,
+                       nullptr, ldb, offsets, C, El, M, Nc, b_blk, mtile_base);
+  else
+    hipLaunchKernelGGL(grouped_wgrad_bf16_kernel<false>, dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st, A,
+                       lda, B, ldb, offsets, C, El, M, Nc, nullptr, nullptr);
   return hipGetLastError();
 }
 

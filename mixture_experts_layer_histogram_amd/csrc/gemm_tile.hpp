@@ -424,14 +424,4 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
   }
 }
 
-// which local expert owns global row tile mt (binary search on the tile prefix)
-__device__ __forceinline__ int find_expert(const int32_t* __restrict__ mtile_base, int El, int mt) {
-  int lo = 0, hi = El - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (mtile_base[mid] <= mt) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 }  // namespace moe

@@ -34,19 +34,25 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
                              const int32_t* offsets, char* ring, long long slot_bytes, int blk_log2,
                              const sched::Plan& plan, int grid, long long budget, void* const* recv, char* ws,
                              const WsLayout& L, moe_trace_event_t* trace, int32_t* trace_count, int trace_cap,
-                             hipStream_t st);
+                             const uint64_t* row_dst, hipStream_t st);
 hipError_t persistent_occupancy(int* blocks_per_cu);
 hipError_t launch_rows_bmn(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, int ksplit, uint16_t* C, int K,
                            int Nout, const int32_t* offsets, const int32_t* mtb, const int32_t* ctrl, int El, int cus,
                            hipStream_t st, const uint64_t* row_dst);
 hipError_t launch_gemm1_bwd(const uint16_t* xe, const uint16_t* w1, const uint16_t* w3, const uint16_t* dh,
                             uint16_t* h, uint16_t* dab, int d, int F, const int32_t* offsets, const int32_t* mtb,
-                            const int32_t* ctrl, int El, int cus, hipStream_t st);
+                            const int32_t* ctrl, int El, int cus, hipStream_t st, const uint64_t* row_src = nullptr);
 hipError_t launch_wgrad(const uint16_t* A, int lda, const uint16_t* B, int ldb, const int32_t* offsets, uint16_t* C,
-                        int El, int M, int Nc, int cus, hipStream_t st);
+                        int El, int M, int Nc, int cus, hipStream_t st, const uint64_t* b_blk = nullptr,
+                        const int32_t* mtile_base = nullptr);
 hipError_t launch_pull_reverse(const moe_shape_t& s, const void* const* dy, const uint16_t* ye,
                                const int32_t* pull_src, const int32_t* slot_of, const float* topk_w,
-                               const int32_t* ctrl, uint16_t* dO, float* dg, int cus, hipStream_t st);
+                               const int32_t* ctrl, uint16_t* dO, float* dg, int cus, hipStream_t st,
+                               void* const* recv = nullptr);
+hipError_t launch_ring_rows(const moe_shape_t& s, int El, int max_mtiles, const void* const* x, const int32_t* pull_src,
+                            const int32_t* offsets, const int32_t* mtile_base, const int32_t* ctrl,
+                            const int32_t* resident, const void* ring, long long slot_bytes, int n_slots,
+                            int chunk_log2, void* xe, uint64_t* blk_src, uint64_t* row_src, int cus, hipStream_t st);
 hipError_t launch_gate_grad(const moe_shape_t& s, const float* topk_w, const int32_t* topk_idx, const int32_t* slot_of,
                             const float* dgp, float* const* dlogits, int cus, hipStream_t st);
 hipError_t launch_push_grad(const moe_shape_t& s, const char* dX, const float* dg, const int32_t* pull_src,
@@ -155,7 +161,7 @@ int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
 // execution knobs of the multi-kernel entry points: the trace is the persistent path's only
 int check_ex(const moe_exec_t* ex) {
-  if (ex && (ex->trace != 0 || ex->minibatch_rows < 0)) return MOE_EINVAL;
+  if (ex && (ex->trace != 0 || ex->reverse_ring != 0 || ex->minibatch_rows < 0)) return MOE_EINVAL;
   return MOE_OK;
 }
 
@@ -388,12 +394,16 @@ int trace_capacity(const moe_shape_t& s, const WsLayout& L, const moe_exec_t* ex
 size_t trace_bytes(const moe_shape_t& s, const WsLayout& L, const moe_exec_t* ex) {
   return align256(256 + size_t(trace_capacity(s, L, ex)) * sizeof(moe_trace_event_t));
 }
+// reverse ring: the per-pair recv address table of the down GEMM's stores, at L.hbuf
+size_t reverse_table_bytes(const WsLayout& L, const moe_exec_t* ex) {
+  return (ex && ex->reverse_ring == 1) ? align256(size_t(L.max_pairs) * 8) : 0;
+}
 }  // namespace
 
 size_t moe_persistent_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex) {
   if (check_shape(s, p) != MOE_OK) return 0;
   const WsLayout L = ws_layout(*s, p->E_local);
-  return L.hbuf + ((ex && ex->trace) ? trace_bytes(*s, L, ex) : 0);   // no h staging
+  return L.hbuf + reverse_table_bytes(L, ex) + ((ex && ex->trace) ? trace_bytes(*s, L, ex) : 0);   // no h staging
 }
 
 int moe_persistent_trace_info(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex, size_t* offset,
@@ -401,9 +411,17 @@ int moe_persistent_trace_info(const moe_shape_t* s, const moe_placement_t* p, co
   if (check_shape(s, p) != MOE_OK || !ex || ex->trace != 1 || !offset || !capacity || !ticks_per_us)
     return MOE_EINVAL;
   const WsLayout L = ws_layout(*s, p->E_local);
-  *offset = L.hbuf;
+  *offset = L.hbuf + reverse_table_bytes(L, ex);
   *capacity = trace_capacity(*s, L, ex);
   *ticks_per_us = static_cast<int32_t>(wall_ticks_per_us());
+  return MOE_OK;
+}
+
+int moe_persistent_resident_info(const moe_shape_t* s, const moe_placement_t* p, size_t* offset, int32_t* entries) {
+  if (check_shape(s, p) != MOE_OK || !offset || !entries) return MOE_EINVAL;
+  const WsLayout L = ws_layout(*s, p->E_local);
+  *offset = L.pctrl + size_t(sched::ctrl_layout(L.max_mtiles, kMaxRingSlots).resident) * 4;
+  *entries = L.max_mtiles * 4;
   return MOE_OK;
 }
 
@@ -415,7 +433,8 @@ struct PersistSetup {
   sched::Plan plan;
   long long slot_bytes, budget;
   int blk_log2, cus;
-  bool tracing;
+  bool tracing, reverse;
+  size_t rev_bytes;      // reverse ring: the recv address table at L.hbuf
 };
 
 int persist_setup(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex, const void* const* x,
@@ -430,7 +449,8 @@ int persist_setup(const moe_shape_t* s, const moe_placement_t* p, const moe_exec
   if (!ring) return MOE_EINVAL;
   if (reinterpret_cast<uintptr_t>(ring) & 255) return MOE_EALIGN;
   if ((rc = check_ptr_table(x, s->R)) || (rc = check_ptr_table(recv, s->R))) return rc;
-  if (ex && (ex->minibatch_rows < 0 || ex->comm_cus < 0 || ex->ring_slots < 0 || ex->trace < 0 || ex->trace > 1))
+  if (ex && (ex->minibatch_rows < 0 || ex->comm_cus < 0 || ex->ring_slots < 0 || ex->trace < 0 || ex->trace > 1 ||
+             ex->reverse_ring < 0 || ex->reverse_ring > 1))
     return MOE_EINVAL;
   out->blk_log2 = chunk_log2_of(ex);
   if (out->blk_log2 < 0) return MOE_EUNSUP;
@@ -438,7 +458,9 @@ int persist_setup(const moe_shape_t* s, const moe_placement_t* p, const moe_exec
   if (!ws) return MOE_EINVAL;
   if (reinterpret_cast<uintptr_t>(ws) & 255) return MOE_EALIGN;
   out->tracing = ex && ex->trace == 1;
-  if (ws_bytes < out->L.hbuf + (out->tracing ? trace_bytes(*s, out->L, ex) : 0)) return MOE_ENOSPC;
+  out->reverse = ex && ex->reverse_ring == 1;
+  out->rev_bytes = reverse_table_bytes(out->L, ex);
+  if (ws_bytes < out->L.hbuf + out->rev_bytes + (out->tracing ? trace_bytes(*s, out->L, ex) : 0)) return MOE_ENOSPC;
   const int cpm = kGemmBM >> out->blk_log2;
   out->slot_bytes = static_cast<long long>(ring_slot_bytes(*s, out->blk_log2));
   long long slots = static_cast<long long>(ring_bytes / size_t(out->slot_bytes));
@@ -461,11 +483,20 @@ int persist_launch(const moe_shape_t* s, const moe_placement_t* p, const moe_exe
                    const int32_t* pull_src, const int32_t* slot_of, const int32_t* offsets, void* const* recv,
                    void* ws, hipStream_t st) {
   char* wsc = static_cast<char*>(ws);
-  moe_trace_event_t* trace = P.tracing ? reinterpret_cast<moe_trace_event_t*>(wsc + P.L.hbuf + 256) : nullptr;
-  int32_t* trace_count = P.tracing ? reinterpret_cast<int32_t*>(wsc + P.L.hbuf) : nullptr;
+  const size_t toff = P.L.hbuf + P.rev_bytes;
+  moe_trace_event_t* trace = P.tracing ? reinterpret_cast<moe_trace_event_t*>(wsc + toff + 256) : nullptr;
+  int32_t* trace_count = P.tracing ? reinterpret_cast<int32_t*>(wsc + toff) : nullptr;
+  uint64_t* row_dst = nullptr;
+  if (P.reverse) {      // the recv address of every local pair, for the down GEMM's stores
+    row_dst = reinterpret_cast<uint64_t*>(wsc + P.L.hbuf);
+    const hipError_t e = launch_pair_addr(*s, pull_src, slot_of, recv, nullptr,
+                                          reinterpret_cast<const int32_t*>(wsc + P.L.ctrl), row_dst, nullptr,
+                                          P.cus, st, nullptr, nullptr);
+    if (e != hipSuccess) return MOE_EHIP;
+  }
   return hip_rc(launch_persistent(*s, p->E_local, x, w1, w3, w2, pull_src, slot_of, offsets, static_cast<char*>(ring),
                                   P.slot_bytes, P.blk_log2, P.plan, P.cus, P.budget, recv, wsc, P.L, trace,
-                                  trace_count, P.tracing ? trace_capacity(*s, P.L, ex) : 0, st));
+                                  trace_count, P.tracing ? trace_capacity(*s, P.L, ex) : 0, row_dst, st));
 }
 
 int persist_occupancy_ok() {
@@ -630,10 +661,12 @@ int moe_combine_pull_reverse(const moe_shape_t* s, const moe_placement_t* p, con
 
 // recv == null: dX rows to the backward workspace (the staged API); else the push of dX fused
 // into its GEMM (rows straight to recv, the gate gradients pushed to dgp by the table kernel)
+// row_src / blk_src (both or neither): the token rows by address (per row, and per 64-row
+// block of each row tile) instead of from xe
 static int ffn_backward_impl(const moe_shape_t* s, const moe_placement_t* p, const void* xe, const int32_t* offsets,
                              const void* w1, const void* w3, const void* w2, const void* ws, void* dw1, void* dw3,
                              void* dw2, void* bws, const int32_t* pull_src, const int32_t* slot_of, void* const* recv,
-                             void* stream) {
+                             void* stream, const uint64_t* row_src = nullptr, const uint64_t* blk_src = nullptr) {
   const WsLayout L = ws_layout(*s, p->E_local);
   const BwdLayout B = bwd_layout(*s, p->E_local);
   const char* w = static_cast<const char*>(ws);
@@ -653,7 +686,7 @@ static int ffn_backward_impl(const moe_shape_t* s, const moe_placement_t* p, con
   hipStream_t st = static_cast<hipStream_t>(stream);
   // dh = dO W2; then h, da, db in GEMM1's backward epilogue; dX = [da|db] [W1; W3]
   hipError_t e = launch_rows_bmn(dO, w2b, nullptr, d, dh, d, F, offsets, mtb, ctrl, El, cus, st, nullptr);
-  if (e == hipSuccess) e = launch_gemm1_bwd(xeb, w1b, w3b, dh, h, dab, d, F, offsets, mtb, ctrl, El, cus, st);
+  if (e == hipSuccess) e = launch_gemm1_bwd(xeb, w1b, w3b, dh, h, dab, d, F, offsets, mtb, ctrl, El, cus, st, row_src);
   uint64_t* dx_dst = nullptr;
   if (recv) {             // the address table lives in the dX staging region, unused when fused
     dx_dst = reinterpret_cast<uint64_t*>(dX);
@@ -664,9 +697,10 @@ static int ffn_backward_impl(const moe_shape_t* s, const moe_placement_t* p, con
   if (e == hipSuccess)
     e = launch_rows_bmn(dab, w1b, w3b, F, recv ? nullptr : dX, 2 * F, d, offsets, mtb, ctrl, El, cus, st, dx_dst);
   // weight gradients over each expert's rows: dW1 = da^T x, dW3 = db^T x, dW2 = dO^T h
-  if (e == hipSuccess) e = launch_wgrad(dab, 2 * F, xeb, d, offsets, static_cast<uint16_t*>(dw1), El, F, d, cus, st);
   if (e == hipSuccess)
-    e = launch_wgrad(dab + F, 2 * F, xeb, d, offsets, static_cast<uint16_t*>(dw3), El, F, d, cus, st);
+    e = launch_wgrad(dab, 2 * F, xeb, d, offsets, static_cast<uint16_t*>(dw1), El, F, d, cus, st, blk_src, mtb);
+  if (e == hipSuccess)
+    e = launch_wgrad(dab + F, 2 * F, xeb, d, offsets, static_cast<uint16_t*>(dw3), El, F, d, cus, st, blk_src, mtb);
   if (e == hipSuccess) e = launch_wgrad(dO, d, h, F, offsets, static_cast<uint16_t*>(dw2), El, d, F, cus, st);
   return hip_rc(e);
 }
@@ -736,6 +770,71 @@ int moe_backward(const moe_shape_t* s, const moe_placement_t* p, const void* con
   const int cus = cu_count();
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_merge(*s, slot_of, nullptr, recv, dx, cus, st);
+  if (e == hipSuccess) e = launch_gate_grad(*s, topk_w, topk_idx, slot_of, dgp, dlogits, cus, st);
+  return hip_rc(e);
+}
+
+int moe_backward_ring(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
+                      const void* const* dy, const void* const* x, const void* ring, size_t ring_bytes,
+                      const void* pws, size_t pws_bytes, const void* w1, const void* w3, const void* w2,
+                      const int32_t* topk_idx, const float* topk_w, const int32_t* offsets,
+                      const int32_t* pull_src, const int32_t* slot_of, void* const* recv, void* const* dx,
+                      float* const* dlogits, void* dw1, void* dw3, void* dw2, void* xe, void* bws,
+                      size_t bws_bytes, void* stream) {
+  int rc = check_shape(s, p);
+  if (rc) return rc;
+  if (s->dtype != MOE_BF16) return MOE_EUNSUP;
+  // the forward's workspace: its layout tables and control block (moe_persistent_workspace_bytes)
+  const WsLayout L = ws_layout(*s, p->E_local);
+  if (!pws) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(pws) & 255) return MOE_EALIGN;
+  if (pws_bytes < L.hbuf) return MOE_ENOSPC;
+  if (!bws) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(bws) & 255) return MOE_EALIGN;
+  const BwdLayout B = bwd_layout(*s, p->E_local);
+  if (bws_bytes < B.total) return MOE_ENOSPC;
+  if (ex && (ex->minibatch_rows < 0 || ex->reverse_ring < 0 || ex->reverse_ring > 1)) return MOE_EINVAL;
+  const int blk_log2 = chunk_log2_of(ex);
+  if (blk_log2 < 0) return MOE_EUNSUP;
+  if (!topk_idx || !topk_w || !offsets || !pull_src || !slot_of) return MOE_EINVAL;
+  const void* bufs[] = {xe, w1, w3, w2, dw1, dw3, dw2};
+  for (const void* q : bufs)
+    if (!aligned16(q)) return q ? MOE_EALIGN : MOE_EINVAL;
+  if (ring && (reinterpret_cast<uintptr_t>(ring) & 255)) return MOE_EALIGN;
+  if ((rc = check_ptr_table(dy, s->R)) || (rc = check_ptr_table(x, s->R)) || (rc = check_ptr_table(recv, s->R)) ||
+      (rc = check_ptr_table(dx, s->R)))
+    return rc;
+  if (!dlogits) return MOE_EINVAL;
+  for (int r = 0; r < s->R; ++r)
+    if (!dlogits[r]) return MOE_EINVAL;
+  // ring slots the recorded chunks may name (a slot past the ring counts as not held)
+  const long long slot_bytes = static_cast<long long>(ring_slot_bytes(*s, blk_log2));
+  long long n_slots = ring ? static_cast<long long>(ring_bytes / size_t(slot_bytes)) : 0;
+  if (n_slots > kMaxRingSlots) n_slots = kMaxRingSlots;
+
+  const char* w = static_cast<const char*>(pws);
+  const int32_t* ctrl = reinterpret_cast<const int32_t*>(w + L.ctrl);
+  const int32_t* mtb = reinterpret_cast<const int32_t*>(w + L.mtile_base);
+  const sched::CtrlLayout cl = sched::ctrl_layout(L.max_mtiles, kMaxRingSlots);
+  const int32_t* resident = reinterpret_cast<const int32_t*>(w + L.pctrl) + cl.resident;
+  char* b = static_cast<char*>(bws);
+  uint64_t* row_src = reinterpret_cast<uint64_t*>(b + B.rows);
+  uint64_t* blk_src = reinterpret_cast<uint64_t*>(b + B.blks);
+  const int cus = cu_count();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // pull reverse-combine with the expert outputs read from recv, then where every token row is
+  hipError_t e = launch_pull_reverse(*s, dy, nullptr, pull_src, slot_of, topk_w, ctrl,
+                                     reinterpret_cast<uint16_t*>(b + B.dO), reinterpret_cast<float*>(b + B.dg), cus, st,
+                                     recv);
+  if (e == hipSuccess)
+    e = launch_ring_rows(*s, p->E_local, L.max_mtiles, x, pull_src, offsets, mtb, ctrl, resident, ring, slot_bytes,
+                         int(n_slots), blk_log2, xe, blk_src, row_src, cus, st);
+  if (e != hipSuccess) return MOE_EHIP;
+  if ((rc = ffn_backward_impl(s, p, nullptr, offsets, w1, w3, w2, pws, dw1, dw3, dw2, bws, pull_src, slot_of, recv,
+                              stream, row_src, blk_src)))
+    return rc;
+  float* dgp = reinterpret_cast<float*>(b + B.dgp);
+  e = launch_merge(*s, slot_of, nullptr, recv, dx, cus, st);
   if (e == hipSuccess) e = launch_gate_grad(*s, topk_w, topk_idx, slot_of, dgp, dlogits, cus, st);
   return hip_rc(e);
 }

@@ -63,6 +63,8 @@ struct CtrlLayout {
   int grp_len;       // [max_mtiles]
   int phase_start;   // [2 * max_mtiles + kMaxPipes]: pipeline p's phases from 2 lo + p
   int slot_epoch;    // [max_slots]: pushes that freed the slot
+  int resident;      // [max_mtiles * 4]: after a reverse-ring launch, 1 + the ring slot that
+                     // still holds chunk h of row tile m (m * 4 + h), or 0
   int words;         // total
 };
 
@@ -77,7 +79,8 @@ MOE_HD CtrlLayout ctrl_layout(int max_mtiles, int max_slots) {
   c.grp_len = c.grp_first + max_mtiles;
   c.phase_start = c.grp_len + max_mtiles;
   c.slot_epoch = c.phase_start + 2 * max_mtiles + kMaxPipes;
-  c.words = c.slot_epoch + max_slots;
+  c.resident = c.slot_epoch + max_slots;
+  c.words = c.resident + max_mtiles * 4;
   return c;
 }
 

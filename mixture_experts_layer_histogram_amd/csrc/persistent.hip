@@ -30,6 +30,14 @@
 //   drops stale lines of its own).
 // * Ring slot.  One minibatch (chunk) of token rows, overwritten in place by the expert
 //   outputs of those rows, followed by the rows' h.
+// * Reverse ring (qubstore.ru, ring buffer paragraph: the forward walks the ring in reverse
+//   so that at its end the ring holds the activations the gradients need).  Each pipeline
+//   takes its row tiles from last to first: the rules below run on the pipeline's own order
+//   (tile index m in [lo, hi)) and only the data addressing maps m to the layout's row tile
+//   lo + hi - 1 - m.  The down GEMM then stores each output row straight to its recv slot,
+//   so a slot keeps its chunk's token rows and h rows until it is reused, and a push only
+//   frees the slot.  The last S chunks of a pipeline's order -- its first chunks in layout
+//   order -- are never overwritten; the check kernel records which slot holds each of them.
 // * Watchdog.  Every wait is bounded by a wall-clock budget; on expiry the workgroup sets
 //   the status word (MOE_ETIMEOUT) and an abort word that every loop checks, so all
 //   workgroups exit.  A check kernel afterwards reports MOE_EINCOMPLETE if any pipeline's
@@ -63,8 +71,16 @@ struct PersistArgs {
   int T, k, d, F, El;
   int blk_log2, cpm;            // chunk rows (log2) and chunks per 256-row tile
   int n_part, light, comm_pp, S, G, lookahead;
+  int reverse;                  // 1: reverse ring (pipelines walk their row tiles backwards)
+  int max_mtiles;               // entries of the resident record: 4 per row tile
+  const uint64_t* row_dst;      // reverse ring: per local pair, the address of its recv row
   CtrlLayout cl;
 };
+
+// Layout row tile of pipeline tile m (the pipeline owns [lo, lo + n_m)).
+__device__ __forceinline__ int layout_tile(int reverse, int lo, int n_m, int m) {
+  return reverse ? 2 * lo + n_m - 1 - m : m;
+}
 
 struct DevOps {
   int32_t* pc;
@@ -218,7 +234,9 @@ __global__ __launch_bounds__(1024) void persist_prep_kernel(PersistArgs A, int z
   int32_t* gf = A.pc + A.cl.grp_first + lo;
   int32_t* gl = A.pc + A.cl.grp_len + lo;
   const int El = A.El;
-  const int n = sched::build_groups(lo, hi, A.G, [&](int m) { return find_expert(mtb, El, m); }, gf, gl);
+  const int rev = A.reverse, n_m = hi - lo;
+  const int n = sched::build_groups(
+      lo, hi, A.G, [&](int m) { return find_expert(mtb, El, layout_tile(rev, lo, n_m, m)); }, gf, gl);
   const int NT1 = (A.F + kGemmBN / 2 - 1) / (kGemmBN / 2);
   const int NT2 = (A.d + kGemmBN - 1) / kGemmBN;
   const int tickets = n ? sched::build_phases(n, gl, NT1, NT2, A.lookahead != 0, A.pc + A.cl.phase_start + 2 * lo + p)
@@ -231,7 +249,10 @@ __global__ __launch_bounds__(1024) void persist_prep_kernel(PersistArgs A, int z
 }
 
 // After the persistent kernel: every pipeline must have claimed all its gathers, pushes and
-// tickets; otherwise (and unless a watchdog already reported) MOE_EINCOMPLETE.
+// tickets; otherwise (and unless a watchdog already reported) MOE_EINCOMPLETE.  Then the
+// record of the chunks the ring still holds (reverse ring only, and only after a clean run:
+// pipeline p's last S chunks in its order, each in slot q mod S, never overwritten).  One
+// block of 64 threads.
 __global__ void persist_check_kernel(PersistArgs A) {
   const int p = threadIdx.x;
   bool bad = false;
@@ -241,13 +262,25 @@ __global__ void persist_check_kernel(PersistArgs A) {
     bad = pw[sched::kGatherNext] < n_m * A.cpm || pw[sched::kPushNext] < n_m * A.cpm ||
           pw[sched::kTicketNext] < pw[sched::kNTickets];
   }
-  if (__any(bad) && threadIdx.x == 0 && *A.status == MOE_OK) *A.status = MOE_EINCOMPLETE;
+  const bool any_bad = __any(bad);
+  if (any_bad && threadIdx.x == 0 && *A.status == MOE_OK) *A.status = MOE_EINCOMPLETE;
+  int32_t* res = A.pc + A.cl.resident;
+  for (int i = threadIdx.x; i < A.max_mtiles * 4; i += blockDim.x) res[i] = 0;
+  __syncthreads();
+  if (!A.reverse || any_bad || *A.status != MOE_OK || p >= A.n_part) return;
+  const int32_t* pw = A.pc + A.cl.pipe0 + p * sched::kPipeWords;
+  const int lo = pw[sched::kLo], n_m = pw[sched::kHi] - lo;
+  const int n_chunks = n_m * A.cpm;
+  for (int q = max(0, n_chunks - A.S); q < n_chunks; ++q) {
+    const int m = layout_tile(1, lo, n_m, lo + q / A.cpm);
+    res[m * 4 + q % A.cpm] = 1 + p * A.S + sched::chunk_slot(q, A.S);
+  }
 }
 
 // One workgroup's view of its pipeline.
 struct PipeCtx {
   int p, lo, n_m, S, cpm, chunk_rows, row_bytes, n16, NT2;
-  bool light;
+  bool light, reverse;
 };
 
 __device__ __forceinline__ char* slot_ptr(const PersistArgs& A, const PipeCtx& c, int q) {   // pipeline-local chunk q
@@ -267,7 +300,7 @@ __device__ void do_gather(const PersistArgs& A, const PipeCtx& c, int q, char* s
   uint64_t* dst_tab = src_tab + kGemmBM;
   int row0, l;
   const int m = c.lo + q / c.cpm, h = q % c.cpm;
-  const int rows = tile_rows(A, m, &row0, &l);
+  const int rows = tile_rows(A, layout_tile(c.reverse, c.lo, c.n_m, m), &row0, &l);
   const int c_lo = h * c.chunk_rows, c_n = min(c.chunk_rows, rows - c_lo);
   char* dst = slot_ptr(A, c, q);
   for (int r = threadIdx.x; r < c_n; r += kGemmThreads) {
@@ -286,11 +319,17 @@ __device__ void do_gather(const PersistArgs& A, const PipeCtx& c, int q, char* s
 // Push pipeline-local chunk q: its output rows (in place in the ring) to recv[rank][token][j];
 // then free its slot (whole workgroup).
 __device__ void do_push(const PersistArgs& A, const PipeCtx& c, int q, char* smem) {
+  if (c.reverse) {      // the down GEMM already stored the rows to recv: only free the slot
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(A.pc + sched::slot_epoch_word(A.cl, c.p, c.S, q), 1, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   uint64_t* src_tab = reinterpret_cast<uint64_t*>(smem);
   uint64_t* dst_tab = src_tab + kGemmBM;
   int row0, l;
   const int m = c.lo + q / c.cpm, h = q % c.cpm;
-  const int rows = tile_rows(A, m, &row0, &l);
+  const int rows = tile_rows(A, layout_tile(c.reverse, c.lo, c.n_m, m), &row0, &l);
   const int c_lo = h * c.chunk_rows, c_n = min(c.chunk_rows, rows - c_lo);
   const char* src = slot_ptr(A, c, q);
   for (int r = threadIdx.x; r < c_n; r += kGemmThreads) {
@@ -367,6 +406,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
   c.p = int(xcc & 7) * A.n_part / 8;
   const int p = c.p;
   c.light = A.light;
+  c.reverse = A.reverse != 0;
   const int pbase = A.cl.pipe0 + p * sched::kPipeWords;
   int32_t* pw = A.pc + pbase;
   int32_t* g1_done = A.pc + A.cl.g1_done;
@@ -410,9 +450,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
       __syncthreads();
       if (ticket >= n_tickets) break;
       const sched::Task tk = sched::task_of_ticket(ticket, n_groups, phase_start, grp_first, grp_len, A.lookahead != 0);
-      const int m = tk.m;
+      const int m = tk.m;                                   // pipeline order
+      const int ml = layout_tile(A.reverse, lo, c.n_m, m);   // layout row tile
       int row0, l;
-      const int rows = tile_rows(A, m, &row0, &l);
+      const int rows = tile_rows(A, ml, &row0, &l);
       const long long t_w = wall_clock64();
       const bool ok = !tk.down ? wait_chunks(A, c, m, smem, sh) : wait_ge(g1_done + m, NT1, A, sh);
       if (!ok) {
@@ -448,7 +489,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
         const uint16_t* b1 = A.w3 + size_t(l) * A.F * A.d;
         gemm_tile<0, 16>(io, b0, b1, tk.j * (kGemmBN / 2), A.F, A.d, smem, A.d);   // x rows: sc1 loads
         release_add(g1_done + m, 1, light);
-        trace_event(A, 3, m * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
+        trace_event(A, 3, ml * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
       } else {
         io.a0 = reinterpret_cast<const uint16_t*>(s0 + xpart);
         io.a1 = reinterpret_cast<const uint16_t*>(s1 + xpart);
@@ -460,10 +501,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
         io.o3 = reinterpret_cast<uint16_t*>(s3);
         io.a_ld = A.F;
         io.o_ld = A.d;
+        if (A.reverse) io.row_dst = A.row_dst + row0;       // outputs straight to recv
         const uint16_t* b0 = A.w2 + size_t(l) * A.d * A.F;
         gemm_tile<1, 16>(io, b0, b0, tk.j * kGemmBN, A.d, A.F, smem, A.F);         // h rows: sc1 loads
         release_add(g2_done + m, 1, light);
-        trace_event(A, 4, m * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
+        trace_event(A, 4, ml * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
       }
     }
   }
@@ -528,7 +570,7 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
                              const int32_t* offsets, char* ring, long long slot_bytes, int blk_log2,
                              const sched::Plan& plan, int grid, long long budget, void* const* recv, char* ws,
                              const WsLayout& L, moe_trace_event_t* trace, int32_t* trace_count, int trace_cap,
-                             hipStream_t st) {
+                             const uint64_t* row_dst, hipStream_t st) {
   PersistArgs A{};
   for (int r = 0; r < s.R; ++r) {
     A.x.p[r] = static_cast<const char*>(x[r]);
@@ -563,6 +605,9 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
   A.S = plan.S;
   A.G = plan.G;
   A.lookahead = plan.lookahead;
+  A.reverse = row_dst ? 1 : 0;
+  A.max_mtiles = L.max_mtiles;
+  A.row_dst = row_dst;
   A.cl = sched::ctrl_layout(L.max_mtiles, kMaxRingSlots);
 
   int occ = 0;

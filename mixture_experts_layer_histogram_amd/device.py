@@ -177,6 +177,16 @@ class DeviceProblem:
                                    self.recv, self.dx, self.dlogits, self.dw1, self.dw3, self.dw2, self.bws,
                                    stream=stream, check=check)
 
+    def backward_ring(self, use_ring=True, ex=None, stream=None, check=True):
+        """moe_backward_ring after forward_persistent (same ex): token rows still in the ring are
+        read there (use_ring=False pulls every row again); expert outputs come from recv; xe is
+        staging for the rows not in the ring."""
+        return moe.moe_backward_ring(self.shape, self.placement, ex if ex is not None else self.pex, self.dy, self.x,
+                                     self.ring if use_ring else None, self.ws, self.w1, self.w3, self.w2,
+                                     self.topk_idx, self.topk_w, self.offsets, self.pull_src, self.slot_of,
+                                     self.recv, self.dx, self.dlogits, self.dw1, self.dw3, self.dw2, self.xe,
+                                     self.bws, stream=stream, check=check)
+
     def backward(self, stream=None, check=True):
         return moe.moe_backward(self.shape, self.placement, self.dy, self.xe, self.ye, self.w1, self.w3, self.w2,
                                 self.topk_idx, self.topk_w, self.offsets, self.pull_src, self.slot_of,

@@ -25,9 +25,11 @@ EXPORTS = ["moe_max_pairs", "moe_workspace_bytes", "moe_mx_quantize", "moe_layou
            "moe_expert_ffn", "moe_expert_ffn_push", "moe_weighted_merge", "moe_combine_push", "moe_forward",
            "moe_forward_fused", "moe_forward_persistent", "moe_persistent_dispatch_ffn_combine",
            "moe_forward_persistent_noalloc", "moe_ring_slot_bytes", "moe_persistent_workspace_bytes", "moe_persistent_trace_info",
+           "moe_persistent_resident_info",
            "moe_backward_workspace_bytes",
            "moe_combine_pull_reverse", "moe_expert_ffn_backward",
-           "moe_dispatch_push_reverse", "moe_backward", "moe_backward_prepare_mx", "moe_backward_mx",
+           "moe_dispatch_push_reverse", "moe_backward", "moe_backward_ring", "moe_backward_prepare_mx",
+           "moe_backward_mx",
            "moe_signal_probe_bytes", "moe_signal_probe", "moe_read_status", "moe_strerror", "moe_version"]
 
 
@@ -55,7 +57,7 @@ class MXScales(ctypes.Structure):
 class Exec(ctypes.Structure):
     _fields_ = [("minibatch_rows", ctypes.c_int32), ("comm_cus", ctypes.c_int32),
                 ("ring_slots", ctypes.c_int32), ("trace", ctypes.c_int32),
-                ("watchdog_us", ctypes.c_uint64)]
+                ("watchdog_us", ctypes.c_uint64), ("reverse_ring", ctypes.c_int32)]
 
 
 _lib = None
@@ -97,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.moe_persistent_workspace_bytes.restype = SZ
         L.moe_persistent_trace_info.argtypes = [S, PL, EX, P(SZ), P(ctypes.c_int32), P(ctypes.c_int32)]
         L.moe_persistent_trace_info.restype = I32
+        L.moe_persistent_resident_info.argtypes = [S, PL, P(SZ), P(ctypes.c_int32)]
+        L.moe_persistent_resident_info.restype = I32
         L.moe_backward_workspace_bytes.argtypes = [S, PL]
         L.moe_backward_workspace_bytes.restype = SZ
         L.moe_combine_pull_reverse.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, SZ, VP, SZ, VP]
@@ -104,6 +108,8 @@ def lib() -> ctypes.CDLL:
         L.moe_dispatch_push_reverse.argtypes = [S, PL, VP, VP, VP, VP, VP, SZ, VP, VP, VP, VP, SZ, VP]
         L.moe_backward.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ,
                                    VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_backward_ring.argtypes = [S, PL, EX, VP, VP, VP, SZ, VP, SZ, VP, VP, VP, VP, VP, VP, VP, VP,
+                                        VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_backward_prepare_mx.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, VP]
         L.moe_backward_mx.argtypes = [S, PL, VP, VP, VP, VP, VP, VP, VP, MS, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP,
                                       SZ, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
@@ -119,7 +125,7 @@ def lib() -> ctypes.CDLL:
                   "moe_forward", "moe_forward_persistent", "moe_persistent_dispatch_ffn_combine",
                   "moe_forward_persistent_noalloc",
                   "moe_combine_pull_reverse", "moe_expert_ffn_backward", "moe_dispatch_push_reverse", "moe_backward", "moe_backward_prepare_mx",
-                  "moe_backward_mx", "moe_read_status"):
+                  "moe_backward_ring", "moe_backward_mx", "moe_read_status"):
             getattr(L, f).restype = I32
         _lib = L
     return _lib
@@ -368,6 +374,31 @@ def moe_backward(shape, placement, dy, xe, ye, w1, w3, w2, topk_idx, topk_w, off
                             _table(dx), _table(dlogits), _p(dw1), _p(dw3), _p(dw2), _p(bws),
                             bws.numel() if bws_bytes is None else bws_bytes, _stream(stream))
     return _check(rc, "moe_backward") if check else rc
+
+
+def read_resident(ws, shape, placement):
+    """The persistent forward's record of which ring slot holds each chunk (host int32 array,
+    entry 4 m + h = 1 + slot, or 0)."""
+    off, n = ctypes.c_size_t(), ctypes.c_int32()
+    _check(lib().moe_persistent_resident_info(ctypes.byref(shape), ctypes.byref(placement), ctypes.byref(off),
+                                              ctypes.byref(n)), "moe_persistent_resident_info")
+    import numpy as np
+    raw = ws[off.value:off.value + 4 * n.value].cpu().numpy()
+    return raw.view(np.int32).copy()
+
+
+def moe_backward_ring(shape, placement, ex, dy, x, ring, pws, w1, w3, w2, topk_idx, topk_w, offsets, pull_src,
+                      slot_of, recv, dx, dlogits, dw1, dw3, dw2, xe, bws, ring_bytes=None, pws_bytes=None,
+                      bws_bytes=None, stream=None, check=True):
+    """ring = None: every token row is pulled again (nothing is read from the ring)."""
+    rb = 0 if ring is None else (ring.numel() if ring_bytes is None else ring_bytes)
+    rc = lib().moe_backward_ring(ctypes.byref(shape), ctypes.byref(placement), ctypes.byref(ex), _table(dy), _table(x),
+                                 None if ring is None else _p(ring), rb, _p(pws),
+                                 pws.numel() if pws_bytes is None else pws_bytes, _p(w1), _p(w3), _p(w2),
+                                 _p(topk_idx), _p(topk_w), _p(offsets), _p(pull_src), _p(slot_of), _table(recv),
+                                 _table(dx), _table(dlogits), _p(dw1), _p(dw3), _p(dw2), _p(xe), _p(bws),
+                                 bws.numel() if bws_bytes is None else bws_bytes, _stream(stream))
+    return _check(rc, "moe_backward_ring") if check else rc
 
 
 def moe_backward_prepare_mx(shape, placement, w1, w3, w2, w2t, w2t_scales, w13t, w13t_scales, stream=None,

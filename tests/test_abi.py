@@ -406,3 +406,64 @@ def test_fused_push_entries_reject_bad_arguments_before_launch():
     sc = moe.MXScales(FAKE, FAKE, FAKE)
     assert L.moe_expert_ffn_push(ctypes.byref(smx), ctypes.byref(p), None, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                  ctypes.byref(sc), FAKE, FAKE, tabp, FAKE, big, None) == -6
+
+
+def test_reverse_ring_layout_and_rejection():
+    """reverse_ring adds the per-pair recv address table to the persistent workspace (before
+    the trace region); the resident-chunk record lies inside the workspace proper; every
+    entry point other than the persistent ones rejects reverse_ring, and those take 0 or 1."""
+    L = moe.lib()
+    s, p = _shape(), _pl()
+    assert ctypes.sizeof(moe.Exec) == 32
+    ex0 = moe.Exec(128, 16, 0, 0, 0)
+    exr = moe.Exec(128, 16, 0, 0, 0, 1)
+    exrt = moe.Exec(128, 16, 0, 1, 0, 1)
+    base = moe.moe_persistent_workspace_bytes(s, p, ex0)
+    npairs = moe.moe_max_pairs(s, p)
+    with_table = moe.moe_persistent_workspace_bytes(s, p, exr)
+    assert with_table == base + (npairs * 8 + 255) // 256 * 256
+    off, cap, _ = moe.moe_persistent_trace_info(s, p, exrt)
+    assert off == with_table
+    roff, n = ctypes.c_size_t(), ctypes.c_int32()
+    assert L.moe_persistent_resident_info(ctypes.byref(s), ctypes.byref(p), ctypes.byref(roff), ctypes.byref(n)) == 0
+    max_mtiles = (npairs + 255) // 256 + 32
+    assert n.value == 4 * max_mtiles
+    assert roff.value % 4 == 0 and roff.value + 4 * n.value <= base
+    assert L.moe_persistent_resident_info(ctypes.byref(s), ctypes.byref(p), None, ctypes.byref(n)) == -1
+    tab = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    tabp = ctypes.cast(tab, ctypes.c_void_p)
+    big = 1 << 40
+    assert L.moe_layout(ctypes.byref(s), ctypes.byref(p), ctypes.byref(exr), tabp, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, FAKE, big, None) == -1
+    assert L.moe_forward(ctypes.byref(s), ctypes.byref(p), ctypes.byref(exr), tabp, tabp, FAKE, FAKE, FAKE, None,
+                         FAKE, None, FAKE, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    bad = moe.Exec(128, 0, 0, 0, 0, 2)
+    assert L.moe_forward_persistent(ctypes.byref(s), ctypes.byref(p), ctypes.byref(bad), tabp, tabp, FAKE, FAKE,
+                                    FAKE, FAKE, big, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big,
+                                    None) == -1
+
+
+def test_backward_ring_rejects_bad_arguments_before_launch():
+    L = moe.lib()
+    s, p = _shape(), _pl()
+    tab = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    tabp = ctypes.cast(tab, ctypes.c_void_p)
+    big = 1 << 40
+    ex = moe.Exec(128, 16, 0, 0, 0, 1)
+
+    def call(shape=s, exx=ex, ring=FAKE, pws=FAKE, pws_bytes=big, xe=FAKE, bws=FAKE, bws_bytes=big, dlog=tabp):
+        return L.moe_backward_ring(ctypes.byref(shape), ctypes.byref(p), ctypes.byref(exx), tabp, tabp, ring, big,
+                                   pws, pws_bytes, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, tabp, tabp, dlog,
+                                   FAKE, FAKE, FAKE, xe, bws, bws_bytes, None)
+    assert call(shape=_shape(dtype=moe.MOE_MXFP8)) == -6
+    assert call(shape=_shape(k=0)) == -1
+    assert call(pws=None) == -1
+    assert call(pws=FAKE + 16) == -2
+    assert call(pws_bytes=1024) == -3
+    assert call(bws_bytes=1024) == -3
+    assert call(bws=FAKE + 16) == -2
+    assert call(ring=FAKE + 16) == -2
+    assert call(xe=None) == -1
+    assert call(dlog=None) == -1
+    assert call(exx=moe.Exec(96, 16, 0, 0, 0, 1)) == -6            # chunk must divide 256
+    assert call(exx=moe.Exec(128, 16, 0, 0, 0, 2)) == -1

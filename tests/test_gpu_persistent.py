@@ -4,7 +4,9 @@ pipelines with L2-local hand-offs; fewer pipelines with agent-scope hand-offs an
 look-ahead when the ring is small), minibatch sizes, data-movement partition sizes and
 skewed load; the layout outputs against the oracle at full size; repeatability; a watchdog
 expiry forced from the host that ends the kernel cleanly with MOE_ETIMEOUT; and the event
-trace (every task recorded once, sane times)."""
+trace (every task recorded once, sane times); and the reverse ring: the same outputs, and at
+the end exactly each pipeline's first chunks (layout order) in the ring, in the slots the
+reversed walk puts them in, holding their token rows and h rows bit for bit."""
 import sys
 
 import numpy as np
@@ -48,6 +50,10 @@ def _reference(cfg, seed=0):
         torch.cuda.synchronize()
         ref = {"y": [t.clone() for t in P.y], "recv": [t.clone() for t in P.recv],
                "slot_of": P.slot_of.clone(), "offsets": P.offsets.clone()}
+        # the unfused path's h rows: the workspace region from moe_persistent_workspace_bytes on
+        hb = moe.moe_persistent_workspace_bytes(P.shape, P.placement, moe.Exec(cfg.minibatch, 0, 0, 0, 0))
+        n = int(P.offsets[cfg.E_local].item())
+        ref["h"] = P.ws[hb:hb + n * cfg.F * 2].clone().view(torch.bfloat16).view(n, cfg.F)
         _cache[key] = (inp, P, ref)
     return _cache[key]
 
@@ -184,3 +190,89 @@ def test_persistent_full_share(cfg):
     _assert_same(P, ref)
     cnt = lay["counts"][:cfg.E_local]
     _say(f"  N={lay['N']} hottest local/mean={cnt.max() / cnt.mean():.2f}")
+
+
+REVERSE_CASES = [
+    # (config, minibatch, comm_cus, ring_slots, ring MiB)
+    ("small", 128, 0, 0, 16),          # eight pipelines; the ring holds every chunk
+    ("small", 64, 16, 32, 16),         # eight pipelines of 4 slots, 64-row chunks: slots reused
+    ("mid-ragged", 128, 8, 24, 64),    # four pipelines (agent-scope hand-offs), slots reused
+    ("dsv3-slice", 128, 16, 16, 256),  # four pipelines of 4 slots
+    ("dsv3-slice-zipf", 128, 16, 0, 256),
+]
+
+
+def _expected_resident(P, mb, comm, ring_slots, ring_bytes, n_entries):
+    """Entry 4 m + h of the resident record after a reverse-ring launch: pipeline p walks its
+    row tiles [lo, hi) from hi - 1 down (chunk q = (hi - 1 - m) cpm + h of its walk, in slot
+    q mod S), and its last S chunks of that walk stay.  n_part and S follow the launch plan's
+    rule: the most pipelines (8, 4, 2, 1; more than one only on 256 CUs) whose S = slots / n
+    holds two row tiles with fewer movers than CUs, else one pipeline with every slot."""
+    import torch
+    cfg = P.cfg
+    cpm = 256 // mb
+    slot_bytes = moe.moe_ring_slot_bytes(P.shape, moe.Exec(mb, 0, 0, 0, 0))
+    slots = ring_bytes // slot_bytes
+    if ring_slots > 0:
+        slots = min(slots, ring_slots)
+    slots = min(slots, 65536)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    comm = comm or 16
+    n_part, S = 1, slots
+    for np_ in (8, 4, 2, 1):
+        if np_ > 1 and cus != 256:
+            continue
+        if slots // np_ >= 2 * cpm and max(comm // np_, 1) < cus // np_:
+            n_part, S = np_, slots // np_
+            break
+    counts = np.diff(P.offsets.cpu().numpy()[:cfg.E_local + 1])
+    n_mt = int(((counts + 255) // 256).sum())
+    exp = np.zeros(n_entries, np.int32)
+    for p in range(n_part):
+        lo, hi = n_mt * p // n_part, n_mt * (p + 1) // n_part
+        nch = (hi - lo) * cpm
+        for m in range(lo, hi):
+            for h in range(cpm):
+                q = (hi - 1 - m) * cpm + h
+                if q >= nch - S:
+                    exp[m * 4 + h] = 1 + p * S + q % S
+    return exp, slot_bytes
+
+
+@pytest.mark.parametrize("name,mb,comm,slots,mib", REVERSE_CASES)
+def test_reverse_ring(name, mb, comm, slots, mib):
+    import torch
+    cfg = CFG[name]
+    _say(f"[persistent-reverse] {name} minibatch={mb} comm_cus={comm} ring_slots={slots} ring={mib}MiB")
+    inp, P, ref = _reference(cfg)
+    # layout order first: nothing is recorded as held
+    assert _run_persistent(P, moe.Exec(mb, comm, slots, 0, WATCHDOG_US), mib) == 0
+    assert not moe.read_resident(P.ws, P.shape, P.placement).any()
+    st = _run_persistent(P, moe.Exec(mb, comm, slots, 0, WATCHDOG_US, 1), mib)
+    assert st == 0, moe.ERRORS.get(st, st)
+    _assert_same(P, ref)
+    res = moe.read_resident(P.ws, P.shape, P.placement)
+    exp, slot_bytes = _expected_resident(P, mb, comm, slots, mib << 20, res.size)
+    np.testing.assert_array_equal(res, exp)
+    # every held chunk's token rows and h rows, bit for bit
+    offs = P.offsets.cpu().numpy()
+    counts = np.diff(offs[:cfg.E_local + 1])
+    mtb = np.concatenate([[0], np.cumsum((counts + 255) // 256)])
+    ps = P.pull_src.cpu().numpy().reshape(-1, 2)
+    d, F = cfg.d, cfg.F
+    held = 0
+    for e in np.nonzero(res)[0]:
+        m, h = divmod(int(e), 4)
+        l = int(np.searchsorted(mtb, m, side="right") - 1)
+        row0 = int(offs[l] + (m - mtb[l]) * 256)
+        r0, r1 = row0 + h * mb, min(row0 + (h + 1) * mb, int(offs[l + 1]), row0 + 256)
+        if r1 <= r0:
+            continue
+        base = (int(res[e]) - 1) * slot_bytes
+        xs = P.ring[base:base + mb * d * 2].view(torch.bfloat16).view(mb, d)[:r1 - r0]
+        hs = P.ring[base + mb * d * 2:base + mb * (d + F) * 2].view(torch.bfloat16).view(mb, F)[:r1 - r0]
+        want = torch.stack([P.x[ps[s_, 0]][ps[s_, 1]] for s_ in range(r0, r1)])
+        assert torch.equal(xs, want), (m, h)
+        assert torch.equal(hs, ref["h"][r0:r1]), (m, h)
+        held += r1 - r0
+    _say(f"  rows held in the ring: {held} of {int(offs[cfg.E_local])}")
