@@ -389,6 +389,61 @@ def run_backward_mx(args, cfg, inp, P, stream, N):
     print(json.dumps(result), flush=True)
 
 
+def run_ring_backward(args, cfg, P, stream, N, ms_staged_backward):
+    """The backward after the persistent forward with the reverse ring (moe_backward_ring):
+    each step runs that forward, then the backward timed alone, once reading the token rows
+    the ring still holds in place and once pulling every row again (ring unused).  Also the
+    gather moe_backward would need first (moe_dispatch_pull of all N rows)."""
+    import torch
+    from mixture_experts_layer_histogram_amd import moe
+    ex = moe.Exec(args.minibatch or cfg.minibatch, args.comm_cus, 0, 0, 0, 1)
+    P.alloc_ring(args.ring_mib or cfg.ring_mib, ex)
+    out = {"ring_mib": args.ring_mib or cfg.ring_mib, "rows": N}
+    for use_ring in (True, False):
+        for _ in range(max(1, args.warmup // 2)):
+            P.forward_persistent(ex)
+            P.backward_ring(use_ring=use_ring)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(args.steps):
+            P.forward_persistent(ex)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            P.backward_ring(use_ring=use_ring)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        out["ms_with_ring" if use_ring else "ms_without_ring"] = float(np.mean(times))
+    if P.status() != 0:
+        raise SystemExit("device status after the ring backward")
+    res = moe.read_resident(P.ws, P.shape, P.placement)
+    offs = P.offsets.cpu().numpy()
+    counts = np.diff(offs[:cfg.E_local + 1])
+    mtb = np.concatenate([[0], np.cumsum((counts + 255) // 256)])
+    mb = ex.minibatch_rows
+    held = 0
+    for e in np.nonzero(res)[0]:
+        m, h = divmod(int(e), 4)
+        l = int(np.searchsorted(mtb, m, side="right") - 1)
+        row0 = int(offs[l] + (m - mtb[l]) * 256)
+        held += max(0, min(row0 + (h + 1) * mb, int(offs[l + 1]), row0 + 256) - (row0 + h * mb))
+    # what moe_backward needs on top after this forward: every token row gathered into xe
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        P.dispatch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gather_ms = e0.elapsed_time(e1) / args.steps
+    out.update({"rows_held": held, "rows_pulled_again": N - held,
+                "bytes_pulled_again": (N - held) * cfg.d * 2,
+                "moe_backward_plus_gather_ms": ms_staged_backward + gather_ms, "gather_all_rows_ms": gather_ms,
+                "path": "moe_forward_persistent with reverse_ring (not timed), then moe_backward_ring: expert "
+                        "outputs from recv, held token rows read in the ring, the rest pulled again"})
+    log(f"[bench] ring backward: {out}")
+    return out
+
+
 def run_backward(args, cfg, inp, P, stream, N):
     import torch
     if cfg.dtype == "mxfp8":
@@ -474,6 +529,7 @@ def run_backward(args, cfg, inp, P, stream, N):
             "push_reverse": (push_bytes + merge_bytes + gate_bytes) / (stage_ms["push_reverse"] * 1e-3) / PEAK_HBM,
         },
     }
+    result["ring_backward"] = run_ring_backward(args, cfg, P, stream, N, ms_fused)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU backward oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline_bwd(cfg, inp, dy, args.cpu_sample_ranks or 1)

@@ -95,7 +95,8 @@ inline WsLayout ws_layout(const moe_shape_t& s, int32_t E_local) {
 // of the dispatched token rows for the weight gradients.
 struct BwdLayout {
   size_t dO, dg, dh, h, dab, dX, dgp;
-  size_t rows, blks;                  // moe_backward_ring: token row addresses (per row, per 64-row block)
+  size_t rows, blks, held;            // moe_backward_ring: token row addresses (per row, per 64-row block),
+                                      // and whether each block is read in the ring
   size_t dOq, dOs, dabq, dabs, xeb;   // MXFP8 only (0 otherwise)
   size_t total;
 };
@@ -115,6 +116,7 @@ inline BwdLayout bwd_layout(const moe_shape_t& s, int32_t E_local) {
   const size_t mtiles = size_t((mp + kGemmBM - 1) / kGemmBM + E_local);
   b.rows = o; o = align256(o + n * 8);
   b.blks = o; o = align256(o + mtiles * 4 * 8);
+  b.held = o; o = align256(o + mtiles * 4 * 4);
   if (s.dtype == MOE_MXFP8) {
     b.dOq = o;  o = align256(o + n * d);
     b.dOs = o;  o = align256(o + n * (d / 32));

@@ -52,7 +52,8 @@ hipError_t launch_pull_reverse(const moe_shape_t& s, const void* const* dy, cons
 hipError_t launch_ring_rows(const moe_shape_t& s, int El, int max_mtiles, const void* const* x, const int32_t* pull_src,
                             const int32_t* offsets, const int32_t* mtile_base, const int32_t* ctrl,
                             const int32_t* resident, const void* ring, long long slot_bytes, int n_slots,
-                            int chunk_log2, void* xe, uint64_t* blk_src, uint64_t* row_src, int cus, hipStream_t st);
+                            int chunk_log2, void* xe, uint64_t* blk_src, int32_t* blk_held, uint64_t* row_src, int cus,
+                            hipStream_t st);
 hipError_t launch_gate_grad(const moe_shape_t& s, const float* topk_w, const int32_t* topk_idx, const int32_t* slot_of,
                             const float* dgp, float* const* dlogits, int cus, hipStream_t st);
 hipError_t launch_push_grad(const moe_shape_t& s, const char* dX, const float* dg, const int32_t* pull_src,
@@ -828,7 +829,7 @@ int moe_backward_ring(const moe_shape_t* s, const moe_placement_t* p, const moe_
                                      recv);
   if (e == hipSuccess)
     e = launch_ring_rows(*s, p->E_local, L.max_mtiles, x, pull_src, offsets, mtb, ctrl, resident, ring, slot_bytes,
-                         int(n_slots), blk_log2, xe, blk_src, row_src, cus, st);
+                         int(n_slots), blk_log2, xe, blk_src, reinterpret_cast<int32_t*>(b + B.held), row_src, cus, st);
   if (e != hipSuccess) return MOE_EHIP;
   if ((rc = ffn_backward_impl(s, p, nullptr, offsets, w1, w3, w2, pws, dw1, dw3, dw2, bws, pull_src, slot_of, recv,
                               stream, row_src, blk_src)))

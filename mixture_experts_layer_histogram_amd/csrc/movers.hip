@@ -53,44 +53,60 @@ __global__ __launch_bounds__(256) void dispatch_pull_kernel(RankPtrs<const char*
 }
 
 // The backward after a reverse-ring persistent forward: where each expert-side token row is.
-// For 64-row block b of row tile m (rows row0 + 64 b ..): if the ring slot that still holds
-// its chunk is recorded (resident[m * 4 + h] = 1 + slot, slot < n_slots), the block is read
-// in place there; else its rows are pulled again from the source buffers into xe at their
-// rows.  blk_src[m * 4 + b] gets the address of the block's first row and row_src[s] that
-// of every row s.  One 256-thread block per 64-row block; a wave per row for the pulls.
-__global__ __launch_bounds__(256) void ring_rows_kernel(RankPtrs<const char*> x, const int32_t* __restrict__ pull_src,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ mtile_base,
-                                                        const int32_t* __restrict__ ctrl,
-                                                        const int32_t* __restrict__ resident, const char* ring,
-                                                        long long slot_bytes, int n_slots, int chunk_log2, char* xe,
-                                                        int El, int max_mtiles, int row_bytes,
-                                                        uint64_t* __restrict__ blk_src, uint64_t* __restrict__ row_src) {
+// Block b of row tile m is its rows row0 + 64 b .. (at most 64).  If the ring slot that still
+// holds its chunk is recorded (resident[m * 4 + h] = 1 + slot, slot < n_slots), the block is
+// read in place there; else its rows are pulled again from the source buffers into xe at
+// their rows.  ring_blocks_kernel writes blk_src[m * 4 + b] (the block's first row) and a
+// held flag per block, one thread per block; ring_rows_kernel then gives every row s its
+// address row_src[s] and pulls the rows of blocks not held, one wave per row as the gather.
+__global__ __launch_bounds__(256) void ring_blocks_kernel(const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ mtile_base,
+                                                          const int32_t* __restrict__ ctrl,
+                                                          const int32_t* __restrict__ resident, const char* ring,
+                                                          long long slot_bytes, int n_slots, int chunk_log2,
+                                                          char* xe, int El, int max_mtiles, int row_bytes,
+                                                          uint64_t* __restrict__ blk_src, int32_t* __restrict__ blk_held) {
   const int n_mt = min(ctrl[kCtrlMTiles], max_mtiles);
-  const int lane = threadIdx.x & 63;
-  const int n16 = row_bytes >> 4;
-  for (int bid = blockIdx.x; bid < n_mt * 4; bid += gridDim.x) {
+  for (int bid = blockIdx.x * 256 + threadIdx.x; bid < n_mt * 4; bid += gridDim.x * 256) {
     const int m = bid >> 2, b = bid & 3;
     const int l = find_expert(mtile_base, El, m);
     const int row0 = offsets[l] + (m - mtile_base[l]) * kGemmBM;
     const int r_lo = b * 64;
-    const int nrows = min(64, min(kGemmBM, offsets[l + 1] - row0) - r_lo);
     const int h = r_lo >> chunk_log2;
     int rs = ring ? resident[m * 4 + h] : 0;
     if (rs < 1 || rs > n_slots) rs = 0;
     const char* base = rs ? ring + (long long)(rs - 1) * slot_bytes + (long long)(r_lo - (h << chunk_log2)) * row_bytes
                           : xe + (long long)(row0 + r_lo) * row_bytes;
-    if (threadIdx.x == 0) blk_src[bid] = reinterpret_cast<uint64_t>(base);
-    for (int r = threadIdx.x; r < nrows; r += 256)
-      row_src[row0 + r_lo + r] = reinterpret_cast<uint64_t>(base + (long long)r * row_bytes);
-    if (!rs) {
-      for (int r = threadIdx.x >> 6; r < nrows; r += 4) {
-        const int s = row0 + r_lo + r;
-        const int rk = pull_src[2 * int64_t(s)];
-        const int t = pull_src[2 * int64_t(s) + 1];
-        copy_row<16>(reinterpret_cast<const u32x4*>(x.p[rk] + int64_t(t) * row_bytes),
-                     reinterpret_cast<u32x4*>(xe + int64_t(s) * row_bytes), n16, lane);
-      }
+    blk_src[bid] = reinterpret_cast<uint64_t>(base);
+    blk_held[bid] = rs ? 1 : 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void ring_rows_kernel(RankPtrs<const char*> x, const int32_t* __restrict__ pull_src,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ mtile_base,
+                                                        const int32_t* __restrict__ ctrl,
+                                                        const uint64_t* __restrict__ blk_src,
+                                                        const int32_t* __restrict__ blk_held, char* xe, int El,
+                                                        int row_bytes, uint64_t* __restrict__ row_src) {
+  const int N = ctrl[kCtrlN];
+  const int lane = threadIdx.x & 63;
+  const int n16 = row_bytes >> 4;
+  const int nw = gridDim.x * 4;
+  for (int s = blockIdx.x * 4 + (threadIdx.x >> 6); s < N; s += nw) {
+    int lo = 0, hi = El - 1;                              // the expert whose rows hold s
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offsets[mid] <= s) lo = mid; else hi = mid - 1;
+    }
+    const int i = s - offsets[lo];
+    const int bid = (mtile_base[lo] + (i >> 8)) * 4 + ((i & 255) >> 6);
+    if (lane == 0) row_src[s] = blk_src[bid] + uint64_t(i & 63) * uint64_t(row_bytes);
+    if (!blk_held[bid]) {
+      const int rk = pull_src[2 * int64_t(s)];
+      const int t = pull_src[2 * int64_t(s) + 1];
+      copy_row<16>(reinterpret_cast<const u32x4*>(x.p[rk] + int64_t(t) * row_bytes),
+                   reinterpret_cast<u32x4*>(xe + int64_t(s) * row_bytes), n16, lane);
     }
   }
 }
@@ -245,15 +261,20 @@ hipError_t launch_dispatch(const moe_shape_t& s, const void* const* x, const int
   return hipGetLastError();
 }
 
+// blk_held: n_mt * 4 int32 of scratch
 hipError_t launch_ring_rows(const moe_shape_t& s, int El, int max_mtiles, const void* const* x, const int32_t* pull_src,
                             const int32_t* offsets, const int32_t* mtile_base, const int32_t* ctrl,
                             const int32_t* resident, const void* ring, long long slot_bytes, int n_slots,
-                            int chunk_log2, void* xe, uint64_t* blk_src, uint64_t* row_src, int cus, hipStream_t st) {
+                            int chunk_log2, void* xe, uint64_t* blk_src, int32_t* blk_held, uint64_t* row_src, int cus,
+                            hipStream_t st) {
   RankPtrs<const char*> xp{};
   for (int r = 0; r < s.R; ++r) xp.p[r] = static_cast<const char*>(x[r]);
+  const int row_bytes = s.d * 2;
+  hipLaunchKernelGGL(ring_blocks_kernel, dim3((max_mtiles * 4 + 255) / 256), dim3(256), 0, st, offsets, mtile_base,
+                     ctrl, resident, static_cast<const char*>(ring), slot_bytes, n_slots, chunk_log2,
+                     static_cast<char*>(xe), El, max_mtiles, row_bytes, blk_src, blk_held);
   hipLaunchKernelGGL(ring_rows_kernel, dim3(cus * kGatherBlocksPerCU), dim3(256), 0, st, xp, pull_src, offsets,
-                     mtile_base, ctrl, resident, static_cast<const char*>(ring), slot_bytes, n_slots, chunk_log2,
-                     static_cast<char*>(xe), El, max_mtiles, s.d * 2, blk_src, row_src);
+                     mtile_base, ctrl, blk_src, blk_held, static_cast<char*>(xe), El, row_bytes, row_src);
   return hipGetLastError();
 }
 
