@@ -89,6 +89,12 @@ __global__ __launch_bounds__(256) void ring_rows_kernel(RankPtrs<const char*> x,
                                                         const uint64_t* __restrict__ blk_src,
                                                         const int32_t* __restrict__ blk_held, char* xe, int El,
                                                         int row_bytes, uint64_t* __restrict__ row_src) {
+  __shared__ int32_t s_off[1025], s_mtb[1025];           // E_local <= E <= 1024
+  for (int i = threadIdx.x; i <= El; i += blockDim.x) {
+    s_off[i] = offsets[i];
+    s_mtb[i] = mtile_base[i];
+  }
+  __syncthreads();
   const int N = ctrl[kCtrlN];
   const int lane = threadIdx.x & 63;
   const int n16 = row_bytes >> 4;
@@ -97,10 +103,10 @@ __global__ __launch_bounds__(256) void ring_rows_kernel(RankPtrs<const char*> x,
     int lo = 0, hi = El - 1;                              // the expert whose rows hold s
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (offsets[mid] <= s) lo = mid; else hi = mid - 1;
+      if (s_off[mid] <= s) lo = mid; else hi = mid - 1;
     }
-    const int i = s - offsets[lo];
-    const int bid = (mtile_base[lo] + (i >> 8)) * 4 + ((i & 255) >> 6);
+    const int i = s - s_off[lo];
+    const int bid = (s_mtb[lo] + (i >> 8)) * 4 + ((i & 255) >> 6);
     if (lane == 0) row_src[s] = blk_src[bid] + uint64_t(i & 63) * uint64_t(row_bytes);
     if (!blk_held[bid]) {
       const int rk = pull_src[2 * int64_t(s)];
