@@ -285,7 +285,10 @@ int moe_forward(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t
  *   for MXFP8, moe_dispatch_pull (which quantises the rows) runs first and only the push is
  *   fused.  recv (local-pair entries) and y are bit-identical to moe_forward's.  Arguments
  *   as moe_forward without ye; xe and xe_scales are only used (and required) for MXFP8.
- *   A caller that needs xe for moe_backward runs moe_dispatch_pull (or moe_forward).
+ *   moe_backward reads xe and ye, which this call does not write: a caller that runs the
+ *   backward after it runs moe_forward instead, or moe_forward_persistent and then
+ *   moe_backward_ring (which reads the expert outputs from recv and the token rows from the
+ *   ring or the source buffers).
  */
 int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
                       const float* const* logits, const void* const* x, const void* w1, const void* w3,
