@@ -69,19 +69,18 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
   const int rows = io.rows;
 
   // fills: this wave's row groups g = wave*4 + i (rows g*8 + lrow) of the A and B tiles
-  const uint8_t* ap[4];
-  const uint8_t* bp[4];
+  // (32-bit offsets from a base shared by the wave: B rows of one wave are all W1 rows or all
+  // W3 rows, since rows 32 w .. 32 w + 31 are filled by wave w)
+  const uint8_t* abase = io.a;
+  const uint8_t* bbase = (MODE != 1 && (wave & 1)) ? b1 : b0;
+  uint32_t aoff[4], boff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (wave * 4 + i) * 8 + lrow;
     const int lch = (i & 1) ? lch_odd : lch_even;
-    ap[i] = io.a + size_t(min(row, rows - 1)) * K + lch * 16;
-    if (MODE != 1) {
-      const int n = min(c0 + (row >> 6) * 32 + (row & 31), Nout - 1);
-      bp[i] = (((row >> 5) & 1) ? b1 : b0) + size_t(n) * K + lch * 16;
-    } else {
-      bp[i] = b0 + size_t(min(c0 + row, Nout - 1)) * K + lch * 16;
-    }
+    aoff[i] = uint32_t(min(row, rows - 1)) * uint32_t(K) + lch * 16;
+    const int n = (MODE != 1) ? min(c0 + (row >> 6) * 32 + (row & 31), Nout - 1) : min(c0 + row, Nout - 1);
+    boff[i] = uint32_t(n) * uint32_t(K) + lch * 16;
   }
   // scale words: waves 0-3 fetch A rows 64*wave + lane, waves 4-7 B rows 64*(wave-4) + lane
   const uint8_t* sp;
@@ -108,8 +107,8 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int g = wave * 4 + i;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(ap[i] + koff), (lds_void_ptr)(sa + g * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bp[i] + koff), (lds_void_ptr)(sb + g * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(abase + (aoff[i] + koff)), (lds_void_ptr)(sa + g * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bbase + (boff[i] + koff)), (lds_void_ptr)(sb + g * 1024), 16, 0, 0);
     }
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(sp + ks * splane), (lds_void_ptr)(ss + wave * 256), 4, 0, 0);
   };
@@ -122,8 +121,54 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
 
+  // Software pipeline over K (two sub-steps of 64 per 128-value stage).  A fragment or scale
+  // register is reloaded as soon as the last MFMA that reads it has issued, so the reads of
+  // the next sub-step overlap the MFMAs of this one; each MFMA waits only for its own
+  // operands.  A stage's barrier sits between its two sub-steps: by then every wave has read
+  // the stage's second-sub-step fragments, so the fill two stages ahead goes into it, and the
+  // second sub-step's MFMAs cover the reads of the next stage's first fragments and of its
+  // scales.  A fill has one stage of MFMA work to land.  Per accumulator the MFMAs run in K
+  // order, so the result does not depend on this schedule.  Scales: lane (row r32, half hi)
+  // takes byte 2 st + hi of its row's word (block hi of sub-step st), read as one byte.
+  // Per-lane LDS byte offsets inside a stage: the two 16-byte chunks of a fragment of
+  // sub-step st (rows 32 apart share the XOR pattern, so a row block adds 4096), and the
+  // scale word of the lane's row (a row block adds 128).  They are passed
+  // through an opaque copy every K step, so the compiler keeps these ten values instead of
+  // hoisting every address of both stages out of the loop.
+  int offA[2][2], offB[2][2], offSA, offSB;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      offA[st][h] = swz_off(wm * 64 + r32, 4 * st + hi + 2 * h);
+      offB[st][h] = kGemmBM * kMxBK + swz_off(wn * 128 + r32, 4 * st + hi + 2 * h);
+    }
+  offSA = kMxDataBytes + 4 * (wm * 64 + r32);
+  offSB = kMxDataBytes + 4 * (kGemmBM + wn * 128 + r32);
+  auto ld2 = [&](const char* stg, int o0, int o1, int imm) -> i32x8 {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(stg + o0 + imm);
+    const u32x4 up = *reinterpret_cast<const u32x4*>(stg + o1 + imm);
+    return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(up[0]), int(up[1]), int(up[2]), int(up[3])};
+  };
+  auto frag_a = [&](const char* stg, int st, int m) { return ld2(stg, offA[st][0], offA[st][1], m * 4096); };
+  auto frag_b = [&](const char* stg, int st, int n) { return ld2(stg, offB[st][0], offB[st][1], n * 4096); };
+  // the scale word of a row (its four blocks), shifted so that byte 0 / byte 2 is block
+  // hi / 2 + hi: the MFMA's op_sel picks the sub-step's byte
+  auto scl_a = [&](const char* stg, int m) -> int {
+    return int(*reinterpret_cast<const uint32_t*>(stg + offSA + 128 * m) >> (8 * hi));
+  };
+  auto scl_b = [&](const char* stg, int n) -> int {
+    return int(*reinterpret_cast<const uint32_t*>(stg + offSB + 128 * n) >> (8 * hi));
+  };
+  auto mfma = [&](int st, int m, int n, const i32x8& a, const i32x8& b, int sa, int sb) {
+    if (st == 0) acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[m][n], 0, 0, 0, sa, 0, sb);
+    else acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[m][n], 0, 0, 2, sa, 2, sb);
+  };
+
   issue(0);
-  __builtin_amdgcn_s_waitcnt(0);
+  if (nk > 1) issue(1);
+  if (nk > 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");   // stage 0 landed (9 fills a stage)
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   // Row padding: a wave whose 32-row blocks lie wholly past the tile's valid rows skips
@@ -132,40 +177,125 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
   const int mv = __builtin_amdgcn_readfirstlane(min(2, max(0, (rows - wm * 64 + 31) >> 5)));
   auto kloop = [&](auto mvc) {
     constexpr int MV = decltype(mvc)::value;
-    for (int ks = 0; ks < nk; ++ks) {
-      if (ks + 1 < nk) issue(ks + 1);     // other stage: everyone finished reading it
-      const char* sa = smem + (ks & 1) * kMxStageBytes;
-      const char* sb = sa + kGemmBM * kMxBK;
-      const uint32_t* ss = reinterpret_cast<const uint32_t*>(sa + kMxDataBytes);
-      if constexpr (MV > 0) {
-        int wa[2], wb[4];
+    i32x8 fa[2], fb[4];
+    int sa[2], sb[4];                 // the stage's scale words; the next stage's are loaded in
+                                      // place after their last MFMA
+    if constexpr (MV > 0) {
 #pragma unroll
-        for (int m = 0; m < MV; ++m) wa[m] = int(ss[wm * 64 + m * 32 + r32] >> (8 * hi));
-#pragma unroll
-        for (int n = 0; n < 4; ++n) wb[n] = int(ss[kGemmBM + wn * 128 + n * 32 + r32] >> (8 * hi));
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          i32x8 fa[2], fb[4];
-#pragma unroll
-          for (int m = 0; m < MV; ++m) fa[m] = ld_frag(sa, wm * 64 + m * 32 + r32, 4 * st + hi);
-#pragma unroll
-          for (int n = 0; n < 4; ++n) fb[n] = ld_frag(sb, wn * 128 + n * 32 + r32, 4 * st + hi);
-#pragma unroll
-          for (int m = 0; m < MV; ++m)
-#pragma unroll
-            for (int n = 0; n < 4; ++n)
-              acc[m][n] = (st == 0)
-                  ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[m], fb[n], acc[m][n], 0, 0, 0, wa[m], 0, wb[n])
-                  : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[m], fb[n], acc[m][n], 0, 0, 2, wa[m], 2, wb[n]);
-        }
+      for (int m = 0; m < MV; ++m) {
+        fa[m] = frag_a(smem, 0, m);
+        sa[m] = scl_a(smem, m);
       }
-      __builtin_amdgcn_s_waitcnt(0);      // this wave's fills of the next stage landed
-      __syncthreads();                    // ... and everyone's
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        fb[n] = frag_b(smem, 0, n);
+        sb[n] = scl_b(smem, n);
+      }
+    }
+    for (int ks = 0; ks < nk; ++ks) {
+      const char* cs = smem + (ks & 1) * kMxStageBytes;
+      const char* ns = smem + ((ks + 1) & 1) * kMxStageBytes;   // after the last stage: stale, unused
+      asm volatile("" : "+v"(offA[0][0]), "+v"(offA[0][1]), "+v"(offA[1][0]), "+v"(offA[1][1]), "+v"(offB[0][0]),
+                   "+v"(offB[0][1]), "+v"(offB[1][0]), "+v"(offB[1][1]), "+v"(offSA), "+v"(offSB));
+      // sub-step 0 of stage ks; reload sub-step 1's fragments of stage ks
+      if constexpr (MV == 2) {
+        mfma(0, 0, 0, fa[0], fb[0], sa[0], sb[0]);
+        mfma(0, 0, 1, fa[0], fb[1], sa[0], sb[1]);
+        mfma(0, 0, 2, fa[0], fb[2], sa[0], sb[2]);
+        mfma(0, 0, 3, fa[0], fb[3], sa[0], sb[3]);
+        fa[0] = frag_a(cs, 1, 0);
+        mfma(0, 1, 0, fa[1], fb[0], sa[1], sb[0]);
+        fb[0] = frag_b(cs, 1, 0);
+        mfma(0, 1, 1, fa[1], fb[1], sa[1], sb[1]);
+        fb[1] = frag_b(cs, 1, 1);
+        mfma(0, 1, 2, fa[1], fb[2], sa[1], sb[2]);
+        fb[2] = frag_b(cs, 1, 2);
+        mfma(0, 1, 3, fa[1], fb[3], sa[1], sb[3]);
+        fb[3] = frag_b(cs, 1, 3);
+        fa[1] = frag_a(cs, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      } else if constexpr (MV == 1) {
+        mfma(0, 0, 0, fa[0], fb[0], sa[0], sb[0]);
+        fb[0] = frag_b(cs, 1, 0);
+        mfma(0, 0, 1, fa[0], fb[1], sa[0], sb[1]);
+        fb[1] = frag_b(cs, 1, 1);
+        mfma(0, 0, 2, fa[0], fb[2], sa[0], sb[2]);
+        fb[2] = frag_b(cs, 1, 2);
+        mfma(0, 0, 3, fa[0], fb[3], sa[0], sb[3]);
+        fb[3] = frag_b(cs, 1, 3);
+        fa[0] = frag_a(cs, 1, 0);
+      }
+      // this wave's fills of stage ks + 1 and its reads of stage ks are done; then everyone's.
+      // The accumulators pass through the statement, so no MFMA moves across the barrier.
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier"
+                   : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]), "+v"(acc[1][0]),
+                     "+v"(acc[1][1]), "+v"(acc[1][2]), "+v"(acc[1][3])
+                   :
+                   : "memory");
+      if (ks + 2 < nk) issue(ks + 2);     // into stage ks, which nobody reads any more
+      // sub-step 1 of stage ks; reload the next stage's sub-step-0 fragments and scale words
+      if constexpr (MV == 2) {
+        mfma(1, 0, 0, fa[0], fb[0], sa[0], sb[0]);
+        mfma(1, 0, 1, fa[0], fb[1], sa[0], sb[1]);
+        mfma(1, 0, 2, fa[0], fb[2], sa[0], sb[2]);
+        mfma(1, 0, 3, fa[0], fb[3], sa[0], sb[3]);
+        fa[0] = frag_a(ns, 0, 0);
+        sa[0] = scl_a(ns, 0);
+        mfma(1, 1, 0, fa[1], fb[0], sa[1], sb[0]);
+        fb[0] = frag_b(ns, 0, 0);
+        sb[0] = scl_b(ns, 0);
+        mfma(1, 1, 1, fa[1], fb[1], sa[1], sb[1]);
+        fb[1] = frag_b(ns, 0, 1);
+        sb[1] = scl_b(ns, 1);
+        mfma(1, 1, 2, fa[1], fb[2], sa[1], sb[2]);
+        fb[2] = frag_b(ns, 0, 2);
+        sb[2] = scl_b(ns, 2);
+        mfma(1, 1, 3, fa[1], fb[3], sa[1], sb[3]);
+        fb[3] = frag_b(ns, 0, 3);
+        sb[3] = scl_b(ns, 3);
+        fa[1] = frag_a(ns, 0, 1);
+        sa[1] = scl_a(ns, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      } else if constexpr (MV == 1) {
+        mfma(1, 0, 0, fa[0], fb[0], sa[0], sb[0]);
+        fb[0] = frag_b(ns, 0, 0);
+        sb[0] = scl_b(ns, 0);
+        mfma(1, 0, 1, fa[0], fb[1], sa[0], sb[1]);
+        fb[1] = frag_b(ns, 0, 1);
+        sb[1] = scl_b(ns, 1);
+        mfma(1, 0, 2, fa[0], fb[2], sa[0], sb[2]);
+        fb[2] = frag_b(ns, 0, 2);
+        sb[2] = scl_b(ns, 2);
+        mfma(1, 0, 3, fa[0], fb[3], sa[0], sb[3]);
+        fb[3] = frag_b(ns, 0, 3);
+        sb[3] = scl_b(ns, 3);
+        fa[0] = frag_a(ns, 0, 0);
+        sa[0] = scl_a(ns, 0);
+      }
     }
   };
   if (mv == 2) kloop(std::integral_constant<int, 2>{});
   else if (mv == 1) kloop(std::integral_constant<int, 1>{});
   else kloop(std::integral_constant<int, 0>{});
+  __syncthreads();                        // the epilogues reuse the stages
 
   if (MODE == 2) {
     // Backward epilogue, two passes of 128 tile rows: stage (a, b) as fp32 pairs in LDS
