@@ -79,7 +79,11 @@ __global__ __launch_bounds__(256) void pull_reverse_kernel(RankPtrs<const char*>
 // The MXFP8 variant: dO[s] = g dY[r][t] as bf16 (for the weight gradients) and as MX codes
 // of the fp32 products in blocks of 32 along d (for dh = dO W2; scales in the MXFP8 scale
 // layout of nmax rows), and dg[s] = <dY[r][t], ye[s]>.  One wave per row, every lane in the
-// quad shuffles of the quantiser (lanes past the row end carry zeros).
+// quad shuffles of the quantiser (lanes past the row end carry zeros).  The dO and code
+// stores are non-temporal: measured at the DeepSeek-V3 share the kernel takes 327 us with
+// them and 437 us with plain stores (the code stores account for almost all of the
+// difference); the bf16 kernel above and the forward's quantising gather are slower with
+// non-temporal stores, so they keep plain ones.
 __global__ __launch_bounds__(256) void pull_reverse_mx_kernel(RankPtrs<const char*> dy, const uint16_t* __restrict__ ye,
                                                               const int32_t* __restrict__ pull_src,
                                                               const int32_t* __restrict__ slot_of,
@@ -88,10 +92,10 @@ __global__ __launch_bounds__(256) void pull_reverse_mx_kernel(RankPtrs<const cha
                                                               uint16_t* __restrict__ dO, uint8_t* __restrict__ dOq,
                                                               uint8_t* __restrict__ dOs, float* __restrict__ dg, int T,
                                                               int k, int d, int64_t nmax) {
-  constexpr int UNROLL = 4;
+  constexpr int UNROLL = 8;
   const int N = ctrl[kCtrlN];
   const int lane = threadIdx.x & 63;
-  const int n16 = d >> 3;                 // 16-byte vectors of 8 bf16 (d % 32 == 0: whole quads)
+  const int n16 = d >> 3;                 // 16-byte vectors of 8 bf16 (d % 128 == 0: whole 16-lane groups)
   const int nw = gridDim.x * 4;
   for (int s = blockIdx.x * 4 + (threadIdx.x >> 6); s < N; s += nw) {
     const int r = pull_src[2 * int64_t(s)];
@@ -133,10 +137,12 @@ __global__ __launch_bounds__(256) void pull_reverse_mx_kernel(RankPtrs<const cha
         }
         uint32_t sc;
         const uint2 q = mx_quant8_f32(p0, p1, &sc);          // all lanes: quad shuffles inside
+        const uint32_t sw = mx_scale_word(sc);                // all lanes: row shifts inside
         if (i < n16) {
-          out[i] = o;
-          qout[i] = q;
-          if ((i & 3) == 0) dOs[mx_scale_index(nmax, s, i >> 2)] = uint8_t(sc);
+          __builtin_nontemporal_store(o, out + i);
+          __builtin_nontemporal_store(q.x, reinterpret_cast<uint32_t*>(qout + i));
+          __builtin_nontemporal_store(q.y, reinterpret_cast<uint32_t*>(qout + i) + 1);
+          if ((i & 15) == 0) *reinterpret_cast<uint32_t*>(dOs + mx_scale_index(nmax, s, i >> 2)) = sw;
         }
       }
     }
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(256) void gate_grad_kernel(const float* __restrict_
   }
 }
 
-constexpr int kPullRevBlocksPerCU = 4, kGateBlocksPerCU = 4;
+constexpr int kPullRevBlocksPerCU = 4, kPullRevMxBlocksPerCU = 8, kGateBlocksPerCU = 4;
 
 // o rows from ye, or (recv != null) from the forward's recv rows
 hipError_t launch_pull_reverse(const moe_shape_t& s, const void* const* dy, const uint16_t* ye,
@@ -210,7 +216,7 @@ hipError_t launch_pull_reverse_mx(const moe_shape_t& s, const void* const* dy, c
                                   int cus, hipStream_t st) {
   RankPtrs<const char*> dp{};
   for (int r = 0; r < s.R; ++r) dp.p[r] = static_cast<const char*>(dy[r]);
-  hipLaunchKernelGGL(pull_reverse_mx_kernel, dim3(cus * kPullRevBlocksPerCU), dim3(256), 0, st, dp, ye, pull_src,
+  hipLaunchKernelGGL(pull_reverse_mx_kernel, dim3(cus * kPullRevMxBlocksPerCU), dim3(256), 0, st, dp, ye, pull_src,
                      slot_of, topk_w, ctrl, dO, dOq, dOs, dg, s.T, s.k, s.d, nmax);
   return hipGetLastError();
 }

@@ -48,9 +48,20 @@ __device__ __forceinline__ uint32_t mx_pack4(float a, float b, float c, float d,
 }
 
 // Max over the 4 lanes of an aligned lane quad (the 4 lanes holding one 32-value block).
+// Two DPP quad permutations (lanes 1,0,3,2 then 2,3,0,1), no LDS round trip.
 __device__ __forceinline__ uint32_t quad_max(uint32_t m) {
-  m = max(m, uint32_t(__shfl_xor(int(m), 1)));
-  return max(m, uint32_t(__shfl_xor(int(m), 2)));
+  m = max(m, uint32_t(__builtin_amdgcn_update_dpp(int(m), int(m), 0xB1, 0xF, 0xF, false)));
+  return max(m, uint32_t(__builtin_amdgcn_update_dpp(int(m), int(m), 0x4E, 0xF, 0xF, false)));
+}
+
+// The 4 block scales of one K-tile plane, held by lanes 16c, +4, +8, +12 of a 16-lane DPP
+// row, as the little-endian 32-bit word the scale layout stores (valid in lanes 16c; row_shl
+// 4, 8 and 12 read lane l + 4, 8, 12 of the same row).
+__device__ __forceinline__ uint32_t mx_scale_word(uint32_t sc) {
+  const uint32_t s1 = uint32_t(__builtin_amdgcn_update_dpp(0, int(sc), 0x104, 0xF, 0xF, false));
+  const uint32_t s2 = uint32_t(__builtin_amdgcn_update_dpp(0, int(sc), 0x108, 0xF, 0xF, false));
+  const uint32_t s3 = uint32_t(__builtin_amdgcn_update_dpp(0, int(sc), 0x10C, 0xF, 0xF, false));
+  return (sc & 0xFFu) | ((s1 & 0xFFu) << 8) | ((s2 & 0xFFu) << 16) | ((s3 & 0xFFu) << 24);
 }
 
 // Quantise 8 consecutive bf16 values (one 16-byte vector) that form a quarter of a block

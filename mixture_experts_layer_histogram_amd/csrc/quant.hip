@@ -68,13 +68,10 @@ __global__ __launch_bounds__(256) void dispatch_pull_mx_kernel(RankPtrs<const ch
         const int i = base + u * 64 + lane;
         uint32_t sc;
         const uint2 q = mx_quant8_bf16(v[u], &sc);     // all lanes: quad shuffles inside
-        // the 4 block scales of one K-tile plane (lanes 16 c, +4, +8, +12) as one 4-byte word
-        const uint32_t sc1 = __shfl_down(sc, 4), sc2 = __shfl_down(sc, 8), sc3 = __shfl_down(sc, 12);
+        const uint32_t sw = mx_scale_word(sc);          // all lanes: row shifts inside
         if (i < n16) {
           dst[i] = q;
-          if ((i & 15) == 0)
-            *reinterpret_cast<uint32_t*>(xes + mx_scale_index(nmax, s, i >> 2)) =
-                (sc & 0xFFu) | ((sc1 & 0xFFu) << 8) | ((sc2 & 0xFFu) << 16) | ((sc3 & 0xFFu) << 24);
+          if ((i & 15) == 0) *reinterpret_cast<uint32_t*>(xes + mx_scale_index(nmax, s, i >> 2)) = sw;
         }
       }
     }
