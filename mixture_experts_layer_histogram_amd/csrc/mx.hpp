@@ -23,6 +23,16 @@ __device__ __forceinline__ int64_t mx_scale_index(int64_t rows, int64_t r, int b
   return 4 * (rows * (b >> 2) + r) + (b & 3);
 }
 
+// Rows per workgroup chunk of the quantising gather, which keeps the chunk's scale words in
+// LDS ([rows][d / 128 + 1] words) and writes each K-tile plane's words as one run.  Up to 32
+// rows, within 32 KiB.
+inline int mx_chunk_rows(int d) {
+  const int per_row = 4 * ((d >> 7) + 1);
+  int cr = 32;
+  while (cr > 4 && cr * per_row > 32768) cr >>= 1;
+  return cr;
+}
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Unbiased exponent of the block scale, from the fp32 bit pattern of the block's largest
