@@ -64,6 +64,10 @@ def parse():
                     help="comma-separated tokens per rank: time the forward at each (one JSON line per value; "
                          "the minibatch-size curve of the unfused path)"),
     ap.add_argument("--cpu-sample-ranks", type=int, default=0, help="0 = all ranks (the whole step)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure this GPU's ceilings instead of the layer: bf16 and MXFP8 MFMA issue rates, the "
+                         "direct global->LDS fill bandwidth missing and hitting the L2, a 1 GiB device copy; "
+                         "prints its own JSON line (add --sample-clocks for the clock during the MFMA runs)")
     ap.add_argument("--signal-latency", action="store_true",
                     help="time the inter-partition hand-off (flag round trip between workgroup pairs, same XCD and "
                          "across XCDs, L2-local and agent-scope) instead of the layer; prints its own JSON line")
@@ -565,6 +569,58 @@ def run_signal_latency(args):
                       "rounds": rounds, "pairs": 128, "higher_is_better": False, "results": res}), flush=True)
 
 
+def run_ceilings(args):
+    """The ceilings the kernels' rooflines are read against, measured on this GPU through
+    moe_ceiling_probe: MFMA issue rates with operands in registers (bf16 32x32x16, MXFP8
+    32x32x64), the tiles' direct global->LDS fill pattern from HBM-resident and from
+    L2-resident rows, and a 1 GiB device-to-device copy."""
+    import torch
+    from mixture_experts_layer_histogram_amd import moe
+    scratch = torch.empty(moe.moe_ceiling_probe_bytes(), dtype=torch.uint8, device="cuda:0")
+    src = torch.empty(4 << 30, dtype=torch.uint8, device="cuda:0")
+    src.view(torch.int32).random_(0, 1 << 30)
+    torch.cuda.synchronize()
+    out = {"metric": "hardware ceilings (one GPU)", "n_gpus": 1, "cus": torch.cuda.get_device_properties(0).multi_processor_count}
+    reps_mfma = 100000
+    for kind, name, peak in ((0, "mfma_bf16", 2500.0), (1, "mfma_mxfp8", 5000.0)):
+        rc, work, ms = moe.moe_ceiling_probe(kind, reps_mfma, None, 0, scratch)
+        tf = work / ms / 1e9
+        out[name] = {"TFLOP/s": tf, "frac_of_nameplate": tf / peak, "ms": ms, "reps_per_wave": reps_mfma}
+        log(f"[ceilings] {name}: {tf:.0f} TFLOP/s = {tf / peak:.3f} of {peak:.0f} ({ms:.1f} ms)")
+        if args.sample_clocks:
+            # back-to-back launches for a few seconds: the sustained rate and its clock
+            clk = ClockSampler(0.1)
+            tot_w = tot_ms = 0.0
+            with clk:
+                t_end = time.time() + 4.0
+                while time.time() < t_end:
+                    rc, work, ms = moe.moe_ceiling_probe(kind, reps_mfma, None, 0, scratch)
+                    tot_w += work
+                    tot_ms += ms
+            out[name]["sustained_TFLOP/s"] = tot_w / tot_ms / 1e9
+            out[name]["clock"] = clk.summary(peak * 1e12)
+            log(f"[ceilings] {name} sustained over 4 s: {tot_w / tot_ms / 1e9:.0f} TFLOP/s; clock {out[name]['clock']}")
+    for kind, name, reps in ((2, "lds_dma_fill_from_hbm", 2), (3, "lds_dma_fill_from_l2", 200)):
+        rc, work, ms = moe.moe_ceiling_probe(kind, reps, src, src.numel(), scratch)
+        tbs = work / ms / 1e9
+        out[name] = {"TB/s": tbs, "bytes_per_cu_cycle_at_2.4GHz": work / (ms * 1e-3) / out["cus"] / 2.4e9, "ms": ms,
+                     "bytes": work}
+        log(f"[ceilings] {name}: {tbs:.2f} TB/s")
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    dst.copy_(src[:1 << 30])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src[:1 << 30])
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    out["device_copy_1GiB"] = {"TB/s (read + write)": 2 * (1 << 30) / ms / 1e9, "ms": ms,
+                               "frac_of_8TBps": 2 * (1 << 30) / ms / 1e9 / 8.0}
+    log(f"[ceilings] 1 GiB copy: {out['device_copy_1GiB']['TB/s (read + write)']:.2f} TB/s")
+    print(json.dumps(out), flush=True)
+
+
 def run_sweep(args, cfg, P, stream):
     """Forward time against tokens handed to the layer at once.  The problem's buffers are
     sized for T tokens per rank; each point lowers the shape's T in place (every call reads
@@ -715,6 +771,9 @@ def main():
 
     if args.signal_latency:
         run_signal_latency(args)
+        return
+    if args.ceilings:
+        run_ceilings(args)
         return
     cfg = configs.CONFIGS[args.config]
     dev = torch.device("cuda:0")

@@ -623,6 +623,37 @@ int moe_signal_probe(int32_t cross_xcd, int32_t scope, int32_t payload_words, in
                      size_t scratch_bytes, float* us_per_round, int32_t* stale_words, int32_t* timeouts,
                      int32_t* pairs_same_xcd, void* stream);
 
+/*
+ * Hardware ceilings of this GPU -- a measurement utility, not an operation of the layer.  It
+ * measures what the expert GEMMs' rooflines are read against: the bf16 and MXFP8 MFMA issue
+ * rates [kucoin §02: the expert GEMMs in bf16 and MXFP8] and the bandwidth of the direct
+ * global->LDS fills that feed their tiles.
+ *   kind 0: v_mfma_f32_32x32x16_bf16, 8 independent accumulators per wave, operands in
+ *     registers, one 4-wave workgroup per CU, `reps` iterations of 8 MFMAs per wave.
+ *   kind 1: the same with v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands, unit scales).
+ *   kind 2: one 512-thread workgroup per CU streams its contiguous share of src (src_bytes /
+ *     CUs, rounded down to 64 KiB) `reps` times through two 64 KiB LDS stages with
+ *     global_load_lds_dwordx4 and one barrier per 64 KiB -- the tiles' fill pattern, missing
+ *     the L2.
+ *   kind 3: the same, each workgroup re-reading one 64 KiB window of the first 1 MiB of src
+ *     (window = workgroup mod 16), 16 * reps times: fills that hit the L2.
+ *   reps: [1, 1000000].  src, src_bytes: device memory, 16-byte aligned, read only (kinds 2
+ *     and 3; kind 2 needs 64 KiB per CU, kind 3 1 MiB; ignored by kinds 0 and 1).
+ *   scratch, scratch_bytes: caller-owned device memory, 256-byte aligned, at least
+ *     moe_ceiling_probe_bytes(); each thread writes one 32-bit word: kinds 0 and 1 the first
+ *     element of its first accumulator as fp32 (16 * reps, resp. 64 * reps: all operands are
+ *     1.0); kinds 2 and 3 the int32 word at its index in the last LDS stage filled (thread t
+ *     of workgroup b at index b * 512 + t; its word of src is the word t of the last 64 KiB
+ *     round that workgroup read).
+ * Outputs (host): work = FLOP (kinds 0, 1) or bytes read (kinds 2, 3) of the timed launch;
+ * ms = its duration by HIP events on `stream`.  One untimed launch runs first.  Synchronous.
+ * Errors: MOE_EINVAL (kind outside 0..3, reps out of range, null pointer), MOE_EALIGN,
+ * MOE_ENOSPC (scratch or src too small), MOE_EHIP.
+ */
+size_t moe_ceiling_probe_bytes(void);
+int moe_ceiling_probe(int32_t kind, int32_t reps, const void* src, size_t src_bytes, void* scratch,
+                      size_t scratch_bytes, double* work, float* ms, void* stream);
+
 /* Syncs `stream` and returns the device status word (0, MOE_EINVAL or MOE_ETIMEOUT). */
 int moe_read_status(const void* ws, void* stream);
 

@@ -30,7 +30,8 @@ EXPORTS = ["moe_max_pairs", "moe_workspace_bytes", "moe_mx_quantize", "moe_layou
            "moe_combine_pull_reverse", "moe_expert_ffn_backward",
            "moe_dispatch_push_reverse", "moe_backward", "moe_backward_ring", "moe_backward_prepare_mx",
            "moe_backward_mx",
-           "moe_signal_probe_bytes", "moe_signal_probe", "moe_read_status", "moe_strerror", "moe_version"]
+           "moe_signal_probe_bytes", "moe_signal_probe", "moe_ceiling_probe_bytes", "moe_ceiling_probe",
+           "moe_read_status", "moe_strerror", "moe_version"]
 
 
 class MoEError(RuntimeError):
@@ -116,6 +117,9 @@ def lib() -> ctypes.CDLL:
         L.moe_signal_probe_bytes.argtypes = [I32]
         L.moe_signal_probe_bytes.restype = SZ
         L.moe_signal_probe.argtypes = [I32, I32, I32, I32, VP, SZ, VP, VP, VP, VP, VP]
+        L.moe_ceiling_probe_bytes.argtypes = []
+        L.moe_ceiling_probe_bytes.restype = SZ
+        L.moe_ceiling_probe.argtypes = [I32, I32, VP, SZ, VP, SZ, VP, VP, VP]
         L.moe_read_status.argtypes = [VP, VP]
         L.moe_strerror.argtypes = [I32]
         L.moe_strerror.restype = ctypes.c_char_p
@@ -125,7 +129,7 @@ def lib() -> ctypes.CDLL:
                   "moe_forward", "moe_forward_persistent", "moe_persistent_dispatch_ffn_combine",
                   "moe_forward_persistent_noalloc",
                   "moe_combine_pull_reverse", "moe_expert_ffn_backward", "moe_dispatch_push_reverse", "moe_backward", "moe_backward_prepare_mx",
-                  "moe_backward_ring", "moe_backward_mx", "moe_read_status"):
+                  "moe_backward_ring", "moe_backward_mx", "moe_signal_probe", "moe_ceiling_probe", "moe_read_status"):
             getattr(L, f).restype = I32
         _lib = L
     return _lib
@@ -439,3 +443,19 @@ def moe_signal_probe(cross_xcd: int, scope: int, payload_words: int, rounds: int
     if check:
         _check(rc, "moe_signal_probe")
     return rc, float(us.value), int(stale.value), int(tmo.value), int(same.value)
+
+
+def moe_ceiling_probe_bytes() -> int:
+    return int(lib().moe_ceiling_probe_bytes())
+
+
+def moe_ceiling_probe(kind: int, reps: int, src, src_bytes: int, scratch, scratch_bytes=None, stream=None, check=True):
+    """Returns (rc, work, ms): FLOP (kinds 0, 1) or bytes (kinds 2, 3) of the timed launch and its time."""
+    work = ctypes.c_double(0.0)
+    ms = ctypes.c_float(0.0)
+    rc = lib().moe_ceiling_probe(int(kind), int(reps), _p(src), int(src_bytes), _p(scratch),
+                                 scratch.numel() * scratch.element_size() if scratch_bytes is None else scratch_bytes,
+                                 ctypes.byref(work), ctypes.byref(ms), _stream(stream))
+    if check:
+        _check(rc, "moe_ceiling_probe")
+    return rc, float(work.value), float(ms.value)

@@ -372,6 +372,23 @@ def test_signal_probe_sizes_and_rejects_bad_arguments_before_launch():
     assert call(nbytes=need - 1) == -3
 
 
+def test_ceiling_probe_rejects_bad_arguments_before_launch():
+    L = moe.lib()
+    work, ms = ctypes.c_double(), ctypes.c_float()
+
+    def call(kind=0, reps=10, src=FAKE, nbytes=1 << 30, scratch=FAKE, sbytes=1 << 20, w=ctypes.byref(work),
+             t=ctypes.byref(ms)):
+        return L.moe_ceiling_probe(kind, reps, src, nbytes, scratch, sbytes, w, t, None)
+    assert call(kind=-1) == -1
+    assert call(kind=4) == -1
+    assert call(reps=0) == -1
+    assert call(reps=1000001) == -1
+    assert call(scratch=None) == -1
+    assert call(w=None) == -1
+    assert call(t=None) == -1
+    assert call(scratch=FAKE + 64) == -2
+
+
 def test_fused_push_entries_reject_bad_arguments_before_launch():
     s, p = _shape(), _pl()
     L = moe.lib()
