@@ -43,8 +43,8 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict
 // rows at a time and keeps their scale words in LDS (row stride nq + 1 words, so the
 // column-wise reads below hit distinct banks); once all its waves are done it writes each
 // K-tile plane's cr words as one contiguous run.  Written row by row, every 4-byte scale
-// word was a partial write to its own line (56 lines per row at d = 7168): 133 us
-// against 116 us without the scale stores at the DeepSeek-V3 share.
+// word was a partial write to its own line (56 lines per row at d = 7168).  Measured at the
+// DeepSeek-V3 share: 133 us that way, 126 us this way, 116 us with no scale stores at all.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void dispatch_pull_mx_kernel(RankPtrs<const char*> x,
                                                                const int32_t* __restrict__ pull_src,
                                                                const int32_t* __restrict__ ctrl,
