@@ -889,6 +889,30 @@ def main():
                    "ms_per_step": cms, "tokens_per_s": cfg.R * cfg.T / cfg.G / (cms * 1e-3), "ffn_ms": cffn,
                    "ffn_frac_bf16_peak": 6.0 * cfg.d * cfg.F * N / (cffn * 1e-3) / PEAK_BF16_FLOPS}
         log(f"[bench] fused multi-kernel path for comparison: {cms:.3f} ms/step (FFN {cffn:.3f} ms)")
+        # the pull and the push as kernels of their own (the unfused path's movers) on the same
+        # inputs: the HBM fractions of gather and combine by themselves
+        P.dispatch()
+        P.ffn()
+        P.combine()
+        torch.cuda.synchronize()
+        mev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            mev[i][0].record(stream)
+            P.dispatch()
+            mev[i][1].record(stream)
+            P.ffn()
+            mev[i][2].record(stream)
+            P.combine()
+            mev[i][3].record(stream)
+        torch.cuda.synchronize()
+        row_b = cfg.d * 2
+        g_ms = float(np.mean([mev[i][0].elapsed_time(mev[i][1]) for i in range(args.steps)]))
+        c_ms = float(np.mean([mev[i][2].elapsed_time(mev[i][3]) for i in range(args.steps)]))
+        compare["standalone_movers"] = {
+            "gather_ms": g_ms, "gather_hbm_frac": (2.0 * N * row_b + N * 8) / (g_ms * 1e-3) / PEAK_HBM,
+            "push+merge_ms": c_ms,
+            "push+merge_hbm_frac": (2.0 * N * row_b + N * row_b + cfg.R * cfg.T * row_b) / (c_ms * 1e-3) / PEAK_HBM}
+        log(f"[bench] standalone movers: {compare['standalone_movers']}")
     graph = None
     if args.graph:
         side = torch.cuda.Stream()
