@@ -91,9 +91,15 @@ def parse():
                     help="time the fused multi-kernel path (layout, FFN with the pull and push fused in, merge)")
     ap.add_argument("--no-compare", action="store_true",
                     help="persistent path: skip timing the fused multi-kernel path beside it")
-    ap.add_argument("--comm-cus", type=int, default=16, help="persistent path: data-movement workgroups")
+    ap.add_argument("--comm-cus", type=int, default=8,
+                    help="persistent path: data-movement workgroups (8, one per XCD pipeline: the best in the sweep with the reverse ring, whose movers only gather)")
     ap.add_argument("--minibatch", type=int, default=0, help="persistent path: rows per chunk (64, 128, 256)")
     ap.add_argument("--ring-mib", type=int, default=0, help="persistent path: ring size (default: the config's)")
+    ap.add_argument("--ring-order", choices=("reverse", "forward"), default="reverse",
+                    help="persistent path: 'reverse' (default) walks each pipeline's row tiles from last to first, "
+                         "the down GEMM stores each output row straight to recv and the ring keeps the activations "
+                         "the backward reads; 'forward' walks them in layout order and the data-movement "
+                         "workgroups push the output rows from the ring to recv")
     ap.add_argument("--trace", action="store_true",
                     help="persistent path: after the timed steps, one traced call; per-role busy and wait summary")
     ap.add_argument("--trace-out", default="",
@@ -660,7 +666,8 @@ def run_sweep(args, cfg, P, stream):
 
 def persistent_exec(args, cfg, comm=None, mb=None, trace=0):
     from mixture_experts_layer_histogram_amd import moe
-    return moe.Exec(mb or args.minibatch or cfg.minibatch, args.comm_cus if comm is None else comm, 0, trace, 0)
+    return moe.Exec(mb or args.minibatch or cfg.minibatch, args.comm_cus if comm is None else comm, 0, trace, 0,
+                    1 if getattr(args, "ring_order", "reverse") == "reverse" else 0)
 
 
 def trace_summary(ev, tpu, grid):
@@ -1000,9 +1007,14 @@ def main():
         "data": "synthetic (seeded N(0,1) tokens, fan-in scaled random expert weights, router logits x@W_r)",
         "config": {"workload": cfg.name, "R": cfg.R, "T": cfg.T, "d": cfg.d, "E": cfg.E,
                    "E_local": cfg.E_local, "k": cfg.k, "F": cfg.F, "local_pairs": N, "load": load,
-                   "path": ("persistent megakernel (layout; one persistent kernel whose data-movement "
-                            "workgroups pull token rows into the ring and push finished rows to recv while its "
-                            "compute workgroups run the grouped SwiGLU GEMMs; merge)" if args.persistent else
+                   "path": (("persistent megakernel, reverse ring (layout; one persistent kernel whose "
+                             "data-movement workgroups pull token rows into the ring while its compute workgroups run "
+                             "the grouped SwiGLU GEMMs, each pipeline walking its row tiles from last to first; the "
+                             "down GEMM stores every output row straight to recv and the ring keeps the token and h "
+                             "rows of its last chunks for the backward; merge)" if args.ring_order == "reverse" else
+                             "persistent megakernel (layout; one persistent kernel whose data-movement "
+                             "workgroups pull token rows into the ring and push finished rows to recv while its "
+                             "compute workgroups run the grouped SwiGLU GEMMs; merge)") if args.persistent else
                             "unfused (layout, dispatch, ffn writing ye, push + merge kernels on one stream)"
                             if args.unfused else
                             ("fused push (layout, dispatch, ffn whose down GEMM writes each row to its recv slot, "
@@ -1026,9 +1038,10 @@ def main():
     if args.persistent:
         pex = persistent_exec(args, cfg)
         result["config"].update({"ring_mib": args.ring_mib or cfg.ring_mib, "minibatch": pex.minibatch_rows,
-                                 "comm_cus": pex.comm_cus})
-        result["roofline"]["kernel"] = ("persistent kernel (pull into the ring, gate/up+SwiGLU and down GEMMs, "
-                                        "push), FLOPs of the GEMMs")
+                                 "comm_cus": pex.comm_cus, "ring_order": args.ring_order})
+        result["roofline"]["kernel"] = ("persistent kernel (pull into the ring, gate/up+SwiGLU and down GEMMs, push"
+                                        + (" by the down GEMM's row stores" if args.ring_order == "reverse" else "")
+                                        + "), FLOPs of the GEMMs")
         # the movers' algorithmic bytes inside the persistent kernel: rows in and out of the ring
         result["stages_hbm_frac"]["dispatch+combine in the persistent kernel"] = (
             (gather_bytes + push_bytes) / t_ffn / PEAK_HBM)
