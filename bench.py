@@ -38,11 +38,15 @@ CSRC = os.path.join(ROOT, "mixture_experts_layer_histogram_amd", "csrc")
 # per workload: committed traffic record, GEMM kernel name, and the sources the kernels are built from
 TRAFFIC = {
     "dsv3/persistent": ("traffic_persistent_dsv3_bf16.json", "moe_persistent_kernel",
-                        ("persistent.hip", "persist_sched.hpp", "gemm_tile.hpp", "common.hpp")),
+                        ("persistent.hip", "persist_sched.hpp", "gemm_tile.hpp", "gemm_mx_tile.hpp", "mx.hpp",
+                         "common.hpp")),
+    "dsv3_mx/persistent": ("traffic_persistent_dsv3_mxfp8.json", "moe_persistent_kernel",
+                           ("persistent.hip", "persist_sched.hpp", "gemm_tile.hpp", "gemm_mx_tile.hpp", "mx.hpp",
+                            "common.hpp")),
     "dsv3": ("traffic_grouped_gemm_dsv3_bf16.json", "grouped_gemm_bf16_kernel",
              ("gemm.hip", "gemm_tile.hpp", "common.hpp")),
     "dsv3_mx": ("traffic_grouped_gemm_dsv3_mxfp8.json", "grouped_gemm_mx_kernel",
-                ("gemm_mx.hip", "gemm_tile.hpp", "mx.hpp", "common.hpp")),
+                ("gemm_mx.hip", "gemm_mx_tile.hpp", "gemm_tile.hpp", "mx.hpp", "common.hpp")),
 }
 
 
@@ -758,7 +762,9 @@ def run_persistent_sweep(args, cfg, P, stream):
             ms = e0.elapsed_time(e1) / args.steps
             line = {"metric": "persistent kernel ms (dispatch + FFN + combine)", "workload": cfg.name,
                     "comm_cus": comm, "minibatch": mb, "ring_mib": args.ring_mib or cfg.ring_mib, "ms": ms,
-                    "ffn_tflops": flops / (ms * 1e-3) / 1e12, "frac_bf16_peak": flops / (ms * 1e-3) / PEAK_BF16_FLOPS}
+                    "ring_order": args.ring_order, "ffn_tflops": flops / (ms * 1e-3) / 1e12,
+                    ("frac_fp8_peak" if cfg.dtype == "mxfp8" else "frac_bf16_peak"):
+                        flops / (ms * 1e-3) / (PEAK_FP8_FLOPS if cfg.dtype == "mxfp8" else PEAK_BF16_FLOPS)}
             print(json.dumps(line), flush=True)
             log(f"[sweep-persistent] comm={comm} mb={mb}: {ms:.3f} ms")
 
@@ -793,7 +799,7 @@ def main():
 
     # the timed path: the persistent megakernel for bf16 (every step of the share, the CU
     # partition and the ring included) unless another is asked for; the fused multi-kernel path
-    # for the other dtypes (the persistent kernel is bf16 only)
+    # for the other dtypes unless --persistent (the persistent kernel takes bf16 and MXFP8)
     if args.unfused:
         path = "unfused"
     elif args.fused:
@@ -876,6 +882,9 @@ def main():
     if args.persistent and not args.no_compare:
         # context: the fused multi-kernel path on the same inputs (pull fused into the gate/up
         # GEMM, push into the down GEMM; no CU partition, no ring, h staged at worst-case size)
+        # (MXFP8: the gather quantises the rows, so it stays a kernel of its own; "FFN" is then
+        # the gather and the two GEMMs)
+        mx = cfg.dtype == "mxfp8"
         P.forward_fused()
         torch.cuda.synchronize()
         cev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -883,7 +892,11 @@ def main():
             cev[i][0].record(stream)
             P.layout()
             cev[i][1].record(stream)
-            P.ffn_push(pull=True)
+            if mx:
+                P.dispatch()
+                P.ffn_push()
+            else:
+                P.ffn_push(pull=True)
             cev[i][2].record(stream)
             P.merge()
             cev[i][3].record(stream)
@@ -891,10 +904,14 @@ def main():
         cst = [cev[i][0].elapsed_time(cev[i][3]) for i in range(args.steps)]
         cffn = float(np.mean([cev[i][1].elapsed_time(cev[i][2]) for i in range(args.steps)]))
         cms = float(np.mean(cst))
-        compare = {"path": "fused multi-kernel (layout, FFN with the pull fused into the gate/up GEMM and the push "
-                           "into the down GEMM, merge; no CU partition, no ring, h staged at worst-case size)",
+        cpeak = PEAK_FP8_FLOPS if mx else PEAK_BF16_FLOPS
+        compare = {"path": ("fused multi-kernel (layout, quantising gather, FFN with the push fused into the down "
+                            "GEMM, merge; no CU partition, no ring, xe and h staged at worst-case size)" if mx else
+                            "fused multi-kernel (layout, FFN with the pull fused into the gate/up GEMM and the push "
+                            "into the down GEMM, merge; no CU partition, no ring, h staged at worst-case size)"),
                    "ms_per_step": cms, "tokens_per_s": cfg.R * cfg.T / cfg.G / (cms * 1e-3), "ffn_ms": cffn,
-                   "ffn_frac_bf16_peak": 6.0 * cfg.d * cfg.F * N / (cffn * 1e-3) / PEAK_BF16_FLOPS}
+                   ("gather_ffn_frac_fp8_peak" if mx else "ffn_frac_bf16_peak"):
+                       6.0 * cfg.d * cfg.F * N / (cffn * 1e-3) / cpeak}
         log(f"[bench] fused multi-kernel path for comparison: {cms:.3f} ms/step (FFN {cffn:.3f} ms)")
         # the pull and the push as kernels of their own (the unfused path's movers) on the same
         # inputs: the HBM fractions of gather and combine by themselves
@@ -915,8 +932,9 @@ def main():
         row_b = cfg.d * 2
         g_ms = float(np.mean([mev[i][0].elapsed_time(mev[i][1]) for i in range(args.steps)]))
         c_ms = float(np.mean([mev[i][2].elapsed_time(mev[i][3]) for i in range(args.steps)]))
+        g_bytes = N * row_b + N * (cfg.d + cfg.d // 32) + N * 8 if mx else 2.0 * N * row_b + N * 8
         compare["standalone_movers"] = {
-            "gather_ms": g_ms, "gather_hbm_frac": (2.0 * N * row_b + N * 8) / (g_ms * 1e-3) / PEAK_HBM,
+            "gather_ms": g_ms, "gather_hbm_frac": g_bytes / (g_ms * 1e-3) / PEAK_HBM,
             "push+merge_ms": c_ms,
             "push+merge_hbm_frac": (2.0 * N * row_b + N * row_b + cfg.R * cfg.T * row_b) / (c_ms * 1e-3) / PEAK_HBM}
         log(f"[bench] standalone movers: {compare['standalone_movers']}")
@@ -1039,8 +1057,17 @@ def main():
         pex = persistent_exec(args, cfg)
         result["config"].update({"ring_mib": args.ring_mib or cfg.ring_mib, "minibatch": pex.minibatch_rows,
                                  "comm_cus": pex.comm_cus, "ring_order": args.ring_order})
+        if cfg.dtype == "mxfp8":
+            result["config"]["path"] = (
+                "persistent megakernel, MXFP8 (layout; one persistent kernel whose data-movement workgroups "
+                "quantise token rows into the ring slots (E4M3 codes and E8M0 scale words) while its compute "
+                "workgroups run the grouped SwiGLU GEMMs on the slots, writing h's codes and scales back into "
+                "the slot; the down GEMM stores every output row straight to recv; "
+                + ("each pipeline walks its row tiles from last to first; " if args.ring_order == "reverse" else "")
+                + "merge)")
         result["roofline"]["kernel"] = ("persistent kernel (pull into the ring, gate/up+SwiGLU and down GEMMs, push"
-                                        + (" by the down GEMM's row stores" if args.ring_order == "reverse" else "")
+                                        + (" by the down GEMM's row stores" if args.ring_order == "reverse"
+                                           or cfg.dtype == "mxfp8" else "")
                                         + "), FLOPs of the GEMMs")
         # the movers' algorithmic bytes inside the persistent kernel: rows in and out of the ring
         result["stages_hbm_frac"]["dispatch+combine in the persistent kernel"] = (
@@ -1049,9 +1076,9 @@ def main():
             tex = persistent_exec(args, cfg, trace=1)
             wsb = moe.moe_persistent_workspace_bytes(P.shape, P.placement, tex)
             tws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
-            moe.moe_forward_persistent(P.shape, P.placement, tex, P.logits, P.x, P.w1, P.w3, P.w2, P.ring,
+            moe.moe_forward_persistent(P.shape, P.placement, tex, P.logits, P.x, *P.weights(), P.ring,
                                        P.recv, P.y, P.topk_idx, P.topk_w, P.counts, P.offsets, P.pull_src,
-                                       P.slot_of, tws)
+                                       P.slot_of, tws, w_scales=P.w_scales)
             if moe.moe_read_status(tws) != 0:
                 raise SystemExit("device status after the traced call")
             ev, tpu = moe.read_trace(tws, P.shape, P.placement, tex)

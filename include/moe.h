@@ -112,8 +112,9 @@ typedef struct {
                                (the down GEMM stores the outputs straight to recv), so that
                                at the end the ring holds the activations of the first chunks,
                                which moe_backward_ring reads in place; 0 = layout order, the
-                               outputs overwrite the token rows in the ring.  Every other
-                               entry point requires 0 (else MOE_EINVAL) */
+                               outputs overwrite the token rows in the ring (in MXFP8 they always
+                               go straight to recv).  Every other entry point requires 0 (else
+                               MOE_EINVAL) */
 } moe_exec_t;
 
 /* Limits checked by every call: 1 <= k <= 16, k <= E <= 1024, 1 <= E_local <= E. */
@@ -305,11 +306,18 @@ int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_
  * fixed-size ring buffer whose slots are reused right after combine, so the combine of one
  * batch overlaps the dispatch of the next; qubstore, ring buffer and megakernel
  * paragraphs: no CPU in the loop, no worst-case buffers].
- * Same inputs and outputs as moe_forward (bf16 only), plus:
+ * Same inputs and outputs as moe_forward (bf16 or MXFP8), plus:
+ *   w_scales: MXFP8 only (else ignored): the weights' block scales, as for moe_forward
+ *     (the weights are E4M3 codes, moe_mx_quantize).  [kucoin §02: MXFP8 quantisation fused
+ *     into the dispatch, grouped-GEMM and SwiGLU data paths.]  The gather quantises each
+ *     token row on its way into the ring, the gate/up GEMM's epilogue quantises h into the
+ *     ring, and the down GEMM stores each bf16 output row straight to recv (a per-pair
+ *     address table in the workspace); the push then only frees the slot.
  *   ring, ring_bytes: caller-owned device buffer, 256-byte aligned, of at least
  *     256 / minibatch_rows slots of moe_ring_slot_bytes() each.  A slot holds one
  *     minibatch of token rows (overwritten in place by their expert outputs) and their h
- *     rows.  Fewer slots mean more back-pressure, never a different result.
+ *     rows; in MXFP8 the token rows' codes and scale words, then h's codes and scale words.
+ *     Fewer slots mean more back-pressure, never a different result.
  *   ws: at least moe_persistent_workspace_bytes() bytes (no worst-case row staging).
  * Launch sequence on `stream`: the layout kernels, a preparation kernel (clears the control
  * words, builds the per-pipeline task tables), the persistent kernel (one 512-thread
@@ -328,7 +336,7 @@ int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_
  * moe_read_status() returns MOE_ETIMEOUT.  If a pipeline's work was left undone (no
  * workgroup reached it) moe_read_status() returns MOE_EINCOMPLETE.
  * recv (local-pair entries) and y are bit-identical to moe_forward's for the same inputs
- * (same tile arithmetic, same merge order).
+ * (same quantisation and tile arithmetic, same merge order).
  * With ex->trace = 1 the kernel records one moe_trace_event_t per task and per workgroup
  * start / end into the workspace (moe_persistent_trace_info).
  * With ex->reverse_ring = 1 [qubstore, ring buffer paragraph: in the forward the ring is
@@ -340,15 +348,17 @@ int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_
  * ring holds each pipeline's first chunks in layout order (all of them when the ring is large
  * enough), and the workspace records which slot holds which chunk, for moe_backward_ring.
  * Results are bit-identical to the layout order.
- * Errors: MOE_EUNSUP for a non-bf16 dtype, minibatch_rows not in {64, 128, 256}, or a
- * device where one workgroup per CU cannot be resident; MOE_ENOSPC for a ring below one
- * 256-row tile or a small workspace; MOE_EINVAL when comm_cus leaves no CU for compute.
+ * Errors: MOE_EUNSUP for an fp32 dtype, minibatch_rows not in {64, 128, 256}, or a device
+ * where one workgroup per CU cannot be resident; MOE_EINVAL for a missing MXFP8 w_scales or
+ * when comm_cus leaves no CU for compute; MOE_EALIGN for misaligned scales; MOE_ENOSPC for a
+ * ring below one 256-row tile or a small workspace.
  */
 int moe_forward_persistent(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
                            const float* const* logits, const void* const* x, const void* w1, const void* w3,
-                           const void* w2, void* ring, size_t ring_bytes, void* const* recv, void* const* y,
-                           int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
-                           int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes, void* stream);
+                           const void* w2, const moe_mx_scales_t* w_scales, void* ring, size_t ring_bytes,
+                           void* const* recv, void* const* y, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                           int32_t* offsets, int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /*
  * moe_persistent_dispatch_ffn_combine -- the persistent kernel of moe_forward_persistent alone
@@ -361,9 +371,9 @@ int moe_forward_persistent(const moe_shape_t* s, const moe_placement_t* p, const
  */
 int moe_persistent_dispatch_ffn_combine(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
                                         const void* const* x, const void* w1, const void* w3, const void* w2,
-                                        void* ring, size_t ring_bytes, const int32_t* pull_src,
-                                        const int32_t* slot_of, const int32_t* offsets, void* const* recv, void* ws,
-                                        size_t ws_bytes, void* stream);
+                                        const moe_mx_scales_t* w_scales, void* ring, size_t ring_bytes,
+                                        const int32_t* pull_src, const int32_t* slot_of, const int32_t* offsets,
+                                        void* const* recv, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_forward_persistent_noalloc -- for callers that cannot allocate device memory (code
@@ -381,6 +391,7 @@ int moe_persistent_dispatch_ffn_combine(const moe_shape_t* s, const moe_placemen
  * Every call on one GPU shares that GPU's array and leaves its contents behind; each call
  * clears what must start at zero, but calls that overlap on one GPU (no ordering between
  * their streams) race on the array.
+ * bf16 only: it takes no weight scales, so MXFP8 shapes return MOE_EUNSUP.
  * Errors: as moe_forward_persistent; MOE_ENOSPC when the shape's workspace
  * (moe_persistent_workspace_bytes) exceeds MOE_NOALLOC_WORKSPACE_BYTES or the ring part
  * holds less than one 256-row tile; MOE_EINVAL for ex->trace != 0; MOE_EHIP if the array's
@@ -398,8 +409,8 @@ int moe_forward_persistent_noalloc(const moe_shape_t* s, const moe_placement_t* 
 size_t moe_ring_slot_bytes(const moe_shape_t* s, const moe_exec_t* ex);
 
 /* Workspace bytes moe_forward_persistent needs (smaller than moe_workspace_bytes); includes
- * a per-pair recv address table (8 bytes per moe_max_pairs) when ex->reverse_ring is 1 and
- * the trace region after it when ex->trace is 1. */
+ * a per-pair recv address table (8 bytes per moe_max_pairs) when ex->reverse_ring is 1 or the
+ * dtype is MXFP8, and the trace region after it when ex->trace is 1. */
 size_t moe_persistent_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex);
 
 /* One event of the persistent kernel's trace.  Times are wall-clock ticks of the GPU's

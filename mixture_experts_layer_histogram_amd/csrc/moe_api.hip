@@ -34,8 +34,10 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
                              const int32_t* offsets, char* ring, long long slot_bytes, int blk_log2,
                              const sched::Plan& plan, int grid, long long budget, void* const* recv, char* ws,
                              const WsLayout& L, moe_trace_event_t* trace, int32_t* trace_count, int trace_cap,
-                             const uint64_t* row_dst, hipStream_t st);
-hipError_t persistent_occupancy(int* blocks_per_cu);
+                             const uint64_t* row_dst, bool reverse, const moe_mx_scales_t* w_scales,
+                             hipStream_t st);
+hipError_t persistent_occupancy(int* blocks_per_cu, bool mx);
+long long persist_mx_slot_layout(int d, int F, int cr, long long* tok_s_off, long long* h_off, long long* h_s_off);
 hipError_t launch_rows_bmn(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, int ksplit, uint16_t* C, int K,
                            int Nout, const int32_t* offsets, const int32_t* mtb, const int32_t* ctrl, int El, int cus,
                            hipStream_t st, const uint64_t* row_dst);
@@ -147,6 +149,10 @@ int chunk_log2_of(const moe_exec_t* ex) {
 }
 
 size_t ring_slot_bytes(const moe_shape_t& s, int blk_log2) {
+  if (s.dtype == MOE_MXFP8) {     // codes and scale words of the token rows and of h
+    long long a, b, c;
+    return size_t(persist_mx_slot_layout(s.d, s.F, 1 << blk_log2, &a, &b, &c));
+  }
   return (size_t(1) << blk_log2) * (size_t(s.d) + size_t(s.F)) * 2;
 }
 
@@ -378,7 +384,8 @@ int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_
 }
 
 size_t moe_ring_slot_bytes(const moe_shape_t* s, const moe_exec_t* ex) {
-  if (!s || s->dtype != MOE_BF16 || s->d < 1 || s->F < 1) return 0;
+  if (!s || (s->dtype != MOE_BF16 && s->dtype != MOE_MXFP8) || s->d < 1 || s->F < 1) return 0;
+  if (s->dtype == MOE_MXFP8 && (s->d % 128 || s->F % 128)) return 0;
   const int b = chunk_log2_of(ex);
   return b < 0 ? 0 : ring_slot_bytes(*s, b);
 }
@@ -395,16 +402,16 @@ int trace_capacity(const moe_shape_t& s, const WsLayout& L, const moe_exec_t* ex
 size_t trace_bytes(const moe_shape_t& s, const WsLayout& L, const moe_exec_t* ex) {
   return align256(256 + size_t(trace_capacity(s, L, ex)) * sizeof(moe_trace_event_t));
 }
-// reverse ring: the per-pair recv address table of the down GEMM's stores, at L.hbuf
-size_t reverse_table_bytes(const WsLayout& L, const moe_exec_t* ex) {
-  return (ex && ex->reverse_ring == 1) ? align256(size_t(L.max_pairs) * 8) : 0;
+// reverse ring and MXFP8: the per-pair recv address table of the down GEMM's stores, at L.hbuf
+size_t reverse_table_bytes(const moe_shape_t& s, const WsLayout& L, const moe_exec_t* ex) {
+  return ((ex && ex->reverse_ring == 1) || s.dtype == MOE_MXFP8) ? align256(size_t(L.max_pairs) * 8) : 0;
 }
 }  // namespace
 
 size_t moe_persistent_workspace_bytes(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex) {
   if (check_shape(s, p) != MOE_OK) return 0;
   const WsLayout L = ws_layout(*s, p->E_local);
-  return L.hbuf + reverse_table_bytes(L, ex) + ((ex && ex->trace) ? trace_bytes(*s, L, ex) : 0);   // no h staging
+  return L.hbuf + reverse_table_bytes(*s, L, ex) + ((ex && ex->trace) ? trace_bytes(*s, L, ex) : 0);   // no h staging
 }
 
 int moe_persistent_trace_info(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex, size_t* offset,
@@ -412,7 +419,7 @@ int moe_persistent_trace_info(const moe_shape_t* s, const moe_placement_t* p, co
   if (check_shape(s, p) != MOE_OK || !ex || ex->trace != 1 || !offset || !capacity || !ticks_per_us)
     return MOE_EINVAL;
   const WsLayout L = ws_layout(*s, p->E_local);
-  *offset = L.hbuf + reverse_table_bytes(L, ex);
+  *offset = L.hbuf + reverse_table_bytes(*s, L, ex);
   *capacity = trace_capacity(*s, L, ex);
   *ticks_per_us = static_cast<int32_t>(wall_ticks_per_us());
   return MOE_OK;
@@ -435,15 +442,19 @@ struct PersistSetup {
   long long slot_bytes, budget;
   int blk_log2, cus;
   bool tracing, reverse;
-  size_t rev_bytes;      // reverse ring: the recv address table at L.hbuf
+  size_t rev_bytes;      // reverse ring and MXFP8: the recv address table at L.hbuf
+  const moe_mx_scales_t* w_scales;   // MXFP8: the weights' scales; null in bf16
 };
 
 int persist_setup(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex, const void* const* x,
-                  const void* w1, const void* w3, const void* w2, const void* ring, size_t ring_bytes,
-                  void* const* recv, const void* ws, size_t ws_bytes, PersistSetup* out) {
+                  const void* w1, const void* w3, const void* w2, const moe_mx_scales_t* w_scales,
+                  const void* ring, size_t ring_bytes, void* const* recv, const void* ws, size_t ws_bytes,
+                  PersistSetup* out) {
   int rc = check_shape(s, p);
   if (rc) return rc;
-  if (s->dtype != MOE_BF16) return MOE_EUNSUP;
+  if (s->dtype != MOE_BF16 && s->dtype != MOE_MXFP8) return MOE_EUNSUP;
+  if (s->dtype == MOE_MXFP8 && (rc = check_w_scales(w_scales))) return rc;
+  out->w_scales = s->dtype == MOE_MXFP8 ? w_scales : nullptr;
   const void* bufs[] = {w1, w3, w2};
   for (const void* b : bufs)
     if (!aligned16(b)) return b ? MOE_EALIGN : MOE_EINVAL;
@@ -460,7 +471,7 @@ int persist_setup(const moe_shape_t* s, const moe_placement_t* p, const moe_exec
   if (reinterpret_cast<uintptr_t>(ws) & 255) return MOE_EALIGN;
   out->tracing = ex && ex->trace == 1;
   out->reverse = ex && ex->reverse_ring == 1;
-  out->rev_bytes = reverse_table_bytes(out->L, ex);
+  out->rev_bytes = reverse_table_bytes(*s, out->L, ex);
   if (ws_bytes < out->L.hbuf + out->rev_bytes + (out->tracing ? trace_bytes(*s, out->L, ex) : 0)) return MOE_ENOSPC;
   const int cpm = kGemmBM >> out->blk_log2;
   out->slot_bytes = static_cast<long long>(ring_slot_bytes(*s, out->blk_log2));
@@ -488,7 +499,7 @@ int persist_launch(const moe_shape_t* s, const moe_placement_t* p, const moe_exe
   moe_trace_event_t* trace = P.tracing ? reinterpret_cast<moe_trace_event_t*>(wsc + toff + 256) : nullptr;
   int32_t* trace_count = P.tracing ? reinterpret_cast<int32_t*>(wsc + toff) : nullptr;
   uint64_t* row_dst = nullptr;
-  if (P.reverse) {      // the recv address of every local pair, for the down GEMM's stores
+  if (P.reverse || P.w_scales) {      // the recv address of every local pair, for the down GEMM's stores
     row_dst = reinterpret_cast<uint64_t*>(wsc + P.L.hbuf);
     const hipError_t e = launch_pair_addr(*s, pull_src, slot_of, recv, nullptr,
                                           reinterpret_cast<const int32_t*>(wsc + P.L.ctrl), row_dst, nullptr,
@@ -497,42 +508,44 @@ int persist_launch(const moe_shape_t* s, const moe_placement_t* p, const moe_exe
   }
   return hip_rc(launch_persistent(*s, p->E_local, x, w1, w3, w2, pull_src, slot_of, offsets, static_cast<char*>(ring),
                                   P.slot_bytes, P.blk_log2, P.plan, P.cus, P.budget, recv, wsc, P.L, trace,
-                                  trace_count, P.tracing ? trace_capacity(*s, P.L, ex) : 0, row_dst, st));
+                                  trace_count, P.tracing ? trace_capacity(*s, P.L, ex) : 0, row_dst, P.reverse,
+                                  P.w_scales, st));
 }
 
-int persist_occupancy_ok() {
+int persist_occupancy_ok(bool mx) {
   int occ = 0;
-  if (persistent_occupancy(&occ) != hipSuccess) return MOE_EHIP;
+  if (persistent_occupancy(&occ, mx) != hipSuccess) return MOE_EHIP;
   return occ < 1 ? MOE_EUNSUP : MOE_OK;                   // one workgroup per CU must fit
 }
 }  // namespace
 
 int moe_persistent_dispatch_ffn_combine(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
                                         const void* const* x, const void* w1, const void* w3, const void* w2,
-                                        void* ring, size_t ring_bytes, const int32_t* pull_src,
-                                        const int32_t* slot_of, const int32_t* offsets, void* const* recv, void* ws,
-                                        size_t ws_bytes, void* stream) {
+                                        const moe_mx_scales_t* w_scales, void* ring, size_t ring_bytes,
+                                        const int32_t* pull_src, const int32_t* slot_of, const int32_t* offsets,
+                                        void* const* recv, void* ws, size_t ws_bytes, void* stream) {
   PersistSetup P;
-  int rc = persist_setup(s, p, ex, x, w1, w3, w2, ring, ring_bytes, recv, ws, ws_bytes, &P);
+  int rc = persist_setup(s, p, ex, x, w1, w3, w2, w_scales, ring, ring_bytes, recv, ws, ws_bytes, &P);
   if (rc) return rc;
   if (!pull_src || !slot_of || !offsets) return MOE_EINVAL;
-  if ((rc = persist_occupancy_ok())) return rc;
+  if ((rc = persist_occupancy_ok(P.w_scales != nullptr))) return rc;
   return persist_launch(s, p, ex, P, x, w1, w3, w2, ring, pull_src, slot_of, offsets, recv, ws,
                         static_cast<hipStream_t>(stream));
 }
 
 int moe_forward_persistent(const moe_shape_t* s, const moe_placement_t* p, const moe_exec_t* ex,
                            const float* const* logits, const void* const* x, const void* w1, const void* w3,
-                           const void* w2, void* ring, size_t ring_bytes, void* const* recv, void* const* y,
-                           int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* pull_src,
-                           int32_t* slot_of, void* ws, size_t ws_bytes, void* stream) {
+                           const void* w2, const moe_mx_scales_t* w_scales, void* ring, size_t ring_bytes,
+                           void* const* recv, void* const* y, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                           int32_t* offsets, int32_t* pull_src, int32_t* slot_of, void* ws, size_t ws_bytes,
+                           void* stream) {
   PersistSetup P;
-  int rc = persist_setup(s, p, ex, x, w1, w3, w2, ring, ring_bytes, recv, ws, ws_bytes, &P);
+  int rc = persist_setup(s, p, ex, x, w1, w3, w2, w_scales, ring, ring_bytes, recv, ws, ws_bytes, &P);
   if (rc) return rc;
   if (!p->expert_to_local || !topk_idx || !topk_w || !counts || !offsets || !pull_src || !slot_of)
     return MOE_EINVAL;
   if ((rc = check_ptr_table(logits, s->R)) || (rc = check_ptr_table(y, s->R))) return rc;
-  if ((rc = persist_occupancy_ok())) return rc;
+  if ((rc = persist_occupancy_ok(P.w_scales != nullptr))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_layout(*s, p->expert_to_local, p->E_local, minibatch_of(ex), logits, topk_idx, topk_w, counts,
                                offsets, pull_src, slot_of, static_cast<char*>(ws), P.L, st);

@@ -61,10 +61,11 @@ extern "C" int moe_forward_persistent_noalloc(const moe_shape_t* s, const moe_pl
   if (need == 0) return MOE_EINVAL;                       // bad shape or placement
   if (need > kNoAllocWsBytes) return MOE_ENOSPC;          // shape beyond the array's workspace part
   if (status && (reinterpret_cast<uintptr_t>(status) & 3)) return MOE_EALIGN;
+  if (s->dtype != MOE_BF16) return MOE_EUNSUP;               // the MXFP8 ring needs the weights' scales
   int rc = MOE_OK;
   char* base = scratch_ptr(&rc);
   if (!base) return rc;
-  rc = moe_forward_persistent(s, p, ex, logits, x, w1, w3, w2, base + kNoAllocWsBytes, kNoAllocBytes - kNoAllocWsBytes,
+  rc = moe_forward_persistent(s, p, ex, logits, x, w1, w3, w2, nullptr, base + kNoAllocWsBytes, kNoAllocBytes - kNoAllocWsBytes,
                               recv, y, topk_idx, topk_w, counts, offsets, pull_src, slot_of, base, kNoAllocWsBytes,
                               stream);
   if (rc || !status) return rc;

@@ -29,7 +29,10 @@
 //   agent-scope release/acquire (the producer also writes back its XCD's L2, the consumer
 //   drops stale lines of its own).
 // * Ring slot.  One minibatch (chunk) of token rows, overwritten in place by the expert
-//   outputs of those rows, followed by the rows' h.
+//   outputs of those rows, followed by the rows' h.  In MXFP8 the slot holds the rows'
+//   E4M3 codes and scale words (quantised by the gather, as the standalone quantising
+//   gather does), then h's codes and scale words (quantised by the gate/up GEMM's
+//   epilogue); the down GEMM stores each bf16 output row straight to recv.
 // * Reverse ring (qubstore.ru, ring buffer paragraph: the forward walks the ring in reverse
 //   so that at its end the ring holds the activations the gradients need).  Each pipeline
 //   takes its row tiles from last to first: the rules below run on the pipeline's own order
@@ -42,7 +45,7 @@
 //   the status word (MOE_ETIMEOUT) and an abort word that every loop checks, so all
 //   workgroups exit.  A check kernel afterwards reports MOE_EINCOMPLETE if any pipeline's
 //   work was left undone (e.g. a pipeline that received no workgroup).
-#include "gemm_tile.hpp"
+#include "gemm_mx_tile.hpp"
 #include "persist_sched.hpp"
 
 namespace moe {
@@ -73,7 +76,19 @@ struct PersistArgs {
   int n_part, light, comm_pp, S, G, lookahead;
   int reverse;                  // 1: reverse ring (pipelines walk their row tiles backwards)
   int max_mtiles;               // entries of the resident record: 4 per row tile
-  const uint64_t* row_dst;      // reverse ring: per local pair, the address of its recv row
+  const uint64_t* row_dst;      // reverse ring and MXFP8: per local pair, the address of its recv row
+  // MXFP8: weight codes and scales (the MXFP8 scale layout over each weight matrix's
+  // E_local * rows), and the slot layout: token codes at 0 (row stride d), their scale words
+  // at tok_s_off (K-tile planes 4 * chunk rows apart), h codes at h_off (row stride F), h's
+  // scale words at h_s_off
+  int mx;
+  const uint8_t* w1q;
+  const uint8_t* w3q;
+  const uint8_t* w2q;
+  const uint8_t* w1s;
+  const uint8_t* w3s;
+  const uint8_t* w2s;
+  long long tok_s_off, h_off, h_s_off;
   CtrlLayout cl;
 };
 
@@ -316,10 +331,67 @@ __device__ void do_gather(const PersistArgs& A, const PipeCtx& c, int q, char* s
   __syncthreads();                                              // the row tables are reused
 }
 
+// MXFP8: gather chunk q's rows quantised on the way (E4M3 codes at row stride d; the scale
+// word of row r in K-tile plane p at tok_s_off + p * 4 * chunk_rows + 4 * r), then signal it.
+// One wave per row, 8 of the row's 16-byte vectors per lane at a time; every lane of the wave
+// takes part in the quantiser's shuffles (lanes past the row end carry zeros).
+__device__ void do_gather_mx(const PersistArgs& A, const PipeCtx& c, int q, char* smem) {
+  uint64_t* src_tab = reinterpret_cast<uint64_t*>(smem);
+  int row0, l;
+  const int m = c.lo + q / c.cpm, h = q % c.cpm;
+  const int rows = tile_rows(A, layout_tile(c.reverse, c.lo, c.n_m, m), &row0, &l);
+  const int c_lo = h * c.chunk_rows, c_n = min(c.chunk_rows, rows - c_lo);
+  char* dst = slot_ptr(A, c, q);
+  for (int r = threadIdx.x; r < c_n; r += kGemmThreads) {
+    const int s = row0 + c_lo + r;
+    const int rk = A.pull_src[2 * (long long)s];
+    const int t = A.pull_src[2 * (long long)s + 1];
+    src_tab[r] = reinterpret_cast<uint64_t>(A.x.p[rk] + (long long)t * A.d * 2);
+  }
+  __syncthreads();
+  constexpr int U = 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n16 = A.d >> 3;                        // d % 128 == 0: whole 16-lane groups
+  const long long splane = 4LL * c.chunk_rows;
+  for (int r = wave; r < c_n; r += kGemmThreads / 64) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(src_tab[r]);    // the sources never change
+    uint2* code = reinterpret_cast<uint2*>(dst + (long long)r * A.d);
+    char* sw0 = dst + A.tok_s_off + 4LL * r;
+    for (int base = 0; base < n16; base += 64 * U) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = base + u * 64 + lane;
+        v[u] = u32x4{0, 0, 0, 0};
+        if (i < n16) v[u] = src[i];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = base + u * 64 + lane;
+        uint32_t sc;
+        const uint2 qv = mx_quant8_bf16(v[u], &sc);     // all lanes: quad shuffles inside
+        const uint32_t sw = mx_scale_word(sc);            // all lanes: row shifts inside
+        if (i < n16) {
+          code[i] = qv;
+          if ((i & 15) == 0) *reinterpret_cast<uint32_t*>(sw0 + (i >> 4) * splane) = sw;
+        }
+      }
+    }
+  }
+  release_add(A.pc + A.cl.filled + m * 4 + h, 1, c.light);
+  __syncthreads();                                              // the row table is reused
+}
+
+template <bool MX>
+__device__ __forceinline__ void gather_chunk(const PersistArgs& A, const PipeCtx& c, int q, char* smem) {
+  if constexpr (MX) do_gather_mx(A, c, q, smem);
+  else do_gather(A, c, q, smem);
+}
+
 // Push pipeline-local chunk q: its output rows (in place in the ring) to recv[rank][token][j];
 // then free its slot (whole workgroup).
 __device__ void do_push(const PersistArgs& A, const PipeCtx& c, int q, char* smem) {
-  if (c.reverse) {      // the down GEMM already stored the rows to recv: only free the slot
+  if (A.row_dst) {      // the down GEMM already stored the rows to recv: only free the slot
     if (threadIdx.x == 0)
       __hip_atomic_fetch_add(A.pc + sched::slot_epoch_word(A.cl, c.p, c.S, q), 1, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
@@ -355,6 +427,7 @@ __device__ void do_push(const PersistArgs& A, const PipeCtx& c, int q, char* sme
 // A compute workgroup waits until every chunk of row tile m is in its slot; meanwhile it
 // gathers claimable chunks of its pipeline itself (a gather never waits, so this cannot
 // deadlock).  Returns false on abort or watchdog expiry.
+template <bool MX>
 __device__ bool wait_chunks(const PersistArgs& A, const PipeCtx& c, int m, char* smem, int* sh) {
   const DevOps ops{A.pc};
   long long t0 = wall_clock64();
@@ -387,13 +460,14 @@ __device__ bool wait_chunks(const PersistArgs& A, const PipeCtx& c, int m, char*
     if (st == 2) return false;
     if (st == 3) {
       const long long tb = wall_clock64();
-      do_gather(A, c, arg, smem);
+      gather_chunk<MX>(A, c, arg, smem);
       trace_event(A, 1, arg, c.p, tb, wall_clock64(), tb - t0);
       t0 = wall_clock64();
     }
   }
 }
 
+template <bool MX>
 __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(PersistArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int sh[4];
@@ -455,7 +529,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
       int row0, l;
       const int rows = tile_rows(A, ml, &row0, &l);
       const long long t_w = wall_clock64();
-      const bool ok = !tk.down ? wait_chunks(A, c, m, smem, sh) : wait_ge(g1_done + m, NT1, A, sh);
+      const bool ok = !tk.down ? wait_chunks<MX>(A, c, m, smem, sh) : wait_ge(g1_done + m, NT1, A, sh);
       if (!ok) {
         aborted = true;
         break;
@@ -467,45 +541,83 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
       char* s1 = slot_ptr(A, c, q0 + min(1, cpm - 1));
       char* s2 = slot_ptr(A, c, q0 + min(2, cpm - 1));
       char* s3 = slot_ptr(A, c, q0 + min(3, cpm - 1));
-      TileIO io;
-      io.blk_log2 = A.blk_log2;
-      io.rows = rows;
-      io.row_dst = nullptr;
-      io.row_src = nullptr;
-      io.dh = nullptr;
-      io.dab = nullptr;
-      if (!tk.down) {
-        io.a0 = reinterpret_cast<const uint16_t*>(s0);
-        io.a1 = reinterpret_cast<const uint16_t*>(s1);
-        io.a2 = reinterpret_cast<const uint16_t*>(s2);
-        io.a3 = reinterpret_cast<const uint16_t*>(s3);
-        io.o0 = reinterpret_cast<uint16_t*>(s0 + xpart);
-        io.o1 = reinterpret_cast<uint16_t*>(s1 + xpart);
-        io.o2 = reinterpret_cast<uint16_t*>(s2 + xpart);
-        io.o3 = reinterpret_cast<uint16_t*>(s3 + xpart);
-        io.a_ld = A.d;
-        io.o_ld = A.F;
-        const uint16_t* b0 = A.w1 + size_t(l) * A.F * A.d;
-        const uint16_t* b1 = A.w3 + size_t(l) * A.F * A.d;
-        gemm_tile<0, 16>(io, b0, b1, tk.j * (kGemmBN / 2), A.F, A.d, smem, A.d);   // x rows: sc1 loads
-        release_add(g1_done + m, 1, light);
-        trace_event(A, 3, ml * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
+      if constexpr (MX) {
+        // the tile's rows are the chunks' slots: token codes / scale words for the gate/up
+        // GEMM, h codes / scale words for the down GEMM, whose outputs go straight to recv
+        char* sl[4] = {s0, s1, s2, s3};
+        TileMX io{};
+        io.blk_log2 = A.blk_log2;
+        io.rows = rows;
+        io.as_plane = 4LL * c.chunk_rows;
+        io.os_plane = 4LL * c.chunk_rows;
+        if (!tk.down) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            io.ablk[i] = reinterpret_cast<const uint8_t*>(sl[i]);
+            io.asblk[i] = reinterpret_cast<const uint8_t*>(sl[i] + A.tok_s_off);
+            io.oblk[i] = reinterpret_cast<uint8_t*>(sl[i] + A.h_off);
+            io.osblk[i] = reinterpret_cast<uint8_t*>(sl[i] + A.h_s_off);
+          }
+          const uint8_t* b0 = A.w1q + size_t(l) * A.F * A.d;
+          const uint8_t* b1 = A.w3q + size_t(l) * A.F * A.d;
+          gemm_mx_tile<0, 16, true>(io, b0, b1, A.w1s + 4 * size_t(l) * A.F, A.w3s + 4 * size_t(l) * A.F,
+                                    4LL * A.El * A.F, tk.j * (kGemmBN / 2), A.F, A.d, smem);
+          release_add(g1_done + m, 1, light);
+          trace_event(A, 3, ml * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            io.ablk[i] = reinterpret_cast<const uint8_t*>(sl[i] + A.h_off);
+            io.asblk[i] = reinterpret_cast<const uint8_t*>(sl[i] + A.h_s_off);
+          }
+          io.row_dst = A.row_dst + row0;
+          const uint8_t* b0 = A.w2q + size_t(l) * A.d * A.F;
+          const uint8_t* bs0 = A.w2s + 4 * size_t(l) * A.d;
+          gemm_mx_tile<1, 16, true>(io, b0, b0, bs0, bs0, 4LL * A.El * A.d, tk.j * kGemmBN, A.d, A.F, smem);
+          release_add(g2_done + m, 1, light);
+          trace_event(A, 4, ml * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
+        }
       } else {
-        io.a0 = reinterpret_cast<const uint16_t*>(s0 + xpart);
-        io.a1 = reinterpret_cast<const uint16_t*>(s1 + xpart);
-        io.a2 = reinterpret_cast<const uint16_t*>(s2 + xpart);
-        io.a3 = reinterpret_cast<const uint16_t*>(s3 + xpart);
-        io.o0 = reinterpret_cast<uint16_t*>(s0);
-        io.o1 = reinterpret_cast<uint16_t*>(s1);
-        io.o2 = reinterpret_cast<uint16_t*>(s2);
-        io.o3 = reinterpret_cast<uint16_t*>(s3);
-        io.a_ld = A.F;
-        io.o_ld = A.d;
-        if (A.reverse) io.row_dst = A.row_dst + row0;       // outputs straight to recv
-        const uint16_t* b0 = A.w2 + size_t(l) * A.d * A.F;
-        gemm_tile<1, 16>(io, b0, b0, tk.j * kGemmBN, A.d, A.F, smem, A.F);         // h rows: sc1 loads
-        release_add(g2_done + m, 1, light);
-        trace_event(A, 4, ml * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
+        TileIO io;
+        io.blk_log2 = A.blk_log2;
+        io.rows = rows;
+        io.row_dst = nullptr;
+        io.row_src = nullptr;
+        io.dh = nullptr;
+        io.dab = nullptr;
+        if (!tk.down) {
+          io.a0 = reinterpret_cast<const uint16_t*>(s0);
+          io.a1 = reinterpret_cast<const uint16_t*>(s1);
+          io.a2 = reinterpret_cast<const uint16_t*>(s2);
+          io.a3 = reinterpret_cast<const uint16_t*>(s3);
+          io.o0 = reinterpret_cast<uint16_t*>(s0 + xpart);
+          io.o1 = reinterpret_cast<uint16_t*>(s1 + xpart);
+          io.o2 = reinterpret_cast<uint16_t*>(s2 + xpart);
+          io.o3 = reinterpret_cast<uint16_t*>(s3 + xpart);
+          io.a_ld = A.d;
+          io.o_ld = A.F;
+          const uint16_t* b0 = A.w1 + size_t(l) * A.F * A.d;
+          const uint16_t* b1 = A.w3 + size_t(l) * A.F * A.d;
+          gemm_tile<0, 16>(io, b0, b1, tk.j * (kGemmBN / 2), A.F, A.d, smem, A.d);   // x rows: sc1 loads
+          release_add(g1_done + m, 1, light);
+          trace_event(A, 3, ml * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
+        } else {
+          io.a0 = reinterpret_cast<const uint16_t*>(s0 + xpart);
+          io.a1 = reinterpret_cast<const uint16_t*>(s1 + xpart);
+          io.a2 = reinterpret_cast<const uint16_t*>(s2 + xpart);
+          io.a3 = reinterpret_cast<const uint16_t*>(s3 + xpart);
+          io.o0 = reinterpret_cast<uint16_t*>(s0);
+          io.o1 = reinterpret_cast<uint16_t*>(s1);
+          io.o2 = reinterpret_cast<uint16_t*>(s2);
+          io.o3 = reinterpret_cast<uint16_t*>(s3);
+          io.a_ld = A.F;
+          io.o_ld = A.d;
+          if (A.row_dst) io.row_dst = A.row_dst + row0;       // outputs straight to recv
+          const uint16_t* b0 = A.w2 + size_t(l) * A.d * A.F;
+          gemm_tile<1, 16>(io, b0, b0, tk.j * kGemmBN, A.d, A.F, smem, A.F);         // h rows: sc1 loads
+          release_add(g2_done + m, 1, light);
+          trace_event(A, 4, ml * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
+        }
       }
     }
   }
@@ -542,7 +654,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
         do_push(A, c, arg, smem);
         trace_event(A, 2, arg, p, t_b, wall_clock64(), t_b - idle_since);
       } else {
-        do_gather(A, c, arg, smem);
+        gather_chunk<MX>(A, c, arg, smem);
         trace_event(A, 1, arg, p, t_b, wall_clock64(), t_b - idle_since);
       }
       idle_since = wall_clock64();
@@ -554,15 +666,34 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
 // ---------------------------------------------------------------------------- host side
 int persist_ctrl_words(int max_mtiles) { return sched::ctrl_layout(max_mtiles, kMaxRingSlots).words; }
 
-hipError_t persistent_occupancy(int* blocks_per_cu) {
+// MXFP8 ring slot of cr rows: the token rows' codes, their scale words (d / 128 K-tile planes
+// of cr words), h's codes, h's scale words; each part 256-byte aligned.  Returns the slot size.
+long long persist_mx_slot_layout(int d, int F, int cr, long long* tok_s_off, long long* h_off, long long* h_s_off) {
+  long long o = static_cast<long long>(cr) * d;
+  *tok_s_off = static_cast<long long>(align256(size_t(o)));
+  o = *tok_s_off + 4LL * cr * (d / 128);
+  *h_off = static_cast<long long>(align256(size_t(o)));
+  o = *h_off + static_cast<long long>(cr) * F;
+  *h_s_off = static_cast<long long>(align256(size_t(o)));
+  o = *h_s_off + 4LL * cr * (F / 128);
+  return static_cast<long long>(align256(size_t(o)));
+}
+
+hipError_t persistent_occupancy(int* blocks_per_cu, bool mx) {
   static std::atomic<uint64_t> attr_set{0};
   const hipError_t ea = once_per_device(attr_set, [] {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(moe_persistent_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_persistent_kernel<false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_persistent_kernel<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
+    return e;
   });
   if (ea != hipSuccess) return ea;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, reinterpret_cast<const void*>(moe_persistent_kernel),
-                                                      kGemmThreads, kGemmLds);
+  return mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                  blocks_per_cu, reinterpret_cast<const void*>(moe_persistent_kernel<true>), kGemmThreads, kMxLds)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                  blocks_per_cu, reinterpret_cast<const void*>(moe_persistent_kernel<false>), kGemmThreads, kGemmLds);
 }
 
 hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x, const void* w1, const void* w3,
@@ -570,7 +701,8 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
                              const int32_t* offsets, char* ring, long long slot_bytes, int blk_log2,
                              const sched::Plan& plan, int grid, long long budget, void* const* recv, char* ws,
                              const WsLayout& L, moe_trace_event_t* trace, int32_t* trace_count, int trace_cap,
-                             const uint64_t* row_dst, hipStream_t st) {
+                             const uint64_t* row_dst, bool reverse, const moe_mx_scales_t* w_scales,
+                             hipStream_t st) {
   PersistArgs A{};
   for (int r = 0; r < s.R; ++r) {
     A.x.p[r] = static_cast<const char*>(x[r]);
@@ -605,19 +737,32 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
   A.S = plan.S;
   A.G = plan.G;
   A.lookahead = plan.lookahead;
-  A.reverse = row_dst ? 1 : 0;
+  A.reverse = reverse ? 1 : 0;
   A.max_mtiles = L.max_mtiles;
   A.row_dst = row_dst;
   A.cl = sched::ctrl_layout(L.max_mtiles, kMaxRingSlots);
+  A.mx = w_scales ? 1 : 0;
+  if (A.mx) {
+    A.w1q = static_cast<const uint8_t*>(w1);
+    A.w3q = static_cast<const uint8_t*>(w3);
+    A.w2q = static_cast<const uint8_t*>(w2);
+    A.w1s = w_scales->w1;
+    A.w3s = w_scales->w3;
+    A.w2s = w_scales->w2;
+    persist_mx_slot_layout(s.d, s.F, 1 << blk_log2, &A.tok_s_off, &A.h_off, &A.h_s_off);
+  }
 
   int occ = 0;
-  hipError_t e = persistent_occupancy(&occ);
+  hipError_t e = persistent_occupancy(&occ, A.mx != 0);
   if (e != hipSuccess) return e;
   const int zero_words = A.cl.slot_epoch + plan.n_part * plan.S;
   hipLaunchKernelGGL(persist_prep_kernel, dim3(1), dim3(1024), 0, st, A, zero_words);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(moe_persistent_kernel, dim3(grid), dim3(kGemmThreads), kGemmLds, st, A);
+  if (A.mx)
+    hipLaunchKernelGGL(moe_persistent_kernel<true>, dim3(grid), dim3(kGemmThreads), kMxLds, st, A);
+  else
+    hipLaunchKernelGGL(moe_persistent_kernel<false>, dim3(grid), dim3(kGemmThreads), kGemmLds, st, A);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(persist_check_kernel, dim3(1), dim3(64), 0, st, A);

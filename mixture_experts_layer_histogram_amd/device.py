@@ -204,19 +204,22 @@ class DeviceProblem:
     def forward_persistent(self, ex=None, stream=None, check=True):
         if not hasattr(self, "ring"):
             self.alloc_ring()
+        w1, w3, w2 = self.weights()
         return moe.moe_forward_persistent(self.shape, self.placement, ex if ex is not None else self.pex,
-                                          self.logits, self.x, self.w1, self.w3, self.w2, self.ring, self.recv,
+                                          self.logits, self.x, w1, w3, w2, self.ring, self.recv,
                                           self.y, self.topk_idx, self.topk_w, self.counts, self.offsets,
-                                          self.pull_src, self.slot_of, self.ws, stream=stream, check=check)
+                                          self.pull_src, self.slot_of, self.ws, stream=stream, check=check,
+                                          w_scales=self.w_scales)
 
     def persistent_dfc(self, ex=None, stream=None, check=True):
         """The persistent kernel alone (dispatch, FFN, push) after layout() with the same ex."""
         if not hasattr(self, "ring"):
             self.alloc_ring()
+        w1, w3, w2 = self.weights()
         return moe.moe_persistent_dispatch_ffn_combine(self.shape, self.placement, ex if ex is not None else self.pex,
-                                                       self.x, self.w1, self.w3, self.w2, self.ring, self.pull_src,
+                                                       self.x, w1, w3, w2, self.ring, self.pull_src,
                                                        self.slot_of, self.offsets, self.recv, self.ws, stream=stream,
-                                                       check=check)
+                                                       check=check, w_scales=self.w_scales)
 
     def status(self, stream=None) -> int:
         return moe.moe_read_status(self.ws, stream)

@@ -88,10 +88,10 @@ def lib() -> ctypes.CDLL:
                                         VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_forward.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, MS, VP, VP, VP, VP, VP,
                                   VP, VP, VP, VP, VP, VP, VP, SZ, VP]
-        L.moe_forward_persistent.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, SZ, VP, VP,
+        L.moe_forward_persistent.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, VP, SZ, VP, VP,
                                              VP, VP, VP, VP, VP, VP, VP, SZ, VP]
-        L.moe_persistent_dispatch_ffn_combine.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, SZ, VP, VP, VP, VP, VP,
-                                                          SZ, VP]
+        L.moe_persistent_dispatch_ffn_combine.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, SZ, VP, VP, VP, VP,
+                                                          VP, SZ, VP]
         L.moe_forward_persistent_noalloc.argtypes = [S, PL, EX, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP,
                                                      VP, VP, VP]
         L.moe_ring_slot_bytes.argtypes = [S, EX]
@@ -266,10 +266,10 @@ def moe_forward_fused(shape, placement, ex, logits, x, w1, w3, w2, xe, recv, y, 
 
 def moe_forward_persistent(shape, placement, ex, logits, x, w1, w3, w2, ring, recv, y, topk_idx, topk_w,
                            counts, offsets, pull_src, slot_of, ws, ring_bytes=None, ws_bytes=None, stream=None,
-                           check=True):
+                           check=True, w_scales=None):
     rc = lib().moe_forward_persistent(ctypes.byref(shape), ctypes.byref(placement),
                                       ctypes.byref(ex) if ex is not None else None, _table(logits), _table(x),
-                                      _p(w1), _p(w3), _p(w2), _p(ring),
+                                      _p(w1), _p(w3), _p(w2), _ref(w_scales), _p(ring),
                                       ring.numel() if ring_bytes is None else ring_bytes, _table(recv),
                                       _table(y), _p(topk_idx), _p(topk_w), _p(counts), _p(offsets),
                                       _p(pull_src), _p(slot_of), _p(ws),
@@ -278,10 +278,10 @@ def moe_forward_persistent(shape, placement, ex, logits, x, w1, w3, w2, ring, re
 
 
 def moe_persistent_dispatch_ffn_combine(shape, placement, ex, x, w1, w3, w2, ring, pull_src, slot_of, offsets, recv,
-                                        ws, ring_bytes=None, ws_bytes=None, stream=None, check=True):
+                                        ws, ring_bytes=None, ws_bytes=None, stream=None, check=True, w_scales=None):
     rc = lib().moe_persistent_dispatch_ffn_combine(ctypes.byref(shape), ctypes.byref(placement),
                                                    ctypes.byref(ex) if ex is not None else None, _table(x), _p(w1),
-                                                   _p(w3), _p(w2), _p(ring),
+                                                   _p(w3), _p(w2), _ref(w_scales), _p(ring),
                                                    ring.numel() if ring_bytes is None else ring_bytes,
                                                    _p(pull_src), _p(slot_of), _p(offsets), _table(recv), _p(ws),
                                                    ws.numel() if ws_bytes is None else ws_bytes, _stream(stream))

@@ -171,9 +171,25 @@ def test_mx_entry_points_need_their_scales():
     rc = L.moe_forward(ctypes.byref(s), ctypes.byref(p), None, tabp, tabp, FAKE, FAKE, FAKE, None, FAKE, FAKE,
                        FAKE, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None)
     assert rc == -1
-    # the persistent path is bf16 only
-    assert L.moe_forward_persistent(ctypes.byref(s), ctypes.byref(p), None, tabp, tabp, FAKE, FAKE, FAKE, FAKE,
-                                    big, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == -6
+    # the persistent path takes MXFP8 weights with their scales; the ring slot holds codes and
+    # scale words of the token rows and of h, each part 256-byte aligned
+    def pers(wsc, ws_bytes=big):
+        return L.moe_forward_persistent(ctypes.byref(s), ctypes.byref(p), None, tabp, tabp, FAKE, FAKE, FAKE,
+                                        ctypes.byref(wsc) if wsc is not None else None, FAKE, big, tabp, tabp, FAKE,
+                                        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+    assert pers(None) == -1
+    assert pers(moe.MXScales(FAKE, FAKE, FAKE + 1)) == -2
+    assert pers(ok, ws_bytes=1024) == -3
+    ex = moe.Exec(128, 0, 0, 0, 0)
+    slot = moe.moe_ring_slot_bytes(s, ex)
+    a = lambda n: (n + 255) // 256 * 256
+    assert slot == a(128 * 7168) + a(128 * 7168 // 32) + a(128 * 2048) + a(128 * 2048 // 32)
+    assert moe.moe_ring_slot_bytes(_shape(dtype=moe.MOE_MXFP8, d=7168 + 64), ex) == 0    # d % 128
+    # the pair address table is part of the MXFP8 workspace, reverse ring or not
+    assert moe.moe_persistent_workspace_bytes(s, p, ex) == moe.moe_persistent_workspace_bytes(
+        s, p, moe.Exec(128, 0, 0, 0, 0, 1))
+    assert moe.moe_persistent_workspace_bytes(s, p, ex) == moe.moe_persistent_workspace_bytes(
+        _shape(), p, moe.Exec(128, 0, 0, 0, 0, 1))
 
 
 def test_persistent_entry_rejects_bad_arguments_before_launch():
@@ -189,7 +205,7 @@ def test_persistent_entry_rejects_bad_arguments_before_launch():
 
     def call(shape=s, ex=None, ring_bytes=big, ring=FAKE, ws_bytes=big):
         return L.moe_forward_persistent(ctypes.byref(shape), ctypes.byref(p), ctypes.byref(ex) if ex else None,
-                                        tabp, tabp, FAKE, FAKE, FAKE, ring, ring_bytes, tabp, tabp, FAKE, FAKE,
+                                        tabp, tabp, FAKE, FAKE, FAKE, None, ring, ring_bytes, tabp, tabp, FAKE, FAKE,
                                         FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
     assert call(shape=_shape(dtype=moe.MOE_F32)) == -6                 # bf16 only
     assert call(ex=moe.Exec(96, 0, 0, 0, 0)) == -6                      # chunk must divide 256
@@ -237,7 +253,7 @@ def test_trace_is_rejected_outside_the_persistent_path():
     # the persistent path takes 0 or 1 only
     bad = moe.Exec(128, 0, 0, 2, 0)
     assert L.moe_forward_persistent(ctypes.byref(s), ctypes.byref(p), ctypes.byref(bad), tabp, tabp, FAKE, FAKE,
-                                    FAKE, FAKE, big, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big,
+                                    FAKE, None, FAKE, big, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big,
                                     None) == -1
 
 
@@ -249,7 +265,7 @@ def test_persistent_entry_rejects_a_partition_without_compute():
     tabp = ctypes.cast(tab, ctypes.c_void_p)
     ex = moe.Exec(128, 4096, 0, 0, 0)
     assert L.moe_forward_persistent(ctypes.byref(s), ctypes.byref(p), ctypes.byref(ex), tabp, tabp, FAKE, FAKE,
-                                    FAKE, FAKE, 1 << 40, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, None, FAKE, 1 << 40, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                     1 << 40, None) == -1
 
 
@@ -456,7 +472,7 @@ def test_reverse_ring_layout_and_rejection():
                          FAKE, None, FAKE, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == -1
     bad = moe.Exec(128, 0, 0, 0, 0, 2)
     assert L.moe_forward_persistent(ctypes.byref(s), ctypes.byref(p), ctypes.byref(bad), tabp, tabp, FAKE, FAKE,
-                                    FAKE, FAKE, big, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big,
+                                    FAKE, None, FAKE, big, tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big,
                                     None) == -1
 
 
@@ -484,3 +500,15 @@ def test_backward_ring_rejects_bad_arguments_before_launch():
     assert call(dlog=None) == -1
     assert call(exx=moe.Exec(96, 16, 0, 0, 0, 1)) == -6            # chunk must divide 256
     assert call(exx=moe.Exec(128, 16, 0, 0, 0, 2)) == -1
+
+
+def test_noalloc_entry_refuses_mxfp8_before_touching_the_device():
+    """The no-allocation entry point takes no weight scales: an MXFP8 shape is refused before
+    the device array is looked up."""
+    L = moe.lib()
+    s, p = _shape(dtype=moe.MOE_MXFP8), _pl()
+    tab = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    tabp = ctypes.cast(tab, ctypes.c_void_p)
+    rc = L.moe_forward_persistent_noalloc(ctypes.byref(s), ctypes.byref(p), None, tabp, tabp, FAKE, FAKE, FAKE,
+                                          tabp, tabp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert rc == -6

@@ -321,9 +321,12 @@ def test_mx_forward_full_dsv3_sampled():
 def _h_device(P, cfg, N):
     """The device's h of the unfused forward (MXFP8 codes [N][F] and block scale codes
     [N][F/32]) from the workspace's h staging, which starts where the persistent workspace
-    ends (the same layout: control words and tables first, h staging after them)."""
+    proper ends (the same layout: control words and tables first, h staging after them); in
+    MXFP8 the persistent workspace adds the per-pair recv address table (8 bytes a pair,
+    256-byte aligned) after its proper part."""
     F = cfg.F
-    hb = moe.moe_persistent_workspace_bytes(P.shape, P.placement)
+    table = (moe.moe_max_pairs(P.shape, P.placement) * 8 + 255) // 256 * 256
+    hb = moe.moe_persistent_workspace_bytes(P.shape, P.placement) - table
     nmax = P.nmax
     codes = P.ws[hb: hb + N * F].cpu().numpy().reshape(N, F)
     soff = hb + ((nmax * F + 255) // 256) * 256
