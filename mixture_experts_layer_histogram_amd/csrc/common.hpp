@@ -18,8 +18,8 @@ constexpr int kTokPerLayoutBlock = 64;   // tokens per histogram block of the la
 constexpr int kGemmBM = 256;             // rows of one grouped-GEMM tile (bf16 path)
 constexpr int kGemmBN = 256;             // output columns of one tile
 constexpr int kGemmBK = 64;              // K step staged in LDS
-constexpr int kSimtBM = 64;              // fp32 SIMT path tile
-constexpr int kSimtBN = 64;
+constexpr int kF32BM = 64;               // fp32 MFMA path tile (rows x columns)
+constexpr int kF32BN = 64;
 
 // ---------------------------------------------------------------------------
 // host: a kernel-attribute grant (hipFuncSetAttribute acts on the current device), done
@@ -64,7 +64,7 @@ inline WsLayout ws_layout(const moe_shape_t& s, int32_t E_local) {
   const int64_t tokens = int64_t(s.R) * s.T;
   w.nb = int32_t((tokens + kTokPerLayoutBlock - 1) / kTokPerLayoutBlock);
   w.max_pairs = tokens * (s.k < E_local ? s.k : E_local);
-  const int bm = (s.dtype == MOE_F32) ? kSimtBM : kGemmBM;
+  const int bm = (s.dtype == MOE_F32) ? kF32BM : kGemmBM;
   w.max_mtiles = int32_t((w.max_pairs + bm - 1) / bm + E_local);
   const size_t esz = (s.dtype == MOE_F32) ? 4 : 2;
   size_t o = 0;

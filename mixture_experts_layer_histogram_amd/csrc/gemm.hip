@@ -11,7 +11,7 @@
 // and ordered expert-major with the row tiles of one expert innermost, so the
 // workgroups sharing an XCD's L2 work on one expert's weights at a time.  Tile ->
 // (expert, row tile) comes from the layout's per-expert tile prefix on the device, so
-// the host never reads N.  The fp32 path (small shapes) is a plain SIMT kernel.
+// the host never reads N.  The fp32 path (small shapes) runs a smaller fp32-MFMA tile.
 #include "gemm_tile.hpp"
 
 namespace moe {
@@ -66,46 +66,84 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   }
 }
 
-// fp32 path (small shapes): 64 rows x 64 output columns per tile, 16 rows per thread
+// fp32 path (small shapes) on the fp32 MFMA (v_mfma_f32_32x32x2_f32): a 64-row x 64-column
+// output tile per 256-thread workgroup, wave w owning the 32 x 32 block (w >> 1, w & 1); in
+// MODE 0 each wave keeps a gate and an up accumulator for the same (row, f), so SwiGLU runs
+// in registers.  K steps of 32 staged in LDS (rows padded to 36 floats: a 16-lane
+// ds_read_b128 then touches 16 disjoint 4-bank groups); K past the end and rows past the
+// tile's end are filled with zeros / the last row.  Within a K step lane l of a wave feeds
+// k = 8 c + s (l < 32) or 8 c + 4 + s (l >= 32) to MFMA step s of 8-wide chunk c, so one
+// 16-byte LDS read per operand serves four MFMAs.
+constexpr int kF32BK = 32, kF32Pitch = kF32BK + 4;
+
 template <int MODE>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     const float* __restrict__ A, const float* __restrict__ B0, const float* __restrict__ B1,
     float* __restrict__ C, const int32_t* __restrict__ offsets, const int32_t* __restrict__ mtile_base,
     const int32_t* __restrict__ ctrl, int El, int K, int Nout, const uint64_t* __restrict__ RowDst,
     const uint64_t* __restrict__ RowSrc) {
-  const int NT = (Nout + kSimtBN - 1) / kSimtBN;
+  constexpr int kBRows = (MODE == 0) ? 2 * kF32BN : kF32BN;     // W1 rows then W3 rows
+  __shared__ __attribute__((aligned(16))) float sa[kF32BM * kF32Pitch];
+  __shared__ __attribute__((aligned(16))) float sb[kBRows * kF32Pitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, hi = lane >> 5;
+  const int NT = (Nout + kF32BN - 1) / kF32BN;
   const int total = ctrl[kCtrlMTiles] * NT;
-  const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
   for (int tau = blockIdx.x; tau < total; tau += gridDim.x) {
     const int mtg = tau / NT;
     const int nt = tau - mtg * NT;
     const int l = find_expert(mtile_base, El, mtg);
-    const int row0 = offsets[l] + (mtg - mtile_base[l]) * kSimtBM;
-    const int rows = min(kSimtBM, offsets[l + 1] - row0);
-    const int col = nt * kSimtBN + cl;
-    if (col >= Nout) continue;
-    float a[16], b[16];
+    const int row0 = offsets[l] + (mtg - mtile_base[l]) * kF32BM;
+    const int rows = min(kF32BM, offsets[l + 1] - row0);
+    const int c0 = nt * kF32BN;
+    const float* w0 = B0 + size_t(l) * Nout * K;
+    const float* w1 = (MODE == 0) ? B1 + size_t(l) * Nout * K : nullptr;
+    f32x16 acc0, acc1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) a[r] = b[r] = 0.0f;
-    const float* w0 = B0 + (size_t(l) * Nout + col) * K;
-    const float* w1 = (MODE == 0) ? B1 + (size_t(l) * Nout + col) * K : nullptr;
-    for (int kk = 0; kk < K; ++kk) {
-      const float u0 = w0[kk];
-      const float u1 = (MODE == 0) ? w1[kk] : 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = min(rg * 16 + r, rows - 1);
-        const float xv = RowSrc ? reinterpret_cast<const float*>(RowSrc[row0 + row])[kk] : A[size_t(row0 + row) * K + kk];
-        a[r] = fmaf(xv, u0, a[r]);
-        if (MODE == 0) b[r] = fmaf(xv, u1, b[r]);
+    for (int e = 0; e < 16; ++e) acc0[e] = acc1[e] = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += kF32BK) {
+      // fills: consecutive threads take consecutive k of one row (128-byte row segments)
+      for (int i = tid; i < kF32BM * kF32BK; i += 256) {
+        const int r = i / kF32BK, k = i - r * kF32BK;
+        const int row = min(r, rows - 1);
+        const float* src = RowSrc ? reinterpret_cast<const float*>(RowSrc[row0 + row]) : A + size_t(row0 + row) * K;
+        sa[r * kF32Pitch + k] = (k0 + k < K) ? src[k0 + k] : 0.0f;
       }
-    }
+      for (int i = tid; i < kBRows * kF32BK; i += 256) {
+        const int r = i / kF32BK, k = i - r * kF32BK;
+        const int n = min(c0 + (r % kF32BN), Nout - 1);
+        const float* src = (MODE == 0 && r >= kF32BN) ? w1 : w0;
+        sb[r * kF32Pitch + k] = (k0 + k < K) ? src[size_t(n) * K + k0 + k] : 0.0f;
+      }
+      __syncthreads();
+      const float* pa = sa + (wm * 32 + r32) * kF32Pitch + hi * 4;
+      const float* pb0 = sb + (wn * 32 + r32) * kF32Pitch + hi * 4;
+      const float* pb1 = pb0 + kF32BN * kF32Pitch;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = rg * 16 + r;
-      if (row < rows) {
-        float* dst = (MODE == 1 && RowDst) ? reinterpret_cast<float*>(RowDst[row0 + row]) : C + size_t(row0 + row) * Nout;
-        dst[col] = (MODE == 0) ? silu_f32(a[r]) * b[r] : a[r];
+      for (int c = 0; c < kF32BK / 8; ++c) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(pa + c * 8);
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(pb0 + c * 8);
+        f32x4 b1 = b0;
+        if (MODE == 0) b1 = *reinterpret_cast<const f32x4*>(pb1 + c * 8);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[st], b0[st], acc0, 0, 0, 0);
+          if (MODE == 0) acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[st], b1[st], acc1, 0, 0, 0);
+        }
+      }
+      __syncthreads();                         // the next fills overwrite the tiles
+    }
+    // lane l holds column wn * 32 + (l & 31), rows wm * 32 + 8 (e >> 2) + 4 (l >> 5) + (e & 3)
+    const int col = c0 + wn * 32 + r32;
+    if (col < Nout) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = wm * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+        if (row < rows) {
+          float* dst = (MODE == 1 && RowDst) ? reinterpret_cast<float*>(RowDst[row0 + row])
+                                              : C + size_t(row0 + row) * Nout;
+          dst[col] = (MODE == 0) ? silu_f32(acc0[e]) * acc1[e] : acc0[e];
+        }
       }
     }
   }

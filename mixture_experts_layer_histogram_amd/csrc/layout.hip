@@ -360,7 +360,7 @@ hipError_t launch_layout(const moe_shape_t& s, const int32_t* e2l, int El, int m
   else if (vpl_need <= 32) launch_topk<32>(grid, st, lp, s, topk_idx, topk_w, blockhist);
   else launch_topk<64>(grid, st, lp, s, topk_idx, topk_w, blockhist);
 
-  const int bm = (s.dtype == MOE_F32) ? kSimtBM : kGemmBM;
+  const int bm = (s.dtype == MOE_F32) ? kF32BM : kGemmBM;
   hipLaunchKernelGGL(layout_scan_kernel, dim3(1 + (s.E + 63) / 64), dim3(1024), 0, st, e2l, s.E, El,
                      L.nb, bm, mb, blockhist, blockbase, counts, offsets,
                      reinterpret_cast<int32_t*>(ws + L.l2g), reinterpret_cast<int32_t*>(ws + L.mtile_base),
