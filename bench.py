@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -117,10 +118,19 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and blank lines: what the compiler sees."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def gemm_source_sha(config) -> str:
+    """Hash of the kernels' sources (comments and blank lines left out, so that a comment
+    edit does not retire a counter record)."""
     h = hashlib.sha256()
     for f in TRAFFIC[config][2]:
-        h.update(open(os.path.join(CSRC, f), "rb").read())
+        h.update(_code_only(open(os.path.join(CSRC, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

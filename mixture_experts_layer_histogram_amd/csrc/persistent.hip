@@ -12,13 +12,14 @@
 // mover claims) are persist_sched.hpp, shared with a host-threaded model of this kernel.
 //
 // MI355X design:
-// * Launch.  An ordinary launch of one 512-thread workgroup per CU with 128 KiB of LDS (the
-//   launch shape of the grouped GEMM kernels).  No grid-wide barrier is used, so nothing
-//   needs a cooperative launch.  Roles go by arrival order inside a pipeline, so the first
-//   workgroups to run are the movers; compute workgroups take tickets in order and a task
-//   waits only for movers or smaller tickets, so progress does not depend on every
-//   workgroup being resident at once.  A compute workgroup whose pipeline has no ticket left
-//   joins the movers, so the last pushes (after the last GEMM) are spread over more CUs.
+// * Launch.  An ordinary launch of one 512-thread workgroup per CU with 128 KiB of LDS,
+//   132 KiB with MXFP8 weights (the launch shape of the grouped GEMM kernels).  No
+//   grid-wide barrier is used, so nothing needs a cooperative launch.  Roles go by
+//   arrival order inside a pipeline, so the first workgroups to run are the movers;
+//   compute workgroups take tickets in order and a task waits only for movers or smaller
+//   tickets, so progress does not depend on every workgroup being resident at once.  A
+//   compute workgroup whose pipeline has no ticket left joins the movers, so the last
+//   pushes (after the last GEMM) are spread over more CUs.
 // * Pipelines per XCD.  The eight XCDs' L2 caches are not coherent with one another, and an
 //   agent-scope release/acquire writes back / invalidates a whole L2.  With a ring large
 //   enough, the row tiles are split into eight pipelines, one per XCD (the kernel reads the
