@@ -721,6 +721,11 @@ def trace_summary(ev, tpu, grid):
             d = (e["t_end"] - e["t_begin"]) / tpu
             out["tasks"][name] = {"n": int(len(e)), "us_mean": float(d.mean()), "us_max": float(d.max()),
                                   "wait_us_mean": float((e["t_wait"] / tpu).mean())}
+    # down tiles a workgroup ran for another pipeline (work stealing at the end of a launch)
+    pipe_of = {int(w): int(q) for w, q in zip(starts["workgroup"], starts["pipeline"])}
+    dn = ev[ev["kind"] == 4]
+    out["stolen_down_tiles"] = int(sum(1 for w, q in zip(dn["workgroup"], dn["pipeline"])
+                                       if pipe_of.get(int(w), int(q)) != int(q)))
     # per pipeline: row tiles, end of its last GEMM and of its last task
     out["pipelines"] = []
     for p in np.unique(ev["pipeline"]):

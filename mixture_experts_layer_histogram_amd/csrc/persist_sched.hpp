@@ -216,6 +216,27 @@ MOE_HD int mover_claim(Ops& ops, const CtrlLayout& cl, int p, int lo, int n_m, i
   return kIdle;
 }
 
+// Work stealing at the end of a launch (outputs stored straight to recv, so a down tile
+// leaves nothing in the ring that its own pipeline must copy).  A compute workgroup whose
+// pipeline has handed out all its tickets takes tickets of another pipeline's last phase --
+// the down tiles of that pipeline's last group -- while there are any.  The last group's
+// gate/up tiles release their counters at agent scope, so the h rows a stolen down tile
+// reads are visible from another XCD.  A stolen ticket is an ordinary ticket of its
+// pipeline (claimed on the same counter), so every task still runs exactly once, and a
+// down tile waits only for gate/up tiles with smaller tickets: stealing adds no wait.
+// One attempt on pipeline v: the ticket, kStealWait if v's next ticket is not in its last
+// phase yet (or the CAS lost a race), kStealDone if v has no ticket left.
+constexpr int kStealWait = -1, kStealDone = -2;
+
+template <class Ops>
+MOE_HD int steal_claim(Ops& ops, const CtrlLayout& cl, int v, int last_phase_start, int n_tickets) {
+  const int w = cl.pipe0 + v * kPipeWords + kTicketNext;
+  const int t = ops.ld(w);
+  if (t >= n_tickets) return kStealDone;
+  if (t < last_phase_start) return kStealWait;
+  return ops.cas(w, t, t + 1) ? t : kStealWait;
+}
+
 // ---------------------------------------------------------------------------- host plan
 // Pipelines, ring partition and roles for one launch.
 struct Plan {

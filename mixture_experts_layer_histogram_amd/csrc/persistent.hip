@@ -76,6 +76,7 @@ struct PersistArgs {
   int blk_log2, cpm;            // chunk rows (log2) and chunks per 256-row tile
   int n_part, light, comm_pp, S, G, lookahead;
   int reverse;                  // 1: reverse ring (pipelines walk their row tiles backwards)
+  int steal;                    // 1: compute workgroups out of tickets take other pipelines' last down tiles
   int max_mtiles;               // entries of the resident record: 4 per row tile
   const uint64_t* row_dst;      // reverse ring and MXFP8: per local pair, the address of its recv row
   // MXFP8: weight codes and scales (the MXFP8 scale layout over each weight matrix's
@@ -118,6 +119,21 @@ __device__ __forceinline__ void release_add(int32_t* ctr, int v, bool light) {
     if (light) __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// A gate/up tile of a row tile another XCD may take down tiles of (work stealing): the light
+// hand-off as above, and the tile that completes the row tile (the counter reaches `target`)
+// then writes back its XCD's L2 -- every gate/up tile of the row tile ran on this XCD, so
+// that one write-back publishes all their h rows -- and adds 1 more, the mark a down tile
+// on another XCD waits for (target + 1).
+__device__ __forceinline__ void release_add_publish(int32_t* ctr, int target, int* sh_flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == target - 1) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  (void)sh_flag;
 }
 
 // Consumer side, after the workgroup observed the counter: make the producer's data visible.
@@ -428,6 +444,40 @@ __device__ void do_push(const PersistArgs& A, const PipeCtx& c, int q, char* sme
 // A compute workgroup waits until every chunk of row tile m is in its slot; meanwhile it
 // gathers claimable chunks of its pipeline itself (a gather never waits, so this cannot
 // deadlock).  Returns false on abort or watchdog expiry.
+// Work stealing at the end of a launch (bf16 with outputs stored straight to recv;
+// persist_sched.hpp states the rule).  Thread 0 only: polls the other pipelines (those some
+// workgroup joined) for a ticket in their last phase.  0: *tp / *t hold the ticket; 1: every
+// other pipeline has handed out all its tickets; 2: abort or watchdog.
+__device__ int steal_next(const PersistArgs& A, int p, int* tp, int* t) {
+  const DevOps ops{A.pc};
+  const long long t0 = wall_clock64();
+  while (true) {
+    if (ld_relaxed(A.pc + A.cl.abort_word)) return 2;
+    bool pending = false;
+    for (int k = 1; k < A.n_part; ++k) {
+      const int v = p + k < A.n_part ? p + k : p + k - A.n_part;
+      const int32_t* vw = A.pc + A.cl.pipe0 + v * sched::kPipeWords;
+      if (ld_relaxed(vw + sched::kJoin) == 0) continue;
+      const int ng = vw[sched::kNGroups], nt = vw[sched::kNTickets];    // written by the preparation kernel
+      if (ng == 0) continue;
+      const int last = A.pc[A.cl.phase_start + 2 * vw[sched::kLo] + v + 2 * ng - 1];
+      const int r = sched::steal_claim(ops, A.cl, v, last, nt);
+      if (r >= 0) {
+        *tp = v;
+        *t = r;
+        return 0;
+      }
+      if (r == sched::kStealWait) pending = true;
+    }
+    if (!pending) return 1;
+    __builtin_amdgcn_s_sleep(2);
+    if (wall_clock64() - t0 > A.budget) {
+      set_abort(A, MOE_ETIMEOUT);
+      return 2;
+    }
+  }
+}
+
 template <bool MX>
 __device__ bool wait_chunks(const PersistArgs& A, const PipeCtx& c, int m, char* smem, int* sh) {
   const DevOps ops{A.pc};
@@ -518,30 +568,76 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
     const int32_t* phase_start = A.pc + A.cl.phase_start + 2 * lo + p;
     const int32_t* grp_first = A.pc + A.cl.grp_first + lo;
     const int32_t* grp_len = A.pc + A.cl.grp_len + lo;
+    // with stealing on, the gate/up tiles of this pipeline's last group release at agent
+    // scope: another XCD may run the down tiles that read their h rows
+    const int last_first = n_groups > 0 ? grp_first[n_groups - 1] : lo;
+    bool own_left = true;                                  // thread 0's view
     while (true) {
-      if (tid == 0) sh[3] = __hip_atomic_fetch_add(pw + sched::kTicketNext, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) {
+        int st = 0, tp = p, t = -1;                        // st: 0 task, 1 none left, 2 abort
+        if (own_left) {
+          t = __hip_atomic_fetch_add(pw + sched::kTicketNext, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (t >= n_tickets) own_left = false;
+        }
+        if (!own_left) {
+          st = 1;
+          if constexpr (!MX) {
+            if (A.steal) st = steal_next(A, p, &tp, &t);
+          }
+        }
+        sh[1] = st;
+        sh[2] = tp;
+        sh[3] = t;
+      }
       __syncthreads();
-      const int ticket = sh[3];
+      const int st = sh[1], tp = sh[2], ticket = sh[3];
       __syncthreads();
-      if (ticket >= n_tickets) break;
-      const sched::Task tk = sched::task_of_ticket(ticket, n_groups, phase_start, grp_first, grp_len, A.lookahead != 0);
+      if (st == 2) {
+        aborted = true;
+        break;
+      }
+      if (st == 1) break;
+      // the ticket's pipeline: another one for a stolen ticket (a down tile of its last group)
+      PipeCtx cv = c;
+      const int32_t* t_ps = phase_start;
+      const int32_t* t_gf = grp_first;
+      const int32_t* t_gl = grp_len;
+      int t_ng = n_groups;
+      bool remote = false;
+      if constexpr (!MX) {
+        if (tp != p) {
+          const int32_t* vw = A.pc + A.cl.pipe0 + tp * sched::kPipeWords;
+          cv.p = tp;
+          cv.lo = vw[sched::kLo];
+          cv.n_m = vw[sched::kHi] - cv.lo;
+          t_ng = vw[sched::kNGroups];
+          t_ps = A.pc + A.cl.phase_start + 2 * cv.lo + tp;
+          t_gf = A.pc + A.cl.grp_first + cv.lo;
+          t_gl = A.pc + A.cl.grp_len + cv.lo;
+          remote = true;
+        }
+      }
+      const sched::Task tk = sched::task_of_ticket(ticket, t_ng, t_ps, t_gf, t_gl, A.lookahead != 0);
       const int m = tk.m;                                   // pipeline order
-      const int ml = layout_tile(A.reverse, lo, c.n_m, m);   // layout row tile
+      const int ml = layout_tile(A.reverse, cv.lo, cv.n_m, m);   // layout row tile
       int row0, l;
       const int rows = tile_rows(A, ml, &row0, &l);
       const long long t_w = wall_clock64();
-      const bool ok = !tk.down ? wait_chunks<MX>(A, c, m, smem, sh) : wait_ge(g1_done + m, NT1, A, sh);
+      // (a stolen down tile waits for the publishing mark of its row tile's gate/up tiles when
+      // they handed off L2-locally)
+      const bool ok = !tk.down ? wait_chunks<MX>(A, cv, m, smem, sh)
+                               : wait_ge(g1_done + m, NT1 + ((remote && light) ? 1 : 0), A, sh);
       if (!ok) {
         aborted = true;
         break;
       }
       const long long t_b = wall_clock64();
-      acquire_after_poll(light);
-      const int q0 = (m - lo) * cpm;
-      char* s0 = slot_ptr(A, c, q0);
-      char* s1 = slot_ptr(A, c, q0 + min(1, cpm - 1));
-      char* s2 = slot_ptr(A, c, q0 + min(2, cpm - 1));
-      char* s3 = slot_ptr(A, c, q0 + min(3, cpm - 1));
+      acquire_after_poll(light && !remote);                // a stolen tile's h came through another L2
+      const int q0 = (m - cv.lo) * cpm;
+      char* s0 = slot_ptr(A, cv, q0);
+      char* s1 = slot_ptr(A, cv, q0 + min(1, cpm - 1));
+      char* s2 = slot_ptr(A, cv, q0 + min(2, cpm - 1));
+      char* s3 = slot_ptr(A, cv, q0 + min(3, cpm - 1));
       if constexpr (MX) {
         // the tile's rows are the chunks' slots: token codes / scale words for the gate/up
         // GEMM, h codes / scale words for the down GEMM, whose outputs go straight to recv
@@ -600,7 +696,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
           const uint16_t* b0 = A.w1 + size_t(l) * A.F * A.d;
           const uint16_t* b1 = A.w3 + size_t(l) * A.F * A.d;
           gemm_tile<0, 16>(io, b0, b1, tk.j * (kGemmBN / 2), A.F, A.d, smem, A.d);   // x rows: sc1 loads
-          release_add(g1_done + m, 1, light);
+          if (A.steal && m >= last_first && light) release_add_publish(g1_done + m, NT1, sh);
+          else release_add(g1_done + m, 1, light);
           trace_event(A, 3, ml * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
         } else {
           io.a0 = reinterpret_cast<const uint16_t*>(s0 + xpart);
@@ -616,8 +713,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
           if (A.row_dst) io.row_dst = A.row_dst + row0;       // outputs straight to recv
           const uint16_t* b0 = A.w2 + size_t(l) * A.d * A.F;
           gemm_tile<1, 16>(io, b0, b0, tk.j * kGemmBN, A.d, A.F, smem, A.F);         // h rows: sc1 loads
-          release_add(g2_done + m, 1, light);
-          trace_event(A, 4, ml * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
+          release_add(g2_done + m, 1, light && !remote);
+          trace_event(A, 4, ml * 256 + tk.j, tp, t_b, wall_clock64(), t_b - t_w);
         }
       }
     }
@@ -752,6 +849,9 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
     A.w2s = w_scales->w2;
     persist_mx_slot_layout(s.d, s.F, 1 << blk_log2, &A.tok_s_off, &A.h_off, &A.h_s_off);
   }
+  // work stealing at the end of the launch: bf16 with the outputs stored straight to recv,
+  // and more than one pipeline
+  A.steal = (!A.mx && row_dst && plan.n_part > 1) ? 1 : 0;
 
   int occ = 0;
   hipError_t e = persistent_occupancy(&occ, A.mx != 0);

@@ -10,7 +10,9 @@
 //   * a down tile starts only after every gate/up tile of its row tile finished;
 //   * a push starts only after every down tile of its row tile finished, while the slots
 //     still hold that row tile;
-//   * every chunk, task and push runs exactly once, and every run ends (no deadlock).
+//   * every chunk, task and push runs exactly once, and every run ends (no deadlock),
+//     also when workgroups out of tickets take down tiles of other pipelines' last groups;
+//   * a stolen ticket is a down tile of its pipeline's last group.
 // It also checks the completion rule of the check kernel: a pipeline that receives no
 // workgroup is reported, one that receives workgroups never is.
 //
@@ -33,6 +35,7 @@ using namespace moe::sched;
 namespace {
 
 constexpr int kBM = 256;
+std::atomic<long long> g_stolen{0};   // down tiles run by another pipeline's workgroups, all cases
 
 struct Fail {
   std::mutex mu;
@@ -52,6 +55,7 @@ struct Case {
   long long slots;
   std::vector<int> counts;         // rows per local expert
   bool drop_pipeline;              // give one pipeline no workgroup at all
+  bool steal;                      // workgroups out of tickets take other pipelines' last down tiles
 };
 
 struct Ops {
@@ -190,6 +194,72 @@ struct Model {
     }
   }
 
+  // what the kernel's compute workgroups do once their own tickets are exhausted: take
+  // down-tile tickets of other pipelines' last phases (pipelines no workgroup joined are
+  // skipped) until every other pipeline has handed out all its tickets
+  bool steal_loop(int p, std::mt19937& rng) {
+    Ops ops{pc.data()};
+    auto t0 = std::chrono::steady_clock::now();
+    while (true) {
+      if (abort_flag.load()) return false;
+      bool pending = false;
+      int sv = -1, st = -1;
+      for (int k = 1; k < plan.n_part && st < 0; ++k) {
+        const int v = (p + k) % plan.n_part, vb = cl.pipe0 + v * kPipeWords;
+        if (pc[vb + kJoin].load() == 0) continue;
+        const int ng = pc[vb + kNGroups].load(), nt = pc[vb + kNTickets].load();
+        if (!ng) continue;
+        const int vlo = pc[vb + kLo].load();
+        const int last = pc[cl.phase_start + 2 * vlo + v + 2 * ng - 1].load();
+        const int r = steal_claim(ops, cl, v, last, nt);
+        if (r >= 0) {
+          sv = v;
+          st = r;
+        } else if (r == kStealWait) {
+          pending = true;
+        }
+      }
+      if (st >= 0) {
+        const int vb = cl.pipe0 + sv * kPipeWords;
+        const int ng = pc[vb + kNGroups].load(), vlo = pc[vb + kLo].load(), vhi = pc[vb + kHi].load();
+        std::vector<int> ps(2 * ng + 1), gf(ng), gl(ng);
+        for (int k = 0; k <= 2 * ng; ++k) ps[k] = pc[cl.phase_start + 2 * vlo + sv + k].load();
+        for (int g = 0; g < ng; ++g) {
+          gf[g] = pc[cl.grp_first + vlo + g].load();
+          gl[g] = pc[cl.grp_len + vlo + g].load();
+        }
+        const Task tk = task_of_ticket(st, ng, ps.data(), gf.data(), gl.data(), plan.lookahead != 0);
+        const int m = tk.m;
+        if (!tk.down) fail->add("a stolen ticket is not a down tile");
+        if (m < vlo || m >= vhi) fail->add("a stolen ticket maps outside its pipeline's row tiles");
+        if (m < gf[ng - 1]) fail->add("a stolen ticket is not in its pipeline's last group");
+        // with L2-local hand-offs the last gate/up tile of the row tile publishes its h rows
+        // and adds a mark: a down tile on another XCD waits for NT1 + 1
+        if (!wait_ge(cl.g1_done + m, c.NT1 + (plan.light ? 1 : 0))) return false;
+        for (int h = 0; h < c.cpm; ++h) {
+          const int q = (m - vlo) * c.cpm + h;
+          if (slot_occ[sv * plan.S + chunk_slot(q, plan.S)].load() != q || !gathered[m * 4 + h].load())
+            fail->add("stolen down tile on a row tile whose chunks are not all in their slots");
+        }
+        if (u_done[m].load() != c.NT1) fail->add("stolen down tile before all gate/up tiles finished");
+        delay(rng, 20);
+        d_runs[m * 64 + tk.j].fetch_add(1);
+        d_done[m].fetch_add(1);
+        pc[cl.g2_done + m].fetch_add(1, std::memory_order_release);
+        g_stolen.fetch_add(1);
+        t0 = std::chrono::steady_clock::now();
+        continue;
+      }
+      if (!pending) return true;
+      std::this_thread::yield();
+      if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(10)) {
+        fail->add("watchdog: a stealing workgroup waited 10 s (deadlock)");
+        abort_flag.store(1);
+        return false;
+      }
+    }
+  }
+
   void workgroup(int p, unsigned wseed) {
     std::mt19937 rng(wseed);
     const int pb = cl.pipe0 + p * kPipeWords;
@@ -225,13 +295,16 @@ struct Model {
         if (!tk.down) {
           u_runs[m * 64 + tk.j].fetch_add(1);
           u_done[m].fetch_add(1);
-          pc[cl.g1_done + m].fetch_add(1, std::memory_order_release);
+          const int old = pc[cl.g1_done + m].fetch_add(1, std::memory_order_release);
+          if (c.steal && plan.n_part > 1 && plan.light && m >= gf[n_groups - 1] && old == c.NT1 - 1)
+            pc[cl.g1_done + m].fetch_add(1, std::memory_order_release);      // the publishing mark
         } else {
           d_runs[m * 64 + tk.j].fetch_add(1);
           d_done[m].fetch_add(1);
           pc[cl.g2_done + m].fetch_add(1, std::memory_order_release);
         }
       }
+      if (c.steal && plan.n_part > 1 && !steal_loop(p, rng)) return;
     }
     auto idle_since = std::chrono::steady_clock::now();
     while (true) {
@@ -280,6 +353,7 @@ Case random_case(std::mt19937& rng) {
   c.slots = c.cpm + int(rng() % 60);
   c.wg_per_pipe_override = 0;
   c.drop_pipeline = false;
+  c.steal = rng() % 2 != 0;
   c.counts.resize(c.El);
   const int hot = int(rng() % c.El);
   for (int l = 0; l < c.El; ++l) {
@@ -369,8 +443,9 @@ int run_case(const Case& cs, unsigned seed, Fail& fail) {
 
 std::string describe(const Case& c) {
   char buf[256];
-  std::snprintf(buf, sizeof buf, "El=%d cpm=%d NT1=%d NT2=%d cus=%d eight_xcds=%d comm=%d slots=%lld drop=%d rows=[",
-                c.El, c.cpm, c.NT1, c.NT2, c.cus, int(c.eight_xcds), c.comm, c.slots, int(c.drop_pipeline));
+  std::snprintf(buf, sizeof buf,
+                "El=%d cpm=%d NT1=%d NT2=%d cus=%d eight_xcds=%d comm=%d slots=%lld drop=%d steal=%d rows=[", c.El,
+                c.cpm, c.NT1, c.NT2, c.cus, int(c.eight_xcds), c.comm, c.slots, int(c.drop_pipeline), int(c.steal));
   std::string s = buf;
   for (int v : c.counts) s += std::to_string(v) + ",";
   return s + "]";
@@ -391,7 +466,14 @@ int main(int argc, char** argv) {
     Case c{};
     c.El = 32; c.cpm = 2; c.NT1 = 4; c.NT2 = 4; c.cus = 256; c.eight_xcds = true; c.comm = 16; c.slots = 113;
     c.counts.assign(32, 1024);
+    c.steal = true;
     fixed.push_back(c);
+    c.steal = false;
+    fixed.push_back(c);
+    c.steal = true;
+    for (int l = 0; l < 32; ++l) c.counts[l] = 1024 + 37 * ((l * 7) % 11) - 180;   // uneven pipelines
+    fixed.push_back(c);
+    c.counts.assign(32, 1024);
     c.slots = 2;           // one row tile of ring: one pipeline, no look-ahead
     c.cus = 24;
     fixed.push_back(c);
@@ -410,6 +492,6 @@ int main(int argc, char** argv) {
     }
     ++run;
   }
-  std::printf("OK %d\n", run);
+  std::printf("OK %d (stolen down tiles: %lld)\n", run, g_stolen.load());
   return 0;
 }

@@ -28,7 +28,9 @@ def model(tmp_path_factory):
 @pytest.mark.parametrize("seed", [1, 2, 3, 4])
 def test_protocol_random_layouts(model, seed):
     """Random expert loads (empty, one-row, partial and hot experts), ring sizes from one row
-    tile up, 1..8 pipelines, uneven data-movement shares, and dropped pipelines."""
+    tile up, 1..8 pipelines, uneven data-movement shares, dropped pipelines, and work stealing
+    at the end of a launch on or off."""
     r = subprocess.run([model, str(seed), "150"], capture_output=True, text=True, timeout=240)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.startswith("OK"), r.stdout
+    assert int(r.stdout.split("stolen down tiles: ")[1].split(")")[0]) > 0, r.stdout   # stealing happened
