@@ -126,14 +126,13 @@ __device__ __forceinline__ void release_add(int32_t* ctr, int v, bool light) {
 // then writes back its XCD's L2 -- every gate/up tile of the row tile ran on this XCD, so
 // that one write-back publishes all their h rows -- and adds 1 more, the mark a down tile
 // on another XCD waits for (target + 1).
-__device__ __forceinline__ void release_add_publish(int32_t* ctr, int target, int* sh_flag) {
+__device__ __forceinline__ void release_add_publish(int32_t* ctr, int target) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == target - 1) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   }
-  (void)sh_flag;
 }
 
 // Consumer side, after the workgroup observed the counter: make the producer's data visible.
@@ -696,7 +695,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
           const uint16_t* b0 = A.w1 + size_t(l) * A.F * A.d;
           const uint16_t* b1 = A.w3 + size_t(l) * A.F * A.d;
           gemm_tile<0, 16>(io, b0, b1, tk.j * (kGemmBN / 2), A.F, A.d, smem, A.d);   // x rows: sc1 loads
-          if (A.steal && m >= last_first && light) release_add_publish(g1_done + m, NT1, sh);
+          if (A.steal && m >= last_first && light) release_add_publish(g1_done + m, NT1);
           else release_add(g1_done + m, 1, light);
           trace_event(A, 3, ml * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
         } else {
