@@ -326,8 +326,8 @@ int moe_forward_fused(const moe_shape_t* s, const moe_placement_t* p, const moe_
  * they gather chunks of token rows from the source buffers into free ring slots and push
  * finished output rows to recv chunk by chunk, freeing the slots -- and the others take
  * GEMM tasks in ticket order (gathering claimable chunks themselves while a task waits for
- * its rows), then join the data movement once their pipeline has no task left -- in bf16
- * with the outputs stored straight to recv (reverse_ring = 1) they first take down-tile
+ * its rows), then join the data movement once their pipeline has no task left -- with the
+ * outputs stored straight to recv (reverse_ring = 1, or MXFP8) they first take down-tile
  * tasks of other pipelines' last groups while there are any (work stealing across XCDs).
  * Row tiles (256 rows of one expert) are split evenly over the pipelines:
  * eight (one per XCD, every hand-off inside one L2) when each XCD's share of the ring holds

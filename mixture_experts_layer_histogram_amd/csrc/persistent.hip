@@ -443,8 +443,8 @@ __device__ void do_push(const PersistArgs& A, const PipeCtx& c, int q, char* sme
 // A compute workgroup waits until every chunk of row tile m is in its slot; meanwhile it
 // gathers claimable chunks of its pipeline itself (a gather never waits, so this cannot
 // deadlock).  Returns false on abort or watchdog expiry.
-// Work stealing at the end of a launch (bf16 with outputs stored straight to recv;
-// persist_sched.hpp states the rule).  Thread 0 only: polls the other pipelines (those some
+// Work stealing at the end of a launch (outputs stored straight to recv; persist_sched.hpp
+// states the rule).  Thread 0 only: polls the other pipelines (those some
 // workgroup joined) for a ticket in their last phase.  0: *tp / *t hold the ticket; 1: every
 // other pipeline has handed out all its tickets; 2: abort or watchdog.
 __device__ int steal_next(const PersistArgs& A, int p, int* tp, int* t) {
@@ -580,9 +580,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
         }
         if (!own_left) {
           st = 1;
-          if constexpr (!MX) {
-            if (A.steal) st = steal_next(A, p, &tp, &t);
-          }
+          if (A.steal) st = steal_next(A, p, &tp, &t);
         }
         sh[1] = st;
         sh[2] = tp;
@@ -603,7 +601,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
       const int32_t* t_gl = grp_len;
       int t_ng = n_groups;
       bool remote = false;
-      if constexpr (!MX) {
+      {
         if (tp != p) {
           const int32_t* vw = A.pc + A.cl.pipe0 + tp * sched::kPipeWords;
           cv.p = tp;
@@ -658,7 +656,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
           const uint8_t* b1 = A.w3q + size_t(l) * A.F * A.d;
           gemm_mx_tile<0, 16, true>(io, b0, b1, A.w1s + 4 * size_t(l) * A.F, A.w3s + 4 * size_t(l) * A.F,
                                     4LL * A.El * A.F, tk.j * (kGemmBN / 2), A.F, A.d, smem);
-          release_add(g1_done + m, 1, light);
+          if (A.steal && m >= last_first && light) release_add_publish(g1_done + m, NT1);
+          else release_add(g1_done + m, 1, light);
           trace_event(A, 3, ml * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
         } else {
 #pragma unroll
@@ -670,8 +669,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_persistent_kernel(Persist
           const uint8_t* b0 = A.w2q + size_t(l) * A.d * A.F;
           const uint8_t* bs0 = A.w2s + 4 * size_t(l) * A.d;
           gemm_mx_tile<1, 16, true>(io, b0, b0, bs0, bs0, 4LL * A.El * A.d, tk.j * kGemmBN, A.d, A.F, smem);
-          release_add(g2_done + m, 1, light);
-          trace_event(A, 4, ml * 256 + tk.j, p, t_b, wall_clock64(), t_b - t_w);
+          release_add(g2_done + m, 1, light && !remote);
+          trace_event(A, 4, ml * 256 + tk.j, tp, t_b, wall_clock64(), t_b - t_w);
         }
       } else {
         TileIO io;
@@ -848,9 +847,9 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
     A.w2s = w_scales->w2;
     persist_mx_slot_layout(s.d, s.F, 1 << blk_log2, &A.tok_s_off, &A.h_off, &A.h_s_off);
   }
-  // work stealing at the end of the launch: bf16 with the outputs stored straight to recv,
-  // and more than one pipeline
-  A.steal = (!A.mx && row_dst && plan.n_part > 1) ? 1 : 0;
+  // work stealing at the end of the launch: outputs stored straight to recv, and more than
+  // one pipeline
+  A.steal = (row_dst && plan.n_part > 1) ? 1 : 0;
 
   int occ = 0;
   hipError_t e = persistent_occupancy(&occ, A.mx != 0);
