@@ -192,6 +192,39 @@ def test_persistent_full_share(cfg):
     _say(f"  N={lay['N']} hottest local/mean={cnt.max() / cnt.mean():.2f}")
 
 
+def test_work_stealing_full_share():
+    """The reverse ring at the full share with the Zipf load (143 row tiles over eight
+    pipelines, so some own one more than others): compute workgroups whose pipeline has no
+    ticket left run down tiles of other pipelines' last groups (seen in the trace: a down
+    tile recorded under a pipeline other than its workgroup's), and the outputs stay
+    bit-identical to the unfused path."""
+    import torch
+    cfg = configs.DSV3_SKEW
+    _say(f"[persistent-steal] {cfg.name}")
+    inp, P, ref = _reference(cfg)
+    ex = moe.Exec(128, 8, 0, 1, 0, 1)                # trace on, reverse ring, 8 movers
+    P.alloc_ring(cfg.ring_mib, ex)
+    ws = torch.zeros(moe.moe_persistent_workspace_bytes(P.shape, P.placement, ex), dtype=torch.uint8,
+                     device=P.device)
+    for t in P.y:
+        t.fill_(7.0)
+    for t in P.recv:
+        t.fill_(-3.0)
+    moe.moe_forward_persistent(P.shape, P.placement, ex, P.logits, P.x, P.w1, P.w3, P.w2, P.ring, P.recv, P.y,
+                               P.topk_idx, P.topk_w, P.counts, P.offsets, P.pull_src, P.slot_of, ws)
+    assert moe.moe_read_status(ws) == 0
+    _assert_same(P, ref)
+    ev, tpu = moe.read_trace(ws, P.shape, P.placement, ex)
+    starts = ev[ev["kind"] == 0]
+    pipe_of = {int(w): int(q) for w, q in zip(starts["workgroup"], starts["pipeline"])}
+    dn = ev[ev["kind"] == 4]
+    stolen = sum(1 for w, q in zip(dn["workgroup"], dn["pipeline"]) if pipe_of[int(w)] != int(q))
+    ends = [int(ev[ev["pipeline"] == q]["t_end"].max()) for q in np.unique(ev["pipeline"])]
+    _say(f"  stolen down tiles {stolen} of {len(dn)}; pipelines end within {(max(ends) - min(ends)) / tpu:.0f} us")
+    assert stolen > 0
+    assert len(dn) == int(np.sum((P.counts.cpu().numpy()[:cfg.E_local] + 255) // 256)) * (cfg.d // 256)
+
+
 REVERSE_CASES = [
     # (config, minibatch, comm_cus, ring_slots, ring MiB)
     ("small", 128, 0, 0, 16),          # eight pipelines; the ring holds every chunk
