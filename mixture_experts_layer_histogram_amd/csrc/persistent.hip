@@ -251,15 +251,25 @@ __device__ void wg_copy_rows(const uint64_t* src, const uint64_t* dst, int nrows
 
 // Zero the control block and build every pipeline's group and phase tables (one block; the
 // per-expert row-tile prefix is staged in LDS first, so the group walk reads no global memory).
+// The local expert of every row tile is looked up by all threads at once (when the tiles
+// fit in LDS), so the per-pipeline threads that build the groups read it with one LDS load
+// instead of each running a binary search per tile.
+constexpr int kPrepLdsTiles = 8192;
+
 __global__ __launch_bounds__(1024) void persist_prep_kernel(PersistArgs A, int zero_words) {
   __shared__ int32_t mtb[1025];                 // E_local <= E <= 1024
+  __shared__ int16_t s_exp[kPrepLdsTiles];      // local expert of row tile m (E_local <= 1024)
   for (int i = threadIdx.x; i < zero_words; i += blockDim.x) A.pc[i] = 0;
   for (int i = threadIdx.x; i <= A.El; i += blockDim.x) mtb[i] = A.mtile_base[i];
   if (A.trace && threadIdx.x == 0) *A.trace_count = 0;
+  const int n_mt = A.ctrl[kCtrlMTiles];
+  const bool in_lds = n_mt <= kPrepLdsTiles;
+  __syncthreads();
+  if (in_lds)
+    for (int m = threadIdx.x; m < n_mt; m += blockDim.x) s_exp[m] = int16_t(find_expert(mtb, A.El, m));
   __syncthreads();
   const int p = threadIdx.x;
   if (p >= A.n_part) return;
-  const int n_mt = A.ctrl[kCtrlMTiles];
   int lo, hi;
   sched::pipe_range(n_mt, A.n_part, p, &lo, &hi);
   int32_t* gf = A.pc + A.cl.grp_first + lo;
@@ -267,7 +277,12 @@ __global__ __launch_bounds__(1024) void persist_prep_kernel(PersistArgs A, int z
   const int El = A.El;
   const int rev = A.reverse, n_m = hi - lo;
   const int n = sched::build_groups(
-      lo, hi, A.G, [&](int m) { return find_expert(mtb, El, layout_tile(rev, lo, n_m, m)); }, gf, gl);
+      lo, hi, A.G,
+      [&](int m) {
+        const int ml = layout_tile(rev, lo, n_m, m);
+        return in_lds ? int(s_exp[ml]) : find_expert(mtb, El, ml);
+      },
+      gf, gl);
   const int NT1 = (A.F + kGemmBN / 2 - 1) / (kGemmBN / 2);
   const int NT2 = (A.d + kGemmBN - 1) / kGemmBN;
   const int tickets = n ? sched::build_phases(n, gl, NT1, NT2, A.lookahead != 0, A.pc + A.cl.phase_start + 2 * lo + p)
@@ -283,8 +298,8 @@ __global__ __launch_bounds__(1024) void persist_prep_kernel(PersistArgs A, int z
 // tickets; otherwise (and unless a watchdog already reported) MOE_EINCOMPLETE.  Then the
 // record of the chunks the ring still holds (reverse ring only, and only after a clean run:
 // pipeline p's last S chunks in its order, each in slot q mod S, never overwritten).  One
-// block of 64 threads.
-__global__ void persist_check_kernel(PersistArgs A) {
+// block of 1024 threads; the first wave holds one thread per pipeline.
+__global__ __launch_bounds__(1024) void persist_check_kernel(PersistArgs A) {
   const int p = threadIdx.x;
   bool bad = false;
   if (p < A.n_part) {
@@ -293,7 +308,7 @@ __global__ void persist_check_kernel(PersistArgs A) {
     bad = pw[sched::kGatherNext] < n_m * A.cpm || pw[sched::kPushNext] < n_m * A.cpm ||
           pw[sched::kTicketNext] < pw[sched::kNTickets];
   }
-  const bool any_bad = __any(bad);
+  const bool any_bad = __any(bad);              // pipelines <= 8: all in wave 0
   if (any_bad && threadIdx.x == 0 && *A.status == MOE_OK) *A.status = MOE_EINCOMPLETE;
   int32_t* res = A.pc + A.cl.resident;
   for (int i = threadIdx.x; i < A.max_mtiles * 4; i += blockDim.x) res[i] = 0;
@@ -864,7 +879,7 @@ hipError_t launch_persistent(const moe_shape_t& s, int El, const void* const* x,
     hipLaunchKernelGGL(moe_persistent_kernel<false>, dim3(grid), dim3(kGemmThreads), kGemmLds, st, A);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(persist_check_kernel, dim3(1), dim3(64), 0, st, A);
+  hipLaunchKernelGGL(persist_check_kernel, dim3(1), dim3(1024), 0, st, A);
   return hipGetLastError();
 }
 
