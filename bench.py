@@ -231,7 +231,7 @@ def write_traffic(config, fetch_csv, write_csv):
         else:
             g = {}
             for mode in (0, 1):
-                vals = [v for k, v in rows if f"{kname}<{mode}>" in k]
+                vals = [v for k, v in rows if re.search(rf"{kname}<{mode}[,>]", k)]
                 g[mode] = float(np.median(vals)) * factor
             rec[name] = {"copy_factor": factor, "gemm1_bytes": g[0], "gemm2_bytes": g[1]}
     if persistent:

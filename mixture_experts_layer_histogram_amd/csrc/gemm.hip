@@ -21,7 +21,8 @@ namespace moe {
 //         with RowDst each row s to the address RowDst[s] instead (the push fused in)
 // RowSrc (any MODE): A row s read from the address RowSrc[s] instead (the pull fused in)
 // MODE 2: as MODE 0, with the backward epilogue: DH in, C = h, DAB = [da | db] out
-template <int MODE>
+// ROWSRC: A rows by address (RowSrc, the pull fused in) instead of from A
+template <int MODE, bool ROWSRC>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
     uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, const int32_t* __restrict__ mtile_base,
@@ -59,10 +60,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     io.dh = (MODE == 2) ? DH + size_t(row0) * Nout : nullptr;
     io.dab = (MODE == 2) ? DAB + size_t(row0) * 2 * Nout : nullptr;
     io.row_dst = (MODE == 1 && RowDst) ? RowDst + row0 : nullptr;
-    io.row_src = RowSrc ? RowSrc + row0 : nullptr;
+    io.row_src = ROWSRC ? RowSrc + row0 : nullptr;
     const uint16_t* b0 = B0 + size_t(l) * Nout * K;
     const uint16_t* b1 = (MODE != 1) ? B1 + size_t(l) * Nout * K : b0;
-    gemm_tile<MODE>(io, b0, b1, nt * cols_per_tile, Nout, K, smem, K);
+    gemm_tile<MODE, 0, ROWSRC>(io, b0, b1, nt * cols_per_tile, Nout, K, smem, K);
   }
 }
 
@@ -153,9 +154,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
 hipError_t set_gemm_lds_attrs() {
   static std::atomic<uint64_t> done{0};
   return once_per_device(done, [] {
-    const void* ks[] = {reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<0>),
-                        reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<1>),
-                        reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<2>)};
+    const void* ks[] = {reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<0, false>),
+                        reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<0, true>),
+                        reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<1, false>),
+                        reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<2, false>),
+                        reinterpret_cast<const void*>(grouped_gemm_bf16_kernel<2, true>)};
     for (const void* k : ks) {
       const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
       if (e != hipSuccess) return e;
@@ -185,10 +188,16 @@ hipError_t launch_ffn(const moe_shape_t& s, int El, const void* xe, const int32_
   if (e != hipSuccess) return e;
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.hbuf);
   const int grid = (cus / 8) * 8;
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<0>, dim3(grid), dim3(kGemmThreads), kGemmLds, st,
-                     static_cast<const uint16_t*>(xe), static_cast<const uint16_t*>(w1),
-                     static_cast<const uint16_t*>(w3), h, offsets, mtb, ctrl, El, s.d, s.F, nullptr, nullptr, nullptr, row_src);
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<1>, dim3(grid), dim3(kGemmThreads), kGemmLds, st,
+  if (row_src)
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<0, true>), dim3(grid), dim3(kGemmThreads), kGemmLds, st, nullptr,
+                       static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), h, offsets, mtb, ctrl, El,
+                       s.d, s.F, nullptr, nullptr, nullptr, row_src);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<0, false>), dim3(grid), dim3(kGemmThreads), kGemmLds, st,
+                       static_cast<const uint16_t*>(xe), static_cast<const uint16_t*>(w1),
+                       static_cast<const uint16_t*>(w3), h, offsets, mtb, ctrl, El, s.d, s.F, nullptr, nullptr, nullptr,
+                       nullptr);
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<1, false>), dim3(grid), dim3(kGemmThreads), kGemmLds, st,
                      static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w2), nullptr,
                      static_cast<uint16_t*>(ye), offsets, mtb, ctrl, El, s.F, s.d, nullptr, nullptr, row_dst, nullptr);
   return hipGetLastError();
@@ -202,8 +211,12 @@ hipError_t launch_gemm1_bwd(const uint16_t* xe, const uint16_t* w1, const uint16
                             const int32_t* ctrl, int El, int cus, hipStream_t st, const uint64_t* row_src) {
   hipError_t e = set_gemm_lds_attrs();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<2>, dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st,
-                     row_src ? nullptr : xe, w1, w3, h, offsets, mtb, ctrl, El, d, F, dh, dab, nullptr, row_src);
+  if (row_src)
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<2, true>), dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st,
+                       nullptr, w1, w3, h, offsets, mtb, ctrl, El, d, F, dh, dab, nullptr, row_src);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<2, false>), dim3((cus / 8) * 8), dim3(kGemmThreads), kGemmLds, st,
+                       xe, w1, w3, h, offsets, mtb, ctrl, El, d, F, dh, dab, nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -74,9 +74,12 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
   // (block mode, BLK: a wave's 32 rows lie in one block, whose base is the wave's A base)
   constexpr bool bmode = BLK;
   const int bmask = bmode ? (1 << io.blk_log2) - 1 : 0;
-  const uint8_t* abase =
-      bmode ? pick4((wave * 32) >> io.blk_log2, io.ablk[0], io.ablk[1], io.ablk[2], io.ablk[3]) : io.a;
-  const uint8_t* bbase = (MODE != 1 && (wave & 1)) ? b1 : b0;
+  // (both bases are the same for the whole wave; read through readfirstlane they stay in
+  // scalar registers, so every fill takes the scalar-base + 32-bit-offset form instead of a
+  // 64-bit vector address add per fill)
+  const uint8_t* abase = wave_uniform(
+      bmode ? pick4((wave * 32) >> io.blk_log2, io.ablk[0], io.ablk[1], io.ablk[2], io.ablk[3]) : io.a);
+  const uint8_t* bbase = wave_uniform((MODE != 1 && (wave & 1)) ? b1 : b0);
   uint32_t aoff[4], boff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

@@ -57,6 +57,16 @@ struct TileIO {
   const uint64_t* row_src;  // null, or per tile row the address of its A row (replaces a0..a3)
 };
 
+// A pointer the caller knows to be the same in every lane of the wave, moved to scalar
+// registers (the compiler cannot prove that values derived from the wave index are uniform).
+template <typename T>
+__device__ __forceinline__ T* wave_uniform(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<T*>((uint64_t(hi) << 32) | lo);
+}
+
 template <typename P>
 __device__ __forceinline__ P pick4(int i, P p0, P p1, P p2, P p3) {
   return i == 0 ? p0 : (i == 1 ? p1 : (i == 2 ? p2 : p3));
@@ -162,7 +172,7 @@ __device__ __forceinline__ uint32_t lds_addr(const char* q) {
 // b0/b1: this expert's weight matrices ([Nout][K], row stride b_ld); c0: first output
 // column of the tile.  A_CPOL: cache policy of the A-row loads (0 = default; 16 = sc1, a
 // device-coherent load that does not hit this CU's L1, for rows another CU just wrote).
-template <int MODE, int A_CPOL = 0>
+template <int MODE, int A_CPOL = 0, bool A_BY_ADDR = false>
 __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __restrict__ b0,
                                           const uint16_t* __restrict__ b1, int c0, int Nout, int K,
                                           char* smem, int b_ld) {
@@ -179,25 +189,30 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
   const int rows = io.rows;
   const int bmask = (1 << io.blk_log2) - 1;
 
-  // this wave fills row groups g = wave*4 + i (rows g*8 + lrow) of the A and B tiles
+  // this wave fills row groups g = wave*4 + i (rows g*8 + lrow) of the A and B tiles.  A
+  // rows come from one block (the wave's 32 rows, or the clamped last row, lie in one block of
+  // 1 << blk_log2 rows) unless A_BY_ADDR, where each row has its own address (row_src).  The B
+  // rows of one wave are all W1 rows or all W3 rows (32-row blocks alternate, and wave w fills
+  // rows 32 w .. 32 w + 31).  So A (from blocks) and B are scalar bases plus 32-bit byte
+  // offsets, the fills' scalar-base form.
   const uint16_t* ap[4];
-  const uint16_t* bp[4];
+  uint32_t aoff[4];
+  const char* abase = nullptr;
+  if constexpr (!A_BY_ADDR)
+    abase = reinterpret_cast<const char*>(
+        wave_uniform(pick4(min(wave * 32, rows - 1) >> io.blk_log2, io.a0, io.a1, io.a2, io.a3)));
+  const char* bbase = reinterpret_cast<const char*>(wave_uniform((MODE != 1 && (wave & 1)) ? b1 : b0));
+  uint32_t boff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (wave * 4 + i) * 8 + lrow;
     const int lch = (i & 1) ? lch_odd : lch_even;
     const int rr = min(row, rows - 1);
-    ap[i] = (io.row_src ? reinterpret_cast<const uint16_t*>(io.row_src[rr])
-                        : pick4(rr >> io.blk_log2, io.a0, io.a1, io.a2, io.a3) + size_t(rr & bmask) * io.a_ld) +
-            lch * 8;
-    if (MODE != 1) {
-      // 32-row blocks alternate W1 / W3 rows of the same 32 f values
-      const int n = min(c0 + (row >> 6) * 32 + (row & 31), Nout - 1);
-      bp[i] = (((row >> 5) & 1) ? b1 : b0) + size_t(n) * b_ld + lch * 8;
-    } else {
-      const int n = min(c0 + row, Nout - 1);
-      bp[i] = b0 + size_t(n) * b_ld + lch * 8;
-    }
+    if constexpr (A_BY_ADDR) ap[i] = reinterpret_cast<const uint16_t*>(io.row_src[rr]) + lch * 8;
+    else aoff[i] = (uint32_t(rr & bmask) * uint32_t(io.a_ld) + uint32_t(lch * 8)) * 2u;
+    // (MODE 0/2: 32-row blocks alternate W1 / W3 rows of the same 32 f values)
+    const int n = (MODE != 1) ? min(c0 + (row >> 6) * 32 + (row & 31), Nout - 1) : min(c0 + row, Nout - 1);
+    boff[i] = (uint32_t(n) * uint32_t(b_ld) + uint32_t(lch * 8)) * 2u;
   }
   auto issue = [&](int ks) {
     char* sa = smem + (ks & 1) * kStageBytes;
@@ -206,8 +221,13 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int g = wave * 4 + i;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(ap[i] + koff), (lds_void_ptr)(sa + g * 1024), 16, 0, A_CPOL);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bp[i] + koff), (lds_void_ptr)(sb + g * 1024), 16, 0, 0);
+      if constexpr (A_BY_ADDR)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(ap[i] + koff), (lds_void_ptr)(sa + g * 1024), 16, 0, A_CPOL);
+      else
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(abase + (aoff[i] + uint32_t(koff * 2))),
+                                         (lds_void_ptr)(sa + g * 1024), 16, 0, A_CPOL);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bbase + (boff[i] + uint32_t(koff * 2))),
+                                       (lds_void_ptr)(sb + g * 1024), 16, 0, 0);
     }
   };
 
