@@ -107,21 +107,26 @@ __device__ __forceinline__ void gemm_mx_tile(const TileMX& io, const uint8_t* __
       splane = bs_plane;
     }
   }
+  // LDS destinations of this wave's fills (the M0 operand) as scalars: the wave's first A
+  // row group and its scale words in stage 0; stage 1 and the B tile are constant offsets
+  const uint32_t lds_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(smem + wave * 4 * 1024));
+  const uint32_t lds_sc0 = __builtin_amdgcn_readfirstlane(lds_addr(smem + kMxDataBytes + wave * 256));
   auto issue = [&](int ks) {
-    char* sa = smem + (ks & 1) * kMxStageBytes;
-    char* sb = sa + kGemmBM * kMxBK;
-    char* ss = sa + kMxDataBytes;
+    const uint32_t stage = uint32_t((ks & 1) * kMxStageBytes);
+    const uint32_t da = lds_dst0 + stage, db = da + uint32_t(kGemmBM * kMxBK);
+    const lds_void_ptr ls = (lds_void_ptr)(uintptr_t)(lds_sc0 + stage);
     const int koff = ks * kMxBK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int g = wave * 4 + i;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(abase + (aoff[i] + koff)), (lds_void_ptr)(sa + g * 1024), 16, 0, A_CPOL);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bbase + (boff[i] + koff)), (lds_void_ptr)(sb + g * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(abase + (aoff[i] + koff)),
+                                       (lds_void_ptr)(uintptr_t)(da + uint32_t(i * 1024)), 16, 0, A_CPOL);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bbase + (boff[i] + koff)),
+                                       (lds_void_ptr)(uintptr_t)(db + uint32_t(i * 1024)), 16, 0, 0);
     }
     if (A_CPOL != 0 && wave < 4)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(sp + ks * splane), (lds_void_ptr)(ss + wave * 256), 4, 0, A_CPOL);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(sp + ks * splane), ls, 4, 0, A_CPOL);
     else
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(sp + ks * splane), (lds_void_ptr)(ss + wave * 256), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(sp + ks * splane), ls, 4, 0, 0);
   };
 
   f32x16 acc[2][4];

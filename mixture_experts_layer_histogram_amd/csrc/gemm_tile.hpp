@@ -214,20 +214,23 @@ __device__ __forceinline__ void gemm_tile(const TileIO& io, const uint16_t* __re
     const int n = (MODE != 1) ? min(c0 + (row >> 6) * 32 + (row & 31), Nout - 1) : min(c0 + row, Nout - 1);
     boff[i] = (uint32_t(n) * uint32_t(b_ld) + uint32_t(lch * 8)) * 2u;
   }
+  // LDS destination of this wave's fills (the M0 operand): the wave's first A row group in
+  // stage 0, as a scalar; stage 1 and the B tile are constant offsets from it
+  const uint32_t lds_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(smem + wave * 4 * 1024));
   auto issue = [&](int ks) {
-    char* sa = smem + (ks & 1) * kStageBytes;
-    char* sb = sa + kGemmBM * kGemmBK * 2;
+    const uint32_t da = lds_dst0 + uint32_t((ks & 1) * kStageBytes);
+    const uint32_t db = da + uint32_t(kGemmBM * kGemmBK * 2);
     const int koff = ks * kGemmBK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int g = wave * 4 + i;
+      const lds_void_ptr la = (lds_void_ptr)(uintptr_t)(da + uint32_t(i * 1024));
+      const lds_void_ptr lb = (lds_void_ptr)(uintptr_t)(db + uint32_t(i * 1024));
       if constexpr (A_BY_ADDR)
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(ap[i] + koff), (lds_void_ptr)(sa + g * 1024), 16, 0, A_CPOL);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(ap[i] + koff), la, 16, 0, A_CPOL);
       else
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(abase + (aoff[i] + uint32_t(koff * 2))),
-                                         (lds_void_ptr)(sa + g * 1024), 16, 0, A_CPOL);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bbase + (boff[i] + uint32_t(koff * 2))),
-                                       (lds_void_ptr)(sb + g * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(abase + (aoff[i] + uint32_t(koff * 2))), la, 16, 0,
+                                         A_CPOL);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bbase + (boff[i] + uint32_t(koff * 2))), lb, 16, 0, 0);
     }
   };
 
