@@ -546,7 +546,7 @@ def run_backward(args, cfg, inp, P, stream, N):
                      "frac": flops / t_ffn / PEAK_BF16_FLOPS, "traffic": None},
         "stages_ms": stage_ms,
         "step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step)),
-                    "staged_calls_mean": staged_ms},
+                    "staged_calls_mean": ms_staged},
         "ms_per_step_staged": ms_staged,
         "ms_per_step_fused": ms_fused,
         "stages_hbm_frac": {
