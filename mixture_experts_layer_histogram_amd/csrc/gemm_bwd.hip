@@ -88,9 +88,13 @@ __device__ __forceinline__ void gemm_tile_t(const Operand& A, const Operand& B, 
   const int lch_odd = lpos ^ (4 + (lrow >> 1));
   const int nk = K / kGemmBK;
 
-  // per fill i (LDS block g = wave*4 + i): K-major source pointers, or MN-major columns
-  const uint16_t* ak[4];
-  const uint16_t* bk[4];
+  // Fills take the scalar-base form: a wave-uniform 64-bit base per operand and K step plus
+  // a 32-bit byte offset per lane.  K-major: the base is the tile's first row, the offset
+  // that of the lane's row and 16-byte chunk, plus the K step's.  MN-major: the base is the
+  // K step's first K row (from p0 or p1: ksplit is a multiple of 64, so one K step never
+  // straddles it; or the K step's 64-row block), the offset that of the lane's K row within
+  // the step, clamped to kvalid - 1, and of its column.
+  uint32_t akoff[4], bkoff[4];
   int acol[4], bcol[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -98,33 +102,43 @@ __device__ __forceinline__ void gemm_tile_t(const Operand& A, const Operand& B, 
     const int lch = (i & 1) ? lch_odd : lch_even;
     const int mrow = 8 * wave + 2 * i + hi;                 // MN-major: K row of this lane
     const int mcol = (r32 ^ (4 * (mrow & 3))) * 8;
-    if (!A_MN) ak[i] = A.p0 + size_t(min(krow, A.rows - 1)) * A.ld + lch * 8;
+    if (!A_MN) akoff[i] = (uint32_t(min(krow, A.rows - 1)) * uint32_t(A.ld) + uint32_t(lch * 8)) * 2u;
     else acol[i] = min(mcol, A.rows - 8);
-    if (!B_MN) bk[i] = B.p0 + size_t(min(krow, B.rows - 1)) * B.ld + lch * 8;
+    if (!B_MN) bkoff[i] = (uint32_t(min(krow, B.rows - 1)) * uint32_t(B.ld) + uint32_t(lch * 8)) * 2u;
     else bcol[i] = min(mcol, B.rows - 8);
   }
-  auto mn_src = [&](const Operand& X, int kg, int col) -> const uint16_t* {
-    kg = min(kg, X.kvalid - 1);
-    return (kg < X.ksplit ? X.p0 + size_t(kg) * X.ld : X.p1 + size_t(kg - X.ksplit) * X.ld) + col;
+  const char* akbase = A_MN ? nullptr : reinterpret_cast<const char*>(wave_uniform(A.p0));
+  const char* bkbase = B_MN ? nullptr : reinterpret_cast<const char*>(wave_uniform(B.p0));
+  auto mn_base = [&](const Operand& X, int koff) -> const char* {
+    return reinterpret_cast<const char*>(wave_uniform(koff < X.ksplit ? X.p0 + size_t(koff) * X.ld
+                                                                     : X.p1 + size_t(koff - X.ksplit) * X.ld));
+  };
+  auto mn_lane_off = [&](const Operand& X, int koff, int i, int col) -> uint32_t {
+    const int kr = min(8 * wave + 2 * i + hi, X.kvalid - 1 - koff);
+    return (uint32_t(kr) * uint32_t(X.ld) + uint32_t(col)) * 2u;
   };
   // B_BLK: the base of B's 64-row block of the K step being issued (bblk), and of the next
   // one, loaded a K step ahead
   const uint16_t* bblk = nullptr;
   uint64_t bnext = 0;
+  // LDS destination of this wave's fills (the M0 operand), as a scalar
+  const uint32_t lds_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(smem + wave * 4 * 1024));
   auto issue = [&](int ks) {
-    char* sa = smem + (ks & 1) * kStageBytes;
-    char* sb = sa + kGemmBM * kGemmBK * 2;
+    const uint32_t da = lds_dst0 + uint32_t((ks & 1) * kStageBytes);
+    const uint32_t db = da + uint32_t(kGemmBM * kGemmBK * 2);
     const int koff = ks * kGemmBK;
+    const char* abase = A_MN ? mn_base(A, koff) : akbase;
+    const char* bbase;
+    if constexpr (B_BLK) bbase = reinterpret_cast<const char*>(wave_uniform(bblk + B.coff));
+    else bbase = B_MN ? mn_base(B, koff) : bkbase;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int g = wave * 4 + i;
-      const int kg = koff + 8 * wave + 2 * i + hi;
-      const uint16_t* pa = A_MN ? mn_src(A, kg, acol[i]) : ak[i] + koff;
-      const uint16_t* pb;
-      if constexpr (B_BLK) pb = bblk + size_t(min(kg, B.kvalid - 1) - koff) * B.ld + B.coff + bcol[i];
-      else pb = B_MN ? mn_src(B, kg, bcol[i]) : bk[i] + koff;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(pa), (lds_void_ptr)(sa + g * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(pb), (lds_void_ptr)(sb + g * 1024), 16, 0, 0);
+      const lds_void_ptr la = (lds_void_ptr)(uintptr_t)(da + uint32_t(i * 1024));
+      const lds_void_ptr lb = (lds_void_ptr)(uintptr_t)(db + uint32_t(i * 1024));
+      const uint32_t ao = A_MN ? mn_lane_off(A, koff, i, acol[i]) : akoff[i] + uint32_t(koff * 2);
+      const uint32_t bo = B_MN ? mn_lane_off(B, koff, i, bcol[i]) : bkoff[i] + uint32_t(koff * 2);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(abase + ao), la, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(bbase + bo), lb, 16, 0, 0);
     }
   };
 
